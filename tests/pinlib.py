@@ -1,0 +1,289 @@
+"""Checks that pin the fp64 oracle to facts fixed outside of it.
+
+Each check takes an oracle library handle (``lib=None`` means the real one) so
+that tests/test_oracle_mutants.py can run the same checks against deliberately
+broken copies of the oracle and show that every planted mistake is caught.
+
+Sources of truth used here, none of them the oracle itself:
+  * closed forms (uniform rows, equal-others peaked rows, V = 2 logistic, V = 1);
+  * 120-digit brute force with mpmath straight from the definitions
+    log p_t = x_t - log sum_j e^{x_j}, H = -sum p log p,
+    dL/dz_j = (g/T)(p_j - [j = t]), and mpmath central differences of the loss;
+  * invariants (shift, column permutation, temperature scaling, zero row sum);
+  * library routines (numpy.argmax, numpy.flatnonzero).
+"""
+from __future__ import annotations
+
+import math
+
+import mpmath as mp
+import numpy as np
+
+import oracle
+from workloads import bf16_bits, bf16_to_f32
+
+# 120 digits: the peaked brute-force rows need log p_t ~ e^{-115} resolved
+# after an O(100) cancellation, so 50 digits would not be enough.
+mp.mp.dps = 120
+
+
+# ----------------------------------------------------------------- references
+def mp_row(z, t, T, g=1.0):
+    """Brute-force log p_t, loss, entropy, dlogits, and log p at every column,
+    for one row of stored values z (float array) at 50 digits, unshifted."""
+    x = [mp.mpf(float(v)) / mp.mpf(T) for v in z]
+    Z = mp.fsum(mp.e ** xi for xi in x)
+    lse = mp.log(Z)
+    logp_all = [xi - lse for xi in x]
+    p = [mp.e ** lp for lp in logp_all]
+    H = -mp.fsum(pj * lp for pj, lp in zip(p, logp_all))
+    w = mp.mpf(g) / mp.mpf(T)
+    dl = [w * (p[j] - (1 if j == t else 0)) for j in range(len(z))]
+    return dict(logp=logp_all[t], loss=-logp_all[t], entropy=H, dl=dl, logp_all=logp_all)
+
+
+def mp_loss_of(z, t, T):
+    x = [mp.mpf(v) / mp.mpf(T) for v in z]
+    return mp.log(mp.fsum(mp.e ** xi for xi in x)) - x[t]
+
+
+def rel(a, b):
+    a = float(a)
+    b = float(b)
+    if a == b:
+        return 0.0
+    return abs(a - b) / max(abs(b), 1e-300)
+
+
+# --------------------------------------------------------------------- P1..P4
+def check_uniform(lib=None):
+    """All-equal row: log p = -log V, H = log V, argmax 0 (lowest index),
+    dl_j = (g/T)(1/V - [j = t])."""
+    for V in (3, 7, 4096, 151936):
+        for T in (1.0, 0.9, 0.7):
+            z = np.full((1, V), 3.25, dtype=np.float32)
+            t = V // 3
+            lab = np.array([t], dtype=np.int64)
+            o = oracle.ce_rows(z, lab, T, lib=lib, threads=1)
+            assert rel(o["logp"][0], -math.log(V)) < 1e-14, (V, T, o["logp"][0])
+            # plain sequential fp64 summation of V terms: error bound ~ V * eps
+            assert rel(o["entropy"][0], math.log(V)) < 1e-14 + 2.3e-16 * V, (V, T, o["entropy"][0])
+            assert o["argmax"][0] == 0
+            g = np.array([1.5])
+            d = oracle.ce_grad_rows(z, lab, g, T, lib=lib, threads=1)[0]
+            w = 1.5 / T
+            expect = np.full(V, w / V)
+            expect[t] = w * (1.0 / V - 1.0)
+            assert np.max(np.abs(d - expect) / np.abs(expect)) < 1e-14 + 2.3e-16 * V, (V, T)
+
+
+def check_peaked_closed_form(lib=None):
+    """Target at margin M above V-1 equal others:
+    log p_t = -softplus(log(V-1) - M/T); dl_t = -(g/T) sigmoid(log(V-1) - M/T);
+    dl_j = (g/T) e^{-M/T} / (1 + (V-1) e^{-M/T}); H from p_t and the equal others."""
+    for V in (2, 1003, 40001):
+        for T in (1.0, 0.9):
+            for M in (5.0, 17.0, 20.0, 30.0, 36.75, 40.0, 50.0, 80.0, 300.0):
+                z = np.zeros((1, V), dtype=np.float32)
+                t = (7 * V) // 11
+                z[0, t] = M
+                lab = np.array([t], dtype=np.int64)
+                o = oracle.ce_rows(z, lab, T, lib=lib, threads=1)
+                a = mp.log(V - 1) - mp.mpf(M) / mp.mpf(T)
+                sp = mp.log1p(mp.e ** a)
+                assert rel(o["logp"][0], -sp) < 1e-13, (V, T, M, o["logp"][0], sp)
+                assert rel(o["loss"][0], sp) < 1e-13
+                # closed form with -log p_t = log1p((V-1) e^{-M/T}) and
+                # -log p_o = M/T - log p_t, so nothing rounds to 1 at 50 digits
+                b = mp.mpf(M) / mp.mpf(T)
+                nlpt = mp.log1p((V - 1) * mp.e ** (-b))
+                pt = mp.e ** (-nlpt)
+                po = pt * mp.e ** (-b)
+                H = pt * nlpt + (V - 1) * po * (b + nlpt)
+                assert rel(o["entropy"][0], H) < 1e-13 + 2.3e-16 * V, (V, T, M, o["entropy"][0], H)
+                assert o["argmax"][0] == t
+                d = oracle.ce_grad_rows(z, lab, np.array([2.0]), T, lib=lib, threads=1)[0]
+                w = 2.0 / T
+                q = (V - 1) * mp.e ** (-b) / (1 + (V - 1) * mp.e ** (-b))
+                assert rel(d[t], -w * q) < 1e-12, (V, T, M)
+                other = 0 if t != 0 else 1
+                assert rel(d[other], w * po) < 1e-12, (V, T, M)
+
+
+def check_two_class(lib=None):
+    """V = 2: log p_t = -softplus(x_o - x_t), the logistic."""
+    rng = np.random.default_rng(11)
+    for _ in range(40):
+        z = (rng.standard_normal((1, 2)) * 30).astype(np.float32)
+        t = int(rng.integers(0, 2))
+        for T in (1.0, 0.7):
+            o = oracle.ce_rows(z, np.array([t]), T, lib=lib, threads=1)
+            d = (mp.mpf(float(z[0, 1 - t])) - mp.mpf(float(z[0, t]))) / mp.mpf(T)
+            assert rel(o["logp"][0], -mp.log1p(mp.e ** d)) < 1e-13
+
+
+def check_single_class(lib=None):
+    """V = 1: log p = loss = H = 0, argmax 0, dl = 0; log p is -0.0, never +."""
+    z = np.array([[1.75]], dtype=np.float32)
+    o = oracle.ce_rows(z, np.array([0]), 0.9, lib=lib, threads=1)
+    assert o["logp"][0] == 0 and math.copysign(1, o["logp"][0]) == -1
+    assert o["loss"][0] == 0 and o["entropy"][0] == 0 and o["argmax"][0] == 0
+    d = oracle.ce_grad_rows(z, np.array([0]), np.array([1.0]), 0.9, lib=lib, threads=1)
+    assert d[0, 0] == 0
+
+
+# ------------------------------------------------------------------------ P5
+def _brute_rows(seed):
+    """Small rows: random (fp32 and bf16 values), and peaked rows up to margin 80."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for V in (5, 17, 64):
+        z = (rng.standard_normal(V) * 3).astype(np.float32)
+        rows.append(("f32", z))
+        rows.append(("bf16", bf16_bits(z)))
+        for M in (17.0, 50.0, 80.0):
+            zp = rng.standard_normal(V).astype(np.float32)
+            t = int(rng.integers(0, V))
+            zp[t] = -np.inf
+            zp[t] = np.float32(zp.max() + M)
+            rows.append(("f32p%d" % t, zp))
+    return rows
+
+
+def check_bruteforce(lib=None):
+    """Oracle vs 120-digit brute force: log p, loss, H, every dl_j, top-K, argmax."""
+    for kind, z in _brute_rows(5):
+        V = z.shape[0]
+        stored = bf16_to_f32(z) if z.dtype == np.uint16 else z
+        if kind.startswith("f32p"):
+            t = int(kind[4:])
+        else:
+            t = (3 * V) // 5
+        for T in (1.0, 0.9, 0.7):
+            ref = mp_row(stored, t, T, g=1.25)
+            o = oracle.ce_rows(z[None, :], np.array([t]), T, lib=lib, threads=1)
+            assert rel(o["logp"][0], ref["logp"]) < 1e-13, (kind, V, T)
+            assert rel(o["loss"][0], ref["loss"]) < 1e-13, (kind, V, T)
+            assert rel(o["entropy"][0], ref["entropy"]) < 1e-12, (kind, V, T)
+            assert o["argmax"][0] == int(np.argmax(stored))
+            d = oracle.ce_grad_rows(z[None, :], np.array([t]), np.array([1.25]), T, lib=lib,
+                                    threads=1)[0]
+            for j in range(V):
+                assert rel(d[j], ref["dl"][j]) < 1e-12, (kind, V, T, j, d[j], ref["dl"][j])
+            idx = np.array([[t, 0, V - 1, V // 2]], dtype=np.int64)
+            lp, _ = oracle.topk_rows(z[None, :], idx, T, lib=lib, threads=1)
+            for k in range(idx.shape[1]):
+                assert rel(lp[0, k], ref["logp_all"][idx[0, k]]) < 1e-13, (kind, V, T, k)
+
+
+def check_central_difference(lib=None):
+    """dl_j against mpmath central differences of the loss (g = 1)."""
+    rng = np.random.default_rng(9)
+    for V in (4, 9):
+        z = (rng.standard_normal(V) * 2).astype(np.float32)
+        t = 1
+        T = 0.9
+        d = oracle.ce_grad_rows(z[None, :], np.array([t]), np.array([1.0]), T, lib=lib,
+                                threads=1)[0]
+        for j in range(V):
+            def f(h, j=j):
+                zz = [mp.mpf(float(v)) for v in z]
+                zz[j] += h
+                return mp_loss_of(zz, t, T)
+            num = mp.diff(f, 0)
+            assert rel(d[j], num) < 1e-12, (V, j, d[j], num)
+
+
+# ------------------------------------------------------------------------ P6
+def _grid_row(rng, V):
+    # Values on a 2^-10 grid within +-64: adding 5 or doubling stays exact in fp32.
+    return (np.round(rng.standard_normal(V) * 3 * 1024) / 1024).astype(np.float32)
+
+
+def check_invariants(lib=None):
+    rng = np.random.default_rng(21)
+    V = 1000
+    z = np.stack([_grid_row(rng, V) for _ in range(6)])
+    lab = rng.integers(0, V, 6).astype(np.int64)
+    g = rng.standard_normal(6)
+    base = oracle.ce_rows(z, lab, 0.9, lib=lib, threads=1)
+    # log p <= 0, loss = -log p
+    assert np.all(np.signbit(base["logp"]) | (base["logp"] == 0))
+    assert np.all(base["loss"] == -base["logp"])
+    assert np.all(base["entropy"] >= 0) and np.all(base["entropy"] <= math.log(V) + 1e-12)
+    # gradient rows sum to zero
+    d = oracle.ce_grad_rows(z, lab, g, 0.9, lib=lib, threads=1)
+    assert np.all(np.abs(d.sum(1)) <= 1e-14 * np.abs(d).sum(1) * V ** 0.5 + 1e-300)
+    # shift invariance (exact shift)
+    sh = oracle.ce_rows(z + np.float32(5.0), lab, 0.9, lib=lib, threads=1)
+    for k in ("logp", "entropy"):
+        assert np.max(np.abs(sh[k] - base[k]) / np.abs(base[k])) < 1e-12, k
+    assert np.array_equal(sh["argmax"], base["argmax"])
+    # column permutation equivariance
+    perm = rng.permutation(V)
+    inv = np.argsort(perm)
+    zp = np.ascontiguousarray(z[:, perm])
+    lp = inv[lab]
+    pp = oracle.ce_rows(zp, lp, 0.9, lib=lib, threads=1)
+    for k in ("logp", "entropy"):
+        assert np.max(np.abs(pp[k] - base[k]) / np.abs(base[k])) < 1e-12, k
+    dp = oracle.ce_grad_rows(zp, lp, g, 0.9, lib=lib, threads=1)
+    assert np.max(np.abs(dp[:, inv] - d) / np.abs(d)) < 1e-12
+    # temperature scaling: T = 0.5 on z equals T = 1 on 2z (both exact)
+    a = oracle.ce_rows(z, lab, 0.5, lib=lib, threads=1)
+    b = oracle.ce_rows(z * np.float32(2.0), lab, 1.0, lib=lib, threads=1)
+    for k in ("logp", "entropy"):
+        assert np.array_equal(a[k], b[k]), k
+    # top-K at index = label equals the single-target log p
+    idx = np.stack([lab, (lab + 1) % V], axis=1)
+    tk, _ = oracle.topk_rows(z, idx, 0.9, lib=lib, threads=1)
+    assert np.max(np.abs(tk[:, 0] - base["logp"]) / np.abs(base["logp"])) < 1e-14
+
+
+# ------------------------------------------------------------------------ P7
+def check_library_routines(lib=None):
+    rng = np.random.default_rng(33)
+    V = 300
+    z = bf16_bits((rng.standard_normal((40, V)) * 0.5).astype(np.float32))  # many ties
+    stored = bf16_to_f32(z)
+    # force explicit ties of the maximum in a few rows
+    for r in range(0, 40, 5):
+        c = rng.choice(V, 3, replace=False)
+        z[r, c] = bf16_bits(np.array([9.0], dtype=np.float32))[0]
+    stored = bf16_to_f32(z)
+    lab = rng.integers(0, V, 40).astype(np.int64)
+    o = oracle.ce_rows(z, lab, 1.0, lib=lib, threads=1)
+    assert np.array_equal(o["argmax"], np.argmax(stored, axis=1))
+    lab[rng.permutation(40)[:9]] = -100
+    mask = (rng.random(40) > 0.2).astype(np.uint8)
+    vr, st = oracle.valid_rows(lab, mask, V, lib=lib)
+    assert np.array_equal(vr, np.flatnonzero((lab != -100) & (mask != 0)))
+    assert st == 0
+    lab[3] = V + 4
+    vr, st = oracle.valid_rows(lab, None, V, lib=lib)
+    assert st == oracle.BAD_LABEL and 3 not in vr
+
+
+def check_strided(lib=None):
+    """A padded row stride reads the same rows as the dense copy."""
+    rng = np.random.default_rng(44)
+    big = (rng.standard_normal((7, 150)) * 2).astype(np.float32)
+    view = big[:, :101]
+    dense = np.ascontiguousarray(view)
+    lab = rng.integers(0, 101, 7).astype(np.int64)
+    a = oracle.ce_rows(view, lab, 0.8, lib=lib, threads=1)
+    b = oracle.ce_rows(dense, lab, 0.8, lib=lib, threads=1)
+    for k in ("logp", "entropy", "argmax"):
+        assert np.array_equal(a[k], b[k]), k
+    g = rng.standard_normal(7)
+    assert np.array_equal(oracle.ce_grad_rows(view, lab, g, 0.8, lib=lib, threads=1),
+                          oracle.ce_grad_rows(dense, lab, g, 0.8, lib=lib, threads=1))
+    # and each row of the dense copy equals the brute force of that row
+    for r in range(7):
+        ref = mp_row(dense[r], int(lab[r]), 0.8)
+        assert rel(a["logp"][r], ref["logp"]) < 1e-13
+
+
+ALL_CHECKS = [check_strided, check_uniform, check_peaked_closed_form, check_two_class, check_single_class,
+              check_bruteforce, check_central_difference, check_invariants,
+              check_library_routines]

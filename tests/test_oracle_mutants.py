@@ -1,0 +1,70 @@
+"""Plant plausible mistakes in a copy of the oracle's C source (on the CPU) and
+show that the pins catch every one of them: a dropped term, a wrong sign, a
+wrong index, a transposed operand, a missing 1/T."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+import pinlib
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle_cev.c")
+
+# (name, text in oracle_cev.c, replacement)
+MUTANTS = [
+    ("softplus_drops_one", "log1p(exp(-fabs(u)))", "log(exp(-fabs(u)))"),
+    ("softplus_sign", "fmax(u, 0.0) + log1p", "fmax(-u, 0.0) + log1p"),
+    ("sigmoid_neg_branch", "return e / (1.0 + e);", "return 1.0 / (1.0 + e);"),
+    ("sum_includes_target", "        if (j != excl)\n            s += exp",
+     "        if (1)\n            s += exp"),
+    ("lse_drops_shift", "return m + log(s);", "return log(s);"),
+    ("u_sign", "double u = lse_excluding(row, dtype, vocab, T, t) - xt;\n        double l = softplus",
+     "double u = xt - lse_excluding(row, dtype, vocab, T, t);\n        double l = softplus"),
+    ("target_not_scaled", "double xt = load_z(row, dtype, t) / T;\n        double u = lse_excluding(row, dtype, vocab, T, t) - xt;\n        double l = softplus",
+     "double xt = load_z(row, dtype, t);\n        double u = lse_excluding(row, dtype, vocab, T, t) - xt;\n        double l = softplus"),
+    ("entropy_drops_target_term", "double h = exp(-l) * l;", "double h = 0.0;"),
+    ("entropy_sign", "h += exp(x - lse) * (lse - x);", "h += exp(x - lse) * (x - lse);"),
+    ("argmax_last_tie", "if (z > best) {", "if (z >= best) {"),
+    ("grad_target_sign", "-w * sigmoid(u)", "w * sigmoid(u)"),
+    ("grad_drops_chain_rule", "double w = g[r] / T;", "double w = g[r];"),
+    ("grad_other_index", "w * exp(load_z(row, dtype, j) / T - lse)",
+     "w * exp(load_z(row, dtype, vocab - 1 - j) / T - lse)"),
+    ("bf16_widen_shift", "<< 16;", "<< 15;"),
+    ("row_stride_ignored", "(size_t)r * (size_t)row_stride * esz", "(size_t)r * (size_t)1 * esz"),
+    ("topk_no_exclusion", "v = -softplus(lse_excluding(row, dtype, vocab, T, i) - xi);",
+     "v = -softplus(lse_excluding(row, dtype, vocab, T, -1) - xi);"),
+    ("topk_row_index", "int64_t i = idx[r * idx_stride + k];", "int64_t i = idx[k * idx_stride + r % 1];"),
+    ("mask_inverted", "if (row_mask && row_mask[r] == 0)\n        return 0;",
+     "if (row_mask && row_mask[r] != 0)\n        return 0;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation site for {name} not unique or missing"
+    src = tmp_path / "oracle_cev.c"
+    src.write_text(text.replace(old, new))
+    lib_path = str(tmp_path / "liboracle_mut.so")
+    oracle.build(force=True, src=str(src), out=lib_path)
+    lib = oracle.load_library(lib_path)
+    caught = []
+    for check in pinlib.ALL_CHECKS:
+        try:
+            check(lib=lib)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(check.__name__)
+            break
+    assert caught, f"no pin caught mutant {name}"
+
+
+def test_unmutated_source_passes_all_pins(tmp_path):
+    src = tmp_path / "oracle_cev.c"
+    shutil.copy(SRC, src)
+    lib_path = str(tmp_path / "liboracle_copy.so")
+    oracle.build(force=True, src=str(src), out=lib_path)
+    lib = oracle.load_library(lib_path)
+    for check in pinlib.ALL_CHECKS:
+        check(lib=lib)

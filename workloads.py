@@ -1,0 +1,175 @@
+"""Seeded synthetic inputs for the five workloads of the hot path.
+
+This module holds input construction only -- random draws, bf16 rounding of
+the draws, label/mask/index layouts -- and none of the log-softmax arithmetic.
+It is the one module that both the HIP-path tests and the oracle tests take
+their inputs from.
+
+Recipes (numpy PCG64; fp32 draws, rounded to bf16 by round-to-nearest-even
+where the workload is bf16).  Per-row parameters come from
+``default_rng(seed)``; the logit matrix is drawn in blocks of BLOCK_ROWS rows,
+block b from ``default_rng([seed, 1, b])``, so any block can be regenerated on
+its own and blocks can be drawn in parallel.
+
+  tiny   seed 0  64 x 4096 fp32, z = 2 N(0,1); labels uniform; 8 rows chosen by
+                 permutation get -100; T = 1; g = 1.
+                 (ms-swift PR #10337, the selective log-softmax semantics)
+  chunk  seed 1  4096 x 32768 bf16, z = bf16(3 N(0,1)); labels uniform; T = 0.7;
+                 top-K: 8 distinct uniform indices per row.
+                 (ms-swift PR #10337, Experiment results table: 4096 x 32768)
+  grpo   seed 2  8192 x 152064 bf16, z = bf16(3 N(0,1) + shift_r),
+                 shift_r ~ U(-5, 5); labels uniform; exactly rows // 10 rows
+                 masked out; g ~ N(0,1) fp32; T = 1.
+                 (ms-swift PR #10337, Experiment results table: 8192 x 152064)
+  sparse seed 3  2 sequences x 1024 tokens, suffix-cropped to 961 rows each
+                 (1922 rows), V = 4096 fp32, z = 2 N(0,1); per sequence 4 spans
+                 of 32 supervised rows at local rows 104, 344, 584, 824, labels
+                 uniform there and -100 elsewhere; g = 1; T = 1.
+                 (ms-swift PR #10353, Experiment results: 1922 kept rows,
+                 256 supervised, vocabulary 4096)
+  peaked seed 4  2048 x 151936; others N(0,1) (fp32, or their bf16 rounding);
+                 labels uniform; margin per row uniform over
+                 {5, 17, 20, 30, 50, 80}; z_t = dtype(max of the stored
+                 others + margin); T in {1.0, 0.9}; g = 1.
+                 (Liger PR #1555 page, unsloth-zoo #2080 Accuracy table:
+                 margins 17/20/30/50 at V = 151936; Details: targets 5 to 40
+                 above the rest)
+"""
+from __future__ import annotations
+
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+IGNORE_INDEX = -100
+BLOCK_ROWS = 256
+PEAK_MARGINS = (5.0, 17.0, 20.0, 30.0, 50.0, 80.0)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even) and return
+    the 16-bit patterns as uint16.  Inputs are finite."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to float32 exactly."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def stored_values(logits: np.ndarray) -> np.ndarray:
+    """The stored logits as float32 (exact for both fp32 and bf16 storage)."""
+    return bf16_to_f32(logits) if logits.dtype == np.uint16 else logits
+
+
+def _draw_matrix(seed, rows, vocab, fill, threads=8):
+    """Draw [rows, vocab] block by block; fill(block_index, rng, r0, r1) returns
+    the block's stored values."""
+    nb = (rows + BLOCK_ROWS - 1) // BLOCK_ROWS
+    blocks = [None] * nb
+
+    def one(b):
+        r0 = b * BLOCK_ROWS
+        r1 = min(rows, r0 + BLOCK_ROWS)
+        rng = np.random.default_rng([seed, 1, b])
+        blocks[b] = fill(b, rng, r0, r1)
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(one, range(nb)))
+    return blocks
+
+
+def _assemble(blocks, rows, vocab, dtype):
+    out = np.empty((rows, vocab), dtype=dtype)
+    r = 0
+    for blk in blocks:
+        out[r:r + blk.shape[0]] = blk
+        r += blk.shape[0]
+    return out
+
+
+def tiny(rows=64, vocab=4096, n_ignored=8, seed=0):
+    rng = np.random.default_rng(seed)
+    labels = rng.integers(0, vocab, rows).astype(np.int64)
+    labels[rng.permutation(rows)[:n_ignored]] = IGNORE_INDEX
+    blocks = _draw_matrix(seed, rows, vocab,
+                          lambda b, g, r0, r1: (2.0 * g.standard_normal((r1 - r0, vocab),
+                                                                        dtype=np.float32)))
+    logits = _assemble(blocks, rows, vocab, np.float32)
+    return dict(name="tiny", logits=logits, labels=labels, row_mask=None, temperature=1.0,
+                g=np.ones(rows, dtype=np.float32))
+
+
+def chunk(rows=4096, vocab=32768, K=8, seed=1):
+    rng = np.random.default_rng(seed)
+    labels = rng.integers(0, vocab, rows).astype(np.int64)
+    indices = np.stack([rng.choice(vocab, K, replace=False) for _ in range(rows)]).astype(np.int64)
+    blocks = _draw_matrix(seed, rows, vocab,
+                          lambda b, g, r0, r1: bf16_bits(3.0 * g.standard_normal(
+                              (r1 - r0, vocab), dtype=np.float32)))
+    logits = _assemble(blocks, rows, vocab, np.uint16)
+    return dict(name="chunk", logits=logits, labels=labels, row_mask=None, temperature=0.7,
+                indices=indices, g=np.ones(rows, dtype=np.float32))
+
+
+def grpo(rows=8192, vocab=152064, seed=2, temperature=1.0):
+    rng = np.random.default_rng(seed)
+    shift = rng.uniform(-5.0, 5.0, rows).astype(np.float32)
+    labels = rng.integers(0, vocab, rows).astype(np.int64)
+    row_mask = np.ones(rows, dtype=np.uint8)
+    row_mask[rng.permutation(rows)[:rows // 10]] = 0
+    g = rng.standard_normal(rows, dtype=np.float32)
+
+    def fill(b, gen, r0, r1):
+        z = 3.0 * gen.standard_normal((r1 - r0, vocab), dtype=np.float32)
+        z += shift[r0:r1, None]
+        return bf16_bits(z)
+
+    logits = _assemble(_draw_matrix(seed, rows, vocab, fill), rows, vocab, np.uint16)
+    return dict(name="grpo", logits=logits, labels=labels, row_mask=row_mask,
+                temperature=temperature, g=g)
+
+
+def sparse(n_seq=2, seq_len=1024, kept=961, vocab=4096, span_starts=(104, 344, 584, 824),
+           span_len=32, seed=3):
+    rng = np.random.default_rng(seed)
+    rows = n_seq * kept
+    labels = np.full(rows, IGNORE_INDEX, dtype=np.int64)
+    for s in range(n_seq):
+        for a in span_starts:
+            r0 = s * kept + a
+            labels[r0:r0 + span_len] = rng.integers(0, vocab, span_len)
+    blocks = _draw_matrix(seed, rows, vocab,
+                          lambda b, g, r0, r1: (2.0 * g.standard_normal((r1 - r0, vocab),
+                                                                        dtype=np.float32)))
+    logits = _assemble(blocks, rows, vocab, np.float32)
+    return dict(name="sparse", logits=logits, labels=labels, row_mask=None, temperature=1.0,
+                g=np.ones(rows, dtype=np.float32), seq_shape=(n_seq, kept), seq_len=seq_len)
+
+
+def peaked(dtype="f32", temperature=1.0, rows=2048, vocab=151936, seed=4):
+    rng = np.random.default_rng(seed)
+    labels = rng.integers(0, vocab, rows).astype(np.int64)
+    margins = np.asarray(PEAK_MARGINS, dtype=np.float32)[rng.integers(0, len(PEAK_MARGINS), rows)]
+
+    def fill(b, gen, r0, r1):
+        z = gen.standard_normal((r1 - r0, vocab), dtype=np.float32)
+        if dtype == "bf16":
+            z = bf16_to_f32(bf16_bits(z))
+        for i, r in enumerate(range(r0, r1)):
+            t = labels[r]
+            z[i, t] = -np.inf
+            peak = np.float32(z[i].max() + margins[r])
+            z[i, t] = peak
+        return bf16_bits(z) if dtype == "bf16" else z
+
+    store = np.uint16 if dtype == "bf16" else np.float32
+    logits = _assemble(_draw_matrix(seed, rows, vocab, fill), rows, vocab, store)
+    return dict(name=f"peaked_{dtype}_T{temperature:g}", logits=logits, labels=labels,
+                row_mask=None, temperature=float(temperature), margins=margins,
+                g=np.ones(rows, dtype=np.float32))
+
+
+BUILDERS = dict(tiny=tiny, chunk=chunk, grpo=grpo, sparse=sparse, peaked=peaked)
