@@ -1,0 +1,224 @@
+"""cross_entropy_vocab_amd -- collapse-safe selective log-softmax and
+cross-entropy over a [rows, vocab] logit matrix on AMD MI355X (gfx950).
+
+Thin binding over libcevocab.so (see include/cevocab.h).  The functions below
+check tensor metadata, allocate outputs with PyTorch when the caller does not
+pass them, and hand device pointers plus the current HIP stream to the C ABI.
+Every step of the computation runs in the library's HIP kernels; PyTorch is
+used for device memory and streams only.
+
+    out = ce_forward(logits, labels, temperature=1.0, row_mask=mask)
+    dlogits = ce_backward(logits, labels, g, out["saved"], temperature=1.0, row_mask=mask)
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+__all__ = ["sls_forward", "sls_topk_forward", "ce_forward", "ce_backward", "workspace_size",
+           "status_string", "version", "CEV_F32", "CEV_BF16", "STATUS_BAD_LABEL",
+           "STATUS_BAD_INDEX", "SAVED_BYTES", "CevError"]
+
+CEV_F32 = 0
+CEV_BF16 = 1
+STATUS_BAD_LABEL = 1
+STATUS_BAD_INDEX = 2
+SAVED_BYTES = 16
+
+
+class CevError(RuntimeError):
+    """A non-zero return code from libcevocab.so."""
+
+    def __init__(self, fn, code):
+        self.code = code
+        super().__init__(f"{fn}: {status_string(code)} (code {code})")
+
+
+def status_string(code: int) -> str:
+    return _lib.get().cev_status_string(int(code)).decode()
+
+
+def version() -> int:
+    return int(_lib.get().cev_version())
+
+
+def workspace_size(rows: int) -> int:
+    return int(_lib.get().cev_workspace_size(int(rows)))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return CEV_F32
+    if t.dtype == torch.bfloat16:
+        return CEV_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _check_logits(logits: torch.Tensor):
+    if not logits.is_cuda:
+        raise ValueError("logits must be a GPU tensor")
+    if logits.dim() != 2:
+        raise ValueError("logits must be 2-D [rows, vocab] (flatten leading dimensions)")
+    if logits.shape[0] > 0 and logits.shape[1] > 1 and logits.stride(1) != 1:
+        raise ValueError("logits must have unit column stride")
+    rows, vocab = logits.shape
+    stride = logits.stride(0) if rows > 1 else max(vocab, logits.stride(0))
+    return rows, vocab, max(stride, vocab)
+
+
+def _dev(t, name, dtype, shape, device):
+    if t is None:
+        return None
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _mask(row_mask, rows, device):
+    if row_mask is None:
+        return None
+    if row_mask.dtype == torch.bool:
+        row_mask = row_mask.view(torch.uint8)
+    return _dev(row_mask, "row_mask", torch.uint8, (rows,), device)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise CevError(fn, rc)
+
+
+def sls_forward(logits, labels, temperature=1.0, row_mask=None, ignore_index=-100,
+                entropy=False, argmax=False, status=None):
+    """log p at the label per row (fp32 [rows]), plus optional entropy and
+    argmax.  Returns a dict with keys logp, entropy, argmax."""
+    rows, vocab, stride = _check_logits(logits)
+    dev = logits.device
+    _dev(labels, "labels", torch.int64, (rows,), dev)
+    m = _mask(row_mask, rows, dev)
+    _dev(status, "status", torch.int32, (1,), dev)
+    out = {
+        "logp": torch.empty(rows, dtype=torch.float32, device=dev),
+        "entropy": torch.empty(rows, dtype=torch.float32, device=dev) if entropy else None,
+        "argmax": torch.empty(rows, dtype=torch.int64, device=dev) if argmax else None,
+    }
+    rc = _lib.get().sls_forward(_ptr(logits), rows, vocab, stride, _dtype_code(logits),
+                                _ptr(labels), int(ignore_index), float(temperature), _ptr(m),
+                                _ptr(out["logp"]), _ptr(out["entropy"]), _ptr(out["argmax"]),
+                                _ptr(status), _stream(dev))
+    _check("sls_forward", rc)
+    return out
+
+
+def sls_topk_forward(logits, indices, temperature=1.0, row_mask=None, ignore_index=-100,
+                     status=None):
+    """log p at K gathered indices per row: fp32 [rows, K]."""
+    rows, vocab, stride = _check_logits(logits)
+    dev = logits.device
+    if indices.dim() != 2 or indices.shape[0] != rows or indices.dtype != torch.int64:
+        raise ValueError("indices must be int64 [rows, K]")
+    if not indices.is_cuda or indices.device != dev:
+        raise ValueError(f"indices must be on {dev}")
+    K = indices.shape[1]
+    if rows > 1 and K > 1 and indices.stride(1) != 1:
+        raise ValueError("indices must have unit column stride")
+    istride = indices.stride(0) if rows > 1 else K
+    m = _mask(row_mask, rows, dev)
+    _dev(status, "status", torch.int32, (1,), dev)
+    logp = torch.empty((rows, K), dtype=torch.float32, device=dev)
+    rc = _lib.get().sls_topk_forward(_ptr(logits), rows, vocab, stride, _dtype_code(logits),
+                                     _ptr(indices), K, max(istride, K), int(ignore_index),
+                                     float(temperature), _ptr(m), _ptr(logp), _ptr(status),
+                                     _stream(dev))
+    _check("sls_topk_forward", rc)
+    return logp
+
+
+def ce_forward(logits, labels, temperature=1.0, row_mask=None, ignore_index=-100, logp=True,
+               entropy=False, argmax=False, valid_rows=True, status=None, out=None):
+    """Per-row cross-entropy forward with device-side compaction of the valid
+    rows.  Returns a dict: loss [rows] fp32, saved [rows, 16] uint8 (for
+    ce_backward), and optionally logp, entropy, argmax, valid_rows [rows] int64
+    (first n_valid entries meaningful) and n_valid [1] int64.
+
+    `out` may hold preallocated tensors under the same keys (plus "workspace")
+    so that repeated calls allocate nothing."""
+    rows, vocab, stride = _check_logits(logits)
+    dev = logits.device
+    _dev(labels, "labels", torch.int64, (rows,), dev)
+    m = _mask(row_mask, rows, dev)
+    _dev(status, "status", torch.int32, (1,), dev)
+    o = dict(out) if out else {}
+
+    def want(key, flag, dtype, shape):
+        if not flag:
+            o[key] = None
+        elif o.get(key) is None:
+            o[key] = torch.empty(shape, dtype=dtype, device=dev)
+        else:
+            _dev(o[key], key, dtype, shape, dev)
+
+    want("loss", True, torch.float32, (rows,))
+    want("saved", True, torch.uint8, (rows, SAVED_BYTES))
+    want("logp", logp, torch.float32, (rows,))
+    want("entropy", entropy, torch.float32, (rows,))
+    want("argmax", argmax, torch.int64, (rows,))
+    want("valid_rows", valid_rows, torch.int64, (rows,))
+    want("n_valid", valid_rows, torch.int64, (1,))
+    ws = None
+    ws_bytes = 0
+    if not valid_rows:
+        ws_bytes = workspace_size(rows)
+        ws = o.get("workspace")
+        if ws is None or ws.numel() < ws_bytes:
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        o["workspace"] = ws
+    rc = _lib.get().ce_forward(_ptr(logits), rows, vocab, stride, _dtype_code(logits),
+                               _ptr(labels), int(ignore_index), float(temperature), _ptr(m),
+                               _ptr(o["loss"]), _ptr(o["saved"]), _ptr(o["logp"]),
+                               _ptr(o["entropy"]), _ptr(o["argmax"]), _ptr(o["valid_rows"]),
+                               _ptr(o["n_valid"]), _ptr(ws), ws_bytes, _ptr(status),
+                               _stream(dev))
+    _check("ce_forward", rc)
+    return o
+
+
+def ce_backward(logits, labels, g, saved, temperature=1.0, row_mask=None, ignore_index=-100,
+                dlogits=None, status=None):
+    """dlogits = (g/T)(softmax(logits/T) - onehot(labels)) per valid row, zero
+    rows elsewhere, in the logits dtype."""
+    rows, vocab, stride = _check_logits(logits)
+    dev = logits.device
+    _dev(labels, "labels", torch.int64, (rows,), dev)
+    _dev(g, "g", torch.float32, (rows,), dev)
+    _dev(saved, "saved", torch.uint8, (rows, SAVED_BYTES), dev)
+    m = _mask(row_mask, rows, dev)
+    _dev(status, "status", torch.int32, (1,), dev)
+    if dlogits is None:
+        dlogits = torch.empty((rows, vocab), dtype=logits.dtype, device=dev)
+    else:
+        if dlogits.dtype != logits.dtype or tuple(dlogits.shape) != (rows, vocab):
+            raise ValueError("dlogits must match logits in dtype and shape")
+        if rows > 0 and vocab > 1 and dlogits.stride(1) != 1:
+            raise ValueError("dlogits must have unit column stride")
+    dstride = max(dlogits.stride(0) if rows > 1 else vocab, vocab)
+    rc = _lib.get().ce_backward(_ptr(logits), rows, vocab, stride, _dtype_code(logits),
+                                _ptr(labels), int(ignore_index), float(temperature), _ptr(m),
+                                _ptr(g), _ptr(saved), _ptr(dlogits), dstride, _ptr(status),
+                                _stream(dev))
+    _check("ce_backward", rc)
+    return dlogits

@@ -1,0 +1,276 @@
+// api.cpp -- the C ABI of libcevocab.so: argument validation on the host, then
+// kernel launches on the caller's stream.  Nothing here allocates, frees or
+// synchronizes.  Entry points and their semantics are declared in cevocab.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "cev_launch.h"
+#include "cevocab.h"
+
+namespace {
+
+using cev::BackwardArgs;
+using cev::CompactArgs;
+using cev::SweepArgs;
+
+constexpr int64_t kMaxRows = INT32_MAX;       // one workgroup per row in the grid
+constexpr int64_t kMaxVocab = INT32_MAX / 2;  // step codes are 32-bit
+constexpr int64_t kMaxK = 1024;               // gathered indices per row held in LDS
+
+int elem_size(int dtype) { return dtype == CEV_F32 ? 4 : 2; }
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+hipStream_t to_hip(cev_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Checks shared by every entry point.  On success *done is set when rows == 0
+// (nothing to enqueue).
+int check_common(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride, int dtype,
+                 double temperature, bool *done)
+{
+    *done = false;
+    if (dtype != CEV_F32 && dtype != CEV_BF16)
+        return CEV_EDTYPE;
+    if (!(std::isfinite(temperature) && temperature > 0.0))
+        return CEV_ETEMP;
+    if (rows < 0 || vocab < 1 || rows > kMaxRows || vocab > kMaxVocab)
+        return CEV_ESHAPE;
+    if (row_stride < vocab)
+        return CEV_ESTRIDE;
+    if (rows == 0) {
+        *done = true;
+        return CEV_OK;
+    }
+    if (row_stride > INT64_MAX / 4 / rows)
+        return CEV_ESHAPE;
+    if (!logits)
+        return CEV_ENULL;
+    if (!aligned(logits, (uintptr_t)elem_size(dtype)))
+        return CEV_EALIGN;
+    // The per-row closing step works from fp32 copies of log2(e)/T and 1/T;
+    // both must be finite and non-zero.
+    const double c = 1.4426950408889634074 / temperature;
+    if (!(c < 3.0e38 && c > 1.0e-37) || !(1.0 / temperature < 3.0e38))
+        return CEV_ETEMP;
+    return CEV_OK;
+}
+
+void fill_temperature(SweepArgs &a, double temperature)
+{
+    a.temperature = temperature;
+    a.c = (float)(1.4426950408889634074 / temperature);
+    a.inv_t = (float)(1.0 / temperature);
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? CEV_OK : CEV_ELAUNCH; }
+
+} // namespace
+
+extern "C" {
+
+int sls_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride, int dtype,
+                const int64_t *labels, int64_t ignore_index, double temperature,
+                const uint8_t *row_mask, float *logp, float *entropy, int64_t *argmax,
+                int32_t *status, cev_stream_t stream)
+{
+    bool done;
+    int rc = check_common(logits, rows, vocab, row_stride, dtype, temperature, &done);
+    if (rc != CEV_OK || done)
+        return rc;
+    if (!labels || !logp)
+        return CEV_ENULL;
+    if (!aligned(labels, 8) || !aligned(logp, 4) || !aligned(entropy, 4) || !aligned(argmax, 8) ||
+        !aligned(status, 4))
+        return CEV_EALIGN;
+    SweepArgs a{};
+    a.logits = logits;
+    a.rows = rows;
+    a.vocab = vocab;
+    a.row_stride = row_stride;
+    a.labels = labels;
+    a.ignore_index = ignore_index;
+    a.row_mask = row_mask;
+    fill_temperature(a, temperature);
+    a.logp = logp;
+    a.entropy = entropy;
+    a.argmax = argmax;
+    a.status = status;
+    return launch_status(cev::launch_sls_sweep(dtype, a, entropy != nullptr, argmax != nullptr,
+                                               to_hip(stream)));
+}
+
+int sls_topk_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride,
+                     int dtype, const int64_t *indices, int64_t K, int64_t index_row_stride,
+                     int64_t ignore_index, double temperature, const uint8_t *row_mask,
+                     float *logp, int32_t *status, cev_stream_t stream)
+{
+    if (K < 1 || K > kMaxK)
+        return CEV_ESHAPE;
+    if (index_row_stride < K)
+        return CEV_ESTRIDE;
+    bool done;
+    int rc = check_common(logits, rows, vocab, row_stride, dtype, temperature, &done);
+    if (rc != CEV_OK || done)
+        return rc;
+    if (!indices || !logp)
+        return CEV_ENULL;
+    if (!aligned(indices, 8) || !aligned(logp, 4) || !aligned(status, 4))
+        return CEV_EALIGN;
+    SweepArgs a{};
+    a.logits = logits;
+    a.rows = rows;
+    a.vocab = vocab;
+    a.row_stride = row_stride;
+    a.indices = indices;
+    a.K = K;
+    a.index_row_stride = index_row_stride;
+    a.ignore_index = ignore_index;
+    a.row_mask = row_mask;
+    fill_temperature(a, temperature);
+    a.logp = logp;
+    a.status = status;
+    return launch_status(cev::launch_topk_sweep(dtype, a, to_hip(stream)));
+}
+
+size_t cev_workspace_size(int64_t rows)
+{
+    if (rows < 0)
+        return 0;
+    return (size_t)(rows + 1) * sizeof(int64_t);
+}
+
+int ce_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride, int dtype,
+               const int64_t *labels, int64_t ignore_index, double temperature,
+               const uint8_t *row_mask, float *loss, void *saved, float *logp, float *entropy,
+               int64_t *argmax, int64_t *valid_rows, int64_t *n_valid, void *workspace,
+               size_t workspace_bytes, int32_t *status, cev_stream_t stream)
+{
+    bool done;
+    int rc = check_common(logits, rows, vocab, row_stride, dtype, temperature, &done);
+    if (rc != CEV_OK || done)
+        return rc;
+    if (!labels || !loss || !saved)
+        return CEV_ENULL;
+    if (!aligned(labels, 8) || !aligned(loss, 4) || !aligned(saved, 16) || !aligned(logp, 4) ||
+        !aligned(entropy, 4) || !aligned(argmax, 8) || !aligned(valid_rows, 8) ||
+        !aligned(n_valid, 8) || !aligned(status, 4))
+        return CEV_EALIGN;
+    int64_t *list = valid_rows;
+    int64_t *count = n_valid;
+    if (!list || !count) {
+        if (!workspace)
+            return CEV_ENULL;
+        if (!aligned(workspace, 8))
+            return CEV_EALIGN;
+        if (workspace_bytes < cev_workspace_size(rows))
+            return CEV_EWORKSPACE;
+        int64_t *ws = static_cast<int64_t *>(workspace);
+        if (!list)
+            list = ws;
+        if (!count)
+            count = ws + rows;
+    }
+
+    CompactArgs ca{};
+    ca.rows = rows;
+    ca.vocab = vocab;
+    ca.labels = labels;
+    ca.ignore_index = ignore_index;
+    ca.row_mask = row_mask;
+    ca.rowlist = list;
+    ca.nlist = count;
+    ca.logp = logp;
+    ca.loss = loss;
+    ca.entropy = entropy;
+    ca.argmax = argmax;
+    ca.saved = static_cast<cev_saved *>(saved);
+    ca.status = status;
+    hipError_t e = cev::launch_compact(ca, to_hip(stream));
+    if (e != hipSuccess)
+        return CEV_ELAUNCH;
+
+    SweepArgs a{};
+    a.logits = logits;
+    a.rows = rows;
+    a.vocab = vocab;
+    a.row_stride = row_stride;
+    a.labels = labels;
+    a.ignore_index = ignore_index;
+    a.row_mask = row_mask;
+    a.rowlist = list;
+    a.nlist = count;
+    fill_temperature(a, temperature);
+    a.logp = logp;
+    a.loss = loss;
+    a.entropy = entropy;
+    a.argmax = argmax;
+    a.saved = static_cast<cev_saved *>(saved);
+    a.status = status;
+    return launch_status(cev::launch_sls_sweep(dtype, a, entropy != nullptr, argmax != nullptr,
+                                               to_hip(stream)));
+}
+
+int ce_backward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride, int dtype,
+                const int64_t *labels, int64_t ignore_index, double temperature,
+                const uint8_t *row_mask, const float *g, const void *saved, void *dlogits,
+                int64_t dlogits_row_stride, int32_t *status, cev_stream_t stream)
+{
+    bool done;
+    int rc = check_common(logits, rows, vocab, row_stride, dtype, temperature, &done);
+    if (rc != CEV_OK || done)
+        return rc;
+    if (dlogits_row_stride < vocab)
+        return CEV_ESTRIDE;
+    if (dlogits_row_stride > INT64_MAX / 4 / rows)
+        return CEV_ESHAPE;
+    if (!labels || !g || !saved || !dlogits)
+        return CEV_ENULL;
+    const int es = elem_size(dtype);
+    if (!aligned(labels, 8) || !aligned(g, 4) || !aligned(saved, 16) ||
+        !aligned(dlogits, (uintptr_t)es) || !aligned(status, 4))
+        return CEV_EALIGN;
+    const uintptr_t l0 = (uintptr_t)logits, l1 = l0 + (uintptr_t)(((rows - 1) * row_stride + vocab) * es);
+    const uintptr_t d0 = (uintptr_t)dlogits,
+                    d1 = d0 + (uintptr_t)(((rows - 1) * dlogits_row_stride + vocab) * es);
+    if (l0 < d1 && d0 < l1)
+        return CEV_EALIAS;
+    BackwardArgs a{};
+    a.logits = logits;
+    a.rows = rows;
+    a.vocab = vocab;
+    a.row_stride = row_stride;
+    a.labels = labels;
+    a.ignore_index = ignore_index;
+    a.row_mask = row_mask;
+    a.g = g;
+    a.saved = static_cast<const cev_saved *>(saved);
+    a.dlogits = dlogits;
+    a.d_row_stride = dlogits_row_stride;
+    a.temperature = temperature;
+    a.c = (float)(1.4426950408889634074 / temperature);
+    a.status = status;
+    return launch_status(cev::launch_backward(dtype, a, to_hip(stream)));
+}
+
+const char *cev_status_string(int code)
+{
+    switch (code) {
+    case CEV_OK: return "ok";
+    case CEV_ENULL: return "a required pointer is NULL";
+    case CEV_ESHAPE: return "invalid shape: rows < 0, vocab < 1, K outside [1, 1024], or a size overflows";
+    case CEV_ESTRIDE: return "a row stride is smaller than the row";
+    case CEV_EALIGN: return "a pointer is not aligned to its element size";
+    case CEV_EDTYPE: return "unknown dtype (expected CEV_F32 or CEV_BF16)";
+    case CEV_ETEMP: return "temperature must be finite and > 0";
+    case CEV_EWORKSPACE: return "workspace smaller than cev_workspace_size(rows)";
+    case CEV_EALIAS: return "dlogits overlaps logits";
+    case CEV_ELAUNCH: return "kernel launch failed";
+    default: return "unknown error code";
+    }
+}
+
+int cev_version(void) { return 100; }
+
+} // extern "C"

@@ -1,0 +1,79 @@
+// cev_launch.h -- host-side launchers between the C ABI (api.cpp) and the
+// kernels.  Arguments arrive validated; each launcher only enqueues work and
+// returns the hipError_t of the launch.  Internal to libcevocab.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cevocab.h"
+
+namespace cev {
+
+// Everything a forward sweep needs for one call.  Row selection: when rowlist
+// is non-null the block index b maps to row rowlist[b] for b < *nlist (the
+// compacted sparse-supervision path); otherwise block b is row b.
+struct SweepArgs {
+    const void *logits;
+    int64_t rows;
+    int64_t vocab;
+    int64_t row_stride;        // elements
+    const int64_t *labels;     // single-target sweeps
+    const int64_t *indices;    // top-K sweeps: [rows, K]
+    int64_t K;
+    int64_t index_row_stride;
+    int64_t ignore_index;
+    const uint8_t *row_mask;
+    const int64_t *rowlist;
+    const int64_t *nlist;
+    double temperature;
+    float c;                   // log2(e) / T, rounded to fp32
+    float inv_t;               // 1 / T, rounded to fp32
+    float *logp;               // [rows] or [rows, K]
+    float *loss;
+    float *entropy;
+    int64_t *argmax;
+    cev_saved *saved;
+    int32_t *status;
+};
+
+struct CompactArgs {
+    int64_t rows;
+    int64_t vocab;
+    const int64_t *labels;
+    int64_t ignore_index;
+    const uint8_t *row_mask;
+    int64_t *rowlist;          // out [rows]
+    int64_t *nlist;            // out [1]
+    float *logp;
+    float *loss;
+    float *entropy;
+    int64_t *argmax;
+    cev_saved *saved;
+    int32_t *status;
+};
+
+struct BackwardArgs {
+    const void *logits;
+    int64_t rows;
+    int64_t vocab;
+    int64_t row_stride;
+    const int64_t *labels;
+    int64_t ignore_index;
+    const uint8_t *row_mask;
+    const float *g;
+    const cev_saved *saved;
+    void *dlogits;
+    int64_t d_row_stride;
+    double temperature;
+    float c;                   // log2(e) / T
+    int32_t *status;
+};
+
+hipError_t launch_sls_sweep(int dtype, const SweepArgs &a, bool want_entropy, bool want_argmax,
+                            hipStream_t stream);
+hipError_t launch_topk_sweep(int dtype, const SweepArgs &a, hipStream_t stream);
+hipError_t launch_compact(const CompactArgs &a, hipStream_t stream);
+hipError_t launch_backward(int dtype, const BackwardArgs &a, hipStream_t stream);
+
+} // namespace cev

@@ -1,0 +1,540 @@
+// sweep.hip -- forward vocab sweeps for gfx950: one workgroup per row, one HBM
+// pass over the row, target-excluded online softmax statistics in fp32, and a
+// per-row closing step in fp64.
+//
+// The form follows Liger-Kernel PR #1555 ("Fix softmax collapse in CE, GRPO,
+// KL/JSD and softmax"), Summary, CE/FLCE bullet: the first pass accumulates the
+// sum WITHOUT the target, and the loss is softplus(log(sum_others) + m - x_t),
+// so e^0 = 1 is never added to e^{-margin}.  Unlike the pages' Triton kernels
+// (which skip the target's whole block and re-read it afterwards, per the
+// unsloth-zoo #2080 Summary quoted there), the sweep here excludes the target
+// per 16-byte vector: a wave-uniform range test per step, with a per-element
+// mask only in the one step that holds the target.  The sum is based at m_o,
+// the largest NON-target logit, so it is >= 1 and cannot underflow to zero
+// even when every other term is below the fp32 normal range.
+#include "cev_device.h"
+#include "cev_launch.h"
+
+namespace cev {
+namespace {
+
+constexpr float kBig = 3.0e38f;
+constexpr int kMaxK = 1024; // gathered indices per row in sls_topk_forward
+constexpr double kLog2e = 1.4426950408889634074;
+
+// Running statistics of one lane over the (non-excluded) columns it has seen.
+struct LaneState {
+    float m;    // exact largest stored value seen, -inf if none
+    float s;    // sum of 2^((z - b) c), b = max(m, -FLT_MAX), c = log2(e)/T
+    float comp; // Kahan compensation: the true sum is about s - comp
+    float h;    // sum of 2^((z - b) c) (b - z) / T, for the entropy
+    int best;   // code of the first step in which m was reached
+};
+
+template <int N> __device__ __forceinline__ float tree_sum(float (&e)[N])
+{
+#pragma unroll
+    for (int w = 1; w < N; w *= 2)
+#pragma unroll
+        for (int i = 0; i + w < N; i += 2 * w)
+            e[i] += e[i + w];
+    return e[0];
+}
+
+// Fold one step of N values into the lane state.  Excluded columns arrive as
+// -inf; MAYBE_INF selects the guarded entropy term for such steps.
+template <int DT, int N, bool WANT_H, bool WANT_ARG, bool MAYBE_INF>
+__device__ __forceinline__ void fold(LaneState &st, float (&v)[N], int code, float c, float inv_t)
+{
+    float sm = v[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i)
+        sm = fmaxf(sm, v[i]);
+    if constexpr (WANT_ARG)
+        st.best = sm > st.m ? code : st.best;
+    const float mnew = fmaxf(st.m, sm);
+    const float bold = fmaxf(st.m, -FLT_MAX);
+    const float bnew = fmaxf(mnew, -FLT_MAX);
+    // Rescale to the new base; f == 1 exactly when the maximum did not move.
+    const float f = exp2_hw((bold - bnew) * c);
+    if constexpr (WANT_H)
+        st.h = f * fmaf(fminf((bnew - bold) * inv_t, kBig), st.s, st.h);
+    st.s *= f;
+    st.comp *= f;
+    st.m = mnew;
+
+    float e[N];
+    if constexpr (DT == CEV_F32) {
+        // (z - b) first: exact for the terms near the maximum that dominate.
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            e[i] = exp2_hw((v[i] - bnew) * c);
+    } else {
+        const float nb = fminf(-bnew * c, kBig);
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            e[i] = exp2_hw(fmaf(v[i], c, nb));
+    }
+    if constexpr (WANT_H) {
+        float ph = 0.0f;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            float d = (bnew - v[i]) * inv_t;
+            if constexpr (MAYBE_INF)
+                d = fminf(d, kBig);
+            ph = fmaf(e[i], d, ph);
+        }
+        st.h += ph;
+    }
+    const float ps = tree_sum(e);
+    const float y = ps - st.comp;
+    const float tsum = st.s + y;
+    st.comp = (tsum - st.s) - y;
+    st.s = tsum;
+}
+
+template <int DT, int U>
+__device__ __forceinline__ void unpack_step(const u32x4 (&w)[U], float (&v)[U * Elem<DT>::kVE])
+{
+    constexpr int VE = Elem<DT>::kVE;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float t[VE];
+        unpack16<DT>(w[u], t);
+#pragma unroll
+        for (int e = 0; e < VE; ++e)
+            v[u * VE + e] = t[e];
+    }
+}
+
+// Row geometry: `head` scalar columns up to the first 16-byte boundary, then
+// nvec 16-byte vectors (nfull wave steps of CH vectors plus nrem more), then
+// scalar columns from tail0 to V.
+struct RowGeom {
+    int head;
+    int64_t nvec, nfull, nrem, tail0;
+};
+
+template <int DT, int U> __device__ __forceinline__ RowGeom row_geom(const char *rowp, int64_t V)
+{
+    constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize;
+    constexpr int64_t CH = (int64_t)kWave * U;
+    RowGeom g;
+    int64_t h = (int64_t)(((16u - ((unsigned)(uintptr_t)rowp & 15u)) & 15u) / ES);
+    g.head = (int)(h < V ? h : V);
+    g.nvec = (V - g.head) / VE;
+    g.nfull = g.nvec / CH;
+    g.nrem = g.nvec - g.nfull * CH;
+    g.tail0 = g.head + g.nvec * VE;
+    return g;
+}
+
+// Codes name the step where a lane's maximum first appeared, so that the
+// argmax can be found by re-reading that one step:
+//   [0, 16)                         head column
+//   16 + k                          wave step (chunk) k
+//   16 + nfull + i                  remainder vector nfull*CH + i
+//   16 + nfull + nrem + i           tail column tail0 + i
+template <int DT, int U>
+__device__ int64_t rescan_argmax(const char *rowp, const RowGeom &g, int code, float M, int64_t t)
+{
+    constexpr int VE = Elem<DT>::kVE;
+    constexpr int64_t CH = (int64_t)kWave * U;
+    const int lane = threadIdx.x & (kWave - 1);
+    const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp + (size_t)g.head * Elem<DT>::kSize);
+    int64_t found = INT64_MAX;
+    if (code < 16)
+        return code;
+    int64_t c2 = code - 16;
+    if (c2 < g.nfull) {
+        const int64_t k = c2;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float v[VE];
+            unpack16<DT>(load16_stream(vp + k * CH + u * kWave + lane), v);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                int64_t col = g.head + (k * CH + u * kWave + lane) * VE + e;
+                if (found == INT64_MAX && v[e] == M && col != t)
+                    found = col;
+            }
+        }
+        return found;
+    }
+    c2 -= g.nfull;
+    if (c2 < g.nrem) {
+        const int64_t j = g.nfull * CH + c2;
+        float v[VE];
+        unpack16<DT>(load16_stream(vp + j), v);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+            int64_t col = g.head + j * VE + e;
+            if (found == INT64_MAX && v[e] == M && col != t)
+                found = col;
+        }
+        return found;
+    }
+    c2 -= g.nrem;
+    return g.tail0 + c2;
+}
+
+// ------------------------------------------------------------------------
+// Single-target sweep: sls_forward and the sweep stage of ce_forward.
+template <int DT, int BLOCK, int U, bool WANT_H, bool WANT_ARG>
+__global__ __launch_bounds__(BLOCK) void k_sls_sweep(SweepArgs a)
+{
+    constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize, W = BLOCK / kWave;
+    constexpr int64_t CH = (int64_t)kWave * U;
+    __shared__ float sh_f[W];
+    __shared__ double sh_d[W];
+    __shared__ int64_t sh_i[W];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+
+    int64_t r;
+    if (a.rowlist) {
+        if ((int64_t)blockIdx.x >= *a.nlist)
+            return;
+        r = a.rowlist[blockIdx.x];
+    } else {
+        r = blockIdx.x;
+    }
+    const int64_t V = a.vocab;
+    const int64_t t = a.labels[r];
+    if (!a.rowlist) {
+        const bool masked = a.row_mask && a.row_mask[r] == 0;
+        const bool ignored = masked || t == a.ignore_index;
+        const bool bad = !ignored && (t < 0 || t >= V);
+        if (ignored || bad) {
+            if (tid == 0) {
+                a.logp[r] = 0.0f;
+                if (a.entropy)
+                    a.entropy[r] = 0.0f;
+                if (a.argmax)
+                    a.argmax[r] = -1;
+                if (bad && a.status)
+                    atomicOr(a.status, (int32_t)CEV_STATUS_BAD_LABEL);
+            }
+            return;
+        }
+    }
+
+    const char *rowp = static_cast<const char *>(a.logits) + (size_t)r * (size_t)a.row_stride * ES;
+    const RowGeom g = row_geom<DT, U>(rowp, V);
+    const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp + (size_t)g.head * ES);
+    const float c = a.c, inv_t = a.inv_t;
+    LaneState st{-INFINITY, 0.0f, 0.0f, 0.0f, -1};
+
+    if (tid < g.head) {
+        float v[1] = {tid == t ? -INFINITY : load_elem<DT>(rowp, tid)};
+        fold<DT, 1, WANT_H, WANT_ARG, true>(st, v, tid, c, inv_t);
+    }
+
+    // Full wave steps, interleaved over the waves, one step of loads in flight
+    // ahead of the arithmetic.
+    {
+        int64_t k = wave;
+        u32x4 cur[U], nxt[U];
+        if (k < g.nfull) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                cur[u] = load16_stream(vp + k * CH + u * kWave + lane);
+        }
+        for (; k < g.nfull; k += W) {
+            const int64_t kn = k + W;
+            if (kn < g.nfull) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    nxt[u] = load16_stream(vp + kn * CH + u * kWave + lane);
+            }
+            float v[U * VE];
+            unpack_step<DT, U>(cur, v);
+            const int64_t lo = g.head + k * CH * VE;
+            if ((uint64_t)(t - lo) < (uint64_t)(CH * VE)) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int e = 0; e < VE; ++e)
+                        if (g.head + (k * CH + u * kWave + lane) * VE + e == t)
+                            v[u * VE + e] = -INFINITY;
+                fold<DT, U * VE, WANT_H, WANT_ARG, true>(st, v, 16 + (int)k, c, inv_t);
+            } else {
+                fold<DT, U * VE, WANT_H, WANT_ARG, false>(st, v, 16 + (int)k, c, inv_t);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                cur[u] = nxt[u];
+        }
+    }
+
+    for (int64_t j = g.nfull * CH + tid; j < g.nvec; j += BLOCK) {
+        float v[VE];
+        unpack16<DT>(load16_stream(vp + j), v);
+#pragma unroll
+        for (int e = 0; e < VE; ++e)
+            if (g.head + j * VE + e == t)
+                v[e] = -INFINITY;
+        fold<DT, VE, WANT_H, WANT_ARG, true>(st, v, 16 + (int)(g.nfull + (j - g.nfull * CH)), c,
+                                             inv_t);
+    }
+    if (g.tail0 + tid < V) {
+        const int64_t col = g.tail0 + tid;
+        float v[1] = {col == t ? -INFINITY : load_elem<DT>(rowp, col)};
+        fold<DT, 1, WANT_H, WANT_ARG, true>(st, v, 16 + (int)(g.nfull + g.nrem + tid), c, inv_t);
+    }
+
+    // Combine the lanes: exact maximum first, then each lane rescales its own
+    // sum once to the common base and the sums are added in fp64.
+    const float M = block_max<BLOCK>(st.m, sh_f);
+    const float B = fmaxf(M, -FLT_MAX);
+    const float bl = fmaxf(st.m, -FLT_MAX);
+    const float f = exp2_hw((bl - B) * c);
+    const float sl = st.s - st.comp;
+    const double S = block_sum<BLOCK>((double)sl * (double)f, sh_d);
+    double Hs = 0.0;
+    if constexpr (WANT_H)
+        Hs = block_sum<BLOCK>((double)f * (double)fmaf(fminf((B - bl) * inv_t, kBig), sl, st.h),
+                              sh_d);
+    int64_t a_o = INT64_MAX;
+    if constexpr (WANT_ARG) {
+        int64_t mine = INT64_MAX;
+        if (M != -INFINITY && st.m == M)
+            mine = rescan_argmax<DT, U>(rowp, g, st.best, M, t);
+        a_o = block_min<BLOCK>(mine, sh_i);
+    }
+
+    if (tid == 0) {
+        // Per-row closing step in fp64 from exact inputs (z_t, B) and the sum.
+        const double T = a.temperature;
+        const float zt = load_elem<DT>(rowp, t);
+        const double u = S > 0.0 ? log(S) + ((double)B - (double)zt) / T : -INFINITY;
+        const double loss = softplus64(u);
+        const double q = sigmoid64(u);
+        const double lse = (double)zt / T + loss;
+        if (a.logp)
+            a.logp[r] = (float)(-loss);
+        if (a.loss)
+            a.loss[r] = (float)loss;
+        if constexpr (WANT_H) {
+            // H = p_t * loss + sum_{j != t} p_j (lse - x_j), every term >= 0,
+            // with sum_{j != t} p_j = q and lse - x_j = (lse - B/T) + (B - z_j)/T.
+            double H = 0.0;
+            if (S > 0.0)
+                H = exp(-loss) * loss + q * (lse - (double)B / T) + exp((double)B / T - lse) * Hs;
+            a.entropy[r] = (float)H;
+        }
+        if constexpr (WANT_ARG)
+            a.argmax[r] = (zt > M || (zt == M && t < a_o)) ? t : a_o;
+        if (a.saved) {
+            const float mz = fmaxf(zt, M);
+            cev_saved sv;
+            sv.m_z = mz;
+            sv.log2_d = (float)((lse - (double)mz / T) * kLog2e);
+            sv.q = (float)q;
+            sv.flags = 1;
+            a.saved[r] = sv;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
+// Top-K sweep: the sum runs over the columns outside the gathered set; each
+// gathered column's complement is that sum plus the other gathered terms.
+template <int DT, int BLOCK, int U>
+__global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
+{
+    constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize, W = BLOCK / kWave;
+    constexpr int64_t CH = (int64_t)kWave * U;
+    __shared__ float sh_f[W];
+    __shared__ double sh_d[W];
+    __shared__ int64_t xcol[kMaxK];
+    __shared__ float xz[kMaxK];
+    __shared__ unsigned char xfirst[kMaxK];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int64_t r = blockIdx.x;
+    const int64_t V = a.vocab;
+    const int K = (int)a.K;
+    float *out = a.logp + (size_t)r * (size_t)K;
+
+    if (a.row_mask && a.row_mask[r] == 0) {
+        for (int k = tid; k < K; k += BLOCK)
+            out[k] = 0.0f;
+        return;
+    }
+    const char *rowp = static_cast<const char *>(a.logits) + (size_t)r * (size_t)a.row_stride * ES;
+    bool bad = false;
+    for (int k = tid; k < K; k += BLOCK) {
+        const int64_t i = a.indices[(size_t)r * (size_t)a.index_row_stride + k];
+        const bool ok = i != a.ignore_index && i >= 0 && i < V;
+        bad |= (i != a.ignore_index && !ok);
+        xcol[k] = ok ? i : -1;
+        xz[k] = ok ? load_elem<DT>(rowp, i) : -INFINITY;
+    }
+    if (bad && a.status)
+        atomicOr(a.status, (int32_t)CEV_STATUS_BAD_INDEX);
+    __syncthreads();
+    for (int k = tid; k < K; k += BLOCK) {
+        bool first = xcol[k] >= 0;
+        for (int k2 = 0; k2 < k && first; ++k2)
+            first = xcol[k2] != xcol[k];
+        xfirst[k] = first;
+    }
+    __syncthreads();
+
+    const RowGeom g = row_geom<DT, U>(rowp, V);
+    const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp + (size_t)g.head * ES);
+    const float c = a.c, inv_t = a.inv_t;
+    LaneState st{-INFINITY, 0.0f, 0.0f, 0.0f, -1};
+
+    auto excluded = [&](int64_t col) {
+        bool x = false;
+        for (int k = 0; k < K; ++k)
+            x |= xcol[k] == col;
+        return x;
+    };
+
+    if (tid < g.head) {
+        float v[1] = {excluded(tid) ? -INFINITY : load_elem<DT>(rowp, tid)};
+        fold<DT, 1, false, false, true>(st, v, 0, c, inv_t);
+    }
+    {
+        int64_t k = wave;
+        u32x4 cur[U], nxt[U];
+        if (k < g.nfull) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                cur[u] = load16_stream(vp + k * CH + u * kWave + lane);
+        }
+        for (; k < g.nfull; k += W) {
+            const int64_t kn = k + W;
+            if (kn < g.nfull) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    nxt[u] = load16_stream(vp + kn * CH + u * kWave + lane);
+            }
+            float v[U * VE];
+            unpack_step<DT, U>(cur, v);
+            const int64_t lo = g.head + k * CH * VE;
+            bool any = false;
+            for (int kk = 0; kk < K; kk += kWave) {
+                const int64_t x = kk + lane < K ? xcol[kk + lane] : -1;
+                any |= __any(x >= 0 && (uint64_t)(x - lo) < (uint64_t)(CH * VE)) != 0;
+            }
+            if (any) {
+                for (int k2 = 0; k2 < K; ++k2) {
+                    const int64_t x = xcol[k2];
+                    if (x >= 0 && (uint64_t)(x - lo) < (uint64_t)(CH * VE)) {
+#pragma unroll
+                        for (int u = 0; u < U; ++u)
+#pragma unroll
+                            for (int e = 0; e < VE; ++e)
+                                if (g.head + (k * CH + u * kWave + lane) * VE + e == x)
+                                    v[u * VE + e] = -INFINITY;
+                    }
+                }
+                fold<DT, U * VE, false, false, true>(st, v, 0, c, inv_t);
+            } else {
+                fold<DT, U * VE, false, false, false>(st, v, 0, c, inv_t);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                cur[u] = nxt[u];
+        }
+    }
+    for (int64_t j = g.nfull * CH + tid; j < g.nvec; j += BLOCK) {
+        float v[VE];
+        unpack16<DT>(load16_stream(vp + j), v);
+#pragma unroll
+        for (int e = 0; e < VE; ++e)
+            if (excluded(g.head + j * VE + e))
+                v[e] = -INFINITY;
+        fold<DT, VE, false, false, true>(st, v, 0, c, inv_t);
+    }
+    if (g.tail0 + tid < V) {
+        const int64_t col = g.tail0 + tid;
+        float v[1] = {excluded(col) ? -INFINITY : load_elem<DT>(rowp, col)};
+        fold<DT, 1, false, false, true>(st, v, 0, c, inv_t);
+    }
+
+    const float M = block_max<BLOCK>(st.m, sh_f);
+    const float B = fmaxf(M, -FLT_MAX);
+    const float bl = fmaxf(st.m, -FLT_MAX);
+    const float f = exp2_hw((bl - B) * c);
+    const double S = block_sum<BLOCK>((double)(st.s - st.comp) * (double)f, sh_d);
+    float gm = -INFINITY;
+    for (int k = tid; k < K; k += BLOCK)
+        gm = fmaxf(gm, xz[k]);
+    const float Mall = fmaxf(block_max<BLOCK>(gm, sh_f), M);
+    const float Ball = fmaxf(Mall, -FLT_MAX);
+    const double T = a.temperature;
+    for (int k = tid; k < K; k += BLOCK) {
+        if (xcol[k] < 0) {
+            out[k] = 0.0f;
+            continue;
+        }
+        double s = S > 0.0 ? S * exp(((double)B - (double)Ball) / T) : 0.0;
+        for (int k2 = 0; k2 < K; ++k2)
+            if (xfirst[k2] && xcol[k2] != xcol[k])
+                s += exp(((double)xz[k2] - (double)Ball) / T);
+        const double u = s > 0.0 ? log(s) + ((double)Ball - (double)xz[k]) / T : -INFINITY;
+        out[k] = (float)(-softplus64(u));
+    }
+}
+
+template <int DT, int BLOCK, int U>
+hipError_t launch_sls_t(const SweepArgs &a, bool want_h, bool want_arg, hipStream_t s)
+{
+    dim3 grid((unsigned)a.rows), block(BLOCK);
+    if (want_h && want_arg)
+        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, true, true>), grid, block, 0, s, a);
+    else if (want_h)
+        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, true, false>), grid, block, 0, s, a);
+    else if (want_arg)
+        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, false, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, false, false>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+// Workgroup size for a row: enough 16-byte vectors that every wave gets at
+// least two full steps, up to 256 threads (4 waves) per row.
+template <int DT> int pick_block(int64_t vocab, int U)
+{
+    const int64_t nvec = vocab / Elem<DT>::kVE;
+    const int64_t steps = nvec / ((int64_t)kWave * U);
+    if (steps >= 8)
+        return 256;
+    if (steps >= 4)
+        return 128;
+    return 64;
+}
+
+} // namespace
+
+hipError_t launch_sls_sweep(int dtype, const SweepArgs &a, bool want_h, bool want_arg,
+                            hipStream_t s)
+{
+    if (dtype == CEV_BF16) {
+        switch (pick_block<CEV_BF16>(a.vocab, 4)) {
+        case 256: return launch_sls_t<CEV_BF16, 256, 4>(a, want_h, want_arg, s);
+        case 128: return launch_sls_t<CEV_BF16, 128, 4>(a, want_h, want_arg, s);
+        default: return launch_sls_t<CEV_BF16, 64, 4>(a, want_h, want_arg, s);
+        }
+    }
+    switch (pick_block<CEV_F32>(a.vocab, 4)) {
+    case 256: return launch_sls_t<CEV_F32, 256, 4>(a, want_h, want_arg, s);
+    case 128: return launch_sls_t<CEV_F32, 128, 4>(a, want_h, want_arg, s);
+    default: return launch_sls_t<CEV_F32, 64, 4>(a, want_h, want_arg, s);
+    }
+}
+
+hipError_t launch_topk_sweep(int dtype, const SweepArgs &a, hipStream_t s)
+{
+    dim3 grid((unsigned)a.rows), block(256);
+    if (dtype == CEV_BF16)
+        hipLaunchKernelGGL((k_topk_sweep<CEV_BF16, 256, 4>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((k_topk_sweep<CEV_F32, 256, 4>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+} // namespace cev

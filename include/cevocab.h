@@ -1,0 +1,201 @@
+/*
+ * cevocab.h -- collapse-safe selective log-softmax and cross-entropy over a
+ * [rows, vocab] logit matrix, forward and analytic backward, for AMD Instinct
+ * MI355X (gfx950).  C ABI of libcevocab.so.
+ *
+ * Pages cited below:
+ *   [swift-10337]  ms-swift PR #10337, "perf(rlhf): chunk selective_log_softmax
+ *                  instead of looping per token"
+ *   [swift-10353]  ms-swift PR #10353, custom SFT loss (sparse supervision and
+ *                  the analytic chunked backward)
+ *   [liger-1555]   Liger-Kernel PR #1555, "Fix softmax collapse in CE, GRPO,
+ *                  KL/JSD and softmax", with the unsloth-zoo commit #2080 that
+ *                  the page quotes ([unsloth-2080])
+ *
+ * Notation, per row r: z_j the stored logit, T > 0 the temperature,
+ * x_j = z_j / T, t = labels[r].  A row is VALID when row_mask is NULL or
+ * row_mask[r] != 0, t != ignore_index, and 0 <= t < vocab.  A label outside
+ * [0, vocab) that is not ignore_index makes the row ignored and ORs
+ * CEV_STATUS_BAD_LABEL into *status.
+ *
+ * Conventions shared by every entry point
+ *   Memory    Every array argument is a device pointer owned by the caller.
+ *             The library never allocates, frees, keeps a pointer, or
+ *             synchronizes.  All work is enqueued on `stream` (NULL = the
+ *             default stream) and is asynchronous: buffers must stay alive
+ *             until the stream reaches that point.
+ *   Layout    logits is row-major with `row_stride` ELEMENTS between row
+ *             starts (row_stride >= vocab) and unit column stride.  The base
+ *             pointer must be aligned to the element size.  Rows whose start
+ *             is 16-byte aligned take the vector path; others a peeled head.
+ *   Dtypes    CEV_F32 (IEEE binary32) or CEV_BF16 (upper half of binary32),
+ *             widened to fp32 exactly.  Accumulation is fp32; every per-row
+ *             closing step (log, softplus, sigmoid, entropy) is fp64.
+ *   Errors    The return value is CEV_OK or a negative CEV_E* code.  Argument
+ *             errors are detected on the host BEFORE anything is enqueued and
+ *             have no side effects.  rows == 0 is a successful no-op.  A failed
+ *             kernel launch returns CEV_ELAUNCH.  Data errors inside arrays
+ *             (a bad label or index) do not fail the call: the affected rows
+ *             or entries are treated as ignored and a CEV_STATUS_* bit is ORed
+ *             into *status, if status is non-NULL; the caller reads it after
+ *             its own synchronization.  *status is never cleared by the library.
+ *   Outputs   Ignored rows get log p = loss = entropy = 0 and argmax = -1
+ *             ([swift-10353], PR information: ignored labels get zero upstream
+ *             weight and losses are scattered back to the per-token shape).
+ *             Every log p written is <= 0 ([unsloth-2080], Summary: the log-prob
+ *             must never come out positive).
+ *   Determinism  Fixed reduction order, no floating-point atomics: repeated
+ *             calls with the same arguments give bit-identical results.  The
+ *             functions hold no state and may be called concurrently on
+ *             different streams with disjoint outputs.
+ */
+#ifndef CEVOCAB_H
+#define CEVOCAB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t *cev_stream_t; /* the same handle as hipStream_t */
+
+enum cev_dtype { CEV_F32 = 0, CEV_BF16 = 1 };
+
+enum cev_error {
+    CEV_OK = 0,
+    CEV_ENULL = -1,        /* a required pointer is NULL */
+    CEV_ESHAPE = -2,       /* rows < 0, vocab < 1, K < 1, or a size overflows */
+    CEV_ESTRIDE = -3,      /* a row stride smaller than the row */
+    CEV_EALIGN = -4,       /* a pointer not aligned to its element size */
+    CEV_EDTYPE = -5,       /* unknown dtype */
+    CEV_ETEMP = -6,        /* temperature not finite or not > 0 */
+    CEV_EWORKSPACE = -7,   /* workspace too small */
+    CEV_EALIAS = -8,       /* dlogits overlaps logits */
+    CEV_ELAUNCH = -9       /* the HIP runtime refused a launch */
+};
+
+/* Bits ORed into the optional device status word. */
+#define CEV_STATUS_BAD_LABEL 1u /* a label outside [0, vocab) and != ignore_index */
+#define CEV_STATUS_BAD_INDEX 2u /* a gathered index outside [0, vocab) and != ignore_index */
+
+/* Per-row record written by ce_forward and read by ce_backward: 16 bytes,
+ * 16-byte aligned.  m_z is the exact largest stored logit of the row,
+ * log2_d = log2 sum_j exp((z_j - m_z)/T), q = 1 - p_t computed as sigmoid(u)
+ * (never by subtraction), flags bit 0 = row valid.  ([liger-1555], Summary,
+ * GRPO bullet: the forward keeps an accurate log p rather than only lse, and
+ * the backward rebuilds the normaliser from it.) */
+typedef struct cev_saved {
+    float m_z;
+    float log2_d;
+    float q;
+    int32_t flags;
+} cev_saved;
+
+/*
+ * sls_forward -- selective log-softmax at the label ([swift-10337], PR
+ * information: gather(log_softmax(logits / T), labels) with temperature and
+ * row_mask), in the collapse-safe form of [liger-1555] (Summary, CE bullet):
+ *   u = log sum_{j != t} e^{x_j - m_o} + m_o - x_t,  m_o = max_{j != t} x_j,
+ *   logp[r] = -softplus(u)   (never positive; exact 0 only when V = 1).
+ *
+ *   logits        [rows, row_stride] fp32 or bf16 (dtype), read only
+ *   labels        [rows] int64
+ *   ignore_index  label value meaning "ignored" (conventionally -100)
+ *   temperature   T > 0, finite; x = z / T
+ *   row_mask      [rows] uint8 or NULL; 0 = row ignored
+ *   logp          [rows] fp32 out, required
+ *   entropy       [rows] fp32 out or NULL: H = -sum_j p_j log p_j, summed as
+ *                 non-negative terms ([unsloth-2080], Summary: entropy takes
+ *                 log s from the target-excluded term)
+ *   argmax        [rows] int64 out or NULL: lowest j with z_j = max_k z_k,
+ *                 compared on the stored values; -1 for ignored rows
+ *   status        device int32 or NULL (see Errors)
+ */
+int sls_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride, int dtype,
+                const int64_t *labels, int64_t ignore_index, double temperature,
+                const uint8_t *row_mask, float *logp, float *entropy, int64_t *argmax,
+                int32_t *status, cev_stream_t stream);
+
+/*
+ * sls_topk_forward -- selective log-softmax at K gathered indices per row
+ * ([swift-10337], PR information: top-K indices are supported), each in the
+ * collapse-safe form logp[r,k] = -softplus(log sum_{j != i_k} e^{x_j - M}
+ * + M - x_{i_k}), where the sum over the columns outside the gathered set comes
+ * from one sweep and the other gathered columns are added to it (nothing is
+ * subtracted, so a peaked gathered column keeps its tiny complement).
+ *
+ *   indices       [rows, K] int64 with row stride index_row_stride (>= K)
+ *   logp          [rows, K] fp32 out, dense.  An index equal to ignore_index
+ *                 gives 0; an index outside [0, vocab) gives 0 and sets
+ *                 CEV_STATUS_BAD_INDEX; a masked row gives K zeros.
+ *   Other arguments as sls_forward.
+ */
+int sls_topk_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride,
+                     int dtype, const int64_t *indices, int64_t K, int64_t index_row_stride,
+                     int64_t ignore_index, double temperature, const uint8_t *row_mask,
+                     float *logp, int32_t *status, cev_stream_t stream);
+
+/*
+ * ce_forward -- per-row cross-entropy forward with sparse-supervision
+ * compaction ([swift-10353], PR information: supervised rows are selected
+ * before the cross-entropy, losses scattered back to the per-token shape).
+ * On the device it (1) compacts the valid rows into an ascending list and a
+ * count, and writes the zero outputs of every ignored row, then (2) sweeps
+ * only the listed rows.  No host synchronization happens in between.
+ *
+ *   loss          [rows] fp32 out, required: softplus(u) = -log p_t, 0 at holes
+ *   saved         [rows] cev_saved out, required, 16-byte aligned: the record
+ *                 ce_backward needs
+ *   logp, entropy, argmax   as sls_forward, each optional (NULL)
+ *   valid_rows    [rows] int64 out or NULL: the first *n_valid entries are the
+ *                 valid rows in ascending order; the rest are left untouched
+ *   n_valid       device int64 out or NULL: the number of valid rows
+ *   workspace     device scratch of at least cev_workspace_size(rows) bytes,
+ *                 8-byte aligned; may be NULL (with workspace_bytes 0) when both
+ *                 valid_rows and n_valid are given
+ */
+int ce_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride, int dtype,
+               const int64_t *labels, int64_t ignore_index, double temperature,
+               const uint8_t *row_mask, float *loss, void *saved, float *logp, float *entropy,
+               int64_t *argmax, int64_t *valid_rows, int64_t *n_valid, void *workspace,
+               size_t workspace_bytes, int32_t *status, cev_stream_t stream);
+
+/*
+ * ce_backward -- analytic gradient of the per-row loss with respect to the
+ * stored logits, one pass over each valid row ([swift-10353], PR information:
+ * g * softmax(logits) - g * one_hot(labels), ignored labels get zero weight,
+ * written into a separate gradient buffer), with the 1/T of x = z/T applied,
+ * and the target column taken as -(g/T) q, q = s_others / d = 1 - p_t
+ * ([liger-1555], Summary: dx_y = -sum_others / d), so each row sums to zero:
+ *   dlogits[r, j] = (g[r]/T) p_j  (j != t),   dlogits[r, t] = -(g[r]/T) q_r.
+ * Ignored rows get an all-zero row.  The output dtype is the logits dtype;
+ * bf16 is rounded to nearest even from fp32.
+ *
+ *   g             [rows] fp32: upstream gradient of loss[r] (for a caller that
+ *                 differentiates log p instead, pass g = -dL/dlogp)
+ *   saved         [rows] cev_saved from ce_forward with identical arguments
+ *   dlogits       [rows, dlogits_row_stride] out, same dtype as logits; must
+ *                 not overlap logits (CEV_EALIAS); columns >= vocab untouched
+ */
+int ce_backward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride, int dtype,
+                const int64_t *labels, int64_t ignore_index, double temperature,
+                const uint8_t *row_mask, const float *g, const void *saved, void *dlogits,
+                int64_t dlogits_row_stride, int32_t *status, cev_stream_t stream);
+
+/* Bytes of workspace ce_forward needs when valid_rows or n_valid is NULL. */
+size_t cev_workspace_size(int64_t rows);
+
+/* Static text for a CEV_* return code. */
+const char *cev_status_string(int code);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int cev_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CEVOCAB_H */

@@ -1,0 +1,173 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function that
+include/cevocab.h declares, and rejects bad arguments on the host before any
+launch (these calls never reach the GPU, so they run without one)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import cross_entropy_vocab_amd as cev
+from cross_entropy_vocab_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cevocab.h")
+
+E = dict(OK=0, NULL=-1, SHAPE=-2, STRIDE=-3, ALIGN=-4, DTYPE=-5, TEMP=-6, WORKSPACE=-7,
+         ALIAS=-8, LAUNCH=-9)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from cross_entropy_vocab_amd import build
+        build.build()
+    return _lib.get()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^(?:int|size_t|const char \*)\s*(\w+)\(", text, flags=re.M)
+
+
+def test_header_declares_the_boundary():
+    names = set(declared_functions())
+    assert {"sls_forward", "sls_topk_forward", "ce_forward", "ce_backward",
+            "cev_workspace_size", "cev_status_string", "cev_version"} <= names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, name
+
+
+def test_codes_match_header():
+    text = open(HEADER).read()
+    for key, val in E.items():
+        if key == "OK":
+            continue
+        m = re.search(r"CEV_E%s\s*=\s*(-?\d+)" % key, text)
+        assert m and int(m.group(1)) == val, key
+    assert re.search(r"CEV_STATUS_BAD_LABEL\s+1u", text)
+    assert cev.STATUS_BAD_LABEL == 1 and cev.STATUS_BAD_INDEX == 2
+
+
+def test_version_and_strings(lib):
+    assert lib.cev_version() == 100
+    for code in E.values():
+        assert lib.cev_status_string(code)
+    assert lib.cev_workspace_size(10) == 88
+    assert lib.cev_workspace_size(-1) == 0
+
+
+# fake, never-dereferenced device addresses (validation fails before any launch)
+A = 0x10000
+B = 0x900000
+
+
+def sls(lib, **kw):
+    a = dict(logits=A, rows=4, vocab=100, stride=100, dtype=0, labels=A, ig=-100, T=1.0,
+             mask=None, logp=A, ent=None, arg=None, status=None, stream=None)
+    a.update(kw)
+    return lib.sls_forward(a["logits"], a["rows"], a["vocab"], a["stride"], a["dtype"],
+                           a["labels"], a["ig"], a["T"], a["mask"], a["logp"], a["ent"], a["arg"],
+                           a["status"], a["stream"])
+
+
+def test_sls_forward_validation(lib):
+    assert sls(lib, dtype=7) == E["DTYPE"]
+    assert sls(lib, T=0.0) == E["TEMP"]
+    assert sls(lib, T=-1.0) == E["TEMP"]
+    assert sls(lib, T=float("nan")) == E["TEMP"]
+    assert sls(lib, T=float("inf")) == E["TEMP"]
+    assert sls(lib, T=1e-40) == E["TEMP"]
+    assert sls(lib, rows=-1) == E["SHAPE"]
+    assert sls(lib, vocab=0) == E["SHAPE"]
+    assert sls(lib, rows=2 ** 31) == E["SHAPE"]
+    assert sls(lib, stride=99) == E["STRIDE"]
+    assert sls(lib, logits=None) == E["NULL"]
+    assert sls(lib, labels=None) == E["NULL"]
+    assert sls(lib, logp=None) == E["NULL"]
+    assert sls(lib, logits=A + 1) == E["ALIGN"]
+    assert sls(lib, logits=A + 1, dtype=1) == E["ALIGN"]
+    assert sls(lib, labels=A + 4) == E["ALIGN"]
+    assert sls(lib, logp=A + 2) == E["ALIGN"]
+    assert sls(lib, arg=A + 4) == E["ALIGN"]
+    assert sls(lib, status=A + 2) == E["ALIGN"]
+    # rows == 0 is a no-op that succeeds without touching any pointer
+    assert sls(lib, rows=0, logits=None, labels=None, logp=None) == E["OK"]
+
+
+def test_topk_validation(lib):
+    def call(**kw):
+        a = dict(logits=A, rows=4, vocab=100, stride=100, dtype=1, idx=A, K=8, istride=8,
+                 ig=-100, T=0.7, mask=None, logp=A, status=None)
+        a.update(kw)
+        return lib.sls_topk_forward(a["logits"], a["rows"], a["vocab"], a["stride"], a["dtype"],
+                                    a["idx"], a["K"], a["istride"], a["ig"], a["T"], a["mask"],
+                                    a["logp"], a["status"], None)
+    assert call(K=0) == E["SHAPE"]
+    assert call(K=1025) == E["SHAPE"]
+    assert call(istride=7) == E["STRIDE"]
+    assert call(idx=None) == E["NULL"]
+    assert call(idx=A + 4) == E["ALIGN"]
+    assert call(T=0.0) == E["TEMP"]
+    assert call(rows=0) == E["OK"]
+
+
+def test_ce_forward_validation(lib):
+    def call(**kw):
+        a = dict(logits=A, rows=4, vocab=100, stride=100, dtype=0, labels=A, ig=-100, T=1.0,
+                 mask=None, loss=A, saved=A, logp=None, ent=None, arg=None, vr=None, nv=None,
+                 ws=None, wsb=0, status=None)
+        a.update(kw)
+        return lib.ce_forward(a["logits"], a["rows"], a["vocab"], a["stride"], a["dtype"],
+                              a["labels"], a["ig"], a["T"], a["mask"], a["loss"], a["saved"],
+                              a["logp"], a["ent"], a["arg"], a["vr"], a["nv"], a["ws"], a["wsb"],
+                              a["status"], None)
+    assert call() == E["NULL"]                       # no list/count and no workspace
+    assert call(ws=A, wsb=39) == E["WORKSPACE"]      # needs (4 + 1) * 8 = 40 bytes
+    assert call(ws=A + 4, wsb=40) == E["ALIGN"]
+    assert call(vr=A, nv=A, saved=A + 8) == E["ALIGN"]  # saved records are 16-byte aligned
+    assert call(vr=A, nv=A, loss=None) == E["NULL"]
+    assert call(vr=A, nv=A, saved=None) == E["NULL"]
+    assert call(vr=A, nv=A, dtype=3) == E["DTYPE"]
+    assert call(rows=0) == E["OK"]
+
+
+def test_ce_backward_validation(lib):
+    def call(**kw):
+        a = dict(logits=A, rows=4, vocab=100, stride=100, dtype=1, labels=A, ig=-100, T=1.0,
+                 mask=None, g=A, saved=A, dl=B, dstride=100, status=None)
+        a.update(kw)
+        return lib.ce_backward(a["logits"], a["rows"], a["vocab"], a["stride"], a["dtype"],
+                               a["labels"], a["ig"], a["T"], a["mask"], a["g"], a["saved"],
+                               a["dl"], a["dstride"], a["status"], None)
+    assert call(dl=A) == E["ALIAS"]
+    assert call(dl=A + 2 * 350) == E["ALIAS"]                 # overlaps the last row
+    assert call(dstride=50) == E["STRIDE"]
+    assert call(g=None) == E["NULL"]
+    assert call(saved=None) == E["NULL"]
+    assert call(dl=None) == E["NULL"]
+    assert call(saved=A + 8) == E["ALIGN"]
+    assert call(dl=B + 1) == E["ALIGN"]
+    assert call(T=float("nan")) == E["TEMP"]
+    assert call(rows=0) == E["OK"]
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(_lib.LibraryMissing):
+        cev.version()
+
+
+def test_product_never_imports_the_oracle():
+    """The package and its sources do not reference the oracle."""
+    pkg = os.path.join(ROOT, "cross_entropy_vocab_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "oracle_" not in text, f

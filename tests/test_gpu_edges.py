@@ -1,0 +1,252 @@
+"""Edge cases of the HIP path against the oracle: tiny and odd vocabularies,
+misaligned and padded rows, empty inputs, all-ignored and bad labels, argmax
+ties, top-K duplicates and ignored entries, determinism, guard bands."""
+import numpy as np
+import pytest
+import torch
+
+import cross_entropy_vocab_amd as cev
+import oracle
+import workloads
+from tolerance import RTOL, assert_close, assert_nonpositive, assert_row_sums
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand_case(rows, V, dtype="f32", T=1.0, seed=0, scale=3.0, n_ignored=0, mask_frac=0.0):
+    rng = np.random.default_rng(seed)
+    z = (rng.standard_normal((rows, V)) * scale).astype(np.float32)
+    logits = workloads.bf16_bits(z) if dtype == "bf16" else z
+    labels = rng.integers(0, V, rows).astype(np.int64)
+    if n_ignored:
+        labels[rng.permutation(rows)[:n_ignored]] = -100
+    mask = None
+    if mask_frac:
+        mask = (rng.random(rows) >= mask_frac).astype(np.uint8)
+    g = rng.standard_normal(rows).astype(np.float32)
+    return dict(logits=logits, labels=labels, row_mask=mask, temperature=T, g=g)
+
+
+def _check_against_oracle(w, got, name):
+    kind = "bf16" if w["logits"].dtype == np.uint16 else "f32"
+    tol = RTOL[kind]
+    V = w["logits"].shape[1]
+    ref = oracle.ce_rows(w["logits"], w["labels"], w["temperature"], row_mask=w.get("row_mask"))
+    dref = oracle.ce_grad_rows(w["logits"], w["labels"], np.asarray(w["g"], np.float64),
+                               w["temperature"], row_mask=w.get("row_mask"))
+    vr, _ = oracle.valid_rows(w["labels"], w.get("row_mask"), V)
+    n = int(got["n_valid"][0])
+    assert n == vr.shape[0] and np.array_equal(got["valid_rows"][:n], vr), name
+    assert_close(f"{name} logp", got["logp"], ref["logp"], tol["logp"])
+    assert_close(f"{name} loss", got["loss"], ref["loss"], tol["loss"])
+    assert_close(f"{name} entropy", got["entropy"], ref["entropy"], tol["entropy"], 1e-30)
+    assert np.array_equal(got["argmax"], ref["argmax"]), name
+    valid = np.zeros(w["logits"].shape[0], dtype=bool)
+    valid[vr] = True
+    assert_nonpositive(name, got["logp"], valid)
+    assert_close(f"{name} dlogits", got["dlogits"], dref, tol["dlogits"], 2.0 ** -126)
+    assert_row_sums(f"{name} dlogits", got["dlogits"], tol["dlogits"])
+
+
+@pytest.mark.parametrize("V", [1, 2, 3, 5, 7, 8, 9, 15, 16, 17, 31, 33, 63, 64, 65, 127, 511,
+                               512, 513, 1023, 2049, 4097])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_small_and_odd_vocab(V, dtype):
+    from gpu_helpers import run_ce
+    w = _rand_case(9, V, dtype, T=0.8, seed=V, n_ignored=2)
+    got = run_ce(w)
+    _check_against_oracle(w, got, f"V={V} {dtype}")
+    if V == 1:
+        valid = w["labels"] != -100
+        assert np.all(got["logp"][valid] == 0) and np.all(np.signbit(got["logp"][valid]))
+        assert np.all(got["dlogits"] == 0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V,stride", [(1000, 1003), (4093, 4100), (32768, 32775), (777, 777)])
+def test_padded_and_misaligned_rows(dtype, V, stride):
+    """Row starts at every alignment modulo 16 bytes; padding holds NaN
+    canaries that must not leak into any output."""
+    from gpu_helpers import DEV, run_ce, strided_dev
+    w = _rand_case(11, V, dtype, seed=stride, n_ignored=1)
+    dev = strided_dev(w["logits"], stride)
+    got = run_ce(w, logits_dev=dev)
+    _check_against_oracle(w, got, f"V={V} stride={stride} {dtype}")
+
+
+def test_dlogits_padded_stride_untouched():
+    from gpu_helpers import DEV, to_dev
+    w = _rand_case(6, 300, "bf16", seed=3)
+    logits = to_dev(w["logits"])
+    labels = to_dev(w["labels"])
+    g = to_dev(w["g"])
+    out = cev.ce_forward(logits, labels, 1.0)
+    big = torch.full((6, 307), 12345, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    dl = big[:, :300]
+    cev.ce_backward(logits, labels, g, out["saved"], 1.0, dlogits=dl)
+    ref = cev.ce_backward(logits, labels, g, out["saved"], 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(dl.view(torch.int16), ref.view(torch.int16))
+    assert torch.all(big.view(torch.int16)[:, 300:] == 12345)
+
+
+def test_empty_rows():
+    from gpu_helpers import DEV
+    logits = torch.empty((0, 100), dtype=torch.float32, device=DEV)
+    labels = torch.empty(0, dtype=torch.int64, device=DEV)
+    out = cev.ce_forward(logits, labels, 1.0)
+    assert out["loss"].shape == (0,)
+    dl = cev.ce_backward(logits, labels, torch.empty(0, device=DEV), out["saved"], 1.0)
+    assert dl.shape == (0, 100)
+    assert cev.sls_forward(logits, labels)["logp"].shape == (0,)
+    idx = torch.empty((0, 4), dtype=torch.int64, device=DEV)
+    assert cev.sls_topk_forward(logits, idx).shape == (0, 4)
+
+
+def test_all_rows_ignored():
+    from gpu_helpers import run_ce
+    w = _rand_case(20, 5000, "bf16", seed=5, n_ignored=20)
+    got = run_ce(w)
+    assert int(got["n_valid"][0]) == 0
+    assert np.all(got["loss"] == 0) and np.all(got["logp"] == 0)
+    assert np.all(got["argmax"] == -1) and np.all(got["dlogits"] == 0)
+
+
+def test_all_rows_masked_and_mixed_mask():
+    from gpu_helpers import run_ce
+    w = _rand_case(40, 3000, "f32", seed=6, mask_frac=0.5, n_ignored=5)
+    got = run_ce(w)
+    _check_against_oracle(w, got, "mixed mask")
+    w["row_mask"][:] = 0
+    got = run_ce(w)
+    assert int(got["n_valid"][0]) == 0 and np.all(got["dlogits"] == 0)
+
+
+def test_bad_labels_set_status_and_are_ignored():
+    from gpu_helpers import run_ce, run_sls
+    w = _rand_case(12, 700, "f32", seed=7)
+    w["labels"][3] = 700
+    w["labels"][8] = -5
+    got = run_ce(w)
+    assert got["status"] & cev.STATUS_BAD_LABEL
+    _check_against_oracle(w, got, "bad labels")
+    assert got["argmax"][3] == -1 and got["logp"][8] == 0
+    s = run_sls(w)
+    assert s["status"] & cev.STATUS_BAD_LABEL
+
+
+def test_argmax_ties_lowest_index():
+    """Ties of the row maximum, on and off the target, resolve to the lowest
+    column, compared on the stored values."""
+    from gpu_helpers import run_ce
+    rng = np.random.default_rng(8)
+    rows, V = 16, 40000
+    z = (rng.standard_normal((rows, V)) * 0.3).astype(np.float32)
+    labels = rng.integers(0, V, rows).astype(np.int64)
+    for r in range(rows):
+        cols = np.sort(rng.choice(V, 3, replace=False))
+        z[r, cols] = 7.0
+        if r % 4 == 0:
+            labels[r] = cols[1]          # target ties a lower column
+        elif r % 4 == 1:
+            labels[r] = cols[0]          # target is the lowest tied column
+        elif r % 4 == 2:
+            z[r, labels[r]] = 7.0        # target joins the tie
+    for dtype in ("f32", "bf16"):
+        logits = workloads.bf16_bits(z) if dtype == "bf16" else z.copy()
+        w = dict(logits=logits, labels=labels, row_mask=None, temperature=0.9,
+                 g=np.ones(rows, np.float32))
+        got = run_ce(w)
+        stored = workloads.stored_values(logits)
+        assert np.array_equal(got["argmax"], np.argmax(stored, axis=1)), dtype
+        _check_against_oracle(w, got, f"ties {dtype}")
+
+
+def test_deterministic_bits():
+    from gpu_helpers import run_ce
+    w = workloads.grpo(rows=24, vocab=152064)
+    a = run_ce(w)
+    b = run_ce(w)
+    for k in ("logp", "loss", "entropy", "argmax", "saved", "dlogits"):
+        assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8)), k
+
+
+def test_output_guard_bands():
+    """Outputs written into the middle of larger buffers touch nothing else."""
+    from gpu_helpers import DEV, to_dev
+    w = _rand_case(10, 2000, "bf16", seed=9, n_ignored=3)
+    logits = to_dev(w["logits"])
+    labels = to_dev(w["labels"])
+    pad = 64
+    buf = {
+        "loss": torch.full((10 + 2 * pad,), 77.0, device=DEV),
+        "logp": torch.full((10 + 2 * pad,), 77.0, device=DEV),
+        "entropy": torch.full((10 + 2 * pad,), 77.0, device=DEV),
+        "argmax": torch.full((10 + 2 * pad,), 77, dtype=torch.int64, device=DEV),
+        "valid_rows": torch.full((10 + 2 * pad,), 77, dtype=torch.int64, device=DEV),
+    }
+    saved = torch.full((10 + 2 * pad, 16), 77, dtype=torch.uint8, device=DEV)
+    nv = torch.full((1 + 2 * pad,), 77, dtype=torch.int64, device=DEV)
+    out = {k: v[pad:pad + 10] for k, v in buf.items()}
+    out["saved"] = saved[pad:pad + 10]
+    out["n_valid"] = nv[pad:pad + 1]
+    cev.ce_forward(logits, labels, 1.0, entropy=True, argmax=True, out=out)
+    torch.cuda.synchronize()
+    for k, v in buf.items():
+        assert torch.all(v[:pad] == 77) and torch.all(v[pad + 10:] == 77), k
+    assert torch.all(saved[:pad] == 77) and torch.all(saved[pad + 10:] == 77)
+    assert torch.all(nv[:pad] == 77) and torch.all(nv[pad + 1:] == 77)
+    n = int(out["n_valid"].item())
+    vrows = out["valid_rows"][:n].cpu().numpy()
+    assert np.array_equal(vrows, np.flatnonzero(w["labels"] != -100))
+
+
+def test_topk_duplicates_ignored_and_bad_indices():
+    from gpu_helpers import run_topk
+    w = _rand_case(10, 5000, "bf16", T=0.7, seed=10, mask_frac=0.2)
+    rng = np.random.default_rng(11)
+    idx = rng.integers(0, 5000, (10, 12)).astype(np.int64)
+    idx[:, 3] = idx[:, 1]          # duplicate column
+    idx[2, 5] = -100               # ignored entry
+    idx[4, 0] = 5000               # out of range
+    idx[6, 7] = -3                 # out of range
+    got, st = run_topk(w, idx)
+    want, wst = oracle.topk_rows(w["logits"], idx, 0.7, row_mask=w["row_mask"])
+    assert st & cev.STATUS_BAD_INDEX or w["row_mask"][4] == 0 and w["row_mask"][6] == 0
+    assert_close("topk dup", got, want, RTOL["bf16"]["topk"])
+    assert_nonpositive("topk dup", got)
+
+
+def test_topk_large_k_and_peaked():
+    """K = 100 gathered columns on peaked rows: the peak's own log p keeps its
+    tiny complement (never 0, never positive)."""
+    from gpu_helpers import run_topk
+    w = workloads.peaked("f32", 0.9, rows=12, vocab=20000)
+    rng = np.random.default_rng(12)
+    idx = np.stack([rng.choice(20000, 100, replace=False) for _ in range(12)]).astype(np.int64)
+    idx[:, 50] = w["labels"]
+    idx[idx[:, 49] == w["labels"], 49] = (w["labels"][idx[:, 49] == w["labels"]] + 1) % 20000
+    got, st = run_topk(w, idx)
+    want, _ = oracle.topk_rows(w["logits"], idx, 0.9)
+    assert_close("topk K=100", got, want, RTOL["f32"]["topk"])
+    assert np.all(got[:, 50] < 0)
+
+
+def test_topk_index_equals_label_matches_sls():
+    from gpu_helpers import run_sls, run_topk
+    w = _rand_case(30, 32768, "bf16", T=0.7, seed=13)
+    idx = np.stack([w["labels"], (w["labels"] + 7) % 32768], axis=1)
+    got, _ = run_topk(w, idx)
+    s = run_sls(w, entropy=False, argmax=False)
+    assert_close("topk vs sls", got[:, 0], s["logp"], 1e-6)
+
+
+def test_temperature_scaling_identity():
+    """T = 0.5 on z equals T = 1 on 2z (both exact), up to fp32 rounding of log2(e)/T."""
+    from gpu_helpers import run_ce
+    w = _rand_case(8, 9000, "f32", T=0.5, seed=14)
+    a = run_ce(w)
+    w2 = dict(w, logits=w["logits"] * np.float32(2.0), temperature=1.0)
+    b = run_ce(w2)
+    assert_close("T scaling logp", a["logp"], b["logp"].astype(np.float64), 2e-6)
+    assert np.array_equal(a["argmax"], b["argmax"])
