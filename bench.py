@@ -1,0 +1,213 @@
+"""Throughput of the collapse-safe cross-entropy hot path on one MI355X.
+
+One step = ce_forward (device compaction + one sweep per valid row; log p,
+loss, argmax and the saved record; entropy off) followed by ce_backward (one
+read of each valid row, one bf16 write of every row) on the 8192 x 152064
+bf16 GRPO-shaped workload: logits 3 N(0,1) + a per-row shift U(-5, 5), labels
+uniform, 819 rows masked out, g ~ N(0,1), T = 1.  Inputs are resident in HBM
+before timing starts.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+
+Prints one JSON line.  The roofline object describes the dominant kernel
+(the backward sweep): algorithmic bytes per launch over its mean duration,
+measured with HIP events on the stream the library launches on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD published
+METRIC = "rows/s and achieved HBM GB/s (% peak), 8192x152064 bf16 fwd+bwd, 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_backward_grpo_8192x152064_bf16.json")
+KERNEL_SOURCES = ["backward.hip", "cev_device.h"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "cross_entropy_vocab_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per backward launch from the committed rocprofv3 counter runs,
+    if they were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, valid_rows, seconds=12.0, threads=None):
+    """The fp64 oracle (as it stands) on a bounded sample of the same rows:
+    forward (log p, loss, argmax) plus the gradient rows, chunk by chunk."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    threads = threads or min(16, oracle.default_threads())
+    rng = np.random.default_rng(123)
+    order = rng.permutation(valid_rows)
+    g64 = w["g"].astype(np.float64)
+
+    def grad_row(r):
+        oracle.ce_grad_rows(w["logits"], w["labels"], g64, w["temperature"],
+                            row_mask=w["row_mask"], r0=int(r), r1=int(r) + 1, threads=1)
+
+    done = 0
+    t0 = time.perf_counter()
+    chunk = 2 * threads
+    with ThreadPoolExecutor(threads) as ex:
+        while time.perf_counter() - t0 < seconds and done < order.shape[0]:
+            rows = np.sort(order[done:done + chunk])
+            oracle.ce_rows(w["logits"], w["labels"], w["temperature"], row_mask=w["row_mask"],
+                           rows_list=rows, threads=threads, want_entropy=False)
+            list(ex.map(grad_row, rows))
+            done += rows.shape[0]
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} random valid rows of the 8192x152064 bf16 workload "
+                      f"(forward with argmax + full gradient row each), {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rows", type=int, default=8192)
+    ap.add_argument("--vocab", type=int, default=152064)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain elementwise kernel over 1 GiB in / 1 GiB out, "
+                         "the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(rows shard across GPUs with no communication; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import cross_entropy_vocab_amd as cev
+    import workloads
+
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {args.rows}x{args.vocab} bf16 workload")
+    w = workloads.grpo(rows=args.rows, vocab=args.vocab)
+    R, V = w["logits"].shape
+    logits = torch.from_numpy(w["logits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    labels = torch.from_numpy(w["labels"]).to(dev)
+    mask = torch.from_numpy(w["row_mask"]).to(dev)
+    g = torch.from_numpy(w["g"]).to(dev)
+    T = w["temperature"]
+    n_valid = int(((w["labels"] != -100) & (w["row_mask"] != 0)).sum())
+    out = cev.ce_forward(logits, labels, T, row_mask=mask, logp=True, argmax=True)
+    dl = torch.empty((R, V), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        cev.ce_forward(logits, labels, T, row_mask=mask, logp=True, argmax=True, out=out)
+        cev.ce_backward(logits, labels, g, out["saved"], T, row_mask=mask, dlogits=dl)
+    torch.cuda.synchronize()
+    assert int(out["n_valid"].item()) == n_valid
+
+    # K back-to-back steps: wall clock around all of them, and HIP events
+    # recorded on the library's stream (torch's current stream) between the
+    # calls.  The host runs ahead of the GPU, so each event pair brackets the
+    # GPU time of one call (its kernels plus the short dispatch gap).
+    log(f"[bench] timing {args.steps} steps")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record()
+        cev.ce_forward(logits, labels, T, row_mask=mask, logp=True, argmax=True, out=out)
+        e1.record()
+        cev.ce_backward(logits, labels, g, out["saved"], T, row_mask=mask, dlogits=dl)
+        e2.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+    fwd_ms = [e0.elapsed_time(e1) for e0, e1, _ in ev]
+    bwd_ms = [e1.elapsed_time(e2) for _, e1, e2 in ev]
+    fwd = float(np.mean(fwd_ms))
+    bwd = float(np.mean(bwd_ms))
+
+    ES = 2
+    fwd_bytes = n_valid * V * ES                    # valid rows read once
+    bwd_bytes = n_valid * V * ES + R * V * ES       # valid rows re-read, every row written
+    step_bytes = fwd_bytes + bwd_bytes
+    rows_per_s = R / (ms_step / 1e3)
+    achieved = bwd_bytes / (bwd / 1e3) / 1e9
+    traffic = measured_traffic()
+    res = {
+        "metric": METRIC,
+        "value": rows_per_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"grpo-shaped {R}x{V} bf16 logits, {R - n_valid} rows masked, "
+                               "ce_forward (argmax, no entropy) + ce_backward, T=1",
+                   "rows": R, "vocab": V, "valid_rows": n_valid},
+        "hbm_GBps": step_bytes / (ms_step / 1e3) / 1e9,
+        "hbm_frac_of_peak": step_bytes / (ms_step / 1e3) / 1e9 / PEAK_HBM_GBS,
+        "step_algorithmic_bytes": step_bytes,
+        "kernels_ms": {"ce_forward": fwd, "ce_backward": bwd,
+                       "ce_backward_min": float(np.min(bwd_ms)),
+                       "ce_backward_max": float(np.max(bwd_ms)),
+                       "ce_forward_GBps": fwd_bytes / (fwd / 1e3) / 1e9,
+                       "ce_backward_GBps": achieved},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "k_backward (ce_backward)", "bytes_per_launch": bwd_bytes},
+        "cpu_baseline": None,
+    }
+    log(f"[bench] {ms_step:.3f} ms/step, fwd {fwd:.3f} ms, bwd {bwd:.3f} ms")
+    if args.copy_calibration:
+        # torch's elementwise add: reads exactly 2^30 bytes, writes exactly 2^30 bytes
+        src = torch.ones(2 ** 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.add(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        res["copy_calibration"] = {"kernel": "torch elementwise add (float32)",
+                                   "read_bytes": 2 ** 30, "write_bytes": 2 ** 30}
+        del src, dst
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
+        vr = np.flatnonzero((w["labels"] != -100) & (w["row_mask"] != 0))
+        res["cpu_baseline"] = cpu_baseline(w, vr, seconds=args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

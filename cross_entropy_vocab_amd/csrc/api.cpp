@@ -15,7 +15,7 @@ using cev::BackwardArgs;
 using cev::CompactArgs;
 using cev::SweepArgs;
 
-constexpr int64_t kMaxRows = INT32_MAX;       // one workgroup per row in the grid
+constexpr int64_t kMaxRows = 1 << 22;         // one workgroup per row; the grid stays < 2^32 work-items
 constexpr int64_t kMaxVocab = INT32_MAX / 2;  // step codes are 32-bit
 constexpr int64_t kMaxK = 1024;               // gathered indices per row held in LDS
 
@@ -250,6 +250,7 @@ int ce_backward(const void *logits, int64_t rows, int64_t vocab, int64_t row_str
     a.d_row_stride = dlogits_row_stride;
     a.temperature = temperature;
     a.c = (float)(1.4426950408889634074 / temperature);
+    a.inv_t = (float)(1.0 / temperature);
     a.status = status;
     return launch_status(cev::launch_backward(dtype, a, to_hip(stream)));
 }

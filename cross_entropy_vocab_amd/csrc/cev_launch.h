@@ -67,6 +67,7 @@ struct BackwardArgs {
     int64_t d_row_stride;
     double temperature;
     float c;                   // log2(e) / T
+    float inv_t;               // 1 / T
     int32_t *status;
 };
 
@@ -75,5 +76,14 @@ hipError_t launch_sls_sweep(int dtype, const SweepArgs &a, bool want_entropy, bo
 hipError_t launch_topk_sweep(int dtype, const SweepArgs &a, hipStream_t stream);
 hipError_t launch_compact(const CompactArgs &a, hipStream_t stream);
 hipError_t launch_backward(int dtype, const BackwardArgs &a, hipStream_t stream);
+
+// Explicit launch configurations (workgroup size, 16-byte vectors per thread
+// per step, and for the backward the steps per workgroup, 0 = a whole row,
+// and whether rows are walked from the last to the first).
+// The entry points above pick one of these; tuning harnesses call them directly.
+hipError_t launch_sls_sweep_cfg(int dtype, const SweepArgs &a, bool want_entropy,
+                                bool want_argmax, int block, int U, hipStream_t stream);
+hipError_t launch_backward_cfg(int dtype, const BackwardArgs &a, int block, int U, int iters,
+                               int reverse, hipStream_t stream);
 
 } // namespace cev

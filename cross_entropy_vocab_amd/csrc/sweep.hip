@@ -495,36 +495,49 @@ hipError_t launch_sls_t(const SweepArgs &a, bool want_h, bool want_arg, hipStrea
     return hipGetLastError();
 }
 
-// Workgroup size for a row: enough 16-byte vectors that every wave gets at
-// least two full steps, up to 256 threads (4 waves) per row.
-template <int DT> int pick_block(int64_t vocab, int U)
+// Launch shape for a row of nvec 16-byte vectors: the widest workgroup whose
+// waves each still get at least four full steps.  512 threads x 2 vectors was
+// the fastest shape measured on MI355X for 152064-wide bf16 rows (6.7 TB/s of
+// the ~7.0 TB/s streaming-read ceiling), 256 x 4 next.
+struct Shape {
+    int block, U;
+};
+
+Shape pick_shape(int64_t nvec)
 {
-    const int64_t nvec = vocab / Elem<DT>::kVE;
-    const int64_t steps = nvec / ((int64_t)kWave * U);
-    if (steps >= 8)
-        return 256;
-    if (steps >= 4)
-        return 128;
-    return 64;
+    if (nvec >= 4 * 512 * 2)
+        return {512, 2};
+    if (nvec >= 4 * 256 * 4)
+        return {256, 4};
+    if (nvec >= 4 * 128 * 4)
+        return {128, 4};
+    return {64, 4};
 }
 
 } // namespace
 
+// Launch configuration, exposed for tuning harnesses.
+hipError_t launch_sls_sweep_cfg(int dtype, const SweepArgs &a, bool want_h, bool want_arg,
+                                int block, int U, hipStream_t s)
+{
+#define CEV_SLS_CASE(B, UU)                                                                     \
+    if (block == B && U == UU)                                                                  \
+        return dtype == CEV_BF16 ? launch_sls_t<CEV_BF16, B, UU>(a, want_h, want_arg, s)        \
+                                 : launch_sls_t<CEV_F32, B, UU>(a, want_h, want_arg, s);
+    CEV_SLS_CASE(64, 4)
+    CEV_SLS_CASE(128, 4)
+    CEV_SLS_CASE(256, 4)
+    CEV_SLS_CASE(512, 2)
+    CEV_SLS_CASE(512, 4)
+#undef CEV_SLS_CASE
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_sls_sweep(int dtype, const SweepArgs &a, bool want_h, bool want_arg,
                             hipStream_t s)
 {
-    if (dtype == CEV_BF16) {
-        switch (pick_block<CEV_BF16>(a.vocab, 4)) {
-        case 256: return launch_sls_t<CEV_BF16, 256, 4>(a, want_h, want_arg, s);
-        case 128: return launch_sls_t<CEV_BF16, 128, 4>(a, want_h, want_arg, s);
-        default: return launch_sls_t<CEV_BF16, 64, 4>(a, want_h, want_arg, s);
-        }
-    }
-    switch (pick_block<CEV_F32>(a.vocab, 4)) {
-    case 256: return launch_sls_t<CEV_F32, 256, 4>(a, want_h, want_arg, s);
-    case 128: return launch_sls_t<CEV_F32, 128, 4>(a, want_h, want_arg, s);
-    default: return launch_sls_t<CEV_F32, 64, 4>(a, want_h, want_arg, s);
-    }
+    const Shape sh = pick_shape(a.vocab / (dtype == CEV_BF16 ? 8 : 4));
+    return launch_sls_sweep_cfg(dtype, a, want_h, want_arg, sh.block, sh.U, s);
 }
 
 hipError_t launch_topk_sweep(int dtype, const SweepArgs &a, hipStream_t s)

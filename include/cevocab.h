@@ -67,7 +67,8 @@ enum cev_dtype { CEV_F32 = 0, CEV_BF16 = 1 };
 enum cev_error {
     CEV_OK = 0,
     CEV_ENULL = -1,        /* a required pointer is NULL */
-    CEV_ESHAPE = -2,       /* rows < 0, vocab < 1, K < 1, or a size overflows */
+    CEV_ESHAPE = -2,       /* rows outside [0, 2^22], vocab outside [1, 2^30), K outside
+                              [1, 1024], or a size overflows */
     CEV_ESTRIDE = -3,      /* a row stride smaller than the row */
     CEV_EALIGN = -4,       /* a pointer not aligned to its element size */
     CEV_EDTYPE = -5,       /* unknown dtype */

@@ -85,6 +85,7 @@ def test_sls_forward_validation(lib):
     assert sls(lib, rows=-1) == E["SHAPE"]
     assert sls(lib, vocab=0) == E["SHAPE"]
     assert sls(lib, rows=2 ** 31) == E["SHAPE"]
+    assert sls(lib, rows=2 ** 22 + 1) == E["SHAPE"]
     assert sls(lib, stride=99) == E["STRIDE"]
     assert sls(lib, logits=None) == E["NULL"]
     assert sls(lib, labels=None) == E["NULL"]

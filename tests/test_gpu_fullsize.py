@@ -1,0 +1,147 @@
+"""The full-size workloads in the launch configuration the benchmark times:
+every output on the GPU, the oracle on sampled rows (it computes one row at a
+time), and properties that hold at any size on every row (bit-exact compaction,
+log p <= 0, strictly positive loss on peaked rows, zero dlogits row sums)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tolerance import FLOOR, RTOL, assert_close, assert_nonpositive
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def _sample_rows(rng, valid, n_valid_rows, n_invalid_rows):
+    v = np.flatnonzero(valid)
+    iv = np.flatnonzero(~valid)
+    pick = list(rng.choice(v, min(n_valid_rows, v.size), replace=False))
+    pick += [v[0], v[-1]]
+    if iv.size:
+        pick += list(rng.choice(iv, min(n_invalid_rows, iv.size), replace=False))
+    return np.unique(np.asarray(pick, dtype=np.int64))
+
+
+def _row_sums_ok(dl: torch.Tensor, tol, chunk=256):
+    """|sum_j dl_j| <= tol * sum_j |dl_j| + V 2^-126 on every row (fp64 on the GPU)."""
+    R, V = dl.shape
+    for a in range(0, R, chunk):
+        d = dl[a:a + chunk].double()
+        s = d.sum(1).abs()
+        bound = tol * d.abs().sum(1) + V * FLOOR
+        bad = s > bound
+        assert not bool(bad.any()), f"rows {a + torch.nonzero(bad).flatten()[:5].tolist()}"
+
+
+def _ce_full(w, entropy, tol, sample_valid=24, sample_invalid=4, seed=0):
+    from gpu_helpers import DEV, say, to_dev, to_host
+    import cross_entropy_vocab_amd as cev
+    R, V = w["logits"].shape
+    logits = to_dev(w["logits"])
+    labels = to_dev(w["labels"])
+    mask = None if w.get("row_mask") is None else to_dev(w["row_mask"])
+    g = to_dev(np.asarray(w["g"], np.float32))
+    T = w["temperature"]
+    out = cev.ce_forward(logits, labels, T, row_mask=mask, entropy=entropy, argmax=True)
+    dl = cev.ce_backward(logits, labels, g, out["saved"], T, row_mask=mask)
+    torch.cuda.synchronize()
+    vr, _ = oracle.valid_rows(w["labels"], w.get("row_mask"), V)
+    n = int(out["n_valid"].item())
+    assert n == vr.size and np.array_equal(out["valid_rows"][:n].cpu().numpy(), vr)
+    valid = np.zeros(R, dtype=bool)
+    valid[vr] = True
+    logp = to_host(out["logp"])
+    loss = to_host(out["loss"])
+    assert_nonpositive("logp", logp, valid)
+    assert np.all(loss[valid] >= 0) and np.all(loss[~valid] == 0)
+    _row_sums_ok(dl, tol["dlogits"])
+    rng = np.random.default_rng(seed)
+    rows = _sample_rows(rng, valid, sample_valid, sample_invalid)
+    ref = oracle.ce_rows(w["logits"], w["labels"], T, row_mask=w.get("row_mask"),
+                         rows_list=rows, want_entropy=entropy)
+    assert_close("logp", logp[rows], ref["logp"][rows], tol["logp"])
+    assert_close("loss", loss[rows], ref["loss"][rows], tol["loss"])
+    if entropy:
+        assert_close("entropy", to_host(out["entropy"])[rows], ref["entropy"][rows],
+                     tol["entropy"])
+    assert np.array_equal(to_host(out["argmax"])[rows], ref["argmax"][rows])
+    g64 = np.asarray(w["g"], np.float64)
+    dsel = to_host(dl[torch.from_numpy(rows).to(DEV)])
+    worst = 0.0
+    for i, r in enumerate(rows):
+        dref = oracle.ce_grad_rows(w["logits"], w["labels"], g64, T,
+                                   row_mask=w.get("row_mask"), r0=int(r), r1=int(r) + 1)[0]
+        worst = max(worst, assert_close(f"dlogits row {r}", dsel[i], dref, tol["dlogits"],
+                                        FLOOR))
+    say(f"  {R}x{V}: {n} valid, sampled {rows.size} rows, max rel err logp "
+        f"{np.max(np.abs(logp[rows] - ref['logp'][rows]) / np.maximum(np.abs(ref['logp'][rows]), 1e-300)):.2e}, "
+        f"dlogits {worst:.2e}")
+    return out, logp, loss, valid
+
+
+def test_grpo_full_8192x152064_bf16():
+    from gpu_helpers import say
+    say("[full] grpo 8192x152064 bf16, 819 rows masked")
+    w = workloads.grpo()
+    _ce_full(w, entropy=False, tol=RTOL["bf16"])
+
+
+@pytest.fixture(scope="module", params=["f32", "bf16"])
+def peaked_full(request):
+    return workloads.peaked(request.param, 1.0)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.9])
+def test_peaked_full_2048x151936(peaked_full, T):
+    """Every margin in {5,17,20,30,50,80}: loss stays strictly positive (no
+    collapse) and matches the oracle on sampled rows of every margin."""
+    from gpu_helpers import say
+    w = dict(peaked_full, temperature=T)
+    kind = "bf16" if w["logits"].dtype == np.uint16 else "f32"
+    say(f"[full] peaked 2048x151936 {kind} T={T}")
+    out, logp, loss, valid = _ce_full(w, entropy=True, tol=RTOL[kind], sample_valid=36,
+                                      sample_invalid=0, seed=int(T * 10))
+    assert np.all(loss > 0) and np.all(logp < 0), "a peaked row collapsed to 0"
+
+
+def test_chunk_full_4096x32768_bf16_sls_and_topk():
+    from gpu_helpers import DEV, say, to_dev, to_host
+    import cross_entropy_vocab_amd as cev
+    say("[full] chunk 4096x32768 bf16 T=0.7, sls + top-8")
+    w = workloads.chunk()
+    logits = to_dev(w["logits"])
+    labels = to_dev(w["labels"])
+    idx = to_dev(w["indices"])
+    s = cev.sls_forward(logits, labels, 0.7, argmax=True)
+    lp = cev.sls_topk_forward(logits, idx, 0.7)
+    torch.cuda.synchronize()
+    logp = to_host(s["logp"])
+    tk = to_host(lp)
+    assert_nonpositive("sls", logp, np.ones(4096, dtype=bool))
+    assert_nonpositive("topk", tk)
+    rows = _sample_rows(np.random.default_rng(4), np.ones(4096, bool), 32, 0)
+    ref = oracle.ce_rows(w["logits"], w["labels"], 0.7, rows_list=rows, want_entropy=False)
+    assert_close("sls logp", logp[rows], ref["logp"][rows], RTOL["bf16"]["logp"])
+    assert np.array_equal(to_host(s["argmax"])[rows], ref["argmax"][rows])
+    tref, _ = oracle.topk_rows(w["logits"], w["indices"], 0.7, rows_list=rows)
+    assert_close("topk", tk[rows], tref[rows], RTOL["bf16"]["topk"])
+
+
+def test_compaction_many_rows():
+    """Compaction across many tiles (300000 rows, so each workgroup owns
+    several 1024-row sub-tiles): bit-exact against numpy.flatnonzero."""
+    from gpu_helpers import DEV, to_dev
+    import cross_entropy_vocab_amd as cev
+    rng = np.random.default_rng(21)
+    R, V = 300000, 6
+    z = rng.standard_normal((R, V)).astype(np.float32)
+    labels = rng.integers(0, V, R).astype(np.int64)
+    labels[rng.random(R) < 0.3] = -100
+    mask = (rng.random(R) > 0.2).astype(np.uint8)
+    out = cev.ce_forward(to_dev(z), to_dev(labels), 1.0, row_mask=to_dev(mask))
+    torch.cuda.synchronize()
+    want = np.flatnonzero((labels != -100) & (mask != 0))
+    n = int(out["n_valid"].item())
+    assert n == want.size
+    assert np.array_equal(out["valid_rows"][:n].cpu().numpy(), want)
