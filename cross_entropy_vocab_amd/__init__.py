@@ -43,8 +43,8 @@ def version() -> int:
     return int(_lib.get().cev_version())
 
 
-def workspace_size(rows: int) -> int:
-    return int(_lib.get().cev_workspace_size(int(rows)))
+def workspace_size(rows: int, vocab: int, dtype: int) -> int:
+    return int(_lib.get().cev_workspace_size(int(rows), int(vocab), int(dtype)))
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -179,14 +179,11 @@ def ce_forward(logits, labels, temperature=1.0, row_mask=None, ignore_index=-100
     want("argmax", argmax, torch.int64, (rows,))
     want("valid_rows", valid_rows, torch.int64, (rows,))
     want("n_valid", valid_rows, torch.int64, (1,))
-    ws = None
-    ws_bytes = 0
-    if not valid_rows:
-        ws_bytes = workspace_size(rows)
-        ws = o.get("workspace")
-        if ws is None or ws.numel() < ws_bytes:
-            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-        o["workspace"] = ws
+    ws_bytes = workspace_size(rows, vocab, _dtype_code(logits))
+    ws = o.get("workspace")
+    if ws is None or ws.numel() < ws_bytes:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    o["workspace"] = ws
     rc = _lib.get().ce_forward(_ptr(logits), rows, vocab, stride, _dtype_code(logits),
                                _ptr(labels), int(ignore_index), float(temperature), _ptr(m),
                                _ptr(o["loss"]), _ptr(o["saved"]), _ptr(o["logp"]),

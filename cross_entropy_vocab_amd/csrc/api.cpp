@@ -92,6 +92,7 @@ int sls_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_str
     a.labels = labels;
     a.ignore_index = ignore_index;
     a.row_mask = row_mask;
+    a.splits = 1;
     fill_temperature(a, temperature);
     a.logp = logp;
     a.entropy = entropy;
@@ -126,6 +127,7 @@ int sls_topk_forward(const void *logits, int64_t rows, int64_t vocab, int64_t ro
     a.indices = indices;
     a.K = K;
     a.index_row_stride = index_row_stride;
+    a.splits = 1;
     a.ignore_index = ignore_index;
     a.row_mask = row_mask;
     fill_temperature(a, temperature);
@@ -134,11 +136,20 @@ int sls_topk_forward(const void *logits, int64_t rows, int64_t vocab, int64_t ro
     return launch_status(cev::launch_topk_sweep(dtype, a, to_hip(stream)));
 }
 
-size_t cev_workspace_size(int64_t rows)
+// Workspace of ce_forward: the compacted row list and its count, then (for
+// few rows) the partial records of the split sweep, 32-byte aligned.
+static size_t list_bytes(int64_t rows) { return (size_t)(rows + 1) * sizeof(int64_t); }
+
+static size_t partial_offset(int64_t rows) { return (list_bytes(rows) + 31) & ~(size_t)31; }
+
+size_t cev_workspace_size(int64_t rows, int64_t vocab, int dtype)
 {
-    if (rows < 0)
+    if (rows < 0 || vocab < 1 || (dtype != CEV_F32 && dtype != CEV_BF16))
         return 0;
-    return (size_t)(rows + 1) * sizeof(int64_t);
+    const int64_t sp = cev::sweep_splits(rows, vocab, dtype);
+    if (sp <= 1)
+        return list_bytes(rows);
+    return partial_offset(rows) + (size_t)rows * (size_t)sp * sizeof(cev::SplitPartial);
 }
 
 int ce_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride, int dtype,
@@ -164,7 +175,7 @@ int ce_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stri
             return CEV_ENULL;
         if (!aligned(workspace, 8))
             return CEV_EALIGN;
-        if (workspace_bytes < cev_workspace_size(rows))
+        if (workspace_bytes < list_bytes(rows))
             return CEV_EWORKSPACE;
         int64_t *ws = static_cast<int64_t *>(workspace);
         if (!list)
@@ -172,6 +183,15 @@ int ce_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stri
         if (!count)
             count = ws + rows;
     }
+    // Few rows: split each row over several workgroups when the workspace
+    // holds the partial records; otherwise sweep whole rows.
+    int64_t splits = cev::sweep_splits(rows, vocab, dtype);
+    void *partials = nullptr;
+    if (splits > 1 && workspace && aligned(workspace, 32) &&
+        workspace_bytes >= cev_workspace_size(rows, vocab, dtype))
+        partials = static_cast<char *>(workspace) + partial_offset(rows);
+    else
+        splits = 1;
 
     CompactArgs ca{};
     ca.rows = rows;
@@ -201,6 +221,8 @@ int ce_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stri
     a.row_mask = row_mask;
     a.rowlist = list;
     a.nlist = count;
+    a.splits = splits;
+    a.partials = partials;
     fill_temperature(a, temperature);
     a.logp = logp;
     a.loss = loss;

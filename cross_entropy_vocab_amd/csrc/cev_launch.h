@@ -26,6 +26,8 @@ struct SweepArgs {
     const uint8_t *row_mask;
     const int64_t *rowlist;
     const int64_t *nlist;
+    int64_t splits;            // workgroups per row (1 = whole rows); needs partials
+    void *partials;            // [rows * splits] SplitPartial, device scratch
     double temperature;
     float c;                   // log2(e) / T, rounded to fp32
     float inv_t;               // 1 / T, rounded to fp32
@@ -36,6 +38,19 @@ struct SweepArgs {
     cev_saved *saved;
     int32_t *status;
 };
+
+// Statistics of one part of a row split over several workgroups.
+struct SplitPartial {
+    float m;                   // largest non-target stored logit of the part, -inf if none
+    int32_t pad;
+    int64_t arg;               // lowest non-target column holding m (INT64_MAX if none)
+    double s;                  // sum of e^{(z - b)/T}, b = max(m, -FLT_MAX)
+    double h;                  // sum of e^{(z - b)/T} (b - z)/T
+};
+
+// Workgroups per row for the split forward: enough workgroups to fill the
+// chip when rows are few (< 128), each part at least 2048 16-byte vectors.
+int64_t sweep_splits(int64_t rows, int64_t vocab, int dtype);
 
 struct CompactArgs {
     int64_t rows;

@@ -107,33 +107,44 @@ __device__ __forceinline__ void unpack_step(const u32x4 (&w)[U], float (&v)[U * 
     }
 }
 
-// Row geometry: `head` scalar columns up to the first 16-byte boundary, then
-// nvec 16-byte vectors (nfull wave steps of CH vectors plus nrem more), then
-// scalar columns from tail0 to V.
+// Geometry of the column range one workgroup sweeps.  A row is `ahead` scalar
+// columns up to its first 16-byte boundary, then 16-byte vectors, then fewer
+// than VE scalar columns.  A workgroup takes vectors [vbeg, vbeg + nvec) of
+// that row (nfull wave steps of CH vectors, then nrem single vectors), plus the
+// head columns [0, head) if it owns the row's start and the tail columns
+// [tail0, tail1) if it owns the row's end.
 struct RowGeom {
     int head;
-    int64_t nvec, nfull, nrem, tail0;
+    int64_t ahead;            // the row's head length (column of vector 0)
+    int64_t vbeg, nvec, nfull, nrem;
+    int64_t tail0, tail1;
 };
 
-template <int DT, int U> __device__ __forceinline__ RowGeom row_geom(const char *rowp, int64_t V)
+// Split the row into `parts` ranges of whole vectors; part `p` of them.
+template <int DT, int U>
+__device__ __forceinline__ RowGeom row_geom(const char *rowp, int64_t V, int64_t p, int64_t parts)
 {
     constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize;
     constexpr int64_t CH = (int64_t)kWave * U;
     RowGeom g;
     int64_t h = (int64_t)(((16u - ((unsigned)(uintptr_t)rowp & 15u)) & 15u) / ES);
-    g.head = (int)(h < V ? h : V);
-    g.nvec = (V - g.head) / VE;
+    g.ahead = h < V ? h : V;
+    const int64_t nv = (V - g.ahead) / VE;
+    g.vbeg = nv * p / parts;
+    g.nvec = nv * (p + 1) / parts - g.vbeg;
     g.nfull = g.nvec / CH;
     g.nrem = g.nvec - g.nfull * CH;
-    g.tail0 = g.head + g.nvec * VE;
+    g.head = p == 0 ? (int)g.ahead : 0;
+    g.tail0 = g.ahead + nv * VE;
+    g.tail1 = p == parts - 1 ? V : g.tail0;
     return g;
 }
 
 // Codes name the step where a lane's maximum first appeared, so that the
 // argmax can be found by re-reading that one step:
 //   [0, 16)                         head column
-//   16 + k                          wave step (chunk) k
-//   16 + nfull + i                  remainder vector nfull*CH + i
+//   16 + k                          wave step (chunk) k of the range
+//   16 + nfull + i                  remainder vector vbeg + nfull*CH + i
 //   16 + nfull + nrem + i           tail column tail0 + i
 template <int DT, int U>
 __device__ int64_t rescan_argmax(const char *rowp, const RowGeom &g, int code, float M, int64_t t)
@@ -141,7 +152,7 @@ __device__ int64_t rescan_argmax(const char *rowp, const RowGeom &g, int code, f
     constexpr int VE = Elem<DT>::kVE;
     constexpr int64_t CH = (int64_t)kWave * U;
     const int lane = threadIdx.x & (kWave - 1);
-    const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp + (size_t)g.head * Elem<DT>::kSize);
+    const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp + (size_t)g.ahead * Elem<DT>::kSize);
     int64_t found = INT64_MAX;
     if (code < 16)
         return code;
@@ -150,11 +161,12 @@ __device__ int64_t rescan_argmax(const char *rowp, const RowGeom &g, int code, f
         const int64_t k = c2;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            const int64_t j = g.vbeg + k * CH + u * kWave + lane;
             float v[VE];
-            unpack16<DT>(load16_stream(vp + k * CH + u * kWave + lane), v);
+            unpack16<DT>(load16_stream(vp + j), v);
 #pragma unroll
             for (int e = 0; e < VE; ++e) {
-                int64_t col = g.head + (k * CH + u * kWave + lane) * VE + e;
+                const int64_t col = g.ahead + j * VE + e;
                 if (found == INT64_MAX && v[e] == M && col != t)
                     found = col;
             }
@@ -163,12 +175,12 @@ __device__ int64_t rescan_argmax(const char *rowp, const RowGeom &g, int code, f
     }
     c2 -= g.nfull;
     if (c2 < g.nrem) {
-        const int64_t j = g.nfull * CH + c2;
+        const int64_t j = g.vbeg + g.nfull * CH + c2;
         float v[VE];
         unpack16<DT>(load16_stream(vp + j), v);
 #pragma unroll
         for (int e = 0; e < VE; ++e) {
-            int64_t col = g.head + j * VE + e;
+            const int64_t col = g.ahead + j * VE + e;
             if (found == INT64_MAX && v[e] == M && col != t)
                 found = col;
         }
@@ -178,9 +190,53 @@ __device__ int64_t rescan_argmax(const char *rowp, const RowGeom &g, int code, f
     return g.tail0 + c2;
 }
 
+// Per-row closing step in fp64 from exact inputs: the target logit z_t, the
+// largest non-target logit M (base B = max(M, -FLT_MAX)), the target-excluded
+// sum S = sum_{j != t} e^{(z_j - B)/T}, the entropy term
+// Hs = sum_{j != t} e^{(z_j - B)/T} (B - z_j)/T, and the lowest non-target
+// column holding M.
+template <int DT, bool WANT_H, bool WANT_ARG>
+__device__ void close_row(const SweepArgs &a, int64_t r, const char *rowp, int64_t t, float M,
+                          double S, double Hs, int64_t a_o)
+{
+    const float B = fmaxf(M, -FLT_MAX);
+    const double T = a.temperature;
+    const float zt = load_elem<DT>(rowp, t);
+    const double u = S > 0.0 ? log(S) + ((double)B - (double)zt) / T : -INFINITY;
+    const double loss = softplus64(u);
+    const double q = sigmoid64(u);
+    const double lse = (double)zt / T + loss;
+    if (a.logp)
+        a.logp[r] = (float)(-loss);
+    if (a.loss)
+        a.loss[r] = (float)loss;
+    if constexpr (WANT_H) {
+        // H = p_t * loss + sum_{j != t} p_j (lse - x_j), every term >= 0,
+        // with sum_{j != t} p_j = q and lse - x_j = (lse - B/T) + (B - z_j)/T.
+        double H = 0.0;
+        if (S > 0.0)
+            H = exp(-loss) * loss + q * (lse - (double)B / T) + exp((double)B / T - lse) * Hs;
+        a.entropy[r] = (float)H;
+    }
+    if constexpr (WANT_ARG)
+        a.argmax[r] = (zt > M || (zt == M && t < a_o)) ? t : a_o;
+    if (a.saved) {
+        const float mz = fmaxf(zt, M);
+        cev_saved sv;
+        sv.m_z = mz;
+        sv.log2_d = (float)((lse - (double)mz / T) * kLog2e);
+        sv.q = (float)q;
+        sv.flags = 1;
+        a.saved[r] = sv;
+    }
+}
+
 // ------------------------------------------------------------------------
-// Single-target sweep: sls_forward and the sweep stage of ce_forward.
-template <int DT, int BLOCK, int U, bool WANT_H, bool WANT_ARG>
+// Single-target sweep: sls_forward and the sweep stage of ce_forward.  With
+// SPLIT, `a.splits` workgroups share one row (block b * splits + p takes part
+// p of compacted row b) and each writes a partial record for k_merge instead
+// of closing the row.
+template <int DT, int BLOCK, int U, bool WANT_H, bool WANT_ARG, bool SPLIT>
 __global__ __launch_bounds__(BLOCK) void k_sls_sweep(SweepArgs a)
 {
     constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize, W = BLOCK / kWave;
@@ -190,13 +246,19 @@ __global__ __launch_bounds__(BLOCK) void k_sls_sweep(SweepArgs a)
     __shared__ int64_t sh_i[W];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
 
+    int64_t b = blockIdx.x, part = 0, parts = 1;
+    if constexpr (SPLIT) {
+        parts = a.splits;
+        b = blockIdx.x / parts;
+        part = blockIdx.x % parts;
+    }
     int64_t r;
     if (a.rowlist) {
-        if ((int64_t)blockIdx.x >= *a.nlist)
+        if (b >= *a.nlist)
             return;
-        r = a.rowlist[blockIdx.x];
+        r = a.rowlist[b];
     } else {
-        r = blockIdx.x;
+        r = b;
     }
     const int64_t V = a.vocab;
     const int64_t t = a.labels[r];
@@ -219,8 +281,9 @@ __global__ __launch_bounds__(BLOCK) void k_sls_sweep(SweepArgs a)
     }
 
     const char *rowp = static_cast<const char *>(a.logits) + (size_t)r * (size_t)a.row_stride * ES;
-    const RowGeom g = row_geom<DT, U>(rowp, V);
-    const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp + (size_t)g.head * ES);
+    const RowGeom g = row_geom<DT, U>(rowp, V, part, parts);
+    const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp + (size_t)g.ahead * ES) + g.vbeg;
+    const int64_t col_v = g.ahead + g.vbeg * VE;   // first column of the range's vectors
     const float c = a.c, inv_t = a.inv_t;
     LaneState st{-INFINITY, 0.0f, 0.0f, 0.0f, -1};
 
@@ -248,13 +311,13 @@ __global__ __launch_bounds__(BLOCK) void k_sls_sweep(SweepArgs a)
             }
             float v[U * VE];
             unpack_step<DT, U>(cur, v);
-            const int64_t lo = g.head + k * CH * VE;
+            const int64_t lo = col_v + k * CH * VE;
             if ((uint64_t)(t - lo) < (uint64_t)(CH * VE)) {
 #pragma unroll
                 for (int u = 0; u < U; ++u)
 #pragma unroll
                     for (int e = 0; e < VE; ++e)
-                        if (g.head + (k * CH + u * kWave + lane) * VE + e == t)
+                        if (col_v + (k * CH + u * kWave + lane) * VE + e == t)
                             v[u * VE + e] = -INFINITY;
                 fold<DT, U * VE, WANT_H, WANT_ARG, true>(st, v, 16 + (int)k, c, inv_t);
             } else {
@@ -271,12 +334,12 @@ __global__ __launch_bounds__(BLOCK) void k_sls_sweep(SweepArgs a)
         unpack16<DT>(load16_stream(vp + j), v);
 #pragma unroll
         for (int e = 0; e < VE; ++e)
-            if (g.head + j * VE + e == t)
+            if (col_v + j * VE + e == t)
                 v[e] = -INFINITY;
         fold<DT, VE, WANT_H, WANT_ARG, true>(st, v, 16 + (int)(g.nfull + (j - g.nfull * CH)), c,
                                              inv_t);
     }
-    if (g.tail0 + tid < V) {
+    if (g.tail0 + tid < g.tail1) {
         const int64_t col = g.tail0 + tid;
         float v[1] = {col == t ? -INFINITY : load_elem<DT>(rowp, col)};
         fold<DT, 1, WANT_H, WANT_ARG, true>(st, v, 16 + (int)(g.nfull + g.nrem + tid), c, inv_t);
@@ -303,36 +366,66 @@ __global__ __launch_bounds__(BLOCK) void k_sls_sweep(SweepArgs a)
     }
 
     if (tid == 0) {
-        // Per-row closing step in fp64 from exact inputs (z_t, B) and the sum.
-        const double T = a.temperature;
-        const float zt = load_elem<DT>(rowp, t);
-        const double u = S > 0.0 ? log(S) + ((double)B - (double)zt) / T : -INFINITY;
-        const double loss = softplus64(u);
-        const double q = sigmoid64(u);
-        const double lse = (double)zt / T + loss;
-        if (a.logp)
-            a.logp[r] = (float)(-loss);
-        if (a.loss)
-            a.loss[r] = (float)loss;
-        if constexpr (WANT_H) {
-            // H = p_t * loss + sum_{j != t} p_j (lse - x_j), every term >= 0,
-            // with sum_{j != t} p_j = q and lse - x_j = (lse - B/T) + (B - z_j)/T.
-            double H = 0.0;
-            if (S > 0.0)
-                H = exp(-loss) * loss + q * (lse - (double)B / T) + exp((double)B / T - lse) * Hs;
-            a.entropy[r] = (float)H;
+        if constexpr (SPLIT) {
+            SplitPartial pr;
+            pr.m = M;
+            pr.pad = 0;
+            pr.arg = a_o;
+            pr.s = S;
+            pr.h = Hs;
+            static_cast<SplitPartial *>(a.partials)[b * parts + part] = pr;
+        } else {
+            close_row<DT, WANT_H, WANT_ARG>(a, r, rowp, t, M, S, Hs, a_o);
         }
-        if constexpr (WANT_ARG)
-            a.argmax[r] = (zt > M || (zt == M && t < a_o)) ? t : a_o;
-        if (a.saved) {
-            const float mz = fmaxf(zt, M);
-            cev_saved sv;
-            sv.m_z = mz;
-            sv.log2_d = (float)((lse - (double)mz / T) * kLog2e);
-            sv.q = (float)q;
-            sv.flags = 1;
-            a.saved[r] = sv;
+    }
+}
+
+// Merge of the split partials (fixed order, fp64), then the closing step: one
+// wave per compacted row.  Part p holds, over its columns, the largest
+// non-target logit m_p, its lowest column, the sum S_p based at B_p =
+// max(m_p, -FLT_MAX) and the entropy term H_p at the same base; moving to the
+// common base B multiplies both by e^{(B_p - B)/T} and adds (B - B_p)/T * S_p
+// to H_p (the partial/combine rescaling of the unsloth-zoo #2080 Summary
+// quoted on the Liger-Kernel PR #1555 page).
+template <int DT, bool WANT_H, bool WANT_ARG>
+__global__ __launch_bounds__(256) void k_merge(SweepArgs a)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t b = (int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+    if (b >= *a.nlist)
+        return;
+    const int64_t r = a.rowlist[b];
+    const int parts = a.splits;
+    const SplitPartial *pp = static_cast<const SplitPartial *>(a.partials) + b * parts;
+    float m = -INFINITY;
+    for (int p = lane; p < parts; p += kWave)
+        m = fmaxf(m, pp[p].m);
+    const float M = wave_max(m);
+    const float B = fmaxf(M, -FLT_MAX);
+    const double T = a.temperature;
+    double S = 0.0, H = 0.0;
+    int64_t arg = INT64_MAX;
+    for (int p = lane; p < parts; p += kWave) {
+        const SplitPartial pr = pp[p];
+        if (pr.s > 0.0) {
+            const double bp = (double)fmaxf(pr.m, -FLT_MAX);
+            const double f = exp((bp - (double)B) / T);
+            S += pr.s * f;
+            if constexpr (WANT_H)
+                H += f * (pr.h + ((double)B - bp) / T * pr.s);
         }
+        if (pr.m == M && pr.arg < arg)
+            arg = pr.arg;
+    }
+    S = wave_sum(S);
+    if constexpr (WANT_H)
+        H = wave_sum(H);
+    if constexpr (WANT_ARG)
+        arg = wave_min(arg);
+    if (lane == 0) {
+        const char *rowp = static_cast<const char *>(a.logits) +
+                           (size_t)r * (size_t)a.row_stride * Elem<DT>::kSize;
+        close_row<DT, WANT_H, WANT_ARG>(a, r, rowp, a.labels[r], M, S, H, arg);
     }
 }
 
@@ -380,8 +473,8 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
     }
     __syncthreads();
 
-    const RowGeom g = row_geom<DT, U>(rowp, V);
-    const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp + (size_t)g.head * ES);
+    const RowGeom g = row_geom<DT, U>(rowp, V, 0, 1);
+    const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp + (size_t)g.ahead * ES);
     const float c = a.c, inv_t = a.inv_t;
     LaneState st{-INFINITY, 0.0f, 0.0f, 0.0f, -1};
 
@@ -413,7 +506,7 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
             }
             float v[U * VE];
             unpack_step<DT, U>(cur, v);
-            const int64_t lo = g.head + k * CH * VE;
+            const int64_t lo = g.ahead + k * CH * VE;
             bool any = false;
             for (int kk = 0; kk < K; kk += kWave) {
                 const int64_t x = kk + lane < K ? xcol[kk + lane] : -1;
@@ -427,7 +520,7 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
                         for (int u = 0; u < U; ++u)
 #pragma unroll
                             for (int e = 0; e < VE; ++e)
-                                if (g.head + (k * CH + u * kWave + lane) * VE + e == x)
+                                if (g.ahead + (k * CH + u * kWave + lane) * VE + e == x)
                                     v[u * VE + e] = -INFINITY;
                     }
                 }
@@ -445,11 +538,11 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
         unpack16<DT>(load16_stream(vp + j), v);
 #pragma unroll
         for (int e = 0; e < VE; ++e)
-            if (excluded(g.head + j * VE + e))
+            if (excluded(g.ahead + j * VE + e))
                 v[e] = -INFINITY;
         fold<DT, VE, false, false, true>(st, v, 0, c, inv_t);
     }
-    if (g.tail0 + tid < V) {
+    if (g.tail0 + tid < g.tail1) {
         const int64_t col = g.tail0 + tid;
         float v[1] = {excluded(col) ? -INFINITY : load_elem<DT>(rowp, col)};
         fold<DT, 1, false, false, true>(st, v, 0, c, inv_t);
@@ -480,18 +573,32 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
     }
 }
 
-template <int DT, int BLOCK, int U>
+template <int DT, int BLOCK, int U, bool SPLIT>
 hipError_t launch_sls_t(const SweepArgs &a, bool want_h, bool want_arg, hipStream_t s)
 {
-    dim3 grid((unsigned)a.rows), block(BLOCK);
+    dim3 grid((unsigned)(a.rows * (SPLIT ? a.splits : 1))), block(BLOCK);
     if (want_h && want_arg)
-        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, true, true>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, true, true, SPLIT>), grid, block, 0, s, a);
     else if (want_h)
-        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, true, false>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, true, false, SPLIT>), grid, block, 0, s, a);
     else if (want_arg)
-        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, false, true>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, false, true, SPLIT>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, false, false>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, false, false, SPLIT>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+template <int DT> hipError_t launch_merge_t(const SweepArgs &a, bool want_h, bool want_arg, hipStream_t s)
+{
+    dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
+    if (want_h && want_arg)
+        hipLaunchKernelGGL((k_merge<DT, true, true>), grid, block, 0, s, a);
+    else if (want_h)
+        hipLaunchKernelGGL((k_merge<DT, true, false>), grid, block, 0, s, a);
+    else if (want_arg)
+        hipLaunchKernelGGL((k_merge<DT, false, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((k_merge<DT, false, false>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -522,8 +629,8 @@ hipError_t launch_sls_sweep_cfg(int dtype, const SweepArgs &a, bool want_h, bool
 {
 #define CEV_SLS_CASE(B, UU)                                                                     \
     if (block == B && U == UU)                                                                  \
-        return dtype == CEV_BF16 ? launch_sls_t<CEV_BF16, B, UU>(a, want_h, want_arg, s)        \
-                                 : launch_sls_t<CEV_F32, B, UU>(a, want_h, want_arg, s);
+        return dtype == CEV_BF16 ? launch_sls_t<CEV_BF16, B, UU, false>(a, want_h, want_arg, s) \
+                                 : launch_sls_t<CEV_F32, B, UU, false>(a, want_h, want_arg, s);
     CEV_SLS_CASE(64, 4)
     CEV_SLS_CASE(128, 4)
     CEV_SLS_CASE(256, 4)
@@ -533,9 +640,36 @@ hipError_t launch_sls_sweep_cfg(int dtype, const SweepArgs &a, bool want_h, bool
     return hipErrorInvalidValue;
 }
 
+int64_t sweep_splits(int64_t rows, int64_t vocab, int dtype)
+{
+    // Measured on MI355X (152064-wide bf16 rows, ce_forward): splitting wins
+    // at 8 and 64 rows (16.1 -> 14.9 us, 21.6 -> 17.9 us) and loses from 256
+    // rows up, where the extra merge launch costs more than the occupancy gains.
+    constexpr int64_t kMaxSplitRows = 128;
+    constexpr int64_t kTargetBlocks = 2048;  // 8 workgroups per CU on 256 CUs
+    constexpr int64_t kMinPartVectors = 2048;
+    constexpr int64_t kMaxSplits = 256;
+    if (rows <= 0 || rows >= kMaxSplitRows)
+        return 1;
+    const int64_t nvec = vocab / (dtype == CEV_BF16 ? 8 : 4);
+    int64_t sp = (kTargetBlocks + rows - 1) / rows;
+    const int64_t by_size = nvec / kMinPartVectors;
+    sp = sp < by_size ? sp : by_size;
+    sp = sp < kMaxSplits ? sp : kMaxSplits;
+    return sp >= 2 ? sp : 1;
+}
+
 hipError_t launch_sls_sweep(int dtype, const SweepArgs &a, bool want_h, bool want_arg,
                             hipStream_t s)
 {
+    if (a.splits > 1 && a.partials && a.rowlist) {
+        hipError_t e = dtype == CEV_BF16 ? launch_sls_t<CEV_BF16, 256, 4, true>(a, want_h, want_arg, s)
+                                         : launch_sls_t<CEV_F32, 256, 4, true>(a, want_h, want_arg, s);
+        if (e != hipSuccess)
+            return e;
+        return dtype == CEV_BF16 ? launch_merge_t<CEV_BF16>(a, want_h, want_arg, s)
+                                 : launch_merge_t<CEV_F32>(a, want_h, want_arg, s);
+    }
     const Shape sh = pick_shape(a.vocab / (dtype == CEV_BF16 ? 8 : 4));
     return launch_sls_sweep_cfg(dtype, a, want_h, want_arg, sh.block, sh.U, s);
 }

@@ -154,9 +154,15 @@ int sls_topk_forward(const void *logits, int64_t rows, int64_t vocab, int64_t ro
  *   valid_rows    [rows] int64 out or NULL: the first *n_valid entries are the
  *                 valid rows in ascending order; the rest are left untouched
  *   n_valid       device int64 out or NULL: the number of valid rows
- *   workspace     device scratch of at least cev_workspace_size(rows) bytes,
- *                 8-byte aligned; may be NULL (with workspace_bytes 0) when both
- *                 valid_rows and n_valid are given
+ *   workspace     device scratch, or NULL.  With fewer than 128 rows and long
+ *                 rows, each row is split over several workgroups whose partial
+ *                 (max, sum) records are merged in a fixed order afterwards; this
+ *                 needs workspace_bytes >= cev_workspace_size(rows, vocab, dtype)
+ *                 and a 32-byte aligned workspace, else whole rows are swept
+ *                 (same results up to rounding, lower occupancy).  When
+ *                 valid_rows or n_valid is NULL the workspace also holds them and
+ *                 must be at least (rows + 1) * 8 bytes, 8-byte aligned.
+ *                 The workspace is overwritten; calls that share one race.
  */
 int ce_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride, int dtype,
                const int64_t *labels, int64_t ignore_index, double temperature,
@@ -186,8 +192,10 @@ int ce_backward(const void *logits, int64_t rows, int64_t vocab, int64_t row_str
                 const uint8_t *row_mask, const float *g, const void *saved, void *dlogits,
                 int64_t dlogits_row_stride, int32_t *status, cev_stream_t stream);
 
-/* Bytes of workspace ce_forward needs when valid_rows or n_valid is NULL. */
-size_t cev_workspace_size(int64_t rows);
+/* Bytes of workspace that let ce_forward hold the compacted row list and
+ * count and, for few rows, the split-row partial records (0 for invalid
+ * arguments). */
+size_t cev_workspace_size(int64_t rows, int64_t vocab, int dtype);
 
 /* Static text for a CEV_* return code. */
 const char *cev_status_string(int code);

@@ -57,8 +57,12 @@ def test_version_and_strings(lib):
     assert lib.cev_version() == 100
     for code in E.values():
         assert lib.cev_status_string(code)
-    assert lib.cev_workspace_size(10) == 88
-    assert lib.cev_workspace_size(-1) == 0
+    assert lib.cev_workspace_size(10, 100, 0) == 88          # list + count only
+    assert lib.cev_workspace_size(8192, 152064, 1) == 8193 * 8  # enough rows: no split
+    # few long rows split over workgroups: 32-byte partial records follow the list
+    assert lib.cev_workspace_size(64, 152064, 1) == 544 + 64 * 9 * 32
+    assert lib.cev_workspace_size(-1, 100, 0) == 0
+    assert lib.cev_workspace_size(10, 100, 5) == 0
 
 
 # fake, never-dereferenced device addresses (validation fails before any launch)

@@ -250,3 +250,74 @@ def test_temperature_scaling_identity():
     b = run_ce(w2)
     assert_close("T scaling logp", a["logp"], b["logp"].astype(np.float64), 2e-6)
     assert np.array_equal(a["argmax"], b["argmax"])
+
+
+def _ce_raw(w, workspace_bytes):
+    """ce_forward through the C ABI with an explicit workspace size (0 = none),
+    so the whole-row and the split-row sweeps can both be exercised."""
+    from gpu_helpers import DEV, to_dev
+    from cross_entropy_vocab_amd import _lib
+    logits = to_dev(w["logits"])
+    labels = to_dev(w["labels"])
+    R, V = w["logits"].shape
+    dt = 1 if w["logits"].dtype == np.uint16 else 0
+    mask = None if w.get("row_mask") is None else to_dev(w["row_mask"])
+    loss = torch.empty(R, device=DEV)
+    logp = torch.empty(R, device=DEV)
+    ent = torch.empty(R, device=DEV)
+    arg = torch.empty(R, dtype=torch.int64, device=DEV)
+    saved = torch.empty((R, 16), dtype=torch.uint8, device=DEV)
+    vr = torch.empty(R, dtype=torch.int64, device=DEV)
+    nv = torch.empty(1, dtype=torch.int64, device=DEV)
+    ws = torch.empty(max(workspace_bytes, 1), dtype=torch.uint8, device=DEV)
+    rc = _lib.get().ce_forward(logits.data_ptr(), R, V, V, dt, labels.data_ptr(), -100,
+                               float(w["temperature"]),
+                               None if mask is None else mask.data_ptr(), loss.data_ptr(),
+                               saved.data_ptr(), logp.data_ptr(), ent.data_ptr(), arg.data_ptr(),
+                               vr.data_ptr(), nv.data_ptr(),
+                               ws.data_ptr() if workspace_bytes else None, workspace_bytes, None,
+                               torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, rc
+    torch.cuda.synchronize()
+    return dict(loss=loss.cpu().numpy(), logp=logp.cpu().numpy(), entropy=ent.cpu().numpy(),
+                argmax=arg.cpu().numpy(), saved=saved.cpu().numpy(), n_valid=int(nv.item()),
+                valid_rows=vr.cpu().numpy())
+
+
+@pytest.mark.parametrize("rows,V,dtype,T", [(1, 152064, "bf16", 1.0), (3, 151936, "f32", 0.9),
+                                            (64, 152064, "bf16", 1.0), (100, 65537, "f32", 0.7),
+                                            (7, 40001, "bf16", 1.3)])
+def test_split_rows_match_oracle_and_whole_rows(rows, V, dtype, T):
+    """Few long rows: the split-row sweep (partials + fixed-order merge) and the
+    whole-row sweep both match the oracle, and the integer outputs agree."""
+    w = _rand_case(rows, V, dtype, T=T, seed=rows + V, n_ignored=rows // 5)
+    if rows >= 3:
+        w["logits"][1] = w["logits"][0]        # duplicated row: identical outputs
+        w["labels"][1] = w["labels"][0] if w["labels"][0] != -100 else 5
+        w["labels"][0] = w["labels"][1]
+    import cross_entropy_vocab_amd as cev
+    full = cev.workspace_size(rows, V, 1 if dtype == "bf16" else 0)
+    split = _ce_raw(w, full)
+    whole = _ce_raw(w, 0)
+    tol = RTOL[dtype]
+    ref = oracle.ce_rows(w["logits"], w["labels"], T)
+    for got, kind in ((split, "split"), (whole, "whole")):
+        assert_close(f"{kind} logp", got["logp"], ref["logp"], tol["logp"])
+        assert_close(f"{kind} loss", got["loss"], ref["loss"], tol["loss"])
+        assert_close(f"{kind} entropy", got["entropy"], ref["entropy"], tol["entropy"], 1e-30)
+        assert np.array_equal(got["argmax"], ref["argmax"]), kind
+    assert split["n_valid"] == whole["n_valid"]
+    assert np.array_equal(split["valid_rows"][:split["n_valid"]],
+                          whole["valid_rows"][:whole["n_valid"]])
+    # saved records: same maximum bits and flags; sums agree to rounding
+    s1 = split["saved"].view(np.float32).reshape(rows, 4)
+    s2 = whole["saved"].view(np.float32).reshape(rows, 4)
+    assert np.array_equal(s1[:, 0], s2[:, 0]) and np.array_equal(s1[:, 3], s2[:, 3])
+    # log2 d enters dlogits as an exponent: 1e-6 absolute is 7e-7 relative in p
+    assert_close("log2 d", s1[:, 1], s2[:, 1].astype(np.float64), 1e-6, 1e-6)
+    if rows >= 3:
+        assert split["logp"][0] == split["logp"][1] and split["argmax"][0] == split["argmax"][1]
+    # a second split call is bit-identical
+    again = _ce_raw(w, full)
+    assert np.array_equal(again["saved"], split["saved"])
+    assert np.array_equal(again["logp"].view(np.uint32), split["logp"].view(np.uint32))

@@ -75,9 +75,10 @@ def test_sls_forward_matches_ce(case):
     assert_close(f"{name} sls logp", got["logp"], ref["logp"], tol["logp"])
     assert_close(f"{name} sls entropy", got["entropy"], ref["entropy"], tol["entropy"])
     assert np.array_equal(got["argmax"], ref["argmax"])
-    # the two entry points share one sweep: identical bits
+    # the two entry points share one sweep (ce_forward may split few long rows
+    # over several workgroups, which changes only the summation order)
     ce = run_ce(w)
-    assert np.array_equal(got["logp"].view(np.uint32), ce["logp"].view(np.uint32))
+    assert_close(f"{name} sls vs ce", got["logp"], ce["logp"].astype(np.float64), 1e-6)
     # the same sweep without the optional outputs gives the same log p
     lean = run_sls(w, entropy=False, argmax=False)
     assert np.array_equal(lean["logp"].view(np.uint32), got["logp"].view(np.uint32))
