@@ -16,7 +16,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["sls_forward", "sls_topk_forward", "ce_forward", "ce_backward", "workspace_size",
+__all__ = ["sls_forward", "sls_topk_forward", "ce_forward", "ce_backward", "ce_fused",
+           "workspace_size",
            "status_string", "version", "CEV_F32", "CEV_BF16", "STATUS_BAD_LABEL",
            "STATUS_BAD_INDEX", "SAVED_BYTES", "CevError"]
 
@@ -219,3 +220,56 @@ def ce_backward(logits, labels, g, saved, temperature=1.0, row_mask=None, ignore
                                 _stream(dev))
     _check("ce_backward", rc)
     return dlogits
+
+
+def ce_fused(logits, labels, g, temperature=1.0, row_mask=None, ignore_index=-100, logp=True,
+             entropy=False, argmax=False, valid_rows=False, dlogits=None, status=None, out=None):
+    """ce_forward and ce_backward in one call for a g known up front (one HBM
+    pass when the row fits in a compute unit's registers).  Returns the
+    ce_forward dict plus "dlogits"."""
+    rows, vocab, stride = _check_logits(logits)
+    dev = logits.device
+    _dev(labels, "labels", torch.int64, (rows,), dev)
+    _dev(g, "g", torch.float32, (rows,), dev)
+    m = _mask(row_mask, rows, dev)
+    _dev(status, "status", torch.int32, (1,), dev)
+    o = dict(out) if out else {}
+
+    def want(key, flag, dtype, shape):
+        if not flag:
+            o[key] = None
+        elif o.get(key) is None:
+            o[key] = torch.empty(shape, dtype=dtype, device=dev)
+        else:
+            _dev(o[key], key, dtype, shape, dev)
+
+    want("loss", True, torch.float32, (rows,))
+    want("saved", True, torch.uint8, (rows, SAVED_BYTES))
+    want("logp", logp, torch.float32, (rows,))
+    want("entropy", entropy, torch.float32, (rows,))
+    want("argmax", argmax, torch.int64, (rows,))
+    want("valid_rows", valid_rows, torch.int64, (rows,))
+    want("n_valid", valid_rows, torch.int64, (1,))
+    if dlogits is None:
+        dlogits = o.get("dlogits")
+    if dlogits is None:
+        dlogits = torch.empty((rows, vocab), dtype=logits.dtype, device=dev)
+    elif dlogits.dtype != logits.dtype or tuple(dlogits.shape) != (rows, vocab):
+        raise ValueError("dlogits must match logits in dtype and shape")
+    elif rows > 0 and vocab > 1 and dlogits.stride(1) != 1:
+        raise ValueError("dlogits must have unit column stride")
+    o["dlogits"] = dlogits
+    dstride = max(dlogits.stride(0) if rows > 1 else vocab, vocab)
+    ws_bytes = workspace_size(rows, vocab, _dtype_code(logits))
+    ws = o.get("workspace")
+    if ws is None or ws.numel() < ws_bytes:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    o["workspace"] = ws
+    rc = _lib.get().ce_fused(_ptr(logits), rows, vocab, stride, _dtype_code(logits),
+                             _ptr(labels), int(ignore_index), float(temperature), _ptr(m), _ptr(g),
+                             _ptr(o["loss"]), _ptr(o["saved"]), _ptr(o["logp"]),
+                             _ptr(o["entropy"]), _ptr(o["argmax"]), _ptr(dlogits), dstride,
+                             _ptr(o["valid_rows"]), _ptr(o["n_valid"]), _ptr(ws), ws_bytes,
+                             _ptr(status), _stream(dev))
+    _check("ce_fused", rc)
+    return o

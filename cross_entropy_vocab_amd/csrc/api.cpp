@@ -277,6 +277,101 @@ int ce_backward(const void *logits, int64_t rows, int64_t vocab, int64_t row_str
     return launch_status(cev::launch_backward(dtype, a, to_hip(stream)));
 }
 
+int ce_fused(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride, int dtype,
+             const int64_t *labels, int64_t ignore_index, double temperature,
+             const uint8_t *row_mask, const float *g, float *loss, void *saved, float *logp,
+             float *entropy, int64_t *argmax, void *dlogits, int64_t dlogits_row_stride,
+             int64_t *valid_rows, int64_t *n_valid, void *workspace, size_t workspace_bytes,
+             int32_t *status, cev_stream_t stream)
+{
+    bool done;
+    int rc = check_common(logits, rows, vocab, row_stride, dtype, temperature, &done);
+    if (rc != CEV_OK || done)
+        return rc;
+    if (dlogits_row_stride < vocab)
+        return CEV_ESTRIDE;
+    if (dlogits_row_stride > INT64_MAX / 4 / rows)
+        return CEV_ESHAPE;
+    if (!labels || !g || !loss || !saved || !dlogits)
+        return CEV_ENULL;
+    const int es = elem_size(dtype);
+    if (!aligned(labels, 8) || !aligned(g, 4) || !aligned(loss, 4) || !aligned(saved, 16) ||
+        !aligned(logp, 4) || !aligned(entropy, 4) || !aligned(argmax, 8) ||
+        !aligned(valid_rows, 8) || !aligned(n_valid, 8) || !aligned(dlogits, (uintptr_t)es) ||
+        !aligned(status, 4))
+        return CEV_EALIGN;
+    const uintptr_t l0 = (uintptr_t)logits, l1 = l0 + (uintptr_t)(((rows - 1) * row_stride + vocab) * es);
+    const uintptr_t d0 = (uintptr_t)dlogits,
+                    d1 = d0 + (uintptr_t)(((rows - 1) * dlogits_row_stride + vocab) * es);
+    if (l0 < d1 && d0 < l1)
+        return CEV_EALIAS;
+    const bool want_list = valid_rows || n_valid;
+    if (want_list && (!valid_rows || !n_valid)) {
+        if (!workspace)
+            return CEV_ENULL;
+        if (!aligned(workspace, 8))
+            return CEV_EALIGN;
+        if (workspace_bytes < list_bytes(rows))
+            return CEV_EWORKSPACE;
+    }
+
+    // One workgroup per row for both passes when every row of both matrices
+    // starts 16-byte aligned; otherwise ce_forward then ce_backward.
+    const bool aligned_rows = aligned(logits, 16) && aligned(dlogits, 16) &&
+                              (row_stride * es) % 16 == 0 && (dlogits_row_stride * es) % 16 == 0;
+    if (!aligned_rows) {
+        rc = ce_forward(logits, rows, vocab, row_stride, dtype, labels, ignore_index, temperature,
+                        row_mask, loss, saved, logp, entropy, argmax, valid_rows, n_valid,
+                        workspace, workspace_bytes, status, stream);
+        if (rc != CEV_OK)
+            return rc;
+        return ce_backward(logits, rows, vocab, row_stride, dtype, labels, ignore_index,
+                           temperature, row_mask, g, saved, dlogits, dlogits_row_stride, status,
+                           stream);
+    }
+    if (want_list) {
+        int64_t *list = valid_rows ? valid_rows : static_cast<int64_t *>(workspace);
+        int64_t *count = n_valid ? n_valid : static_cast<int64_t *>(workspace) + rows;
+        CompactArgs ca{};
+        ca.rows = rows;
+        ca.vocab = vocab;
+        ca.labels = labels;
+        ca.ignore_index = ignore_index;
+        ca.row_mask = row_mask;
+        ca.rowlist = list;
+        ca.nlist = count;
+        ca.logp = logp;
+        ca.loss = loss;
+        ca.entropy = entropy;
+        ca.argmax = argmax;
+        ca.saved = static_cast<cev_saved *>(saved);
+        ca.status = status;
+        if (cev::launch_compact(ca, to_hip(stream)) != hipSuccess)
+            return CEV_ELAUNCH;
+    }
+    cev::FusedArgs fa{};
+    fa.logits = logits;
+    fa.rows = rows;
+    fa.vocab = vocab;
+    fa.row_stride = row_stride;
+    fa.labels = labels;
+    fa.ignore_index = ignore_index;
+    fa.row_mask = row_mask;
+    fa.g = g;
+    fa.temperature = temperature;
+    fa.c = (float)(1.4426950408889634074 / temperature);
+    fa.inv_t = (float)(1.0 / temperature);
+    fa.loss = loss;
+    fa.logp = logp;
+    fa.entropy = entropy;
+    fa.argmax = argmax;
+    fa.saved = static_cast<cev_saved *>(saved);
+    fa.dlogits = dlogits;
+    fa.d_row_stride = dlogits_row_stride;
+    fa.status = status;
+    return launch_status(cev::launch_fused(dtype, fa, entropy != nullptr, to_hip(stream)));
+}
+
 const char *cev_status_string(int code)
 {
     switch (code) {

@@ -86,6 +86,41 @@ struct BackwardArgs {
     int32_t *status;
 };
 
+// Single-pass forward + backward with the row resident in registers.
+struct FusedArgs {
+    const void *logits;
+    int64_t rows;
+    int64_t vocab;
+    int64_t row_stride;        // elements; rows start 16-byte aligned
+    const int64_t *labels;
+    int64_t ignore_index;
+    const uint8_t *row_mask;
+    const float *g;
+    double temperature;
+    float c;                   // log2(e) / T
+    float inv_t;               // 1 / T
+    float *loss;
+    float *logp;
+    float *entropy;
+    int64_t *argmax;
+    cev_saved *saved;
+    void *dlogits;
+    int64_t d_row_stride;      // elements; rows start 16-byte aligned
+    int32_t *status;
+};
+
+// Registers per thread for the resident row: 16-byte vectors per thread of a
+// 512-thread workgroup, in steps of 8 up to kMaxFusedVectors (196608 bf16 or
+// 98304 fp32 columns); 0 when the row does not fit (then the two-pass path
+// serves the call).
+constexpr int kMaxFusedVectors = 48;
+int fused_vectors_per_thread(int64_t vocab, int dtype);
+hipError_t launch_fused(int dtype, const FusedArgs &a, bool want_entropy, hipStream_t stream);
+hipError_t launch_fused_cfg(int dtype, const FusedArgs &a, bool want_entropy, int variant,
+                            hipStream_t stream);
+hipError_t launch_fused_stream_cfg(int dtype, const FusedArgs &a, int block, int U, bool desc,
+                                   size_t lds_bytes, hipStream_t stream);
+
 hipError_t launch_sls_sweep(int dtype, const SweepArgs &a, bool want_entropy, bool want_argmax,
                             hipStream_t stream);
 hipError_t launch_topk_sweep(int dtype, const SweepArgs &a, hipStream_t stream);

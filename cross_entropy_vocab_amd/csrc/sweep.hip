@@ -14,221 +14,27 @@
 // even when every other term is below the fp32 normal range.
 #include "cev_device.h"
 #include "cev_launch.h"
+#include "cev_rowclose.h"
+#include "cev_sweep_row.h"
 
 namespace cev {
 namespace {
 
-constexpr float kBig = 3.0e38f;
 constexpr int kMaxK = 1024; // gathered indices per row in sls_topk_forward
-constexpr double kLog2e = 1.4426950408889634074;
 
-// Running statistics of one lane over the (non-excluded) columns it has seen.
-struct LaneState {
-    float m;    // exact largest stored value seen, -inf if none
-    float s;    // sum of 2^((z - b) c), b = max(m, -FLT_MAX), c = log2(e)/T
-    float comp; // Kahan compensation: the true sum is about s - comp
-    float h;    // sum of 2^((z - b) c) (b - z) / T, for the entropy
-    int best;   // code of the first step in which m was reached
-};
 
-template <int N> __device__ __forceinline__ float tree_sum(float (&e)[N])
-{
-#pragma unroll
-    for (int w = 1; w < N; w *= 2)
-#pragma unroll
-        for (int i = 0; i + w < N; i += 2 * w)
-            e[i] += e[i + w];
-    return e[0];
-}
-
-// Fold one step of N values into the lane state.  Excluded columns arrive as
-// -inf; MAYBE_INF selects the guarded entropy term for such steps.
-template <int DT, int N, bool WANT_H, bool WANT_ARG, bool MAYBE_INF>
-__device__ __forceinline__ void fold(LaneState &st, float (&v)[N], int code, float c, float inv_t)
-{
-    float sm = v[0];
-#pragma unroll
-    for (int i = 1; i < N; ++i)
-        sm = fmaxf(sm, v[i]);
-    if constexpr (WANT_ARG)
-        st.best = sm > st.m ? code : st.best;
-    const float mnew = fmaxf(st.m, sm);
-    const float bold = fmaxf(st.m, -FLT_MAX);
-    const float bnew = fmaxf(mnew, -FLT_MAX);
-    // Rescale to the new base; f == 1 exactly when the maximum did not move.
-    const float f = exp2_hw((bold - bnew) * c);
-    if constexpr (WANT_H)
-        st.h = f * fmaf(fminf((bnew - bold) * inv_t, kBig), st.s, st.h);
-    st.s *= f;
-    st.comp *= f;
-    st.m = mnew;
-
-    float e[N];
-    if constexpr (DT == CEV_F32) {
-        // (z - b) first: exact for the terms near the maximum that dominate.
-#pragma unroll
-        for (int i = 0; i < N; ++i)
-            e[i] = exp2_hw((v[i] - bnew) * c);
-    } else {
-        const float nb = fminf(-bnew * c, kBig);
-#pragma unroll
-        for (int i = 0; i < N; ++i)
-            e[i] = exp2_hw(fmaf(v[i], c, nb));
-    }
-    if constexpr (WANT_H) {
-        float ph = 0.0f;
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            float d = (bnew - v[i]) * inv_t;
-            if constexpr (MAYBE_INF)
-                d = fminf(d, kBig);
-            ph = fmaf(e[i], d, ph);
-        }
-        st.h += ph;
-    }
-    const float ps = tree_sum(e);
-    const float y = ps - st.comp;
-    const float tsum = st.s + y;
-    st.comp = (tsum - st.s) - y;
-    st.s = tsum;
-}
-
-template <int DT, int U>
-__device__ __forceinline__ void unpack_step(const u32x4 (&w)[U], float (&v)[U * Elem<DT>::kVE])
-{
-    constexpr int VE = Elem<DT>::kVE;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        float t[VE];
-        unpack16<DT>(w[u], t);
-#pragma unroll
-        for (int e = 0; e < VE; ++e)
-            v[u * VE + e] = t[e];
-    }
-}
-
-// Geometry of the column range one workgroup sweeps.  A row is `ahead` scalar
-// columns up to its first 16-byte boundary, then 16-byte vectors, then fewer
-// than VE scalar columns.  A workgroup takes vectors [vbeg, vbeg + nvec) of
-// that row (nfull wave steps of CH vectors, then nrem single vectors), plus the
-// head columns [0, head) if it owns the row's start and the tail columns
-// [tail0, tail1) if it owns the row's end.
-struct RowGeom {
-    int head;
-    int64_t ahead;            // the row's head length (column of vector 0)
-    int64_t vbeg, nvec, nfull, nrem;
-    int64_t tail0, tail1;
-};
-
-// Split the row into `parts` ranges of whole vectors; part `p` of them.
-template <int DT, int U>
-__device__ __forceinline__ RowGeom row_geom(const char *rowp, int64_t V, int64_t p, int64_t parts)
-{
-    constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize;
-    constexpr int64_t CH = (int64_t)kWave * U;
-    RowGeom g;
-    int64_t h = (int64_t)(((16u - ((unsigned)(uintptr_t)rowp & 15u)) & 15u) / ES);
-    g.ahead = h < V ? h : V;
-    const int64_t nv = (V - g.ahead) / VE;
-    g.vbeg = nv * p / parts;
-    g.nvec = nv * (p + 1) / parts - g.vbeg;
-    g.nfull = g.nvec / CH;
-    g.nrem = g.nvec - g.nfull * CH;
-    g.head = p == 0 ? (int)g.ahead : 0;
-    g.tail0 = g.ahead + nv * VE;
-    g.tail1 = p == parts - 1 ? V : g.tail0;
-    return g;
-}
-
-// Codes name the step where a lane's maximum first appeared, so that the
-// argmax can be found by re-reading that one step:
-//   [0, 16)                         head column
-//   16 + k                          wave step (chunk) k of the range
-//   16 + nfull + i                  remainder vector vbeg + nfull*CH + i
-//   16 + nfull + nrem + i           tail column tail0 + i
-template <int DT, int U>
-__device__ int64_t rescan_argmax(const char *rowp, const RowGeom &g, int code, float M, int64_t t)
-{
-    constexpr int VE = Elem<DT>::kVE;
-    constexpr int64_t CH = (int64_t)kWave * U;
-    const int lane = threadIdx.x & (kWave - 1);
-    const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp + (size_t)g.ahead * Elem<DT>::kSize);
-    int64_t found = INT64_MAX;
-    if (code < 16)
-        return code;
-    int64_t c2 = code - 16;
-    if (c2 < g.nfull) {
-        const int64_t k = c2;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t j = g.vbeg + k * CH + u * kWave + lane;
-            float v[VE];
-            unpack16<DT>(load16_stream(vp + j), v);
-#pragma unroll
-            for (int e = 0; e < VE; ++e) {
-                const int64_t col = g.ahead + j * VE + e;
-                if (found == INT64_MAX && v[e] == M && col != t)
-                    found = col;
-            }
-        }
-        return found;
-    }
-    c2 -= g.nfull;
-    if (c2 < g.nrem) {
-        const int64_t j = g.vbeg + g.nfull * CH + c2;
-        float v[VE];
-        unpack16<DT>(load16_stream(vp + j), v);
-#pragma unroll
-        for (int e = 0; e < VE; ++e) {
-            const int64_t col = g.ahead + j * VE + e;
-            if (found == INT64_MAX && v[e] == M && col != t)
-                found = col;
-        }
-        return found;
-    }
-    c2 -= g.nrem;
-    return g.tail0 + c2;
-}
-
-// Per-row closing step in fp64 from exact inputs: the target logit z_t, the
-// largest non-target logit M (base B = max(M, -FLT_MAX)), the target-excluded
-// sum S = sum_{j != t} e^{(z_j - B)/T}, the entropy term
-// Hs = sum_{j != t} e^{(z_j - B)/T} (B - z_j)/T, and the lowest non-target
-// column holding M.
+// Per-row closing step (cev_rowclose.h) with the sweep's outputs.
 template <int DT, bool WANT_H, bool WANT_ARG>
 __device__ void close_row(const SweepArgs &a, int64_t r, const char *rowp, int64_t t, float M,
                           double S, double Hs, int64_t a_o)
 {
-    const float B = fmaxf(M, -FLT_MAX);
-    const double T = a.temperature;
-    const float zt = load_elem<DT>(rowp, t);
-    const double u = S > 0.0 ? log(S) + ((double)B - (double)zt) / T : -INFINITY;
-    const double loss = softplus64(u);
-    const double q = sigmoid64(u);
-    const double lse = (double)zt / T + loss;
-    if (a.logp)
-        a.logp[r] = (float)(-loss);
-    if (a.loss)
-        a.loss[r] = (float)loss;
-    if constexpr (WANT_H) {
-        // H = p_t * loss + sum_{j != t} p_j (lse - x_j), every term >= 0,
-        // with sum_{j != t} p_j = q and lse - x_j = (lse - B/T) + (B - z_j)/T.
-        double H = 0.0;
-        if (S > 0.0)
-            H = exp(-loss) * loss + q * (lse - (double)B / T) + exp((double)B / T - lse) * Hs;
-        a.entropy[r] = (float)H;
-    }
-    if constexpr (WANT_ARG)
-        a.argmax[r] = (zt > M || (zt == M && t < a_o)) ? t : a_o;
-    if (a.saved) {
-        const float mz = fmaxf(zt, M);
-        cev_saved sv;
-        sv.m_z = mz;
-        sv.log2_d = (float)((lse - (double)mz / T) * kLog2e);
-        sv.q = (float)q;
-        sv.flags = 1;
-        a.saved[r] = sv;
-    }
+    RowOutputs o;
+    o.logp = a.logp;
+    o.loss = a.loss;
+    o.entropy = WANT_H ? a.entropy : nullptr;
+    o.argmax = WANT_ARG ? a.argmax : nullptr;
+    o.saved = a.saved;
+    close_row_fp64(o, r, load_elem<DT>(rowp, t), t, M, S, Hs, a_o, a.temperature);
 }
 
 // ------------------------------------------------------------------------
@@ -239,12 +45,11 @@ __device__ void close_row(const SweepArgs &a, int64_t r, const char *rowp, int64
 template <int DT, int BLOCK, int U, bool WANT_H, bool WANT_ARG, bool SPLIT>
 __global__ __launch_bounds__(BLOCK) void k_sls_sweep(SweepArgs a)
 {
-    constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize, W = BLOCK / kWave;
-    constexpr int64_t CH = (int64_t)kWave * U;
+    constexpr int ES = Elem<DT>::kSize, W = BLOCK / kWave;
     __shared__ float sh_f[W];
     __shared__ double sh_d[W];
     __shared__ int64_t sh_i[W];
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int tid = threadIdx.x;
 
     int64_t b = blockIdx.x, part = 0, parts = 1;
     if constexpr (SPLIT) {
@@ -281,89 +86,11 @@ __global__ __launch_bounds__(BLOCK) void k_sls_sweep(SweepArgs a)
     }
 
     const char *rowp = static_cast<const char *>(a.logits) + (size_t)r * (size_t)a.row_stride * ES;
-    const RowGeom g = row_geom<DT, U>(rowp, V, part, parts);
-    const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp + (size_t)g.ahead * ES) + g.vbeg;
-    const int64_t col_v = g.ahead + g.vbeg * VE;   // first column of the range's vectors
-    const float c = a.c, inv_t = a.inv_t;
-    LaneState st{-INFINITY, 0.0f, 0.0f, 0.0f, -1};
-
-    if (tid < g.head) {
-        float v[1] = {tid == t ? -INFINITY : load_elem<DT>(rowp, tid)};
-        fold<DT, 1, WANT_H, WANT_ARG, true>(st, v, tid, c, inv_t);
-    }
-
-    // Full wave steps, interleaved over the waves, one step of loads in flight
-    // ahead of the arithmetic.
-    {
-        int64_t k = wave;
-        u32x4 cur[U], nxt[U];
-        if (k < g.nfull) {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                cur[u] = load16_stream(vp + k * CH + u * kWave + lane);
-        }
-        for (; k < g.nfull; k += W) {
-            const int64_t kn = k + W;
-            if (kn < g.nfull) {
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    nxt[u] = load16_stream(vp + kn * CH + u * kWave + lane);
-            }
-            float v[U * VE];
-            unpack_step<DT, U>(cur, v);
-            const int64_t lo = col_v + k * CH * VE;
-            if ((uint64_t)(t - lo) < (uint64_t)(CH * VE)) {
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-#pragma unroll
-                    for (int e = 0; e < VE; ++e)
-                        if (col_v + (k * CH + u * kWave + lane) * VE + e == t)
-                            v[u * VE + e] = -INFINITY;
-                fold<DT, U * VE, WANT_H, WANT_ARG, true>(st, v, 16 + (int)k, c, inv_t);
-            } else {
-                fold<DT, U * VE, WANT_H, WANT_ARG, false>(st, v, 16 + (int)k, c, inv_t);
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                cur[u] = nxt[u];
-        }
-    }
-
-    for (int64_t j = g.nfull * CH + tid; j < g.nvec; j += BLOCK) {
-        float v[VE];
-        unpack16<DT>(load16_stream(vp + j), v);
-#pragma unroll
-        for (int e = 0; e < VE; ++e)
-            if (col_v + j * VE + e == t)
-                v[e] = -INFINITY;
-        fold<DT, VE, WANT_H, WANT_ARG, true>(st, v, 16 + (int)(g.nfull + (j - g.nfull * CH)), c,
-                                             inv_t);
-    }
-    if (g.tail0 + tid < g.tail1) {
-        const int64_t col = g.tail0 + tid;
-        float v[1] = {col == t ? -INFINITY : load_elem<DT>(rowp, col)};
-        fold<DT, 1, WANT_H, WANT_ARG, true>(st, v, 16 + (int)(g.nfull + g.nrem + tid), c, inv_t);
-    }
-
-    // Combine the lanes: exact maximum first, then each lane rescales its own
-    // sum once to the common base and the sums are added in fp64.
-    const float M = block_max<BLOCK>(st.m, sh_f);
-    const float B = fmaxf(M, -FLT_MAX);
-    const float bl = fmaxf(st.m, -FLT_MAX);
-    const float f = exp2_hw((bl - B) * c);
-    const float sl = st.s - st.comp;
-    const double S = block_sum<BLOCK>((double)sl * (double)f, sh_d);
-    double Hs = 0.0;
-    if constexpr (WANT_H)
-        Hs = block_sum<BLOCK>((double)f * (double)fmaf(fminf((B - bl) * inv_t, kBig), sl, st.h),
-                              sh_d);
-    int64_t a_o = INT64_MAX;
-    if constexpr (WANT_ARG) {
-        int64_t mine = INT64_MAX;
-        if (M != -INFINITY && st.m == M)
-            mine = rescan_argmax<DT, U>(rowp, g, st.best, M, t);
-        a_o = block_min<BLOCK>(mine, sh_i);
-    }
+    const RowStats rs = sweep_row<DT, BLOCK, U, WANT_H, WANT_ARG, true>(
+        rowp, V, t, part, parts, a.c, a.inv_t, sh_f, sh_d, sh_i);
+    const float M = rs.M;
+    const double S = rs.S, Hs = rs.Hs;
+    const int64_t a_o = rs.a_o;
 
     if (tid == 0) {
         if constexpr (SPLIT) {

@@ -192,6 +192,31 @@ int ce_backward(const void *logits, int64_t rows, int64_t vocab, int64_t row_str
                 const uint8_t *row_mask, const float *g, const void *saved, void *dlogits,
                 int64_t dlogits_row_stride, int32_t *status, cev_stream_t stream);
 
+/*
+ * ce_fused -- ce_forward and ce_backward in one call, for an upstream weight g
+ * that is known before the forward (token weights, a mean over rows).  When
+ * each row fits in one compute unit's registers (up to 196608 bf16 or 98304
+ * fp32 columns) and every row of logits and dlogits starts 16-byte aligned, a
+ * single pass reads each valid row once and writes each dlogits row once: one
+ * workgroup keeps the whole row resident, takes the exact non-target maximum,
+ * then the target-excluded sum, closes the row in fp64 and writes
+ * (g/T)(softmax - onehot) from the same registers.  This realises the
+ * gradient-in-the-forward idea of the unsloth-zoo #2079 Summary quoted on the
+ * Liger-Kernel PR #1555 page for a plain logit matrix.  Otherwise it runs
+ * ce_forward then ce_backward.  Outputs and their meaning are those of
+ * ce_forward (loss, saved, logp, entropy, argmax, valid_rows, n_valid) and
+ * ce_backward (dlogits); g, dlogits and dlogits_row_stride as in ce_backward.
+ * valid_rows / n_valid are computed only when requested; a missing one of the
+ * pair takes (rows + 1) * 8 bytes of workspace, and the two-pass fallback uses
+ * the workspace as ce_forward does.
+ */
+int ce_fused(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride, int dtype,
+             const int64_t *labels, int64_t ignore_index, double temperature,
+             const uint8_t *row_mask, const float *g, float *loss, void *saved, float *logp,
+             float *entropy, int64_t *argmax, void *dlogits, int64_t dlogits_row_stride,
+             int64_t *valid_rows, int64_t *n_valid, void *workspace, size_t workspace_bytes,
+             int32_t *status, cev_stream_t stream);
+
 /* Bytes of workspace that let ce_forward hold the compacted row list and
  * count and, for few rows, the split-row partial records (0 for invalid
  * arguments). */

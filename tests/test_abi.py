@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = set(declared_functions())
-    assert {"sls_forward", "sls_topk_forward", "ce_forward", "ce_backward",
+    assert {"sls_forward", "sls_topk_forward", "ce_forward", "ce_backward", "ce_fused",
             "cev_workspace_size", "cev_status_string", "cev_version"} <= names
 
 
@@ -158,6 +158,30 @@ def test_ce_backward_validation(lib):
     assert call(saved=A + 8) == E["ALIGN"]
     assert call(dl=B + 1) == E["ALIGN"]
     assert call(T=float("nan")) == E["TEMP"]
+    assert call(rows=0) == E["OK"]
+
+
+def test_ce_fused_validation(lib):
+    def call(**kw):
+        a = dict(logits=A, rows=4, vocab=100, stride=100, dtype=1, labels=A, ig=-100, T=1.0,
+                 mask=None, g=A, loss=A, saved=A, logp=None, ent=None, arg=None, dl=B,
+                 dstride=100, vr=None, nv=None, ws=None, wsb=0, status=None)
+        a.update(kw)
+        return lib.ce_fused(a["logits"], a["rows"], a["vocab"], a["stride"], a["dtype"],
+                            a["labels"], a["ig"], a["T"], a["mask"], a["g"], a["loss"],
+                            a["saved"], a["logp"], a["ent"], a["arg"], a["dl"], a["dstride"],
+                            a["vr"], a["nv"], a["ws"], a["wsb"], a["status"], None)
+    assert call(dl=A) == E["ALIAS"]
+    assert call(g=None) == E["NULL"]
+    assert call(saved=None) == E["NULL"]
+    assert call(loss=None) == E["NULL"]
+    assert call(dl=None) == E["NULL"]
+    assert call(saved=A + 8) == E["ALIGN"]
+    assert call(dstride=99) == E["STRIDE"]
+    assert call(vr=A) == E["NULL"]                    # count missing and no workspace
+    assert call(vr=A, ws=A, wsb=39) == E["WORKSPACE"]
+    assert call(T=0.0) == E["TEMP"]
+    assert call(dtype=9) == E["DTYPE"]
     assert call(rows=0) == E["OK"]
 
 

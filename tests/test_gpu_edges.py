@@ -321,3 +321,72 @@ def test_split_rows_match_oracle_and_whole_rows(rows, V, dtype, T):
     again = _ce_raw(w, full)
     assert np.array_equal(again["saved"], split["saved"])
     assert np.array_equal(again["logp"].view(np.uint32), split["logp"].view(np.uint32))
+
+
+def _run_fused(w, logits_dev=None, dl_stride=None, entropy=True):
+    from gpu_helpers import DEV, to_dev, to_host
+    logits = logits_dev if logits_dev is not None else to_dev(w["logits"])
+    labels = to_dev(w["labels"])
+    mask = None if w.get("row_mask") is None else to_dev(w["row_mask"])
+    g = to_dev(np.asarray(w["g"], np.float32))
+    R, V = w["logits"].shape
+    dl = None
+    if dl_stride is not None:
+        dl = torch.zeros((R, dl_stride), dtype=logits.dtype, device=DEV)[:, :V]
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = cev.ce_fused(logits, labels, g, w["temperature"], row_mask=mask, entropy=entropy,
+                       argmax=True, valid_rows=True, dlogits=dl, status=status)
+    torch.cuda.synchronize()
+    res = {k: to_host(v) for k, v in out.items() if v is not None and k != "workspace"}
+    res["status"] = int(status.item())
+    return res
+
+
+FUSED_CASES = {
+    "grpo_40x152064_bf16": lambda: workloads.grpo(rows=40, vocab=152064),
+    "peaked_16x151936_bf16_T0.9": lambda: workloads.peaked("bf16", 0.9, rows=16),
+    "peaked_12x151936_f32_T1_two_pass": lambda: workloads.peaked("f32", 1.0, rows=12),
+    "tiny_64x4096_f32": lambda: workloads.tiny(),
+    "sparse_1922x4096_f32": lambda: workloads.sparse(),
+    "chunk_20x32768_bf16_T0.7": lambda: workloads.chunk(rows=20, vocab=32768),
+    "small_9x300_f32_two_pass": lambda: _rand_case(9, 300, "f32", seed=1, n_ignored=2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FUSED_CASES))
+def test_ce_fused_matches_oracle(name):
+    """ce_fused against the oracle on every output, in both its one-pass form
+    (row resident in registers) and its two-pass fallback."""
+    w = FUSED_CASES[name]()
+    got = _run_fused(w)
+    _check_against_oracle(w, got, f"fused {name}")
+    assert got["status"] == 0
+
+
+def test_ce_fused_tail_columns_and_padded_strides():
+    """V not a multiple of 8 with 16-byte aligned padded rows (one pass, tail
+    columns in the registers), and the same with an unaligned stride (two pass);
+    padding columns of dlogits stay untouched."""
+    from gpu_helpers import strided_dev
+    for V, stride in ((32781, 32784), (32781, 32781), (40007, 40016)):
+        w = _rand_case(10, V, "bf16", T=0.8, seed=V + stride, n_ignored=2)
+        w["labels"][3] = V - 1            # target in the tail columns
+        w["labels"][4] = V - 3
+        got = _run_fused(w, logits_dev=strided_dev(w["logits"], stride), dl_stride=stride)
+        _check_against_oracle(w, got, f"fused V={V} stride={stride}")
+
+
+def test_ce_fused_equals_separate_calls():
+    """The one-pass result matches ce_forward + ce_backward (summation order
+    differs: log p to 1e-6, bf16 dlogits to one rounding step)."""
+    from gpu_helpers import run_ce
+    w = workloads.grpo(rows=48, vocab=152064)
+    a = _run_fused(w, entropy=False)
+    b = run_ce(w, entropy=False)
+    assert_close("fused vs two-pass logp", a["logp"], b["logp"].astype(np.float64), 1e-6)
+    assert np.array_equal(a["argmax"], b["argmax"])
+    assert np.array_equal(a["valid_rows"][:int(a["n_valid"][0])],
+                          b["valid_rows"][:int(b["n_valid"][0])])
+    assert_close("fused vs two-pass dlogits", a["dlogits"], b["dlogits"], 8e-3, 2.0 ** -126)
+    again = _run_fused(w, entropy=False)
+    assert np.array_equal(again["dlogits"], a["dlogits"])
