@@ -86,7 +86,7 @@ struct BackwardArgs {
     int32_t *status;
 };
 
-// Single-pass forward + backward with the row resident in registers.
+// Forward + backward in one call, one workgroup per row (rows 16-byte aligned).
 struct FusedArgs {
     const void *logits;
     int64_t rows;
@@ -109,15 +109,7 @@ struct FusedArgs {
     int32_t *status;
 };
 
-// Registers per thread for the resident row: 16-byte vectors per thread of a
-// 512-thread workgroup, in steps of 8 up to kMaxFusedVectors (196608 bf16 or
-// 98304 fp32 columns); 0 when the row does not fit (then the two-pass path
-// serves the call).
-constexpr int kMaxFusedVectors = 48;
-int fused_vectors_per_thread(int64_t vocab, int dtype);
 hipError_t launch_fused(int dtype, const FusedArgs &a, bool want_entropy, hipStream_t stream);
-hipError_t launch_fused_cfg(int dtype, const FusedArgs &a, bool want_entropy, int variant,
-                            hipStream_t stream);
 hipError_t launch_fused_stream_cfg(int dtype, const FusedArgs &a, int block, int U, bool desc,
                                    size_t lds_bytes, hipStream_t stream);
 
