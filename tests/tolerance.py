@@ -36,8 +36,12 @@ def assert_close(name, got, ref, rtol, atol=0.0):
         raise AssertionError(
             f"{name}: {int(bad.sum())} of {bad.size} outside |d| <= {rtol:g}|ref| + {atol:g}; "
             f"worst at {i}: got {got[i]!r} ref {ref[i]!r}")
+    # report the worst relative error where the relative bound governs (the
+    # absolute floor covers the rest, e.g. flushed fp32 subnormals)
     with np.errstate(divide="ignore", invalid="ignore"):
         rel = np.where(ref != 0, err / np.abs(ref), np.where(err == 0, 0.0, np.inf))
+    governed = rtol * np.abs(ref) >= atol
+    rel = rel[governed] if atol > 0 else rel
     return float(np.max(rel)) if rel.size else 0.0
 
 
