@@ -15,7 +15,8 @@ values: fp32 logits are passed as float32 arrays, bf16 logits as their uint16
 bit patterns, and the C side widens both exactly.
 
 Parity status of each function (what pins it is listed in the tests):
-  valid_rows, ce_rows, ce_grad_rows, topk_rows -- pinned by closed forms,
+  valid_rows, ce_rows (with label smoothing), ce_grad_rows (with label
+  smoothing), topk_rows (with q), topk_grad_rows -- pinned by closed forms,
   invariants, 120-digit brute force and library routines (tests/test_oracle_pins.py).
 """
 from __future__ import annotations
@@ -60,15 +61,18 @@ def load_library(path: str):
     I64 = ctypes.c_int64
     lib.oracle_valid_rows.argtypes = [P, P, I64, I64, I64, P, P]
     lib.oracle_valid_rows.restype = I64
-    lib.oracle_ce_rows.argtypes = [P, I64, I64, I64, ctypes.c_int, P, I64, ctypes.c_double, P,
-                                   I64, I64, P, P, P, P, P]
+    lib.oracle_ce_rows.argtypes = [P, I64, I64, I64, ctypes.c_int, P, I64, ctypes.c_double,
+                                   ctypes.c_double, P, I64, I64, P, P, P, P, P]
     lib.oracle_ce_rows.restype = ctypes.c_int
     lib.oracle_ce_grad_rows.argtypes = [P, I64, I64, I64, ctypes.c_int, P, I64, ctypes.c_double,
-                                        P, P, I64, I64, P]
+                                        ctypes.c_double, P, P, I64, I64, P]
     lib.oracle_ce_grad_rows.restype = ctypes.c_int
     lib.oracle_topk_rows.argtypes = [P, I64, I64, I64, ctypes.c_int, P, I64, I64, I64,
-                                     ctypes.c_double, P, I64, I64, P]
+                                     ctypes.c_double, P, I64, I64, P, P]
     lib.oracle_topk_rows.restype = ctypes.c_int
+    lib.oracle_topk_grad_rows.argtypes = [P, I64, I64, I64, ctypes.c_int, P, I64, I64, I64,
+                                          ctypes.c_double, P, P, I64, I64, P]
+    lib.oracle_topk_grad_rows.restype = ctypes.c_int
     return lib
 
 
@@ -149,7 +153,7 @@ def valid_rows(labels, row_mask=None, vocab=None, ignore_index=-100, lib=None):
 
 
 def ce_rows(logits, labels, temperature=1.0, row_mask=None, ignore_index=-100, rows_list=None,
-            threads=None, want_entropy=True, want_argmax=True, lib=None):
+            threads=None, want_entropy=True, want_argmax=True, lib=None, label_smoothing=0.0):
     """Per-row forward.  Returns dict of float64/int64 arrays over all rows
     (rows not in rows_list, if given, are left as NaN / -2) and the status."""
     lib = _load(lib)
@@ -169,7 +173,8 @@ def ce_rows(logits, labels, temperature=1.0, row_mask=None, ignore_index=-100, r
 
     def work(rng):
         return lib.oracle_ce_rows(_ptr(logits), rows, vocab, stride, dt, _ptr(lab),
-                                  int(ignore_index), float(temperature), _ptr(m), rng[0], rng[1],
+                                  int(ignore_index), float(temperature), float(label_smoothing),
+                                  _ptr(m), rng[0], rng[1],
                                   _ptr(out["logp"]), _ptr(out["loss"]), _ptr(out["entropy"]),
                                   _ptr(out["argmax"]), _ptr(out["q"]))
 
@@ -182,7 +187,7 @@ def ce_rows(logits, labels, temperature=1.0, row_mask=None, ignore_index=-100, r
 
 
 def ce_grad_rows(logits, labels, g, temperature=1.0, row_mask=None, ignore_index=-100, r0=0,
-                 r1=None, threads=None, lib=None):
+                 r1=None, threads=None, lib=None, label_smoothing=0.0):
     """float64 dlogits for rows [r0, r1) as an array of shape [r1 - r0, vocab]."""
     lib = _load(lib)
     dt = _dtype_code(logits)
@@ -200,7 +205,8 @@ def ce_grad_rows(logits, labels, g, temperature=1.0, row_mask=None, ignore_index
     def work(rng):
         a, b = rng
         return lib.oracle_ce_grad_rows(_ptr(logits), rows, vocab, stride, dt, _ptr(lab),
-                                       int(ignore_index), float(temperature), _ptr(m), _ptr(gg),
+                                       int(ignore_index), float(temperature),
+                                       float(label_smoothing), _ptr(m), _ptr(gg),
                                        r0 + a, r0 + b, out[a:].ctypes.data)
 
     st = 0
@@ -211,9 +217,10 @@ def ce_grad_rows(logits, labels, g, temperature=1.0, row_mask=None, ignore_index
 
 
 def topk_rows(logits, indices, temperature=1.0, row_mask=None, ignore_index=-100, rows_list=None,
-              threads=None, lib=None):
+              threads=None, lib=None, want_q=False):
     """float64 log p at K gathered indices per row: [rows, K] (rows outside
-    rows_list, if given, are NaN) and the status."""
+    rows_list, if given, are NaN) and the status; with want_q also
+    q = 1 - p at each gathered index (0 for ignored entries and masked rows)."""
     lib = _load(lib)
     dt = _dtype_code(logits)
     stride = _check_2d(logits)
@@ -224,15 +231,54 @@ def topk_rows(logits, indices, temperature=1.0, row_mask=None, ignore_index=-100
     K = idx.shape[1]
     m = _mask(row_mask, rows)
     out = np.full((rows, K), np.nan)
+    q = np.full((rows, K), np.nan) if want_q else None
     threads = threads or default_threads()
 
     def work(rng):
         return lib.oracle_topk_rows(_ptr(logits), rows, vocab, stride, dt, _ptr(idx), K,
                                     idx.strides[0] // 8, int(ignore_index), float(temperature),
-                                    _ptr(m), rng[0], rng[1], _ptr(out))
+                                    _ptr(m), rng[0], rng[1], _ptr(out), _ptr(q))
 
     st = 0
     with ThreadPoolExecutor(threads) as ex:
         for s in ex.map(work, _ranges(rows, rows_list, threads)):
             st |= s
+    if want_q:
+        return out, q, st
     return out, st
+
+
+def topk_grad_rows(logits, indices, g, temperature=1.0, row_mask=None, ignore_index=-100, r0=0,
+                   r1=None, threads=None, lib=None):
+    """float64 gradient of sum_k g[r, k] log p_{i_k} for rows [r0, r1):
+    an array of shape [r1 - r0, vocab]."""
+    lib = _load(lib)
+    dt = _dtype_code(logits)
+    stride = _check_2d(logits)
+    rows, vocab = logits.shape
+    r1 = rows if r1 is None else r1
+    idx = np.asarray(indices, dtype=np.int64)
+    if idx.ndim != 2 or idx.shape[0] != rows or idx.strides[1] != 8:
+        raise ValueError("indices must be [rows, K] int64 with unit column stride")
+    K = idx.shape[1]
+    gg = np.ascontiguousarray(g, dtype=np.float64)
+    if gg.shape != (rows, K):
+        raise ValueError("g must be [rows, K]")
+    m = _mask(row_mask, rows)
+    out = np.empty((r1 - r0, vocab), dtype=np.float64)
+    threads = threads or default_threads()
+    n = r1 - r0
+    parts = _ranges(n, None, threads) if n > 0 else []
+
+    def work(rng):
+        a, b = rng
+        return lib.oracle_topk_grad_rows(_ptr(logits), rows, vocab, stride, dt, _ptr(idx), K,
+                                         idx.strides[0] // 8, int(ignore_index),
+                                         float(temperature), _ptr(m), _ptr(gg), r0 + a, r0 + b,
+                                         out[a:].ctypes.data)
+
+    st = 0
+    with ThreadPoolExecutor(threads) as ex:
+        for s in ex.map(work, parts):
+            st |= s
+    return out

@@ -126,16 +126,19 @@ static double lse_excluding(const void *row, int dtype, int64_t V, double T, int
  *
  *  - loss = -log p_t = softplus(u), u = lse_{j != t}(x) - x_t
  *    (Liger PR #1555, Summary, CE/FLCE bullet: loss from the sum without the
- *    target; Details: the fp64 reference form softplus(lse_others - x_y)).
+ *    target; Details: the fp64 reference form softplus(lse_others - x_y));
+ *    with label smoothing eps (the unsloth-zoo #2080 Summary quoted on the
+ *    Liger page keeps smoothing in the collapse-safe target term):
+ *    loss = (1 - eps)(-log p_t) + (eps / V) sum_j (-log p_j).
  *  - q = 1 - p_t = sigmoid(u) = s_others / d (same bullet: dx_y = -sum_others/d).
  *  - entropy H = -sum_j p_j log p_j, with log p_t = -loss and, for j != t,
  *    log p_j = x_j - lse, lse = x_t + loss.
  *  - argmax = lowest j with z_j = max_k z_k, compared on the stored values.
  */
 int oracle_ce_rows(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride, int dtype,
-                   const int64_t *labels, int64_t ignore_index, double T, const uint8_t *row_mask,
-                   int64_t r0, int64_t r1, double *logp, double *loss, double *entropy,
-                   int64_t *argmax, double *q)
+                   const int64_t *labels, int64_t ignore_index, double T, double eps,
+                   const uint8_t *row_mask, int64_t r0, int64_t r1, double *logp, double *loss,
+                   double *entropy, int64_t *argmax, double *q)
 {
     int st = 0;
     (void)rows;
@@ -154,7 +157,18 @@ int oracle_ce_rows(const void *logits, int64_t rows, int64_t vocab, int64_t row_
         double u = lse_excluding(row, dtype, vocab, T, t) - xt;
         double l = softplus(u);
         if (logp) logp[r] = -l;
-        if (loss) loss[r] = l;
+        if (loss) {
+            /* label smoothing: (1 - eps) (-log p_t) + eps * mean_j (-log p_j),
+             * with -log p_j = lse - x_j and lse = x_t + l */
+            double ls = 0.0;
+            if (eps != 0.0) {
+                double lse = xt + l;
+                for (int64_t j = 0; j < vocab; ++j)
+                    ls += lse - load_z(row, dtype, j) / T;
+                ls /= (double)vocab;
+            }
+            loss[r] = (1.0 - eps) * l + eps * ls;
+        }
         if (q) q[r] = sigmoid(u);
         if (entropy) {
             double lse = xt + l;
@@ -184,17 +198,17 @@ int oracle_ce_rows(const void *logits, int64_t rows, int64_t vocab, int64_t row_
 
 /*
  * Gradient rows [r0, r1) of the per-row loss with respect to the stored logits:
- * dl_j = (g_r / T) (p_j - [j == t]), with the target column taken as
- * -(g_r / T) q, q = 1 - p_t = sigmoid(u), so no 1 - p_t is ever formed by
- * subtraction (ms-swift PR #10353, PR information: backward as
+ * dl_j = (g_r / T) (p_j - (1 - eps) [j == t] - eps / V), with the target
+ * column taken as (g_r / T)(-q + eps - eps / V), q = 1 - p_t = sigmoid(u), so
+ * no 1 - p_t is ever formed by subtraction (ms-swift PR #10353, PR information: backward as
  * g*softmax - g*one_hot with zero weight for ignored labels; Liger PR #1555,
  * Summary: dx_y = -sum_others/d).  out has (r1 - r0) rows of vocab doubles;
  * ignored rows are all zero.
  */
 int oracle_ce_grad_rows(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride,
                         int dtype, const int64_t *labels, int64_t ignore_index, double T,
-                        const uint8_t *row_mask, const double *g, int64_t r0, int64_t r1,
-                        double *out)
+                        double eps, const uint8_t *row_mask, const double *g, int64_t r0,
+                        int64_t r1, double *out)
 {
     int st = 0;
     (void)rows;
@@ -211,8 +225,10 @@ int oracle_ce_grad_rows(const void *logits, int64_t rows, int64_t vocab, int64_t
         double u = lse_excluding(row, dtype, vocab, T, t) - xt;
         double lse = xt + softplus(u);
         double w = g[r] / T;
+        double ev = eps / (double)vocab;
         for (int64_t j = 0; j < vocab; ++j)
-            o[j] = j == t ? -w * sigmoid(u) : w * exp(load_z(row, dtype, j) / T - lse);
+            o[j] = j == t ? w * (-sigmoid(u) + eps - ev)
+                          : w * (exp(load_z(row, dtype, j) / T - lse) - ev);
     }
     return st;
 }
@@ -224,11 +240,14 @@ int oracle_ce_grad_rows(const void *logits, int64_t rows, int64_t vocab, int64_t
  * target: log p_k = -softplus(lse_{j != i_k}(x) - x_{i_k}).
  * idx is [rows, K] with row stride idx_stride; logp_out is [rows, K] dense.
  * An entry equal to ignore_index, and every entry of a masked row, gives 0.
- * An entry outside [0, V) gives 0 and sets ORACLE_BAD_INDEX.
+ * An entry outside [0, V) gives 0 and sets ORACLE_BAD_INDEX.  q_out (nullable,
+ * [rows, K]) receives 1 - p at each gathered index as sigmoid(u), 0 for
+ * entries that give 0.
  */
 int oracle_topk_rows(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride, int dtype,
                      const int64_t *idx, int64_t K, int64_t idx_stride, int64_t ignore_index,
-                     double T, const uint8_t *row_mask, int64_t r0, int64_t r1, double *logp_out)
+                     double T, const uint8_t *row_mask, int64_t r0, int64_t r1, double *logp_out,
+                     double *q_out)
 {
     int st = 0;
     (void)rows;
@@ -236,7 +255,7 @@ int oracle_topk_rows(const void *logits, int64_t rows, int64_t vocab, int64_t ro
         const void *row = row_ptr(logits, dtype, row_stride, r);
         for (int64_t k = 0; k < K; ++k) {
             int64_t i = idx[r * idx_stride + k];
-            double v = 0.0;
+            double v = 0.0, qk = 0.0;
             if (row_mask && row_mask[r] == 0) {
                 v = 0.0;
             } else if (i == ignore_index) {
@@ -246,9 +265,75 @@ int oracle_topk_rows(const void *logits, int64_t rows, int64_t vocab, int64_t ro
                 v = 0.0;
             } else {
                 double xi = load_z(row, dtype, i) / T;
-                v = -softplus(lse_excluding(row, dtype, vocab, T, i) - xi);
+                double u = lse_excluding(row, dtype, vocab, T, i) - xi;
+                v = -softplus(u);
+                qk = sigmoid(u);
             }
+            if (q_out)
+                q_out[r * K + k] = qk;
             logp_out[r * K + k] = v;
+        }
+    }
+    return st;
+}
+
+/*
+ * Gradient rows [r0, r1) of L = sum_k g[r, k] log p_{i_k} (the top-K
+ * selective log-softmax) with respect to the stored logits:
+ * dL/dz_j = (1/T) sum_k g_k ([j = i_k] - p_j).  At a gathered column j the
+ * two terms combine to (1/T)(G_j (1 - p_j) - p_j (Gs - G_j)), G_j the sum of
+ * the g_k gathered at j, Gs the sum over all valid entries; 1 - p_j is taken
+ * as sigmoid(lse_{m != j}(x) - x_j), never by subtraction (the same
+ * collapse-safe rule as the single target).  Ignored or out-of-range entries
+ * contribute nothing; masked rows are zero.  g is [rows, K] dense; out has
+ * (r1 - r0) rows of vocab doubles.
+ */
+int oracle_topk_grad_rows(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride,
+                          int dtype, const int64_t *idx, int64_t K, int64_t idx_stride,
+                          int64_t ignore_index, double T, const uint8_t *row_mask,
+                          const double *g, int64_t r0, int64_t r1, double *out)
+{
+    int st = 0;
+    (void)rows;
+    for (int64_t r = r0; r < r1; ++r) {
+        const void *row = row_ptr(logits, dtype, row_stride, r);
+        double *o = out + (size_t)(r - r0) * (size_t)vocab;
+        for (int64_t j = 0; j < vocab; ++j)
+            o[j] = 0.0;
+        if (row_mask && row_mask[r] == 0)
+            continue;
+        double gs = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t i = idx[r * idx_stride + k];
+            if (i == ignore_index)
+                continue;
+            if (i < 0 || i >= vocab) {
+                st |= ORACLE_BAD_INDEX;
+                continue;
+            }
+            gs += g[r * K + k];
+        }
+        double lse = lse_excluding(row, dtype, vocab, T, -1);
+        for (int64_t j = 0; j < vocab; ++j)
+            o[j] = -(gs / T) * exp(load_z(row, dtype, j) / T - lse);
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t i = idx[r * idx_stride + k];
+            if (i == ignore_index || i < 0 || i >= vocab)
+                continue;
+            int first = 1;
+            for (int64_t k2 = 0; k2 < k; ++k2)
+                if (idx[r * idx_stride + k2] == i)
+                    first = 0;
+            if (!first)
+                continue;
+            double gj = 0.0;
+            for (int64_t k2 = k; k2 < K; ++k2)
+                if (idx[r * idx_stride + k2] == i)
+                    gj += g[r * K + k2];
+            double xi = load_z(row, dtype, i) / T;
+            double qj = sigmoid(lse_excluding(row, dtype, vocab, T, i) - xi);
+            double pj = exp(xi - lse);
+            o[i] = (gj * qj - pj * (gs - gj)) / T;
         }
     }
     return st;

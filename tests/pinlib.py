@@ -284,6 +284,109 @@ def check_strided(lib=None):
         assert rel(a["logp"][r], ref["logp"]) < 1e-13
 
 
-ALL_CHECKS = [check_strided, check_uniform, check_peaked_closed_form, check_two_class, check_single_class,
+def mp_smoothed(z, t, T, eps, g=1.0):
+    """120-digit label-smoothed loss (1-eps)(-log p_t) + (eps/V) sum_j (-log p_j)
+    and its gradient (g/T)(p_j - (1-eps)[j = t] - eps/V), unshifted."""
+    ref = mp_row(z, t, T, g)
+    V = len(z)
+    e = mp.mpf(eps)
+    loss = (1 - e) * ref["loss"] + e * mp.fsum(-lp for lp in ref["logp_all"]) / V
+    w = mp.mpf(g) / mp.mpf(T)
+    p = [mp.e ** lp for lp in ref["logp_all"]]
+    dl = [w * (p[j] - (1 - e) * (1 if j == t else 0) - e / V) for j in range(V)]
+    return loss, dl
+
+
+def check_label_smoothing(lib=None):
+    """Smoothed loss and gradient: 120-digit brute force on random and peaked
+    rows, the uniform-row closed form (loss = log V for any eps), zero row
+    sums, and central differences of the smoothed loss."""
+    for kind, z in _brute_rows(17):
+        V = z.shape[0]
+        stored = bf16_to_f32(z) if z.dtype == np.uint16 else z
+        t = int(kind[4:]) if kind.startswith("f32p") else V // 3
+        for T, eps in ((1.0, 0.1), (0.7, 0.3)):
+            loss, dl = mp_smoothed(stored, t, T, eps, g=0.75)
+            o = oracle.ce_rows(z[None, :], np.array([t]), T, lib=lib, threads=1,
+                               label_smoothing=eps)
+            assert rel(o["loss"][0], loss) < 1e-13, (kind, T, eps)
+            ref = mp_row(stored, t, T)
+            assert rel(o["logp"][0], ref["logp"]) < 1e-13   # log p is not smoothed
+            d = oracle.ce_grad_rows(z[None, :], np.array([t]), np.array([0.75]), T, lib=lib,
+                                    threads=1, label_smoothing=eps)[0]
+            for j in range(V):
+                assert abs(d[j] - float(dl[j])) <= 1e-12 * (abs(float(dl[j])) + eps / V), \
+                    (kind, T, eps, j)
+            assert abs(d.sum()) <= 1e-13 * np.abs(d).sum()
+    for V in (5, 1000):
+        z = np.full((1, V), -2.5, dtype=np.float32)
+        o = oracle.ce_rows(z, np.array([1]), 0.9, lib=lib, threads=1, label_smoothing=0.2)
+        assert rel(o["loss"][0], math.log(V)) < 1e-13
+    rng = np.random.default_rng(3)
+    z = (rng.standard_normal(7) * 2).astype(np.float32)
+    d = oracle.ce_grad_rows(z[None, :], np.array([2]), np.array([1.0]), 0.8, lib=lib, threads=1,
+                            label_smoothing=0.25)[0]
+    for j in range(7):
+        def f(h, j=j):
+            zz = [mp.mpf(float(v)) for v in z]
+            zz[j] += h
+            x = [v / mp.mpf(0.8) for v in zz]
+            lse = mp.log(mp.fsum(mp.e ** xi for xi in x))
+            return mp.mpf(0.75) * (lse - x[2]) + mp.mpf(0.25) * mp.fsum(lse - xi for xi in x) / 7
+        assert rel(d[j], mp.diff(f, 0)) < 1e-12, j
+
+
+def mp_topk_grad(z, idx, gk, T):
+    """Gradient of sum_k g_k log p_{i_k} at 120 digits: (1/T) sum_k g_k([j = i_k] - p_j)."""
+    ref = mp_row(z, 0, T)
+    p = [mp.e ** lp for lp in ref["logp_all"]]
+    V = len(z)
+    out = [mp.mpf(0)] * V
+    for i, g in zip(idx, gk):
+        for j in range(V):
+            out[j] += mp.mpf(g) * ((1 if j == i else 0) - p[j]) / mp.mpf(T)
+    return out, ref
+
+
+def check_topk_grad(lib=None):
+    """Top-K gradient and q = 1 - p at gathered columns: 120-digit brute force
+    on random and peaked rows with duplicate and ignored entries, and central
+    differences of sum_k g_k log p_{i_k}."""
+    rng = np.random.default_rng(29)
+    for kind, z in _brute_rows(23):
+        V = z.shape[0]
+        stored = bf16_to_f32(z) if z.dtype == np.uint16 else z
+        top = int(np.argmax(stored))
+        idx = np.array([[top, (top + 1) % V, top, -100, (top + 3) % V]], dtype=np.int64)
+        gk = rng.standard_normal((1, 5))
+        for T in (1.0, 0.7):
+            want, ref = mp_topk_grad(stored, [i for i in idx[0] if i != -100],
+                                     [g for i, g in zip(idx[0], gk[0]) if i != -100], T)
+            d = oracle.topk_grad_rows(z[None, :], idx, gk, T, lib=lib, threads=1)[0]
+            for j in range(V):
+                assert abs(d[j] - float(want[j])) <= 1e-12 * max(abs(float(want[j])), 1e-300), \
+                    (kind, T, j, d[j], want[j])
+            lp, q, _ = oracle.topk_rows(z[None, :], idx, T, lib=lib, threads=1, want_q=True)
+            for k in range(5):
+                if idx[0, k] == -100:
+                    assert q[0, k] == 0 and lp[0, k] == 0
+                else:
+                    pk = mp.e ** ref["logp_all"][idx[0, k]]
+                    assert rel(q[0, k], 1 - pk) < 1e-13, (kind, k)
+    z = (rng.standard_normal(6) * 2).astype(np.float32)
+    idx = np.array([[1, 4, 1]], dtype=np.int64)
+    gk = np.array([[0.5, -1.25, 2.0]])
+    d = oracle.topk_grad_rows(z[None, :], idx, gk, 0.9, lib=lib, threads=1)[0]
+    for j in range(6):
+        def f(h, j=j):
+            zz = [mp.mpf(float(v)) for v in z]
+            zz[j] += h
+            x = [v / mp.mpf(0.9) for v in zz]
+            lse = mp.log(mp.fsum(mp.e ** xi for xi in x))
+            return sum(mp.mpf(g) * (x[i] - lse) for i, g in zip(idx[0], gk[0]))
+        assert rel(d[j], mp.diff(f, 0)) < 1e-12, j
+
+
+ALL_CHECKS = [check_label_smoothing, check_topk_grad, check_strided, check_uniform, check_peaked_closed_form, check_two_class, check_single_class,
               check_bruteforce, check_central_difference, check_invariants,
               check_library_routines]

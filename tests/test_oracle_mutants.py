@@ -27,15 +27,24 @@ MUTANTS = [
     ("entropy_drops_target_term", "double h = exp(-l) * l;", "double h = 0.0;"),
     ("entropy_sign", "h += exp(x - lse) * (lse - x);", "h += exp(x - lse) * (x - lse);"),
     ("argmax_last_tie", "if (z > best) {", "if (z >= best) {"),
-    ("grad_target_sign", "-w * sigmoid(u)", "w * sigmoid(u)"),
+    ("grad_target_sign", "w * (-sigmoid(u) + eps - ev)", "w * (sigmoid(u) + eps - ev)"),
     ("grad_drops_chain_rule", "double w = g[r] / T;", "double w = g[r];"),
-    ("grad_other_index", "w * exp(load_z(row, dtype, j) / T - lse)",
-     "w * exp(load_z(row, dtype, vocab - 1 - j) / T - lse)"),
+    ("grad_other_index", "w * (exp(load_z(row, dtype, j) / T - lse) - ev)",
+     "w * (exp(load_z(row, dtype, vocab - 1 - j) / T - lse) - ev)"),
     ("bf16_widen_shift", "<< 16;", "<< 15;"),
     ("row_stride_ignored", "(size_t)r * (size_t)row_stride * esz", "(size_t)r * (size_t)1 * esz"),
-    ("topk_no_exclusion", "v = -softplus(lse_excluding(row, dtype, vocab, T, i) - xi);",
-     "v = -softplus(lse_excluding(row, dtype, vocab, T, -1) - xi);"),
-    ("topk_row_index", "int64_t i = idx[r * idx_stride + k];", "int64_t i = idx[k * idx_stride + r % 1];"),
+    ("topk_no_exclusion", "double u = lse_excluding(row, dtype, vocab, T, i) - xi;\n                v",
+     "double u = lse_excluding(row, dtype, vocab, T, -1) - xi;\n                v"),
+    ("smoothing_scale", "loss[r] = (1.0 - eps) * l + eps * ls;", "loss[r] = (1.0 - eps) * l + ls;"),
+    ("smoothing_term_sign", "ls += lse - load_z(row, dtype, j) / T;", "ls += load_z(row, dtype, j) / T - lse;"),
+    ("smoothing_grad_target", "w * (-sigmoid(u) + eps - ev)", "w * (-sigmoid(u) + eps)"),
+    ("smoothing_grad_other", "/ T - lse) - ev)", "/ T - lse))"),
+    ("topk_q_sign", "qk = sigmoid(u);", "qk = sigmoid(-u);"),
+    ("topk_grad_gathered", "o[i] = (gj * qj - pj * (gs - gj)) / T;", "o[i] = (gj * qj - pj * gs) / T;"),
+    ("topk_grad_other_sign", "o[j] = -(gs / T) * exp(", "o[j] = (gs / T) * exp("),
+    ("topk_grad_dup", "for (int64_t k2 = k; k2 < K; ++k2)", "for (int64_t k2 = k; k2 < k + 1; ++k2)"),
+    ("topk_row_index", "int64_t i = idx[r * idx_stride + k];\n            double v = 0.0, qk",
+     "int64_t i = idx[k * idx_stride + r % 1];\n            double v = 0.0, qk"),
     ("mask_inverted", "if (row_mask && row_mask[r] == 0)\n        return 0;",
      "if (row_mask && row_mask[r] != 0)\n        return 0;"),
 ]
