@@ -58,6 +58,95 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
+def _counter_means(csv_path, counter):
+    """Mean value per dispatch of one rocprofv3 counter, by kernel name."""
+    import csv
+    acc = {}
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter:
+                acc.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return {k: float(np.mean(v)) for k, v in acc.items()}
+
+
+def write_traffic(fetch_csv, write_csv, rows=8192, vocab=152064):
+    """Turn the two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE, of
+    `bench.py --copy-calibration`) into HBM bytes per launch: each counter is
+    scaled by what it reads for torch's float32 add over exactly 2^30 bytes in
+    and 2^30 bytes out.  Writes the backward's figures to the traffic file and
+    prints a table of every kernel of the step."""
+    import workloads
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+    cal = [k for k in fetch if "vectorized_elementwise_kernel" in k and "_add" in k]
+    if len(cal) != 1:
+        raise SystemExit(f"calibration kernel not found exactly once: {cal}")
+    true = float(2 ** 30)
+    f_scale = true / (fetch[cal[0]] * 1024.0)
+    w_scale = true / (write[cal[0]] * 1024.0)
+    _, labels, mask, _ = workloads.grpo_rows(rows, vocab)
+    n_valid = int(((labels != -100) & (mask != 0)).sum())
+    ES = 2
+    algo = {"k_backward": (n_valid * vocab * ES, rows * vocab * ES),
+            "k_sls_sweep": (n_valid * vocab * ES, 0),
+            "k_fused_stream": (n_valid * vocab * ES, rows * vocab * ES)}
+    table = []
+    backward = None
+    for name in sorted(fetch):
+        short = name.replace("void ", "").replace("cev::(anonymous namespace)::", "").split("(")[0]
+        key = next((k for k in algo if short.startswith(k)), None)
+        rd = fetch[name] * 1024.0 * f_scale
+        wr = write.get(name, 0.0) * 1024.0 * w_scale
+        entry = {"kernel": short, "fetch_kib": fetch[name], "write_kib": write.get(name),
+                 "read_bytes": rd, "write_bytes": wr}
+        if key:
+            a_rd, a_wr = algo[key]
+            entry.update(algorithmic_read=a_rd, algorithmic_write=a_wr,
+                         ratio=(rd + wr) / (a_rd + a_wr))
+            if key == "k_backward":
+                backward = (name, entry)
+        table.append(entry)
+    if backward is None:
+        raise SystemExit("no k_backward dispatch in the counter runs")
+    name, e = backward
+    out = {
+        "kernel": name,
+        "workload": f"grpo-shaped {rows}x{vocab} bf16, {n_valid} valid rows",
+        "kernel_source_sha": kernel_source_hash(),
+        "kernel_sources": KERNEL_SOURCES,
+        "fetch_size_kib_per_dispatch": e["fetch_kib"],
+        "write_size_kib_per_dispatch": e["write_kib"],
+        "calibration": {"kernel": "torch float32 add over 2^28 elements", "true_read_bytes": 2 ** 30,
+                        "true_write_bytes": 2 ** 30, "fetch_size_kib": fetch[cal[0]],
+                        "write_size_kib": write[cal[0]], "fetch_scale": f_scale,
+                        "write_scale": w_scale},
+        "read_bytes_per_launch": e["read_bytes"],
+        "write_bytes_per_launch": e["write_bytes"],
+        "bytes_per_launch": e["read_bytes"] + e["write_bytes"],
+        "algorithmic_bytes_per_launch": e["algorithmic_read"] + e["algorithmic_write"],
+        "traffic_over_algorithmic": e["ratio"],
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/prof_fetch -o grpo -- "
+            "python bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/prof_write -o grpo -- "
+            "python bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration",
+            "python bench.py --traffic-from <out>/prof_fetch/grpo_counter_collection.csv "
+            "<out>/prof_write/grpo_counter_collection.csv"],
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=2)
+        f.write("\n")
+    print(f"scales: fetch {f_scale:.4f}, write {w_scale:.4f}")
+    print("| Kernel | FETCH_SIZE (KiB/dispatch) | WRITE_SIZE (KiB/dispatch) | Read bytes | "
+          "Written bytes | Algorithmic bytes | Measured / algorithmic |")
+    print("|---|---|---|---|---|---|---|")
+    for e in table:
+        a = e.get("algorithmic_read", 0) + e.get("algorithmic_write", 0)
+        print(f"| {e['kernel']} | {e['fetch_kib']:.0f} | {e['write_kib'] or 0:.0f} | "
+              f"{e['read_bytes']:.4e} | {e['write_bytes']:.4e} | {a:.4e} | "
+              f"{e.get('ratio', float('nan')):.4f} |")
+
+
 def cpu_baseline(w, valid_rows, seconds=12.0, threads=None):
     """The fp64 oracle (as it stands) on a bounded sample of the same rows:
     forward (log p, loss, argmax) plus the gradient rows, chunk by chunk."""
@@ -101,7 +190,13 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain elementwise kernel over 1 GiB in / 1 GiB out, "
                          "the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn the two counter runs' csv files into the "
+                         "committed traffic figures and print the counter table")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from, rows=args.rows, vocab=args.vocab)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(rows shard across GPUs with no communication; see the design notes).",
@@ -207,8 +302,8 @@ def main():
                      "kernel": "k_backward (ce_backward)", "bytes_per_launch": bwd_bytes},
         "cpu_baseline": None,
         "fused": {"entry": "ce_fused: the same outputs in one call for a g known up front; "
-                           "each valid row read once from HBM, re-read from the Infinity "
-                           "Cache, every dlogits row written once",
+                           "each valid row swept once and re-read at once (largely from the "
+                           "Infinity Cache), every dlogits row written once",
                   "ms_per_step": fused_wall, "kernel_ms": fused_ms,
                   "rows_per_s": R / (fused_wall / 1e3),
                   "algorithmic_bytes": fwd_bytes + R * V * ES,

@@ -16,8 +16,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["sls_forward", "sls_topk_forward", "ce_forward", "ce_backward", "ce_fused",
-           "workspace_size",
+__all__ = ["sls_forward", "sls_topk_forward", "sls_topk_backward", "ce_forward",
+           "ce_backward", "ce_fused", "workspace_size",
            "status_string", "version", "CEV_F32", "CEV_BF16", "STATUS_BAD_LABEL",
            "STATUS_BAD_INDEX", "SAVED_BYTES", "CevError"]
 
@@ -125,11 +125,7 @@ def sls_forward(logits, labels, temperature=1.0, row_mask=None, ignore_index=-10
     return out
 
 
-def sls_topk_forward(logits, indices, temperature=1.0, row_mask=None, ignore_index=-100,
-                     status=None):
-    """log p at K gathered indices per row: fp32 [rows, K]."""
-    rows, vocab, stride = _check_logits(logits)
-    dev = logits.device
+def _indices(indices, rows, dev):
     if indices.dim() != 2 or indices.shape[0] != rows or indices.dtype != torch.int64:
         raise ValueError("indices must be int64 [rows, K]")
     if not indices.is_cuda or indices.device != dev:
@@ -138,19 +134,67 @@ def sls_topk_forward(logits, indices, temperature=1.0, row_mask=None, ignore_ind
     if rows > 1 and K > 1 and indices.stride(1) != 1:
         raise ValueError("indices must have unit column stride")
     istride = indices.stride(0) if rows > 1 else K
+    return K, max(istride, K)
+
+
+def sls_topk_forward(logits, indices, temperature=1.0, row_mask=None, ignore_index=-100,
+                     status=None, saved=False):
+    """log p at K gathered indices per row: fp32 [rows, K].  With saved=True
+    returns (logp, q, saved): q = 1 - p at each index [rows, K] and the per-row
+    record [rows, 16] that sls_topk_backward takes."""
+    rows, vocab, stride = _check_logits(logits)
+    dev = logits.device
+    K, istride = _indices(indices, rows, dev)
     m = _mask(row_mask, rows, dev)
     _dev(status, "status", torch.int32, (1,), dev)
     logp = torch.empty((rows, K), dtype=torch.float32, device=dev)
+    q = torch.empty((rows, K), dtype=torch.float32, device=dev) if saved else None
+    sv = torch.empty((rows, SAVED_BYTES), dtype=torch.uint8, device=dev) if saved else None
     rc = _lib.get().sls_topk_forward(_ptr(logits), rows, vocab, stride, _dtype_code(logits),
-                                     _ptr(indices), K, max(istride, K), int(ignore_index),
-                                     float(temperature), _ptr(m), _ptr(logp), _ptr(status),
-                                     _stream(dev))
+                                     _ptr(indices), K, istride, int(ignore_index),
+                                     float(temperature), _ptr(m), _ptr(logp), _ptr(q), _ptr(sv),
+                                     _ptr(status), _stream(dev))
     _check("sls_topk_forward", rc)
-    return logp
+    return (logp, q, sv) if saved else logp
+
+
+def sls_topk_backward(logits, indices, g, saved, q, temperature=1.0, row_mask=None,
+                      ignore_index=-100, dlogits=None, status=None):
+    """Gradient of sum_k g[r, k] logp[r, k] with respect to logits, in the
+    logits dtype; `saved` and `q` come from sls_topk_forward(saved=True)."""
+    rows, vocab, stride = _check_logits(logits)
+    dev = logits.device
+    K, istride = _indices(indices, rows, dev)
+    _dev(g, "g", torch.float32, (rows, K), dev)
+    _dev(q, "q", torch.float32, (rows, K), dev)
+    _dev(saved, "saved", torch.uint8, (rows, SAVED_BYTES), dev)
+    m = _mask(row_mask, rows, dev)
+    _dev(status, "status", torch.int32, (1,), dev)
+    dlogits, dstride = _dlogits(dlogits, logits, rows, vocab, dev)
+    rc = _lib.get().sls_topk_backward(_ptr(logits), rows, vocab, stride, _dtype_code(logits),
+                                      _ptr(indices), K, istride, int(ignore_index),
+                                      float(temperature), _ptr(m), _ptr(g), _ptr(saved), _ptr(q),
+                                      _ptr(dlogits), dstride, _ptr(status), _stream(dev))
+    _check("sls_topk_backward", rc)
+    return dlogits
+
+
+def _dlogits(dlogits, logits, rows, vocab, dev):
+    if dlogits is None:
+        dlogits = torch.empty((rows, vocab), dtype=logits.dtype, device=dev)
+    else:
+        if dlogits.dtype != logits.dtype or tuple(dlogits.shape) != (rows, vocab):
+            raise ValueError("dlogits must match logits in dtype and shape")
+        if not dlogits.is_cuda or dlogits.device != dev:
+            raise ValueError(f"dlogits must be on {dev}")
+        if rows > 0 and vocab > 1 and dlogits.stride(1) != 1:
+            raise ValueError("dlogits must have unit column stride")
+    return dlogits, max(dlogits.stride(0) if rows > 1 else vocab, vocab)
 
 
 def ce_forward(logits, labels, temperature=1.0, row_mask=None, ignore_index=-100, logp=True,
-               entropy=False, argmax=False, valid_rows=True, status=None, out=None):
+               entropy=False, argmax=False, valid_rows=True, status=None, out=None,
+               label_smoothing=0.0):
     """Per-row cross-entropy forward with device-side compaction of the valid
     rows.  Returns a dict: loss [rows] fp32, saved [rows, 16] uint8 (for
     ce_backward), and optionally logp, entropy, argmax, valid_rows [rows] int64
@@ -186,7 +230,8 @@ def ce_forward(logits, labels, temperature=1.0, row_mask=None, ignore_index=-100
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     o["workspace"] = ws
     rc = _lib.get().ce_forward(_ptr(logits), rows, vocab, stride, _dtype_code(logits),
-                               _ptr(labels), int(ignore_index), float(temperature), _ptr(m),
+                               _ptr(labels), int(ignore_index), float(temperature),
+                               float(label_smoothing), _ptr(m),
                                _ptr(o["loss"]), _ptr(o["saved"]), _ptr(o["logp"]),
                                _ptr(o["entropy"]), _ptr(o["argmax"]), _ptr(o["valid_rows"]),
                                _ptr(o["n_valid"]), _ptr(ws), ws_bytes, _ptr(status),
@@ -196,9 +241,10 @@ def ce_forward(logits, labels, temperature=1.0, row_mask=None, ignore_index=-100
 
 
 def ce_backward(logits, labels, g, saved, temperature=1.0, row_mask=None, ignore_index=-100,
-                dlogits=None, status=None):
-    """dlogits = (g/T)(softmax(logits/T) - onehot(labels)) per valid row, zero
-    rows elsewhere, in the logits dtype."""
+                dlogits=None, status=None, label_smoothing=0.0):
+    """dlogits = (g/T)(softmax(logits/T) - onehot(labels)) per valid row (with
+    label smoothing eps: minus (g/T) eps (1/V - onehot)), zero rows elsewhere,
+    in the logits dtype."""
     rows, vocab, stride = _check_logits(logits)
     dev = logits.device
     _dev(labels, "labels", torch.int64, (rows,), dev)
@@ -206,16 +252,10 @@ def ce_backward(logits, labels, g, saved, temperature=1.0, row_mask=None, ignore
     _dev(saved, "saved", torch.uint8, (rows, SAVED_BYTES), dev)
     m = _mask(row_mask, rows, dev)
     _dev(status, "status", torch.int32, (1,), dev)
-    if dlogits is None:
-        dlogits = torch.empty((rows, vocab), dtype=logits.dtype, device=dev)
-    else:
-        if dlogits.dtype != logits.dtype or tuple(dlogits.shape) != (rows, vocab):
-            raise ValueError("dlogits must match logits in dtype and shape")
-        if rows > 0 and vocab > 1 and dlogits.stride(1) != 1:
-            raise ValueError("dlogits must have unit column stride")
-    dstride = max(dlogits.stride(0) if rows > 1 else vocab, vocab)
+    dlogits, dstride = _dlogits(dlogits, logits, rows, vocab, dev)
     rc = _lib.get().ce_backward(_ptr(logits), rows, vocab, stride, _dtype_code(logits),
-                                _ptr(labels), int(ignore_index), float(temperature), _ptr(m),
+                                _ptr(labels), int(ignore_index), float(temperature),
+                                float(label_smoothing), _ptr(m),
                                 _ptr(g), _ptr(saved), _ptr(dlogits), dstride, _ptr(status),
                                 _stream(dev))
     _check("ce_backward", rc)
@@ -223,10 +263,10 @@ def ce_backward(logits, labels, g, saved, temperature=1.0, row_mask=None, ignore
 
 
 def ce_fused(logits, labels, g, temperature=1.0, row_mask=None, ignore_index=-100, logp=True,
-             entropy=False, argmax=False, valid_rows=False, dlogits=None, status=None, out=None):
-    """ce_forward and ce_backward in one call for a g known up front (one HBM
-    pass when the row fits in a compute unit's registers).  Returns the
-    ce_forward dict plus "dlogits"."""
+             entropy=False, argmax=False, valid_rows=False, dlogits=None, status=None, out=None,
+             label_smoothing=0.0):
+    """ce_forward and ce_backward in one call for a g known up front (each row
+    read from HBM about once).  Returns the ce_forward dict plus "dlogits"."""
     rows, vocab, stride = _check_logits(logits)
     dev = logits.device
     _dev(labels, "labels", torch.int64, (rows,), dev)
@@ -252,21 +292,16 @@ def ce_fused(logits, labels, g, temperature=1.0, row_mask=None, ignore_index=-10
     want("n_valid", valid_rows, torch.int64, (1,))
     if dlogits is None:
         dlogits = o.get("dlogits")
-    if dlogits is None:
-        dlogits = torch.empty((rows, vocab), dtype=logits.dtype, device=dev)
-    elif dlogits.dtype != logits.dtype or tuple(dlogits.shape) != (rows, vocab):
-        raise ValueError("dlogits must match logits in dtype and shape")
-    elif rows > 0 and vocab > 1 and dlogits.stride(1) != 1:
-        raise ValueError("dlogits must have unit column stride")
+    dlogits, dstride = _dlogits(dlogits, logits, rows, vocab, dev)
     o["dlogits"] = dlogits
-    dstride = max(dlogits.stride(0) if rows > 1 else vocab, vocab)
     ws_bytes = workspace_size(rows, vocab, _dtype_code(logits))
     ws = o.get("workspace")
     if ws is None or ws.numel() < ws_bytes:
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     o["workspace"] = ws
     rc = _lib.get().ce_fused(_ptr(logits), rows, vocab, stride, _dtype_code(logits),
-                             _ptr(labels), int(ignore_index), float(temperature), _ptr(m), _ptr(g),
+                             _ptr(labels), int(ignore_index), float(temperature),
+                             float(label_smoothing), _ptr(m), _ptr(g),
                              _ptr(o["loss"]), _ptr(o["saved"]), _ptr(o["logp"]),
                              _ptr(o["entropy"]), _ptr(o["argmax"]), _ptr(dlogits), dstride,
                              _ptr(o["valid_rows"]), _ptr(o["n_valid"]), _ptr(ws), ws_bytes,

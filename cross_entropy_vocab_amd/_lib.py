@@ -20,11 +20,14 @@ SZ = ctypes.c_size_t
 # name -> (restype, argtypes), mirroring include/cevocab.h
 SIGNATURES = {
     "sls_forward": (I32, [P, I64, I64, I64, I32, P, I64, D, P, P, P, P, P, P]),
-    "sls_topk_forward": (I32, [P, I64, I64, I64, I32, P, I64, I64, I64, D, P, P, P, P]),
-    "ce_forward": (I32, [P, I64, I64, I64, I32, P, I64, D, P, P, P, P, P, P, P, P, P, SZ, P, P]),
-    "ce_backward": (I32, [P, I64, I64, I64, I32, P, I64, D, P, P, P, P, I64, P, P]),
-    "ce_fused": (I32, [P, I64, I64, I64, I32, P, I64, D, P, P, P, P, P, P, P, P, I64, P, P, P, SZ,
-                       P, P]),
+    "sls_topk_forward": (I32, [P, I64, I64, I64, I32, P, I64, I64, I64, D, P, P, P, P, P, P]),
+    "sls_topk_backward": (I32, [P, I64, I64, I64, I32, P, I64, I64, I64, D, P, P, P, P, P, I64,
+                                P, P]),
+    "ce_forward": (I32, [P, I64, I64, I64, I32, P, I64, D, D, P, P, P, P, P, P, P, P, P, SZ, P,
+                         P]),
+    "ce_backward": (I32, [P, I64, I64, I64, I32, P, I64, D, D, P, P, P, P, I64, P, P]),
+    "ce_fused": (I32, [P, I64, I64, I64, I32, P, I64, D, D, P, P, P, P, P, P, P, P, I64, P, P, P,
+                       SZ, P, P]),
     "cev_workspace_size": (SZ, [I64, I64, I32]),
     "cev_status_string": (ctypes.c_char_p, [I32]),
     "cev_version": (I32, []),

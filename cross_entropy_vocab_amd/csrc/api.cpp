@@ -66,6 +66,18 @@ void fill_temperature(SweepArgs &a, double temperature)
 
 int launch_status(hipError_t e) { return e == hipSuccess ? CEV_OK : CEV_ELAUNCH; }
 
+bool smoothing_ok(double eps) { return std::isfinite(eps) && eps >= 0.0 && eps <= 1.0; }
+
+// dlogits must not overlap logits (the kernels read a row after other
+// workgroups may have written theirs).
+bool overlaps(const void *logits, int64_t row_stride, const void *dlogits, int64_t d_row_stride,
+              int64_t rows, int64_t vocab, int es)
+{
+    const uintptr_t l0 = (uintptr_t)logits, l1 = l0 + (uintptr_t)(((rows - 1) * row_stride + vocab) * es);
+    const uintptr_t d0 = (uintptr_t)dlogits, d1 = d0 + (uintptr_t)(((rows - 1) * d_row_stride + vocab) * es);
+    return l0 < d1 && d0 < l1;
+}
+
 } // namespace
 
 extern "C" {
@@ -105,7 +117,7 @@ int sls_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_str
 int sls_topk_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride,
                      int dtype, const int64_t *indices, int64_t K, int64_t index_row_stride,
                      int64_t ignore_index, double temperature, const uint8_t *row_mask,
-                     float *logp, int32_t *status, cev_stream_t stream)
+                     float *logp, float *q, void *saved, int32_t *status, cev_stream_t stream)
 {
     if (K < 1 || K > kMaxK)
         return CEV_ESHAPE;
@@ -117,7 +129,8 @@ int sls_topk_forward(const void *logits, int64_t rows, int64_t vocab, int64_t ro
         return rc;
     if (!indices || !logp)
         return CEV_ENULL;
-    if (!aligned(indices, 8) || !aligned(logp, 4) || !aligned(status, 4))
+    if (!aligned(indices, 8) || !aligned(logp, 4) || !aligned(q, 4) || !aligned(saved, 16) ||
+        !aligned(status, 4))
         return CEV_EALIGN;
     SweepArgs a{};
     a.logits = logits;
@@ -132,8 +145,57 @@ int sls_topk_forward(const void *logits, int64_t rows, int64_t vocab, int64_t ro
     a.row_mask = row_mask;
     fill_temperature(a, temperature);
     a.logp = logp;
+    a.q = q;
+    a.saved = static_cast<cev_saved *>(saved);
     a.status = status;
     return launch_status(cev::launch_topk_sweep(dtype, a, to_hip(stream)));
+}
+
+int sls_topk_backward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride,
+                      int dtype, const int64_t *indices, int64_t K, int64_t index_row_stride,
+                      int64_t ignore_index, double temperature, const uint8_t *row_mask,
+                      const float *g, const void *saved, const float *q, void *dlogits,
+                      int64_t dlogits_row_stride, int32_t *status, cev_stream_t stream)
+{
+    if (K < 1 || K > kMaxK)
+        return CEV_ESHAPE;
+    if (index_row_stride < K)
+        return CEV_ESTRIDE;
+    bool done;
+    int rc = check_common(logits, rows, vocab, row_stride, dtype, temperature, &done);
+    if (rc != CEV_OK || done)
+        return rc;
+    if (dlogits_row_stride < vocab)
+        return CEV_ESTRIDE;
+    if (dlogits_row_stride > INT64_MAX / 4 / rows || index_row_stride > INT64_MAX / 8 / rows)
+        return CEV_ESHAPE;
+    if (!indices || !g || !saved || !q || !dlogits)
+        return CEV_ENULL;
+    const int es = elem_size(dtype);
+    if (!aligned(indices, 8) || !aligned(g, 4) || !aligned(saved, 16) || !aligned(q, 4) ||
+        !aligned(dlogits, (uintptr_t)es) || !aligned(status, 4))
+        return CEV_EALIGN;
+    if (overlaps(logits, row_stride, dlogits, dlogits_row_stride, rows, vocab, es))
+        return CEV_EALIAS;
+    cev::TopkBackwardArgs a{};
+    a.logits = logits;
+    a.rows = rows;
+    a.vocab = vocab;
+    a.row_stride = row_stride;
+    a.indices = indices;
+    a.K = K;
+    a.index_row_stride = index_row_stride;
+    a.ignore_index = ignore_index;
+    a.row_mask = row_mask;
+    a.g = g;
+    a.saved = static_cast<const cev_saved *>(saved);
+    a.q = q;
+    a.dlogits = dlogits;
+    a.d_row_stride = dlogits_row_stride;
+    a.c = (float)(1.4426950408889634074 / temperature);
+    a.inv_t = (float)(1.0 / temperature);
+    a.status = status;
+    return launch_status(cev::launch_topk_backward(dtype, a, to_hip(stream)));
 }
 
 // Workspace of ce_forward: the compacted row list and its count, then (for
@@ -154,13 +216,18 @@ size_t cev_workspace_size(int64_t rows, int64_t vocab, int dtype)
 
 int ce_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride, int dtype,
                const int64_t *labels, int64_t ignore_index, double temperature,
-               const uint8_t *row_mask, float *loss, void *saved, float *logp, float *entropy,
-               int64_t *argmax, int64_t *valid_rows, int64_t *n_valid, void *workspace,
-               size_t workspace_bytes, int32_t *status, cev_stream_t stream)
+               double label_smoothing, const uint8_t *row_mask, float *loss, void *saved,
+               float *logp, float *entropy, int64_t *argmax, int64_t *valid_rows,
+               int64_t *n_valid, void *workspace, size_t workspace_bytes, int32_t *status,
+               cev_stream_t stream)
 {
     bool done;
     int rc = check_common(logits, rows, vocab, row_stride, dtype, temperature, &done);
-    if (rc != CEV_OK || done)
+    if (rc != CEV_OK)
+        return rc;
+    if (!smoothing_ok(label_smoothing))
+        return CEV_ESMOOTH;
+    if (done)
         return rc;
     if (!labels || !loss || !saved)
         return CEV_ENULL;
@@ -224,6 +291,7 @@ int ce_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stri
     a.splits = splits;
     a.partials = partials;
     fill_temperature(a, temperature);
+    a.label_smoothing = label_smoothing;
     a.logp = logp;
     a.loss = loss;
     a.entropy = entropy;
@@ -236,12 +304,17 @@ int ce_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stri
 
 int ce_backward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride, int dtype,
                 const int64_t *labels, int64_t ignore_index, double temperature,
-                const uint8_t *row_mask, const float *g, const void *saved, void *dlogits,
-                int64_t dlogits_row_stride, int32_t *status, cev_stream_t stream)
+                double label_smoothing, const uint8_t *row_mask, const float *g,
+                const void *saved, void *dlogits, int64_t dlogits_row_stride, int32_t *status,
+                cev_stream_t stream)
 {
     bool done;
     int rc = check_common(logits, rows, vocab, row_stride, dtype, temperature, &done);
-    if (rc != CEV_OK || done)
+    if (rc != CEV_OK)
+        return rc;
+    if (!smoothing_ok(label_smoothing))
+        return CEV_ESMOOTH;
+    if (done)
         return rc;
     if (dlogits_row_stride < vocab)
         return CEV_ESTRIDE;
@@ -253,10 +326,7 @@ int ce_backward(const void *logits, int64_t rows, int64_t vocab, int64_t row_str
     if (!aligned(labels, 8) || !aligned(g, 4) || !aligned(saved, 16) ||
         !aligned(dlogits, (uintptr_t)es) || !aligned(status, 4))
         return CEV_EALIGN;
-    const uintptr_t l0 = (uintptr_t)logits, l1 = l0 + (uintptr_t)(((rows - 1) * row_stride + vocab) * es);
-    const uintptr_t d0 = (uintptr_t)dlogits,
-                    d1 = d0 + (uintptr_t)(((rows - 1) * dlogits_row_stride + vocab) * es);
-    if (l0 < d1 && d0 < l1)
+    if (overlaps(logits, row_stride, dlogits, dlogits_row_stride, rows, vocab, es))
         return CEV_EALIAS;
     BackwardArgs a{};
     a.logits = logits;
@@ -271,6 +341,7 @@ int ce_backward(const void *logits, int64_t rows, int64_t vocab, int64_t row_str
     a.dlogits = dlogits;
     a.d_row_stride = dlogits_row_stride;
     a.temperature = temperature;
+    a.label_smoothing = label_smoothing;
     a.c = (float)(1.4426950408889634074 / temperature);
     a.inv_t = (float)(1.0 / temperature);
     a.status = status;
@@ -279,14 +350,18 @@ int ce_backward(const void *logits, int64_t rows, int64_t vocab, int64_t row_str
 
 int ce_fused(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride, int dtype,
              const int64_t *labels, int64_t ignore_index, double temperature,
-             const uint8_t *row_mask, const float *g, float *loss, void *saved, float *logp,
-             float *entropy, int64_t *argmax, void *dlogits, int64_t dlogits_row_stride,
-             int64_t *valid_rows, int64_t *n_valid, void *workspace, size_t workspace_bytes,
-             int32_t *status, cev_stream_t stream)
+             double label_smoothing, const uint8_t *row_mask, const float *g, float *loss,
+             void *saved, float *logp, float *entropy, int64_t *argmax, void *dlogits,
+             int64_t dlogits_row_stride, int64_t *valid_rows, int64_t *n_valid, void *workspace,
+             size_t workspace_bytes, int32_t *status, cev_stream_t stream)
 {
     bool done;
     int rc = check_common(logits, rows, vocab, row_stride, dtype, temperature, &done);
-    if (rc != CEV_OK || done)
+    if (rc != CEV_OK)
+        return rc;
+    if (!smoothing_ok(label_smoothing))
+        return CEV_ESMOOTH;
+    if (done)
         return rc;
     if (dlogits_row_stride < vocab)
         return CEV_ESTRIDE;
@@ -300,10 +375,7 @@ int ce_fused(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride
         !aligned(valid_rows, 8) || !aligned(n_valid, 8) || !aligned(dlogits, (uintptr_t)es) ||
         !aligned(status, 4))
         return CEV_EALIGN;
-    const uintptr_t l0 = (uintptr_t)logits, l1 = l0 + (uintptr_t)(((rows - 1) * row_stride + vocab) * es);
-    const uintptr_t d0 = (uintptr_t)dlogits,
-                    d1 = d0 + (uintptr_t)(((rows - 1) * dlogits_row_stride + vocab) * es);
-    if (l0 < d1 && d0 < l1)
+    if (overlaps(logits, row_stride, dlogits, dlogits_row_stride, rows, vocab, es))
         return CEV_EALIAS;
     const bool want_list = valid_rows || n_valid;
     if (want_list && (!valid_rows || !n_valid)) {
@@ -321,13 +393,13 @@ int ce_fused(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride
                               (row_stride * es) % 16 == 0 && (dlogits_row_stride * es) % 16 == 0;
     if (!aligned_rows) {
         rc = ce_forward(logits, rows, vocab, row_stride, dtype, labels, ignore_index, temperature,
-                        row_mask, loss, saved, logp, entropy, argmax, valid_rows, n_valid,
-                        workspace, workspace_bytes, status, stream);
+                        label_smoothing, row_mask, loss, saved, logp, entropy, argmax,
+                        valid_rows, n_valid, workspace, workspace_bytes, status, stream);
         if (rc != CEV_OK)
             return rc;
         return ce_backward(logits, rows, vocab, row_stride, dtype, labels, ignore_index,
-                           temperature, row_mask, g, saved, dlogits, dlogits_row_stride, status,
-                           stream);
+                           temperature, label_smoothing, row_mask, g, saved, dlogits,
+                           dlogits_row_stride, status, stream);
     }
     if (want_list) {
         int64_t *list = valid_rows ? valid_rows : static_cast<int64_t *>(workspace);
@@ -359,6 +431,7 @@ int ce_fused(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride
     fa.row_mask = row_mask;
     fa.g = g;
     fa.temperature = temperature;
+    fa.label_smoothing = label_smoothing;
     fa.c = (float)(1.4426950408889634074 / temperature);
     fa.inv_t = (float)(1.0 / temperature);
     fa.loss = loss;
@@ -385,10 +458,11 @@ const char *cev_status_string(int code)
     case CEV_EWORKSPACE: return "workspace smaller than cev_workspace_size(rows)";
     case CEV_EALIAS: return "dlogits overlaps logits";
     case CEV_ELAUNCH: return "kernel launch failed";
+    case CEV_ESMOOTH: return "label_smoothing must be finite and in [0, 1]";
     default: return "unknown error code";
     }
 }
 
-int cev_version(void) { return 100; }
+int cev_version(void) { return 200; }
 
 } // extern "C"

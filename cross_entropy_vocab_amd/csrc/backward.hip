@@ -1,7 +1,9 @@
 // backward.hip -- analytic backward sweep for gfx950: one pass that reads each
 // valid row once and writes dlogits once, in the logits dtype.
 //
-// dlogits[r, j] = (g_r / T) p_j for j != t and -(g_r / T) q_r at the target,
+// dlogits[r, j] = (g_r / T) p_j for j != t and -(g_r / T) q_r at the target
+// (label smoothing eps, unsloth-zoo #2080 Summary on the Liger page:
+// (g/T)(p_j - eps/V), and (g/T)(eps - eps/V - q) at the target),
 // where q_r = s_others / d = 1 - p_t comes from the forward's saved record
 // (Liger-Kernel PR #1555, Summary: dx_y = -sum_others / d; ms-swift PR #10353,
 // PR information: g * softmax - g * one_hot with zero weight for ignored
@@ -17,7 +19,8 @@ namespace {
 struct RowConst {
     float mz;      // exact row maximum of the stored logits
     float kexp;    // log2 d - log2 |g / T|
-    float tval;    // -|g / T| q, the target entry before the sign
+    float ev;      // |g / T| eps / V, the label-smoothing share of every column
+    float tval;    // -|g / T| (q - eps + eps / V), the target entry before the sign
     unsigned sgn;  // 0x80000000 when g < 0 (or is -0)
     bool valid;
 };
@@ -29,7 +32,7 @@ __device__ __forceinline__ void grad_vec(const float (&z)[Elem<DT>::kVE], float 
     constexpr int VE = Elem<DT>::kVE;
 #pragma unroll
     for (int e = 0; e < VE; ++e)
-        o[e] = exp2_hw(fmaf(z[e] - rc.mz, c, -rc.kexp));
+        o[e] = exp2_hw(fmaf(z[e] - rc.mz, c, -rc.kexp)) - rc.ev;
     if ((uint64_t)(t - col0) < (uint64_t)VE) {
 #pragma unroll
         for (int e = 0; e < VE; ++e)
@@ -67,7 +70,7 @@ template <int DT> __device__ __forceinline__ void store_elem(char *rowp, int64_t
 template <int DT>
 __device__ __forceinline__ float grad_scalar(float z, const RowConst &rc, float c, int64_t col, int64_t t)
 {
-    return col == t ? rc.tval : exp2_hw(fmaf(z - rc.mz, c, -rc.kexp));
+    return col == t ? rc.tval : exp2_hw(fmaf(z - rc.mz, c, -rc.kexp)) - rc.ev;
 }
 
 // blockIdx.x = row * slices + slice; slice sl covers the row's 16-byte vectors
@@ -100,13 +103,17 @@ __global__ __launch_bounds__(BLOCK) void k_backward(BackwardArgs a, int slices, 
     rc.mz = sv.m_z;
     rc.sgn = 0u;
     rc.kexp = 0.0f;
+    rc.ev = 0.0f;
     rc.tval = 0.0f;
     if (rc.valid) {
         const float gp = a.g[r] * a.inv_t;
         const float ag = fabsf(gp);
+        const float eps = (float)a.label_smoothing;
+        const float epv = (float)(a.label_smoothing / (double)V);
         rc.sgn = __float_as_uint(gp) & 0x80000000u;
         rc.kexp = sv.log2_d - __log2f(ag);
-        rc.tval = -(ag * sv.q);
+        rc.ev = ag * epv;
+        rc.tval = -(ag * ((sv.q - eps) + epv));
     }
     const float c = a.c;
 
@@ -169,6 +176,186 @@ __global__ __launch_bounds__(BLOCK) void k_backward(BackwardArgs a, int slices, 
     }
 }
 
+// ------------------------------------------------------------------------
+// Top-K backward: gradient of sum_k g_k log p_{i_k} with respect to the
+// logits (ms-swift PR #10337, PR information: gradients through top-K
+// indices), dL/dz_j = (1/T) sum_k g_k ([j = i_k] - p_j).  Every column gets
+// -(Gs/T) p_j, Gs = sum of the valid g_k (|Gs/T| folded into the exponent);
+// a gathered column j gets (G_j q_j - p_j (Gs - G_j)) / T instead, G_j the sum
+// of the g_k gathered at j and q_j = 1 - p_j from the forward as sigmoid(u),
+// so the peaked case never forms 1 - p_j by subtraction.  Same one-shot slices
+// as k_backward; each workgroup first lists the gathered columns that fall in
+// its slice.
+template <int DT, int BLOCK, int U>
+__global__ __launch_bounds__(BLOCK) void k_topk_backward(TopkBackwardArgs a, int slices, int64_t per)
+{
+    constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize, W = BLOCK / kWave;
+    // Dynamic LDS, K entries each: the row's indices, its g, and the list of
+    // gathered columns this slice writes (first index k of each, and the two
+    // per-column terms).
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int K = (int)a.K;
+    int64_t *sidx = reinterpret_cast<int64_t *>(lds);
+    float *sg = reinterpret_cast<float *>(sidx + K);
+    int *lk = reinterpret_cast<int *>(sg + K);
+    float *la = reinterpret_cast<float *>(lk + K);
+    float *lb = la + K;
+    __shared__ double sh_d[W];
+    __shared__ int ln;
+    __shared__ int sbad;
+    const int tid = threadIdx.x;
+    const int64_t r = blockIdx.x / slices;
+    const int sl = blockIdx.x % slices;
+    const int64_t V = a.vocab;
+    const char *lrow = static_cast<const char *>(a.logits) + (size_t)r * (size_t)a.row_stride * ES;
+    char *drow = static_cast<char *>(a.dlogits) + (size_t)r * (size_t)a.d_row_stride * ES;
+    const bool scalar_path = (((uintptr_t)lrow ^ (uintptr_t)drow) & 15u) != 0;
+    int64_t head = (int64_t)(((16u - ((unsigned)(uintptr_t)lrow & 15u)) & 15u) / ES);
+    head = head < V ? head : V;
+    const int64_t nvec = (V - head) / VE;
+    const int64_t tail0 = head + nvec * VE;
+    const int64_t v0 = (int64_t)sl * per;
+    const int64_t v1 = v0 + per < nvec ? v0 + per : nvec;
+    // Does this workgroup write column `col`?
+    auto owns = [&](int64_t col) {
+        if (scalar_path)
+            return col >= V * sl / slices && col < V * (sl + 1) / slices;
+        if (col < head)
+            return sl == 0;
+        if (col >= tail0)
+            return sl == slices - 1;
+        const int64_t j = (col - head) / VE;
+        return j >= v0 && j < v1;
+    };
+    const cev_saved sv = a.saved[r];
+    const bool masked = (a.row_mask && a.row_mask[r] == 0) || !(sv.flags & 1);
+    const int64_t *idx = a.indices + (size_t)r * (size_t)a.index_row_stride;
+    const float *gk = a.g + (size_t)r * (size_t)K;
+    const float *qk = a.q + (size_t)r * (size_t)K;
+
+    if (tid == 0) {
+        ln = 0;
+        sbad = 0;
+    }
+    __syncthreads();
+    // Gs = sum of the g_k at valid indices (fp64, fixed order per thread and
+    // across the block, so every slice of the row gets the same value).
+    double gpart = 0.0;
+    for (int k = tid; k < K; k += BLOCK) {
+        const int64_t i = idx[k];
+        sidx[k] = i;
+        const float g = gk[k];
+        sg[k] = g;
+        if (i == a.ignore_index)
+            continue;
+        if (i < 0 || i >= V) {
+            sbad = 1;
+            continue;
+        }
+        gpart += (double)g;
+    }
+    const float gs = (float)block_sum<BLOCK>(gpart, sh_d); // block_sum synchronises
+    if (tid == 0 && sbad && sl == 0 && a.status && !masked)
+        atomicOr(a.status, (int32_t)CEV_STATUS_BAD_INDEX);
+    if (!masked) {
+        for (int k = tid; k < K; k += BLOCK) {
+            const int64_t i = sidx[k];
+            if (i == a.ignore_index || i < 0 || i >= V || !owns(i))
+                continue;
+            bool first = true;
+            for (int k2 = 0; k2 < k && first; ++k2)
+                first = sidx[k2] != i;
+            if (!first)
+                continue;
+            double gj = 0.0;
+            for (int k2 = k; k2 < K; ++k2)
+                if (sidx[k2] == i)
+                    gj += (double)sg[k2];
+            const int n = atomicAdd(&ln, 1);
+            lk[n] = k;
+            la[n] = (float)(gj * (double)qk[k] * (double)a.inv_t);
+            lb[n] = (float)(((double)gs - gj) * (double)a.inv_t);
+        }
+    }
+    __syncthreads();
+    const int L = ln;
+    const float mz = sv.m_z, l2d = sv.log2_d, c = a.c;
+    const float gsT = gs * a.inv_t;
+    const float kexp = l2d - __log2f(fabsf(gsT));
+    // Every column but the gathered ones is -(Gs/T) p_j: the sign applied to
+    // the bits is the opposite of Gs's.  Gathered values carry their own sign
+    // and are pre-flipped so that the same XOR leaves them as computed.
+    const unsigned sgn = (__float_as_uint(gsT) & 0x80000000u) ^ 0x80000000u;
+    auto gathered = [&](float z, int n) {
+        const float p = exp2_hw(fmaf(z - mz, c, -l2d));
+        return __uint_as_float(__float_as_uint(la[n] - p * lb[n]) ^ sgn);
+    };
+    auto value = [&](float z, int64_t col) {
+        float o = exp2_hw(fmaf(z - mz, c, -kexp));
+        for (int n = 0; n < L; ++n)
+            if (sidx[lk[n]] == col)
+                o = gathered(z, n);
+        return o;
+    };
+
+    if (scalar_path) {
+        const int64_t c0 = V * sl / slices, c1 = V * (sl + 1) / slices;
+        for (int64_t col = c0 + tid; col < c1; col += BLOCK) {
+            const float v = masked ? 0.0f : value(load_elem<DT>(lrow, col), col);
+            store_elem<DT>(drow, col, v, masked ? 0u : sgn);
+        }
+        return;
+    }
+    const u32x4 *lvp = reinterpret_cast<const u32x4 *>(lrow + head * ES);
+    u32x4 *dvp = reinterpret_cast<u32x4 *>(drow + head * ES);
+    if (sl == 0 && tid < head) {
+        const float v = masked ? 0.0f : value(load_elem<DT>(lrow, tid), tid);
+        store_elem<DT>(drow, tid, v, masked ? 0u : sgn);
+    }
+    if (sl == slices - 1 && tail0 + tid < V) {
+        const int64_t col = tail0 + tid;
+        const float v = masked ? 0.0f : value(load_elem<DT>(lrow, col), col);
+        store_elem<DT>(drow, col, v, masked ? 0u : sgn);
+    }
+    if (masked) {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        for (int64_t j = v0 + tid; j < v1; j += BLOCK)
+            store16_stream(zero, dvp + j);
+        return;
+    }
+    for (int64_t base = v0 + tid; base < v1; base += (int64_t)BLOCK * U) {
+        u32x4 w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t j = base + (int64_t)u * BLOCK;
+            if (j < v1)
+                w[u] = load16_stream(lvp + j);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t j = base + (int64_t)u * BLOCK;
+            if (j < v1) {
+                float z[VE], o[VE];
+                unpack16<DT>(w[u], z);
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    o[e] = exp2_hw(fmaf(z[e] - mz, c, -kexp));
+                const int64_t col0 = head + j * VE;
+                for (int n = 0; n < L; ++n) {
+                    const int64_t d = sidx[lk[n]] - col0;
+                    if ((uint64_t)d < (uint64_t)VE) {
+#pragma unroll
+                        for (int e = 0; e < VE; ++e)
+                            if (e == d)
+                                o[e] = gathered(z[e], n);
+                    }
+                }
+                store16_stream(pack_vec<DT>(o, sgn), dvp + j);
+            }
+        }
+    }
+}
+
 template <int DT, int BLOCK, int U>
 hipError_t launch_bwd_t(const BackwardArgs &a, int iters, int reverse, hipStream_t s)
 {
@@ -212,6 +399,26 @@ hipError_t launch_backward_cfg(int dtype, const BackwardArgs &a, int block, int 
 hipError_t launch_backward(int dtype, const BackwardArgs &a, hipStream_t s)
 {
     return launch_backward_cfg(dtype, a, 256, 4, 1, 0, s);
+}
+
+hipError_t launch_topk_backward(int dtype, const TopkBackwardArgs &a, hipStream_t s)
+{
+    constexpr int B = 256, UU = 4;
+    const int64_t nvec = a.vocab / (dtype == CEV_BF16 ? 8 : 4);
+    int64_t per = (int64_t)B * UU;
+    int64_t slices = (nvec + per - 1) / per;
+    slices = slices < 1 ? 1 : slices;
+    while ((uint64_t)a.rows * (uint64_t)slices * B > 0xFFFFFFFFull && slices > 1) {
+        per *= 2;
+        slices = (nvec + per - 1) / per;
+    }
+    dim3 grid((unsigned)(a.rows * slices)), block(B);
+    const size_t lds = (size_t)a.K * (sizeof(int64_t) + 4 * sizeof(float));
+    if (dtype == CEV_BF16)
+        hipLaunchKernelGGL((k_topk_backward<CEV_BF16, B, UU>), grid, block, lds, s, a, (int)slices, per);
+    else
+        hipLaunchKernelGGL((k_topk_backward<CEV_F32, B, UU>), grid, block, lds, s, a, (int)slices, per);
+    return hipGetLastError();
 }
 
 } // namespace cev

@@ -29,9 +29,11 @@ struct SweepArgs {
     int64_t splits;            // workgroups per row (1 = whole rows); needs partials
     void *partials;            // [rows * splits] SplitPartial, device scratch
     double temperature;
+    double label_smoothing;    // eps in [0, 1]; ce_forward only
     float c;                   // log2(e) / T, rounded to fp32
     float inv_t;               // 1 / T, rounded to fp32
     float *logp;               // [rows] or [rows, K]
+    float *q;                  // top-K: [rows, K] 1 - p at each gathered index, or null
     float *loss;
     float *entropy;
     int64_t *argmax;
@@ -46,6 +48,7 @@ struct SplitPartial {
     int64_t arg;               // lowest non-target column holding m (INT64_MAX if none)
     double s;                  // sum of e^{(z - b)/T}, b = max(m, -FLT_MAX)
     double h;                  // sum of e^{(z - b)/T} (b - z)/T
+    double zs;                 // sum of the part's non-target stored values
 };
 
 // Workgroups per row for the split forward: enough workgroups to fill the
@@ -81,10 +84,35 @@ struct BackwardArgs {
     void *dlogits;
     int64_t d_row_stride;
     double temperature;
+    double label_smoothing;    // eps in [0, 1]
     float c;                   // log2(e) / T
     float inv_t;               // 1 / T
     int32_t *status;
 };
+
+// Top-K backward (gradient of sum_k g_k log p_{i_k}).
+constexpr int kMaxTopK = 1024;
+struct TopkBackwardArgs {
+    const void *logits;
+    int64_t rows;
+    int64_t vocab;
+    int64_t row_stride;
+    const int64_t *indices;    // [rows, K], row stride index_row_stride
+    int64_t K;
+    int64_t index_row_stride;
+    int64_t ignore_index;
+    const uint8_t *row_mask;
+    const float *g;            // [rows, K] dense
+    const cev_saved *saved;    // from sls_topk_forward: m_z, log2 d
+    const float *q;            // [rows, K] from sls_topk_forward: 1 - p at each index
+    void *dlogits;
+    int64_t d_row_stride;
+    float c;                   // log2(e) / T
+    float inv_t;               // 1 / T
+    int32_t *status;
+};
+
+hipError_t launch_topk_backward(int dtype, const TopkBackwardArgs &a, hipStream_t stream);
 
 // Forward + backward in one call, one workgroup per row (rows 16-byte aligned).
 struct FusedArgs {
@@ -97,6 +125,7 @@ struct FusedArgs {
     const uint8_t *row_mask;
     const float *g;
     double temperature;
+    double label_smoothing;    // eps in [0, 1]
     float c;                   // log2(e) / T
     float inv_t;               // 1 / T
     float *loss;

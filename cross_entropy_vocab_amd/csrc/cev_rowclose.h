@@ -19,15 +19,18 @@ struct RowOutputs {
 
 // Inputs: the stored target logit zt (column t), the largest non-target logit
 // M (sum base B = max(M, -FLT_MAX)), S = sum_{j != t} e^{(z_j - B)/T},
-// Hs = sum_{j != t} e^{(z_j - B)/T} (B - z_j)/T, the lowest non-target column
-// holding M, and T.  With u = log S + (B - z_t)/T (the collapse-safe form of
-// the Liger-Kernel PR #1555 Summary, CE bullet):
-//   loss = softplus(u) = -log p_t,   q = 1 - p_t = sigmoid(u),
-//   lse = z_t/T + loss,   H = p_t loss + q (lse - B/T) + e^{B/T - lse} Hs,
-// every entropy term non-negative.  Returns the saved record (also written to
-// o.saved when that is non-null).
+// Hs = sum_{j != t} e^{(z_j - B)/T} (B - z_j)/T, Zs = sum_{j != t} z_j, the
+// lowest non-target column holding M, T, the label smoothing eps and V.  With
+// u = log S + (B - z_t)/T (the collapse-safe form of the Liger-Kernel PR #1555
+// Summary, CE bullet):
+//   nll = softplus(u) = -log p_t,   q = 1 - p_t = sigmoid(u),
+//   lse = z_t/T + nll,   H = p_t nll + q (lse - B/T) + e^{B/T - lse} Hs,
+//   loss = (1 - eps) nll + eps (lse - (Zs + z_t) / (T V)),
+// every entropy term non-negative; log p = -nll is never smoothed.  Returns
+// the saved record (also written to o.saved when that is non-null).
 __device__ inline cev_saved close_row_fp64(const RowOutputs &o, int64_t r, float zt, int64_t t,
-                                           float M, double S, double Hs, int64_t a_o, double T)
+                                           float M, double S, double Hs, int64_t a_o, double T,
+                                           double Zs = 0.0, double eps = 0.0, int64_t V = 1)
 {
     const float B = fmaxf(M, -FLT_MAX);
     const double u = S > 0.0 ? log(S) + ((double)B - (double)zt) / T : -INFINITY;
@@ -36,8 +39,10 @@ __device__ inline cev_saved close_row_fp64(const RowOutputs &o, int64_t r, float
     const double lse = (double)zt / T + loss;
     if (o.logp)
         o.logp[r] = (float)(-loss);
-    if (o.loss)
-        o.loss[r] = (float)loss;
+    if (o.loss) {
+        const double smooth = eps != 0.0 ? lse - (Zs + (double)zt) / (T * (double)V) : 0.0;
+        o.loss[r] = (float)((1.0 - eps) * loss + eps * smooth);
+    }
     if (o.entropy) {
         double H = 0.0;
         if (S > 0.0)

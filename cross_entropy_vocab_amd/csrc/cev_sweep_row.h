@@ -16,6 +16,7 @@ struct LaneState {
     float s;    // sum of 2^((z - b) c), b = max(m, -FLT_MAX), c = log2(e)/T
     float comp; // Kahan compensation: the true sum is about s - comp
     float h;    // sum of 2^((z - b) c) (b - z) / T, for the entropy
+    float zs;   // plain sum of the stored values (label smoothing only)
     int best;   // code of the first step in which m was reached
 };
 
@@ -30,8 +31,9 @@ template <int N> __device__ __forceinline__ float tree_sum(float (&e)[N])
 }
 
 // Fold one step of N values into the lane state.  Excluded columns arrive as
-// -inf; MAYBE_INF selects the guarded entropy term for such steps.
-template <int DT, int N, bool WANT_H, bool WANT_ARG, bool MAYBE_INF>
+// -inf; MAYBE_INF selects the guarded entropy term for such steps.  WANT_Z
+// also sums the stored values.
+template <int DT, int N, bool WANT_H, bool WANT_ARG, bool MAYBE_INF, bool WANT_Z = false>
 __device__ __forceinline__ void fold(LaneState &st, float (&v)[N], int code, float c, float inv_t)
 {
     float sm = v[0];
@@ -73,6 +75,14 @@ __device__ __forceinline__ void fold(LaneState &st, float (&v)[N], int code, flo
             ph = fmaf(e[i], d, ph);
         }
         st.h += ph;
+    }
+    if constexpr (WANT_Z) {
+        // sum of the stored values (excluded columns count 0)
+        float zv[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            zv[i] = MAYBE_INF ? (v[i] == -INFINITY ? 0.0f : v[i]) : v[i];
+        st.zs += tree_sum(zv);
     }
     const float ps = tree_sum(e);
     const float y = ps - st.comp;
@@ -193,6 +203,7 @@ struct RowStats {
     float M;       // largest non-target stored value of the range (-inf if none)
     double S;      // sum over the range of e^{(z - B)/T}, B = max(M, -FLT_MAX)
     double Hs;     // sum of e^{(z - B)/T} (B - z)/T (entropy only)
+    double Zs;     // sum of the non-target stored values of the range (WANT_Z)
     int64_t a_o;   // lowest non-target column holding M (argmax only)
 };
 
@@ -202,7 +213,7 @@ struct RowStats {
 // first, one rescale per lane to the common base, fp64 sums; the argmax comes
 // from re-reading the one step where each maximal lane first saw the maximum.
 // Every thread of the workgroup returns the same statistics.
-template <int DT, int BLOCK, int U, bool WANT_H, bool WANT_ARG, bool NT>
+template <int DT, int BLOCK, int U, bool WANT_H, bool WANT_ARG, bool NT, bool WANT_Z = false>
 __device__ RowStats sweep_row(const char *rowp, int64_t V, int64_t t, int64_t part, int64_t parts,
                               float c, float inv_t, float *sh_f, double *sh_d, int64_t *sh_i)
 {
@@ -212,11 +223,11 @@ __device__ RowStats sweep_row(const char *rowp, int64_t V, int64_t t, int64_t pa
     const RowGeom g = row_geom<DT, U>(rowp, V, part, parts);
     const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp + (size_t)g.ahead * ES) + g.vbeg;
     const int64_t col_v = g.ahead + g.vbeg * VE;   // first column of the range's vectors
-    LaneState st{-INFINITY, 0.0f, 0.0f, 0.0f, -1};
+    LaneState st{-INFINITY, 0.0f, 0.0f, 0.0f, 0.0f, -1};
 
     if (tid < g.head) {
         float v[1] = {tid == t ? -INFINITY : load_elem<DT>(rowp, tid)};
-        fold<DT, 1, WANT_H, WANT_ARG, true>(st, v, tid, c, inv_t);
+        fold<DT, 1, WANT_H, WANT_ARG, true, WANT_Z>(st, v, tid, c, inv_t);
     }
 
     // Full wave steps, interleaved over the waves, one step of loads in flight
@@ -246,9 +257,9 @@ __device__ RowStats sweep_row(const char *rowp, int64_t V, int64_t t, int64_t pa
                     for (int e = 0; e < VE; ++e)
                         if (col_v + (k * CH + u * kWave + lane) * VE + e == t)
                             v[u * VE + e] = -INFINITY;
-                fold<DT, U * VE, WANT_H, WANT_ARG, true>(st, v, 16 + (int)k, c, inv_t);
+                fold<DT, U * VE, WANT_H, WANT_ARG, true, WANT_Z>(st, v, 16 + (int)k, c, inv_t);
             } else {
-                fold<DT, U * VE, WANT_H, WANT_ARG, false>(st, v, 16 + (int)k, c, inv_t);
+                fold<DT, U * VE, WANT_H, WANT_ARG, false, WANT_Z>(st, v, 16 + (int)k, c, inv_t);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -263,13 +274,13 @@ __device__ RowStats sweep_row(const char *rowp, int64_t V, int64_t t, int64_t pa
         for (int e = 0; e < VE; ++e)
             if (col_v + j * VE + e == t)
                 v[e] = -INFINITY;
-        fold<DT, VE, WANT_H, WANT_ARG, true>(st, v, 16 + (int)(g.nfull + (j - g.nfull * CH)), c,
+        fold<DT, VE, WANT_H, WANT_ARG, true, WANT_Z>(st, v, 16 + (int)(g.nfull + (j - g.nfull * CH)), c,
                                              inv_t);
     }
     if (g.tail0 + tid < g.tail1) {
         const int64_t col = g.tail0 + tid;
         float v[1] = {col == t ? -INFINITY : load_elem<DT>(rowp, col)};
-        fold<DT, 1, WANT_H, WANT_ARG, true>(st, v, 16 + (int)(g.nfull + g.nrem + tid), c, inv_t);
+        fold<DT, 1, WANT_H, WANT_ARG, true, WANT_Z>(st, v, 16 + (int)(g.nfull + g.nrem + tid), c, inv_t);
     }
 
     // Combine the lanes: exact maximum first, then each lane rescales its own
@@ -284,6 +295,9 @@ __device__ RowStats sweep_row(const char *rowp, int64_t V, int64_t t, int64_t pa
     if constexpr (WANT_H)
         Hs = block_sum<BLOCK>((double)f * (double)fmaf(fminf((B - bl) * inv_t, kBig), sl, st.h),
                               sh_d);
+    double Zs = 0.0;
+    if constexpr (WANT_Z)
+        Zs = block_sum<BLOCK>((double)st.zs, sh_d);
     int64_t a_o = INT64_MAX;
     if constexpr (WANT_ARG) {
         int64_t mine = INT64_MAX;
@@ -292,7 +306,7 @@ __device__ RowStats sweep_row(const char *rowp, int64_t V, int64_t t, int64_t pa
         a_o = block_min<BLOCK>(mine, sh_i);
     }
 
-    return RowStats{M, S, Hs, a_o};
+    return RowStats{M, S, Hs, Zs, a_o};
 }
 
 } // namespace cev

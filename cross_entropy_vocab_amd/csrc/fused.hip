@@ -1,18 +1,21 @@
-// fused.hip -- per-row cross-entropy forward and analytic backward in one call
-// and one HBM read of each row, for an upstream weight g that is known before
-// the forward (token weights, mean reduction).
+// fused.hip -- per-row cross-entropy forward and analytic backward in one call,
+// each row fetched from HBM about once, for an upstream weight g that is known
+// before the forward (token weights, mean reduction).
 //
 // One workgroup per row sweeps the row for the target-excluded statistics
 // with caching loads (Liger-Kernel PR #1555, Summary, CE bullet: the sum
 // without the target), closes it in fp64, and right away re-reads the same
-// row -- the few hundred rows in flight (~80-160 MB) leave it in the 256 MB
-// Infinity Cache -- to write (g/T)(p_j - [j = t]) with the target column
-// -(g/T) q (ms-swift PR #10353, PR information: g * softmax - g * one_hot;
-// Liger PR #1555: dx_y = -sum_others/d).  Several workgroups per CU overlap one
-// row's arithmetic with other rows' memory traffic.  (Holding a whole
-// 152064-wide bf16 row in registers instead was measured slower, 1.42 ms
-// against 0.98 ms for 8192 rows: a CU can then hold only one row, and its
-// load, arithmetic and store phases cannot overlap.)
+// row -- the few hundred rows in flight (~80-160 MB) fit the 256 MB Infinity
+// Cache, which serves much of the re-read -- to write (g/T)(p_j - [j = t])
+// with the target column -(g/T) q (ms-swift PR #10353, PR information:
+// g * softmax - g * one_hot; Liger PR #1555: dx_y = -sum_others/d).  Label
+// smoothing eps (unsloth-zoo #2080 Summary, on the Liger page) takes eps/V off
+// every column, giving (g/T)(p_j - eps/V) and (g/T)(eps - eps/V - q) at t.
+// Several workgroups per CU overlap one row's arithmetic with other rows'
+// memory traffic.  (Holding a whole 152064-wide bf16 row in registers instead
+// was measured slower, 1.42 ms against 0.98 ms for 8192 rows: a CU can then
+// hold only one row, and its load, arithmetic and store phases cannot
+// overlap.)
 #include "cev_device.h"
 #include "cev_launch.h"
 #include "cev_rowclose.h"
@@ -34,7 +37,7 @@ template <int VE> __device__ __forceinline__ void set_elem(float (&v)[VE], int e
 // (NT1 = false; streaming loads there make pass 2 miss the cache: 1.36 ms
 // against 0.98 ms); pass 2, by the same workgroup right after the row is
 // closed, re-reads the row and writes dlogits, last vectors first (DESC).
-template <int DT, int BLOCK, int U, bool WANT_H, bool NT1, bool DESC>
+template <int DT, int BLOCK, int U, bool WANT_H, bool NT1, bool DESC, bool WANT_Z = false>
 __global__ __launch_bounds__(BLOCK) void k_fused_stream(FusedArgs a)
 {
     constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize, W = BLOCK / kWave;
@@ -42,7 +45,7 @@ __global__ __launch_bounds__(BLOCK) void k_fused_stream(FusedArgs a)
     __shared__ float sh_f[W];
     __shared__ double sh_d[W];
     __shared__ int64_t sh_i[W];
-    __shared__ float sh_bc[3];
+    __shared__ float sh_bc[4];
     __shared__ unsigned sh_sgn;
     const int tid = threadIdx.x;
     const int64_t r = blockIdx.x;
@@ -90,8 +93,8 @@ __global__ __launch_bounds__(BLOCK) void k_fused_stream(FusedArgs a)
         return;
     }
 
-    const RowStats rs = sweep_row<DT, BLOCK, U, WANT_H, true, NT1>(lrow, V, t, 0, 1, a.c, a.inv_t,
-                                                                     sh_f, sh_d, sh_i);
+    const RowStats rs = sweep_row<DT, BLOCK, U, WANT_H, true, NT1, WANT_Z>(
+        lrow, V, t, 0, 1, a.c, a.inv_t, sh_f, sh_d, sh_i);
     if (tid == 0) {
         RowOutputs o;
         o.logp = a.logp;
@@ -100,16 +103,19 @@ __global__ __launch_bounds__(BLOCK) void k_fused_stream(FusedArgs a)
         o.argmax = a.argmax;
         o.saved = a.saved;
         const cev_saved sv = close_row_fp64(o, r, load_elem<DT>(lrow, t), t, rs.M, rs.S, rs.Hs,
-                                            rs.a_o, a.temperature);
+                                            rs.a_o, a.temperature, rs.Zs, a.label_smoothing, V);
         const float gp = a.g[r] * a.inv_t;
         const float ag = fabsf(gp);
+        const float eps = (float)a.label_smoothing;
+        const float epv = (float)(a.label_smoothing / (double)V);
         sh_bc[0] = sv.m_z;
         sh_bc[1] = sv.log2_d - __log2f(ag);
-        sh_bc[2] = -(ag * sv.q);
+        sh_bc[2] = -(ag * ((sv.q - eps) + epv));
+        sh_bc[3] = ag * epv;
         sh_sgn = __float_as_uint(gp) & 0x80000000u;
     }
     __syncthreads();
-    const float mz = sh_bc[0], kexp = sh_bc[1], tval = sh_bc[2], c = a.c;
+    const float mz = sh_bc[0], kexp = sh_bc[1], tval = sh_bc[2], ev = sh_bc[3], c = a.c;
     const unsigned sgn = sh_sgn;
 
     // Pass 2, last vectors first: the most recently read part of the row is
@@ -133,7 +139,7 @@ __global__ __launch_bounds__(BLOCK) void k_fused_stream(FusedArgs a)
                 unpack16<DT>(w[u], v);
 #pragma unroll
                 for (int k = 0; k < VE; ++k)
-                    o[k] = exp2_hw(fmaf(v[k] - mz, c, -kexp));
+                    o[k] = exp2_hw(fmaf(v[k] - mz, c, -kexp)) - ev;
                 if ((uint64_t)(t - j * VE) < (uint64_t)VE)
                     set_elem<VE>(o, (int)(t - j * VE), tval);
                 u32x4 out;
@@ -154,7 +160,7 @@ __global__ __launch_bounds__(BLOCK) void k_fused_stream(FusedArgs a)
     if (tail0 + tid < V) {
         const int64_t col = tail0 + tid;
         const float z = load_elem<DT>(lrow, col);
-        const float o = col == t ? tval : exp2_hw(fmaf(z - mz, c, -kexp));
+        const float o = col == t ? tval : exp2_hw(fmaf(z - mz, c, -kexp)) - ev;
         if constexpr (DT == CEV_F32)
             reinterpret_cast<float *>(drow)[col] = __uint_as_float(__float_as_uint(o) ^ sgn);
         else
@@ -168,8 +174,13 @@ __global__ __launch_bounds__(BLOCK) void k_fused_stream(FusedArgs a)
 template <int DT, bool NT1> hipError_t launch_stream_t(const FusedArgs &a, bool want_h, hipStream_t s)
 {
     dim3 grid((unsigned)a.rows), block(512);
-    if (want_h)
+    const bool z = a.label_smoothing != 0.0;
+    if (want_h && z)
+        hipLaunchKernelGGL((k_fused_stream<DT, 512, 4, true, NT1, true, true>), grid, block, 0, s, a);
+    else if (want_h)
         hipLaunchKernelGGL((k_fused_stream<DT, 512, 4, true, NT1, true>), grid, block, 0, s, a);
+    else if (z)
+        hipLaunchKernelGGL((k_fused_stream<DT, 512, 4, false, NT1, true, true>), grid, block, 0, s, a);
     else
         hipLaunchKernelGGL((k_fused_stream<DT, 512, 4, false, NT1, true>), grid, block, 0, s, a);
     return hipGetLastError();
@@ -182,6 +193,8 @@ template <int DT, bool NT1> hipError_t launch_stream_t(const FusedArgs &a, bool 
 hipError_t launch_fused_stream_cfg(int dtype, const FusedArgs &a, int block, int U, bool desc,
                                    size_t lds_bytes, hipStream_t s)
 {
+    if (a.label_smoothing != 0.0)
+        return hipErrorInvalidValue; // the tuning shapes carry no label-smoothing sum
     dim3 grid((unsigned)a.rows);
 #define CEV_FS_CASE(B, UU, D)                                                                   \
     if (block == B && U == UU && desc == D) {                                                   \

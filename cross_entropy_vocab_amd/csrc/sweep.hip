@@ -26,7 +26,7 @@ constexpr int kMaxK = 1024; // gathered indices per row in sls_topk_forward
 // Per-row closing step (cev_rowclose.h) with the sweep's outputs.
 template <int DT, bool WANT_H, bool WANT_ARG>
 __device__ void close_row(const SweepArgs &a, int64_t r, const char *rowp, int64_t t, float M,
-                          double S, double Hs, int64_t a_o)
+                          double S, double Hs, double Zs, int64_t a_o)
 {
     RowOutputs o;
     o.logp = a.logp;
@@ -34,7 +34,8 @@ __device__ void close_row(const SweepArgs &a, int64_t r, const char *rowp, int64
     o.entropy = WANT_H ? a.entropy : nullptr;
     o.argmax = WANT_ARG ? a.argmax : nullptr;
     o.saved = a.saved;
-    close_row_fp64(o, r, load_elem<DT>(rowp, t), t, M, S, Hs, a_o, a.temperature);
+    close_row_fp64(o, r, load_elem<DT>(rowp, t), t, M, S, Hs, a_o, a.temperature, Zs,
+                   a.label_smoothing, a.vocab);
 }
 
 // ------------------------------------------------------------------------
@@ -42,7 +43,7 @@ __device__ void close_row(const SweepArgs &a, int64_t r, const char *rowp, int64
 // SPLIT, `a.splits` workgroups share one row (block b * splits + p takes part
 // p of compacted row b) and each writes a partial record for k_merge instead
 // of closing the row.
-template <int DT, int BLOCK, int U, bool WANT_H, bool WANT_ARG, bool SPLIT>
+template <int DT, int BLOCK, int U, bool WANT_H, bool WANT_ARG, bool SPLIT, bool WANT_Z>
 __global__ __launch_bounds__(BLOCK) void k_sls_sweep(SweepArgs a)
 {
     constexpr int ES = Elem<DT>::kSize, W = BLOCK / kWave;
@@ -86,10 +87,10 @@ __global__ __launch_bounds__(BLOCK) void k_sls_sweep(SweepArgs a)
     }
 
     const char *rowp = static_cast<const char *>(a.logits) + (size_t)r * (size_t)a.row_stride * ES;
-    const RowStats rs = sweep_row<DT, BLOCK, U, WANT_H, WANT_ARG, true>(
+    const RowStats rs = sweep_row<DT, BLOCK, U, WANT_H, WANT_ARG, true, WANT_Z>(
         rowp, V, t, part, parts, a.c, a.inv_t, sh_f, sh_d, sh_i);
     const float M = rs.M;
-    const double S = rs.S, Hs = rs.Hs;
+    const double S = rs.S, Hs = rs.Hs, Zs = rs.Zs;
     const int64_t a_o = rs.a_o;
 
     if (tid == 0) {
@@ -100,9 +101,10 @@ __global__ __launch_bounds__(BLOCK) void k_sls_sweep(SweepArgs a)
             pr.arg = a_o;
             pr.s = S;
             pr.h = Hs;
+            pr.zs = Zs;
             static_cast<SplitPartial *>(a.partials)[b * parts + part] = pr;
         } else {
-            close_row<DT, WANT_H, WANT_ARG>(a, r, rowp, t, M, S, Hs, a_o);
+            close_row<DT, WANT_H, WANT_ARG>(a, r, rowp, t, M, S, Hs, Zs, a_o);
         }
     }
 }
@@ -130,10 +132,11 @@ __global__ __launch_bounds__(256) void k_merge(SweepArgs a)
     const float M = wave_max(m);
     const float B = fmaxf(M, -FLT_MAX);
     const double T = a.temperature;
-    double S = 0.0, H = 0.0;
+    double S = 0.0, H = 0.0, Z = 0.0;
     int64_t arg = INT64_MAX;
     for (int p = lane; p < parts; p += kWave) {
         const SplitPartial pr = pp[p];
+        Z += pr.zs;
         if (pr.s > 0.0) {
             const double bp = (double)fmaxf(pr.m, -FLT_MAX);
             const double f = exp((bp - (double)B) / T);
@@ -145,6 +148,7 @@ __global__ __launch_bounds__(256) void k_merge(SweepArgs a)
             arg = pr.arg;
     }
     S = wave_sum(S);
+    Z = wave_sum(Z);
     if constexpr (WANT_H)
         H = wave_sum(H);
     if constexpr (WANT_ARG)
@@ -152,7 +156,7 @@ __global__ __launch_bounds__(256) void k_merge(SweepArgs a)
     if (lane == 0) {
         const char *rowp = static_cast<const char *>(a.logits) +
                            (size_t)r * (size_t)a.row_stride * Elem<DT>::kSize;
-        close_row<DT, WANT_H, WANT_ARG>(a, r, rowp, a.labels[r], M, S, H, arg);
+        close_row<DT, WANT_H, WANT_ARG>(a, r, rowp, a.labels[r], M, S, H, Z, arg);
     }
 }
 
@@ -175,9 +179,21 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
     const int K = (int)a.K;
     float *out = a.logp + (size_t)r * (size_t)K;
 
+    float *qout = a.q ? a.q + (size_t)r * (size_t)K : nullptr;
     if (a.row_mask && a.row_mask[r] == 0) {
-        for (int k = tid; k < K; k += BLOCK)
+        for (int k = tid; k < K; k += BLOCK) {
             out[k] = 0.0f;
+            if (qout)
+                qout[k] = 0.0f;
+        }
+        if (a.saved && tid == 0) {
+            cev_saved z;
+            z.m_z = 0.0f;
+            z.log2_d = 0.0f;
+            z.q = 0.0f;
+            z.flags = 0;
+            a.saved[r] = z;
+        }
         return;
     }
     const char *rowp = static_cast<const char *>(a.logits) + (size_t)r * (size_t)a.row_stride * ES;
@@ -203,7 +219,7 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
     const RowGeom g = row_geom<DT, U>(rowp, V, 0, 1);
     const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp + (size_t)g.ahead * ES);
     const float c = a.c, inv_t = a.inv_t;
-    LaneState st{-INFINITY, 0.0f, 0.0f, 0.0f, -1};
+    LaneState st{-INFINITY, 0.0f, 0.0f, 0.0f, 0.0f, -1};
 
     auto excluded = [&](int64_t col) {
         bool x = false;
@@ -286,32 +302,62 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
     const float Mall = fmaxf(block_max<BLOCK>(gm, sh_f), M);
     const float Ball = fmaxf(Mall, -FLT_MAX);
     const double T = a.temperature;
+    const double s_rest = S > 0.0 ? S * exp(((double)B - (double)Ball) / T) : 0.0;
     for (int k = tid; k < K; k += BLOCK) {
         if (xcol[k] < 0) {
             out[k] = 0.0f;
+            if (qout)
+                qout[k] = 0.0f;
             continue;
         }
-        double s = S > 0.0 ? S * exp(((double)B - (double)Ball) / T) : 0.0;
+        double s = s_rest;
         for (int k2 = 0; k2 < K; ++k2)
             if (xfirst[k2] && xcol[k2] != xcol[k])
                 s += exp(((double)xz[k2] - (double)Ball) / T);
         const double u = s > 0.0 ? log(s) + ((double)Ball - (double)xz[k]) / T : -INFINITY;
         out[k] = (float)(-softplus64(u));
+        if (qout)
+            qout[k] = (float)sigmoid64(u);
+    }
+    if (a.saved && tid == 0) {
+        // The row's normaliser over all columns, for the top-K backward:
+        // d = sum_j e^{(z_j - m_z)/T} with m_z the exact row maximum.
+        double d = s_rest;
+        for (int k2 = 0; k2 < K; ++k2)
+            if (xfirst[k2])
+                d += exp(((double)xz[k2] - (double)Ball) / T);
+        cev_saved sv;
+        sv.m_z = Mall;
+        sv.log2_d = (float)(log(d) * kLog2e);
+        sv.q = 0.0f;
+        sv.flags = 1;
+        a.saved[r] = sv;
     }
 }
 
-template <int DT, int BLOCK, int U, bool SPLIT>
-hipError_t launch_sls_t(const SweepArgs &a, bool want_h, bool want_arg, hipStream_t s)
+template <int DT, int BLOCK, int U, bool SPLIT, bool WANT_Z>
+void launch_sls_z(const SweepArgs &a, bool want_h, bool want_arg, hipStream_t s)
 {
     dim3 grid((unsigned)(a.rows * (SPLIT ? a.splits : 1))), block(BLOCK);
     if (want_h && want_arg)
-        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, true, true, SPLIT>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, true, true, SPLIT, WANT_Z>), grid, block, 0, s, a);
     else if (want_h)
-        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, true, false, SPLIT>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, true, false, SPLIT, WANT_Z>), grid, block, 0, s, a);
     else if (want_arg)
-        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, false, true, SPLIT>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, false, true, SPLIT, WANT_Z>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, false, false, SPLIT>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, false, false, SPLIT, WANT_Z>), grid, block, 0, s, a);
+}
+
+// The running sum of the stored values is taken only when label smoothing
+// needs it.
+template <int DT, int BLOCK, int U, bool SPLIT>
+hipError_t launch_sls_t(const SweepArgs &a, bool want_h, bool want_arg, hipStream_t s)
+{
+    if (a.label_smoothing != 0.0)
+        launch_sls_z<DT, BLOCK, U, SPLIT, true>(a, want_h, want_arg, s);
+    else
+        launch_sls_z<DT, BLOCK, U, SPLIT, false>(a, want_h, want_arg, s);
     return hipGetLastError();
 }
 

@@ -75,7 +75,8 @@ enum cev_error {
     CEV_ETEMP = -6,        /* temperature not finite or not > 0 */
     CEV_EWORKSPACE = -7,   /* workspace too small */
     CEV_EALIAS = -8,       /* dlogits overlaps logits */
-    CEV_ELAUNCH = -9       /* the HIP runtime refused a launch */
+    CEV_ELAUNCH = -9,      /* the HIP runtime refused a launch */
+    CEV_ESMOOTH = -10      /* label_smoothing not finite or outside [0, 1] */
 };
 
 /* Bits ORed into the optional device status word. */
@@ -123,21 +124,52 @@ int sls_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_str
 /*
  * sls_topk_forward -- selective log-softmax at K gathered indices per row
  * ([swift-10337], PR information: top-K indices are supported), each in the
- * collapse-safe form logp[r,k] = -softplus(log sum_{j != i_k} e^{x_j - M}
- * + M - x_{i_k}), where the sum over the columns outside the gathered set comes
- * from one sweep and the other gathered columns are added to it (nothing is
- * subtracted, so a peaked gathered column keeps its tiny complement).
+ * collapse-safe form logp[r,k] = -softplus(u_k), u_k = log sum_{j != i_k}
+ * e^{x_j - M} + M - x_{i_k}, where the sum over the columns outside the
+ * gathered set comes from one sweep and the other gathered columns are added
+ * to it (nothing is subtracted, so a peaked gathered column keeps its tiny
+ * complement).
  *
  *   indices       [rows, K] int64 with row stride index_row_stride (>= K)
  *   logp          [rows, K] fp32 out, dense.  An index equal to ignore_index
  *                 gives 0; an index outside [0, vocab) gives 0 and sets
  *                 CEV_STATUS_BAD_INDEX; a masked row gives K zeros.
+ *   q             [rows, K] fp32 out or NULL: 1 - p at each index, computed as
+ *                 sigmoid(u_k) (0 where logp is 0 by the rules above)
+ *   saved         [rows] cev_saved out or NULL, 16-byte aligned: m_z and
+ *                 log2_d of the row for sls_topk_backward (q and the target
+ *                 are not used there; flags bit 0 = row not masked)
  *   Other arguments as sls_forward.
  */
 int sls_topk_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride,
                      int dtype, const int64_t *indices, int64_t K, int64_t index_row_stride,
                      int64_t ignore_index, double temperature, const uint8_t *row_mask,
-                     float *logp, int32_t *status, cev_stream_t stream);
+                     float *logp, float *q, void *saved, int32_t *status, cev_stream_t stream);
+
+/*
+ * sls_topk_backward -- gradient of sum_k g[r,k] logp[r,k] with respect to the
+ * stored logits, for the top-K gather of sls_topk_forward ([swift-10337], PR
+ * information: gradients flow through the top-K indices), with the 1/T of
+ * x = z/T applied:
+ *   dlogits[r, j] = (1/T) (G_j - Gs p_j),
+ * Gs = sum of g[r,k] over the entries with a valid index, G_j = the sum of
+ * g[r,k] over the entries whose index is j (repeated indices add).  A gathered
+ * column is formed as (G_j q_j - p_j (Gs - G_j)) / T from the forward's q, so
+ * a peaked column keeps its small value without cancellation; every other
+ * column is -(Gs/T) p_j.  Entries with an ignored or out-of-range index add
+ * nothing (the latter also set CEV_STATUS_BAD_INDEX); masked rows get an
+ * all-zero row.
+ *
+ *   indices, K, index_row_stride, row_mask   as passed to sls_topk_forward
+ *   g             [rows, K] fp32, dense: upstream gradient of logp[r, k]
+ *   saved, q      the sls_topk_forward outputs for the same arguments
+ *   dlogits       [rows, dlogits_row_stride] out, as ce_backward
+ */
+int sls_topk_backward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride,
+                      int dtype, const int64_t *indices, int64_t K, int64_t index_row_stride,
+                      int64_t ignore_index, double temperature, const uint8_t *row_mask,
+                      const float *g, const void *saved, const float *q, void *dlogits,
+                      int64_t dlogits_row_stride, int32_t *status, cev_stream_t stream);
 
 /*
  * ce_forward -- per-row cross-entropy forward with sparse-supervision
@@ -147,7 +179,11 @@ int sls_topk_forward(const void *logits, int64_t rows, int64_t vocab, int64_t ro
  * count, and writes the zero outputs of every ignored row, then (2) sweeps
  * only the listed rows.  No host synchronization happens in between.
  *
- *   loss          [rows] fp32 out, required: softplus(u) = -log p_t, 0 at holes
+ *   label_smoothing  eps in [0, 1] ([unsloth-2080], Summary: smoothing kept in
+ *                 the collapse-safe target term): loss = (1 - eps)(-log p_t)
+ *                 + (eps/V) sum_j (-log p_j); 0 gives the plain loss
+ *   loss          [rows] fp32 out, required: softplus(u) = -log p_t (with
+ *                 smoothing as above), 0 at holes
  *   saved         [rows] cev_saved out, required, 16-byte aligned: the record
  *                 ce_backward needs
  *   logp, entropy, argmax   as sls_forward, each optional (NULL)
@@ -166,7 +202,7 @@ int sls_topk_forward(const void *logits, int64_t rows, int64_t vocab, int64_t ro
  */
 int ce_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride, int dtype,
                const int64_t *labels, int64_t ignore_index, double temperature,
-               const uint8_t *row_mask, float *loss, void *saved, float *logp, float *entropy,
+               double label_smoothing, const uint8_t *row_mask, float *loss, void *saved, float *logp, float *entropy,
                int64_t *argmax, int64_t *valid_rows, int64_t *n_valid, void *workspace,
                size_t workspace_bytes, int32_t *status, cev_stream_t stream);
 
@@ -178,29 +214,29 @@ int ce_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stri
  * and the target column taken as -(g/T) q, q = s_others / d = 1 - p_t
  * ([liger-1555], Summary: dx_y = -sum_others / d), so each row sums to zero:
  *   dlogits[r, j] = (g[r]/T) p_j  (j != t),   dlogits[r, t] = -(g[r]/T) q_r.
- * Ignored rows get an all-zero row.  The output dtype is the logits dtype;
+ * With label smoothing eps every column also gets -(g[r]/T) eps/V and the
+ * target +(g[r]/T) eps.  Ignored rows get an all-zero row.  The output dtype is the logits dtype;
  * bf16 is rounded to nearest even from fp32.
  *
  *   g             [rows] fp32: upstream gradient of loss[r] (for a caller that
  *                 differentiates log p instead, pass g = -dL/dlogp)
  *   saved         [rows] cev_saved from ce_forward with identical arguments
+ *                 (label_smoothing included)
  *   dlogits       [rows, dlogits_row_stride] out, same dtype as logits; must
  *                 not overlap logits (CEV_EALIAS); columns >= vocab untouched
  */
 int ce_backward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride, int dtype,
                 const int64_t *labels, int64_t ignore_index, double temperature,
-                const uint8_t *row_mask, const float *g, const void *saved, void *dlogits,
+                double label_smoothing, const uint8_t *row_mask, const float *g, const void *saved, void *dlogits,
                 int64_t dlogits_row_stride, int32_t *status, cev_stream_t stream);
 
 /*
  * ce_fused -- ce_forward and ce_backward in one call, for an upstream weight g
  * that is known before the forward (token weights, a mean over rows).  When
- * each row fits in one compute unit's registers (up to 196608 bf16 or 98304
- * fp32 columns) and every row of logits and dlogits starts 16-byte aligned, a
- * single pass reads each valid row once and writes each dlogits row once: one
- * workgroup keeps the whole row resident, takes the exact non-target maximum,
- * then the target-excluded sum, closes the row in fp64 and writes
- * (g/T)(softmax - onehot) from the same registers.  This realises the
+ * every row of logits and dlogits starts 16-byte aligned, one workgroup per row
+ * sweeps the row, closes it in fp64 and right away re-reads it (from the
+ * on-chip cache, which still holds it) to write (g/T)(softmax - onehot): each
+ * row comes from HBM about once instead of twice.  This realises the
  * gradient-in-the-forward idea of the unsloth-zoo #2079 Summary quoted on the
  * Liger-Kernel PR #1555 page for a plain logit matrix.  Otherwise it runs
  * ce_forward then ce_backward.  Outputs and their meaning are those of
@@ -212,7 +248,7 @@ int ce_backward(const void *logits, int64_t rows, int64_t vocab, int64_t row_str
  */
 int ce_fused(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride, int dtype,
              const int64_t *labels, int64_t ignore_index, double temperature,
-             const uint8_t *row_mask, const float *g, float *loss, void *saved, float *logp,
+             double label_smoothing, const uint8_t *row_mask, const float *g, float *loss, void *saved, float *logp,
              float *entropy, int64_t *argmax, void *dlogits, int64_t dlogits_row_stride,
              int64_t *valid_rows, int64_t *n_valid, void *workspace, size_t workspace_bytes,
              int32_t *status, cev_stream_t stream);

@@ -44,7 +44,7 @@ def strided_dev(a: np.ndarray, stride: int) -> torch.Tensor:
     return to_dev(pad)[:, :V]
 
 
-def run_ce(w, entropy=True, argmax=True, logits_dev=None):
+def run_ce(w, entropy=True, argmax=True, logits_dev=None, label_smoothing=0.0):
     """ce_forward + ce_backward on a workload dict; returns numpy outputs."""
     logits = logits_dev if logits_dev is not None else to_dev(w["logits"])
     labels = to_dev(w["labels"])
@@ -53,8 +53,9 @@ def run_ce(w, entropy=True, argmax=True, logits_dev=None):
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
     T = w["temperature"]
     out = cev.ce_forward(logits, labels, T, row_mask=mask, entropy=entropy, argmax=argmax,
-                         status=status)
-    dl = cev.ce_backward(logits, labels, g, out["saved"], T, row_mask=mask, status=status)
+                         status=status, label_smoothing=label_smoothing)
+    dl = cev.ce_backward(logits, labels, g, out["saved"], T, row_mask=mask, status=status,
+                         label_smoothing=label_smoothing)
     torch.cuda.synchronize()
     res = {k: (None if v is None else to_host(v)) for k, v in out.items() if k != "workspace"}
     res["dlogits"] = to_host(dl)
@@ -83,3 +84,23 @@ def run_topk(w, indices=None):
     lp = cev.sls_topk_forward(logits, idx, w["temperature"], row_mask=mask, status=status)
     torch.cuda.synchronize()
     return to_host(lp), int(status.item())
+
+
+def run_topk_fb(w, indices, g, logits_dev=None, dl_stride=None):
+    """sls_topk_forward (with q and the saved record) then sls_topk_backward;
+    returns numpy logp, q, dlogits and the status word."""
+    logits = logits_dev if logits_dev is not None else to_dev(w["logits"])
+    idx = to_dev(np.ascontiguousarray(indices))
+    mask = None if w.get("row_mask") is None else to_dev(w["row_mask"])
+    gk = to_dev(np.ascontiguousarray(g, dtype=np.float32))
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    T = w["temperature"]
+    lp, q, saved = cev.sls_topk_forward(logits, idx, T, row_mask=mask, status=status, saved=True)
+    R, V = logits.shape
+    dl = None
+    if dl_stride is not None:
+        dl = torch.zeros((R, dl_stride), dtype=logits.dtype, device=DEV)[:, :V]
+    dl = cev.sls_topk_backward(logits, idx, gk, saved, q, T, row_mask=mask, dlogits=dl,
+                               status=status)
+    torch.cuda.synchronize()
+    return dict(logp=to_host(lp), q=to_host(q), dlogits=to_host(dl), status=int(status.item()))

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "cevocab.h")
 
 E = dict(OK=0, NULL=-1, SHAPE=-2, STRIDE=-3, ALIGN=-4, DTYPE=-5, TEMP=-6, WORKSPACE=-7,
-         ALIAS=-8, LAUNCH=-9)
+         ALIAS=-8, LAUNCH=-9, SMOOTH=-10)
 
 
 @pytest.fixture(scope="module")
@@ -32,8 +32,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = set(declared_functions())
-    assert {"sls_forward", "sls_topk_forward", "ce_forward", "ce_backward", "ce_fused",
-            "cev_workspace_size", "cev_status_string", "cev_version"} <= names
+    assert {"sls_forward", "sls_topk_forward", "sls_topk_backward", "ce_forward", "ce_backward",
+            "ce_fused", "cev_workspace_size", "cev_status_string", "cev_version"} <= names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -54,13 +54,14 @@ def test_codes_match_header():
 
 
 def test_version_and_strings(lib):
-    assert lib.cev_version() == 100
+    assert lib.cev_version() == 200
     for code in E.values():
         assert lib.cev_status_string(code)
     assert lib.cev_workspace_size(10, 100, 0) == 88          # list + count only
     assert lib.cev_workspace_size(8192, 152064, 1) == 8193 * 8  # enough rows: no split
-    # few long rows split over workgroups: 32-byte partial records follow the list
-    assert lib.cev_workspace_size(64, 152064, 1) == 544 + 64 * 9 * 32
+    # few long rows split over workgroups: 40-byte partial records (max, its
+    # column, sum, entropy term, value sum) follow the 32-byte aligned list
+    assert lib.cev_workspace_size(64, 152064, 1) == 544 + 64 * 9 * 40
     assert lib.cev_workspace_size(-1, 100, 0) == 0
     assert lib.cev_workspace_size(10, 100, 5) == 0
 
@@ -107,28 +108,55 @@ def test_sls_forward_validation(lib):
 def test_topk_validation(lib):
     def call(**kw):
         a = dict(logits=A, rows=4, vocab=100, stride=100, dtype=1, idx=A, K=8, istride=8,
-                 ig=-100, T=0.7, mask=None, logp=A, status=None)
+                 ig=-100, T=0.7, mask=None, logp=A, q=None, saved=None, status=None)
         a.update(kw)
         return lib.sls_topk_forward(a["logits"], a["rows"], a["vocab"], a["stride"], a["dtype"],
                                     a["idx"], a["K"], a["istride"], a["ig"], a["T"], a["mask"],
-                                    a["logp"], a["status"], None)
+                                    a["logp"], a["q"], a["saved"], a["status"], None)
     assert call(K=0) == E["SHAPE"]
     assert call(K=1025) == E["SHAPE"]
     assert call(istride=7) == E["STRIDE"]
     assert call(idx=None) == E["NULL"]
     assert call(idx=A + 4) == E["ALIGN"]
+    assert call(q=A + 2) == E["ALIGN"]
+    assert call(saved=A + 8) == E["ALIGN"]
     assert call(T=0.0) == E["TEMP"]
+    assert call(rows=0) == E["OK"]
+
+
+def test_topk_backward_validation(lib):
+    def call(**kw):
+        a = dict(logits=A, rows=4, vocab=100, stride=100, dtype=1, idx=A, K=8, istride=8,
+                 ig=-100, T=0.7, mask=None, g=A, saved=A, q=A, dl=B, dstride=100, status=None)
+        a.update(kw)
+        return lib.sls_topk_backward(a["logits"], a["rows"], a["vocab"], a["stride"], a["dtype"],
+                                     a["idx"], a["K"], a["istride"], a["ig"], a["T"], a["mask"],
+                                     a["g"], a["saved"], a["q"], a["dl"], a["dstride"],
+                                     a["status"], None)
+    assert call(K=0) == E["SHAPE"]
+    assert call(K=1025) == E["SHAPE"]
+    assert call(istride=7) == E["STRIDE"]
+    assert call(dstride=99) == E["STRIDE"]
+    for k in ("idx", "g", "saved", "q", "dl"):
+        assert call(**{k: None}) == E["NULL"], k
+    assert call(saved=A + 8) == E["ALIGN"]
+    assert call(q=A + 2) == E["ALIGN"]
+    assert call(dl=B + 1) == E["ALIGN"]
+    assert call(dl=A) == E["ALIAS"]
+    assert call(T=float("inf")) == E["TEMP"]
+    assert call(dtype=2) == E["DTYPE"]
     assert call(rows=0) == E["OK"]
 
 
 def test_ce_forward_validation(lib):
     def call(**kw):
         a = dict(logits=A, rows=4, vocab=100, stride=100, dtype=0, labels=A, ig=-100, T=1.0,
-                 mask=None, loss=A, saved=A, logp=None, ent=None, arg=None, vr=None, nv=None,
-                 ws=None, wsb=0, status=None)
+                 eps=0.0, mask=None, loss=A, saved=A, logp=None, ent=None, arg=None, vr=None,
+                 nv=None, ws=None, wsb=0, status=None)
         a.update(kw)
         return lib.ce_forward(a["logits"], a["rows"], a["vocab"], a["stride"], a["dtype"],
-                              a["labels"], a["ig"], a["T"], a["mask"], a["loss"], a["saved"],
+                              a["labels"], a["ig"], a["T"], a["eps"], a["mask"], a["loss"],
+                              a["saved"],
                               a["logp"], a["ent"], a["arg"], a["vr"], a["nv"], a["ws"], a["wsb"],
                               a["status"], None)
     assert call() == E["NULL"]                       # no list/count and no workspace
@@ -138,16 +166,20 @@ def test_ce_forward_validation(lib):
     assert call(vr=A, nv=A, loss=None) == E["NULL"]
     assert call(vr=A, nv=A, saved=None) == E["NULL"]
     assert call(vr=A, nv=A, dtype=3) == E["DTYPE"]
+    for eps in (-0.1, 1.5, float("nan"), float("inf")):
+        assert call(vr=A, nv=A, eps=eps) == E["SMOOTH"]
+        assert call(rows=0, eps=eps) == E["SMOOTH"]
     assert call(rows=0) == E["OK"]
 
 
 def test_ce_backward_validation(lib):
     def call(**kw):
         a = dict(logits=A, rows=4, vocab=100, stride=100, dtype=1, labels=A, ig=-100, T=1.0,
-                 mask=None, g=A, saved=A, dl=B, dstride=100, status=None)
+                 eps=0.0, mask=None, g=A, saved=A, dl=B, dstride=100, status=None)
         a.update(kw)
         return lib.ce_backward(a["logits"], a["rows"], a["vocab"], a["stride"], a["dtype"],
-                               a["labels"], a["ig"], a["T"], a["mask"], a["g"], a["saved"],
+                               a["labels"], a["ig"], a["T"], a["eps"], a["mask"], a["g"],
+                               a["saved"],
                                a["dl"], a["dstride"], a["status"], None)
     assert call(dl=A) == E["ALIAS"]
     assert call(dl=A + 2 * 350) == E["ALIAS"]                 # overlaps the last row
@@ -158,17 +190,18 @@ def test_ce_backward_validation(lib):
     assert call(saved=A + 8) == E["ALIGN"]
     assert call(dl=B + 1) == E["ALIGN"]
     assert call(T=float("nan")) == E["TEMP"]
+    assert call(eps=-1e-9) == E["SMOOTH"]
     assert call(rows=0) == E["OK"]
 
 
 def test_ce_fused_validation(lib):
     def call(**kw):
         a = dict(logits=A, rows=4, vocab=100, stride=100, dtype=1, labels=A, ig=-100, T=1.0,
-                 mask=None, g=A, loss=A, saved=A, logp=None, ent=None, arg=None, dl=B,
+                 eps=0.0, mask=None, g=A, loss=A, saved=A, logp=None, ent=None, arg=None, dl=B,
                  dstride=100, vr=None, nv=None, ws=None, wsb=0, status=None)
         a.update(kw)
         return lib.ce_fused(a["logits"], a["rows"], a["vocab"], a["stride"], a["dtype"],
-                            a["labels"], a["ig"], a["T"], a["mask"], a["g"], a["loss"],
+                            a["labels"], a["ig"], a["T"], a["eps"], a["mask"], a["g"], a["loss"],
                             a["saved"], a["logp"], a["ent"], a["arg"], a["dl"], a["dstride"],
                             a["vr"], a["nv"], a["ws"], a["wsb"], a["status"], None)
     assert call(dl=A) == E["ALIAS"]
@@ -182,6 +215,7 @@ def test_ce_fused_validation(lib):
     assert call(vr=A, ws=A, wsb=39) == E["WORKSPACE"]
     assert call(T=0.0) == E["TEMP"]
     assert call(dtype=9) == E["DTYPE"]
+    assert call(eps=1.0 + 1e-12) == E["SMOOTH"]
     assert call(rows=0) == E["OK"]
 
 

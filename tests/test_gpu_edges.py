@@ -252,7 +252,7 @@ def test_temperature_scaling_identity():
     assert np.array_equal(a["argmax"], b["argmax"])
 
 
-def _ce_raw(w, workspace_bytes):
+def _ce_raw(w, workspace_bytes, eps=0.0):
     """ce_forward through the C ABI with an explicit workspace size (0 = none),
     so the whole-row and the split-row sweeps can both be exercised."""
     from gpu_helpers import DEV, to_dev
@@ -271,7 +271,7 @@ def _ce_raw(w, workspace_bytes):
     nv = torch.empty(1, dtype=torch.int64, device=DEV)
     ws = torch.empty(max(workspace_bytes, 1), dtype=torch.uint8, device=DEV)
     rc = _lib.get().ce_forward(logits.data_ptr(), R, V, V, dt, labels.data_ptr(), -100,
-                               float(w["temperature"]),
+                               float(w["temperature"]), float(eps),
                                None if mask is None else mask.data_ptr(), loss.data_ptr(),
                                saved.data_ptr(), logp.data_ptr(), ent.data_ptr(), arg.data_ptr(),
                                vr.data_ptr(), nv.data_ptr(),

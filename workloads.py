@@ -114,13 +114,20 @@ def chunk(rows=4096, vocab=32768, K=8, seed=1):
                 indices=indices, g=np.ones(rows, dtype=np.float32))
 
 
-def grpo(rows=8192, vocab=152064, seed=2, temperature=1.0):
+def grpo_rows(rows=8192, vocab=152064, seed=2):
+    """The per-row draws of grpo() (shift, labels, row mask, g) without the
+    logit matrix."""
     rng = np.random.default_rng(seed)
     shift = rng.uniform(-5.0, 5.0, rows).astype(np.float32)
     labels = rng.integers(0, vocab, rows).astype(np.int64)
     row_mask = np.ones(rows, dtype=np.uint8)
     row_mask[rng.permutation(rows)[:rows // 10]] = 0
     g = rng.standard_normal(rows, dtype=np.float32)
+    return shift, labels, row_mask, g
+
+
+def grpo(rows=8192, vocab=152064, seed=2, temperature=1.0):
+    shift, labels, row_mask, g = grpo_rows(rows, vocab, seed)
 
     def fill(b, gen, r0, r1):
         z = 3.0 * gen.standard_normal((r1 - r0, vocab), dtype=np.float32)
