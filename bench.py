@@ -266,6 +266,47 @@ def main():
     fused_wall = (time.perf_counter() - t0) / args.steps * 1e3
     fused_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in fev]))
 
+    # One rank's share of an 8-way vocab-parallel step: its contiguous
+    # [R, V/8] shard, the shard sweep, the merge of all 8 shards' records
+    # (the other 7 made once, untimed, standing in for the all-gather), and
+    # the shard backward.
+    P = 8
+    Vs = V // P
+    shard = logits[:, :Vs].contiguous()
+    parts = torch.empty((P, R, cev.PARTIAL_BYTES), dtype=torch.uint8, device=dev)
+    for p in range(1, P):
+        cev.ce_vocab_shard_forward(logits[:, p * Vs:(p + 1) * Vs], labels, p * Vs, V, T,
+                                   row_mask=mask, partials=parts[p])
+    dls = torch.empty((R, Vs), dtype=torch.bfloat16, device=dev)
+
+    def shard_step(ev=None):
+        if ev:
+            ev[0].record()
+        cev.ce_vocab_shard_forward(shard, labels, 0, V, T, row_mask=mask, partials=parts[0])
+        if ev:
+            ev[1].record()
+        mo = cev.ce_vocab_merge(parts, labels, V, T, row_mask=mask, argmax=True)
+        if ev:
+            ev[2].record()
+        cev.ce_vocab_shard_backward(shard, labels, g, mo["saved"], 0, V, T, row_mask=mask,
+                                    dlogits=dls)
+        if ev:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        shard_step()
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in sev:
+        shard_step(e)
+    torch.cuda.synchronize()
+    shard_wall = (time.perf_counter() - t0) / args.steps * 1e3
+    s_fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in sev]))
+    s_mrg = float(np.mean([e[1].elapsed_time(e[2]) for e in sev]))
+    s_bwd = float(np.mean([e[2].elapsed_time(e[3]) for e in sev]))
+    del shard, dls, parts
+
     ES = 2
     fwd_bytes = n_valid * V * ES                    # valid rows read once
     bwd_bytes = n_valid * V * ES + R * V * ES       # valid rows re-read, every row written
@@ -309,9 +350,18 @@ def main():
                   "algorithmic_bytes": fwd_bytes + R * V * ES,
                   "GBps": (fwd_bytes + R * V * ES) / (fused_ms / 1e3) / 1e9,
                   "frac_of_peak": (fwd_bytes + R * V * ES) / (fused_ms / 1e3) / 1e9 / PEAK_HBM_GBS},
+        "vocab_shard": {"entry": f"one rank of {P}-way vocab parallelism: "
+                                 "ce_vocab_shard_forward on its contiguous shard, ce_vocab_merge "
+                                 f"of {P} shards' records, ce_vocab_shard_backward",
+                        "shard": [R, Vs], "ms_per_step": shard_wall,
+                        "kernels_ms": {"shard_forward": s_fwd, "merge": s_mrg,
+                                       "shard_backward": s_bwd},
+                        "shard_forward_GBps": n_valid * Vs * ES / (s_fwd / 1e3) / 1e9,
+                        "shard_backward_GBps": (n_valid + R) * Vs * ES / (s_bwd / 1e3) / 1e9},
     }
     log(f"[bench] {ms_step:.3f} ms/step, fwd {fwd:.3f} ms, bwd {bwd:.3f} ms; "
-        f"fused {fused_wall:.3f} ms/step")
+        f"fused {fused_wall:.3f} ms/step; vocab shard {shard_wall:.3f} ms/step "
+        f"(fwd {s_fwd:.3f}, merge {s_mrg:.3f}, bwd {s_bwd:.3f})")
     if args.copy_calibration:
         # torch's elementwise add: reads exactly 2^30 bytes, writes exactly 2^30 bytes
         src = torch.ones(2 ** 28, dtype=torch.float32, device=dev)

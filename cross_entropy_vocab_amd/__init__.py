@@ -17,15 +17,20 @@ import torch
 from . import _lib
 
 __all__ = ["sls_forward", "sls_topk_forward", "sls_topk_backward", "ce_forward",
-           "ce_backward", "ce_fused", "workspace_size",
+           "ce_backward", "ce_fused", "ce_vocab_shard_forward", "ce_vocab_merge",
+           "ce_vocab_shard_backward", "workspace_size",
            "status_string", "version", "CEV_F32", "CEV_BF16", "STATUS_BAD_LABEL",
-           "STATUS_BAD_INDEX", "SAVED_BYTES", "CevError"]
+           "STATUS_BAD_INDEX", "STATUS_BAD_PARTS", "SAVED_BYTES", "PARTIAL_BYTES", "CevError"]
 
 CEV_F32 = 0
 CEV_BF16 = 1
 STATUS_BAD_LABEL = 1
 STATUS_BAD_INDEX = 2
+STATUS_BAD_PARTS = 4
 SAVED_BYTES = 16
+PARTIAL_BYTES = 48
+PART_ENTROPY = 1
+PART_VALUE_SUM = 2
 
 
 class CevError(RuntimeError):
@@ -308,3 +313,77 @@ def ce_fused(logits, labels, g, temperature=1.0, row_mask=None, ignore_index=-10
                              _ptr(status), _stream(dev))
     _check("ce_fused", rc)
     return o
+
+
+def ce_vocab_shard_forward(logits, labels, col_offset, vocab, temperature=1.0, row_mask=None,
+                           ignore_index=-100, entropy=False, value_sum=False, partials=None,
+                           status=None):
+    """Partial records [rows, 48] uint8 of one vocab shard: `logits` holds
+    global columns [col_offset, col_offset + logits.shape[1]) of each row."""
+    rows, sv, stride = _check_logits(logits)
+    dev = logits.device
+    _dev(labels, "labels", torch.int64, (rows,), dev)
+    m = _mask(row_mask, rows, dev)
+    _dev(status, "status", torch.int32, (1,), dev)
+    if partials is None:
+        partials = torch.empty((rows, PARTIAL_BYTES), dtype=torch.uint8, device=dev)
+    else:
+        _dev(partials, "partials", torch.uint8, (rows, PARTIAL_BYTES), dev)
+    what = (PART_ENTROPY if entropy else 0) | (PART_VALUE_SUM if value_sum else 0)
+    rc = _lib.get().ce_vocab_shard_forward(_ptr(logits), rows, sv, stride, _dtype_code(logits),
+                                           int(col_offset), int(vocab), _ptr(labels),
+                                           int(ignore_index), float(temperature), _ptr(m), what,
+                                           _ptr(partials), _ptr(status), _stream(dev))
+    _check("ce_vocab_shard_forward", rc)
+    return partials
+
+
+def ce_vocab_merge(partials, labels, vocab, temperature=1.0, row_mask=None, ignore_index=-100,
+                   label_smoothing=0.0, logp=True, entropy=False, argmax=False, status=None):
+    """Merge [parts, rows, 48] partial records (shard order = ascending column
+    ranges) into the ce_forward outputs of the whole rows: a dict with loss,
+    saved and optionally logp, entropy, argmax."""
+    if partials.dim() != 3 or partials.shape[2] != PARTIAL_BYTES:
+        raise ValueError("partials must be [parts, rows, 48] uint8")
+    parts, rows = partials.shape[0], partials.shape[1]
+    dev = partials.device
+    _dev(partials, "partials", torch.uint8, (parts, rows, PARTIAL_BYTES), dev)
+    _dev(labels, "labels", torch.int64, (rows,), dev)
+    m = _mask(row_mask, rows, dev)
+    _dev(status, "status", torch.int32, (1,), dev)
+    o = {
+        "loss": torch.empty(rows, dtype=torch.float32, device=dev),
+        "saved": torch.empty((rows, SAVED_BYTES), dtype=torch.uint8, device=dev),
+        "logp": torch.empty(rows, dtype=torch.float32, device=dev) if logp else None,
+        "entropy": torch.empty(rows, dtype=torch.float32, device=dev) if entropy else None,
+        "argmax": torch.empty(rows, dtype=torch.int64, device=dev) if argmax else None,
+    }
+    rc = _lib.get().ce_vocab_merge(_ptr(partials), parts, rows, int(vocab), _ptr(labels),
+                                   int(ignore_index), float(temperature), float(label_smoothing),
+                                   _ptr(m), _ptr(o["loss"]), _ptr(o["saved"]), _ptr(o["logp"]),
+                                   _ptr(o["entropy"]), _ptr(o["argmax"]), _ptr(status),
+                                   _stream(dev))
+    _check("ce_vocab_merge", rc)
+    return o
+
+
+def ce_vocab_shard_backward(logits, labels, g, saved, col_offset, vocab, temperature=1.0,
+                            row_mask=None, ignore_index=-100, label_smoothing=0.0, dlogits=None,
+                            status=None):
+    """ce_backward over one vocab shard's columns, from the merged record."""
+    rows, sv, stride = _check_logits(logits)
+    dev = logits.device
+    _dev(labels, "labels", torch.int64, (rows,), dev)
+    _dev(g, "g", torch.float32, (rows,), dev)
+    _dev(saved, "saved", torch.uint8, (rows, SAVED_BYTES), dev)
+    m = _mask(row_mask, rows, dev)
+    _dev(status, "status", torch.int32, (1,), dev)
+    dlogits, dstride = _dlogits(dlogits, logits, rows, sv, dev)
+    rc = _lib.get().ce_vocab_shard_backward(_ptr(logits), rows, sv, stride, _dtype_code(logits),
+                                            int(col_offset), int(vocab), _ptr(labels),
+                                            int(ignore_index), float(temperature),
+                                            float(label_smoothing), _ptr(m), _ptr(g),
+                                            _ptr(saved), _ptr(dlogits), dstride, _ptr(status),
+                                            _stream(dev))
+    _check("ce_vocab_shard_backward", rc)
+    return dlogits

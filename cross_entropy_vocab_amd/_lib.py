@@ -16,6 +16,7 @@ I64 = ctypes.c_int64
 I32 = ctypes.c_int
 D = ctypes.c_double
 SZ = ctypes.c_size_t
+U32 = ctypes.c_uint
 
 # name -> (restype, argtypes), mirroring include/cevocab.h
 SIGNATURES = {
@@ -28,6 +29,11 @@ SIGNATURES = {
     "ce_backward": (I32, [P, I64, I64, I64, I32, P, I64, D, D, P, P, P, P, I64, P, P]),
     "ce_fused": (I32, [P, I64, I64, I64, I32, P, I64, D, D, P, P, P, P, P, P, P, P, I64, P, P, P,
                        SZ, P, P]),
+    "ce_vocab_shard_forward": (I32, [P, I64, I64, I64, I32, I64, I64, P, I64, D, P, U32, P, P,
+                                     P]),
+    "ce_vocab_merge": (I32, [P, I64, I64, I64, P, I64, D, D, P, P, P, P, P, P, P, P]),
+    "ce_vocab_shard_backward": (I32, [P, I64, I64, I64, I32, I64, I64, P, I64, D, D, P, P, P, P,
+                                      I64, P, P]),
     "cev_workspace_size": (SZ, [I64, I64, I32]),
     "cev_status_string": (ctypes.c_char_p, [I32]),
     "cev_version": (I32, []),

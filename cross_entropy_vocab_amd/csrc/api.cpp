@@ -18,6 +18,7 @@ using cev::SweepArgs;
 constexpr int64_t kMaxRows = 1 << 22;         // one workgroup per row; the grid stays < 2^32 work-items
 constexpr int64_t kMaxVocab = INT32_MAX / 2;  // step codes are 32-bit
 constexpr int64_t kMaxK = 1024;               // gathered indices per row held in LDS
+constexpr int64_t kMaxParts = 4096;           // shards merged by ce_vocab_merge
 
 int elem_size(int dtype) { return dtype == CEV_F32 ? 4 : 2; }
 
@@ -333,6 +334,8 @@ int ce_backward(const void *logits, int64_t rows, int64_t vocab, int64_t row_str
     a.rows = rows;
     a.vocab = vocab;
     a.row_stride = row_stride;
+    a.col_offset = 0;
+    a.vocab_total = vocab;
     a.labels = labels;
     a.ignore_index = ignore_index;
     a.row_mask = row_mask;
@@ -443,6 +446,144 @@ int ce_fused(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride
     fa.d_row_stride = dlogits_row_stride;
     fa.status = status;
     return launch_status(cev::launch_fused(dtype, fa, entropy != nullptr, to_hip(stream)));
+}
+
+// Checks of a shard's column range [col_offset, col_offset + shard_vocab) of a
+// vocab-wide row.
+static int check_shard(int64_t shard_vocab, int64_t col_offset, int64_t vocab)
+{
+    if (vocab < 1 || vocab > kMaxVocab || col_offset < 0 || shard_vocab > vocab ||
+        col_offset > vocab - shard_vocab)
+        return CEV_ESHAPE;
+    return CEV_OK;
+}
+
+int ce_vocab_shard_forward(const void *logits, int64_t rows, int64_t shard_vocab,
+                           int64_t row_stride, int dtype, int64_t col_offset, int64_t vocab,
+                           const int64_t *labels, int64_t ignore_index, double temperature,
+                           const uint8_t *row_mask, unsigned what, void *partials,
+                           int32_t *status, cev_stream_t stream)
+{
+    bool done;
+    int rc = check_common(logits, rows, shard_vocab, row_stride, dtype, temperature, &done);
+    if (rc != CEV_OK)
+        return rc;
+    if ((rc = check_shard(shard_vocab, col_offset, vocab)) != CEV_OK)
+        return rc;
+    if (done)
+        return CEV_OK;
+    if (!labels || !partials)
+        return CEV_ENULL;
+    if (!aligned(labels, 8) || !aligned(partials, 8) || !aligned(status, 4))
+        return CEV_EALIGN;
+    cev::ShardArgs a{};
+    a.logits = logits;
+    a.rows = rows;
+    a.vocab = shard_vocab;
+    a.row_stride = row_stride;
+    a.col_offset = col_offset;
+    a.vocab_total = vocab;
+    a.labels = labels;
+    a.ignore_index = ignore_index;
+    a.row_mask = row_mask;
+    a.c = (float)(1.4426950408889634074 / temperature);
+    a.inv_t = (float)(1.0 / temperature);
+    a.partials = static_cast<cev_vocab_partial *>(partials);
+    a.status = status;
+    return launch_status(cev::launch_shard_sweep(dtype, a, (what & CEV_PART_ENTROPY) != 0,
+                                                 (what & CEV_PART_VALUE_SUM) != 0,
+                                                 to_hip(stream)));
+}
+
+int ce_vocab_merge(const void *partials, int64_t parts, int64_t rows, int64_t vocab,
+                   const int64_t *labels, int64_t ignore_index, double temperature,
+                   double label_smoothing, const uint8_t *row_mask, float *loss, void *saved,
+                   float *logp, float *entropy, int64_t *argmax, int32_t *status,
+                   cev_stream_t stream)
+{
+    if (!(std::isfinite(temperature) && temperature > 0.0))
+        return CEV_ETEMP;
+    if (!smoothing_ok(label_smoothing))
+        return CEV_ESMOOTH;
+    if (parts < 1 || parts > kMaxParts || rows < 0 || rows > kMaxRows || vocab < 1 ||
+        vocab > kMaxVocab)
+        return CEV_ESHAPE;
+    if (rows == 0)
+        return CEV_OK;
+    if (!partials || !labels || !loss || !saved)
+        return CEV_ENULL;
+    if (!aligned(partials, 8) || !aligned(labels, 8) || !aligned(loss, 4) ||
+        !aligned(saved, 16) || !aligned(logp, 4) || !aligned(entropy, 4) ||
+        !aligned(argmax, 8) || !aligned(status, 4))
+        return CEV_EALIGN;
+    cev::MergeArgs a{};
+    a.partials = static_cast<const cev_vocab_partial *>(partials);
+    a.parts = parts;
+    a.rows = rows;
+    a.vocab = vocab;
+    a.labels = labels;
+    a.ignore_index = ignore_index;
+    a.row_mask = row_mask;
+    a.temperature = temperature;
+    a.label_smoothing = label_smoothing;
+    a.loss = loss;
+    a.logp = logp;
+    a.entropy = entropy;
+    a.argmax = argmax;
+    a.saved = static_cast<cev_saved *>(saved);
+    a.status = status;
+    return launch_status(cev::launch_vocab_merge(a, to_hip(stream)));
+}
+
+int ce_vocab_shard_backward(const void *logits, int64_t rows, int64_t shard_vocab,
+                            int64_t row_stride, int dtype, int64_t col_offset, int64_t vocab,
+                            const int64_t *labels, int64_t ignore_index, double temperature,
+                            double label_smoothing, const uint8_t *row_mask, const float *g,
+                            const void *saved, void *dlogits, int64_t dlogits_row_stride,
+                            int32_t *status, cev_stream_t stream)
+{
+    bool done;
+    int rc = check_common(logits, rows, shard_vocab, row_stride, dtype, temperature, &done);
+    if (rc != CEV_OK)
+        return rc;
+    if ((rc = check_shard(shard_vocab, col_offset, vocab)) != CEV_OK)
+        return rc;
+    if (!smoothing_ok(label_smoothing))
+        return CEV_ESMOOTH;
+    if (done)
+        return CEV_OK;
+    if (dlogits_row_stride < shard_vocab)
+        return CEV_ESTRIDE;
+    if (dlogits_row_stride > INT64_MAX / 4 / rows)
+        return CEV_ESHAPE;
+    if (!labels || !g || !saved || !dlogits)
+        return CEV_ENULL;
+    const int es = elem_size(dtype);
+    if (!aligned(labels, 8) || !aligned(g, 4) || !aligned(saved, 16) ||
+        !aligned(dlogits, (uintptr_t)es) || !aligned(status, 4))
+        return CEV_EALIGN;
+    if (overlaps(logits, row_stride, dlogits, dlogits_row_stride, rows, shard_vocab, es))
+        return CEV_EALIAS;
+    BackwardArgs a{};
+    a.logits = logits;
+    a.rows = rows;
+    a.vocab = shard_vocab;
+    a.row_stride = row_stride;
+    a.col_offset = col_offset;
+    a.vocab_total = vocab;
+    a.labels = labels;
+    a.ignore_index = ignore_index;
+    a.row_mask = row_mask;
+    a.g = g;
+    a.saved = static_cast<const cev_saved *>(saved);
+    a.dlogits = dlogits;
+    a.d_row_stride = dlogits_row_stride;
+    a.temperature = temperature;
+    a.label_smoothing = label_smoothing;
+    a.c = (float)(1.4426950408889634074 / temperature);
+    a.inv_t = (float)(1.0 / temperature);
+    a.status = status;
+    return launch_status(cev::launch_backward(dtype, a, to_hip(stream)));
 }
 
 const char *cev_status_string(int code)

@@ -88,10 +88,12 @@ __global__ __launch_bounds__(BLOCK) void k_backward(BackwardArgs a, int slices, 
     const int64_t r = reverse ? a.rows - 1 - rb : rb;
     const int sl = blockIdx.x % slices;
     const int64_t V = a.vocab;
-    const int64_t t = a.labels[r];
+    const int64_t tg = a.labels[r];
     const bool masked = a.row_mask && a.row_mask[r] == 0;
-    const bool ignored = masked || t == a.ignore_index;
-    const bool bad = !ignored && (t < 0 || t >= V);
+    const bool ignored = masked || tg == a.ignore_index;
+    const bool bad = !ignored && (tg < 0 || tg >= a.vocab_total);
+    // The target's column here; outside [0, V) when another shard holds it.
+    const int64_t t = tg - a.col_offset;
     const cev_saved sv = a.saved[r];
     if (bad && sl == 0 && tid == 0 && a.status)
         atomicOr(a.status, (int32_t)CEV_STATUS_BAD_LABEL);
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(BLOCK) void k_backward(BackwardArgs a, int slices, 
         const float gp = a.g[r] * a.inv_t;
         const float ag = fabsf(gp);
         const float eps = (float)a.label_smoothing;
-        const float epv = (float)(a.label_smoothing / (double)V);
+        const float epv = (float)(a.label_smoothing / (double)a.vocab_total);
         rc.sgn = __float_as_uint(gp) & 0x80000000u;
         rc.kexp = sv.log2_d - __log2f(ag);
         rc.ev = ag * epv;

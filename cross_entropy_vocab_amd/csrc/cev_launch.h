@@ -51,6 +51,25 @@ struct SplitPartial {
     double zs;                 // sum of the part's non-target stored values
 };
 
+// Launch shape for a row of nvec 16-byte vectors: the widest workgroup whose
+// waves each still get at least four full steps.  512 threads x 2 vectors was
+// the fastest shape measured on MI355X for 152064-wide bf16 rows (6.7 TB/s of
+// the ~7.0 TB/s streaming-read ceiling), 256 x 4 next.
+struct Shape {
+    int block, U;
+};
+
+inline Shape pick_shape(int64_t nvec)
+{
+    if (nvec >= 4 * 512 * 2)
+        return {512, 2};
+    if (nvec >= 4 * 256 * 4)
+        return {256, 4};
+    if (nvec >= 4 * 128 * 4)
+        return {128, 4};
+    return {64, 4};
+}
+
 // Workgroups per row for the split forward: enough workgroups to fill the
 // chip when rows are few (< 128), each part at least 2048 16-byte vectors.
 int64_t sweep_splits(int64_t rows, int64_t vocab, int dtype);
@@ -74,8 +93,10 @@ struct CompactArgs {
 struct BackwardArgs {
     const void *logits;
     int64_t rows;
-    int64_t vocab;
+    int64_t vocab;             // columns held here (a shard's width for the vocab-parallel form)
     int64_t row_stride;
+    int64_t col_offset;        // global column of element 0 (0 unless vocab-parallel)
+    int64_t vocab_total;       // full vocabulary width: label range and eps / V
     const int64_t *labels;
     int64_t ignore_index;
     const uint8_t *row_mask;
@@ -113,6 +134,46 @@ struct TopkBackwardArgs {
 };
 
 hipError_t launch_topk_backward(int dtype, const TopkBackwardArgs &a, hipStream_t stream);
+
+// Vocab-parallel shard sweep: one partial record per row over one shard.
+struct ShardArgs {
+    const void *logits;
+    int64_t rows;
+    int64_t vocab;             // the shard's width
+    int64_t row_stride;
+    int64_t col_offset;
+    int64_t vocab_total;
+    const int64_t *labels;
+    int64_t ignore_index;
+    const uint8_t *row_mask;
+    float c;                   // log2(e) / T
+    float inv_t;               // 1 / T
+    cev_vocab_partial *partials;
+    int32_t *status;
+};
+
+// Merge of P shards' partial records, then the closing step.
+struct MergeArgs {
+    const cev_vocab_partial *partials;  // [parts][rows]
+    int64_t parts;
+    int64_t rows;
+    int64_t vocab;             // full width
+    const int64_t *labels;
+    int64_t ignore_index;
+    const uint8_t *row_mask;
+    double temperature;
+    double label_smoothing;
+    float *loss;
+    float *logp;
+    float *entropy;
+    int64_t *argmax;
+    cev_saved *saved;
+    int32_t *status;
+};
+
+hipError_t launch_shard_sweep(int dtype, const ShardArgs &a, bool want_entropy, bool want_zsum,
+                              hipStream_t stream);
+hipError_t launch_vocab_merge(const MergeArgs &a, hipStream_t stream);
 
 // Forward + backward in one call, one workgroup per row (rows 16-byte aligned).
 struct FusedArgs {

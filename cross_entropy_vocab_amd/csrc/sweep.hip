@@ -375,25 +375,6 @@ template <int DT> hipError_t launch_merge_t(const SweepArgs &a, bool want_h, boo
     return hipGetLastError();
 }
 
-// Launch shape for a row of nvec 16-byte vectors: the widest workgroup whose
-// waves each still get at least four full steps.  512 threads x 2 vectors was
-// the fastest shape measured on MI355X for 152064-wide bf16 rows (6.7 TB/s of
-// the ~7.0 TB/s streaming-read ceiling), 256 x 4 next.
-struct Shape {
-    int block, U;
-};
-
-Shape pick_shape(int64_t nvec)
-{
-    if (nvec >= 4 * 512 * 2)
-        return {512, 2};
-    if (nvec >= 4 * 256 * 4)
-        return {256, 4};
-    if (nvec >= 4 * 128 * 4)
-        return {128, 4};
-    return {64, 4};
-}
-
 } // namespace
 
 // Launch configuration, exposed for tuning harnesses.

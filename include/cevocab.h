@@ -82,6 +82,8 @@ enum cev_error {
 /* Bits ORed into the optional device status word. */
 #define CEV_STATUS_BAD_LABEL 1u /* a label outside [0, vocab) and != ignore_index */
 #define CEV_STATUS_BAD_INDEX 2u /* a gathered index outside [0, vocab) and != ignore_index */
+#define CEV_STATUS_BAD_PARTS 4u /* ce_vocab_merge: the partial records of a valid row do not
+                                   all mark it valid, or not exactly one holds its label */
 
 /* Per-row record written by ce_forward and read by ce_backward: 16 bytes,
  * 16-byte aligned.  m_z is the exact largest stored logit of the row,
@@ -252,6 +254,97 @@ int ce_fused(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride
              float *entropy, int64_t *argmax, void *dlogits, int64_t dlogits_row_stride,
              int64_t *valid_rows, int64_t *n_valid, void *workspace, size_t workspace_bytes,
              int32_t *status, cev_stream_t stream);
+
+/*
+ * Vocab-parallel (tensor-parallel) logits: the columns of each row are split
+ * over P shards, each held by one rank.  The target-excluded sums of every
+ * shard are combined in one exchange step, as the Liger-Kernel PR #1555 page
+ * (Summary, CE bullet) does for vocab-parallel cross-entropy: both sums
+ * reduced together.  Per call on each rank:
+ *   1. ce_vocab_shard_forward on the rank's columns -> one partial record
+ *      per row;
+ *   2. an all-gather of the records (48 B per row per shard) by the caller
+ *      (RCCL), into [P][rows] order of ascending column ranges;
+ *   3. ce_vocab_merge on every rank -> the same loss, log p, entropy, argmax
+ *      and saved record that ce_forward gives for the whole row;
+ *   4. ce_vocab_shard_backward on the rank's columns.
+ * The merge is fixed-order and fp64, so every rank gets bit-identical outputs.
+ */
+
+/* One shard's statistics of one row (written by ce_vocab_shard_forward,
+ * merged by ce_vocab_merge); 48 bytes, 8-byte aligned. */
+typedef struct cev_vocab_partial {
+    float m;       /* largest non-target stored logit of the shard, -inf if none */
+    float zt;      /* the stored target logit if the shard holds the label, else 0 */
+    int64_t arg;   /* lowest global column holding m, INT64_MAX if none */
+    double s;      /* sum over the shard's non-target columns of e^{(z - B)/T},
+                      B = max(m, -FLT_MAX) */
+    double h;      /* sum of e^{(z - B)/T} (B - z)/T (0 unless CEV_PART_ENTROPY) */
+    double zs;     /* sum of the non-target stored values (0 unless CEV_PART_VALUE_SUM) */
+    int32_t flags; /* bit 0: row valid; bit 1: this shard holds the label */
+    int32_t pad;
+} cev_vocab_partial;
+
+#define CEV_PART_ENTROPY 1u   /* also sum the entropy term (needed for entropy) */
+#define CEV_PART_VALUE_SUM 2u /* also sum the values (needed for label smoothing) */
+
+/*
+ * ce_vocab_shard_forward -- the forward sweep of ce_forward over one shard:
+ * columns [col_offset, col_offset + shard_vocab) of a vocab-wide row.
+ *
+ *   logits        [rows, row_stride] the shard's columns only (element 0 of a
+ *                 row is global column col_offset); shard_vocab <= row_stride
+ *   col_offset, vocab   0 <= col_offset, col_offset + shard_vocab <= vocab;
+ *                 labels are global columns in [0, vocab)
+ *   what          CEV_PART_* bits
+ *   partials      [rows] cev_vocab_partial out, 8-byte aligned.  Invalid rows
+ *                 (same rule as ce_forward) get flags = 0.
+ *   Other arguments as sls_forward.
+ */
+int ce_vocab_shard_forward(const void *logits, int64_t rows, int64_t shard_vocab,
+                           int64_t row_stride, int dtype, int64_t col_offset, int64_t vocab,
+                           const int64_t *labels, int64_t ignore_index, double temperature,
+                           const uint8_t *row_mask, unsigned what, void *partials,
+                           int32_t *status, cev_stream_t stream);
+
+/*
+ * ce_vocab_merge -- merge P shards' partial records of every row in a fixed
+ * order (shard 0 first), in fp64: the common base is the largest m, each sum
+ * is rescaled by e^{(B_p - B)/T} (the partial/combine rule of the
+ * unsloth-zoo #2080 Summary quoted on the Liger-Kernel PR #1555 page), the
+ * argmax is the lowest column holding the largest value, and the target logit
+ * comes from the one shard holding the label.  Then the closing step of
+ * ce_forward.
+ *
+ *   partials      [parts][rows] cev_vocab_partial, shard p's records at
+ *                 partials + p * rows; 1 <= parts <= 4096
+ *   vocab         the full vocabulary width (for labels and smoothing)
+ *   loss, saved   required, as ce_forward; logp, entropy, argmax optional.
+ *                 entropy needs records made with CEV_PART_ENTROPY, and
+ *                 label_smoothing != 0 needs CEV_PART_VALUE_SUM.
+ *   A valid row whose records disagree (a shard marks it invalid, or not
+ *   exactly one shard holds its label) gets the ignored-row outputs and ORs
+ *   CEV_STATUS_BAD_PARTS into *status.
+ */
+int ce_vocab_merge(const void *partials, int64_t parts, int64_t rows, int64_t vocab,
+                   const int64_t *labels, int64_t ignore_index, double temperature,
+                   double label_smoothing, const uint8_t *row_mask, float *loss, void *saved,
+                   float *logp, float *entropy, int64_t *argmax, int32_t *status,
+                   cev_stream_t stream);
+
+/*
+ * ce_vocab_shard_backward -- ce_backward over one shard's columns, from the
+ * merged saved record: (g/T)(p_j - eps/V) at every column of the shard, and
+ * (g/T)(eps - eps/V - q) at the label if the shard holds it.  Arguments as
+ * ce_backward, plus col_offset and vocab as in ce_vocab_shard_forward
+ * (logits and dlogits hold the shard's columns only).
+ */
+int ce_vocab_shard_backward(const void *logits, int64_t rows, int64_t shard_vocab,
+                            int64_t row_stride, int dtype, int64_t col_offset, int64_t vocab,
+                            const int64_t *labels, int64_t ignore_index, double temperature,
+                            double label_smoothing, const uint8_t *row_mask, const float *g,
+                            const void *saved, void *dlogits, int64_t dlogits_row_stride,
+                            int32_t *status, cev_stream_t stream);
 
 /* Bytes of workspace that let ce_forward hold the compacted row list and
  * count and, for few rows, the split-row partial records (0 for invalid

@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = set(declared_functions())
     assert {"sls_forward", "sls_topk_forward", "sls_topk_backward", "ce_forward", "ce_backward",
-            "ce_fused", "cev_workspace_size", "cev_status_string", "cev_version"} <= names
+            "ce_fused", "ce_vocab_shard_forward", "ce_vocab_merge", "ce_vocab_shard_backward",
+            "cev_workspace_size", "cev_status_string", "cev_version"} <= names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -50,7 +51,11 @@ def test_codes_match_header():
         m = re.search(r"CEV_E%s\s*=\s*(-?\d+)" % key, text)
         assert m and int(m.group(1)) == val, key
     assert re.search(r"CEV_STATUS_BAD_LABEL\s+1u", text)
-    assert cev.STATUS_BAD_LABEL == 1 and cev.STATUS_BAD_INDEX == 2
+    assert re.search(r"CEV_STATUS_BAD_INDEX\s+2u", text)
+    assert re.search(r"CEV_STATUS_BAD_PARTS\s+4u", text)
+    assert re.search(r"CEV_PART_ENTROPY\s+1u", text) and re.search(r"CEV_PART_VALUE_SUM\s+2u", text)
+    assert cev.STATUS_BAD_LABEL == 1 and cev.STATUS_BAD_INDEX == 2 and cev.STATUS_BAD_PARTS == 4
+    assert cev.PART_ENTROPY == 1 and cev.PART_VALUE_SUM == 2 and cev.PARTIAL_BYTES == 48
 
 
 def test_version_and_strings(lib):
@@ -216,6 +221,70 @@ def test_ce_fused_validation(lib):
     assert call(T=0.0) == E["TEMP"]
     assert call(dtype=9) == E["DTYPE"]
     assert call(eps=1.0 + 1e-12) == E["SMOOTH"]
+    assert call(rows=0) == E["OK"]
+
+
+def test_vocab_shard_forward_validation(lib):
+    def call(**kw):
+        a = dict(logits=A, rows=4, sv=100, stride=100, dtype=1, off=200, V=1000, labels=A,
+                 ig=-100, T=1.0, mask=None, what=0, parts=A, status=None)
+        a.update(kw)
+        return lib.ce_vocab_shard_forward(a["logits"], a["rows"], a["sv"], a["stride"],
+                                          a["dtype"], a["off"], a["V"], a["labels"], a["ig"],
+                                          a["T"], a["mask"], a["what"], a["parts"], a["status"],
+                                          None)
+    assert call(off=-1) == E["SHAPE"]
+    assert call(off=901) == E["SHAPE"]            # shard past the vocabulary
+    assert call(V=99) == E["SHAPE"]
+    assert call(sv=0) == E["SHAPE"]
+    assert call(stride=99) == E["STRIDE"]
+    assert call(labels=None) == E["NULL"]
+    assert call(parts=None) == E["NULL"]
+    assert call(parts=A + 4) == E["ALIGN"]
+    assert call(T=0.0) == E["TEMP"]
+    assert call(dtype=5) == E["DTYPE"]
+    assert call(rows=0, off=-1) == E["SHAPE"]
+    assert call(rows=0) == E["OK"]
+
+
+def test_vocab_merge_validation(lib):
+    def call(**kw):
+        a = dict(parts=A, P=8, rows=4, V=1000, labels=A, ig=-100, T=1.0, eps=0.0, mask=None,
+                 loss=A, saved=A, logp=None, ent=None, arg=None, status=None)
+        a.update(kw)
+        return lib.ce_vocab_merge(a["parts"], a["P"], a["rows"], a["V"], a["labels"], a["ig"],
+                                  a["T"], a["eps"], a["mask"], a["loss"], a["saved"], a["logp"],
+                                  a["ent"], a["arg"], a["status"], None)
+    assert call(P=0) == E["SHAPE"]
+    assert call(P=4097) == E["SHAPE"]
+    assert call(V=0) == E["SHAPE"]
+    assert call(rows=-1) == E["SHAPE"]
+    assert call(parts=None) == E["NULL"]
+    assert call(loss=None) == E["NULL"]
+    assert call(saved=None) == E["NULL"]
+    assert call(parts=A + 4) == E["ALIGN"]
+    assert call(saved=A + 8) == E["ALIGN"]
+    assert call(T=-1.0) == E["TEMP"]
+    assert call(eps=2.0) == E["SMOOTH"]
+    assert call(rows=0, parts=None) == E["OK"]
+
+
+def test_vocab_shard_backward_validation(lib):
+    def call(**kw):
+        a = dict(logits=A, rows=4, sv=100, stride=100, dtype=1, off=0, V=400, labels=A,
+                 ig=-100, T=1.0, eps=0.0, mask=None, g=A, saved=A, dl=B, dstride=100,
+                 status=None)
+        a.update(kw)
+        return lib.ce_vocab_shard_backward(a["logits"], a["rows"], a["sv"], a["stride"],
+                                           a["dtype"], a["off"], a["V"], a["labels"], a["ig"],
+                                           a["T"], a["eps"], a["mask"], a["g"], a["saved"],
+                                           a["dl"], a["dstride"], a["status"], None)
+    assert call(off=301) == E["SHAPE"]
+    assert call(dstride=99) == E["STRIDE"]
+    assert call(g=None) == E["NULL"]
+    assert call(saved=A + 4) == E["ALIGN"]
+    assert call(dl=A + 2) == E["ALIAS"]
+    assert call(eps=-0.5) == E["SMOOTH"]
     assert call(rows=0) == E["OK"]
 
 

@@ -145,3 +145,74 @@ def test_compaction_many_rows():
     n = int(out["n_valid"].item())
     assert n == want.size
     assert np.array_equal(out["valid_rows"][:n].cpu().numpy(), want)
+
+
+def test_chunk_full_topk_backward():
+    """Top-8 backward over the full chunk workload: every row's gradient sums
+    to zero; sampled rows match the oracle (gathered columns with the
+    difference-of-terms bound)."""
+    from gpu_helpers import DEV, say, to_dev, to_host
+    from test_gpu_smoothing_topk import TERM_RTOL, _assert_within, _topk_bound
+    import cross_entropy_vocab_amd as cev
+    say("[full] chunk 4096x32768 bf16 T=0.7, top-8 forward + backward")
+    w = workloads.chunk()
+    g = np.random.default_rng([6, 4096]).standard_normal((4096, 8)).astype(np.float32)
+    logits = to_dev(w["logits"])
+    idx = to_dev(w["indices"])
+    lp, q, sv = cev.sls_topk_forward(logits, idx, 0.7, saved=True)
+    dl = cev.sls_topk_backward(logits, idx, to_dev(g), sv, q, 0.7)
+    torch.cuda.synchronize()
+    _row_sums_ok(dl, RTOL["bf16"]["dlogits"])
+    rows = _sample_rows(np.random.default_rng(5), np.ones(4096, bool), 24, 0)
+    dsel = to_host(dl[torch.from_numpy(rows).to(DEV)])
+    sub = dict(w, logits=w["logits"][rows], indices=w["indices"][rows])
+    dref = oracle.topk_grad_rows(sub["logits"], sub["indices"], g[rows].astype(np.float64), 0.7)
+    extra = _topk_bound(sub, sub["indices"], g[rows])
+    tol = RTOL["bf16"]["dlogits"]
+    _assert_within("topk dlogits", dsel, dref, tol * np.abs(dref) + TERM_RTOL * extra + FLOOR)
+    qref = oracle.topk_rows(sub["logits"], sub["indices"], 0.7, want_q=True)[1]
+    assert_close("topk q", to_host(q)[rows], qref, RTOL["bf16"]["topk"])
+
+
+def test_grpo_full_vocab_parallel_p8():
+    """The grpo workload as 8 vocab shards of 19008 columns (one rank's shard
+    shape): the merged outputs agree with the unsharded call on every row and
+    with the oracle on sampled rows; every gradient row sums to zero."""
+    from gpu_helpers import DEV, say, to_dev, to_host
+    import cross_entropy_vocab_amd as cev
+    say("[full] grpo 8192x152064 bf16 as 8 vocab shards")
+    w = workloads.grpo()
+    R, V = w["logits"].shape
+    P, Vs = 8, V // 8
+    logits = to_dev(w["logits"])
+    labels = to_dev(w["labels"])
+    mask = to_dev(w["row_mask"])
+    g = to_dev(w["g"])
+    parts = torch.empty((P, R, cev.PARTIAL_BYTES), dtype=torch.uint8, device=DEV)
+    for p in range(P):
+        cev.ce_vocab_shard_forward(logits[:, p * Vs:(p + 1) * Vs], labels, p * Vs, V, 1.0,
+                                   row_mask=mask, partials=parts[p])
+    out = cev.ce_vocab_merge(parts, labels, V, 1.0, row_mask=mask, argmax=True)
+    dl = torch.empty_like(logits)
+    for p in range(P):
+        cev.ce_vocab_shard_backward(logits[:, p * Vs:(p + 1) * Vs], labels, g, out["saved"],
+                                    p * Vs, V, 1.0, row_mask=mask, dlogits=dl[:, p * Vs:(p + 1) * Vs])
+    ce = cev.ce_forward(logits, labels, 1.0, row_mask=mask, argmax=True)
+    torch.cuda.synchronize()
+    logp, cel = to_host(out["logp"]), to_host(ce["logp"])
+    assert_close("sharded vs whole logp", logp, cel.astype(np.float64), 1e-6)
+    assert np.array_equal(to_host(out["argmax"]), to_host(ce["argmax"]))
+    _row_sums_ok(dl, RTOL["bf16"]["dlogits"])
+    vr, _ = oracle.valid_rows(w["labels"], w["row_mask"], V)
+    valid = np.zeros(R, bool)
+    valid[vr] = True
+    rows = _sample_rows(np.random.default_rng(8), valid, 16, 4)
+    ref = oracle.ce_rows(w["logits"], w["labels"], 1.0, row_mask=w["row_mask"], rows_list=rows,
+                         want_entropy=False)
+    assert_close("sharded logp", logp[rows], ref["logp"][rows], RTOL["bf16"]["logp"])
+    dsel = to_host(dl[torch.from_numpy(rows).to(DEV)])
+    g64 = np.asarray(w["g"], np.float64)
+    for i, r in enumerate(rows):
+        dref = oracle.ce_grad_rows(w["logits"], w["labels"], g64, 1.0, row_mask=w["row_mask"],
+                                   r0=int(r), r1=int(r) + 1)[0]
+        assert_close(f"sharded dlogits row {r}", dsel[i], dref, RTOL["bf16"]["dlogits"], FLOOR)
