@@ -78,7 +78,9 @@ __device__ __forceinline__ float grad_scalar(float z, const RowConst &rc, float 
 // the tail columns).  With per = BLOCK * U every thread moves exactly U
 // vectors: short-lived workgroups spread over all channels, which measured
 // faster on MI355X than long per-row loops for this read-plus-write stream.
-template <int DT, int BLOCK, int U>
+// SHARD: the row holds global columns [col_offset, col_offset + vocab) of a
+// vocab_total-wide row (vocab-parallel form); otherwise the whole row.
+template <int DT, int BLOCK, int U, bool SHARD>
 __global__ __launch_bounds__(BLOCK) void k_backward(BackwardArgs a, int slices, int64_t per,
                                                     int reverse)
 {
@@ -91,9 +93,10 @@ __global__ __launch_bounds__(BLOCK) void k_backward(BackwardArgs a, int slices, 
     const int64_t tg = a.labels[r];
     const bool masked = a.row_mask && a.row_mask[r] == 0;
     const bool ignored = masked || tg == a.ignore_index;
-    const bool bad = !ignored && (tg < 0 || tg >= a.vocab_total);
+    const int64_t VT = SHARD ? a.vocab_total : V;
+    const bool bad = !ignored && (tg < 0 || tg >= VT);
     // The target's column here; outside [0, V) when another shard holds it.
-    const int64_t t = tg - a.col_offset;
+    const int64_t t = SHARD ? tg - a.col_offset : tg;
     const cev_saved sv = a.saved[r];
     if (bad && sl == 0 && tid == 0 && a.status)
         atomicOr(a.status, (int32_t)CEV_STATUS_BAD_LABEL);
@@ -111,7 +114,7 @@ __global__ __launch_bounds__(BLOCK) void k_backward(BackwardArgs a, int slices, 
         const float gp = a.g[r] * a.inv_t;
         const float ag = fabsf(gp);
         const float eps = (float)a.label_smoothing;
-        const float epv = (float)(a.label_smoothing / (double)a.vocab_total);
+        const float epv = (float)(a.label_smoothing / (double)VT);
         rc.sgn = __float_as_uint(gp) & 0x80000000u;
         rc.kexp = sv.log2_d - __log2f(ag);
         rc.ev = ag * epv;
@@ -358,7 +361,7 @@ __global__ __launch_bounds__(BLOCK) void k_topk_backward(TopkBackwardArgs a, int
     }
 }
 
-template <int DT, int BLOCK, int U>
+template <int DT, int BLOCK, int U, bool SHARD>
 hipError_t launch_bwd_t(const BackwardArgs &a, int iters, int reverse, hipStream_t s)
 {
     // iters wave-steps of BLOCK * U vectors per workgroup; 0 = a whole row.
@@ -374,7 +377,7 @@ hipError_t launch_bwd_t(const BackwardArgs &a, int iters, int reverse, hipStream
         slices = (nvec + per - 1) / per;
     }
     dim3 grid((unsigned)(a.rows * slices)), block(BLOCK);
-    hipLaunchKernelGGL((k_backward<DT, BLOCK, U>), grid, block, 0, s, a, (int)slices, per,
+    hipLaunchKernelGGL((k_backward<DT, BLOCK, U, SHARD>), grid, block, 0, s, a, (int)slices, per,
                        reverse);
     return hipGetLastError();
 }
@@ -385,10 +388,12 @@ hipError_t launch_bwd_t(const BackwardArgs &a, int iters, int reverse, hipStream
 hipError_t launch_backward_cfg(int dtype, const BackwardArgs &a, int block, int U, int iters,
                                int reverse, hipStream_t s)
 {
+    if (a.col_offset != 0 || a.vocab_total != a.vocab)
+        return hipErrorInvalidValue; // whole rows only
 #define CEV_BWD_CASE(B, UU)                                                                     \
     if (block == B && U == UU)                                                                  \
-        return dtype == CEV_BF16 ? launch_bwd_t<CEV_BF16, B, UU>(a, iters, reverse, s)          \
-                                 : launch_bwd_t<CEV_F32, B, UU>(a, iters, reverse, s);
+        return dtype == CEV_BF16 ? launch_bwd_t<CEV_BF16, B, UU, false>(a, iters, reverse, s)   \
+                                 : launch_bwd_t<CEV_F32, B, UU, false>(a, iters, reverse, s);
     CEV_BWD_CASE(256, 2)
     CEV_BWD_CASE(256, 4)
     CEV_BWD_CASE(256, 8)
@@ -400,6 +405,10 @@ hipError_t launch_backward_cfg(int dtype, const BackwardArgs &a, int block, int 
 
 hipError_t launch_backward(int dtype, const BackwardArgs &a, hipStream_t s)
 {
+    // A vocab shard gets its own instantiation (and kernel name in traces).
+    if (a.col_offset != 0 || a.vocab_total != a.vocab)
+        return dtype == CEV_BF16 ? launch_bwd_t<CEV_BF16, 256, 4, true>(a, 1, 0, s)
+                                 : launch_bwd_t<CEV_F32, 256, 4, true>(a, 1, 0, s);
     return launch_backward_cfg(dtype, a, 256, 4, 1, 0, s);
 }
 
