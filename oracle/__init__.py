@@ -18,6 +18,10 @@ Parity status of each function (what pins it is listed in the tests):
   valid_rows, ce_rows (with label smoothing), ce_grad_rows (with label
   smoothing), topk_rows (with q), topk_grad_rows -- pinned by closed forms,
   invariants, 120-digit brute force and library routines (tests/test_oracle_pins.py).
+  linear_logits, linear_ce_rows, linear_ce_grads (the linear head in front
+  of the cross-entropy) -- pinned by the identity head, exact rescaling, a
+  50-digit brute force and central differences of the loss in both the
+  hidden state and the head.
 """
 from __future__ import annotations
 
@@ -37,6 +41,7 @@ BAD_INDEX = 2
 
 F32 = 0
 BF16 = 1
+F64 = 2
 
 _default = None
 
@@ -96,7 +101,9 @@ def _dtype_code(logits: np.ndarray) -> int:
         return F32
     if logits.dtype == np.uint16:
         return BF16
-    raise TypeError("oracle logits must be float32 or uint16 (bf16 bit patterns)")
+    if logits.dtype == np.float64:
+        return F64
+    raise TypeError("oracle logits must be float32, float64 or uint16 (bf16 bit patterns)")
 
 
 def _check_2d(logits):
@@ -281,4 +288,79 @@ def topk_grad_rows(logits, indices, g, temperature=1.0, row_mask=None, ignore_in
     with ThreadPoolExecutor(threads) as ex:
         for s in ex.map(work, parts):
             st |= s
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Linear head in front of the cross-entropy (the fused linear CE / log-prob
+# setting of the unsloth-zoo #2080 Summary quoted on the Liger-Kernel PR #1555
+# page: logits = hidden x head^T, never stored in full by the fused kernels).
+
+def _widen(a: np.ndarray) -> np.ndarray:
+    """Stored values as float64: bf16 bit patterns (uint16), fp32 or fp64."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if a.dtype in (np.float32, np.float64):
+        return a.astype(np.float64)
+    raise TypeError("hidden / head must be uint16 (bf16 bits), float32 or float64")
+
+
+def linear_logits(hidden, weight, rows=None, vchunk=16384):
+    """logits[r, j] = sum_k hidden[r, k] * weight[j, k] in float64 (a library
+    matmul of the widened stored values; every product of two bf16 values is
+    exact in float64).  hidden [R, H], weight [V, H]; rows selects rows."""
+    h = _widen(hidden if rows is None else hidden[np.asarray(rows, dtype=np.int64)])
+    V = weight.shape[0]
+    out = np.empty((h.shape[0], V), dtype=np.float64)
+    for j0 in range(0, V, vchunk):
+        j1 = min(V, j0 + vchunk)
+        out[:, j0:j1] = h @ _widen(weight[j0:j1]).T
+    return out
+
+
+def linear_ce_rows(hidden, weight, labels, temperature=1.0, row_mask=None, ignore_index=-100,
+                   rows_list=None, label_smoothing=0.0, want_entropy=True, lib=None):
+    """ce_rows on the float64 logits hidden x weight^T.  Rows outside
+    rows_list (if given) are NaN / -2, as in ce_rows."""
+    R = hidden.shape[0]
+    rl = np.arange(R, dtype=np.int64) if rows_list is None else np.asarray(rows_list, np.int64)
+    lab = np.asarray(labels, dtype=np.int64)
+    z = linear_logits(hidden, weight, rl)
+    sub_mask = None if row_mask is None else np.ascontiguousarray(np.asarray(row_mask)[rl])
+    sub = ce_rows(z, np.ascontiguousarray(lab[rl]), temperature, row_mask=sub_mask,
+                  ignore_index=ignore_index, label_smoothing=label_smoothing,
+                  want_entropy=want_entropy, lib=lib)
+    out = {}
+    for k, v in sub.items():
+        if k == "status":
+            out[k] = v
+        elif v is None:
+            out[k] = None
+        else:
+            full = np.full(R, -2 if v.dtype == np.int64 else np.nan, dtype=v.dtype)
+            full[rl] = v
+            out[k] = full
+    return out
+
+
+def linear_ce_grads(hidden, weight, labels, g, temperature=1.0, row_mask=None, ignore_index=-100,
+                    rows_list=None, label_smoothing=0.0, want_weight=True, lib=None):
+    """Gradients of sum_r g[r] loss[r] through logits = hidden x weight^T:
+    dlogits = ce_grad_rows(logits), dhidden = dlogits x weight,
+    dweight = dlogits^T x hidden (the chain rule through the product).
+    With rows_list, dhidden holds those rows only and dweight is None (it sums
+    over every row)."""
+    R = hidden.shape[0]
+    rl = np.arange(R, dtype=np.int64) if rows_list is None else np.asarray(rows_list, np.int64)
+    lab = np.asarray(labels, dtype=np.int64)
+    gg = np.asarray(g, dtype=np.float64)
+    z = linear_logits(hidden, weight, rl)
+    sub_mask = None if row_mask is None else np.ascontiguousarray(np.asarray(row_mask)[rl])
+    dl = ce_grad_rows(z, np.ascontiguousarray(lab[rl]), np.ascontiguousarray(gg[rl]),
+                      temperature, row_mask=sub_mask, ignore_index=ignore_index,
+                      label_smoothing=label_smoothing, lib=lib)
+    w64 = _widen(weight)
+    out = {"dhidden": dl @ w64, "dweight": None}
+    if want_weight and rows_list is None:
+        out["dweight"] = dl.T @ _widen(hidden)
     return out

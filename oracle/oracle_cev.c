@@ -33,9 +33,13 @@
 #define ORACLE_BAD_INDEX 2
 
 /* Widen one stored element to double.  dtype 0 = fp32, 1 = bf16 (the upper
- * 16 bits of an IEEE binary32), so the widening is exact in both cases. */
+ * 16 bits of an IEEE binary32), 2 = fp64 (logits formed in double, as the
+ * product of a hidden state and a head), so the widening is exact in all
+ * cases. */
 static double load_z(const void *row, int dtype, int64_t j)
 {
+    if (dtype == 2)
+        return ((const double *)row)[j];
     if (dtype == 0)
         return (double)((const float *)row)[j];
     uint32_t w = (uint32_t)((const uint16_t *)row)[j] << 16;
@@ -46,7 +50,7 @@ static double load_z(const void *row, int dtype, int64_t j)
 
 static const void *row_ptr(const void *logits, int dtype, int64_t row_stride, int64_t r)
 {
-    size_t esz = dtype == 0 ? 4 : 2;
+    size_t esz = dtype == 2 ? 8 : (dtype == 0 ? 4 : 2);
     return (const char *)logits + (size_t)r * (size_t)row_stride * esz;
 }
 

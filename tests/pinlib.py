@@ -390,3 +390,153 @@ def check_topk_grad(lib=None):
 ALL_CHECKS = [check_label_smoothing, check_topk_grad, check_strided, check_uniform, check_peaked_closed_form, check_two_class, check_single_class,
               check_bruteforce, check_central_difference, check_invariants,
               check_library_routines]
+
+
+# ------------------------------------------------ linear head (hidden x head^T)
+def _bf16_identity(n, perm=None):
+    """bf16 bit patterns of a permutation matrix: row j has 1.0 at column perm[j]."""
+    w = np.zeros((n, n), dtype=np.uint16)
+    cols = np.arange(n) if perm is None else perm
+    w[np.arange(n), cols] = 0x3F80
+    return w
+
+
+def check_linear_identity(lib=None, orc=None):
+    """A permutation head: logits_j = h_{perm[j]}, so the linear CE equals the
+    (separately pinned) CE on the permuted hidden state, and the hidden
+    gradient is that CE's gradient moved back: dh[:, perm] = dlogits."""
+    orc = orc or oracle
+    rng = np.random.default_rng(31)
+    n = 37
+    h = bf16_bits((rng.standard_normal((5, n)) * 3).astype(np.float32))
+    labels = np.array([3, 36, -100, 0, 17], dtype=np.int64)
+    g = np.array([1.0, -0.5, 2.0, 0.25, 1.5])
+    for perm in (None, rng.permutation(n)):
+        w = _bf16_identity(n, perm)
+        z = h if perm is None else np.ascontiguousarray(h[:, perm])
+        for T, eps in ((1.0, 0.0), (0.8, 0.1)):
+            got = orc.linear_ce_rows(h, w, labels, T, label_smoothing=eps, lib=lib)
+            ref = orc.ce_rows(z, labels, T, label_smoothing=eps, lib=lib)
+            for k in ("logp", "loss", "entropy", "argmax"):
+                assert np.array_equal(got[k], ref[k]), (k, T, eps)
+            d = orc.linear_ce_grads(h, w, labels, g, T, label_smoothing=eps, lib=lib)
+            dl = orc.ce_grad_rows(z, labels, g, T, label_smoothing=eps, lib=lib)
+            p = np.arange(n) if perm is None else perm
+            assert np.array_equal(d["dhidden"][:, p], dl), (T, eps)
+
+
+def check_linear_scale(lib=None, orc=None):
+    """(2^3 h, 2^-3 head) gives bit-identical logits and losses; the hidden
+    gradient scales by 2^-3 and the head gradient by 2^3, exactly."""
+    orc = orc or oracle
+    rng = np.random.default_rng(32)
+    h = (rng.standard_normal((4, 6)) * 2).astype(np.float32)
+    w = (rng.standard_normal((11, 6)) * 0.5).astype(np.float32)
+    labels = np.array([0, 10, 5, -100], dtype=np.int64)
+    g = np.array([1.0, 2.0, -1.0, 1.0])
+    a = orc.linear_ce_rows(h, w, labels, 0.9, lib=lib)
+    b = orc.linear_ce_rows(h * np.float32(8), w / np.float32(8), labels, 0.9, lib=lib)
+    for k in ("logp", "loss", "entropy", "argmax"):
+        assert np.array_equal(a[k], b[k]), k
+    da = orc.linear_ce_grads(h, w, labels, g, 0.9, lib=lib)
+    db = orc.linear_ce_grads(h * np.float32(8), w / np.float32(8), labels, g, 0.9, lib=lib)
+    assert np.array_equal(da["dhidden"] / 8, db["dhidden"])
+    assert np.array_equal(da["dweight"] * 8, db["dweight"])
+
+
+def check_linear_rows_list(lib=None, orc=None):
+    """A row subset gives the same per-row results as the full call."""
+    orc = orc or oracle
+    rng = np.random.default_rng(33)
+    h = bf16_bits((rng.standard_normal((6, 8)) * 2).astype(np.float32))
+    w = bf16_bits((rng.standard_normal((13, 8)) * 0.7).astype(np.float32))
+    labels = np.array([1, 12, -100, 4, 0, 7], dtype=np.int64)
+    mask = np.array([1, 1, 1, 0, 1, 1], dtype=np.uint8)
+    g = rng.standard_normal(6)
+    full = orc.linear_ce_rows(h, w, labels, 1.1, row_mask=mask, lib=lib)
+    rows = np.array([5, 0, 3], dtype=np.int64)
+    sub = orc.linear_ce_rows(h, w, labels, 1.1, row_mask=mask, rows_list=rows, lib=lib)
+    for k in ("logp", "loss", "argmax"):
+        assert np.array_equal(sub[k][rows], full[k][rows]), k
+    dfull = orc.linear_ce_grads(h, w, labels, g, 1.1, row_mask=mask, lib=lib)
+    dsub = orc.linear_ce_grads(h, w, labels, g, 1.1, row_mask=mask, rows_list=rows, lib=lib)
+    assert np.array_equal(dsub["dhidden"], dfull["dhidden"][rows])
+
+
+def _mp_linear(h, w, labels, g, T, eps=0.0):
+    """Brute force at the working precision of mpmath, straight from the
+    definitions: z = h w^T, per-row CE with smoothing, dz, dh = dz w, dW = dz^T h."""
+    R, H = h.shape
+    V = w.shape[0]
+    hm = [[mp.mpf(float(h[r, k])) for k in range(H)] for r in range(R)]
+    wm = [[mp.mpf(float(w[j, k])) for k in range(H)] for j in range(V)]
+    loss, dz = [], []
+    for r in range(R):
+        z = [mp.fsum(hm[r][k] * wm[j][k] for k in range(H)) for j in range(V)]
+        x = [zj / mp.mpf(T) for zj in z]
+        lse = mp.log(mp.fsum(mp.e ** xi for xi in x))
+        t = int(labels[r])
+        nll = lse - x[t]
+        smooth = mp.fsum(lse - xi for xi in x) / V
+        loss.append((1 - mp.mpf(eps)) * nll + mp.mpf(eps) * smooth)
+        c = mp.mpf(float(g[r])) / mp.mpf(T)
+        dz.append([c * (mp.e ** (xi - lse) - (1 - mp.mpf(eps)) * (1 if j == t else 0)
+                        - mp.mpf(eps) / V) for j, xi in enumerate(x)])
+    dh = [[mp.fsum(dz[r][j] * wm[j][k] for j in range(V)) for k in range(H)] for r in range(R)]
+    dw = [[mp.fsum(dz[r][j] * hm[r][k] for r in range(R)) for k in range(H)] for j in range(V)]
+    return loss, dh, dw
+
+
+def check_linear_bruteforce(lib=None, orc=None):
+    """Loss, hidden and head gradients of a tiny linear CE against mpmath."""
+    orc = orc or oracle
+    rng = np.random.default_rng(34)
+    for T, eps in ((1.0, 0.0), (0.7, 0.3)):
+        h = bf16_bits((rng.standard_normal((2, 3)) * 2).astype(np.float32))
+        w = bf16_bits((rng.standard_normal((5, 3)) * 2).astype(np.float32))
+        labels = np.array([4, 1], dtype=np.int64)
+        g = np.array([1.0, -0.75])
+        loss, dh, dw = _mp_linear(bf16_to_f32(h), bf16_to_f32(w), labels, g, T, eps)
+        got = orc.linear_ce_rows(h, w, labels, T, label_smoothing=eps, lib=lib)
+        d = orc.linear_ce_grads(h, w, labels, g, T, label_smoothing=eps, lib=lib)
+        for r in range(2):
+            assert rel(got["loss"][r], loss[r]) < 1e-12, (T, eps, r)
+            for k in range(3):
+                assert rel(d["dhidden"][r, k], dh[r][k]) < 1e-11, (T, eps, r, k)
+        for j in range(5):
+            for k in range(3):
+                assert rel(d["dweight"][j, k], dw[j][k]) < 1e-11, (T, eps, j, k)
+
+
+def check_linear_central_difference(lib=None, orc=None):
+    """dh and dW against central differences of sum_r g_r loss_r (fp64 inputs,
+    a non-square head, smoothing on, one ignored and one masked row)."""
+    orc = orc or oracle
+    rng = np.random.default_rng(35)
+    R, H, V = 4, 5, 7
+    h = rng.standard_normal((R, H))
+    w = rng.standard_normal((V, H)) * 0.8
+    labels = np.array([2, -100, 6, 0], dtype=np.int64)
+    mask = np.array([1, 1, 1, 0], dtype=np.uint8)
+    g = np.array([1.0, 3.0, -0.5, 2.0])
+    T, eps, step = 0.7, 0.2, 1e-5
+
+    def objective(hh, ww):
+        o = orc.linear_ce_rows(hh, ww, labels, T, row_mask=mask, label_smoothing=eps, lib=lib)
+        return float(np.sum(g * o["loss"]))
+
+    d = orc.linear_ce_grads(h, w, labels, g, T, row_mask=mask, label_smoothing=eps, lib=lib)
+    for arr, grad in ((h, d["dhidden"]), (w, d["dweight"])):
+        for idx in np.ndindex(arr.shape):
+            up = arr.copy()
+            dn = arr.copy()
+            up[idx] += step
+            dn[idx] -= step
+            num = (objective(up, w) - objective(dn, w)) if arr is h else \
+                (objective(h, up) - objective(h, dn))
+            num /= 2 * step
+            assert abs(grad[idx] - num) <= 1e-7 * max(1.0, abs(num)), (idx, grad[idx], num)
+
+
+LINEAR_CHECKS = [check_linear_identity, check_linear_scale, check_linear_rows_list,
+                 check_linear_bruteforce, check_linear_central_difference]

@@ -77,3 +77,55 @@ def test_unmutated_source_passes_all_pins(tmp_path):
     lib = oracle.load_library(lib_path)
     for check in pinlib.ALL_CHECKS:
         check(lib=lib)
+
+
+# Mistakes planted in the Python half of the oracle (the linear head in front
+# of the cross-entropy): a missing transpose, a gradient through the wrong
+# operand layout, rows out of step, labels not following a row subset.
+PKG = os.path.dirname(oracle.__file__)
+PY_MUTANTS = [
+    ("logits_untransposed_head", "out[:, j0:j1] = h @ _widen(weight[j0:j1]).T",
+     "out[:, j0:j1] = h @ _widen(weight[j0:j1])"),
+    ("dhidden_transposed_head", '"dhidden": dl @ w64', '"dhidden": dl @ w64.T'),
+    ("dweight_rows_shifted", 'out["dweight"] = dl.T @ _widen(hidden)',
+     'out["dweight"] = dl.T @ np.roll(_widen(hidden), 1, axis=0)'),
+    ("subset_labels_not_followed", "sub = ce_rows(z, np.ascontiguousarray(lab[rl]), temperature",
+     "sub = ce_rows(z, np.ascontiguousarray(lab[:rl.size]), temperature"),
+]
+
+
+def _load_mutant_package(tmp_path, old, new):
+    import importlib.util
+    import sys
+    d = tmp_path / "oracle_mut"
+    d.mkdir()
+    text = open(os.path.join(PKG, "__init__.py")).read()
+    assert text.count(old) == 1, "mutation site not unique or missing"
+    (d / "__init__.py").write_text(text.replace(old, new))
+    shutil.copy(SRC, d / "oracle_cev.c")
+    name = f"oracle_mut_{abs(hash((old, new)))}"
+    spec = importlib.util.spec_from_file_location(name, d / "__init__.py",
+                                                  submodule_search_locations=[str(d)])
+    mod = importlib.util.module_from_spec(spec)
+    sys.modules[name] = mod
+    spec.loader.exec_module(mod)
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_linear_pins_catch_python_mutant(tmp_path, name, old, new):
+    mod = _load_mutant_package(tmp_path, old, new)
+    caught = []
+    for check in pinlib.LINEAR_CHECKS:
+        try:
+            check(orc=mod)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(check.__name__)
+            break
+    assert caught, f"no pin caught mutant {name}"
+
+
+def test_unmutated_python_oracle_passes_linear_pins(tmp_path):
+    mod = _load_mutant_package(tmp_path, "F64 = 2\n", "F64 = 2\n\n")
+    for check in pinlib.LINEAR_CHECKS:
+        check(orc=mod)

@@ -14,7 +14,8 @@ import workloads
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
-@pytest.mark.parametrize("check", pinlib.ALL_CHECKS, ids=lambda c: c.__name__)
+@pytest.mark.parametrize("check", pinlib.ALL_CHECKS + pinlib.LINEAR_CHECKS,
+                         ids=lambda c: c.__name__)
 def test_pin(check):
     check()
 

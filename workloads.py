@@ -180,3 +180,47 @@ def peaked(dtype="f32", temperature=1.0, rows=2048, vocab=151936, seed=4):
 
 
 BUILDERS = dict(tiny=tiny, chunk=chunk, grpo=grpo, sparse=sparse, peaked=peaked)
+
+
+LINEAR_MARGINS = (17.0, 20.0, 30.0, 50.0)
+
+
+def linear(rows=8192, hidden=2560, vocab=151936, seed=5, peaked_frac=0.0, temperature=1.0):
+    """Hidden states and a frozen head for the fused linear CE (unsloth-zoo
+    #2080 Speed: 2560 x 151936 frozen head, 8192 and 2048 rows; Accuracy:
+    margins 17 / 20 / 30 / 50).  bf16 bits.
+
+    head W [vocab, hidden] ~ N(0, 1/hidden) so each row of W has norm ~1;
+    hidden h [rows, hidden] ~ 3 N(0, 1), so a logit h . w_j is ~ N(0, 9);
+    labels uniform; exactly rows // 10 rows masked; g ~ N(0, 1).  A fraction
+    peaked_frac of the rows (chosen by permutation) is replaced by
+    h = beta w_t + 0.05 N(0, 1) with beta = margin / |w_t|^2, so the target
+    logit leads the others by about the margin (the oracle reads the exact
+    logits of the stored values)."""
+    rng = np.random.default_rng(seed)
+    labels = rng.integers(0, vocab, rows).astype(np.int64)
+    row_mask = np.ones(rows, dtype=np.uint8)
+    row_mask[rng.permutation(rows)[:rows // 10]] = 0
+    g = rng.standard_normal(rows, dtype=np.float32)
+    n_peak = int(round(peaked_frac * rows))
+    peak_rows = np.sort(rng.permutation(rows)[:n_peak])
+    margins = np.asarray(LINEAR_MARGINS, np.float32)[rng.integers(0, len(LINEAR_MARGINS), n_peak)]
+    scale = np.float32(1.0 / np.sqrt(hidden))
+    w = _assemble(_draw_matrix(seed, vocab, hidden,
+                               lambda b, gen, r0, r1: bf16_bits(
+                                   scale * gen.standard_normal((r1 - r0, hidden),
+                                                               dtype=np.float32))),
+                  vocab, hidden, np.uint16)
+    h = _assemble(_draw_matrix(seed + 1000, rows, hidden,
+                               lambda b, gen, r0, r1: bf16_bits(
+                                   3.0 * gen.standard_normal((r1 - r0, hidden),
+                                                             dtype=np.float32))),
+                  rows, hidden, np.uint16)
+    prng = np.random.default_rng([seed, 2])
+    for i, r in enumerate(peak_rows):
+        wt = bf16_to_f32(w[labels[r]])
+        beta = np.float32(margins[i] / float(np.dot(wt.astype(np.float64), wt)))
+        h[r] = bf16_bits(beta * wt + np.float32(0.05) * prng.standard_normal(hidden,
+                                                                              dtype=np.float32))
+    return dict(name="linear", hidden=h, weight=w, labels=labels, row_mask=row_mask,
+                temperature=temperature, g=g, peak_rows=peak_rows)
