@@ -18,7 +18,8 @@ from . import _lib
 
 __all__ = ["sls_forward", "sls_topk_forward", "sls_topk_backward", "ce_forward",
            "ce_backward", "ce_fused", "ce_vocab_shard_forward", "ce_vocab_merge",
-           "ce_vocab_shard_backward", "workspace_size",
+           "ce_vocab_shard_backward", "lce_forward", "lce_backward", "lce_workspace_size",
+           "workspace_size",
            "status_string", "version", "CEV_F32", "CEV_BF16", "STATUS_BAD_LABEL",
            "STATUS_BAD_INDEX", "STATUS_BAD_PARTS", "SAVED_BYTES", "PARTIAL_BYTES", "CevError"]
 
@@ -387,3 +388,98 @@ def ce_vocab_shard_backward(logits, labels, g, saved, col_offset, vocab, tempera
                                             _stream(dev))
     _check("ce_vocab_shard_backward", rc)
     return dlogits
+
+
+def lce_workspace_size(rows: int, hidden_dim: int, vocab: int) -> int:
+    return int(_lib.get().lce_workspace_size(int(rows), int(hidden_dim), int(vocab)))
+
+
+def _check_bf16_2d(t, name, dev=None):
+    if not t.is_cuda or (dev is not None and t.device != dev):
+        raise ValueError(f"{name} must be a GPU tensor on the same device")
+    if t.dtype != torch.bfloat16 or t.dim() != 2:
+        raise TypeError(f"{name} must be a 2-D bfloat16 tensor")
+    if t.shape[0] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return max(t.stride(0) if t.shape[0] > 1 else t.shape[1], t.shape[1])
+
+
+def _lce_workspace(o, rows, H, V, dev):
+    need = lce_workspace_size(rows, H, V)
+    ws = o.get("workspace")
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    return ws, need
+
+
+def lce_forward(hidden, weight, labels, temperature=1.0, row_mask=None, ignore_index=-100,
+                label_smoothing=0.0, logp=True, entropy=False, argmax=False, status=None,
+                out=None):
+    """Linear cross-entropy forward: logits = hidden x weight^T (bf16 in, fp32
+    accumulate, never stored), then the collapse-safe per-row CE.  Returns a
+    dict with loss, saved (for lce_backward) and optionally logp, entropy,
+    argmax, plus the workspace it used."""
+    rows, H = hidden.shape
+    dev = hidden.device
+    hs = _check_bf16_2d(hidden, "hidden")
+    ws_ = _check_bf16_2d(weight, "weight", dev)
+    V = weight.shape[0]
+    if weight.shape[1] != H:
+        raise ValueError("weight must be [vocab, hidden_dim]")
+    _dev(labels, "labels", torch.int64, (rows,), dev)
+    m = _mask(row_mask, rows, dev)
+    _dev(status, "status", torch.int32, (1,), dev)
+    o = dict(out) if out else {}
+
+    def want(key, flag, dtype, shape):
+        if not flag:
+            o[key] = None
+        elif o.get(key) is None:
+            o[key] = torch.empty(shape, dtype=dtype, device=dev)
+        else:
+            _dev(o[key], key, dtype, shape, dev)
+
+    want("loss", True, torch.float32, (rows,))
+    want("saved", True, torch.uint8, (rows, SAVED_BYTES))
+    want("logp", logp, torch.float32, (rows,))
+    want("entropy", entropy, torch.float32, (rows,))
+    want("argmax", argmax, torch.int64, (rows,))
+    ws, need = _lce_workspace(o, rows, H, V, dev)
+    o["workspace"] = ws
+    rc = _lib.get().lce_forward(_ptr(hidden), rows, H, hs, _ptr(weight), V, ws_, _ptr(labels),
+                                int(ignore_index), float(temperature), float(label_smoothing),
+                                _ptr(m), _ptr(o["loss"]), _ptr(o["saved"]), _ptr(o["logp"]),
+                                _ptr(o["entropy"]), _ptr(o["argmax"]), _ptr(ws), need,
+                                _ptr(status), _stream(dev))
+    _check("lce_forward", rc)
+    return o
+
+
+def lce_backward(hidden, weight, labels, g, saved, temperature=1.0, row_mask=None,
+                 ignore_index=-100, label_smoothing=0.0, dweight=False, status=None,
+                 workspace=None, dhidden=None):
+    """Gradients of sum_r g[r] loss[r] through logits = hidden x weight^T:
+    dhidden [rows, hidden_dim] fp32, and dweight [vocab, hidden_dim] fp32 when
+    dweight=True (else None, a frozen head)."""
+    rows, H = hidden.shape
+    dev = hidden.device
+    hs = _check_bf16_2d(hidden, "hidden")
+    ws_ = _check_bf16_2d(weight, "weight", dev)
+    V = weight.shape[0]
+    _dev(labels, "labels", torch.int64, (rows,), dev)
+    _dev(g, "g", torch.float32, (rows,), dev)
+    _dev(saved, "saved", torch.uint8, (rows, SAVED_BYTES), dev)
+    m = _mask(row_mask, rows, dev)
+    _dev(status, "status", torch.int32, (1,), dev)
+    ws, need = _lce_workspace({"workspace": workspace}, rows, H, V, dev)
+    if dhidden is None:
+        dhidden = torch.empty((rows, H), dtype=torch.float32, device=dev)
+    else:
+        _dev(dhidden, "dhidden", torch.float32, (rows, H), dev)
+    dw = torch.empty((V, H), dtype=torch.float32, device=dev) if dweight else None
+    rc = _lib.get().lce_backward(_ptr(hidden), rows, H, hs, _ptr(weight), V, ws_, _ptr(labels),
+                                 int(ignore_index), float(temperature), float(label_smoothing),
+                                 _ptr(m), _ptr(g), _ptr(saved), _ptr(dhidden), H, _ptr(dw), H,
+                                 _ptr(ws), need, _ptr(status), _stream(dev))
+    _check("lce_backward", rc)
+    return dhidden, dw

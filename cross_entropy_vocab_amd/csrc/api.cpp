@@ -586,6 +586,149 @@ int ce_vocab_shard_backward(const void *logits, int64_t rows, int64_t shard_voca
     return launch_status(cev::launch_backward(dtype, a, to_hip(stream)));
 }
 
+// Shapes of the linear cross-entropy: bf16 hidden [rows, hs] and head
+// [vocab, ws], hidden_dim a multiple of 64, strides multiples of 8.
+static int check_lce(const void *hidden, int64_t rows, int64_t hd, int64_t hs, const void *weight,
+                     int64_t vocab, int64_t ws, double temperature, double eps, bool *done)
+{
+    *done = false;
+    if (!(std::isfinite(temperature) && temperature > 0.0))
+        return CEV_ETEMP;
+    if (!smoothing_ok(eps))
+        return CEV_ESMOOTH;
+    if (rows < 0 || rows > kMaxRows || vocab < 1 || vocab > kMaxVocab || hd < 64 ||
+        hd > 65536 || hd % 64 != 0)
+        return CEV_ESHAPE;
+    if (hs < hd || ws < hd || hs % 8 != 0 || ws % 8 != 0)
+        return CEV_ESTRIDE;
+    if (rows == 0) {
+        *done = true;
+        return CEV_OK;
+    }
+    if (!hidden || !weight)
+        return CEV_ENULL;
+    if (!aligned(hidden, 16) || !aligned(weight, 16))
+        return CEV_EALIGN;
+    const double c = 1.4426950408889634074 / temperature;
+    if (!(c < 3.0e38 && c > 1.0e-37) || !(1.0 / temperature < 3.0e38))
+        return CEV_ETEMP;
+    return CEV_OK;
+}
+
+size_t lce_workspace_size(int64_t rows, int64_t hidden_dim, int64_t vocab)
+{
+    if (rows < 0 || rows > kMaxRows || vocab < 1 || vocab > kMaxVocab || hidden_dim < 64 ||
+        hidden_dim % 64 != 0)
+        return 0;
+    const size_t fwd = (size_t)cev::lce_splits(rows, vocab) * (size_t)rows * sizeof(cev_vocab_partial);
+    const size_t bwd = cev::lce_backward_workspace(rows, hidden_dim, vocab);
+    return fwd > bwd ? fwd : bwd;
+}
+
+static cev::LceArgs lce_args(const void *hidden, int64_t rows, int64_t hd, int64_t hs,
+                             const void *weight, int64_t vocab, int64_t ws, const int64_t *labels,
+                             int64_t ignore_index, double temperature, double eps,
+                             const uint8_t *row_mask, int32_t *status)
+{
+    cev::LceArgs a{};
+    a.hidden = static_cast<const unsigned short *>(hidden);
+    a.rows = rows;
+    a.hidden_dim = hd;
+    a.ldh = hs;
+    a.weight = static_cast<const unsigned short *>(weight);
+    a.vocab = vocab;
+    a.ldw = ws;
+    a.labels = labels;
+    a.ignore_index = ignore_index;
+    a.row_mask = row_mask;
+    a.temperature = temperature;
+    a.label_smoothing = eps;
+    a.c = (float)(1.4426950408889634074 / temperature);
+    a.inv_t = (float)(1.0 / temperature);
+    a.splits = cev::lce_splits(rows, vocab);
+    a.ldd = cev::lce_dl_stride(vocab);
+    a.status = status;
+    return a;
+}
+
+int lce_forward(const void *hidden, int64_t rows, int64_t hidden_dim, int64_t hidden_stride,
+                const void *weight, int64_t vocab, int64_t weight_stride, const int64_t *labels,
+                int64_t ignore_index, double temperature, double label_smoothing,
+                const uint8_t *row_mask, float *loss, void *saved, float *logp, float *entropy,
+                int64_t *argmax, void *workspace, size_t workspace_bytes, int32_t *status,
+                cev_stream_t stream)
+{
+    bool done;
+    int rc = check_lce(hidden, rows, hidden_dim, hidden_stride, weight, vocab, weight_stride,
+                       temperature, label_smoothing, &done);
+    if (rc != CEV_OK || done)
+        return rc;
+    if (!labels || !loss || !saved || !workspace)
+        return CEV_ENULL;
+    if (!aligned(labels, 8) || !aligned(loss, 4) || !aligned(saved, 16) || !aligned(logp, 4) ||
+        !aligned(entropy, 4) || !aligned(argmax, 8) || !aligned(workspace, 16) ||
+        !aligned(status, 4))
+        return CEV_EALIGN;
+    if (workspace_bytes < lce_workspace_size(rows, hidden_dim, vocab))
+        return CEV_EWORKSPACE;
+    cev::LceArgs a = lce_args(hidden, rows, hidden_dim, hidden_stride, weight, vocab,
+                              weight_stride, labels, ignore_index, temperature, label_smoothing,
+                              row_mask, status);
+    a.partials = static_cast<cev_vocab_partial *>(workspace);
+    hipError_t e = cev::launch_lce_forward(a, entropy != nullptr, label_smoothing != 0.0,
+                                           to_hip(stream));
+    if (e != hipSuccess)
+        return CEV_ELAUNCH;
+    cev::MergeArgs m{};
+    m.partials = a.partials;
+    m.parts = a.splits;
+    m.rows = rows;
+    m.vocab = vocab;
+    m.labels = labels;
+    m.ignore_index = ignore_index;
+    m.row_mask = row_mask;
+    m.temperature = temperature;
+    m.label_smoothing = label_smoothing;
+    m.loss = loss;
+    m.logp = logp;
+    m.entropy = entropy;
+    m.argmax = argmax;
+    m.saved = static_cast<cev_saved *>(saved);
+    m.status = status;
+    return launch_status(cev::launch_vocab_merge(m, to_hip(stream)));
+}
+
+int lce_backward(const void *hidden, int64_t rows, int64_t hidden_dim, int64_t hidden_stride,
+                 const void *weight, int64_t vocab, int64_t weight_stride,
+                 const int64_t *labels, int64_t ignore_index, double temperature,
+                 double label_smoothing, const uint8_t *row_mask, const float *g,
+                 const void *saved, float *dhidden, int64_t dhidden_stride, float *dweight,
+                 int64_t dweight_stride, void *workspace, size_t workspace_bytes,
+                 int32_t *status, cev_stream_t stream)
+{
+    bool done;
+    int rc = check_lce(hidden, rows, hidden_dim, hidden_stride, weight, vocab, weight_stride,
+                       temperature, label_smoothing, &done);
+    if (rc != CEV_OK || done)
+        return rc;
+    if (dhidden_stride < hidden_dim || (dweight && dweight_stride < hidden_dim))
+        return CEV_ESTRIDE;
+    if (!labels || !g || !saved || !dhidden || !workspace)
+        return CEV_ENULL;
+    if (!aligned(labels, 8) || !aligned(g, 4) || !aligned(saved, 16) || !aligned(dhidden, 4) ||
+        !aligned(dweight, 4) || !aligned(workspace, 16) || !aligned(status, 4))
+        return CEV_EALIGN;
+    if (workspace_bytes < lce_workspace_size(rows, hidden_dim, vocab))
+        return CEV_EWORKSPACE;
+    cev::LceArgs a = lce_args(hidden, rows, hidden_dim, hidden_stride, weight, vocab,
+                              weight_stride, labels, ignore_index, temperature, label_smoothing,
+                              row_mask, status);
+    a.g = g;
+    a.saved = static_cast<const cev_saved *>(saved);
+    return launch_status(cev::launch_lce_backward(a, workspace, dhidden, dhidden_stride,
+                                                  dweight, dweight_stride, to_hip(stream)));
+}
+
 const char *cev_status_string(int code)
 {
     switch (code) {

@@ -175,6 +175,40 @@ hipError_t launch_shard_sweep(int dtype, const ShardArgs &a, bool want_entropy, 
                               hipStream_t stream);
 hipError_t launch_vocab_merge(const MergeArgs &a, hipStream_t stream);
 
+// Linear cross-entropy: logits = hidden x head^T on the matrix cores.
+struct LceArgs {
+    const unsigned short *hidden;   // [rows, ldh] bf16
+    int64_t rows;
+    int64_t hidden_dim;             // multiple of 64
+    int64_t ldh;                    // multiple of 8
+    const unsigned short *weight;   // head [vocab, ldw] bf16
+    int64_t vocab;
+    int64_t ldw;                    // multiple of 8
+    const int64_t *labels;
+    int64_t ignore_index;
+    const uint8_t *row_mask;
+    double temperature;
+    double label_smoothing;
+    float c;                        // log2(e) / T
+    float inv_t;                    // 1 / T
+    int64_t splits;                 // vocab splits (workgroups per row block)
+    cev_vocab_partial *partials;    // forward: [splits][rows]
+    const float *g;                 // backward: [rows]
+    const cev_saved *saved;         // backward: [rows]
+    unsigned short *dlogits;        // backward: [rows, ldd] bf16 scratch
+    int64_t ldd;                    // multiple of 64, >= vocab
+    int32_t *status;
+};
+
+int64_t lce_splits(int64_t rows, int64_t vocab);
+int64_t lce_dl_stride(int64_t vocab);
+hipError_t launch_lce_forward(const LceArgs &a, bool want_entropy, bool want_zsum,
+                              hipStream_t stream);
+size_t lce_backward_workspace(int64_t rows, int64_t hidden_dim, int64_t vocab);
+hipError_t launch_lce_backward(const LceArgs &a, void *workspace, float *dhidden,
+                               int64_t dhidden_stride, float *dweight, int64_t dweight_stride,
+                               hipStream_t stream);
+
 // Forward + backward in one call, one workgroup per row (rows 16-byte aligned).
 struct FusedArgs {
     const void *logits;

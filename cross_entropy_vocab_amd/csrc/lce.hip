@@ -1,0 +1,590 @@
+// lce.hip -- linear cross-entropy: logits = hidden x head^T computed tile by
+// tile on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16) and consumed in
+// registers, so the [rows, vocab] logits never reach HBM (the fused linear CE
+// / log-prob setting of the unsloth-zoo #2080 Summary quoted on the
+// Liger-Kernel PR #1555 page).
+//
+//   forward   k_lce_fwd: each workgroup owns 256 rows and one vocab split; per
+//             256-column tile it runs the K loop over the hidden size, then
+//             folds the tile into target-excluded softmax statistics (the
+//             tile's maximum, first column of the maximum and sum at the
+//             maximum are reduced across the 32 lanes of each row, then merged
+//             into a running state that one lane per row keeps; entropy and
+//             value sums when asked).  At the end of its split each row gets
+//             one cev_vocab_partial record, and k_vocab_merge closes the rows
+//             exactly as for vocab-parallel logits.
+//   backward  k_lce_dl recomputes each logit tile and writes
+//             dlogits = (g/T)(softmax - onehot) in bf16 (the per-element
+//             formula of k_backward, from the saved record); k_lce_gemm then
+//             forms dhidden = dlogits x head (and, for a trainable head,
+//             dhead = dlogits^T x hidden) from transposed copies, so that every
+//             product runs with both operands contiguous along the contraction.
+//
+// Tiles: 8 waves in a 4 x 2 grid (two per SIMD), each wave 64 x 128 of C as
+// 2 x 4 blocks of 32 x 32; K steps of 64, staged through registers into a
+// double-buffered LDS tile of 2 x 64 KB.  A 256 x 256 workgroup tile needs
+// 64 KB of operands per 256 x 256 x 64 MACs, half the traffic per MAC of a
+// 128 x 256 tile, and the second wave on each SIMD covers the first's loads
+// and barriers; the LDS-fragment + MFMA loop alone runs at 88% of the bf16
+// peak on MI355X.  Fragment layout of the 32x32x16 bf16 MFMA on gfx950 (checked on the
+// device): lane l supplies A[l % 32][8 (l / 32) .. +8] and B[same k][l % 32];
+// accumulator element v of lane l is C[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
+#include "cev_device.h"
+#include "cev_launch.h"
+
+namespace cev {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kLT = 512;                         // threads per workgroup (8 waves)
+constexpr int kBM = 256, kBN = 256, kBK = 64;    // workgroup tile
+constexpr int kTM = 2, kTN = 4;                  // 32 x 32 blocks per wave (64 x 128)
+constexpr int kChunks = kBM * kBK / 8 / kLT;     // 16-byte loads per thread per operand
+constexpr float kBigL = 3.0e38f;
+
+struct GemmSmem {
+    unsigned short a[2][kBM * kBK];
+    unsigned short b[2][kBN * kBK];
+};
+
+// Element (row, k) of a staged tile.  Rows are 128 bytes (eight 16-byte
+// chunks, the 32 banks once); chunk c of row r is stored at position
+// c ^ (r & 7), so the 16-byte fragment reads of 8 consecutive rows at one chunk
+// and the staging writes of one row's 8 chunks each touch every bank once.
+__device__ __forceinline__ int lds_at(int row, int k)
+{
+    return row * kBK + ((((k >> 3) ^ row) & 7) << 3) + (k & 7);
+}
+
+// Rows [r0, r0 + 256) x k [k0, k0 + 64) of a K-contiguous bf16 matrix
+// X[row * ld + k] into registers; rows past `rows` re-read the last row
+// (their results are never used).
+__device__ __forceinline__ void load_tile(const unsigned short *X, int64_t ld, int64_t rows,
+                                          int64_t r0, int64_t k0, u32x4 (&r)[kChunks], int tid)
+{
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+        const int c = tid + kLT * i;
+        const int64_t gr = r0 + (c >> 3) < rows ? r0 + (c >> 3) : rows - 1;
+        r[i] = *reinterpret_cast<const u32x4 *>(X + gr * ld + k0 + (c & 7) * 8);
+    }
+}
+
+__device__ __forceinline__ void store_tile(unsigned short *lds, const u32x4 (&r)[kChunks], int tid)
+{
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+        const int c = tid + kLT * i;
+        *reinterpret_cast<u32x4 *>(lds + lds_at(c >> 3, (c & 7) * 8)) = r[i];
+    }
+}
+
+// One K step of 64 from LDS: 4 sub-steps of 16, 16 MFMAs each per wave.
+__device__ __forceinline__ void mma_stage(const unsigned short *la, const unsigned short *lb,
+                                          f32x16 (&acc)[kTM][kTN], int wm, int wn, int lane)
+{
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+        bf16x8 af[kTM], bf[kTN];
+        const int kk = ks * 16 + (lane >> 5) * 8;
+#pragma unroll
+        for (int mb = 0; mb < kTM; ++mb)
+            af[mb] = *reinterpret_cast<const bf16x8 *>(
+                la + lds_at(wm * 64 + mb * 32 + (lane & 31), kk));
+#pragma unroll
+        for (int nb = 0; nb < kTN; ++nb)
+            bf[nb] = *reinterpret_cast<const bf16x8 *>(
+                lb + lds_at(wn * 128 + nb * 32 + (lane & 31), kk));
+#pragma unroll
+        for (int mb = 0; mb < kTM; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < kTN; ++nb)
+                acc[mb][nb] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[kTM][kTN])
+{
+#pragma unroll
+    for (int mb = 0; mb < kTM; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < kTN; ++nb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[mb][nb][v] = 0.0f;
+}
+
+// The K loop over every (N tile, K step) pair of one workgroup, with the next
+// pair's global loads in flight during the current pair's MFMAs; after the
+// last K step of a tile, epi(tile, acc) consumes the accumulators.  A: rows
+// [row0, row0 + 256) of XA; B: 256-row tiles [t_begin, t_end) of XB; nk K
+// steps of 64.
+template <class Epi>
+__device__ __forceinline__ void gemm_tiles(GemmSmem &sm, const unsigned short *XA, int64_t lda,
+                                           int64_t rowsA, int64_t row0, const unsigned short *XB,
+                                           int64_t ldb, int64_t rowsB, int64_t nk,
+                                           int64_t t_begin, int64_t t_end, Epi &&epi)
+{
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;   // 4 x 2 waves
+    const int64_t total = (t_end - t_begin) * nk;
+    if (total <= 0)
+        return;
+    f32x16 acc[kTM][kTN];
+    zero_acc(acc);
+    u32x4 ra[kChunks], rb[kChunks];
+    load_tile(XA, lda, rowsA, row0, 0, ra, tid);
+    load_tile(XB, ldb, rowsB, t_begin * kBN, 0, rb, tid);
+    store_tile(sm.a[0], ra, tid);
+    store_tile(sm.b[0], rb, tid);
+    __syncthreads();
+    for (int64_t it = 0; it < total; ++it) {
+        const int buf = (int)(it & 1);
+        const int64_t tile = t_begin + it / nk, kt = it % nk;
+        const bool more = it + 1 < total;
+        if (more) {
+            const int64_t nt = t_begin + (it + 1) / nk, nkt = (it + 1) % nk;
+            load_tile(XA, lda, rowsA, row0, nkt * kBK, ra, tid);
+            load_tile(XB, ldb, rowsB, nt * kBN, nkt * kBK, rb, tid);
+        }
+        mma_stage(sm.a[buf], sm.b[buf], acc, wm, wn, lane);
+        if (kt == nk - 1) {
+            epi(tile, acc);
+            zero_acc(acc);
+        }
+        if (more) {
+            store_tile(sm.a[buf ^ 1], ra, tid);
+            store_tile(sm.b[buf ^ 1], rb, tid);
+        }
+        __syncthreads();
+    }
+}
+
+// Local row (0..255) of accumulator element v of block mb for this lane.
+__device__ __forceinline__ int acc_row(int wm, int mb, int v, int lane)
+{
+    return wm * 64 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+}
+
+// Reductions over the 32 lanes that hold one row (lane bits 0-4).
+__device__ __forceinline__ float row_max(float x)
+{
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1)
+        x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ __forceinline__ float row_sum(float x)
+{
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1)
+        x += __shfl_xor(x, o);
+    return x;
+}
+__device__ __forceinline__ int row_min(int x)
+{
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1)
+        x = min(x, __shfl_xor(x, o));
+    return x;
+}
+
+// Running target-excluded statistics of one row over the columns seen so far:
+// maximum m, sum s of 2^((z - b) c) at b = max(m, -FLT_MAX), entropy term h at
+// the same base, value sum zs, first column of the maximum.
+struct RowState {
+    float m, s, h, zs;
+    int arg;
+};
+
+// ------------------------------------------------------------------ forward
+template <bool WANT_H, bool WANT_Z>
+__global__ __launch_bounds__(kLT) void k_lce_fwd(LceArgs a)
+{
+    __shared__ GemmSmem sm;
+    __shared__ int s_lab[kBM];
+    __shared__ float s_zt[kBM];
+    __shared__ int s_own[kBM];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int64_t S = a.splits;
+    const int64_t rb = blockIdx.x / S, sp = blockIdx.x % S;   // consecutive blocks: one row block
+    const int64_t row0 = rb * kBM;
+    const int64_t V = a.vocab;
+    const int64_t ntiles = (V + kBN - 1) / kBN;
+    const int64_t t0 = ntiles * sp / S, t1 = ntiles * (sp + 1) / S;
+    if (tid < kBM) {
+        const int64_t r = row0 + tid;
+        int lab = -1;
+        if (r < a.rows) {
+            const int64_t t = a.labels[r];
+            const bool masked = a.row_mask && a.row_mask[r] == 0;
+            if (!masked && t != a.ignore_index && t >= 0 && t < V)
+                lab = (int)t;
+        }
+        s_lab[tid] = lab;
+        s_zt[tid] = 0.0f;
+        s_own[tid] = 0;
+    }
+    __syncthreads();
+
+    const float c = a.c, inv_t = a.inv_t;
+    // Lane j of each half-wave keeps the state of the half's row j (rows
+    // numbered mb * 16 + v).
+    RowState st = RowState{-INFINITY, 0.0f, 0.0f, 0.0f, INT32_MAX};
+
+    auto epi = [&](int64_t tile, f32x16 (&acc)[kTM][kTN]) {
+        const int64_t n0 = tile * kBN + wn * 128 + (lane & 31);
+#pragma unroll
+        for (int mb = 0; mb < kTM; ++mb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int ri = mb * 16 + v;
+                const int rl = acc_row(wm, mb, v, lane);
+                const int lab = s_lab[rl];
+                float x[kTN];
+                float lmax = -INFINITY;
+                int larg = INT32_MAX;
+#pragma unroll
+                for (int nb = 0; nb < kTN; ++nb) {
+                    const int64_t col = n0 + nb * 32;
+                    float z = acc[mb][nb][v];
+                    if (col == lab) {
+                        s_zt[rl] = z;
+                        s_own[rl] = 1;
+                        z = -INFINITY;
+                    }
+                    if (col >= V)
+                        z = -INFINITY;
+                    x[nb] = z;
+                    if (z > lmax) {
+                        lmax = z;
+                        larg = (int)col;
+                    }
+                }
+                const float tmax = row_max(lmax);
+                const float base = fmaxf(tmax, -FLT_MAX);
+                float ls = 0.0f, lh = 0.0f, lz = 0.0f;
+#pragma unroll
+                for (int nb = 0; nb < kTN; ++nb) {
+                    const float e = exp2_hw((x[nb] - base) * c);
+                    ls += e;
+                    if constexpr (WANT_H)
+                        lh = fmaf(e, fminf((base - x[nb]) * inv_t, kBigL), lh);
+                    if constexpr (WANT_Z)
+                        lz += x[nb] == -INFINITY ? 0.0f : x[nb];
+                }
+                const float tsum = row_sum(ls);
+                const int targ = row_min(lmax == tmax && tmax != -INFINITY ? larg : INT32_MAX);
+                float th = 0.0f, tz = 0.0f;
+                if constexpr (WANT_H)
+                    th = row_sum(lh);
+                if constexpr (WANT_Z)
+                    tz = row_sum(lz);
+                if ((lane & 31) == ri) {
+                    // merge the tile (tmax, tsum and th at base) into the row's state
+                    RowState &r = st;
+                    const float M = fmaxf(r.m, tmax);
+                    const float bo = fmaxf(r.m, -FLT_MAX), bn = fmaxf(M, -FLT_MAX);
+                    const float fo = exp2_hw((bo - bn) * c), ft = exp2_hw((base - bn) * c);
+                    if constexpr (WANT_H)
+                        r.h = fo * fmaf(fminf((bn - bo) * inv_t, kBigL), r.s, r.h) +
+                              ft * fmaf(fminf((bn - base) * inv_t, kBigL), tsum, th);
+                    r.s = r.s * fo + tsum * ft;
+                    if (tmax > r.m)
+                        r.arg = targ;
+                    else if (tmax == r.m && tmax != -INFINITY)
+                        r.arg = min(r.arg, targ);
+                    r.m = M;
+                    if constexpr (WANT_Z)
+                        r.zs += tz;
+                }
+            }
+    };
+    gemm_tiles(sm, a.hidden, a.ldh, a.rows, row0, a.weight, a.ldw, V, a.hidden_dim / kBK, t0, t1,
+               epi);
+
+    // The two waves along N hold the two column halves of each row: combine
+    // them through LDS (the operand tiles are done).
+    struct RowPart {
+        float m;
+        int arg;
+        double s, h, z;
+    };
+    RowPart *part = reinterpret_cast<RowPart *>(&sm);   // [2][kBM]
+    {
+        const int ri = lane & 31;
+        RowPart p;
+        p.m = st.m;
+        p.arg = st.arg;
+        p.s = (double)st.s;
+        p.h = (double)st.h;
+        p.z = (double)st.zs;
+        part[wn * kBM + acc_row(wm, ri >> 4, ri & 15, lane)] = p;
+    }
+    __syncthreads();
+    const int64_t r = row0 + tid;
+    if (tid < kBM && r < a.rows) {
+        const RowPart pp[2] = {part[tid], part[kBM + tid]};
+        const float M = fmaxf(pp[0].m, pp[1].m);
+        const double B = (double)fmaxf(M, -FLT_MAX);
+        double S2 = 0.0, H2 = 0.0;
+        int am = INT32_MAX;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            if (pp[q].s > 0.0) {
+                const double bp = (double)fmaxf(pp[q].m, -FLT_MAX);
+                const double f = exp((bp - B) / a.temperature);
+                S2 += pp[q].s * f;
+                H2 += f * (pp[q].h + (B - bp) / a.temperature * pp[q].s);
+            }
+            if (pp[q].m == M && M != -INFINITY)
+                am = min(am, pp[q].arg);
+        }
+        cev_vocab_partial out;
+        out.m = M;
+        out.zt = s_zt[tid];
+        out.arg = am == INT32_MAX ? INT64_MAX : (int64_t)am;
+        out.s = S2;
+        out.h = H2;
+        out.zs = pp[0].z + pp[1].z;
+        out.flags = (s_lab[tid] >= 0 ? 1 : 0) | (s_own[tid] ? 2 : 0);
+        out.pad = 0;
+        a.partials[sp * a.rows + r] = out;
+    }
+}
+
+// ----------------------------------------------------------------- backward
+// dlogits tile by tile: (g/T) p_j - (g/T) eps/V, the target -(g/T)(q - eps +
+// eps/V); p_j = 2^((z_j - m_z) c - log2 d) from the saved record with |g/T|
+// folded into the exponent, the sign of g applied to the bits, bf16 by RNE.
+// Columns [V, ldd) of the dlogits rows are written as zeros.
+__global__ __launch_bounds__(kLT) void k_lce_dl(LceArgs a)
+{
+    __shared__ GemmSmem sm;
+    __shared__ int s_lab[kBM];
+    __shared__ float s_mz[kBM], s_kexp[kBM], s_ev[kBM], s_tv[kBM];
+    __shared__ unsigned s_sgn[kBM];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int64_t S = a.splits;
+    const int64_t rb = blockIdx.x / S, sp = blockIdx.x % S;
+    const int64_t row0 = rb * kBM;
+    const int64_t V = a.vocab, ldd = a.ldd;
+    const int64_t ntiles = (V + kBN - 1) / kBN;
+    const int64_t t0 = ntiles * sp / S, t1 = ntiles * (sp + 1) / S;
+
+    if (tid < kBM) {
+        const int64_t r = row0 + tid;
+        int lab = -1;
+        float mz = 0.0f, kexp = INFINITY, ev = 0.0f, tv = 0.0f;
+        unsigned sgn = 0u;
+        if (r < a.rows) {
+            const int64_t t = a.labels[r];
+            const bool masked = a.row_mask && a.row_mask[r] == 0;
+            const cev_saved sv = a.saved[r];
+            if (!masked && t != a.ignore_index && t >= 0 && t < V && (sv.flags & 1)) {
+                const float gp = a.g[r] * a.inv_t;
+                const float ag = fabsf(gp);
+                const float eps = (float)a.label_smoothing;
+                const float epv = (float)(a.label_smoothing / (double)V);
+                lab = (int)t;
+                mz = sv.m_z;
+                kexp = sv.log2_d - __log2f(ag);
+                ev = ag * epv;
+                tv = -(ag * ((sv.q - eps) + epv));
+                sgn = __float_as_uint(gp) & 0x80000000u;
+            }
+        }
+        s_lab[tid] = lab;
+        s_mz[tid] = mz;
+        s_kexp[tid] = kexp;
+        s_ev[tid] = ev;
+        s_tv[tid] = tv;
+        s_sgn[tid] = sgn;
+    }
+    __syncthreads();
+    const float c = a.c;
+    unsigned short *dl = a.dlogits;
+
+    auto epi = [&](int64_t tile, f32x16 (&acc)[kTM][kTN]) {
+        const int64_t n0 = tile * kBN + wn * 128 + (lane & 31);
+#pragma unroll
+        for (int mb = 0; mb < kTM; ++mb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int rl = acc_row(wm, mb, v, lane);
+                const int64_t r = row0 + rl;
+                if (r >= a.rows)
+                    continue;
+                const int lab = s_lab[rl];
+                const float mz = s_mz[rl], kexp = s_kexp[rl], ev = s_ev[rl], tv = s_tv[rl];
+                const unsigned sgn = s_sgn[rl];
+#pragma unroll
+                for (int nb = 0; nb < kTN; ++nb) {
+                    const int64_t col = n0 + nb * 32;
+                    if (col < ldd) {
+                        float o = exp2_hw(fmaf(acc[mb][nb][v] - mz, c, -kexp)) - ev;
+                        if (col == lab)
+                            o = tv;
+                        if (col >= V)
+                            o = 0.0f;
+                        dl[r * ldd + col] = to_bf16(__uint_as_float(__float_as_uint(o) ^ sgn));
+                    }
+                }
+            }
+    };
+    gemm_tiles(sm, a.hidden, a.ldh, a.rows, row0, a.weight, a.ldw, V, a.hidden_dim / kBK, t0, t1,
+               epi);
+}
+
+// C[M, N] (fp32, row stride ldc) = sum_k A[m][k] B[n][k] over nk K steps of
+// 64, A and B K-contiguous; one 256 x 256 tile per workgroup (M tiles fastest).
+__global__ __launch_bounds__(kLT) void k_lce_gemm(const unsigned short *XA, int64_t lda,
+                                                 int64_t M, const unsigned short *XB,
+                                                 int64_t ldb, int64_t N, int64_t nk, float *C,
+                                                 int64_t ldc)
+{
+    __shared__ GemmSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int64_t mt = (M + kBM - 1) / kBM;
+    const int64_t row0 = (blockIdx.x % mt) * kBM, nt = blockIdx.x / mt;
+    auto epi = [&](int64_t tile, f32x16 (&acc)[kTM][kTN]) {
+        const int64_t n0 = tile * kBN + wn * 128 + (lane & 31);
+#pragma unroll
+        for (int mb = 0; mb < kTM; ++mb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t r = row0 + acc_row(wm, mb, v, lane);
+                if (r >= M)
+                    continue;
+#pragma unroll
+                for (int nb = 0; nb < kTN; ++nb) {
+                    const int64_t col = n0 + nb * 32;
+                    if (col < N)
+                        C[r * ldc + col] = acc[mb][nb][v];
+                }
+            }
+    };
+    gemm_tiles(sm, XA, lda, M, row0, XB, ldb, N, nk, nt, nt + 1, epi);
+}
+
+// D[c][r] = S[r][c] for r < R (zeros for R <= r < rp), c < C: 64 x 64 tiles
+// through LDS (grid: r tiles fastest).
+__global__ __launch_bounds__(256) void k_transpose(const unsigned short *S, int64_t lds_, int64_t R,
+                                                   int64_t C, unsigned short *D, int64_t rp)
+{
+    __shared__ unsigned short t[64][65];
+    const int64_t rtiles = (rp + 63) / 64;
+    const int64_t r0 = (blockIdx.x % rtiles) * 64, c0 = (blockIdx.x / rtiles) * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int i = ty; i < 64; i += 4) {
+        const int64_t r = r0 + i, c = c0 + tx;
+        t[i][tx] = (r < R && c < C) ? S[r * lds_ + c] : (unsigned short)0;
+    }
+    __syncthreads();
+    for (int i = ty; i < 64; i += 4) {
+        const int64_t c = c0 + i, r = r0 + tx;
+        if (c < C && r < rp)
+            D[c * rp + r] = t[tx][i];
+    }
+}
+
+void launch_transpose(const unsigned short *S, int64_t ld, int64_t R, int64_t C,
+                      unsigned short *D, int64_t rp, hipStream_t s)
+{
+    const int64_t tiles = ((rp + 63) / 64) * ((C + 63) / 64);
+    hipLaunchKernelGGL(k_transpose, dim3((unsigned)tiles), dim3(256), 0, s, S, ld, R, C, D, rp);
+}
+
+int64_t round64(int64_t x) { return (x + 63) / 64 * 64; }
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+} // namespace
+
+int64_t lce_splits(int64_t rows, int64_t vocab)
+{
+    // A multiple of 8 vocab splits, enough for 256 workgroups (one per CU):
+    // consecutive workgroups share a row block and the round-robin dispatch
+    // keeps split s on XCD s % 8, so each XCD's L2 streams its part of the
+    // head for every row block.
+    const int64_t ntiles = (vocab + kBN - 1) / kBN;
+    const int64_t nrb = (rows + kBM - 1) / kBM;
+    int64_t s = 8;
+    while (s * nrb < 256 && s < 64)
+        s *= 2;
+    return s <= ntiles ? s : ntiles;
+}
+
+int64_t lce_dl_stride(int64_t vocab) { return round64(vocab); }
+
+hipError_t launch_lce_forward(const LceArgs &a, bool want_h, bool want_z, hipStream_t s)
+{
+    const int64_t nrb = (a.rows + kBM - 1) / kBM;
+    dim3 grid((unsigned)(nrb * a.splits)), block(kLT);
+    if (want_h && want_z)
+        hipLaunchKernelGGL((k_lce_fwd<true, true>), grid, block, 0, s, a);
+    else if (want_h)
+        hipLaunchKernelGGL((k_lce_fwd<true, false>), grid, block, 0, s, a);
+    else if (want_z)
+        hipLaunchKernelGGL((k_lce_fwd<false, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((k_lce_fwd<false, false>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+// Backward workspace: dlogits [R, round64(V)], head^T [H, round64(V)], and
+// for the head gradient dlogits^T [V, round64(R)] and hidden^T [H, round64(R)].
+size_t lce_backward_workspace(int64_t rows, int64_t hidden_dim, int64_t vocab)
+{
+    const size_t vp = (size_t)round64(vocab), rp = (size_t)round64(rows);
+    return align256((size_t)rows * vp * 2) + align256((size_t)hidden_dim * vp * 2) +
+           align256((size_t)vocab * rp * 2) + align256((size_t)hidden_dim * rp * 2);
+}
+
+hipError_t launch_lce_backward(const LceArgs &a, void *workspace, float *dhidden, int64_t ldo,
+                               float *dweight, int64_t ldw_out, hipStream_t s)
+{
+    const int64_t R = a.rows, H = a.hidden_dim, V = a.vocab;
+    const int64_t vp = round64(V), rp = round64(R);
+    char *ws = static_cast<char *>(workspace);
+    unsigned short *dl = reinterpret_cast<unsigned short *>(ws);
+    ws += align256((size_t)R * vp * 2);
+    unsigned short *wt = reinterpret_cast<unsigned short *>(ws);
+    ws += align256((size_t)H * vp * 2);
+    unsigned short *dlt = reinterpret_cast<unsigned short *>(ws);
+    ws += align256((size_t)V * rp * 2);
+    unsigned short *ht = reinterpret_cast<unsigned short *>(ws);
+
+    LceArgs b = a;
+    b.dlogits = dl;
+    b.ldd = vp;
+    const int64_t nrb = (R + kBM - 1) / kBM;
+    hipLaunchKernelGGL(k_lce_dl, dim3((unsigned)(nrb * b.splits)), dim3(kLT), 0, s, b);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    // dhidden[R, H] = dlogits[R, V] x head[V, H]: the head transposed to
+    // [H, vp] (zero columns past V) so both operands run along the vocab.
+    launch_transpose(a.weight, a.ldw, V, H, wt, vp, s);
+    hipLaunchKernelGGL(k_lce_gemm, dim3((unsigned)(nrb * ((H + kBN - 1) / kBN))), dim3(kLT), 0, s,
+                       dl, vp, R, wt, vp, H, vp / kBK, dhidden, ldo);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    // dhead[V, H] = dlogits^T x hidden: both transposed to run along the rows.
+    if (dweight) {
+        launch_transpose(dl, vp, R, V, dlt, rp, s);
+        launch_transpose(a.hidden, a.ldh, R, H, ht, rp, s);
+        const int64_t tiles = ((V + kBM - 1) / kBM) * ((H + kBN - 1) / kBN);
+        hipLaunchKernelGGL(k_lce_gemm, dim3((unsigned)tiles), dim3(kLT), 0, s, dlt, rp, V, ht, rp,
+                           H, rp / kBK, dweight, ldw_out);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+} // namespace cev

@@ -346,6 +346,56 @@ int ce_vocab_shard_backward(const void *logits, int64_t rows, int64_t shard_voca
                             const void *saved, void *dlogits, int64_t dlogits_row_stride,
                             int32_t *status, cev_stream_t stream);
 
+/*
+ * Linear cross-entropy: logits = hidden x head^T, formed tile by tile on the
+ * bf16 matrix cores and consumed in registers, so the [rows, vocab] logits
+ * never reach HBM (the fused linear CE / log-prob setting of [unsloth-2080]
+ * Summary, whose Speed section measures a frozen 2560 x 151936 head).  The
+ * logits are the fp32 accumulations of bf16 products; everything after them
+ * is the collapse-safe cross-entropy of ce_forward / ce_backward.
+ *
+ *   hidden        [rows, hidden_stride] bf16, hidden_dim a multiple of 64 in
+ *                 [64, 65536], hidden_stride >= hidden_dim a multiple of 8,
+ *                 16-byte aligned
+ *   weight        the head, [vocab, weight_stride] bf16 (row j = class j),
+ *                 same rules; no bias
+ *   workspace     device scratch of at least lce_workspace_size(rows,
+ *                 hidden_dim, vocab) bytes, 16-byte aligned; overwritten,
+ *                 calls that share one race
+ *   labels, ignore_index, temperature, label_smoothing, row_mask, status
+ *                 as ce_forward
+ */
+
+/* lce_forward -- loss, log p, entropy, argmax and the saved record of every
+ * row, as ce_forward computes them from the logits hidden x head^T (argmax:
+ * lowest column of the largest fp32 logit).  loss and saved are required;
+ * logp, entropy and argmax may be NULL. */
+int lce_forward(const void *hidden, int64_t rows, int64_t hidden_dim, int64_t hidden_stride,
+                const void *weight, int64_t vocab, int64_t weight_stride, const int64_t *labels,
+                int64_t ignore_index, double temperature, double label_smoothing,
+                const uint8_t *row_mask, float *loss, void *saved, float *logp, float *entropy,
+                int64_t *argmax, void *workspace, size_t workspace_bytes, int32_t *status,
+                cev_stream_t stream);
+
+/* lce_backward -- with dlogits = ce_backward's gradient of the per-row loss
+ * weighted by g (recomputed from hidden, head and the saved record):
+ *   dhidden = dlogits x head   [rows, dhidden_stride] fp32, required
+ *   dweight = dlogits^T x hidden   [vocab, dweight_stride] fp32, or NULL for a
+ *             frozen head
+ * Both strides >= hidden_dim.  dlogits is kept in the workspace in bf16
+ * (rounded to nearest even), the operand the two products read. */
+int lce_backward(const void *hidden, int64_t rows, int64_t hidden_dim, int64_t hidden_stride,
+                 const void *weight, int64_t vocab, int64_t weight_stride,
+                 const int64_t *labels, int64_t ignore_index, double temperature,
+                 double label_smoothing, const uint8_t *row_mask, const float *g,
+                 const void *saved, float *dhidden, int64_t dhidden_stride, float *dweight,
+                 int64_t dweight_stride, void *workspace, size_t workspace_bytes,
+                 int32_t *status, cev_stream_t stream);
+
+/* Bytes of workspace lce_forward and lce_backward need (0 for invalid
+ * arguments). */
+size_t lce_workspace_size(int64_t rows, int64_t hidden_dim, int64_t vocab);
+
 /* Bytes of workspace that let ce_forward hold the compacted row list and
  * count and, for few rows, the split-row partial records (0 for invalid
  * arguments). */

@@ -34,6 +34,7 @@ def test_header_declares_the_boundary():
     names = set(declared_functions())
     assert {"sls_forward", "sls_topk_forward", "sls_topk_backward", "ce_forward", "ce_backward",
             "ce_fused", "ce_vocab_shard_forward", "ce_vocab_merge", "ce_vocab_shard_backward",
+            "lce_forward", "lce_backward", "lce_workspace_size",
             "cev_workspace_size", "cev_status_string", "cev_version"} <= names
 
 
@@ -303,3 +304,50 @@ def test_product_never_imports_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "oracle_" not in text, f
+
+
+def test_lce_validation(lib):
+    def fwd(**kw):
+        a = dict(h=A, rows=4, hd=128, hs=128, w=B, V=1000, ws=128, labels=A, ig=-100, T=1.0,
+                 eps=0.0, mask=None, loss=A, saved=A, logp=None, ent=None, arg=None, wk=A,
+                 wkb=1 << 30, status=None)
+        a.update(kw)
+        return lib.lce_forward(a["h"], a["rows"], a["hd"], a["hs"], a["w"], a["V"], a["ws"],
+                               a["labels"], a["ig"], a["T"], a["eps"], a["mask"], a["loss"],
+                               a["saved"], a["logp"], a["ent"], a["arg"], a["wk"], a["wkb"],
+                               a["status"], None)
+    assert fwd(hd=100, hs=104) == E["SHAPE"]          # hidden size not a multiple of 64
+    assert fwd(hd=0) == E["SHAPE"]
+    assert fwd(hs=120) == E["STRIDE"]
+    assert fwd(hs=132) == E["STRIDE"]                 # stride not a multiple of 8
+    assert fwd(ws=64) == E["STRIDE"]
+    assert fwd(h=A + 8) == E["ALIGN"]                 # 16-byte alignment
+    assert fwd(w=B + 8) == E["ALIGN"]
+    assert fwd(wk=None) == E["NULL"]
+    assert fwd(saved=None) == E["NULL"]
+    assert fwd(wkb=lib.lce_workspace_size(4, 128, 1000) - 1) == E["WORKSPACE"]
+    assert fwd(T=0.0) == E["TEMP"]
+    assert fwd(eps=-1.0) == E["SMOOTH"]
+    assert fwd(V=0) == E["SHAPE"]
+    assert fwd(rows=0, h=None, w=None) == E["OK"]
+    # dlogits [R, V64], head^T [H, V64], dlogits^T [V, R64], hidden^T [H, R64] (bf16)
+    assert lib.lce_workspace_size(8192, 2560, 151936) == 2 * (8192 * 151936 + 2560 * 151936 +
+                                                              151936 * 8192 + 2560 * 8192)
+    assert lib.lce_workspace_size(8, 100, 10) == 0
+
+    def bwd(**kw):
+        a = dict(h=A, rows=4, hd=128, hs=128, w=B, V=1000, ws=128, labels=A, ig=-100, T=1.0,
+                 eps=0.0, mask=None, g=A, saved=A, dh=A, dhs=128, dw=None, dws=0, wk=A,
+                 wkb=1 << 30, status=None)
+        a.update(kw)
+        return lib.lce_backward(a["h"], a["rows"], a["hd"], a["hs"], a["w"], a["V"], a["ws"],
+                                a["labels"], a["ig"], a["T"], a["eps"], a["mask"], a["g"],
+                                a["saved"], a["dh"], a["dhs"], a["dw"], a["dws"], a["wk"],
+                                a["wkb"], a["status"], None)
+    assert bwd(dhs=64) == E["STRIDE"]
+    assert bwd(dw=B, dws=100) == E["STRIDE"]
+    assert bwd(dh=None) == E["NULL"]
+    assert bwd(g=None) == E["NULL"]
+    assert bwd(saved=A + 4) == E["ALIGN"]
+    assert bwd(wkb=16) == E["WORKSPACE"]
+    assert bwd(rows=0) == E["OK"]

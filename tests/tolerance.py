@@ -17,6 +17,9 @@ from __future__ import annotations
 import numpy as np
 
 FLOOR = 2.0 ** -126
+# Spacing of fp32 subnormals: an fp32 output below 2^-126 is exact only to
+# half of this, so a per-row output that small is compared with this floor.
+SUBNORMAL = 2.0 ** -149
 
 RTOL = {
     "f32": dict(logp=2e-6, loss=2e-6, topk=2e-6, entropy=1e-5, dlogits=2e-5),
