@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD published
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, AMD published
 METRIC = "rows/s and achieved HBM GB/s (% peak), 8192x152064 bf16 fwd+bwd, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_backward_grpo_8192x152064_bf16.json")
 KERNEL_SOURCES = ["backward.hip", "cev_device.h"]
@@ -180,6 +181,58 @@ def cpu_baseline(w, valid_rows, seconds=12.0, threads=None):
                       f"(forward with argmax + full gradient row each), {dt:.1f} s wall"}
 
 
+def bench_linear(args, torch, cev, workloads, dev):
+    """lce_forward and lce_backward (frozen head: dhidden only) on the
+    8192 x 2560 x 151936 bf16 shape; FLOP counts are the products' 2 R H V
+    (forward) and 2 x 2 R H V (backward: logits recomputed, then dhidden)."""
+    R, H, Vl = 8192, 2560, 151936
+    log(f"[bench] linear CE: generating {R}x{H} hidden, {Vl}x{H} head")
+    w = workloads.linear(rows=R, hidden=H, vocab=Vl)
+    hid = torch.from_numpy(w["hidden"].view(np.int16)).to(dev).view(torch.bfloat16)
+    head = torch.from_numpy(w["weight"].view(np.int16)).to(dev).view(torch.bfloat16)
+    lab = torch.from_numpy(w["labels"]).to(dev)
+    msk = torch.from_numpy(w["row_mask"]).to(dev)
+    gl = torch.from_numpy(w["g"]).to(dev)
+    out = cev.lce_forward(hid, head, lab, 1.0, row_mask=msk, argmax=True)
+    dh, _ = cev.lce_backward(hid, head, lab, gl, out["saved"], 1.0, row_mask=msk,
+                             workspace=out["workspace"])
+    steps = max(2, args.steps // 4)
+    for _ in range(max(1, args.warmup // 2)):
+        cev.lce_forward(hid, head, lab, 1.0, row_mask=msk, argmax=True, out=out)
+        cev.lce_backward(hid, head, lab, gl, out["saved"], 1.0, row_mask=msk,
+                         workspace=out["workspace"], dhidden=dh)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record()
+        cev.lce_forward(hid, head, lab, 1.0, row_mask=msk, argmax=True, out=out)
+        e1.record()
+        cev.lce_backward(hid, head, lab, gl, out["saved"], 1.0, row_mask=msk,
+                         workspace=out["workspace"], dhidden=dh)
+        e2.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    f_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    b_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    flop = 2.0 * R * H * Vl
+    log(f"[bench] linear CE: forward {f_ms:.2f} ms, backward {b_ms:.2f} ms")
+    res = {"entry": "lce_forward + lce_backward (frozen head: dhidden only), logits never "
+                    "stored; 2560 x 151936 head as in the unsloth-zoo #2080 Speed section",
+           "shape": {"rows": R, "hidden": H, "vocab": Vl}, "steps": steps,
+           "ms_per_step": wall, "rows_per_s": R / (wall / 1e3),
+           "forward_ms": f_ms, "backward_ms": b_ms,
+           "forward_TFLOPs": flop / (f_ms / 1e3) / 1e12,
+           "backward_TFLOPs": 2 * flop / (b_ms / 1e3) / 1e12,
+           "step_TFLOPs": 3 * flop / ((f_ms + b_ms) / 1e3) / 1e12,
+           "roofline": {"bound": "mfma", "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "achieved": 3 * flop / ((f_ms + b_ms) / 1e3) / 1e12,
+                        "frac": 3 * flop / ((f_ms + b_ms) / 1e3) / 1e12 / PEAK_BF16_TFLOPS}}
+    del hid, head, out, dh
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -192,6 +245,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain elementwise kernel over 1 GiB in / 1 GiB out, "
                          "the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--no-linear", action="store_true",
+                    help="skip the linear cross-entropy measurement (8192 x 2560 x 151936)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: turn the two counter runs' csv files into the "
                          "committed traffic figures and print the counter table")
@@ -309,6 +364,10 @@ def main():
     s_bwd = float(np.mean([e[2].elapsed_time(e[3]) for e in sev]))
     del shard, dls, parts
 
+    del logits, dl, out, fout
+    torch.cuda.empty_cache()
+    linear = None if args.no_linear else bench_linear(args, torch, cev, workloads, dev)
+
     ES = 2
     fwd_bytes = n_valid * V * ES                    # valid rows read once
     bwd_bytes = n_valid * V * ES + R * V * ES       # valid rows re-read, every row written
@@ -352,6 +411,7 @@ def main():
                   "algorithmic_bytes": fwd_bytes + R * V * ES,
                   "GBps": (fwd_bytes + R * V * ES) / (fused_ms / 1e3) / 1e9,
                   "frac_of_peak": (fwd_bytes + R * V * ES) / (fused_ms / 1e3) / 1e9 / PEAK_HBM_GBS},
+        "linear_ce": linear,
         "vocab_shard": {"entry": f"one rank of {P}-way vocab parallelism: "
                                  "ce_vocab_shard_forward on its contiguous shard, ce_vocab_merge "
                                  f"of {P} shards' records, ce_vocab_shard_backward",
