@@ -29,6 +29,10 @@
 // peak on MI355X.  Fragment layout of the 32x32x16 bf16 MFMA on gfx950 (checked on the
 // device): lane l supplies A[l % 32][8 (l / 32) .. +8] and B[same k][l % 32];
 // accumulator element v of lane l is C[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
+// The B rows are staged permuted so that the four 32-column blocks of a wave
+// interleave: lane l of block nb holds output column 4 (l % 32) + nb of the
+// wave's 128, so each lane owns four adjacent columns of every row it holds
+// (8- and 16-byte stores of dlogits and of the gradients).
 #include "cev_device.h"
 #include "cev_launch.h"
 
@@ -58,16 +62,26 @@ __device__ __forceinline__ int lds_at(int row, int k)
     return row * kBK + ((((k >> 3) ^ row) & 7) << 3) + (k & 7);
 }
 
+// Tile row q of a B tile holds matrix row perm_b(q): within each half of 128,
+// q = 32 nb + i takes row 4 i + nb.
+__device__ __forceinline__ int perm_b(int q)
+{
+    return (q & 128) | ((q & 31) << 2) | ((q >> 5) & 3);
+}
+
 // Rows [r0, r0 + 256) x k [k0, k0 + 64) of a K-contiguous bf16 matrix
-// X[row * ld + k] into registers; rows past `rows` re-read the last row
+// X[row * ld + k] into registers (tile row q from matrix row r0 + q, or
+// r0 + perm_b(q) for a B tile); rows past `rows` re-read the last row
 // (their results are never used).
+template <bool PERM>
 __device__ __forceinline__ void load_tile(const unsigned short *X, int64_t ld, int64_t rows,
                                           int64_t r0, int64_t k0, u32x4 (&r)[kChunks], int tid)
 {
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
         const int c = tid + kLT * i;
-        const int64_t gr = r0 + (c >> 3) < rows ? r0 + (c >> 3) : rows - 1;
+        const int q = PERM ? perm_b(c >> 3) : (c >> 3);
+        const int64_t gr = r0 + q < rows ? r0 + q : rows - 1;
         r[i] = *reinterpret_cast<const u32x4 *>(X + gr * ld + k0 + (c & 7) * 8);
     }
 }
@@ -120,8 +134,8 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[kTM][kTN])
 // The K loop over every (N tile, K step) pair of one workgroup, with the next
 // pair's global loads in flight during the current pair's MFMAs; after the
 // last K step of a tile, epi(tile, acc) consumes the accumulators.  A: rows
-// [row0, row0 + 256) of XA; B: 256-row tiles [t_begin, t_end) of XB; nk K
-// steps of 64.
+// [row0, row0 + 256) of XA; B: 256-row tiles [t_begin, t_end) of XB (staged
+// permuted, see perm_b); nk K steps of 64.
 template <class Epi>
 __device__ __forceinline__ void gemm_tiles(GemmSmem &sm, const unsigned short *XA, int64_t lda,
                                            int64_t rowsA, int64_t row0, const unsigned short *XB,
@@ -130,37 +144,46 @@ __device__ __forceinline__ void gemm_tiles(GemmSmem &sm, const unsigned short *X
 {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 1, wn = w & 1;   // 4 x 2 waves
-    const int64_t total = (t_end - t_begin) * nk;
-    if (total <= 0)
+    if (t_end <= t_begin || nk <= 0)
         return;
     f32x16 acc[kTM][kTN];
     zero_acc(acc);
     u32x4 ra[kChunks], rb[kChunks];
-    load_tile(XA, lda, rowsA, row0, 0, ra, tid);
-    load_tile(XB, ldb, rowsB, t_begin * kBN, 0, rb, tid);
+    load_tile<false>(XA, lda, rowsA, row0, 0, ra, tid);
+    load_tile<true>(XB, ldb, rowsB, t_begin * kBN, 0, rb, tid);
     store_tile(sm.a[0], ra, tid);
     store_tile(sm.b[0], rb, tid);
     __syncthreads();
-    for (int64_t it = 0; it < total; ++it) {
-        const int buf = (int)(it & 1);
-        const int64_t tile = t_begin + it / nk, kt = it % nk;
-        const bool more = it + 1 < total;
+    // (tile, kt): the pair in the LDS buffer `buf`; (ntile, nkt): the next one
+    int64_t tile = t_begin;
+    int kt = 0, buf = 0;
+    for (;;) {
+        int nkt = kt + 1;
+        int64_t ntile = tile;
+        if (nkt == nk) {
+            nkt = 0;
+            ++ntile;
+        }
+        const bool more = ntile < t_end;
         if (more) {
-            const int64_t nt = t_begin + (it + 1) / nk, nkt = (it + 1) % nk;
-            load_tile(XA, lda, rowsA, row0, nkt * kBK, ra, tid);
-            load_tile(XB, ldb, rowsB, nt * kBN, nkt * kBK, rb, tid);
+            load_tile<false>(XA, lda, rowsA, row0, (int64_t)nkt * kBK, ra, tid);
+            load_tile<true>(XB, ldb, rowsB, ntile * kBN, (int64_t)nkt * kBK, rb, tid);
         }
         mma_stage(sm.a[buf], sm.b[buf], acc, wm, wn, lane);
-        if (kt == nk - 1) {
+        if (nkt == 0) {
             epi(tile, acc);
             zero_acc(acc);
         }
-        if (more) {
-            store_tile(sm.a[buf ^ 1], ra, tid);
-            store_tile(sm.b[buf ^ 1], rb, tid);
-        }
+        if (!more)
+            break;
+        store_tile(sm.a[buf ^ 1], ra, tid);
+        store_tile(sm.b[buf ^ 1], rb, tid);
         __syncthreads();
+        tile = ntile;
+        kt = nkt;
+        buf ^= 1;
     }
+    __syncthreads();
 }
 
 // Local row (0..255) of accumulator element v of block mb for this lane.
@@ -169,27 +192,54 @@ __device__ __forceinline__ int acc_row(int wm, int mb, int v, int lane)
     return wm * 64 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
 }
 
-// Reductions over the 32 lanes that hold one row (lane bits 0-4).
+// Reductions over the 32 lanes that hold one row (lane bits 0-4), without the
+// LDS crossbar: DPP swaps lanes within each quad (quad_perm [1,0,3,2] and
+// [2,3,0,1]), then quad with quad (row_half_mirror: lane i of 8 reads 7 - i)
+// and eight with eight (row_mirror: lane i of 16 reads 15 - i); the two
+// 16-lane rows of each half-wave are combined by v_permlane16_swap, which
+// hands each row the other's values.  Every lane ends with the result.
+template <int CTRL> __device__ __forceinline__ int dpp(int x)
+{
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL> __device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(dpp<CTRL>(__float_as_int(x)));
+}
+constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
+
+template <class T, class Op> __device__ __forceinline__ T row_reduce(T x, Op op)
+{
+    x = op(x, dpp<kQuadSwap1>(x));
+    x = op(x, dpp<kQuadSwap2>(x));
+    x = op(x, dpp<kHalfMirror>(x));
+    x = op(x, dpp<kMirror>(x));
+    unsigned u;
+    __builtin_memcpy(&u, &x, 4);
+    const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    T a, b;
+    const unsigned ua = sw[0], ub = sw[1];
+    __builtin_memcpy(&a, &ua, 4);
+    __builtin_memcpy(&b, &ub, 4);
+    return op(a, b);
+}
 __device__ __forceinline__ float row_max(float x)
 {
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1)
-        x = fmaxf(x, __shfl_xor(x, o));
-    return x;
+    return row_reduce(x, [](float p, float q) { return fmaxf(p, q); });
 }
 __device__ __forceinline__ float row_sum(float x)
 {
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1)
-        x += __shfl_xor(x, o);
-    return x;
+    return row_reduce(x, [](float p, float q) { return p + q; });
 }
 __device__ __forceinline__ int row_min(int x)
 {
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1)
-        x = min(x, __shfl_xor(x, o));
-    return x;
+    return row_reduce(x, [](int p, int q) { return min(p, q); });
+}
+
+// First output column of the four this lane holds in a wave's 128 columns.
+__device__ __forceinline__ int64_t lane_col(int64_t tile, int wn, int lane)
+{
+    return tile * kBN + wn * 128 + 4 * (lane & 31);
 }
 
 // Running target-excluded statistics of one row over the columns seen so far:
@@ -237,33 +287,36 @@ __global__ __launch_bounds__(kLT) void k_lce_fwd(LceArgs a)
     RowState st = RowState{-INFINITY, 0.0f, 0.0f, 0.0f, INT32_MAX};
 
     auto epi = [&](int64_t tile, f32x16 (&acc)[kTM][kTN]) {
-        const int64_t n0 = tile * kBN + wn * 128 + (lane & 31);
+        const int64_t c0 = lane_col(tile, wn, lane);
 #pragma unroll
         for (int mb = 0; mb < kTM; ++mb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int ri = mb * 16 + v;
                 const int rl = acc_row(wm, mb, v, lane);
-                const int lab = s_lab[rl];
-                float x[kTN];
+                const int64_t d = (int64_t)s_lab[rl] - c0;   // the target among this lane's four?
+                const int tn = d >= 0 && d < kTN ? (int)d : -1;
+                float x[kTN], zt = 0.0f;
                 float lmax = -INFINITY;
                 int larg = INT32_MAX;
 #pragma unroll
                 for (int nb = 0; nb < kTN; ++nb) {
-                    const int64_t col = n0 + nb * 32;
                     float z = acc[mb][nb][v];
-                    if (col == lab) {
-                        s_zt[rl] = z;
-                        s_own[rl] = 1;
+                    if (nb == tn) {
+                        zt = z;
                         z = -INFINITY;
                     }
-                    if (col >= V)
+                    if (c0 + nb >= V)
                         z = -INFINITY;
                     x[nb] = z;
                     if (z > lmax) {
                         lmax = z;
-                        larg = (int)col;
+                        larg = (int)(c0 + nb);
                     }
+                }
+                if (tn >= 0) {
+                    s_zt[rl] = zt;
+                    s_own[rl] = 1;
                 }
                 const float tmax = row_max(lmax);
                 const float base = fmaxf(tmax, -FLT_MAX);
@@ -362,12 +415,15 @@ __global__ __launch_bounds__(kLT) void k_lce_fwd(LceArgs a)
 // eps/V); p_j = 2^((z_j - m_z) c - log2 d) from the saved record with |g/T|
 // folded into the exponent, the sign of g applied to the bits, bf16 by RNE.
 // Columns [V, ldd) of the dlogits rows are written as zeros.
+struct __align__(16) DlRow {
+    float mz, kexp, ev, tv;
+};
+
 __global__ __launch_bounds__(kLT) void k_lce_dl(LceArgs a)
 {
     __shared__ GemmSmem sm;
-    __shared__ int s_lab[kBM];
-    __shared__ float s_mz[kBM], s_kexp[kBM], s_ev[kBM], s_tv[kBM];
-    __shared__ unsigned s_sgn[kBM];
+    __shared__ DlRow s_rc[kBM];
+    __shared__ int2 s_ls[kBM];     // label, sign bit of g
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 1, wn = w & 1;
     const int64_t S = a.splits;
@@ -380,7 +436,7 @@ __global__ __launch_bounds__(kLT) void k_lce_dl(LceArgs a)
     if (tid < kBM) {
         const int64_t r = row0 + tid;
         int lab = -1;
-        float mz = 0.0f, kexp = INFINITY, ev = 0.0f, tv = 0.0f;
+        float mz = 0.0f, kexp = INFINITY, ev = 0.0f, tv = 0.0f;   // invalid rows: all zeros
         unsigned sgn = 0u;
         if (r < a.rows) {
             const int64_t t = a.labels[r];
@@ -399,19 +455,19 @@ __global__ __launch_bounds__(kLT) void k_lce_dl(LceArgs a)
                 sgn = __float_as_uint(gp) & 0x80000000u;
             }
         }
-        s_lab[tid] = lab;
-        s_mz[tid] = mz;
-        s_kexp[tid] = kexp;
-        s_ev[tid] = ev;
-        s_tv[tid] = tv;
-        s_sgn[tid] = sgn;
+        s_rc[tid] = DlRow{mz, kexp, ev, tv};
+        s_ls[tid] = make_int2(lab, (int)sgn);
     }
     __syncthreads();
     const float c = a.c;
     unsigned short *dl = a.dlogits;
 
+    // Each lane writes its four adjacent columns of a row as one 8-byte store
+    // (ldd is a multiple of 64, so a group of four is wholly inside or past it).
     auto epi = [&](int64_t tile, f32x16 (&acc)[kTM][kTN]) {
-        const int64_t n0 = tile * kBN + wn * 128 + (lane & 31);
+        const int64_t c0 = lane_col(tile, wn, lane);
+        if (c0 >= ldd)
+            return;
 #pragma unroll
         for (int mb = 0; mb < kTM; ++mb)
 #pragma unroll
@@ -420,41 +476,54 @@ __global__ __launch_bounds__(kLT) void k_lce_dl(LceArgs a)
                 const int64_t r = row0 + rl;
                 if (r >= a.rows)
                     continue;
-                const int lab = s_lab[rl];
-                const float mz = s_mz[rl], kexp = s_kexp[rl], ev = s_ev[rl], tv = s_tv[rl];
-                const unsigned sgn = s_sgn[rl];
+                const DlRow rc = s_rc[rl];
+                const int2 ls = s_ls[rl];
+                float o[kTN];
 #pragma unroll
                 for (int nb = 0; nb < kTN; ++nb) {
-                    const int64_t col = n0 + nb * 32;
-                    if (col < ldd) {
-                        float o = exp2_hw(fmaf(acc[mb][nb][v] - mz, c, -kexp)) - ev;
-                        if (col == lab)
-                            o = tv;
-                        if (col >= V)
-                            o = 0.0f;
-                        dl[r * ldd + col] = to_bf16(__uint_as_float(__float_as_uint(o) ^ sgn));
-                    }
+                    const int64_t col = c0 + nb;
+                    float e = exp2_hw(fmaf(acc[mb][nb][v] - rc.mz, c, -rc.kexp)) - rc.ev;
+                    if (col == ls.x)
+                        e = rc.tv;
+                    if (col >= V)
+                        e = 0.0f;
+                    o[nb] = __uint_as_float(__float_as_uint(e) ^ (unsigned)ls.y);
                 }
+                uint2 pk;
+                pk.x = pack_bf16x2(o[0], o[1]);
+                pk.y = pack_bf16x2(o[2], o[3]);
+                *reinterpret_cast<uint2 *>(dl + r * ldd + c0) = pk;
             }
     };
     gemm_tiles(sm, a.hidden, a.ldh, a.rows, row0, a.weight, a.ldw, V, a.hidden_dim / kBK, t0, t1,
                epi);
 }
 
-// C[M, N] (fp32, row stride ldc) = sum_k A[m][k] B[n][k] over nk K steps of
-// 64, A and B K-contiguous; one 256 x 256 tile per workgroup (M tiles fastest).
+// C[M, N] (fp32, row stride ldc) = sum_k A[m][k] B[n][k], A and B
+// K-contiguous, N a multiple of 4; one 256 x 256 tile per workgroup (M tiles
+// fastest).  Split along K: workgroup split s covers K steps
+// [nk s / splits, nk (s + 1) / splits) of 64 and writes its partial product to
+// C + s * cstride (reduced afterwards in split order).  vec4: C and ldc allow
+// 16-byte stores.
 __global__ __launch_bounds__(kLT) void k_lce_gemm(const unsigned short *XA, int64_t lda,
                                                  int64_t M, const unsigned short *XB,
-                                                 int64_t ldb, int64_t N, int64_t nk, float *C,
-                                                 int64_t ldc)
+                                                 int64_t ldb, int64_t N, int64_t nk,
+                                                 int64_t splits, float *C, int64_t ldc,
+                                                 int64_t cstride, int vec4)
 {
     __shared__ GemmSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 1, wn = w & 1;
     const int64_t mt = (M + kBM - 1) / kBM;
-    const int64_t row0 = (blockIdx.x % mt) * kBM, nt = blockIdx.x / mt;
+    const int64_t tiles = mt * ((N + kBN - 1) / kBN);
+    const int64_t sp = blockIdx.x / tiles, t = blockIdx.x % tiles;
+    const int64_t row0 = (t % mt) * kBM, nt = t / mt;
+    const int64_t k0 = nk * sp / splits, k1 = nk * (sp + 1) / splits;
+    float *Cs = C + sp * cstride;
     auto epi = [&](int64_t tile, f32x16 (&acc)[kTM][kTN]) {
-        const int64_t n0 = tile * kBN + wn * 128 + (lane & 31);
+        const int64_t c0 = lane_col(tile, wn, lane);
+        if (c0 >= N)
+            return;
 #pragma unroll
         for (int mb = 0; mb < kTM; ++mb)
 #pragma unroll
@@ -462,15 +531,45 @@ __global__ __launch_bounds__(kLT) void k_lce_gemm(const unsigned short *XA, int6
                 const int64_t r = row0 + acc_row(wm, mb, v, lane);
                 if (r >= M)
                     continue;
+                float *dst = Cs + r * ldc + c0;
+                if (vec4) {
+                    *reinterpret_cast<float4 *>(dst) =
+                        make_float4(acc[mb][0][v], acc[mb][1][v], acc[mb][2][v], acc[mb][3][v]);
+                } else {
 #pragma unroll
-                for (int nb = 0; nb < kTN; ++nb) {
-                    const int64_t col = n0 + nb * 32;
-                    if (col < N)
-                        C[r * ldc + col] = acc[mb][nb][v];
+                    for (int nb = 0; nb < kTN; ++nb)
+                        dst[nb] = acc[mb][nb][v];
                 }
             }
     };
-    gemm_tiles(sm, XA, lda, M, row0, XB, ldb, N, nk, nt, nt + 1, epi);
+    gemm_tiles(sm, XA + k0 * kBK, lda, M, row0, XB + k0 * kBK, ldb, N, k1 - k0, nt, nt + 1,
+               epi);
+}
+
+// out[r][c] = sum over s in order of P[s][r][c] (P rows of N floats, N a
+// multiple of 4); four columns per thread.
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float *P, int64_t splits,
+                                                      int64_t M, int64_t N, float *out,
+                                                      int64_t ldo)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t nq = N / 4;
+    if (i >= M * nq)
+        return;
+    const int64_t r = i / nq, c = (i % nq) * 4;
+    float4 acc = *reinterpret_cast<const float4 *>(P + r * N + c);
+    for (int64_t s = 1; s < splits; ++s) {
+        const float4 p = *reinterpret_cast<const float4 *>(P + (s * M + r) * N + c);
+        acc.x += p.x;
+        acc.y += p.y;
+        acc.z += p.z;
+        acc.w += p.w;
+    }
+    float *dst = out + r * ldo + c;
+    dst[0] = acc.x;
+    dst[1] = acc.y;
+    dst[2] = acc.z;
+    dst[3] = acc.w;
 }
 
 // D[c][r] = S[r][c] for r < R (zeros for R <= r < rp), c < C: 64 x 64 tiles
@@ -503,6 +602,27 @@ void launch_transpose(const unsigned short *S, int64_t ld, int64_t R, int64_t C,
 
 int64_t round64(int64_t x) { return (x + 63) / 64 * 64; }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+int vec4_ok(const float *p, int64_t ld) { return ((uintptr_t)p % 16 == 0 && ld % 4 == 0) ? 1 : 0; }
+
+// K splits for a product of `tiles` output tiles with nk K steps: the fewest
+// splits that minimise the number of full-chip rounds per split (a grid of
+// tiles x S workgroups on 256 compute units, one workgroup each), keeping at
+// least 16 K steps per split and S partial products within max_by_room.
+int64_t gemm_splits(int64_t tiles, int64_t nk, size_t max_by_room)
+{
+    constexpr int64_t kCUs = 256;
+    int64_t best = 1;
+    double best_t = (double)((tiles + kCUs - 1) / kCUs);
+    for (int64_t s = 2; s <= 16 && (size_t)s <= max_by_room && nk / s >= 16; ++s) {
+        const double t = (double)((tiles * s + kCUs - 1) / kCUs) / (double)s;
+        if (t < best_t - 1e-9) {
+            best = s;
+            best_t = t;
+        }
+    }
+    return best;
+}
 
 } // namespace
 
@@ -570,18 +690,34 @@ hipError_t launch_lce_backward(const LceArgs &a, void *workspace, float *dhidden
         return e;
     // dhidden[R, H] = dlogits[R, V] x head[V, H]: the head transposed to
     // [H, vp] (zero columns past V) so both operands run along the vocab.
+    // Few output tiles and a long contraction: split along K so the grid fills
+    // the chip; the partials live where dlogits^T and hidden^T go later.
     launch_transpose(a.weight, a.ldw, V, H, wt, vp, s);
-    hipLaunchKernelGGL(k_lce_gemm, dim3((unsigned)(nrb * ((H + kBN - 1) / kBN))), dim3(kLT), 0, s,
-                       dl, vp, R, wt, vp, H, vp / kBK, dhidden, ldo);
+    const int64_t tiles = nrb * ((H + kBN - 1) / kBN);
+    const size_t room = align256((size_t)V * rp * 2) + align256((size_t)H * rp * 2);
+    const int64_t S = gemm_splits(tiles, vp / kBK, room / ((size_t)R * H * 4));
+    if (S > 1) {
+        float *part = reinterpret_cast<float *>(dlt);
+        hipLaunchKernelGGL(k_lce_gemm, dim3((unsigned)(tiles * S)), dim3(kLT), 0, s, dl, vp, R, wt,
+                           vp, H, vp / kBK, S, part, H, R * H, 1);
+        const int64_t n = R * (H / 4);
+        hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                           part, S, R, H, dhidden, ldo);
+    } else {
+        hipLaunchKernelGGL(k_lce_gemm, dim3((unsigned)tiles), dim3(kLT), 0, s, dl, vp, R, wt, vp,
+                           H, vp / kBK, (int64_t)1, dhidden, ldo, (int64_t)0,
+                           vec4_ok(dhidden, ldo));
+    }
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     // dhead[V, H] = dlogits^T x hidden: both transposed to run along the rows.
     if (dweight) {
         launch_transpose(dl, vp, R, V, dlt, rp, s);
         launch_transpose(a.hidden, a.ldh, R, H, ht, rp, s);
-        const int64_t tiles = ((V + kBM - 1) / kBM) * ((H + kBN - 1) / kBN);
-        hipLaunchKernelGGL(k_lce_gemm, dim3((unsigned)tiles), dim3(kLT), 0, s, dlt, rp, V, ht, rp,
-                           H, rp / kBK, dweight, ldw_out);
+        const int64_t wtiles = ((V + kBM - 1) / kBM) * ((H + kBN - 1) / kBN);
+        hipLaunchKernelGGL(k_lce_gemm, dim3((unsigned)wtiles), dim3(kLT), 0, s, dlt, rp, V, ht,
+                           rp, H, rp / kBK, (int64_t)1, dweight, ldw_out, (int64_t)0,
+                           vec4_ok(dweight, ldw_out));
         e = hipGetLastError();
     }
     return e;

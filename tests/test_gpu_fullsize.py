@@ -216,3 +216,78 @@ def test_grpo_full_vocab_parallel_p8():
         dref = oracle.ce_grad_rows(w["logits"], w["labels"], g64, 1.0, row_mask=w["row_mask"],
                                    r0=int(r), r1=int(r) + 1)[0]
         assert_close(f"sharded dlogits row {r}", dsel[i], dref, RTOL["bf16"]["dlogits"], FLOOR)
+
+
+def test_linear_full_8192x2560x151936():
+    """lce_forward + lce_backward (frozen head) at the benchmarked shape, 2% of
+    the rows peaked at the accuracy margins.  Every row: log p <= 0, loss >= 0,
+    ignored rows 0 / -1 / zero dhidden, bf16 dlogits rows summing to zero.
+    Sampled rows against the fp64 oracle under the random-bf16 product bound:
+    each logit may err by dz = (H / 16 + 2) 2^-24 max_j sum_k |h_k w_jk| (one
+    fp32 rounding per 16-deep MFMA step), which moves log p, the loss and every
+    probability by at most 2 dz / T relative."""
+    from gpu_helpers import DEV, say, to_dev, to_host
+    import cross_entropy_vocab_amd as cev
+    say("[full] linear 8192x2560x151936 bf16, frozen head")
+    w = workloads.linear(peaked_frac=0.02)
+    R, H = w["hidden"].shape
+    V = w["weight"].shape[0]
+    T = w["temperature"]
+    hid, head = to_dev(w["hidden"]), to_dev(w["weight"])
+    labels, mask = to_dev(w["labels"]), to_dev(w["row_mask"])
+    g = to_dev(w["g"])
+    out = cev.lce_forward(hid, head, labels, T, row_mask=mask, argmax=True)
+    dh, dw = cev.lce_backward(hid, head, labels, g, out["saved"], T, row_mask=mask,
+                              workspace=out["workspace"])
+    torch.cuda.synchronize()
+    assert dw is None
+    ldd = (V + 63) // 64 * 64
+    dl = out["workspace"][:R * ldd * 2].view(torch.bfloat16).view(R, ldd)
+    vr, _ = oracle.valid_rows(w["labels"], w["row_mask"], V)
+    valid = np.zeros(R, bool)
+    valid[vr] = True
+    logp, loss = to_host(out["logp"]), to_host(out["loss"])
+    arg = to_host(out["argmax"])
+    dhn = dh.cpu().numpy()
+    assert_nonpositive("logp", logp, valid)
+    assert np.all(loss[valid] >= 0) and np.all(loss[~valid] == 0)
+    assert np.all(arg[~valid] == -1) and np.all(dhn[~valid] == 0)
+    _row_sums_ok(dl[:, :V], RTOL["bf16"]["dlogits"])
+    assert bool((dl[:, V:] == 0).all())
+
+    rng = np.random.default_rng(11)
+    rows = _sample_rows(rng, valid, 16, 3)
+    rows = np.unique(np.concatenate([rows, w["peak_rows"][:6]]))
+    ref = oracle.linear_ce_rows(w["hidden"], w["weight"], w["labels"], T,
+                                row_mask=w["row_mask"], rows_list=rows, want_entropy=False)
+    z = oracle.linear_logits(w["hidden"], w["weight"], rows)
+    h64, w64 = oracle._widen(w["hidden"][rows]), oracle._widen(w["weight"])
+    dz = (H / 16 + 2) * 2.0 ** -24 * (np.abs(h64) @ np.abs(w64).T).max(axis=1)
+    rel = 2 * dz / T
+    vs = valid[rows]
+    err = np.abs(loss[rows] - ref["loss"][rows])
+    bound = 2e-6 * np.abs(ref["loss"][rows]) + rel * np.abs(ref["loss"][rows]) + 2 * dz / T
+    assert np.all(err[vs] <= bound[vs]), float(np.max(err[vs] / bound[vs]))
+    err = np.abs(logp[rows] - ref["logp"][rows])
+    assert np.all(err[vs] <= bound[vs]), float(np.max(err[vs] / bound[vs]))
+    for i, r in enumerate(rows):
+        if vs[i]:
+            assert z[i, arg[r]] >= z[i].max() - 2 * dz[i], r
+    grads = oracle.linear_ce_grads(w["hidden"], w["weight"], w["labels"], w["g"], T,
+                                   row_mask=w["row_mask"], rows_list=rows)
+    dref = oracle.ce_grad_rows(z, np.ascontiguousarray(w["labels"][rows]),
+                               np.asarray(w["g"], np.float64)[rows], T,
+                               row_mask=np.ascontiguousarray(w["row_mask"][rows]))
+    dsel = to_host(dl[torch.from_numpy(rows).to(DEV), :V])
+    # bf16 bar plus the probabilities' 2 dz / T from the product
+    bdl = (RTOL["bf16"]["dlogits"] + 1.01 * rel[:, None]) * np.abs(dref) + FLOOR
+    assert np.all(np.abs(dsel - dref) <= bdl), float(np.max(np.abs(dsel - dref) / bdl))
+    # dhidden: the same per-entry bar carried through the product, fp32
+    # accumulation over V / 16 MFMA steps (below 6e-4 relative), and the
+    # floor of every flushed entry
+    bh = (4.5e-3 + 1.01 * rel[:, None]) * (np.abs(dref) @ np.abs(w64)) \
+        + FLOOR * vs[:, None] * np.abs(w64).sum(0) + FLOOR
+    err = np.abs(dhn[rows] - grads["dhidden"])
+    assert np.all(err <= bh), float(np.max(err / bh))
+    say(f"  sampled {rows.size} rows; max logit error bound dz {dz.max():.2e}; "
+        f"worst dhidden error / bound {float(np.max(err / bh)):.3f}")
