@@ -136,6 +136,12 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[kTM][kTN])
 // last K step of a tile, epi(tile, acc) consumes the accumulators.  A: rows
 // [row0, row0 + 256) of XA; B: 256-row tiles [t_begin, t_end) of XB (staged
 // permuted, see perm_b); nk K steps of 64.
+//
+// All but the last K step of a tile run a branch-free body (loads of the next
+// step, MFMAs, LDS stores, barrier) that the compiler's MFMA/LDS interleaving
+// strategy (iglp_opt 0) schedules as one region: 15% faster than its default
+// schedule on MI355X.  The last step of a tile is peeled so that the
+// epilogue runs while the next tile's first loads are in flight.
 template <class Epi>
 __device__ __forceinline__ void gemm_tiles(GemmSmem &sm, const unsigned short *XA, int64_t lda,
                                            int64_t rowsA, int64_t row0, const unsigned short *XB,
@@ -154,36 +160,69 @@ __device__ __forceinline__ void gemm_tiles(GemmSmem &sm, const unsigned short *X
     store_tile(sm.a[0], ra, tid);
     store_tile(sm.b[0], rb, tid);
     __syncthreads();
-    // (tile, kt): the pair in the LDS buffer `buf`; (ntile, nkt): the next one
-    int64_t tile = t_begin;
-    int kt = 0, buf = 0;
-    for (;;) {
-        int nkt = kt + 1;
-        int64_t ntile = tile;
-        if (nkt == nk) {
-            nkt = 0;
-            ++ntile;
+    int buf = 0;
+    for (int64_t tile = t_begin; tile < t_end; ++tile) {
+        const int64_t b0 = tile * kBN;
+        for (int64_t kt = 1; kt < nk; ++kt) {
+            load_tile<false>(XA, lda, rowsA, row0, kt * kBK, ra, tid);
+            load_tile<true>(XB, ldb, rowsB, b0, kt * kBK, rb, tid);
+            mma_stage(sm.a[buf], sm.b[buf], acc, wm, wn, lane);
+            store_tile(sm.a[buf ^ 1], ra, tid);
+            store_tile(sm.b[buf ^ 1], rb, tid);
+            __builtin_amdgcn_iglp_opt(0);
+            __syncthreads();
+            buf ^= 1;
         }
-        const bool more = ntile < t_end;
+        const bool more = tile + 1 < t_end;
         if (more) {
-            load_tile<false>(XA, lda, rowsA, row0, (int64_t)nkt * kBK, ra, tid);
-            load_tile<true>(XB, ldb, rowsB, ntile * kBN, (int64_t)nkt * kBK, rb, tid);
+            load_tile<false>(XA, lda, rowsA, row0, 0, ra, tid);
+            load_tile<true>(XB, ldb, rowsB, b0 + kBN, 0, rb, tid);
         }
         mma_stage(sm.a[buf], sm.b[buf], acc, wm, wn, lane);
-        if (nkt == 0) {
-            epi(tile, acc);
-            zero_acc(acc);
+        epi(tile, acc);
+        zero_acc(acc);
+        if (more) {
+            store_tile(sm.a[buf ^ 1], ra, tid);
+            store_tile(sm.b[buf ^ 1], rb, tid);
         }
-        if (!more)
-            break;
-        store_tile(sm.a[buf ^ 1], ra, tid);
-        store_tile(sm.b[buf ^ 1], rb, tid);
         __syncthreads();
-        tile = ntile;
-        kt = nkt;
         buf ^= 1;
     }
+}
+
+// One output tile of a long contraction (the gradient products): the same
+// K step as gemm_tiles in one branch-free loop (the last step reloads its own
+// K range, unused), accumulators returned to the caller.  Measured on MI355X
+// for the dhidden shape: 12% faster than running it through gemm_tiles.
+__device__ __forceinline__ void gemm_one_tile(GemmSmem &sm, const unsigned short *XA,
+                                              int64_t lda, int64_t rowsA, int64_t row0,
+                                              const unsigned short *XB, int64_t ldb,
+                                              int64_t rowsB, int64_t col0, int64_t nk,
+                                              f32x16 (&acc)[kTM][kTN])
+{
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    zero_acc(acc);
+    if (nk <= 0)
+        return;
+    u32x4 ra[kChunks], rb[kChunks];
+    load_tile<false>(XA, lda, rowsA, row0, 0, ra, tid);
+    load_tile<true>(XB, ldb, rowsB, col0, 0, rb, tid);
+    store_tile(sm.a[0], ra, tid);
+    store_tile(sm.b[0], rb, tid);
     __syncthreads();
+    int buf = 0;
+    for (int64_t it = 0; it < nk; ++it) {
+        const int64_t nx = it + 1 < nk ? it + 1 : it;
+        load_tile<false>(XA, lda, rowsA, row0, nx * kBK, ra, tid);
+        load_tile<true>(XB, ldb, rowsB, col0, nx * kBK, rb, tid);
+        mma_stage(sm.a[buf], sm.b[buf], acc, wm, wn, lane);
+        store_tile(sm.a[buf ^ 1], ra, tid);
+        store_tile(sm.b[buf ^ 1], rb, tid);
+        __builtin_amdgcn_iglp_opt(0);
+        __syncthreads();
+        buf ^= 1;
+    }
 }
 
 // Local row (0..255) of accumulator element v of block mb for this lane.
@@ -236,6 +275,28 @@ __device__ __forceinline__ int row_min(int x)
     return row_reduce(x, [](int p, int q) { return min(p, q); });
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b on XCD
+// b % 8), each with its own L2.  The forward and dlogits grids are renumbered
+// so that the workgroups one XCD runs together form a contiguous run of
+// (row block, split) pairs: 256 workgroups of 32 row blocks x 8 splits give
+// each XCD 4 row blocks x 8 splits, whose hidden slices stay in its L2 while
+// the head streams through, instead of every row block on every XCD.
+__device__ __forceinline__ int64_t xcd_order(int64_t b, int64_t grid)
+{
+    return grid % 8 == 0 ? (b % 8) * (grid / 8) + b / 8 : b;
+}
+
+// The lane index as a value the compiler cannot see through.  Epilogues run
+// once per tile inside the tile loop; their per-row addresses only depend on
+// the lane and the row block, so the compiler would otherwise hoist all 32 of
+// them above the K loop and keep them live through it (64 VGPRs).
+__device__ __forceinline__ int opaque_lane()
+{
+    int l = (int)(threadIdx.x & 63);
+    asm volatile("" : "+v"(l));
+    return l;
+}
+
 // First output column of the four this lane holds in a wave's 128 columns.
 __device__ __forceinline__ int64_t lane_col(int64_t tile, int wn, int lane)
 {
@@ -261,7 +322,8 @@ __global__ __launch_bounds__(kLT) void k_lce_fwd(LceArgs a)
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 1, wn = w & 1;
     const int64_t S = a.splits;
-    const int64_t rb = blockIdx.x / S, sp = blockIdx.x % S;   // consecutive blocks: one row block
+    const int64_t vb = xcd_order(blockIdx.x, gridDim.x);
+    const int64_t rb = vb / S, sp = vb % S;
     const int64_t row0 = rb * kBM;
     const int64_t V = a.vocab;
     const int64_t ntiles = (V + kBN - 1) / kBN;
@@ -287,13 +349,14 @@ __global__ __launch_bounds__(kLT) void k_lce_fwd(LceArgs a)
     RowState st = RowState{-INFINITY, 0.0f, 0.0f, 0.0f, INT32_MAX};
 
     auto epi = [&](int64_t tile, f32x16 (&acc)[kTM][kTN]) {
-        const int64_t c0 = lane_col(tile, wn, lane);
+        const int el = opaque_lane();
+        const int64_t c0 = lane_col(tile, wn, el);
 #pragma unroll
         for (int mb = 0; mb < kTM; ++mb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int ri = mb * 16 + v;
-                const int rl = acc_row(wm, mb, v, lane);
+                const int rl = acc_row(wm, mb, v, el);
                 const int64_t d = (int64_t)s_lab[rl] - c0;   // the target among this lane's four?
                 const int tn = d >= 0 && d < kTN ? (int)d : -1;
                 float x[kTN], zt = 0.0f;
@@ -427,7 +490,8 @@ __global__ __launch_bounds__(kLT) void k_lce_dl(LceArgs a)
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 1, wn = w & 1;
     const int64_t S = a.splits;
-    const int64_t rb = blockIdx.x / S, sp = blockIdx.x % S;
+    const int64_t vb = xcd_order(blockIdx.x, gridDim.x);
+    const int64_t rb = vb / S, sp = vb % S;
     const int64_t row0 = rb * kBM;
     const int64_t V = a.vocab, ldd = a.ldd;
     const int64_t ntiles = (V + kBN - 1) / kBN;
@@ -465,14 +529,15 @@ __global__ __launch_bounds__(kLT) void k_lce_dl(LceArgs a)
     // Each lane writes its four adjacent columns of a row as one 8-byte store
     // (ldd is a multiple of 64, so a group of four is wholly inside or past it).
     auto epi = [&](int64_t tile, f32x16 (&acc)[kTM][kTN]) {
-        const int64_t c0 = lane_col(tile, wn, lane);
+        const int el = opaque_lane();
+        const int64_t c0 = lane_col(tile, wn, el);
         if (c0 >= ldd)
             return;
 #pragma unroll
         for (int mb = 0; mb < kTM; ++mb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int rl = acc_row(wm, mb, v, lane);
+                const int rl = acc_row(wm, mb, v, el);
                 const int64_t r = row0 + rl;
                 if (r >= a.rows)
                     continue;
@@ -520,30 +585,29 @@ __global__ __launch_bounds__(kLT) void k_lce_gemm(const unsigned short *XA, int6
     const int64_t row0 = (t % mt) * kBM, nt = t / mt;
     const int64_t k0 = nk * sp / splits, k1 = nk * (sp + 1) / splits;
     float *Cs = C + sp * cstride;
-    auto epi = [&](int64_t tile, f32x16 (&acc)[kTM][kTN]) {
-        const int64_t c0 = lane_col(tile, wn, lane);
-        if (c0 >= N)
-            return;
+    f32x16 acc[kTM][kTN];
+    gemm_one_tile(sm, XA + k0 * kBK, lda, M, row0, XB + k0 * kBK, ldb, N, nt * kBN, k1 - k0,
+                  acc);
+    const int64_t c0 = lane_col(nt, wn, lane);
+    if (c0 >= N)
+        return;
 #pragma unroll
-        for (int mb = 0; mb < kTM; ++mb)
+    for (int mb = 0; mb < kTM; ++mb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t r = row0 + acc_row(wm, mb, v, lane);
-                if (r >= M)
-                    continue;
-                float *dst = Cs + r * ldc + c0;
-                if (vec4) {
-                    *reinterpret_cast<float4 *>(dst) =
-                        make_float4(acc[mb][0][v], acc[mb][1][v], acc[mb][2][v], acc[mb][3][v]);
-                } else {
+        for (int v = 0; v < 16; ++v) {
+            const int64_t r = row0 + acc_row(wm, mb, v, lane);
+            if (r >= M)
+                continue;
+            float *dst = Cs + r * ldc + c0;
+            if (vec4) {
+                *reinterpret_cast<float4 *>(dst) =
+                    make_float4(acc[mb][0][v], acc[mb][1][v], acc[mb][2][v], acc[mb][3][v]);
+            } else {
 #pragma unroll
-                    for (int nb = 0; nb < kTN; ++nb)
-                        dst[nb] = acc[mb][nb][v];
-                }
+                for (int nb = 0; nb < kTN; ++nb)
+                    dst[nb] = acc[mb][nb][v];
             }
-    };
-    gemm_tiles(sm, XA + k0 * kBK, lda, M, row0, XB + k0 * kBK, ldb, N, k1 - k0, nt, nt + 1,
-               epi);
+        }
 }
 
 // out[r][c] = sum over s in order of P[s][r][c] (P rows of N floats, N a
@@ -628,10 +692,7 @@ int64_t gemm_splits(int64_t tiles, int64_t nk, size_t max_by_room)
 
 int64_t lce_splits(int64_t rows, int64_t vocab)
 {
-    // A multiple of 8 vocab splits, enough for 256 workgroups (one per CU):
-    // consecutive workgroups share a row block and the round-robin dispatch
-    // keeps split s on XCD s % 8, so each XCD's L2 streams its part of the
-    // head for every row block.
+    // A multiple of 8 vocab splits, enough for 256 workgroups (one per CU).
     const int64_t ntiles = (vocab + kBN - 1) / kBN;
     const int64_t nrb = (rows + kBM - 1) / kBM;
     int64_t s = 8;
