@@ -216,7 +216,20 @@ def bench_linear(args, torch, cev, workloads, dev):
     f_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
     b_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
     flop = 2.0 * R * H * Vl
-    log(f"[bench] linear CE: forward {f_ms:.2f} ms, backward {b_ms:.2f} ms")
+    # the forward alone at 2048 rows, the other row count of the same head
+    r2 = 2048
+    o2 = cev.lce_forward(hid[:r2], head, lab[:r2], 1.0, row_mask=msk[:r2], argmax=True)
+    e2 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    cev.lce_forward(hid[:r2], head, lab[:r2], 1.0, row_mask=msk[:r2], argmax=True, out=o2)
+    e2[0].record()
+    for _ in range(steps):
+        cev.lce_forward(hid[:r2], head, lab[:r2], 1.0, row_mask=msk[:r2], argmax=True, out=o2)
+    e2[1].record()
+    torch.cuda.synchronize()
+    f2_ms = e2[0].elapsed_time(e2[1]) / steps
+    del o2
+    log(f"[bench] linear CE: forward {f_ms:.2f} ms, backward {b_ms:.2f} ms; "
+        f"forward at {r2} rows {f2_ms:.2f} ms")
     res = {"entry": "lce_forward + lce_backward (frozen head: dhidden only), logits never "
                     "stored; 2560 x 151936 head as in the unsloth-zoo #2080 Speed section",
            "shape": {"rows": R, "hidden": H, "vocab": Vl}, "steps": steps,
@@ -225,6 +238,8 @@ def bench_linear(args, torch, cev, workloads, dev):
            "forward_TFLOPs": flop / (f_ms / 1e3) / 1e12,
            "backward_TFLOPs": 2 * flop / (b_ms / 1e3) / 1e12,
            "step_TFLOPs": 3 * flop / ((f_ms + b_ms) / 1e3) / 1e12,
+           "forward_2048_rows_ms": f2_ms,
+           "forward_2048_rows_TFLOPs": flop * r2 / R / (f2_ms / 1e3) / 1e12,
            "roofline": {"bound": "mfma", "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "achieved": 3 * flop / ((f_ms + b_ms) / 1e3) / 1e12,
                         "frac": 3 * flop / ((f_ms + b_ms) / 1e3) / 1e12 / PEAK_BF16_TFLOPS}}
