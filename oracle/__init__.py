@@ -22,6 +22,10 @@ Parity status of each function (what pins it is listed in the tests):
   of the cross-entropy) -- pinned by the identity head, exact rescaling, a
   50-digit brute force and central differences of the loss in both the
   hidden state and the head.
+  jsd.jsd_rows, jsd.jsd_grad_rows (generalized JSD / KL between a student and
+  a teacher row, numpy fp64 in oracle/jsd.py) -- pinned by identical rows,
+  scipy's relative entropy and Jensen-Shannon distance, the disjoint-support
+  maximum, 250-digit brute force with central differences, and invariants.
 """
 from __future__ import annotations
 

@@ -540,3 +540,212 @@ def check_linear_central_difference(lib=None, orc=None):
 
 LINEAR_CHECKS = [check_linear_identity, check_linear_scale, check_linear_rows_list,
                  check_linear_bruteforce, check_linear_central_difference]
+
+
+# ------------------------------------------------------------ generalized JSD
+# The references below come from the definitions of the generalized
+# Jensen-Shannon divergence between P_t = softmax(z_teacher / T) and
+# P_s = softmax(z_student / T) (beta = 0: KL(P_t || P_s); beta = 1:
+# KL(P_s || P_t); in between beta KL(P_t || M) + (1 - beta) KL(P_s || M),
+# M = beta P_t + (1 - beta) P_s), evaluated by mpmath at 120 digits or by
+# scipy's own relative-entropy and Jensen-Shannon routines.
+
+def _jsd_orc(orc):
+    if orc is None:
+        import oracle.jsd as j
+        return j
+    return orc
+
+
+def _mp_jsd(zs, zt, T, beta):
+    """Loss by brute force from the definitions, unshifted, at 120 digits."""
+    def lsm(z):
+        x = [mp.mpf(float(v)) / mp.mpf(T) for v in z]
+        lse = mp.log(mp.fsum(mp.e ** xi for xi in x))
+        return [xi - lse for xi in x]
+    ls, lt = lsm(zs), lsm(zt)
+    ps = [mp.e ** v for v in ls]
+    pt = [mp.e ** v for v in lt]
+    b = mp.mpf(beta)
+    if beta == 0.0:
+        return mp.fsum(p * (a - c) for p, a, c in zip(pt, lt, ls))
+    if beta == 1.0:
+        return mp.fsum(p * (a - c) for p, a, c in zip(ps, ls, lt))
+    m = [b * q + (1 - b) * p for q, p in zip(pt, ps)]
+    lm = [mp.log(v) for v in m]
+    return (b * mp.fsum(q * (a - c) for q, a, c in zip(pt, lt, lm)) +
+            (1 - b) * mp.fsum(p * (a - c) for p, a, c in zip(ps, ls, lm)))
+
+
+def _jsd_cases():
+    rng = np.random.default_rng(77)
+    cases = []
+    for V in (2, 5, 9):
+        zs = (2.0 * rng.standard_normal(V)).astype(np.float32)
+        zt = (2.0 * rng.standard_normal(V)).astype(np.float32)
+        cases.append((zs, zt))
+    # peaked rows past the fp64 collapse point (36.7): same and different argmax
+    base = rng.standard_normal(6).astype(np.float32)
+    for ms, mt, at in ((50.0, 45.0, 2), (120.0, 80.0, 2), (60.0, 70.0, 4)):
+        zs = base.copy()
+        zs[2] = np.float32(base.max() + ms)
+        zt = (base + np.float32(0.5) * rng.standard_normal(6).astype(np.float32)).astype(np.float32)
+        zt[at] = np.float32(zt.max() + mt)
+        cases.append((zs, zt))
+    return cases
+
+
+def check_jsd_identical(orc=None):
+    """Identical student and teacher rows: every divergence and gradient is 0."""
+    j = _jsd_orc(orc)
+    z = (3.0 * np.random.default_rng(71).standard_normal((4, 50))).astype(np.float32)
+    z[2, 7] += 60.0
+    for beta in (0.0, 0.25, 0.5, 1.0):
+        loss = j.jsd_rows(z, z, 0.8, beta)
+        assert np.all(np.abs(loss) <= 1e-15), (beta, loss)
+        d = j.jsd_grad_rows(z, z, np.ones(4), 0.8, beta)
+        assert np.all(np.abs(d) <= 1e-15), (beta, np.abs(d).max())
+
+
+def check_jsd_scipy(orc=None):
+    """beta = 0 and 1 against scipy.special.rel_entr on scipy.special.softmax;
+    beta = 0.5 against scipy.spatial.distance.jensenshannon (natural log)
+    squared."""
+    from scipy.spatial.distance import jensenshannon
+    from scipy.special import rel_entr, softmax
+    j = _jsd_orc(orc)
+    rng = np.random.default_rng(72)
+    for T in (1.0, 0.7):
+        zs = (2.0 * rng.standard_normal((3, 300))).astype(np.float32)
+        zt = (2.0 * rng.standard_normal((3, 300))).astype(np.float32)
+        ps = softmax(zs.astype(np.float64) / T, axis=1)
+        pt = softmax(zt.astype(np.float64) / T, axis=1)
+        fwd = j.jsd_rows(zs, zt, T, 0.0)
+        rev = j.jsd_rows(zs, zt, T, 1.0)
+        mid = j.jsd_rows(zs, zt, T, 0.5)
+        for r in range(3):
+            assert rel(fwd[r], rel_entr(pt[r], ps[r]).sum()) < 1e-12, ("forward KL", r)
+            assert rel(rev[r], rel_entr(ps[r], pt[r]).sum()) < 1e-12, ("reverse KL", r)
+            assert rel(mid[r], jensenshannon(pt[r], ps[r]) ** 2) < 1e-10, ("JSD", r)
+
+
+def check_jsd_disjoint_limit(orc=None):
+    """Rows peaked on different columns by 300: the two distributions have
+    (numerically) disjoint supports, where the generalized JSD reaches its
+    maximum, the binary entropy -beta log beta - (1 - beta) log(1 - beta)."""
+    j = _jsd_orc(orc)
+    zs = np.zeros((1, 40), np.float32)
+    zt = np.zeros((1, 40), np.float32)
+    zs[0, 3] = 300.0
+    zt[0, 30] = 300.0
+    for beta in (0.1, 0.5, 0.8):
+        h = -beta * math.log(beta) - (1 - beta) * math.log(1 - beta)
+        assert rel(j.jsd_rows(zs, zt, 1.0, beta)[0], h) < 1e-12, beta
+
+
+def check_jsd_bruteforce(orc=None):
+    """Loss against the 120-digit definition and every gradient entry against
+    mpmath central differences of that loss, on random and peaked rows
+    (margins 45 to 120, same and different argmax), beta in {0, 0.3, 0.5, 1}."""
+    j = _jsd_orc(orc)
+    for zs, zt in _jsd_cases():
+        for beta in (0.0, 0.3, 0.5, 1.0):
+            for T in (1.0, 0.7):
+              # a row peaked by 120 / 0.7 has entries near e^-171 and a loss
+              # near e^-120: a central difference of step 1e-80 needs 250 digits
+              with mp.workdps(250):
+                ref = _mp_jsd(zs, zt, T, beta)
+                got = j.jsd_rows(zs[None], zt[None], T, beta)[0]
+                assert abs(got - float(ref)) <= 1e-12 * abs(float(ref)) + 1e-300, \
+                    ("loss", beta, T, got, float(ref))
+                d = j.jsd_grad_rows(zs[None], zt[None], np.array([0.75]), T, beta)[0]
+                mag = _mp_grad_terms(zs, zt, T, beta)
+                # the student's argmax entry is minus the sum of the others, so
+                # it errs like them, not like its own near-1 terms
+                a = int(np.argmax(zs))
+                mag[a] = sum(m for i, m in enumerate(mag) if i != a)
+                h = mp.mpf("1e-80")
+                for k in range(zs.size):
+                    def shifted(s):
+                        z = [mp.mpf(float(v)) for v in zs]
+                        z[k] += s
+                        return z
+                    # the definition with z_k moved by +-h (unrounded)
+                    def f(z):
+                        return _mp_jsd_exact(z, zt, T, beta)
+                    fd = (f(shifted(h)) - f(shifted(-h))) / (2 * h) * mp.mpf("0.75")
+                    # an entry that is the difference of two nearly equal terms
+                    # (rows peaked at different columns) is only as accurate
+                    # as fp64 makes those terms: 1e-15 of their size
+                    bound = 1e-10 * abs(float(fd)) + 1e-15 * 0.75 * mag[k] + 1e-300
+                    assert abs(d[k] - float(fd)) <= bound, ("grad", beta, T, k, d[k], float(fd))
+
+
+def _mp_grad_terms(zs, zt, T, beta):
+    """Per column, the size of the two terms whose difference the gradient
+    entry is: (ps + pt) / T at beta = 0; ps (|ls - lt| + loss) / T at beta = 1;
+    (1 - beta) ps (|ls - lm| + |K|) / T in between (120+ digits, as floats)."""
+    def lsm(z):
+        x = [mp.mpf(float(v)) / mp.mpf(T) for v in z]
+        lse = mp.log(mp.fsum(mp.e ** xi for xi in x))
+        return [xi - lse for xi in x]
+    ls, lt = lsm(zs), lsm(zt)
+    ps = [mp.e ** v for v in ls]
+    pt = [mp.e ** v for v in lt]
+    b = mp.mpf(beta)
+    if beta == 0.0:
+        return [float((p + q) / T) for p, q in zip(ps, pt)]
+    if beta == 1.0:
+        L = mp.fsum(p * (a - c) for p, a, c in zip(ps, ls, lt))
+        return [float(p * (abs(a - c) + abs(L)) / T) for p, a, c in zip(ps, ls, lt)]
+    r = [a - mp.log(b * q + (1 - b) * p) for a, p, q in zip(ls, ps, pt)]
+    K = mp.fsum(p * v for p, v in zip(ps, r))
+    return [float((1 - b) * p * (abs(v) + abs(K)) / T) for p, v in zip(ps, r)]
+
+
+def _mp_jsd_exact(zs_mp, zt, T, beta):
+    """_mp_jsd with the student row already as mpmath numbers."""
+    x = [v / mp.mpf(T) for v in zs_mp]
+    lse = mp.log(mp.fsum(mp.e ** xi for xi in x))
+    ls = [xi - lse for xi in x]
+    y = [mp.mpf(float(v)) / mp.mpf(T) for v in zt]
+    lse_t = mp.log(mp.fsum(mp.e ** yi for yi in y))
+    lt = [yi - lse_t for yi in y]
+    ps = [mp.e ** v for v in ls]
+    pt = [mp.e ** v for v in lt]
+    b = mp.mpf(beta)
+    if beta == 0.0:
+        return mp.fsum(p * (a - c) for p, a, c in zip(pt, lt, ls))
+    if beta == 1.0:
+        return mp.fsum(p * (a - c) for p, a, c in zip(ps, ls, lt))
+    lm = [mp.log(b * q + (1 - b) * p) for q, p in zip(pt, ps)]
+    return (b * mp.fsum(q * (a - c) for q, a, c in zip(pt, lt, lm)) +
+            (1 - b) * mp.fsum(p * (a - c) for p, a, c in zip(ps, ls, lm)))
+
+
+def check_jsd_invariants(orc=None):
+    """Adding a constant to either row changes nothing (up to rounding);
+    every gradient row sums to zero; masked and ignored rows are zero."""
+    j = _jsd_orc(orc)
+    rng = np.random.default_rng(73)
+    zs = (2.0 * rng.standard_normal((4, 200))).astype(np.float64)
+    zt = (2.0 * rng.standard_normal((4, 200))).astype(np.float64)
+    g = rng.standard_normal(4)
+    for beta in (0.0, 0.4, 1.0):
+        a = j.jsd_rows(zs, zt, 1.3, beta)
+        b = j.jsd_rows(zs + 5.0, zt - 3.0, 1.3, beta)
+        assert np.all(np.abs(a - b) <= 1e-12 * np.abs(a)), beta
+        da = j.jsd_grad_rows(zs, zt, g, 1.3, beta)
+        db = j.jsd_grad_rows(zs + 5.0, zt - 3.0, g, 1.3, beta)
+        assert np.all(np.abs(da - db) <= 1e-12 * np.abs(da).max()), beta
+        assert np.all(np.abs(da.sum(1)) <= 1e-15 * np.abs(da).sum(1)), beta
+        labels = np.array([1, -100, 3, 4])
+        mask = np.array([1, 1, 0, 1], np.uint8)
+        lm = j.jsd_rows(zs, zt, 1.3, beta, labels=labels, row_mask=mask)
+        dm = j.jsd_grad_rows(zs, zt, g, 1.3, beta, labels=labels, row_mask=mask)
+        assert lm[1] == 0 and lm[2] == 0 and lm[0] == a[0] and lm[3] == a[3]
+        assert np.all(dm[[1, 2]] == 0) and np.array_equal(dm[[0, 3]], da[[0, 3]])
+
+
+JSD_CHECKS = [check_jsd_identical, check_jsd_scipy, check_jsd_disjoint_limit,
+              check_jsd_bruteforce, check_jsd_invariants]

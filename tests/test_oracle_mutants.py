@@ -129,3 +129,54 @@ def test_unmutated_python_oracle_passes_linear_pins(tmp_path):
     mod = _load_mutant_package(tmp_path, "F64 = 2\n", "F64 = 2\n\n")
     for check in pinlib.LINEAR_CHECKS:
         check(orc=mod)
+
+
+# Mistakes planted in the generalized-JSD oracle (oracle/jsd.py, a plain
+# numpy module): each must be caught by one of the JSD pins.
+JSD_MUTANTS = [
+    ("mixture_weights_swapped", "a = -np.log1p(beta * np.expm1(dn))",
+     "a = -np.log1p((1.0 - beta) * np.expm1(dn))"),
+    ("naive_log_softmax_at_argmax", "ls[a] = -np.log1p(S)",
+     "ls[a] = x[a] - np.log(np.sum(np.exp(x)))"),
+    ("reverse_kl_grad_without_loss", "d = ps * ((ls - lt) - loss) / T", "d = ps * (ls - lt) / T"),
+    ("argmax_rule_dropped", "    d[a] = 0.0\n    d[a] = -np.sum(d)\n", "    pass\n"),
+    ("teacher_not_tempered", "lt, a_t, _ = log_softmax_safe(_widen(zt) / T)",
+     "lt, a_t, _ = log_softmax_safe(_widen(zt))"),
+    ("forward_kl_reversed", "return float(np.sum(pt * (lt - ls))), 0.0, ls, lt, None",
+     "return float(np.sum(pt * (ls - lt))), 0.0, ls, lt, None"),
+    ("mixed_grad_without_K", "d = (1.0 - beta) * ps * (r - K) / T", "d = (1.0 - beta) * ps * r / T"),
+]
+
+
+def _load_jsd_mutant(tmp_path, old, new):
+    import importlib.util
+    text = open(os.path.join(PKG, "jsd.py")).read()
+    assert text.count(old) == 1, "mutation site not unique or missing"
+    f = tmp_path / "jsd_mut.py"
+    f.write_text(text.replace(old, new))
+    spec = importlib.util.spec_from_file_location(f"jsd_mut_{abs(hash((old, new)))}", f)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new", JSD_MUTANTS, ids=[m[0] for m in JSD_MUTANTS])
+def test_jsd_pins_catch_mutant(tmp_path, name, old, new):
+    import warnings
+    mod = _load_jsd_mutant(tmp_path, old, new)
+    caught = []
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")
+        for check in pinlib.JSD_CHECKS:
+            try:
+                check(orc=mod)
+            except (AssertionError, ValueError, IndexError, FloatingPointError):
+                caught.append(check.__name__)
+                break
+    assert caught, f"no pin caught mutant {name}"
+
+
+def test_unmutated_jsd_oracle_passes_pins(tmp_path):
+    mod = _load_jsd_mutant(tmp_path, "import numpy as np\n", "import numpy as np\n\n")
+    for check in pinlib.JSD_CHECKS:
+        check(orc=mod)

@@ -20,6 +20,11 @@ def test_pin(check):
     check()
 
 
+@pytest.mark.parametrize("check", pinlib.JSD_CHECKS, ids=lambda c: c.__name__)
+def test_jsd_pin(check):
+    check()
+
+
 def _golden(name):
     with open(os.path.join(GOLDEN, name)) as f:
         return json.load(f)
