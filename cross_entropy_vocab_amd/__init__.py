@@ -19,7 +19,7 @@ from . import _lib
 __all__ = ["sls_forward", "sls_topk_forward", "sls_topk_backward", "ce_forward",
            "ce_backward", "ce_fused", "ce_vocab_shard_forward", "ce_vocab_merge",
            "ce_vocab_shard_backward", "lce_forward", "lce_backward", "lce_workspace_size",
-           "workspace_size",
+           "jsd_forward", "jsd_backward", "workspace_size", "JSD_SAVED_BYTES",
            "status_string", "version", "CEV_F32", "CEV_BF16", "STATUS_BAD_LABEL",
            "STATUS_BAD_INDEX", "STATUS_BAD_PARTS", "SAVED_BYTES", "PARTIAL_BYTES", "CevError"]
 
@@ -29,6 +29,7 @@ STATUS_BAD_LABEL = 1
 STATUS_BAD_INDEX = 2
 STATUS_BAD_PARTS = 4
 SAVED_BYTES = 16
+JSD_SAVED_BYTES = 32
 PARTIAL_BYTES = 48
 PART_ENTROPY = 1
 PART_VALUE_SUM = 2
@@ -388,6 +389,62 @@ def ce_vocab_shard_backward(logits, labels, g, saved, col_offset, vocab, tempera
                                             _stream(dev))
     _check("ce_vocab_shard_backward", rc)
     return dlogits
+
+
+def _jsd_pair(student, teacher):
+    rows, vocab, sstride = _check_logits(student)
+    if teacher.dtype != student.dtype or tuple(teacher.shape) != (rows, vocab):
+        raise ValueError("teacher must match student in dtype and shape")
+    if teacher.device != student.device:
+        raise ValueError("teacher must be on the student's device")
+    _, _, tstride = _check_logits(teacher)
+    return rows, vocab, sstride, tstride
+
+
+def jsd_forward(student, teacher, temperature=1.0, beta=0.5, labels=None, row_mask=None,
+                ignore_index=-100, status=None, out=None):
+    """Generalized JSD per row between softmax(student / T) and
+    softmax(teacher / T) (beta = 0: KL(teacher || student), beta = 1:
+    KL(student || teacher)).  Returns a dict: loss [rows] fp32 and saved
+    [rows, 32] uint8 (for jsd_backward)."""
+    rows, vocab, ss, ts = _jsd_pair(student, teacher)
+    dev = student.device
+    _dev(labels, "labels", torch.int64, (rows,), dev)
+    m = _mask(row_mask, rows, dev)
+    _dev(status, "status", torch.int32, (1,), dev)
+    o = dict(out) if out else {}
+    if o.get("loss") is None:
+        o["loss"] = torch.empty(rows, dtype=torch.float32, device=dev)
+    if o.get("saved") is None:
+        o["saved"] = torch.empty((rows, JSD_SAVED_BYTES), dtype=torch.uint8, device=dev)
+    _dev(o["loss"], "loss", torch.float32, (rows,), dev)
+    _dev(o["saved"], "saved", torch.uint8, (rows, JSD_SAVED_BYTES), dev)
+    rc = _lib.get().jsd_forward(_ptr(student), _ptr(teacher), rows, vocab, ss, ts,
+                                _dtype_code(student), _ptr(labels), int(ignore_index),
+                                float(temperature), float(beta), _ptr(m), _ptr(o["loss"]),
+                                _ptr(o["saved"]), _ptr(status), _stream(dev))
+    _check("jsd_forward", rc)
+    return o
+
+
+def jsd_backward(student, teacher, g, saved, temperature=1.0, beta=0.5, labels=None,
+                 row_mask=None, ignore_index=-100, dstudent=None, status=None):
+    """g[r] times the gradient of row r's jsd_forward loss with respect to the
+    student logits (dtype and shape of student)."""
+    rows, vocab, ss, ts = _jsd_pair(student, teacher)
+    dev = student.device
+    _dev(labels, "labels", torch.int64, (rows,), dev)
+    _dev(g, "g", torch.float32, (rows,), dev)
+    _dev(saved, "saved", torch.uint8, (rows, JSD_SAVED_BYTES), dev)
+    m = _mask(row_mask, rows, dev)
+    _dev(status, "status", torch.int32, (1,), dev)
+    dstudent, dstride = _dlogits(dstudent, student, rows, vocab, dev)
+    rc = _lib.get().jsd_backward(_ptr(student), _ptr(teacher), rows, vocab, ss, ts,
+                                 _dtype_code(student), _ptr(labels), int(ignore_index),
+                                 float(temperature), float(beta), _ptr(m), _ptr(g), _ptr(saved),
+                                 _ptr(dstudent), dstride, _ptr(status), _stream(dev))
+    _check("jsd_backward", rc)
+    return dstudent
 
 
 def lce_workspace_size(rows: int, hidden_dim: int, vocab: int) -> int:

@@ -39,6 +39,8 @@ SIGNATURES = {
     "lce_backward": (I32, [P, I64, I64, I64, P, I64, I64, P, I64, D, D, P, P, P, P, I64, P, I64,
                            P, SZ, P, P]),
     "lce_workspace_size": (SZ, [I64, I64, I64]),
+    "jsd_forward": (I32, [P, P, I64, I64, I64, I64, I32, P, I64, D, D, P, P, P, P, P]),
+    "jsd_backward": (I32, [P, P, I64, I64, I64, I64, I32, P, I64, D, D, P, P, P, P, I64, P, P]),
     "cev_workspace_size": (SZ, [I64, I64, I32]),
     "cev_status_string": (ctypes.c_char_p, [I32]),
     "cev_version": (I32, []),

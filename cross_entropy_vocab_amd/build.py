@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcevocab.so")
-SOURCES = ["sweep.hip", "backward.hip", "compact.hip", "fused.hip", "shard.hip", "lce.hip", "api.cpp"]
+SOURCES = ["sweep.hip", "backward.hip", "compact.hip", "fused.hip", "shard.hip", "lce.hip", "jsd.hip",
+           "api.cpp"]
 ARCH = "gfx950"
 
 

@@ -729,6 +729,116 @@ int lce_backward(const void *hidden, int64_t rows, int64_t hidden_dim, int64_t h
                                                   dweight, dweight_stride, to_hip(stream)));
 }
 
+// Checks shared by the two JSD entry points.
+static int check_jsd(const void *student, const void *teacher, int64_t rows, int64_t vocab,
+                     int64_t s_stride, int64_t t_stride, int dtype, double temperature,
+                     double beta, bool *done)
+{
+    int rc = check_common(student, rows, vocab, s_stride, dtype, temperature, done);
+    if (rc != CEV_OK)
+        return rc;
+    if (!(std::isfinite(beta) && beta >= 0.0 && beta <= 1.0))
+        return CEV_EBETA;
+    if (t_stride < vocab)
+        return CEV_ESTRIDE;
+    if (*done)
+        return CEV_OK;
+    if (t_stride > INT64_MAX / 4 / rows)
+        return CEV_ESHAPE;
+    if (!teacher)
+        return CEV_ENULL;
+    if (!aligned(teacher, (uintptr_t)elem_size(dtype)))
+        return CEV_EALIGN;
+    return CEV_OK;
+}
+
+// Every row of the matrix starts 16 bytes aligned.
+static bool rows16(const void *p, int64_t stride, int es)
+{
+    return aligned(p, 16) && (stride * es) % 16 == 0;
+}
+
+static cev::JsdArgs jsd_args(const void *student, const void *teacher, int64_t rows,
+                             int64_t vocab, int64_t s_stride, int64_t t_stride,
+                             const int64_t *labels, int64_t ignore_index, double temperature,
+                             double beta, const uint8_t *row_mask, int32_t *status)
+{
+    cev::JsdArgs a{};
+    a.student = student;
+    a.teacher = teacher;
+    a.rows = rows;
+    a.vocab = vocab;
+    a.s_stride = s_stride;
+    a.t_stride = t_stride;
+    a.labels = labels;
+    a.ignore_index = ignore_index;
+    a.row_mask = row_mask;
+    a.beta = beta;
+    a.c = (float)(1.4426950408889634074 / temperature);
+    a.inv_t = (float)(1.0 / temperature);
+    a.status = status;
+    return a;
+}
+
+int jsd_forward(const void *student, const void *teacher, int64_t rows, int64_t vocab,
+                int64_t student_stride, int64_t teacher_stride, int dtype,
+                const int64_t *labels, int64_t ignore_index, double temperature, double beta,
+                const uint8_t *row_mask, float *loss, void *saved, int32_t *status,
+                cev_stream_t stream)
+{
+    bool done;
+    int rc = check_jsd(student, teacher, rows, vocab, student_stride, teacher_stride, dtype,
+                       temperature, beta, &done);
+    if (rc != CEV_OK || done)
+        return rc;
+    if (!loss || !saved)
+        return CEV_ENULL;
+    if (!aligned(labels, 8) || !aligned(loss, 4) || !aligned(saved, 16) || !aligned(status, 4))
+        return CEV_EALIGN;
+    cev::JsdArgs a = jsd_args(student, teacher, rows, vocab, student_stride, teacher_stride,
+                              labels, ignore_index, temperature, beta, row_mask, status);
+    const int es = elem_size(dtype);
+    a.vec = rows16(student, student_stride, es) && rows16(teacher, teacher_stride, es);
+    a.loss = loss;
+    a.saved = static_cast<cev_jsd_saved *>(saved);
+    return launch_status(cev::launch_jsd_forward(dtype, a, to_hip(stream)));
+}
+
+int jsd_backward(const void *student, const void *teacher, int64_t rows, int64_t vocab,
+                 int64_t student_stride, int64_t teacher_stride, int dtype,
+                 const int64_t *labels, int64_t ignore_index, double temperature, double beta,
+                 const uint8_t *row_mask, const float *g, const void *saved, void *dstudent,
+                 int64_t dstudent_stride, int32_t *status, cev_stream_t stream)
+{
+    bool done;
+    int rc = check_jsd(student, teacher, rows, vocab, student_stride, teacher_stride, dtype,
+                       temperature, beta, &done);
+    if (rc != CEV_OK)
+        return rc;
+    if (dstudent_stride < vocab)
+        return CEV_ESTRIDE;
+    if (done)
+        return CEV_OK;
+    if (!g || !saved || !dstudent)
+        return CEV_ENULL;
+    const int es = elem_size(dtype);
+    if (!aligned(labels, 8) || !aligned(g, 4) || !aligned(saved, 16) || !aligned(status, 4) ||
+        !aligned(dstudent, (uintptr_t)es))
+        return CEV_EALIGN;
+    if (overlaps(student, student_stride, dstudent, dstudent_stride, rows, vocab, es) ||
+        overlaps(teacher, teacher_stride, dstudent, dstudent_stride, rows, vocab, es))
+        return CEV_EALIAS;
+    cev::JsdArgs a = jsd_args(student, teacher, rows, vocab, student_stride, teacher_stride,
+                              labels, ignore_index, temperature, beta, row_mask, status);
+    a.vec = rows16(student, student_stride, es) && rows16(teacher, teacher_stride, es) &&
+            rows16(dstudent, dstudent_stride, es);
+    a.g = g;
+    a.saved_in = static_cast<const cev_jsd_saved *>(saved);
+    a.dstudent = dstudent;
+    a.d_stride = dstudent_stride;
+    return launch_status(cev::launch_jsd_backward(dtype, a, to_hip(stream)));
+}
+
 const char *cev_status_string(int code)
 {
     switch (code) {
@@ -743,10 +853,11 @@ const char *cev_status_string(int code)
     case CEV_EALIAS: return "dlogits overlaps logits";
     case CEV_ELAUNCH: return "kernel launch failed";
     case CEV_ESMOOTH: return "label_smoothing must be finite and in [0, 1]";
+    case CEV_EBETA: return "beta must be finite and in [0, 1]";
     default: return "unknown error code";
     }
 }
 
-int cev_version(void) { return 200; }
+int cev_version(void) { return 210; }
 
 } // extern "C"

@@ -209,6 +209,34 @@ hipError_t launch_lce_backward(const LceArgs &a, void *workspace, float *dhidden
                                int64_t dhidden_stride, float *dweight, int64_t dweight_stride,
                                hipStream_t stream);
 
+// Generalized JSD / KL between a student and a teacher row (one workgroup
+// per row).
+struct JsdArgs {
+    const void *student;
+    const void *teacher;
+    int64_t rows;
+    int64_t vocab;
+    int64_t s_stride;          // elements
+    int64_t t_stride;
+    const int64_t *labels;     // nullable: label == ignore_index masks the row
+    int64_t ignore_index;
+    const uint8_t *row_mask;
+    double beta;               // in [0, 1]
+    float c;                   // log2(e) / T
+    float inv_t;               // 1 / T
+    float *loss;               // forward
+    cev_jsd_saved *saved;      // forward
+    const cev_jsd_saved *saved_in;   // backward
+    const float *g;            // backward
+    void *dstudent;            // backward
+    int64_t d_stride;
+    int vec;                   // every row of every operand 16-byte aligned: vector path
+    int32_t *status;
+};
+
+hipError_t launch_jsd_forward(int dtype, const JsdArgs &a, hipStream_t stream);
+hipError_t launch_jsd_backward(int dtype, const JsdArgs &a, hipStream_t stream);
+
 // Forward + backward in one call, one workgroup per row (rows 16-byte aligned).
 struct FusedArgs {
     const void *logits;

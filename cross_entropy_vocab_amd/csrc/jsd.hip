@@ -1,0 +1,430 @@
+// jsd.hip -- collapse-safe generalized Jensen-Shannon divergence between a
+// student and a teacher logit row, with the forward and reverse KL at its two
+// ends (the generalized JSD of the unsloth-zoo #2079 Summary quoted on the
+// Liger-Kernel PR #1555 page: logits divided by T, log-softmax of both rows,
+// beta = 0 forward KL, beta = 1 reverse KL, the mixture in between), and its
+// gradient with respect to the student logits, the entry at the student's
+// argmax taken as minus the sum of the others (Liger-Kernel PR #1555,
+// Summary, "fused KL / JSD" bullet).
+//
+// Per valid row, with x = z_student / T, y = z_teacher / T:
+//   ls_j = (x_j - x_a) - log1p(S_s),  S_s = sum_{j != a} e^(x_j - x_a)
+//   (a = first argmax; the same for the teacher), so log p at the argmax is
+//   -log1p(S), not a difference of two nearly equal numbers;
+//   delta_j = lt_j - ls_j;
+//   beta = 0: loss = sum pt delta,              d_j = (ps_j - pt_j) / T
+//   beta = 1: loss = -sum ps delta,             d_j = ps_j (-delta_j - loss) / T
+//   else:     r = ls - lm, q = lt - lm as functions of delta (log1p / expm1
+//             of a non-positive exponent), K = sum ps r,
+//             loss = beta sum pt q + (1 - beta) K, d_j = (1 - beta) ps_j (r_j - K) / T
+// all times the row's upstream gradient g.
+//
+//   k_jsd_forward   one workgroup per row.  Pass 1 reads both rows once
+//                   (caching loads) and keeps, per lane, each row's maximum,
+//                   its first column and the sum of the other columns at that
+//                   maximum (fp64): when the maximum moves, the old maximum's
+//                   own term 1 joins the rescaled sum, so the argmax is
+//                   excluded without a second sweep.  Pass 2 re-reads both
+//                   rows (mostly from the caches) and sums the loss terms in
+//                   fp64.  Writes the loss and a 32-byte record per row.
+//   k_jsd_backward  one workgroup per row, one read of both rows, one write of
+//                   the student gradient; the argmax entry is written last.
+#include "cev_device.h"
+#include "cev_launch.h"
+
+namespace cev {
+namespace {
+
+constexpr int kJB = 256;   // threads per row
+
+// Largest value m seen, its first column, and the sum over the other columns
+// seen of 2^((z - m) c).
+struct MaxSum {
+    float m;
+    int col;
+    double s;
+};
+
+__device__ __forceinline__ MaxSum ms_empty() { return MaxSum{-INFINITY, INT32_MAX, 0.0}; }
+
+// Add n consecutive values starting at column col0.
+template <int N>
+__device__ __forceinline__ void ms_add(MaxSum &st, const float (&v)[N], int col0, float c)
+{
+    float vm = v[0];
+    int vi = 0;
+#pragma unroll
+    for (int i = 1; i < N; ++i)
+        if (v[i] > vm) {
+            vm = v[i];
+            vi = i;
+        }
+    int excl = -1;
+    if (vm > st.m) {
+        const double carry = st.m == -INFINITY ? 0.0 : 1.0;   // the old maximum's own term
+        st.s = (st.s + carry) * (double)exp2_hw((st.m - vm) * c);
+        st.m = vm;
+        st.col = col0 + vi;
+        excl = vi;
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        if (i != excl)
+            acc += exp2_hw((v[i] - st.m) * c);
+    st.s += (double)acc;
+}
+
+// Merge two states: the larger maximum wins (then the lower column); the
+// loser's maximum element becomes one of the others.
+__device__ __forceinline__ MaxSum ms_merge(MaxSum a, MaxSum b, float c)
+{
+    if (b.m > a.m || (b.m == a.m && b.col < a.col)) {
+        const MaxSum t = a;
+        a = b;
+        b = t;
+    }
+    if (b.m == -INFINITY)
+        return a;
+    if (b.m == a.m)
+        a.s += b.s + 1.0;
+    else
+        a.s += (b.s + 1.0) * (double)exp2_hw((b.m - a.m) * c);
+    return a;
+}
+
+__device__ __forceinline__ MaxSum ms_shfl(const MaxSum &a, int o)
+{
+    MaxSum b;
+    b.m = __shfl_xor(a.m, o);
+    b.col = __shfl_xor(a.col, o);
+    b.s = __shfl_xor(a.s, o);
+    return b;
+}
+
+template <int BLOCK>
+__device__ __forceinline__ MaxSum ms_block(MaxSum st, float c, MaxSum *sh)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1)
+        st = ms_merge(st, ms_shfl(st, o), c);
+    const int w = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0)
+        sh[w] = st;
+    __syncthreads();
+    MaxSum r = sh[0];
+#pragma unroll
+    for (int i = 1; i < BLOCK / kWave; ++i)
+        r = ms_merge(r, sh[i], c);
+    __syncthreads();
+    return r;
+}
+
+// Per-row constants of pass 2 and of the backward.
+struct JsdRow {
+    float ms, mt;          // stored maxima
+    float ls2, lt2;        // log1p(S_s), log1p(S_t) in log2 units
+    float dl0;             // log1p(S_s) - log1p(S_t), rounded once from fp64
+};
+
+__device__ __forceinline__ JsdRow jsd_row(float ms, float ls0, float mt, float lt0, float dl0)
+{
+    constexpr float kLog2e = 1.4426950408889634f;
+    return JsdRow{ms, mt, ls0 * kLog2e, lt0 * kLog2e, dl0};
+}
+
+// The mixture's gaps r = ls - lm and q = lt - lm from delta = lt - ls:
+// beta e^lt + (1 - beta) e^ls = e^ls (1 + beta expm1(delta))
+//                             = e^lt (1 + (1 - beta) expm1(-delta)).
+__device__ __forceinline__ void mix_gaps(float delta, float beta, float &r, float &q)
+{
+    if (delta <= 0.0f) {
+        r = -log1pf(beta * expm1f(delta));
+        q = delta + r;
+    } else {
+        q = -log1pf((1.0f - beta) * expm1f(-delta));
+        r = q - delta;
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void load_vec(const char *row, int64_t v, float (&out)[Elem<DT>::kVE],
+                                         bool stream)
+{
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(row) + v;
+    const u32x4 w = stream ? load16_stream(p) : *p;
+    unpack16<DT>(w, out);
+}
+
+template <int DT> __device__ __forceinline__ float load_one(const char *row, int64_t j)
+{
+    if constexpr (DT == CEV_F32)
+        return reinterpret_cast<const float *>(row)[j];
+    else
+        return bf16_lo(reinterpret_cast<const unsigned short *>(row)[j]);
+}
+
+// Loss terms of n columns: adds to L (and K for the mixture).
+template <int MODE, int N>
+__device__ __forceinline__ void loss_terms(const float (&zs)[N], const float (&zt)[N],
+                                           const JsdRow &rc, float c, float inv_t, float beta,
+                                           double &L, double &K)
+{
+    float l = 0.0f, k = 0.0f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float as = zs[i] - rc.ms, at = zt[i] - rc.mt;
+        const float delta = fmaf(at - as, inv_t, rc.dl0);   // lt - ls
+        if constexpr (MODE == 0) {
+            const float pt = exp2_hw(fmaf(at, c, -rc.lt2));
+            l = fmaf(pt, delta, l);
+        } else if constexpr (MODE == 1) {
+            const float ps = exp2_hw(fmaf(as, c, -rc.ls2));
+            l = fmaf(-ps, delta, l);
+        } else {
+            const float ps = exp2_hw(fmaf(as, c, -rc.ls2));
+            const float pt = exp2_hw(fmaf(at, c, -rc.lt2));
+            float r, q;
+            mix_gaps(delta, beta, r, q);
+            l = fmaf(beta * pt, q, l);
+            k = fmaf(ps, r, k);
+        }
+    }
+    L += (double)l;
+    if constexpr (MODE == 2)
+        K += (double)k;
+}
+
+// ------------------------------------------------------------------ forward
+template <int DT, int MODE>
+__global__ __launch_bounds__(kJB) void k_jsd_forward(JsdArgs a)
+{
+    constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize;
+    __shared__ MaxSum sh_ms[kJB / kWave];
+    __shared__ double sh_d[kJB / kWave];
+    const int tid = threadIdx.x;
+    const int64_t r = blockIdx.x;
+    const bool masked = (a.row_mask && a.row_mask[r] == 0) ||
+                        (a.labels && a.labels[r] == a.ignore_index);
+    cev_jsd_saved *sv = a.saved + r;
+    if (masked) {
+        if (tid == 0) {
+            a.loss[r] = 0.0f;
+            *sv = cev_jsd_saved{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, -1, 0, 0.0f};
+        }
+        return;
+    }
+    const char *rs = static_cast<const char *>(a.student) + (size_t)r * (size_t)a.s_stride * ES;
+    const char *rt = static_cast<const char *>(a.teacher) + (size_t)r * (size_t)a.t_stride * ES;
+    const int64_t V = a.vocab, nv = a.vec ? V / VE : 0;   // rows not 16-byte aligned: scalar
+    const float c = a.c, inv_t = a.inv_t;
+
+    // pass 1: maxima, argmaxes, sums of the others
+    MaxSum ss = ms_empty(), st = ms_empty();
+    for (int64_t v = tid; v < nv; v += kJB) {
+        float xs[VE], xt[VE];
+        load_vec<DT>(rs, v, xs, false);
+        load_vec<DT>(rt, v, xt, false);
+        ms_add(ss, xs, (int)(v * VE), c);
+        ms_add(st, xt, (int)(v * VE), c);
+    }
+    for (int64_t j = nv * VE + tid; j < V; j += kJB) {
+        const float xs[1] = {load_one<DT>(rs, j)}, xt[1] = {load_one<DT>(rt, j)};
+        ms_add(ss, xs, (int)j, c);
+        ms_add(st, xt, (int)j, c);
+    }
+    ss = ms_block<kJB>(ss, c, sh_ms);
+    st = ms_block<kJB>(st, c, sh_ms);
+    const double ls0d = log1p(ss.s), lt0d = log1p(st.s);
+    const float ls0 = (float)ls0d, lt0 = (float)lt0d, dl0 = (float)(ls0d - lt0d);
+    const JsdRow rc = jsd_row(ss.m, ls0, st.m, lt0, dl0);
+
+    // pass 2: the loss terms
+    double L = 0.0, K = 0.0;
+    for (int64_t v = tid; v < nv; v += kJB) {
+        float xs[VE], xt[VE];
+        load_vec<DT>(rs, v, xs, true);
+        load_vec<DT>(rt, v, xt, true);
+        loss_terms<MODE>(xs, xt, rc, c, inv_t, a.beta, L, K);
+    }
+    for (int64_t j = nv * VE + tid; j < V; j += kJB) {
+        const float xs[1] = {load_one<DT>(rs, j)}, xt[1] = {load_one<DT>(rt, j)};
+        loss_terms<MODE>(xs, xt, rc, c, inv_t, a.beta, L, K);
+    }
+    L = block_sum<kJB>(L, sh_d);
+    if constexpr (MODE == 2)
+        K = block_sum<kJB>(K, sh_d);
+    if (tid == 0) {
+        const double beta = a.beta;
+        double loss = L, kk = 0.0;
+        if constexpr (MODE == 1)
+            kk = L;
+        if constexpr (MODE == 2) {
+            loss = L + (1.0 - beta) * K;
+            kk = K;
+        }
+        a.loss[r] = (float)loss;
+        *sv = cev_jsd_saved{ss.m, ls0, st.m, lt0, (float)kk, ss.col, 1, dl0};
+    }
+}
+
+// ----------------------------------------------------------------- backward
+// The row's weight |g| (1 - beta) / T (|g| / T at the ends) is folded into the
+// exponents as log2 of it (es = ls2 - log2 w, et = lt2 - log2 w), and where
+// the probability is then multiplied by a factor (beta > 0: up to a few
+// hundred) it is formed 2^24 too large and scaled back exactly after the
+// product, so an entry is flushed to zero only when it is itself below the
+// fp32 normal range; the sign of g is applied to the bits.
+constexpr float kPre = 16777216.0f, kPreInv = 1.0f / 16777216.0f;   // 2^24, 2^-24
+template <int MODE, int N>
+__device__ __forceinline__ void grad_terms(const float (&zs)[N], const float (&zt)[N],
+                                           const JsdRow &rc, float es, float et, float c,
+                                           float inv_t, float beta, float kk, unsigned sgn,
+                                           int col0, int arg, float (&out)[N], double &sum)
+{
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float as = zs[i] - rc.ms, at = zt[i] - rc.mt;
+        const float pw = exp2_hw(fmaf(as, c, -es));
+        float d;
+        if constexpr (MODE == 0) {
+            d = pw - exp2_hw(fmaf(at, c, -et));
+        } else {
+            const float delta = fmaf(at - as, inv_t, rc.dl0);   // lt - ls
+            if constexpr (MODE == 1) {
+                d = (pw * (-delta - kk)) * kPreInv;
+            } else {
+                float r, q;
+                mix_gaps(delta, beta, r, q);
+                d = (pw * (r - kk)) * kPreInv;
+            }
+        }
+        d = __uint_as_float(__float_as_uint(d) ^ sgn);
+        if (col0 + i == arg)
+            d = 0.0f;
+        acc += d;
+        out[i] = d;
+    }
+    sum += (double)acc;
+}
+
+template <int DT> __device__ __forceinline__ void store_vec(char *row, int64_t v, const float *d)
+{
+    u32x4 o;
+    if constexpr (DT == CEV_F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o[i] = __float_as_uint(d[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o[i] = pack_bf16x2(d[2 * i], d[2 * i + 1]);
+    }
+    store16_stream(o, reinterpret_cast<u32x4 *>(row) + v);
+}
+
+template <int DT> __device__ __forceinline__ void store_one(char *row, int64_t j, float d)
+{
+    if constexpr (DT == CEV_F32)
+        reinterpret_cast<float *>(row)[j] = d;
+    else
+        reinterpret_cast<unsigned short *>(row)[j] = to_bf16(d);
+}
+
+template <int DT, int MODE>
+__global__ __launch_bounds__(kJB) void k_jsd_backward(JsdArgs a)
+{
+    constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize;
+    __shared__ double sh_d[kJB / kWave];
+    const int tid = threadIdx.x;
+    const int64_t r = blockIdx.x;
+    const int64_t V = a.vocab, nv = a.vec ? V / VE : 0;
+    char *rd = static_cast<char *>(a.dstudent) + (size_t)r * (size_t)a.d_stride * ES;
+    const bool masked = (a.row_mask && a.row_mask[r] == 0) ||
+                        (a.labels && a.labels[r] == a.ignore_index);
+    const cev_jsd_saved sv = a.saved_in[r];
+    if (masked || !(sv.flags & 1)) {   // no record from the forward: a zero row
+        const float z[VE] = {};
+        for (int64_t v = tid; v < nv; v += kJB)
+            store_vec<DT>(rd, v, z);
+        for (int64_t j = nv * VE + tid; j < V; j += kJB)
+            store_one<DT>(rd, j, 0.0f);
+        return;
+    }
+    const char *rs = static_cast<const char *>(a.student) + (size_t)r * (size_t)a.s_stride * ES;
+    const char *rt = static_cast<const char *>(a.teacher) + (size_t)r * (size_t)a.t_stride * ES;
+    const float c = a.c, inv_t = a.inv_t;
+    const JsdRow rc = jsd_row(sv.ms, sv.ls0, sv.mt, sv.lt0, sv.dl);
+    const float gr = a.g[r];
+    const float wabs = fabsf(gr) * inv_t * (MODE == 2 ? (float)(1.0 - a.beta) : 1.0f);
+    const float lw = __log2f(wabs);                  // -inf for g = 0: every entry 0
+    const float es = rc.ls2 - lw - (MODE == 0 ? 0.0f : 24.0f), et = rc.lt2 - lw;
+    const unsigned sgn = __float_as_uint(gr) & 0x80000000u;
+    double sum = 0.0;
+    for (int64_t v = tid; v < nv; v += kJB) {
+        float xs[VE], xt[VE], d[VE];
+        load_vec<DT>(rs, v, xs, true);
+        load_vec<DT>(rt, v, xt, true);
+        grad_terms<MODE>(xs, xt, rc, es, et, c, inv_t, a.beta, sv.k, sgn, (int)(v * VE), sv.arg,
+                         d, sum);
+        store_vec<DT>(rd, v, d);
+    }
+    for (int64_t j = nv * VE + tid; j < V; j += kJB) {
+        const float xs[1] = {load_one<DT>(rs, j)}, xt[1] = {load_one<DT>(rt, j)};
+        float d[1];
+        grad_terms<MODE>(xs, xt, rc, es, et, c, inv_t, a.beta, sv.k, sgn, (int)j, sv.arg, d, sum);
+        store_one<DT>(rd, j, d[0]);
+    }
+    sum = block_sum<kJB>(sum, sh_d);   // ends with a barrier: every store above is done
+    if (tid == 0)
+        store_one<DT>(rd, sv.arg, (float)(-sum));
+}
+
+template <int DT>
+void launch_fwd_t(const JsdArgs &a, int mode, hipStream_t s)
+{
+    const dim3 grid((unsigned)a.rows), block(kJB);
+    if (mode == 0)
+        hipLaunchKernelGGL((k_jsd_forward<DT, 0>), grid, block, 0, s, a);
+    else if (mode == 1)
+        hipLaunchKernelGGL((k_jsd_forward<DT, 1>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((k_jsd_forward<DT, 2>), grid, block, 0, s, a);
+}
+
+template <int DT>
+void launch_bwd_t(const JsdArgs &a, int mode, hipStream_t s)
+{
+    const dim3 grid((unsigned)a.rows), block(kJB);
+    if (mode == 0)
+        hipLaunchKernelGGL((k_jsd_backward<DT, 0>), grid, block, 0, s, a);
+    else if (mode == 1)
+        hipLaunchKernelGGL((k_jsd_backward<DT, 1>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((k_jsd_backward<DT, 2>), grid, block, 0, s, a);
+}
+
+int jsd_mode(double beta) { return beta == 0.0 ? 0 : beta == 1.0 ? 1 : 2; }
+
+} // namespace
+
+hipError_t launch_jsd_forward(int dtype, const JsdArgs &a, hipStream_t s)
+{
+    if (dtype == CEV_BF16)
+        launch_fwd_t<CEV_BF16>(a, jsd_mode(a.beta), s);
+    else
+        launch_fwd_t<CEV_F32>(a, jsd_mode(a.beta), s);
+    return hipGetLastError();
+}
+
+hipError_t launch_jsd_backward(int dtype, const JsdArgs &a, hipStream_t s)
+{
+    if (dtype == CEV_BF16)
+        launch_bwd_t<CEV_BF16>(a, jsd_mode(a.beta), s);
+    else
+        launch_bwd_t<CEV_F32>(a, jsd_mode(a.beta), s);
+    return hipGetLastError();
+}
+
+} // namespace cev

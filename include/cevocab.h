@@ -76,7 +76,8 @@ enum cev_error {
     CEV_EWORKSPACE = -7,   /* workspace too small */
     CEV_EALIAS = -8,       /* dlogits overlaps logits */
     CEV_ELAUNCH = -9,      /* the HIP runtime refused a launch */
-    CEV_ESMOOTH = -10      /* label_smoothing not finite or outside [0, 1] */
+    CEV_ESMOOTH = -10,     /* label_smoothing not finite or outside [0, 1] */
+    CEV_EBETA = -11        /* jsd beta not finite or outside [0, 1] */
 };
 
 /* Bits ORed into the optional device status word. */
@@ -395,6 +396,64 @@ int lce_backward(const void *hidden, int64_t rows, int64_t hidden_dim, int64_t h
 /* Bytes of workspace lce_forward and lce_backward need (0 for invalid
  * arguments). */
 size_t lce_workspace_size(int64_t rows, int64_t hidden_dim, int64_t vocab);
+
+/* ---------------------------------------------------------------------------
+ * Generalized Jensen-Shannon divergence between a student and a teacher logit
+ * row, with the KL divergences at its ends (the generalized JSD of the
+ * unsloth-zoo #2079 Summary quoted on the Liger-Kernel PR #1555 page): with
+ * P_s = softmax(student / T), P_t = softmax(teacher / T),
+ *   beta = 0      KL(P_t || P_s)   (forward KL)
+ *   beta = 1      KL(P_s || P_t)   (reverse KL)
+ *   0 < beta < 1  beta KL(P_t || M) + (1 - beta) KL(P_s || M),
+ *                 M = beta P_t + (1 - beta) P_s
+ * per row, no reduction; the teacher is not differentiated.  Log-softmax is
+ * based at each row's argmax (log p there is -log1p of the others' sum) and
+ * the gradient entry at the student's argmax is minus the sum of the others
+ * (Liger-Kernel PR #1555, Summary, "fused KL / JSD" bullet), so rows peaked far
+ * beyond the fp32 softmax collapse keep an accurate, zero-sum gradient.
+ *
+ *   student, teacher  [rows, *_stride] in dtype (both CEV_F32 or both
+ *                     CEV_BF16), element-aligned, read only; when every row
+ *                     of every operand starts 16-byte aligned the kernels
+ *                     use 16-byte vector accesses, otherwise scalar ones
+ *   labels            [rows] int64 or NULL: a row whose label equals
+ *                     ignore_index is masked (any other value is fine)
+ *   row_mask          [rows] u8 or NULL: 0 masks the row
+ *   temperature       finite, > 0 (CEV_ETEMP); beta in [0, 1] (CEV_EBETA)
+ * Masked rows get loss 0, an invalid saved record and an all-zero gradient.
+ * Deterministic: fixed reduction order, no float atomics.
+ */
+
+/* Per-row record of jsd_forward, read by jsd_backward: 32 bytes. */
+typedef struct cev_jsd_saved {
+    float ms;      /* largest stored student logit */
+    float ls0;     /* log1p(sum over the student's other columns of e^{(z - ms)/T}) */
+    float mt;      /* largest stored teacher logit */
+    float lt0;     /* the same for the teacher */
+    float k;       /* the loss at beta = 1, sum P_s log(P_s / M) in between, 0 at beta = 0 */
+    int32_t arg;   /* the student's argmax column (first occurrence), -1 if masked */
+    int32_t flags; /* bit 0: row valid */
+    float dl;      /* ls0 - lt0 formed in fp64, then rounded */
+} cev_jsd_saved;
+
+/* jsd_forward -- loss [rows] fp32 and saved [rows] x 32 bytes (16-byte
+ * aligned), both required. */
+int jsd_forward(const void *student, const void *teacher, int64_t rows, int64_t vocab,
+                int64_t student_stride, int64_t teacher_stride, int dtype,
+                const int64_t *labels, int64_t ignore_index, double temperature, double beta,
+                const uint8_t *row_mask, float *loss, void *saved, int32_t *status,
+                cev_stream_t stream);
+
+/* jsd_backward -- dstudent [rows, dstudent_stride] in dtype (must not overlap
+ * either input) = g[r] times the gradient of row r's
+ * loss with respect to the student logits; bf16 is rounded to nearest even
+ * from fp32, the argmax entry from the fp64 sum of the others.  saved from
+ * jsd_forward with the same arguments. */
+int jsd_backward(const void *student, const void *teacher, int64_t rows, int64_t vocab,
+                 int64_t student_stride, int64_t teacher_stride, int dtype,
+                 const int64_t *labels, int64_t ignore_index, double temperature, double beta,
+                 const uint8_t *row_mask, const float *g, const void *saved, void *dstudent,
+                 int64_t dstudent_stride, int32_t *status, cev_stream_t stream);
 
 /* Bytes of workspace that let ce_forward hold the compacted row list and
  * count and, for few rows, the split-row partial records (0 for invalid

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "cevocab.h")
 
 E = dict(OK=0, NULL=-1, SHAPE=-2, STRIDE=-3, ALIGN=-4, DTYPE=-5, TEMP=-6, WORKSPACE=-7,
-         ALIAS=-8, LAUNCH=-9, SMOOTH=-10)
+         ALIAS=-8, LAUNCH=-9, SMOOTH=-10, BETA=-11)
 
 
 @pytest.fixture(scope="module")
@@ -60,7 +60,7 @@ def test_codes_match_header():
 
 
 def test_version_and_strings(lib):
-    assert lib.cev_version() == 200
+    assert lib.cev_version() == 210
     for code in E.values():
         assert lib.cev_status_string(code)
     assert lib.cev_workspace_size(10, 100, 0) == 88          # list + count only
@@ -350,4 +350,50 @@ def test_lce_validation(lib):
     assert bwd(g=None) == E["NULL"]
     assert bwd(saved=A + 4) == E["ALIGN"]
     assert bwd(wkb=16) == E["WORKSPACE"]
+    assert bwd(rows=0) == E["OK"]
+
+
+def test_jsd_validation(lib):
+    """Every argument error of the JSD entry points is returned before any
+    launch (host-side only; the pointers are never dereferenced)."""
+    def fwd(**kw):
+        a = dict(s=A, t=B, rows=4, V=1000, ss=1000, ts=1000, dtype=0, labels=None, ig=-100,
+                 T=1.0, beta=0.5, mask=None, loss=A, saved=A, status=None)
+        a.update(kw)
+        return lib.jsd_forward(a["s"], a["t"], a["rows"], a["V"], a["ss"], a["ts"], a["dtype"],
+                               a["labels"], a["ig"], a["T"], a["beta"], a["mask"], a["loss"],
+                               a["saved"], a["status"], None)
+    assert fwd(beta=-0.1) == E["BETA"]
+    assert fwd(beta=1.5) == E["BETA"]
+    assert fwd(beta=float("nan")) == E["BETA"]
+    assert fwd(T=0.0) == E["TEMP"]
+    assert fwd(dtype=3) == E["DTYPE"]
+    assert fwd(V=0) == E["SHAPE"]
+    assert fwd(ss=999) == E["STRIDE"]
+    assert fwd(ts=999) == E["STRIDE"]
+    assert fwd(t=None) == E["NULL"]
+    assert fwd(loss=None) == E["NULL"]
+    assert fwd(saved=None) == E["NULL"]
+    assert fwd(s=A + 2) == E["ALIGN"]                  # element alignment
+    assert fwd(t=B + 2) == E["ALIGN"]
+    assert fwd(dtype=1, t=B + 1) == E["ALIGN"]
+    assert fwd(saved=A + 8) == E["ALIGN"]
+    assert fwd(rows=0, s=None, t=None) == E["OK"]
+    for beta in (0.0, 1.0):
+        assert fwd(beta=beta, t=None) == E["NULL"]     # the ends of [0, 1] are accepted
+
+    def bwd(**kw):
+        a = dict(s=A, t=B, rows=4, V=1000, ss=1000, ts=1000, dtype=0, labels=None, ig=-100,
+                 T=1.0, beta=0.5, mask=None, g=A, saved=A, d=A + (1 << 24), ds=1000, status=None)
+        a.update(kw)
+        return lib.jsd_backward(a["s"], a["t"], a["rows"], a["V"], a["ss"], a["ts"], a["dtype"],
+                                a["labels"], a["ig"], a["T"], a["beta"], a["mask"], a["g"],
+                                a["saved"], a["d"], a["ds"], a["status"], None)
+    assert bwd(beta=2.0) == E["BETA"]
+    assert bwd(ds=999) == E["STRIDE"]
+    assert bwd(g=None) == E["NULL"]
+    assert bwd(d=None) == E["NULL"]
+    assert bwd(d=A + (1 << 24) + 2) == E["ALIGN"]
+    assert bwd(d=A + 64) == E["ALIAS"]                  # overlaps the student
+    assert bwd(d=B + 64) == E["ALIAS"]                  # overlaps the teacher
     assert bwd(rows=0) == E["OK"]

@@ -224,3 +224,66 @@ def linear(rows=8192, hidden=2560, vocab=151936, seed=5, peaked_frac=0.0, temper
                                                                               dtype=np.float32))
     return dict(name="linear", hidden=h, weight=w, labels=labels, row_mask=row_mask,
                 temperature=temperature, g=g, peak_rows=peak_rows)
+
+
+DISTILL_MARGINS = (20.0, 40.0, 60.0, 80.0)
+
+
+def distill(rows=2048, vocab=151936, seed=6, dtype="bf16", temperature=1.0, peaked_frac=0.0):
+    """Student and teacher logit rows for the generalized JSD (unsloth-zoo
+    #2079 Numbers: 2048 rows, V = 151936, bf16; the peaked rows lead by 20 to
+    80, the range its Summary names).
+
+    student z_s = 3 N(0, 1) + shift_r with shift_r ~ U(-5, 5); teacher
+    z_t = z_s + N(0, 1) (a teacher close to, but not equal to, the student);
+    labels uniform with rows // 10 of them the ignore index (the label mask);
+    rows // 20 rows masked by row_mask; g ~ U(0.5, 1.5).  A fraction
+    peaked_frac of the rows is made peaked: the student's column a leads its
+    other values by a margin from DISTILL_MARGINS, and the teacher leads by
+    another margin either at the same column (even-numbered peaked rows) or
+    at another one (odd-numbered), so both agreeing and disagreeing confident
+    rows occur.  fp32 or bf16 (stored bit patterns)."""
+    rng = np.random.default_rng(seed)
+    shift = rng.uniform(-5.0, 5.0, rows).astype(np.float32)
+    labels = rng.integers(0, vocab, rows).astype(np.int64)
+    labels[rng.permutation(rows)[:rows // 10]] = IGNORE_INDEX
+    row_mask = np.ones(rows, dtype=np.uint8)
+    row_mask[rng.permutation(rows)[:rows // 20]] = 0
+    g = rng.uniform(0.5, 1.5, rows).astype(np.float32)
+    n_peak = int(round(peaked_frac * rows))
+    peak_rows = np.sort(rng.permutation(rows)[:n_peak])
+    ms = np.asarray(DISTILL_MARGINS, np.float32)[rng.integers(0, len(DISTILL_MARGINS), n_peak)]
+    mt = np.asarray(DISTILL_MARGINS, np.float32)[rng.integers(0, len(DISTILL_MARGINS), n_peak)]
+    cs = rng.integers(0, vocab, n_peak)
+    ct = np.where(np.arange(n_peak) % 2 == 0, cs, (cs + 1 + rng.integers(0, vocab - 1, n_peak)) % vocab)
+    peak_of = {int(r): i for i, r in enumerate(peak_rows)}
+
+    def rnd(z):
+        return bf16_to_f32(bf16_bits(z)) if dtype == "bf16" else z
+
+    def fill(which):
+        def f(b, gen, r0, r1):
+            zs = rnd(3.0 * gen.standard_normal((r1 - r0, vocab), dtype=np.float32)
+                     + shift[r0:r1, None])
+            if which == "student":
+                z = zs
+            else:
+                noise = np.random.default_rng([seed, 7, b]).standard_normal((r1 - r0, vocab),
+                                                                             dtype=np.float32)
+                z = rnd(zs + noise)
+            for i, r in enumerate(range(r0, r1)):
+                k = peak_of.get(r)
+                if k is None:
+                    continue
+                col = cs[k] if which == "student" else ct[k]
+                lead = ms[k] if which == "student" else mt[k]
+                z[i, col] = -np.inf
+                z[i, col] = rnd(np.float32(z[i].max() + lead))
+            return bf16_bits(z) if dtype == "bf16" else z
+        return f
+
+    store = np.uint16 if dtype == "bf16" else np.float32
+    student = _assemble(_draw_matrix(seed, rows, vocab, fill("student")), rows, vocab, store)
+    teacher = _assemble(_draw_matrix(seed, rows, vocab, fill("teacher")), rows, vocab, store)
+    return dict(name=f"distill_{dtype}", student=student, teacher=teacher, labels=labels,
+                row_mask=row_mask, temperature=float(temperature), g=g, peak_rows=peak_rows)
