@@ -248,6 +248,60 @@ def bench_linear(args, torch, cev, workloads, dev):
     return res
 
 
+def bench_jsd(args, torch, cev, workloads, dev):
+    """jsd_forward + jsd_backward on the 2048 x 151936 bf16 student/teacher
+    pair at beta 0, 0.5 and 1.  Algorithmic bytes: the forward reads each
+    valid row of both matrices once; the backward reads them once more and
+    writes every gradient row."""
+    log("[bench] jsd: generating 2048x151936 bf16 student and teacher")
+    w = workloads.distill()
+    R, V = w["student"].shape
+    st = torch.from_numpy(w["student"].view(np.int16)).to(dev).view(torch.bfloat16)
+    te = torch.from_numpy(w["teacher"].view(np.int16)).to(dev).view(torch.bfloat16)
+    lab = torch.from_numpy(w["labels"]).to(dev)
+    msk = torch.from_numpy(w["row_mask"]).to(dev)
+    g = torch.from_numpy(w["g"]).to(dev)
+    n_valid = int(((w["labels"] != -100) & (w["row_mask"] != 0)).sum())
+    fwd_bytes = 2 * n_valid * V * 2
+    bwd_bytes = 2 * n_valid * V * 2 + R * V * 2
+    steps = max(3, args.steps // 2)
+    res = {"entry": "jsd_forward + jsd_backward (student gradient), 2048 x 151936 bf16 "
+                    "student/teacher rows as in the unsloth-zoo #2079 Numbers",
+           "shape": {"rows": R, "vocab": V, "valid_rows": n_valid},
+           "algorithmic_bytes": {"forward": fwd_bytes, "backward": bwd_bytes}}
+    dl = torch.empty_like(st)
+    for beta in (0.0, 0.5, 1.0):
+        out = cev.jsd_forward(st, te, 1.0, beta, labels=lab, row_mask=msk)
+        for _ in range(2):
+            cev.jsd_forward(st, te, 1.0, beta, labels=lab, row_mask=msk, out=out)
+            cev.jsd_backward(st, te, g, out["saved"], 1.0, beta, labels=lab, row_mask=msk,
+                             dstudent=dl)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e0, e1, e2 in ev:
+            e0.record()
+            cev.jsd_forward(st, te, 1.0, beta, labels=lab, row_mask=msk, out=out)
+            e1.record()
+            cev.jsd_backward(st, te, g, out["saved"], 1.0, beta, labels=lab, row_mask=msk,
+                             dstudent=dl)
+            e2.record()
+        torch.cuda.synchronize()
+        f_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+        b_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+        res[f"beta_{beta:g}"] = {"forward_ms": f_ms, "backward_ms": b_ms,
+                                 "forward_GBps": fwd_bytes / (f_ms / 1e3) / 1e9,
+                                 "backward_GBps": bwd_bytes / (b_ms / 1e3) / 1e9,
+                                 "rows_per_s": R / ((f_ms + b_ms) / 1e3)}
+        log(f"[bench] jsd beta={beta:g}: forward {f_ms:.3f} ms, backward {b_ms:.3f} ms")
+    bb = res["beta_0.5"]
+    res["roofline"] = {"bound": "hbm", "kernel": "k_jsd_backward (beta 0.5)", "unit": "GB/s",
+                       "achieved": bb["backward_GBps"], "peak": PEAK_HBM_GBS,
+                       "frac": bb["backward_GBps"] / PEAK_HBM_GBS}
+    del st, te, dl
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,6 +314,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain elementwise kernel over 1 GiB in / 1 GiB out, "
                          "the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--no-jsd", action="store_true",
+                    help="skip the student/teacher JSD measurement (2048 x 151936)")
     ap.add_argument("--no-linear", action="store_true",
                     help="skip the linear cross-entropy measurement (8192 x 2560 x 151936)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -382,6 +438,7 @@ def main():
     del logits, dl, out, fout
     torch.cuda.empty_cache()
     linear = None if args.no_linear else bench_linear(args, torch, cev, workloads, dev)
+    jsd = None if args.no_jsd else bench_jsd(args, torch, cev, workloads, dev)
 
     ES = 2
     fwd_bytes = n_valid * V * ES                    # valid rows read once
@@ -427,6 +484,7 @@ def main():
                   "GBps": (fwd_bytes + R * V * ES) / (fused_ms / 1e3) / 1e9,
                   "frac_of_peak": (fwd_bytes + R * V * ES) / (fused_ms / 1e3) / 1e9 / PEAK_HBM_GBS},
         "linear_ce": linear,
+        "jsd": jsd,
         "vocab_shard": {"entry": f"one rank of {P}-way vocab parallelism: "
                                  "ce_vocab_shard_forward on its contiguous shard, ce_vocab_merge "
                                  f"of {P} shards' records, ce_vocab_shard_backward",

@@ -134,16 +134,24 @@ __device__ __forceinline__ JsdRow jsd_row(float ms, float ls0, float mt, float l
 }
 
 // The mixture's gaps r = ls - lm and q = lt - lm from delta = lt - ls:
-// beta e^lt + (1 - beta) e^ls = e^ls (1 + beta expm1(delta))
-//                             = e^lt (1 + (1 - beta) expm1(-delta)).
+// beta e^lt + (1 - beta) e^ls = e^ls (1 + beta (e^delta - 1))
+//                             = e^lt (1 + (1 - beta) (e^-delta - 1)),
+// with the exponent never positive.  Hardware exp2 / log2 suffice: the
+// gaps then err by a few 1e-7 absolute, the size of the error the
+// log-probabilities they are built from already carry, and delta = 0 gives
+// exactly 0.
 __device__ __forceinline__ void mix_gaps(float delta, float beta, float &r, float &q)
 {
+    constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+    const float e = exp2_hw(-fabsf(delta) * kLog2e);
+    const float w = delta <= 0.0f ? beta : 1.0f - beta;
+    const float gap = -__builtin_amdgcn_logf(fmaf(w, e - 1.0f, 1.0f)) * kLn2;
     if (delta <= 0.0f) {
-        r = -log1pf(beta * expm1f(delta));
-        q = delta + r;
+        r = gap;
+        q = delta + gap;
     } else {
-        q = -log1pf((1.0f - beta) * expm1f(-delta));
-        r = q - delta;
+        q = gap;
+        r = gap - delta;
     }
 }
 
