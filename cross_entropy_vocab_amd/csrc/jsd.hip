@@ -20,13 +20,14 @@
 // all times the row's upstream gradient g.
 //
 //   k_jsd_forward   one workgroup per row.  Pass 1 reads both rows once
-//                   (caching loads) and keeps, per lane, each row's maximum,
-//                   its first column and the sum of the other columns at that
-//                   maximum (fp64): when the maximum moves, the old maximum's
-//                   own term 1 joins the rescaled sum, so the argmax is
-//                   excluded without a second sweep.  Pass 2 re-reads both
-//                   rows (mostly from the caches) and sums the loss terms in
-//                   fp64.  Writes the loss and a 32-byte record per row.
+//                   and keeps, per lane, each row's maximum, its first column
+//                   and the sum of the other columns at that maximum (fp64):
+//                   when the maximum moves, the old maximum's own term 1 joins
+//                   the rescaled sum, so the argmax is excluded without a
+//                   second sweep.  At the two KL ends the loss is accumulated
+//                   in the same pass against the running maxima (KlAcc); in
+//                   between, pass 2 re-reads both rows and sums the loss terms
+//                   in fp64.  Writes the loss and a 32-byte record per row.
 //   k_jsd_backward  one workgroup per row, one read of both rows, one write of
 //                   the student gradient; the argmax entry is written last.
 #include "cev_device.h"
@@ -118,6 +119,88 @@ __device__ __forceinline__ MaxSum ms_block(MaxSum st, float c, MaxSum *sh)
         r = ms_merge(r, sh[i], c);
     __syncthreads();
     return r;
+}
+
+// Single-pass loss of the two KL ends.  P is the row whose probabilities
+// weight the loss (the teacher for beta = 0, the student for beta = 1), Q the
+// other; A = sum_j w_j [(zP_j - mP) - (zQ_j - mQ)] with w_j = e^((zP_j - mP)/T)
+// against the running maxima mP, mQ, so that at the end
+//   loss = A / (T W) +- (log1p(S_s) - log1p(S_t)),  W = sum_j w_j = 1 + S_P.
+// When mQ rises by d every bracket grows by d: A += d W.  When mP rises by d
+// every weight shrinks by e^(-d/T) and every bracket by d:
+// A = e^(-d/T) (A - d W).  The column of each row's own maximum contributes
+// exactly 0 to its bracket, so a peaked row loses nothing to cancellation.
+struct KlAcc {
+    double a;
+};
+
+template <int N>
+__device__ __forceinline__ void kl_add(KlAcc &k, MaxSum &sp, MaxSum &sq, const float (&xp)[N],
+                                       const float (&xq)[N], int col0, float c)
+{
+    float vq = xq[0], vp = xp[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) {
+        vq = fmaxf(vq, xq[i]);
+        vp = fmaxf(vp, xp[i]);
+    }
+    if (vq > sq.m && sq.m != -INFINITY && sp.m != -INFINITY)
+        k.a += (double)(vq - sq.m) * (sp.s + 1.0);
+    if (vp > sp.m && sp.m != -INFINITY) {
+        const double f = (double)exp2_hw((sp.m - vp) * c);
+        k.a = f * (k.a - (double)(vp - sp.m) * (sp.s + 1.0));
+    }
+    ms_add(sq, xq, col0, c);
+    ms_add(sp, xp, col0, c);
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        acc = fmaf(exp2_hw((xp[i] - sp.m) * c), (xp[i] - sp.m) - (xq[i] - sq.m), acc);
+    k.a += (double)acc;
+}
+
+// Merge lane b's (P, Q, A) into lane a's: both A are brought to the merged
+// maxima first.
+__device__ __forceinline__ void kl_merge(KlAcc &ka, MaxSum &pa, MaxSum &qa, KlAcc kb, MaxSum pb,
+                                         MaxSum qb, float c)
+{
+    const float Mp = fmaxf(pa.m, pb.m), Mq = fmaxf(qa.m, qb.m);
+    double A = 0.0;
+    if (pa.m != -INFINITY)
+        A += (double)exp2_hw((pa.m - Mp) * c) *
+             (ka.a + ((double)(Mq - qa.m) - (double)(Mp - pa.m)) * (pa.s + 1.0));
+    if (pb.m != -INFINITY)
+        A += (double)exp2_hw((pb.m - Mp) * c) *
+             (kb.a + ((double)(Mq - qb.m) - (double)(Mp - pb.m)) * (pb.s + 1.0));
+    ka.a = A;
+    pa = ms_merge(pa, pb, c);
+    qa = ms_merge(qa, qb, c);
+}
+
+template <int BLOCK>
+__device__ __forceinline__ void kl_block(KlAcc &k, MaxSum &sp, MaxSum &sq, float c,
+                                         MaxSum *shp, MaxSum *shq, double *sha)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        KlAcc kb;
+        kb.a = __shfl_xor(k.a, o);
+        kl_merge(k, sp, sq, kb, ms_shfl(sp, o), ms_shfl(sq, o), c);
+    }
+    const int w = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        shp[w] = sp;
+        shq[w] = sq;
+        sha[w] = k.a;
+    }
+    __syncthreads();
+    sp = shp[0];
+    sq = shq[0];
+    k.a = sha[0];
+#pragma unroll
+    for (int i = 1; i < BLOCK / kWave; ++i)
+        kl_merge(k, sp, sq, KlAcc{sha[i]}, shp[i], shq[i], c);
+    __syncthreads();
 }
 
 // Per-row constants of pass 2 and of the backward.
@@ -227,8 +310,42 @@ __global__ __launch_bounds__(kJB) void k_jsd_forward(JsdArgs a)
     const int64_t V = a.vocab, nv = a.vec ? V / VE : 0;   // rows not 16-byte aligned: scalar
     const float c = a.c, inv_t = a.inv_t;
 
-    // pass 1: maxima, argmaxes, sums of the others
     MaxSum ss = ms_empty(), st = ms_empty();
+    if constexpr (MODE != 2) {
+        // the KL ends: one pass (P = teacher at beta = 0, student at beta = 1)
+        __shared__ MaxSum sh_q[kJB / kWave];
+        __shared__ double sh_a[kJB / kWave];
+        MaxSum &sp = MODE == 0 ? st : ss, &sq = MODE == 0 ? ss : st;
+        KlAcc k{0.0};
+        for (int64_t v = tid; v < nv; v += kJB) {
+            float xs[VE], xt[VE];
+            load_vec<DT>(rs, v, xs, true);
+            load_vec<DT>(rt, v, xt, true);
+            if constexpr (MODE == 0)
+                kl_add(k, sp, sq, xt, xs, (int)(v * VE), c);
+            else
+                kl_add(k, sp, sq, xs, xt, (int)(v * VE), c);
+        }
+        for (int64_t j = nv * VE + tid; j < V; j += kJB) {
+            const float xs[1] = {load_one<DT>(rs, j)}, xt[1] = {load_one<DT>(rt, j)};
+            if constexpr (MODE == 0)
+                kl_add(k, sp, sq, xt, xs, (int)j, c);
+            else
+                kl_add(k, sp, sq, xs, xt, (int)j, c);
+        }
+        kl_block<kJB>(k, sp, sq, c, sh_ms, sh_q, sh_a);
+        if (tid == 0) {
+            const double ls0d = log1p(ss.s), lt0d = log1p(st.s);
+            const double W = sp.s + 1.0, dl = ls0d - lt0d;
+            const double loss = k.a / W * (double)inv_t + (MODE == 0 ? dl : -dl);
+            a.loss[r] = (float)loss;
+            *sv = cev_jsd_saved{ss.m, (float)ls0d, st.m, (float)lt0d,
+                                MODE == 1 ? (float)loss : 0.0f, ss.col, 1, (float)dl};
+        }
+        return;
+    }
+
+    // pass 1: maxima, argmaxes, sums of the others
     for (int64_t v = tid; v < nv; v += kJB) {
         float xs[VE], xt[VE];
         load_vec<DT>(rs, v, xs, false);
