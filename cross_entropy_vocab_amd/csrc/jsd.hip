@@ -144,11 +144,12 @@ __device__ __forceinline__ void kl_add(KlAcc &k, MaxSum &sp, MaxSum &sq, const f
         vq = fmaxf(vq, xq[i]);
         vp = fmaxf(vp, xp[i]);
     }
+    // (the shifts are differences of two floats, exact in fp64)
     if (vq > sq.m && sq.m != -INFINITY && sp.m != -INFINITY)
-        k.a += (double)(vq - sq.m) * (sp.s + 1.0);
+        k.a += ((double)vq - (double)sq.m) * (sp.s + 1.0);
     if (vp > sp.m && sp.m != -INFINITY) {
         const double f = (double)exp2_hw((sp.m - vp) * c);
-        k.a = f * (k.a - (double)(vp - sp.m) * (sp.s + 1.0));
+        k.a = f * (k.a - ((double)vp - (double)sp.m) * (sp.s + 1.0));
     }
     ms_add(sq, xq, col0, c);
     ms_add(sp, xp, col0, c);
@@ -168,10 +169,10 @@ __device__ __forceinline__ void kl_merge(KlAcc &ka, MaxSum &pa, MaxSum &qa, KlAc
     double A = 0.0;
     if (pa.m != -INFINITY)
         A += (double)exp2_hw((pa.m - Mp) * c) *
-             (ka.a + ((double)(Mq - qa.m) - (double)(Mp - pa.m)) * (pa.s + 1.0));
+             (ka.a + (((double)Mq - qa.m) - ((double)Mp - pa.m)) * (pa.s + 1.0));
     if (pb.m != -INFINITY)
         A += (double)exp2_hw((pb.m - Mp) * c) *
-             (kb.a + ((double)(Mq - qb.m) - (double)(Mp - pb.m)) * (pb.s + 1.0));
+             (kb.a + (((double)Mq - qb.m) - ((double)Mp - pb.m)) * (pb.s + 1.0));
     ka.a = A;
     pa = ms_merge(pa, pb, c);
     qa = ms_merge(qa, qb, c);
