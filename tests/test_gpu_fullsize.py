@@ -329,3 +329,43 @@ def test_jsd_full_2048x151936_bf16(distill_full, beta):
                row_mask=w["row_mask"][rows], g=w["g"][rows], temperature=1.0)
     wl, wd = check(sub, dict(loss=loss[rows], dstudent=dsel), beta, "full jsd")
     say(f"  sampled {rows.size} rows; worst loss error / bound {wl:.3f}, dstudent {wd:.3f}")
+
+
+def test_grpo_full_fused():
+    """ce_fused (g known up front) on the full grpo workload, in the launch
+    configuration bench.py times: every row agrees with ce_forward +
+    ce_backward (log p to 1e-6 relative, argmax exactly), every gradient row
+    sums to zero, masked rows are zero; sampled
+    rows against the oracle."""
+    from gpu_helpers import DEV, say, to_dev, to_host
+    import cross_entropy_vocab_amd as cev
+    say("[full] ce_fused grpo 8192x152064 bf16")
+    w = workloads.grpo()
+    R, V = w["logits"].shape
+    logits, labels = to_dev(w["logits"]), to_dev(w["labels"])
+    mask, g = to_dev(w["row_mask"]), to_dev(w["g"])
+    out = cev.ce_fused(logits, labels, g, 1.0, row_mask=mask, argmax=True)
+    torch.cuda.synchronize()
+    dl = out["dlogits"]
+    two = cev.ce_forward(logits, labels, 1.0, row_mask=mask, argmax=True)
+    torch.cuda.synchronize()
+    logp, logp2 = to_host(out["logp"]), to_host(two["logp"])
+    assert_close("fused vs two calls logp", logp, logp2.astype(np.float64), 1e-6)
+    assert np.array_equal(to_host(out["argmax"]), to_host(two["argmax"]))
+    vr, _ = oracle.valid_rows(w["labels"], w["row_mask"], V)
+    n = vr.size
+    valid = np.zeros(R, bool)
+    valid[vr] = True
+    _row_sums_ok(dl, RTOL["bf16"]["dlogits"])
+    assert bool((dl[torch.from_numpy(np.flatnonzero(~valid)).to(DEV)] == 0).all())
+    rows = _sample_rows(np.random.default_rng(13), valid, 16, 4)
+    ref = oracle.ce_rows(w["logits"], w["labels"], 1.0, row_mask=w["row_mask"], rows_list=rows,
+                         want_entropy=False)
+    assert_close("fused logp", logp[rows], ref["logp"][rows], RTOL["bf16"]["logp"])
+    dsel = to_host(dl[torch.from_numpy(rows).to(DEV)])
+    g64 = np.asarray(w["g"], np.float64)
+    for i, r in enumerate(rows):
+        dref = oracle.ce_grad_rows(w["logits"], w["labels"], g64, 1.0, row_mask=w["row_mask"],
+                                   r0=int(r), r1=int(r) + 1)[0]
+        assert_close(f"fused dlogits row {r}", dsel[i], dref, RTOL["bf16"]["dlogits"], FLOOR)
+    say(f"  {n} valid rows; sampled {rows.size}")
