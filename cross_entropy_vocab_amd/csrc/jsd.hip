@@ -458,11 +458,11 @@ template <int DT> __device__ __forceinline__ void store_one(char *row, int64_t j
         reinterpret_cast<unsigned short *>(row)[j] = to_bf16(d);
 }
 
-template <int DT, int MODE>
-__global__ __launch_bounds__(kJB) void k_jsd_backward(JsdArgs a)
+template <int DT, int MODE, int BB = kJB>
+__global__ __launch_bounds__(BB) void k_jsd_backward(JsdArgs a)
 {
     constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize;
-    __shared__ double sh_d[kJB / kWave];
+    __shared__ double sh_d[BB / kWave];
     const int tid = threadIdx.x;
     const int64_t r = blockIdx.x;
     const int64_t V = a.vocab, nv = a.vec ? V / VE : 0;
@@ -472,9 +472,9 @@ __global__ __launch_bounds__(kJB) void k_jsd_backward(JsdArgs a)
     const cev_jsd_saved sv = a.saved_in[r];
     if (masked || !(sv.flags & 1)) {   // no record from the forward: a zero row
         const float z[VE] = {};
-        for (int64_t v = tid; v < nv; v += kJB)
+        for (int64_t v = tid; v < nv; v += BB)
             store_vec<DT>(rd, v, z);
-        for (int64_t j = nv * VE + tid; j < V; j += kJB)
+        for (int64_t j = nv * VE + tid; j < V; j += BB)
             store_one<DT>(rd, j, 0.0f);
         return;
     }
@@ -488,7 +488,7 @@ __global__ __launch_bounds__(kJB) void k_jsd_backward(JsdArgs a)
     const float es = rc.ls2 - lw - (MODE == 0 ? 0.0f : 24.0f), et = rc.lt2 - lw;
     const unsigned sgn = __float_as_uint(gr) & 0x80000000u;
     double sum = 0.0;
-    for (int64_t v = tid; v < nv; v += kJB) {
+    for (int64_t v = tid; v < nv; v += BB) {
         float xs[VE], xt[VE], d[VE];
         load_vec<DT>(rs, v, xs, true);
         load_vec<DT>(rt, v, xt, true);
@@ -496,13 +496,13 @@ __global__ __launch_bounds__(kJB) void k_jsd_backward(JsdArgs a)
                          d, sum);
         store_vec<DT>(rd, v, d);
     }
-    for (int64_t j = nv * VE + tid; j < V; j += kJB) {
+    for (int64_t j = nv * VE + tid; j < V; j += BB) {
         const float xs[1] = {load_one<DT>(rs, j)}, xt[1] = {load_one<DT>(rt, j)};
         float d[1];
         grad_terms<MODE>(xs, xt, rc, es, et, c, inv_t, a.beta, sv.k, sgn, (int)j, sv.arg, d, sum);
         store_one<DT>(rd, j, d[0]);
     }
-    sum = block_sum<kJB>(sum, sh_d);   // ends with a barrier: every store above is done
+    sum = block_sum<BB>(sum, sh_d);   // ends with a barrier: every store above is done
     if (tid == 0)
         store_one<DT>(rd, sv.arg, (float)(-sum));
 }

@@ -369,3 +369,47 @@ def test_grpo_full_fused():
                                    r0=int(r), r1=int(r) + 1)[0]
         assert_close(f"fused dlogits row {r}", dsel[i], dref, RTOL["bf16"]["dlogits"], FLOOR)
     say(f"  {n} valid rows; sampled {rows.size}")
+
+
+def test_longest_rows_2p27_bf16():
+    """Rows of V = 2^27 + 5 bf16 columns (index arithmetic far past 2^26, a
+    ragged tail, ce_forward's split-row path with few rows): 3 rows, one
+    ignored, one peaked by 30 with its target in the last (tail) column, one
+    with its target past 2^26.  Forward outputs against the oracle on every
+    row; dlogits against the oracle's full gradient rows at 2^20 random
+    columns plus the target and the tail, and zero row sums."""
+    from gpu_helpers import DEV, say, to_dev, to_host
+    import cross_entropy_vocab_amd as cev
+    V = (1 << 27) + 5
+    say(f"[full] 3 rows x {V} bf16")
+    rng = np.random.default_rng(27)
+    z = np.empty((3, V), np.float32)
+    for r in range(3):
+        z[r] = 3.0 * rng.standard_normal(V, dtype=np.float32)
+    labels = np.array([V - 1, -100, (1 << 26) + 12345], np.int64)
+    z[0, V - 1] = z[0].max() + 30.0
+    w = dict(logits=workloads.bf16_bits(z), labels=labels, row_mask=None, temperature=1.0,
+             g=np.array([0.8, 1.0, -1.3], np.float32))
+    del z
+    logits, lab = to_dev(w["logits"]), to_dev(labels)
+    g = to_dev(w["g"])
+    out = cev.ce_forward(logits, lab, 1.0, entropy=True, argmax=True)
+    dl = cev.ce_backward(logits, lab, g, out["saved"], 1.0)
+    torch.cuda.synchronize()
+    ref = oracle.ce_rows(w["logits"], labels, 1.0)
+    tol = RTOL["bf16"]
+    assert_close("logp", to_host(out["logp"]), ref["logp"], tol["logp"])
+    assert_close("loss", to_host(out["loss"]), ref["loss"], tol["loss"])
+    assert_close("entropy", to_host(out["entropy"]), ref["entropy"], tol["entropy"], 1e-30)
+    assert np.array_equal(to_host(out["argmax"]), ref["argmax"])
+    assert to_host(out["loss"])[0] > 0
+    _row_sums_ok(dl, tol["dlogits"])
+    assert bool((dl[1] == 0).all())
+    cols = np.unique(np.concatenate([rng.integers(0, V, 1 << 20), [0, V - 5, V - 1, labels[2]]]))
+    cidx = torch.from_numpy(cols).to(DEV)
+    g64 = np.asarray(w["g"], np.float64)
+    for r in (0, 2):
+        dref = oracle.ce_grad_rows(w["logits"], labels, g64, 1.0, r0=r, r1=r + 1)[0]
+        got = to_host(dl[r][cidx])
+        assert_close(f"dlogits row {r}", got, dref[cols], tol["dlogits"], FLOOR)
+        del dref
