@@ -326,8 +326,8 @@ def main():
         write_traffic(*args.traffic_from, rows=args.rows, vocab=args.vocab)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(rows shard across GPUs with no communication; see the design notes).",
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(rows shard across GPUs with no communication inside the op).",
               file=sys.stderr)
         sys.exit(2)
 
