@@ -29,7 +29,7 @@ STATUS_BAD_LABEL = 1
 STATUS_BAD_INDEX = 2
 STATUS_BAD_PARTS = 4
 SAVED_BYTES = 16
-JSD_SAVED_BYTES = 32
+JSD_SAVED_BYTES = 48
 PARTIAL_BYTES = 48
 PART_ENTROPY = 1
 PART_VALUE_SUM = 2
@@ -406,7 +406,7 @@ def jsd_forward(student, teacher, temperature=1.0, beta=0.5, labels=None, row_ma
     """Generalized JSD per row between softmax(student / T) and
     softmax(teacher / T) (beta = 0: KL(teacher || student), beta = 1:
     KL(student || teacher)).  Returns a dict: loss [rows] fp32 and saved
-    [rows, 32] uint8 (for jsd_backward)."""
+    [rows, 48] uint8 (for jsd_backward)."""
     rows, vocab, ss, ts = _jsd_pair(student, teacher)
     dev = student.device
     _dev(labels, "labels", torch.int64, (rows,), dev)

@@ -27,9 +27,18 @@
 //                   second sweep.  At the two KL ends the loss is accumulated
 //                   in the same pass against the running maxima (KlAcc); in
 //                   between, pass 2 re-reads both rows and sums the loss terms
-//                   in fp64.  Writes the loss and a 32-byte record per row.
-//   k_jsd_backward  one workgroup per row, one read of both rows, one write of
-//                   the student gradient; the argmax entry is written last.
+//                   in fp64.  Writes the loss and a 48-byte record per row,
+//                   which at beta < 1 also holds the student-argmax entry of
+//                   the gradient (minus the fp64 sum of the others) unless
+//                   the row is so peaked that those sums lose terms below the
+//                   fp32 range that matter.
+//   k_jsd_bwd_tiles one-shot slices of 8192 columns (beta < 1, 16-byte
+//                   aligned rows): every entry elementwise, the argmax entry
+//                   from the record; rows without it are left to
+//   k_jsd_backward  one workgroup per row (beta = 1, unaligned rows, or the
+//                   rows above): one read of both rows, one write of the
+//                   gradient, the argmax entry written last from the row's
+//                   own sum.
 #include "cev_device.h"
 #include "cev_launch.h"
 
@@ -256,13 +265,14 @@ template <int DT> __device__ __forceinline__ float load_one(const char *row, int
         return bf16_lo(reinterpret_cast<const unsigned short *>(row)[j]);
 }
 
-// Loss terms of n columns: adds to L (and K for the mixture).
+// Loss terms of n columns: adds to L (and, for the mixture, to K and to
+// G3 = sum_j ps_j (r_j - r_a), r_a the gap at the student's argmax).
 template <int MODE, int N>
 __device__ __forceinline__ void loss_terms(const float (&zs)[N], const float (&zt)[N],
                                            const JsdRow &rc, float c, float inv_t, float beta,
-                                           double &L, double &K)
+                                           float ra, double &L, double &K, double &G3)
 {
-    float l = 0.0f, k = 0.0f;
+    float l = 0.0f, k = 0.0f, k3 = 0.0f;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         const float as = zs[i] - rc.ms, at = zt[i] - rc.mt;
@@ -280,14 +290,28 @@ __device__ __forceinline__ void loss_terms(const float (&zs)[N], const float (&z
             mix_gaps(delta, beta, r, q);
             l = fmaf(beta * pt, q, l);
             k = fmaf(ps, r, k);
+            k3 = fmaf(ps, r - ra, k3);
         }
     }
     L += (double)l;
-    if constexpr (MODE == 2)
+    if constexpr (MODE == 2) {
         K += (double)k;
+        G3 += (double)k3;
+    }
 }
 
 // ------------------------------------------------------------------ forward
+// The forward's fp32 terms (e^((z - m)/T) in the sums of the others, the
+// probabilities in pass 2) are lost below 2^-126.
+// The argmax entry it forms from them is kept only when the student's mass
+// off its argmax, g0, is at least V 2^-80: the V dropped terms then move it by
+// under 2^-46 of g0 (for mixture gaps r up to 10^6 in size, under 2^-26),
+// far inside the error of the terms themselves.
+__device__ __forceinline__ bool garg_usable(double g0, int64_t V)
+{
+    return g0 >= (double)V * 0x1p-80;
+}
+
 template <int DT, int MODE>
 __global__ __launch_bounds__(kJB) void k_jsd_forward(JsdArgs a)
 {
@@ -302,7 +326,9 @@ __global__ __launch_bounds__(kJB) void k_jsd_forward(JsdArgs a)
     if (masked) {
         if (tid == 0) {
             a.loss[r] = 0.0f;
-            *sv = cev_jsd_saved{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, -1, 0, 0.0f};
+            cev_jsd_saved rec{};
+            rec.arg = -1;
+            *sv = rec;
         }
         return;
     }
@@ -340,8 +366,33 @@ __global__ __launch_bounds__(kJB) void k_jsd_forward(JsdArgs a)
             const double W = sp.s + 1.0, dl = ls0d - lt0d;
             const double loss = k.a / W * (double)inv_t + (MODE == 0 ? dl : -dl);
             a.loss[r] = (float)loss;
-            *sv = cev_jsd_saved{ss.m, (float)ls0d, st.m, (float)lt0d,
-                                MODE == 1 ? (float)loss : 0.0f, ss.col, 1, (float)dl};
+            // beta = 0: the argmax entry is sum_{j != a} pt_j - sum_{j != a} ps_j, both
+            // sums formed without cancellation (the teacher's from its own maximum
+            // sum when its argmax is the same column, else as 1 - pt_a < 1/2)
+            double garg = 0.0;
+            if constexpr (MODE == 0) {
+                const double g0 = ss.s / (1.0 + ss.s);
+                double gt;
+                if (ss.col == st.col) {
+                    gt = st.s / (1.0 + st.s);
+                } else {
+                    const double lta = ((double)load_one<DT>(rt, ss.col) - (double)st.m) *
+                                           (double)inv_t - lt0d;
+                    gt = -expm1(lta);
+                }
+                garg = gt - g0;
+            }
+            cev_jsd_saved rec{};
+            rec.ms = ss.m;
+            rec.ls0 = (float)ls0d;
+            rec.mt = st.m;
+            rec.lt0 = (float)lt0d;
+            rec.k = MODE == 1 ? (float)loss : 0.0f;
+            rec.garg = (float)garg;
+            rec.arg = ss.col;
+            rec.flags = (MODE == 0 && garg_usable(ss.s / (1.0 + ss.s), V)) ? 3 : 1;
+            rec.dl = (float)dl;
+            *sv = rec;
         }
         return;
     }
@@ -365,32 +416,48 @@ __global__ __launch_bounds__(kJB) void k_jsd_forward(JsdArgs a)
     const float ls0 = (float)ls0d, lt0 = (float)lt0d, dl0 = (float)(ls0d - lt0d);
     const JsdRow rc = jsd_row(ss.m, ls0, st.m, lt0, dl0);
 
+    // the mixture gap at the student's argmax, in the same fp32 steps as the
+    // terms: with K = sum_j ps_j r_j, sum_{j != a} ps_j (r_j - K) equals
+    // ps_a sum_j ps_j (r_j - r_a), in which every column whose gap rounds to
+    // r_a's (all of them on a saturated row) contributes exactly 0
+    float ra, qa;
+    {
+        const float at = load_one<DT>(rt, ss.col) - rc.mt, as = 0.0f;
+        mix_gaps(fmaf(at - as, inv_t, rc.dl0), (float)a.beta, ra, qa);
+    }
+
     // pass 2: the loss terms
-    double L = 0.0, K = 0.0;
+    double L = 0.0, K = 0.0, G3 = 0.0;
     for (int64_t v = tid; v < nv; v += kJB) {
         float xs[VE], xt[VE];
         load_vec<DT>(rs, v, xs, true);
         load_vec<DT>(rt, v, xt, true);
-        loss_terms<MODE>(xs, xt, rc, c, inv_t, a.beta, L, K);
+        loss_terms<MODE>(xs, xt, rc, c, inv_t, a.beta, ra, L, K, G3);
     }
     for (int64_t j = nv * VE + tid; j < V; j += kJB) {
         const float xs[1] = {load_one<DT>(rs, j)}, xt[1] = {load_one<DT>(rt, j)};
-        loss_terms<MODE>(xs, xt, rc, c, inv_t, a.beta, L, K);
+        loss_terms<MODE>(xs, xt, rc, c, inv_t, a.beta, ra, L, K, G3);
     }
     L = block_sum<kJB>(L, sh_d);
-    if constexpr (MODE == 2)
-        K = block_sum<kJB>(K, sh_d);
+    K = block_sum<kJB>(K, sh_d);
+    G3 = block_sum<kJB>(G3, sh_d);
     if (tid == 0) {
         const double beta = a.beta;
-        double loss = L, kk = 0.0;
-        if constexpr (MODE == 1)
-            kk = L;
-        if constexpr (MODE == 2) {
-            loss = L + (1.0 - beta) * K;
-            kk = K;
-        }
+        const double loss = L + (1.0 - beta) * K;
+        // the argmax entry: -(1 - beta) ps_a G3
+        const double g0 = ss.s / (1.0 + ss.s);
         a.loss[r] = (float)loss;
-        *sv = cev_jsd_saved{ss.m, ls0, st.m, lt0, (float)kk, ss.col, 1, dl0};
+        cev_jsd_saved rec{};
+        rec.ms = ss.m;
+        rec.ls0 = ls0;
+        rec.mt = st.m;
+        rec.lt0 = lt0;
+        rec.k = (float)K;
+        rec.garg = (float)(-(1.0 - beta) * G3 / (1.0 + ss.s));
+        rec.arg = ss.col;
+        rec.flags = garg_usable(g0, V) ? 3 : 1;
+        rec.dl = dl0;
+        *sv = rec;
     }
 }
 
@@ -458,7 +525,9 @@ template <int DT> __device__ __forceinline__ void store_one(char *row, int64_t j
         reinterpret_cast<unsigned short *>(row)[j] = to_bf16(d);
 }
 
-template <int DT, int MODE, int BB = kJB>
+// REST: after k_jsd_bwd_tiles, only the valid rows whose record has no
+// argmax entry.
+template <int DT, int MODE, int BB = kJB, bool REST = false>
 __global__ __launch_bounds__(BB) void k_jsd_backward(JsdArgs a)
 {
     constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize;
@@ -470,6 +539,8 @@ __global__ __launch_bounds__(BB) void k_jsd_backward(JsdArgs a)
     const bool masked = (a.row_mask && a.row_mask[r] == 0) ||
                         (a.labels && a.labels[r] == a.ignore_index);
     const cev_jsd_saved sv = a.saved_in[r];
+    if (REST && (masked || (sv.flags & 3) != 1))
+        return;
     if (masked || !(sv.flags & 1)) {   // no record from the forward: a zero row
         const float z[VE] = {};
         for (int64_t v = tid; v < nv; v += BB)
@@ -507,6 +578,80 @@ __global__ __launch_bounds__(BB) void k_jsd_backward(JsdArgs a)
         store_one<DT>(rd, sv.arg, (float)(-sum));
 }
 
+// One-shot slices (beta < 1, every row 16-byte aligned): workgroup b handles
+// vectors [per sl, per (sl + 1)) of row b / slices, plus the row's tail
+// columns in its last slice; the argmax entry comes from the record.
+constexpr int kTB = 256, kTU = 4;
+
+template <int DT, int MODE>
+__global__ __launch_bounds__(kTB) void k_jsd_bwd_tiles(JsdArgs a, int slices, int64_t per)
+{
+    constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize;
+    const int tid = threadIdx.x;
+    const int64_t r = blockIdx.x / slices;
+    const int sl = (int)(blockIdx.x % slices);
+    const int64_t V = a.vocab, nv = V / VE;
+    const int64_t v0 = (int64_t)sl * per, v1 = v0 + per < nv ? v0 + per : nv;
+    char *rd = static_cast<char *>(a.dstudent) + (size_t)r * (size_t)a.d_stride * ES;
+    u32x4 *dvp = reinterpret_cast<u32x4 *>(rd);
+    const bool masked = (a.row_mask && a.row_mask[r] == 0) ||
+                        (a.labels && a.labels[r] == a.ignore_index);
+    const cev_jsd_saved sv = a.saved_in[r];
+    if (!masked && (sv.flags & 3) == 1)
+        return;   // valid, no argmax entry in the record: the per-row kernel's
+    if (masked || !(sv.flags & 1)) {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        for (int64_t j = v0 + tid; j < v1; j += kTB)
+            store16_stream(zero, dvp + j);
+        if (sl == slices - 1 && nv * VE + tid < V)
+            store_one<DT>(rd, nv * VE + tid, 0.0f);
+        return;
+    }
+    const char *rs = static_cast<const char *>(a.student) + (size_t)r * (size_t)a.s_stride * ES;
+    const char *rt = static_cast<const char *>(a.teacher) + (size_t)r * (size_t)a.t_stride * ES;
+    const float c = a.c, inv_t = a.inv_t;
+    const JsdRow rc = jsd_row(sv.ms, sv.ls0, sv.mt, sv.lt0, sv.dl);
+    const float gr = a.g[r];
+    const float wabs = fabsf(gr) * inv_t * (MODE == 2 ? (float)(1.0 - a.beta) : 1.0f);
+    const float lw = __log2f(wabs);
+    const float es = rc.ls2 - lw - (MODE == 0 ? 0.0f : 24.0f), et = rc.lt2 - lw;
+    const unsigned sgn = __float_as_uint(gr) & 0x80000000u;
+    const float darg = gr * inv_t * sv.garg;
+    double unused = 0.0;
+    for (int64_t base = v0 + tid; base < v1; base += (int64_t)kTB * kTU) {
+        float xs[kTU][VE], xt[kTU][VE];
+#pragma unroll
+        for (int u = 0; u < kTU; ++u) {
+            const int64_t j = base + (int64_t)u * kTB;
+            if (j < v1) {
+                load_vec<DT>(rs, j, xs[u], true);
+                load_vec<DT>(rt, j, xt[u], true);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kTU; ++u) {
+            const int64_t j = base + (int64_t)u * kTB;
+            if (j < v1) {
+                float d[VE];
+                const int col0 = (int)(j * VE);
+                grad_terms<MODE>(xs[u], xt[u], rc, es, et, c, inv_t, a.beta, sv.k, sgn, col0,
+                                 sv.arg, d, unused);
+                if (sv.arg >= col0 && sv.arg < col0 + VE)
+                    d[sv.arg - col0] = darg;
+                store_vec<DT>(rd, j, d);
+            }
+        }
+    }
+    if (sl == slices - 1 && nv * VE + tid < V) {
+        const int64_t j = nv * VE + tid;
+        const float xs[1] = {load_one<DT>(rs, j)}, xt[1] = {load_one<DT>(rt, j)};
+        float d[1];
+        grad_terms<MODE>(xs, xt, rc, es, et, c, inv_t, a.beta, sv.k, sgn, (int)j, sv.arg, d,
+                         unused);
+        store_one<DT>(rd, j, j == sv.arg ? darg : d[0]);
+    }
+}
+
 template <int DT>
 void launch_fwd_t(const JsdArgs &a, int mode, hipStream_t s)
 {
@@ -522,6 +667,24 @@ void launch_fwd_t(const JsdArgs &a, int mode, hipStream_t s)
 template <int DT>
 void launch_bwd_t(const JsdArgs &a, int mode, hipStream_t s)
 {
+    if (mode != 1 && a.vec) {
+        const int64_t nv = a.vocab / Elem<DT>::kVE;
+        int64_t per = (int64_t)kTB * kTU;
+        int64_t slices = nv > 0 ? (nv + per - 1) / per : 1;
+        while ((uint64_t)a.rows * (uint64_t)slices * kTB > 0xFFFFFFFFull && slices > 1) {
+            per *= 2;
+            slices = (nv + per - 1) / per;
+        }
+        const dim3 tgrid((unsigned)(a.rows * slices)), tblock(kTB), grid((unsigned)a.rows);
+        if (mode == 0) {
+            hipLaunchKernelGGL((k_jsd_bwd_tiles<DT, 0>), tgrid, tblock, 0, s, a, (int)slices, per);
+            hipLaunchKernelGGL((k_jsd_backward<DT, 0, kJB, true>), grid, tblock, 0, s, a);
+        } else {
+            hipLaunchKernelGGL((k_jsd_bwd_tiles<DT, 2>), tgrid, tblock, 0, s, a, (int)slices, per);
+            hipLaunchKernelGGL((k_jsd_backward<DT, 2, kJB, true>), grid, tblock, 0, s, a);
+        }
+        return;
+    }
     const dim3 grid((unsigned)a.rows), block(kJB);
     if (mode == 0)
         hipLaunchKernelGGL((k_jsd_backward<DT, 0>), grid, block, 0, s, a);

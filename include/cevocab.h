@@ -424,19 +424,22 @@ size_t lce_workspace_size(int64_t rows, int64_t hidden_dim, int64_t vocab);
  * Deterministic: fixed reduction order, no float atomics.
  */
 
-/* Per-row record of jsd_forward, read by jsd_backward: 32 bytes. */
+/* Per-row record of jsd_forward, read by jsd_backward: 48 bytes. */
 typedef struct cev_jsd_saved {
     float ms;      /* largest stored student logit */
     float ls0;     /* log1p(sum over the student's other columns of e^{(z - ms)/T}) */
     float mt;      /* largest stored teacher logit */
     float lt0;     /* the same for the teacher */
     float k;       /* the loss at beta = 1, sum P_s log(P_s / M) in between, 0 at beta = 0 */
+    float garg;    /* the gradient entry at the student's argmax per unit of g/T (minus
+                      the fp64 sum of the others), when flags bit 1 is set */
     int32_t arg;   /* the student's argmax column (first occurrence), -1 if masked */
-    int32_t flags; /* bit 0: row valid */
+    int32_t flags; /* bit 0: row valid; bit 1: garg holds */
     float dl;      /* ls0 - lt0 formed in fp64, then rounded */
+    float pad[3];
 } cev_jsd_saved;
 
-/* jsd_forward -- loss [rows] fp32 and saved [rows] x 32 bytes (16-byte
+/* jsd_forward -- loss [rows] fp32 and saved [rows] x 48 bytes (16-byte
  * aligned), both required. */
 int jsd_forward(const void *student, const void *teacher, int64_t rows, int64_t vocab,
                 int64_t student_stride, int64_t teacher_stride, int dtype,

@@ -31,7 +31,7 @@ def _row_sums_ok(dl: torch.Tensor, tol, chunk=256):
         s = d.sum(1).abs()
         bound = tol * d.abs().sum(1) + V * FLOOR
         bad = s > bound
-        assert not bool(bad.any()), f"rows {a + torch.nonzero(bad).flatten()[:5].tolist()}"
+        assert not bool(bad.any()), f"rows {[a + i for i in torch.nonzero(bad).flatten()[:5].tolist()]}"
 
 
 def _ce_full(w, entropy, tol, sample_valid=24, sample_invalid=4, seed=0):

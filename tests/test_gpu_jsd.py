@@ -195,8 +195,8 @@ def test_jsd_tiny_vocab_and_ties():
     for beta in BETAS:
         got = run_jsd(w, beta)
         check(w, got, beta, "ties")
-        sv = got["saved"].view(np.int32).reshape(6, 8)
-        assert list(sv[:3, 5]) == [3, 0, 7]
+        sv = got["saved"].view(np.int32).reshape(6, 12)
+        assert list(sv[:3, 6]) == [3, 0, 7]
     say("[jsd] ties ok")
 
 
@@ -219,11 +219,15 @@ def test_jsd_strides_masks_and_zero_sums():
 
 def test_jsd_peaked_rows_keep_signal():
     """Rows peaked by 20-80 with the teacher peaked elsewhere: the loss is
-    large and positive and the gradient moves mass off the student's peak;
-    with the teacher peaked at the same column the gradient is tiny, zero-sum
-    and not exactly zero (no collapse)."""
+    large and positive and the gradient moves mass off the student's peak
+    (wherever the error bound resolves that entry's sign: in between the KL
+    ends a nearly disjoint pair is at the loss's maximum, where the gradient
+    vanishes to far below the size of its terms); with the teacher peaked at
+    the same column the gradient is tiny, zero-sum and not exactly zero (no
+    collapse)."""
     w = workloads.distill(rows=32, vocab=151936, dtype="f32", peaked_frac=1.0)
     w = dict(w, labels=None, row_mask=None)
+    T = w["temperature"]
     for beta in BETAS:
         got = run_jsd(w, beta)
         check(w, got, beta, "peaked")
@@ -233,7 +237,14 @@ def test_jsd_peaked_rows_keep_signal():
         d = got["dstudent"]
         a = np.argmax(zs, 1)
         if beta < 1.0:
-            assert np.all(d[~same, :][np.arange((~same).sum()), a[~same]] > 0), beta
+            resolved = 0
+            for r in np.nonzero(~same)[0]:
+                _, _, dref, bd = row_bounds(w["student"][r], w["teacher"][r],
+                                            float(w["g"][r]), T, beta)
+                if dref[a[r]] > bd[a[r]] + 2 * FLOOR:
+                    assert d[r, a[r]] > 0, (beta, r, d[r, a[r]], dref[a[r]])
+                    resolved += 1
+            assert resolved >= (~same).sum() // 2, (beta, resolved)
         assert np.all(np.abs(d[same]).max(1) > 0), beta
         if beta in (0.0, 1.0):
             assert np.all(got["loss"][~same] > 1.0), beta
@@ -250,3 +261,42 @@ def test_jsd_determinism():
         b = run_jsd(w, beta)
         for k in ("loss", "dstudent", "saved"):
             assert np.array_equal(a[k], b[k]), (beta, k)
+
+
+def test_jsd_record_carries_argmax_entry():
+    """The forward stores the student-argmax gradient entry (per unit of g/T)
+    for beta < 1 unless the student's mass off its argmax is below V 2^-80,
+    where the fp32 sums behind it lose terms; the backward then takes those
+    rows one workgroup each.  Checked against the oracle's mass and entry."""
+    w = workloads.distill(rows=40, vocab=3001, dtype="f32", peaked_frac=0.5)
+    w = dict(w, labels=None, row_mask=None)
+    V = 3001
+    T = w["temperature"]
+    for beta in BETAS:
+        got = run_jsd(w, beta)
+        check(w, got, beta, "record")
+        rec = got["saved"].view(np.int32).reshape(40, 12)
+        flags = rec[:, 7]
+        garg = got["saved"].view(np.float32).reshape(40, 12)[:, 5]
+        seen = set()
+        for r in range(40):
+            zs, zt = w["student"][r], w["teacher"][r]
+            _, _, ls, _, _ = oj.jsd_row(zs, zt, T, beta)
+            a = int(np.argmax(oj._widen(zs)))
+            g0 = -np.expm1(ls[a])
+            assert flags[r] & 1, (beta, r)
+            if beta == 1.0:
+                assert not flags[r] & 2, (beta, r)
+                continue
+            lim = V * 2.0 ** -80
+            if g0 >= 2 * lim:
+                assert flags[r] & 2, (beta, r, g0)
+                # g = T: the entry per unit of g/T, against the entry's error bound
+                _, _, dref, bd = row_bounds(zs, zt, T, T, beta)
+                assert abs(garg[r] - dref[a]) <= 1.2e-7 * abs(dref[a]) + bd[a] + FLOOR, (beta, r)
+                seen.add(True)
+            elif g0 <= lim / 2:
+                assert not flags[r] & 2, (beta, r, g0)
+                seen.add(False)
+        if beta < 1.0:
+            assert seen == {True, False}, (beta, seen)
