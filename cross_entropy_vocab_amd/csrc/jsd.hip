@@ -467,14 +467,18 @@ __global__ __launch_bounds__(kJB) void k_jsd_forward(JsdArgs a)
 // the probability is then multiplied by a factor (beta > 0: up to a few
 // hundred) it is formed 2^24 too large and scaled back exactly after the
 // product, so an entry is flushed to zero only when it is itself below the
-// fp32 normal range; the sign of g is applied to the bits.
+// fp32 normal range; the sign of g is applied to the bits (beta = 0) or to
+// the scale 2^-24.  EXCL: the student's argmax column gets 0 and the entries
+// are summed into sum (the per-row kernel); otherwise every column is written
+// as computed and the caller replaces the argmax one.
 constexpr float kPre = 16777216.0f, kPreInv = 1.0f / 16777216.0f;   // 2^24, 2^-24
-template <int MODE, int N>
+template <int MODE, bool EXCL, int N>
 __device__ __forceinline__ void grad_terms(const float (&zs)[N], const float (&zt)[N],
                                            const JsdRow &rc, float es, float et, float c,
                                            float inv_t, float beta, float kk, unsigned sgn,
                                            int col0, int arg, float (&out)[N], double &sum)
 {
+    const float post = __uint_as_float(__float_as_uint(kPreInv) ^ sgn);
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -483,23 +487,26 @@ __device__ __forceinline__ void grad_terms(const float (&zs)[N], const float (&z
         float d;
         if constexpr (MODE == 0) {
             d = pw - exp2_hw(fmaf(at, c, -et));
+            d = __uint_as_float(__float_as_uint(d) ^ sgn);
         } else {
             const float delta = fmaf(at - as, inv_t, rc.dl0);   // lt - ls
             if constexpr (MODE == 1) {
-                d = (pw * (-delta - kk)) * kPreInv;
+                d = (pw * (-delta - kk)) * post;
             } else {
                 float r, q;
                 mix_gaps(delta, beta, r, q);
-                d = (pw * (r - kk)) * kPreInv;
+                d = (pw * (r - kk)) * post;
             }
         }
-        d = __uint_as_float(__float_as_uint(d) ^ sgn);
-        if (col0 + i == arg)
-            d = 0.0f;
-        acc += d;
+        if constexpr (EXCL) {
+            if (col0 + i == arg)
+                d = 0.0f;
+            acc += d;
+        }
         out[i] = d;
     }
-    sum += (double)acc;
+    if constexpr (EXCL)
+        sum += (double)acc;
 }
 
 template <int DT> __device__ __forceinline__ void store_vec(char *row, int64_t v, const float *d)
@@ -563,14 +570,15 @@ __global__ __launch_bounds__(BB) void k_jsd_backward(JsdArgs a)
         float xs[VE], xt[VE], d[VE];
         load_vec<DT>(rs, v, xs, true);
         load_vec<DT>(rt, v, xt, true);
-        grad_terms<MODE>(xs, xt, rc, es, et, c, inv_t, a.beta, sv.k, sgn, (int)(v * VE), sv.arg,
-                         d, sum);
+        grad_terms<MODE, true>(xs, xt, rc, es, et, c, inv_t, a.beta, sv.k, sgn, (int)(v * VE),
+                               sv.arg, d, sum);
         store_vec<DT>(rd, v, d);
     }
     for (int64_t j = nv * VE + tid; j < V; j += BB) {
         const float xs[1] = {load_one<DT>(rs, j)}, xt[1] = {load_one<DT>(rt, j)};
         float d[1];
-        grad_terms<MODE>(xs, xt, rc, es, et, c, inv_t, a.beta, sv.k, sgn, (int)j, sv.arg, d, sum);
+        grad_terms<MODE, true>(xs, xt, rc, es, et, c, inv_t, a.beta, sv.k, sgn, (int)j, sv.arg, d,
+                               sum);
         store_one<DT>(rd, j, d[0]);
     }
     sum = block_sum<BB>(sum, sh_d);   // ends with a barrier: every store above is done
@@ -634,11 +642,13 @@ __global__ __launch_bounds__(kTB) void k_jsd_bwd_tiles(JsdArgs a, int slices, in
             if (j < v1) {
                 float d[VE];
                 const int col0 = (int)(j * VE);
-                grad_terms<MODE>(xs[u], xt[u], rc, es, et, c, inv_t, a.beta, sv.k, sgn, col0,
-                                 sv.arg, d, unused);
-                if (sv.arg >= col0 && sv.arg < col0 + VE)
-                    d[sv.arg - col0] = darg;
+                grad_terms<MODE, false>(xs[u], xt[u], rc, es, et, c, inv_t, a.beta, sv.k, sgn,
+                                        col0, sv.arg, d, unused);
                 store_vec<DT>(rd, j, d);
+                // the one lane holding the argmax column overwrites it (a later
+                // store of the same work-item to the same address)
+                if ((unsigned)(sv.arg - col0) < (unsigned)VE)
+                    store_one<DT>(rd, sv.arg, darg);
             }
         }
     }
@@ -646,8 +656,8 @@ __global__ __launch_bounds__(kTB) void k_jsd_bwd_tiles(JsdArgs a, int slices, in
         const int64_t j = nv * VE + tid;
         const float xs[1] = {load_one<DT>(rs, j)}, xt[1] = {load_one<DT>(rt, j)};
         float d[1];
-        grad_terms<MODE>(xs, xt, rc, es, et, c, inv_t, a.beta, sv.k, sgn, (int)j, sv.arg, d,
-                         unused);
+        grad_terms<MODE, false>(xs, xt, rc, es, et, c, inv_t, a.beta, sv.k, sgn, (int)j, sv.arg,
+                                d, unused);
         store_one<DT>(rd, j, j == sv.arg ? darg : d[0]);
     }
 }
