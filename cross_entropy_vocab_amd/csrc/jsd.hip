@@ -57,34 +57,6 @@ struct MaxSum {
 
 __device__ __forceinline__ MaxSum ms_empty() { return MaxSum{-INFINITY, INT32_MAX, 0.0}; }
 
-// Add n consecutive values starting at column col0.
-template <int N>
-__device__ __forceinline__ void ms_add(MaxSum &st, const float (&v)[N], int col0, float c)
-{
-    float vm = v[0];
-    int vi = 0;
-#pragma unroll
-    for (int i = 1; i < N; ++i)
-        if (v[i] > vm) {
-            vm = v[i];
-            vi = i;
-        }
-    int excl = -1;
-    if (vm > st.m) {
-        const double carry = st.m == -INFINITY ? 0.0 : 1.0;   // the old maximum's own term
-        st.s = (st.s + carry) * (double)exp2_hw((st.m - vm) * c);
-        st.m = vm;
-        st.col = col0 + vi;
-        excl = vi;
-    }
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        if (i != excl)
-            acc += exp2_hw((v[i] - st.m) * c);
-    st.s += (double)acc;
-}
-
 // Merge two states: the larger maximum wins (then the lower column); the
 // loser's maximum element becomes one of the others.
 __device__ __forceinline__ MaxSum ms_merge(MaxSum a, MaxSum b, float c)
@@ -103,21 +75,88 @@ __device__ __forceinline__ MaxSum ms_merge(MaxSum a, MaxSum b, float c)
     return a;
 }
 
-__device__ __forceinline__ MaxSum ms_shfl(const MaxSum &a, int o)
+// The sweeps keep the running maximum wave-uniform: every lane of a wave holds
+// the same m and col (the largest value the wave has seen and its first
+// column) and its own share s of the sum over the other columns; lane 0 also
+// holds the terms of earlier maxima.  A step moves m only when some lane sees
+// a larger value -- a scalar branch taken about ln(steps) times per row --
+// and otherwise adds its terms with no per-column test.  The loops are
+// wave-convergent: in a step where some lanes have no column (MASK), those
+// lanes add nothing.
+
+// Largest of n values (-inf for a lane without a column).
+template <int N>
+__device__ __forceinline__ float vec_max(const float (&v)[N])
 {
-    MaxSum b;
-    b.m = __shfl_xor(a.m, o);
-    b.col = __shfl_xor(a.col, o);
-    b.s = __shfl_xor(a.s, o);
-    return b;
+    float m = v[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i)
+        m = fmaxf(m, v[i]);
+    return m;
 }
 
+// Move the wave's maximum to m2 = the largest value of this step (larger than
+// st.m), at its lowest column: every lane's share is scaled by
+// f = 2^((m - m2) c) and lane 0 adds the old maximum's own term f.  Returns
+// the index of m2's column among this lane's n values, or -1.
+template <int N>
+__device__ __forceinline__ int wm_move(MaxSum &st, const float (&v)[N], float vm, int col0,
+                                       float c, bool lane0)
+{
+    const float m2 = wave_max(fmaxf(vm, st.m));
+    int64_t mine = INT32_MAX;
+    if (vm == m2) {
+#pragma unroll
+        for (int i = N - 1; i >= 0; --i)
+            if (v[i] == m2)
+                mine = col0 + i;
+    }
+    const int c2 = (int)wave_min(mine);
+    if (st.m != -INFINITY) {
+        const double f = (double)exp2_hw((st.m - m2) * c);
+        st.s = st.s * f + (lane0 ? f : 0.0);
+    }
+    st.m = m2;
+    st.col = c2;
+    const int e = c2 - col0;
+    return (e >= 0 && e < N) ? e : -1;
+}
+
+// One step of a sweep over one row: n values from column col0.
+template <bool MASK, int N>
+__device__ __forceinline__ void ms_step(MaxSum &st, const float (&v)[N], int col0, float c,
+                                        bool lane0, bool valid)
+{
+    float vm = vec_max(v);
+    if (MASK && !valid)
+        vm = -INFINITY;
+    int ex = -1;
+    const bool rise = __any(vm > st.m);
+    if (rise)
+        ex = wm_move(st, v, vm, col0, c, lane0);
+    if (MASK && !valid)
+        return;
+    float acc = 0.0f;
+    if (rise) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const float t = exp2_hw((v[i] - st.m) * c);
+            acc += i == ex ? 0.0f : t;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            acc += exp2_hw((v[i] - st.m) * c);
+    }
+    st.s += (double)acc;
+}
+
+// The row's state from the waves' states: the lanes of a wave share m and
+// col, so their shares add; waves merge through LDS.
 template <int BLOCK>
 __device__ __forceinline__ MaxSum ms_block(MaxSum st, float c, MaxSum *sh)
 {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1)
-        st = ms_merge(st, ms_shfl(st, o), c);
+    st.s = wave_sum(st.s);
     const int w = threadIdx.x / kWave;
     if ((threadIdx.x & (kWave - 1)) == 0)
         sh[w] = st;
@@ -139,34 +178,69 @@ __device__ __forceinline__ MaxSum ms_block(MaxSum st, float c, MaxSum *sh)
 // every weight shrinks by e^(-d/T) and every bracket by d:
 // A = e^(-d/T) (A - d W).  The column of each row's own maximum contributes
 // exactly 0 to its bracket, so a peaked row loses nothing to cancellation.
+// Each lane holds its share of A; W's share is the lane's s (plus the
+// maximum's own term 1 in lane 0).
 struct KlAcc {
     double a;
 };
 
-template <int N>
-__device__ __forceinline__ void kl_add(KlAcc &k, MaxSum &sp, MaxSum &sq, const float (&xp)[N],
-                                       const float (&xq)[N], int col0, float c)
+// The terms of n columns; EX: column ep of P and eq of Q (the maxima, when
+// they moved in this step) are left out of the sums.  The weight
+// 2^((zP - mP) c) of each column serves both P's sum and A.
+template <bool EX, int N>
+__device__ __forceinline__ void kl_terms(KlAcc &k, MaxSum &sp, MaxSum &sq, const float (&xp)[N],
+                                         const float (&xq)[N], float c, int ep, int eq)
 {
-    float vq = xq[0], vp = xp[0];
+    float accp = 0.0f, accq = 0.0f, acca = 0.0f;
 #pragma unroll
-    for (int i = 1; i < N; ++i) {
-        vq = fmaxf(vq, xq[i]);
-        vp = fmaxf(vp, xp[i]);
+    for (int i = 0; i < N; ++i) {
+        const float ap = xp[i] - sp.m, aq = xq[i] - sq.m;
+        const float wp = exp2_hw(ap * c), wq = exp2_hw(aq * c);
+        accp += (EX && i == ep) ? 0.0f : wp;
+        accq += (EX && i == eq) ? 0.0f : wq;
+        acca = fmaf(wp, ap - aq, acca);
+        // one column's chain at a time: the other waves on the SIMD hide its
+        // latency, and the live registers stay within 8 waves per SIMD
+        __builtin_amdgcn_sched_barrier(0);
     }
-    // (the shifts are differences of two floats, exact in fp64)
-    if (vq > sq.m && sq.m != -INFINITY && sp.m != -INFINITY)
-        k.a += ((double)vq - (double)sq.m) * (sp.s + 1.0);
-    if (vp > sp.m && sp.m != -INFINITY) {
-        const double f = (double)exp2_hw((sp.m - vp) * c);
-        k.a = f * (k.a - ((double)vp - (double)sp.m) * (sp.s + 1.0));
+    sp.s += (double)accp;
+    sq.s += (double)accq;
+    k.a += (double)acca;
+}
+
+// One step of the single pass: n values of P and Q from column col0.
+template <bool MASK, int N>
+__device__ __forceinline__ void kl_step(KlAcc &k, MaxSum &sp, MaxSum &sq, const float (&xp)[N],
+                                        const float (&xq)[N], int col0, float c, bool lane0,
+                                        bool valid)
+{
+    float vp = vec_max(xp), vq = vec_max(xq);
+    if (MASK && !valid) {
+        vp = -INFINITY;
+        vq = -INFINITY;
     }
-    ms_add(sq, xq, col0, c);
-    ms_add(sp, xp, col0, c);
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        acc = fmaf(exp2_hw((xp[i] - sp.m) * c), (xp[i] - sp.m) - (xq[i] - sq.m), acc);
-    k.a += (double)acc;
+    int ep = -1, eq = -1;
+    const bool rq = __any(vq > sq.m), rp = __any(vp > sp.m);
+    if (rq) {
+        // (the shifts are differences of two floats, exact in fp64)
+        const float mq0 = sq.m;
+        eq = wm_move(sq, xq, vq, col0, c, lane0);
+        if (mq0 != -INFINITY && sp.m != -INFINITY)
+            k.a += ((double)sq.m - (double)mq0) * (sp.s + (lane0 ? 1.0 : 0.0));
+    }
+    if (rp) {
+        const float mp0 = sp.m;
+        const double w0 = sp.s + (lane0 ? 1.0 : 0.0);
+        ep = wm_move(sp, xp, vp, col0, c, lane0);
+        if (mp0 != -INFINITY)
+            k.a = (double)exp2_hw((mp0 - sp.m) * c) * (k.a - ((double)sp.m - (double)mp0) * w0);
+    }
+    if (MASK && !valid)
+        return;
+    if (rq || rp)
+        kl_terms<true>(k, sp, sq, xp, xq, c, ep, eq);
+    else
+        kl_terms<false>(k, sp, sq, xp, xq, c, -1, -1);
 }
 
 // Merge lane b's (P, Q, A) into lane a's: both A are brought to the merged
@@ -191,12 +265,9 @@ template <int BLOCK>
 __device__ __forceinline__ void kl_block(KlAcc &k, MaxSum &sp, MaxSum &sq, float c,
                                          MaxSum *shp, MaxSum *shq, double *sha)
 {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-        KlAcc kb;
-        kb.a = __shfl_xor(k.a, o);
-        kl_merge(k, sp, sq, kb, ms_shfl(sp, o), ms_shfl(sq, o), c);
-    }
+    sp.s = wave_sum(sp.s);
+    sq.s = wave_sum(sq.s);
+    k.a = wave_sum(k.a);
     const int w = threadIdx.x / kWave;
     if ((threadIdx.x & (kWave - 1)) == 0) {
         shp[w] = sp;
@@ -257,12 +328,76 @@ __device__ __forceinline__ void load_vec(const char *row, int64_t v, float (&out
     unpack16<DT>(w, out);
 }
 
+template <int DT> __device__ __forceinline__ u32x4 load_raw(const char *row, int64_t v, bool stream)
+{
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(row) + v;
+    return stream ? load16_stream(p) : *p;
+}
+
+template <bool B> struct Flag {
+    static constexpr bool value = B;
+};
+
+// Visit the 16-byte vectors tid, tid + kJB, ... < nv of both rows in a
+// wave-convergent loop (every thread takes the same number of steps), with
+// the next pair's loads issued before the current pair's arithmetic.
+// f(xs, xt, col0, Flag<MASK>, valid): MASK only in the last step, where a
+// thread past the end has valid = false and undefined values.
+template <int DT, bool STREAM, class F>
+__device__ __forceinline__ void sweep_pairs(const char *rs, const char *rt, int64_t nv, int tid,
+                                            F &&f)
+{
+    constexpr int VE = Elem<DT>::kVE;
+    const int64_t steps = (nv + kJB - 1) / kJB;
+    int64_t v = tid;
+    u32x4 cs = {0u, 0u, 0u, 0u}, ct = cs;
+    if (steps > 0 && v < nv) {
+        cs = load_raw<DT>(rs, v, STREAM);
+        ct = load_raw<DT>(rt, v, STREAM);
+    }
+    for (int64_t k = 0; k + 1 < steps; ++k) {   // every thread has a vector
+        const int64_t vn = v + kJB;
+        u32x4 ns = cs, nt = ct;
+        if (vn < nv) {
+            ns = load_raw<DT>(rs, vn, STREAM);
+            nt = load_raw<DT>(rt, vn, STREAM);
+        }
+        float xs[VE], xt[VE];
+        unpack16<DT>(cs, xs);
+        unpack16<DT>(ct, xt);
+        f(xs, xt, (int)(v * VE), Flag<false>{}, true);
+        cs = ns;
+        ct = nt;
+        v = vn;
+    }
+    if (steps > 0) {   // the last step, outside the loop
+        float xs[VE], xt[VE];
+        unpack16<DT>(cs, xs);
+        unpack16<DT>(ct, xt);
+        f(xs, xt, (int)(v * VE), Flag<true>{}, v < nv);
+    }
+}
+
 template <int DT> __device__ __forceinline__ float load_one(const char *row, int64_t j)
 {
     if constexpr (DT == CEV_F32)
         return reinterpret_cast<const float *>(row)[j];
     else
         return bf16_lo(reinterpret_cast<const unsigned short *>(row)[j]);
+}
+
+// Columns j0 .. V-1 one at a time, in the same wave-convergent form.
+template <int DT, class F>
+__device__ __forceinline__ void sweep_tail(const char *rs, const char *rt, int64_t j0, int64_t V,
+                                           int tid, F &&f)
+{
+    for (int64_t b = j0; b < V; b += kJB) {
+        const int64_t j = b + tid;
+        const bool valid = j < V;
+        const float xs[1] = {valid ? load_one<DT>(rs, j) : 0.0f};
+        const float xt[1] = {valid ? load_one<DT>(rt, j) : 0.0f};
+        f(xs, xt, (int)j, Flag<true>{}, valid);
+    }
 }
 
 // Loss terms of n columns: adds to L (and, for the mixture, to K and to
@@ -313,7 +448,7 @@ __device__ __forceinline__ bool garg_usable(double g0, int64_t V)
 }
 
 template <int DT, int MODE>
-__global__ __launch_bounds__(kJB) void k_jsd_forward(JsdArgs a)
+__global__ __launch_bounds__(kJB) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_jsd_forward(JsdArgs a)
 {
     constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize;
     __shared__ MaxSum sh_ms[kJB / kWave];
@@ -336,6 +471,7 @@ __global__ __launch_bounds__(kJB) void k_jsd_forward(JsdArgs a)
     const char *rt = static_cast<const char *>(a.teacher) + (size_t)r * (size_t)a.t_stride * ES;
     const int64_t V = a.vocab, nv = a.vec ? V / VE : 0;   // rows not 16-byte aligned: scalar
     const float c = a.c, inv_t = a.inv_t;
+    const bool lane0 = (tid & (kWave - 1)) == 0;
 
     MaxSum ss = ms_empty(), st = ms_empty();
     if constexpr (MODE != 2) {
@@ -344,22 +480,14 @@ __global__ __launch_bounds__(kJB) void k_jsd_forward(JsdArgs a)
         __shared__ double sh_a[kJB / kWave];
         MaxSum &sp = MODE == 0 ? st : ss, &sq = MODE == 0 ? ss : st;
         KlAcc k{0.0};
-        for (int64_t v = tid; v < nv; v += kJB) {
-            float xs[VE], xt[VE];
-            load_vec<DT>(rs, v, xs, true);
-            load_vec<DT>(rt, v, xt, true);
+        const auto step = [&](const auto &xs, const auto &xt, int col0, auto mask, bool valid) {
             if constexpr (MODE == 0)
-                kl_add(k, sp, sq, xt, xs, (int)(v * VE), c);
+                kl_step<decltype(mask)::value>(k, sp, sq, xt, xs, col0, c, lane0, valid);
             else
-                kl_add(k, sp, sq, xs, xt, (int)(v * VE), c);
-        }
-        for (int64_t j = nv * VE + tid; j < V; j += kJB) {
-            const float xs[1] = {load_one<DT>(rs, j)}, xt[1] = {load_one<DT>(rt, j)};
-            if constexpr (MODE == 0)
-                kl_add(k, sp, sq, xt, xs, (int)j, c);
-            else
-                kl_add(k, sp, sq, xs, xt, (int)j, c);
-        }
+                kl_step<decltype(mask)::value>(k, sp, sq, xs, xt, col0, c, lane0, valid);
+        };
+        sweep_pairs<DT, true>(rs, rt, nv, tid, step);
+        sweep_tail<DT>(rs, rt, nv * VE, V, tid, step);
         kl_block<kJB>(k, sp, sq, c, sh_ms, sh_q, sh_a);
         if (tid == 0) {
             const double ls0d = log1p(ss.s), lt0d = log1p(st.s);
@@ -398,18 +526,12 @@ __global__ __launch_bounds__(kJB) void k_jsd_forward(JsdArgs a)
     }
 
     // pass 1: maxima, argmaxes, sums of the others
-    for (int64_t v = tid; v < nv; v += kJB) {
-        float xs[VE], xt[VE];
-        load_vec<DT>(rs, v, xs, false);
-        load_vec<DT>(rt, v, xt, false);
-        ms_add(ss, xs, (int)(v * VE), c);
-        ms_add(st, xt, (int)(v * VE), c);
-    }
-    for (int64_t j = nv * VE + tid; j < V; j += kJB) {
-        const float xs[1] = {load_one<DT>(rs, j)}, xt[1] = {load_one<DT>(rt, j)};
-        ms_add(ss, xs, (int)j, c);
-        ms_add(st, xt, (int)j, c);
-    }
+    const auto step1 = [&](const auto &xs, const auto &xt, int col0, auto mask, bool valid) {
+        ms_step<decltype(mask)::value>(ss, xs, col0, c, lane0, valid);
+        ms_step<decltype(mask)::value>(st, xt, col0, c, lane0, valid);
+    };
+    sweep_pairs<DT, false>(rs, rt, nv, tid, step1);
+    sweep_tail<DT>(rs, rt, nv * VE, V, tid, step1);
     ss = ms_block<kJB>(ss, c, sh_ms);
     st = ms_block<kJB>(st, c, sh_ms);
     const double ls0d = log1p(ss.s), lt0d = log1p(st.s);
@@ -428,12 +550,11 @@ __global__ __launch_bounds__(kJB) void k_jsd_forward(JsdArgs a)
 
     // pass 2: the loss terms
     double L = 0.0, K = 0.0, G3 = 0.0;
-    for (int64_t v = tid; v < nv; v += kJB) {
-        float xs[VE], xt[VE];
-        load_vec<DT>(rs, v, xs, true);
-        load_vec<DT>(rt, v, xt, true);
-        loss_terms<MODE>(xs, xt, rc, c, inv_t, a.beta, ra, L, K, G3);
-    }
+    sweep_pairs<DT, true>(rs, rt, nv, tid, [&](const float (&xs)[VE], const float (&xt)[VE],
+                                               int, auto, bool valid) {
+        if (valid)
+            loss_terms<MODE>(xs, xt, rc, c, inv_t, a.beta, ra, L, K, G3);
+    });
     for (int64_t j = nv * VE + tid; j < V; j += kJB) {
         const float xs[1] = {load_one<DT>(rs, j)}, xt[1] = {load_one<DT>(rt, j)};
         loss_terms<MODE>(xs, xt, rc, c, inv_t, a.beta, ra, L, K, G3);
