@@ -293,10 +293,14 @@ def bench_jsd(args, torch, cev, workloads, dev):
                                  "backward_GBps": bwd_bytes / (b_ms / 1e3) / 1e9,
                                  "rows_per_s": R / ((f_ms + b_ms) / 1e3)}
         log(f"[bench] jsd beta={beta:g}: forward {f_ms:.3f} ms, backward {b_ms:.3f} ms")
-    bb = res["beta_0.5"]
-    res["roofline"] = {"bound": "hbm", "kernel": "k_jsd_backward (beta 0.5)", "unit": "GB/s",
+    # the backward at beta = 0 (k_jsd_bwd_tiles) is bound by HBM; the
+    # forwards and the backward in between are bound by VALU issue
+    bb = res["beta_0"]
+    res["roofline"] = {"bound": "hbm", "kernel": "k_jsd_bwd_tiles (beta 0)", "unit": "GB/s",
                        "achieved": bb["backward_GBps"], "peak": PEAK_HBM_GBS,
-                       "frac": bb["backward_GBps"] / PEAK_HBM_GBS}
+                       "frac": bb["backward_GBps"] / PEAK_HBM_GBS,
+                       "valu_bound": ["k_jsd_forward (every beta)",
+                                      "k_jsd_bwd_tiles (0 < beta < 1)"]}
     del st, te, dl
     torch.cuda.empty_cache()
     return res
