@@ -285,38 +285,41 @@ __device__ __forceinline__ void kl_block(KlAcc &k, MaxSum &sp, MaxSum &sq, float
 }
 
 // Per-row constants of pass 2 and of the backward.
+constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+constexpr double kLn2d = 0.69314718055994530942;
+
 struct JsdRow {
     float ms, mt;          // stored maxima
     float ls2, lt2;        // log1p(S_s), log1p(S_t) in log2 units
     float dl0;             // log1p(S_s) - log1p(S_t), rounded once from fp64
+    float dl2;             // the same in log2 units
+    float lt2b;            // lt2 - log2(beta): beta pt = 2^((zt - mt) c - lt2b)
 };
 
-__device__ __forceinline__ JsdRow jsd_row(float ms, float ls0, float mt, float lt0, float dl0)
+// l2b = log2(beta) as a float (0 where beta * pt is not needed).
+__device__ __forceinline__ JsdRow jsd_row(float ms, float ls0, float mt, float lt0, float dl0,
+                                          float l2b = 0.0f)
 {
-    constexpr float kLog2e = 1.4426950408889634f;
-    return JsdRow{ms, mt, ls0 * kLog2e, lt0 * kLog2e, dl0};
+    const float lt2 = lt0 * kLog2e;
+    return JsdRow{ms, mt, ls0 * kLog2e, lt2, dl0, dl0 * kLog2e, lt2 - l2b};
 }
 
-// The mixture's gaps r = ls - lm and q = lt - lm from delta = lt - ls:
+// The mixture's gaps in log2 units, r2 = (ls - lm)/ln2 and q2 = (lt - lm)/ln2,
+// from d2 = (lt - ls)/ln2:
 // beta e^lt + (1 - beta) e^ls = e^ls (1 + beta (e^delta - 1))
 //                             = e^lt (1 + (1 - beta) (e^-delta - 1)),
-// with the exponent never positive.  Hardware exp2 / log2 suffice: the
-// gaps then err by a few 1e-7 absolute, the size of the error the
-// log-probabilities they are built from already carry, and delta = 0 gives
-// exactly 0.
-__device__ __forceinline__ void mix_gaps(float delta, float beta, float &r, float &q)
+// with the exponent never positive.  Hardware exp2 / log2 suffice: the gaps
+// then err by a few 1e-7 absolute, the size of the error the
+// log-probabilities they are built from already carry, and d2 = 0 gives
+// exactly 0.  Forward and backward form r2 by these same fp32 steps, so a
+// column's gap rounds the same in both.
+__device__ __forceinline__ void mix_gaps2(float d2, float beta, float &r2, float &q2)
 {
-    constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
-    const float e = exp2_hw(-fabsf(delta) * kLog2e);
-    const float w = delta <= 0.0f ? beta : 1.0f - beta;
-    const float gap = -__builtin_amdgcn_logf(fmaf(w, e - 1.0f, 1.0f)) * kLn2;
-    if (delta <= 0.0f) {
-        r = gap;
-        q = delta + gap;
-    } else {
-        q = gap;
-        r = gap - delta;
-    }
+    const float e = exp2_hw(-fabsf(d2));
+    const float w = d2 <= 0.0f ? beta : 1.0f - beta;
+    const float g2 = -__builtin_amdgcn_logf(fmaf(w, e - 1.0f, 1.0f));
+    r2 = g2 - fmaxf(d2, 0.0f);
+    q2 = g2 + fminf(d2, 0.0f);
 }
 
 template <int DT>
@@ -400,39 +403,29 @@ __device__ __forceinline__ void sweep_tail(const char *rs, const char *rt, int64
     }
 }
 
-// Loss terms of n columns: adds to L (and, for the mixture, to K and to
-// G3 = sum_j ps_j (r_j - r_a), r_a the gap at the student's argmax).
-template <int MODE, int N>
-__device__ __forceinline__ void loss_terms(const float (&zs)[N], const float (&zt)[N],
-                                           const JsdRow &rc, float c, float inv_t, float beta,
-                                           float ra, double &L, double &K, double &G3)
+// The mixture's loss terms of n columns, in log2 units: adds sum beta pt q2
+// to L, sum ps r2 to K and G3 = sum ps (r2 - ra2), ra2 the gap at the
+// student's argmax.
+template <int N>
+__device__ __forceinline__ void mix_terms(const float (&zs)[N], const float (&zt)[N],
+                                          const JsdRow &rc, float c, float beta, float ra2,
+                                          double &L, double &K, double &G3)
 {
     float l = 0.0f, k = 0.0f, k3 = 0.0f;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         const float as = zs[i] - rc.ms, at = zt[i] - rc.mt;
-        const float delta = fmaf(at - as, inv_t, rc.dl0);   // lt - ls
-        if constexpr (MODE == 0) {
-            const float pt = exp2_hw(fmaf(at, c, -rc.lt2));
-            l = fmaf(pt, delta, l);
-        } else if constexpr (MODE == 1) {
-            const float ps = exp2_hw(fmaf(as, c, -rc.ls2));
-            l = fmaf(-ps, delta, l);
-        } else {
-            const float ps = exp2_hw(fmaf(as, c, -rc.ls2));
-            const float pt = exp2_hw(fmaf(at, c, -rc.lt2));
-            float r, q;
-            mix_gaps(delta, beta, r, q);
-            l = fmaf(beta * pt, q, l);
-            k = fmaf(ps, r, k);
-            k3 = fmaf(ps, r - ra, k3);
-        }
+        const float ps = exp2_hw(fmaf(as, c, -rc.ls2));
+        const float ptb = exp2_hw(fmaf(at, c, -rc.lt2b));   // beta pt
+        float r2, q2;
+        mix_gaps2(fmaf(at - as, c, rc.dl2), beta, r2, q2);
+        l = fmaf(ptb, q2, l);
+        k = fmaf(ps, r2, k);
+        k3 = fmaf(ps, r2 - ra2, k3);
     }
     L += (double)l;
-    if constexpr (MODE == 2) {
-        K += (double)k;
-        G3 += (double)k3;
-    }
+    K += (double)k;
+    G3 += (double)k3;
 }
 
 // ------------------------------------------------------------------ forward
@@ -536,36 +529,37 @@ __global__ __launch_bounds__(kJB) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     st = ms_block<kJB>(st, c, sh_ms);
     const double ls0d = log1p(ss.s), lt0d = log1p(st.s);
     const float ls0 = (float)ls0d, lt0 = (float)lt0d, dl0 = (float)(ls0d - lt0d);
-    const JsdRow rc = jsd_row(ss.m, ls0, st.m, lt0, dl0);
+    const JsdRow rc = jsd_row(ss.m, ls0, st.m, lt0, dl0, (float)log2(a.beta));
 
     // the mixture gap at the student's argmax, in the same fp32 steps as the
     // terms: with K = sum_j ps_j r_j, sum_{j != a} ps_j (r_j - K) equals
     // ps_a sum_j ps_j (r_j - r_a), in which every column whose gap rounds to
     // r_a's (all of them on a saturated row) contributes exactly 0
-    float ra, qa;
+    const float beta = (float)a.beta;
+    float ra2, qa2;
     {
         const float at = load_one<DT>(rt, ss.col) - rc.mt, as = 0.0f;
-        mix_gaps(fmaf(at - as, inv_t, rc.dl0), (float)a.beta, ra, qa);
+        mix_gaps2(fmaf(at - as, c, rc.dl2), beta, ra2, qa2);
     }
 
-    // pass 2: the loss terms
+    // pass 2: the loss terms (log2 units)
     double L = 0.0, K = 0.0, G3 = 0.0;
     sweep_pairs<DT, true>(rs, rt, nv, tid, [&](const float (&xs)[VE], const float (&xt)[VE],
                                                int, auto, bool valid) {
         if (valid)
-            loss_terms<MODE>(xs, xt, rc, c, inv_t, a.beta, ra, L, K, G3);
+            mix_terms(xs, xt, rc, c, beta, ra2, L, K, G3);
     });
     for (int64_t j = nv * VE + tid; j < V; j += kJB) {
         const float xs[1] = {load_one<DT>(rs, j)}, xt[1] = {load_one<DT>(rt, j)};
-        loss_terms<MODE>(xs, xt, rc, c, inv_t, a.beta, ra, L, K, G3);
+        mix_terms(xs, xt, rc, c, beta, ra2, L, K, G3);
     }
     L = block_sum<kJB>(L, sh_d);
     K = block_sum<kJB>(K, sh_d);
     G3 = block_sum<kJB>(G3, sh_d);
     if (tid == 0) {
         const double beta = a.beta;
-        const double loss = L + (1.0 - beta) * K;
-        // the argmax entry: -(1 - beta) ps_a G3
+        const double loss = kLn2d * (L + (1.0 - beta) * K);
+        // the argmax entry: -(1 - beta) ps_a G3 (G3 in log2 units)
         const double g0 = ss.s / (1.0 + ss.s);
         a.loss[r] = (float)loss;
         cev_jsd_saved rec{};
@@ -573,8 +567,8 @@ __global__ __launch_bounds__(kJB) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
         rec.ls0 = ls0;
         rec.mt = st.m;
         rec.lt0 = lt0;
-        rec.k = (float)K;
-        rec.garg = (float)(-(1.0 - beta) * G3 / (1.0 + ss.s));
+        rec.k = (float)K;   // log2 units
+        rec.garg = (float)(-(1.0 - beta) * kLn2d * G3 / (1.0 + ss.s));
         rec.arg = ss.col;
         rec.flags = garg_usable(g0, V) ? 3 : 1;
         rec.dl = dl0;
@@ -599,7 +593,9 @@ __device__ __forceinline__ void grad_terms(const float (&zs)[N], const float (&z
                                            float inv_t, float beta, float kk, unsigned sgn,
                                            int col0, int arg, float (&out)[N], double &sum)
 {
-    const float post = __uint_as_float(__float_as_uint(kPreInv) ^ sgn);
+    // the scale back from 2^24 (times ln 2 for the mixture, whose gaps are in
+    // log2 units), carrying the sign of g
+    const float post = __uint_as_float(__float_as_uint(MODE == 2 ? kLn2 * kPreInv : kPreInv) ^ sgn);
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -609,15 +605,13 @@ __device__ __forceinline__ void grad_terms(const float (&zs)[N], const float (&z
         if constexpr (MODE == 0) {
             d = pw - exp2_hw(fmaf(at, c, -et));
             d = __uint_as_float(__float_as_uint(d) ^ sgn);
-        } else {
+        } else if constexpr (MODE == 1) {
             const float delta = fmaf(at - as, inv_t, rc.dl0);   // lt - ls
-            if constexpr (MODE == 1) {
-                d = (pw * (-delta - kk)) * post;
-            } else {
-                float r, q;
-                mix_gaps(delta, beta, r, q);
-                d = (pw * (r - kk)) * post;
-            }
+            d = (pw * (-delta - kk)) * post;
+        } else {
+            float r2, q2;   // kk: K in log2 units
+            mix_gaps2(fmaf(at - as, c, rc.dl2), beta, r2, q2);
+            d = (pw * (r2 - kk)) * post;
         }
         if constexpr (EXCL) {
             if (col0 + i == arg)

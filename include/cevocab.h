@@ -430,7 +430,7 @@ typedef struct cev_jsd_saved {
     float ls0;     /* log1p(sum over the student's other columns of e^{(z - ms)/T}) */
     float mt;      /* largest stored teacher logit */
     float lt0;     /* the same for the teacher */
-    float k;       /* the loss at beta = 1, sum P_s log(P_s / M) in between, 0 at beta = 0 */
+    float k;       /* the loss at beta = 1; in between sum P_s log2(P_s / M) (base 2); 0 at beta = 0 */
     float garg;    /* the gradient entry at the student's argmax per unit of g/T (minus
                       the fp64 sum of the others), when flags bit 1 is set */
     int32_t arg;   /* the student's argmax column (first occurrence), -1 if masked */
