@@ -650,31 +650,47 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *P, int64_t s
     dst[3] = acc.w;
 }
 
-// D[c][r] = S[r][c] for r < R (zeros for R <= r < rp), c < C: 64 x 64 tiles
-// through LDS (grid: r tiles fastest).
-__global__ __launch_bounds__(256) void k_transpose(const unsigned short *S, int64_t lds_, int64_t R,
+// D[c][r] = S[r][c] for r < R (zeros for R <= r < rp), c < C.  Each lane
+// moves one 8 x 8 block in registers: eight 16-byte row pieces in, eight
+// 16-byte column pieces out, the 16-bit halves regrouped with shifts and
+// masks.  A wave covers 64 r x 64 c (lane = 8 r-blocks x 8 c-blocks), a
+// workgroup 256 r x 64 c.  Needs S rows 16-byte aligned with ld a multiple of
+// 8 and rp a multiple of 64; a piece past column C stays inside S's row when
+// ld >= round64(C) or C is a multiple of 64 (every caller), and D rows
+// c >= C are not written.
+__global__ __launch_bounds__(256) void k_transpose(const unsigned short *S, int64_t ld, int64_t R,
                                                    int64_t C, unsigned short *D, int64_t rp)
 {
-    __shared__ unsigned short t[64][65];
-    const int64_t rtiles = (rp + 63) / 64;
-    const int64_t r0 = (blockIdx.x % rtiles) * 64, c0 = (blockIdx.x / rtiles) * 64;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    for (int i = ty; i < 64; i += 4) {
-        const int64_t r = r0 + i, c = c0 + tx;
-        t[i][tx] = (r < R && c < C) ? S[r * lds_ + c] : (unsigned short)0;
+    const int64_t rtiles = (rp + 255) / 256;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t r = (blockIdx.x % rtiles) * 256 + w * 64 + (lane >> 3) * 8;
+    const int64_t c = (blockIdx.x / rtiles) * 64 + (lane & 7) * 8;
+    if (r >= rp)
+        return;
+    u32x4 in[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        in[k] = r + k < R ? *reinterpret_cast<const u32x4 *>(S + (r + k) * ld + c) : z;
     }
-    __syncthreads();
-    for (int i = ty; i < 64; i += 4) {
-        const int64_t c = c0 + i, r = r0 + tx;
-        if (c < C && r < rp)
-            D[c * rp + r] = t[tx][i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (c + j >= C)
+            break;
+        u32x4 o;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const unsigned x = in[2 * m][j >> 1], y = in[2 * m + 1][j >> 1];
+            o[m] = (j & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+        }
+        *reinterpret_cast<u32x4 *>(D + (c + j) * rp + r) = o;
     }
 }
 
 void launch_transpose(const unsigned short *S, int64_t ld, int64_t R, int64_t C,
                       unsigned short *D, int64_t rp, hipStream_t s)
 {
-    const int64_t tiles = ((rp + 63) / 64) * ((C + 63) / 64);
+    const int64_t tiles = ((rp + 255) / 256) * ((C + 63) / 64);
     hipLaunchKernelGGL(k_transpose, dim3((unsigned)tiles), dim3(256), 0, s, S, ld, R, C, D, rp);
 }
 
