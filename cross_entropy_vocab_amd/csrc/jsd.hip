@@ -313,11 +313,38 @@ __device__ __forceinline__ JsdRow jsd_row(float ms, float ls0, float mt, float l
 // log-probabilities they are built from already carry, and d2 = 0 gives
 // exactly 0.  Forward and backward form r2 by these same fp32 steps, so a
 // column's gap rounds the same in both.
-__device__ __forceinline__ void mix_gaps2(float d2, float beta, float &r2, float &q2)
+//
+// With w the weight of the larger probability's term (beta where d2 <= 0,
+// else 1 - beta) and c = 1 - w, the argument of the log is w e + c: one FMA
+// of two non-negative terms, good to fp32 precision relative to itself even
+// where it is as small as c (beta = 1e-6 with e near 0, where 1 + w (e - 1)
+// would lose both c, to w's rounding, and e, to the rounding of e - 1).  The
+// fp32 pair (beta, 1 - beta) is chosen so that it sums to exactly 1 in fp32,
+// so e = 1 gives exactly 1 and d2 = 0 a zero gap.
+struct MixW {
+    float b, b1;   // beta and 1 - beta in fp32, b + b1 == 1 exactly in fp32
+};
+
+__device__ __forceinline__ MixW mix_w(double beta)
+{
+    float b = (float)beta, b1 = (float)(1.0 - beta);
+    // the rounding errors of the pair are below 4.5e-8, so moving the larger
+    // by one ulp (6e-8) towards the deficit always reaches a sum of 1
+    const float sum = b + b1;
+    if (sum != 1.0f) {
+        float &big = b >= b1 ? b : b1;
+        // (both are positive and finite: one ulp is one step of the bits)
+        big = __uint_as_float(__float_as_uint(big) + (sum > 1.0f ? 0xFFFFFFFFu : 1u));
+    }
+    return MixW{b, b1};
+}
+
+__device__ __forceinline__ void mix_gaps2(float d2, const MixW &mw, float &r2, float &q2)
 {
     const float e = exp2_hw(-fabsf(d2));
-    const float w = d2 <= 0.0f ? beta : 1.0f - beta;
-    const float g2 = -__builtin_amdgcn_logf(fmaf(w, e - 1.0f, 1.0f));
+    const bool lo = d2 <= 0.0f;
+    const float w = lo ? mw.b : mw.b1, c = lo ? mw.b1 : mw.b;
+    const float g2 = -__builtin_amdgcn_logf(fmaf(w, e, c));
     r2 = g2 - fmaxf(d2, 0.0f);
     q2 = g2 + fminf(d2, 0.0f);
 }
@@ -408,7 +435,7 @@ __device__ __forceinline__ void sweep_tail(const char *rs, const char *rt, int64
 // student's argmax.
 template <int N>
 __device__ __forceinline__ void mix_terms(const float (&zs)[N], const float (&zt)[N],
-                                          const JsdRow &rc, float c, float beta, float ra2,
+                                          const JsdRow &rc, float c, const MixW &mw, float ra2,
                                           double &L, double &K, double &G3)
 {
     float l = 0.0f, k = 0.0f, k3 = 0.0f;
@@ -418,7 +445,7 @@ __device__ __forceinline__ void mix_terms(const float (&zs)[N], const float (&zt
         const float ps = exp2_hw(fmaf(as, c, -rc.ls2));
         const float ptb = exp2_hw(fmaf(at, c, -rc.lt2b));   // beta pt
         float r2, q2;
-        mix_gaps2(fmaf(at - as, c, rc.dl2), beta, r2, q2);
+        mix_gaps2(fmaf(at - as, c, rc.dl2), mw, r2, q2);
         l = fmaf(ptb, q2, l);
         k = fmaf(ps, r2, k);
         k3 = fmaf(ps, r2 - ra2, k3);
@@ -535,11 +562,11 @@ __global__ __launch_bounds__(kJB) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     // terms: with K = sum_j ps_j r_j, sum_{j != a} ps_j (r_j - K) equals
     // ps_a sum_j ps_j (r_j - r_a), in which every column whose gap rounds to
     // r_a's (all of them on a saturated row) contributes exactly 0
-    const float beta = (float)a.beta;
+    const MixW mw = mix_w(a.beta);
     float ra2, qa2;
     {
         const float at = load_one<DT>(rt, ss.col) - rc.mt, as = 0.0f;
-        mix_gaps2(fmaf(at - as, c, rc.dl2), beta, ra2, qa2);
+        mix_gaps2(fmaf(at - as, c, rc.dl2), mw, ra2, qa2);
     }
 
     // pass 2: the loss terms (log2 units)
@@ -547,11 +574,11 @@ __global__ __launch_bounds__(kJB) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
     sweep_pairs<DT, true>(rs, rt, nv, tid, [&](const float (&xs)[VE], const float (&xt)[VE],
                                                int, auto, bool valid) {
         if (valid)
-            mix_terms(xs, xt, rc, c, beta, ra2, L, K, G3);
+            mix_terms(xs, xt, rc, c, mw, ra2, L, K, G3);
     });
     for (int64_t j = nv * VE + tid; j < V; j += kJB) {
         const float xs[1] = {load_one<DT>(rs, j)}, xt[1] = {load_one<DT>(rt, j)};
-        mix_terms(xs, xt, rc, c, beta, ra2, L, K, G3);
+        mix_terms(xs, xt, rc, c, mw, ra2, L, K, G3);
     }
     L = block_sum<kJB>(L, sh_d);
     K = block_sum<kJB>(K, sh_d);
@@ -590,7 +617,7 @@ constexpr float kPre = 16777216.0f, kPreInv = 1.0f / 16777216.0f;   // 2^24, 2^-
 template <int MODE, bool EXCL, int N>
 __device__ __forceinline__ void grad_terms(const float (&zs)[N], const float (&zt)[N],
                                            const JsdRow &rc, float es, float et, float c,
-                                           float inv_t, float beta, float kk, unsigned sgn,
+                                           float inv_t, const MixW &mw, float kk, unsigned sgn,
                                            int col0, int arg, float (&out)[N], double &sum)
 {
     // the scale back from 2^24 (times ln 2 for the mixture, whose gaps are in
@@ -610,7 +637,7 @@ __device__ __forceinline__ void grad_terms(const float (&zs)[N], const float (&z
             d = (pw * (-delta - kk)) * post;
         } else {
             float r2, q2;   // kk: K in log2 units
-            mix_gaps2(fmaf(at - as, c, rc.dl2), beta, r2, q2);
+            mix_gaps2(fmaf(at - as, c, rc.dl2), mw, r2, q2);
             d = (pw * (r2 - kk)) * post;
         }
         if constexpr (EXCL) {
@@ -680,19 +707,20 @@ __global__ __launch_bounds__(BB) void k_jsd_backward(JsdArgs a)
     const float lw = __log2f(wabs);                  // -inf for g = 0: every entry 0
     const float es = rc.ls2 - lw - (MODE == 0 ? 0.0f : 24.0f), et = rc.lt2 - lw;
     const unsigned sgn = __float_as_uint(gr) & 0x80000000u;
+    const MixW mw = mix_w(a.beta);
     double sum = 0.0;
     for (int64_t v = tid; v < nv; v += BB) {
         float xs[VE], xt[VE], d[VE];
         load_vec<DT>(rs, v, xs, true);
         load_vec<DT>(rt, v, xt, true);
-        grad_terms<MODE, true>(xs, xt, rc, es, et, c, inv_t, a.beta, sv.k, sgn, (int)(v * VE),
+        grad_terms<MODE, true>(xs, xt, rc, es, et, c, inv_t, mw, sv.k, sgn, (int)(v * VE),
                                sv.arg, d, sum);
         store_vec<DT>(rd, v, d);
     }
     for (int64_t j = nv * VE + tid; j < V; j += BB) {
         const float xs[1] = {load_one<DT>(rs, j)}, xt[1] = {load_one<DT>(rt, j)};
         float d[1];
-        grad_terms<MODE, true>(xs, xt, rc, es, et, c, inv_t, a.beta, sv.k, sgn, (int)j, sv.arg, d,
+        grad_terms<MODE, true>(xs, xt, rc, es, et, c, inv_t, mw, sv.k, sgn, (int)j, sv.arg, d,
                                sum);
         store_one<DT>(rd, j, d[0]);
     }
@@ -739,6 +767,7 @@ __global__ __launch_bounds__(kTB) void k_jsd_bwd_tiles(JsdArgs a, int slices, in
     const float lw = __log2f(wabs);
     const float es = rc.ls2 - lw - (MODE == 0 ? 0.0f : 24.0f), et = rc.lt2 - lw;
     const unsigned sgn = __float_as_uint(gr) & 0x80000000u;
+    const MixW mw = mix_w(a.beta);
     const float darg = gr * inv_t * sv.garg;
     double unused = 0.0;
     for (int64_t base = v0 + tid; base < v1; base += (int64_t)kTB * kTU) {
@@ -757,7 +786,7 @@ __global__ __launch_bounds__(kTB) void k_jsd_bwd_tiles(JsdArgs a, int slices, in
             if (j < v1) {
                 float d[VE];
                 const int col0 = (int)(j * VE);
-                grad_terms<MODE, false>(xs[u], xt[u], rc, es, et, c, inv_t, a.beta, sv.k, sgn,
+                grad_terms<MODE, false>(xs[u], xt[u], rc, es, et, c, inv_t, mw, sv.k, sgn,
                                         col0, sv.arg, d, unused);
                 store_vec<DT>(rd, j, d);
                 // the one lane holding the argmax column overwrites it (a later
@@ -771,7 +800,7 @@ __global__ __launch_bounds__(kTB) void k_jsd_bwd_tiles(JsdArgs a, int slices, in
         const int64_t j = nv * VE + tid;
         const float xs[1] = {load_one<DT>(rs, j)}, xt[1] = {load_one<DT>(rt, j)};
         float d[1];
-        grad_terms<MODE, false>(xs, xt, rc, es, et, c, inv_t, a.beta, sv.k, sgn, (int)j, sv.arg,
+        grad_terms<MODE, false>(xs, xt, rc, es, et, c, inv_t, mw, sv.k, sgn, (int)j, sv.arg,
                                 d, unused);
         store_one<DT>(rd, j, j == sv.arg ? darg : d[0]);
     }

@@ -300,3 +300,16 @@ def test_jsd_record_carries_argmax_entry():
                 seen.add(False)
         if beta < 1.0:
             assert seen == {True, False}, (beta, seen)
+
+
+def test_jsd_near_end_betas():
+    """beta within 1e-6 of either end takes the mixture path: the teacher's
+    weight beta rides in its exponent as log2(1e-6), and 1 - beta folds into
+    the backward's exponent; both against the oracle's error model."""
+    from gpu_helpers import say
+    for name in ("distill_64x4099_f32_ragged", "distill_24x151936_bf16_peaked_T0.7"):
+        w = CASES[name]()
+        for beta in (1e-6, 1.0 - 1e-6):
+            got = run_jsd(w, beta)
+            wl, wd = check(w, got, beta, name)
+            say(f"[jsd] {name} beta={beta}: worst loss error / bound {wl:.3f}, dstudent {wd:.3f}")
