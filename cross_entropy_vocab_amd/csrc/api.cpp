@@ -347,6 +347,8 @@ int ce_backward(const void *logits, int64_t rows, int64_t vocab, int64_t row_str
     a.label_smoothing = label_smoothing;
     a.c = (float)(1.4426950408889634074 / temperature);
     a.inv_t = (float)(1.0 / temperature);
+    a.eps = (float)label_smoothing;
+    a.eps_over_v = (float)(label_smoothing / (double)vocab);
     a.status = status;
     return launch_status(cev::launch_backward(dtype, a, to_hip(stream)));
 }
@@ -582,6 +584,8 @@ int ce_vocab_shard_backward(const void *logits, int64_t rows, int64_t shard_voca
     a.label_smoothing = label_smoothing;
     a.c = (float)(1.4426950408889634074 / temperature);
     a.inv_t = (float)(1.0 / temperature);
+    a.eps = (float)label_smoothing;
+    a.eps_over_v = (float)(label_smoothing / (double)vocab);
     a.status = status;
     return launch_status(cev::launch_backward(dtype, a, to_hip(stream)));
 }

@@ -80,7 +80,7 @@ __device__ __forceinline__ float grad_scalar(float z, const RowConst &rc, float 
 // faster on MI355X than long per-row loops for this read-plus-write stream.
 // SHARD: the row holds global columns [col_offset, col_offset + vocab) of a
 // vocab_total-wide row (vocab-parallel form); otherwise the whole row.
-template <int DT, int BLOCK, int U, bool SHARD>
+template <int DT, int BLOCK, int U, bool SHARD, bool SNT>
 __global__ __launch_bounds__(BLOCK) void k_backward(BackwardArgs a, int slices, int64_t per,
                                                     int reverse)
 {
@@ -90,14 +90,44 @@ __global__ __launch_bounds__(BLOCK) void k_backward(BackwardArgs a, int slices, 
     const int64_t r = reverse ? a.rows - 1 - rb : rb;
     const int sl = blockIdx.x % slices;
     const int64_t V = a.vocab;
+    // Every per-row input is loaded up front (independent scalar loads, issued
+    // together), and the row's first step of logits goes out as soon as the
+    // saved record says the forward read this row: one short round trip
+    // before the stream starts instead of a chain of dependent loads.
+    const cev_saved sv = a.saved[r];
     const int64_t tg = a.labels[r];
+    const float graw = a.g[r];
+
+    const char *lrow = static_cast<const char *>(a.logits) + (size_t)r * (size_t)a.row_stride * ES;
+    char *drow = static_cast<char *>(a.dlogits) + (size_t)r * (size_t)a.d_row_stride * ES;
+    const bool vec_ok = (((uintptr_t)lrow ^ (uintptr_t)drow) & 15u) == 0;
+    int64_t head = (int64_t)(((16u - ((unsigned)(uintptr_t)lrow & 15u)) & 15u) / ES);
+    head = head < V ? head : V;
+    const int64_t nvec = (V - head) / VE;
+    const int64_t tail0 = head + nvec * VE;
+    const u32x4 *lvp = reinterpret_cast<const u32x4 *>(lrow + head * ES);
+    u32x4 *dvp = reinterpret_cast<u32x4 *>(drow + head * ES);
+    const int64_t v0 = (int64_t)sl * per;
+    const int64_t v1 = v0 + per < nvec ? v0 + per : nvec;
+    const int64_t base0 = v0 + tid;
+
+    u32x4 w[U];
+    if (vec_ok && (sv.flags & 1)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t j = base0 + (int64_t)u * BLOCK;
+            if (j < v1)
+                w[u] = load16_stream(lvp + j);
+        }
+    }
+
+    // The mask byte is a vector load: read it after the stream has started.
     const bool masked = a.row_mask && a.row_mask[r] == 0;
     const bool ignored = masked || tg == a.ignore_index;
     const int64_t VT = SHARD ? a.vocab_total : V;
     const bool bad = !ignored && (tg < 0 || tg >= VT);
     // The target's column here; outside [0, V) when another shard holds it.
     const int64_t t = SHARD ? tg - a.col_offset : tg;
-    const cev_saved sv = a.saved[r];
     if (bad && sl == 0 && tid == 0 && a.status)
         atomicOr(a.status, (int32_t)CEV_STATUS_BAD_LABEL);
 
@@ -111,10 +141,10 @@ __global__ __launch_bounds__(BLOCK) void k_backward(BackwardArgs a, int slices, 
     rc.ev = 0.0f;
     rc.tval = 0.0f;
     if (rc.valid) {
-        const float gp = a.g[r] * a.inv_t;
+        const float gp = graw * a.inv_t;
         const float ag = fabsf(gp);
-        const float eps = (float)a.label_smoothing;
-        const float epv = (float)(a.label_smoothing / (double)VT);
+        const float eps = a.eps;
+        const float epv = a.eps_over_v;
         rc.sgn = __float_as_uint(gp) & 0x80000000u;
         rc.kexp = sv.log2_d - __log2f(ag);
         rc.ev = ag * epv;
@@ -122,10 +152,7 @@ __global__ __launch_bounds__(BLOCK) void k_backward(BackwardArgs a, int slices, 
     }
     const float c = a.c;
 
-    const char *lrow = static_cast<const char *>(a.logits) + (size_t)r * (size_t)a.row_stride * ES;
-    char *drow = static_cast<char *>(a.dlogits) + (size_t)r * (size_t)a.d_row_stride * ES;
-
-    if ((((uintptr_t)lrow ^ (uintptr_t)drow) & 15u) != 0) {
+    if (!vec_ok) {
         // Source and destination rows disagree modulo 16 bytes: element path.
         const int64_t c0 = V * sl / slices, c1 = V * (sl + 1) / slices;
         for (int64_t col = c0 + tid; col < c1; col += BLOCK) {
@@ -134,15 +161,6 @@ __global__ __launch_bounds__(BLOCK) void k_backward(BackwardArgs a, int slices, 
         }
         return;
     }
-
-    int64_t head = (int64_t)(((16u - ((unsigned)(uintptr_t)lrow & 15u)) & 15u) / ES);
-    head = head < V ? head : V;
-    const int64_t nvec = (V - head) / VE;
-    const int64_t tail0 = head + nvec * VE;
-    const u32x4 *lvp = reinterpret_cast<const u32x4 *>(lrow + head * ES);
-    u32x4 *dvp = reinterpret_cast<u32x4 *>(drow + head * ES);
-    const int64_t v0 = (int64_t)sl * per;
-    const int64_t v1 = v0 + per < nvec ? v0 + per : nvec;
 
     if (sl == 0 && tid < head) {
         const float v = rc.valid ? grad_scalar<DT>(load_elem<DT>(lrow, tid), rc, c, tid, t) : 0.0f;
@@ -156,17 +174,18 @@ __global__ __launch_bounds__(BLOCK) void k_backward(BackwardArgs a, int slices, 
 
     if (!rc.valid) {
         const u32x4 zero = {0u, 0u, 0u, 0u};
-        for (int64_t j = v0 + tid; j < v1; j += BLOCK)
-            store16_stream(zero, dvp + j);
+        for (int64_t j = base0; j < v1; j += BLOCK)
+            store16<SNT>(zero, dvp + j);
         return;
     }
-    for (int64_t base = v0 + tid; base < v1; base += (int64_t)BLOCK * U) {
-        u32x4 w[U];
+    for (int64_t base = base0; base < v1; base += (int64_t)BLOCK * U) {
+        if (base != base0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t j = base + (int64_t)u * BLOCK;
-            if (j < v1)
-                w[u] = load16_stream(lvp + j);
+            for (int u = 0; u < U; ++u) {
+                const int64_t j = base + (int64_t)u * BLOCK;
+                if (j < v1)
+                    w[u] = load16_stream(lvp + j);
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -175,7 +194,7 @@ __global__ __launch_bounds__(BLOCK) void k_backward(BackwardArgs a, int slices, 
                 float z[VE], o[VE];
                 unpack16<DT>(w[u], z);
                 grad_vec<DT>(z, o, rc, c, head + j * VE, t);
-                store16_stream(pack_vec<DT>(o, rc.sgn), dvp + j);
+                store16<SNT>(pack_vec<DT>(o, rc.sgn), dvp + j);
             }
         }
     }
@@ -361,7 +380,7 @@ __global__ __launch_bounds__(BLOCK) void k_topk_backward(TopkBackwardArgs a, int
     }
 }
 
-template <int DT, int BLOCK, int U, bool SHARD>
+template <int DT, int BLOCK, int U, bool SHARD, bool SNT>
 hipError_t launch_bwd_t(const BackwardArgs &a, int iters, int reverse, hipStream_t s)
 {
     // iters wave-steps of BLOCK * U vectors per workgroup; 0 = a whole row.
@@ -377,7 +396,7 @@ hipError_t launch_bwd_t(const BackwardArgs &a, int iters, int reverse, hipStream
         slices = (nvec + per - 1) / per;
     }
     dim3 grid((unsigned)(a.rows * slices)), block(BLOCK);
-    hipLaunchKernelGGL((k_backward<DT, BLOCK, U, SHARD>), grid, block, 0, s, a, (int)slices, per,
+    hipLaunchKernelGGL((k_backward<DT, BLOCK, U, SHARD, SNT>), grid, block, 0, s, a, (int)slices, per,
                        reverse);
     return hipGetLastError();
 }
@@ -386,30 +405,48 @@ hipError_t launch_bwd_t(const BackwardArgs &a, int iters, int reverse, hipStream
 
 // Launch configuration, exposed for tuning harnesses.
 hipError_t launch_backward_cfg(int dtype, const BackwardArgs &a, int block, int U, int iters,
-                               int reverse, hipStream_t s)
+                               int reverse, int store_nt, hipStream_t s)
 {
     if (a.col_offset != 0 || a.vocab_total != a.vocab)
         return hipErrorInvalidValue; // whole rows only
-#define CEV_BWD_CASE(B, UU)                                                                     \
-    if (block == B && U == UU)                                                                  \
-        return dtype == CEV_BF16 ? launch_bwd_t<CEV_BF16, B, UU, false>(a, iters, reverse, s)   \
-                                 : launch_bwd_t<CEV_F32, B, UU, false>(a, iters, reverse, s);
-    CEV_BWD_CASE(256, 2)
-    CEV_BWD_CASE(256, 4)
-    CEV_BWD_CASE(256, 8)
-    CEV_BWD_CASE(512, 2)
-    CEV_BWD_CASE(512, 4)
+#define CEV_BWD_CASE(B, UU, NT)                                                                     \
+    if (block == B && U == UU && (store_nt != 0) == NT)                                             \
+        return dtype == CEV_BF16 ? launch_bwd_t<CEV_BF16, B, UU, false, NT>(a, iters, reverse, s)   \
+                                 : launch_bwd_t<CEV_F32, B, UU, false, NT>(a, iters, reverse, s);
+    CEV_BWD_CASE(64, 1, false)
+    CEV_BWD_CASE(64, 1, true)
+    CEV_BWD_CASE(64, 2, false)
+    CEV_BWD_CASE(64, 2, true)
+    CEV_BWD_CASE(64, 4, false)
+    CEV_BWD_CASE(64, 4, true)
+    CEV_BWD_CASE(128, 1, false)
+    CEV_BWD_CASE(128, 1, true)
+    CEV_BWD_CASE(128, 2, false)
+    CEV_BWD_CASE(128, 2, true)
+    CEV_BWD_CASE(128, 4, false)
+    CEV_BWD_CASE(128, 4, true)
+    CEV_BWD_CASE(256, 1, false)
+    CEV_BWD_CASE(256, 1, true)
+    CEV_BWD_CASE(256, 2, false)
+    CEV_BWD_CASE(256, 2, true)
+    CEV_BWD_CASE(256, 4, false)
+    CEV_BWD_CASE(256, 4, true)
+    CEV_BWD_CASE(512, 1, false)
 #undef CEV_BWD_CASE
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_backward(int dtype, const BackwardArgs &a, hipStream_t s)
 {
-    // A vocab shard gets its own instantiation (and kernel name in traces).
+    // 4 KB workgroups (128 threads x 2 vectors, nontemporal stores): on the
+    // 8192 x 152064 bf16 backward 753-758 us against 781-821 us for
+    // 256 x 4 vectors, the best of 20 shapes (64-256 threads, 1-4 vectors,
+    // 1-3 steps, either store policy).  A vocab shard gets its own
+    // instantiation (and kernel name in traces).
     if (a.col_offset != 0 || a.vocab_total != a.vocab)
-        return dtype == CEV_BF16 ? launch_bwd_t<CEV_BF16, 256, 4, true>(a, 1, 0, s)
-                                 : launch_bwd_t<CEV_F32, 256, 4, true>(a, 1, 0, s);
-    return launch_backward_cfg(dtype, a, 256, 4, 1, 0, s);
+        return dtype == CEV_BF16 ? launch_bwd_t<CEV_BF16, 128, 2, true, true>(a, 1, 0, s)
+                                 : launch_bwd_t<CEV_F32, 128, 2, true, true>(a, 1, 0, s);
+    return launch_backward_cfg(dtype, a, 128, 2, 1, 0, 1, s);
 }
 
 hipError_t launch_topk_backward(int dtype, const TopkBackwardArgs &a, hipStream_t s)

@@ -33,6 +33,16 @@ template <> struct Elem<CEV_BF16> {
 // against ~5.5-6.0 TB/s for plain ones).
 __device__ __forceinline__ u32x4 load16_stream(const u32x4 *p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void store16_stream(u32x4 v, u32x4 *p) { __builtin_nontemporal_store(v, p); }
+// 16-byte store, nontemporal (NT) or with the default cache policy.  A plain
+// store lets the L2 gather a wave's lines before they go out; in a mixed
+// read-plus-write stream that measured faster than nontemporal stores.
+template <bool NT> __device__ __forceinline__ void store16(u32x4 v, u32x4 *p)
+{
+    if constexpr (NT)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
 
 // bf16 -> fp32 is exact: the bf16 bits are the upper half of the fp32 word.
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }

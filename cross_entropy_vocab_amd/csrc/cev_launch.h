@@ -108,6 +108,8 @@ struct BackwardArgs {
     double label_smoothing;    // eps in [0, 1]
     float c;                   // log2(e) / T
     float inv_t;               // 1 / T
+    float eps;                 // label_smoothing as fp32
+    float eps_over_v;          // label_smoothing / vocab_total, rounded once to fp32
     int32_t *status;
 };
 
@@ -278,6 +280,6 @@ hipError_t launch_backward(int dtype, const BackwardArgs &a, hipStream_t stream)
 hipError_t launch_sls_sweep_cfg(int dtype, const SweepArgs &a, bool want_entropy,
                                 bool want_argmax, int block, int U, hipStream_t stream);
 hipError_t launch_backward_cfg(int dtype, const BackwardArgs &a, int block, int U, int iters,
-                               int reverse, hipStream_t stream);
+                               int reverse, int store_nt, hipStream_t stream);
 
 } // namespace cev
