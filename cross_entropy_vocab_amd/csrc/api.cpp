@@ -279,6 +279,10 @@ int ce_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stri
     if (e != hipSuccess)
         return CEV_ELAUNCH;
 
+    // The sweep takes the compacted rows in order: valid rows go round-robin
+    // over the chip whatever the mask pattern (sweeping every row in place
+    // and letting ignored rows exit measured 3 us faster with a random mask
+    // but 15 us slower when the ignored rows fell on some XCDs only).
     SweepArgs a{};
     a.logits = logits;
     a.rows = rows;

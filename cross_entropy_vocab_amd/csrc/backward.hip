@@ -95,8 +95,8 @@ __global__ __launch_bounds__(BLOCK) void k_backward(BackwardArgs a, int slices, 
     // saved record says the forward read this row: one short round trip
     // before the stream starts instead of a chain of dependent loads.
     const cev_saved sv = a.saved[r];
-    const int64_t tg = a.labels[r];
-    const float graw = a.g[r];
+    const int64_t tg = load_uniform(a.labels + r);
+    const float graw = load_uniform(a.g + r);
 
     const char *lrow = static_cast<const char *>(a.logits) + (size_t)r * (size_t)a.row_stride * ES;
     char *drow = static_cast<char *>(a.dlogits) + (size_t)r * (size_t)a.d_row_stride * ES;
@@ -121,8 +121,7 @@ __global__ __launch_bounds__(BLOCK) void k_backward(BackwardArgs a, int slices, 
         }
     }
 
-    // The mask byte is a vector load: read it after the stream has started.
-    const bool masked = a.row_mask && a.row_mask[r] == 0;
+    const bool masked = a.row_mask && mask_byte(a.row_mask, r) == 0;
     const bool ignored = masked || tg == a.ignore_index;
     const int64_t VT = SHARD ? a.vocab_total : V;
     const bool bad = !ignored && (tg < 0 || tg >= VT);

@@ -44,6 +44,26 @@ template <bool NT> __device__ __forceinline__ void store16(u32x4 v, u32x4 *p)
         *p = v;
 }
 
+// Workgroup-uniform read of a kernel input that no thread writes during the
+// launch, through the scalar cache: the pointer is cast to the constant
+// address space, so the compiler emits a scalar load even in kernels that
+// also store to memory (where it would otherwise fall back to a vector load,
+// whose latency behind a streaming sweep is microseconds).
+template <class T> __device__ __forceinline__ T load_uniform(const T *p)
+{
+    return *(const __attribute__((address_space(4))) T *)p;
+}
+
+// Row r's mask byte, read as the aligned 4-byte word that holds it so that the
+// load can be a scalar one.  The word lies in the same page as the byte, so
+// the wider read cannot fault; the other three bytes are ignored.
+__device__ __forceinline__ unsigned mask_byte(const uint8_t *m, int64_t r)
+{
+    const uintptr_t p = (uintptr_t)(m + r);
+    const unsigned w = load_uniform(reinterpret_cast<const unsigned *>(p & ~(uintptr_t)3));
+    return (w >> (8u * (unsigned)(p & 3u))) & 0xffu;
+}
+
 // bf16 -> fp32 is exact: the bf16 bits are the upper half of the fp32 word.
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }

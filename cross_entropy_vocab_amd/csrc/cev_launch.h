@@ -24,7 +24,7 @@ struct SweepArgs {
     int64_t index_row_stride;
     int64_t ignore_index;
     const uint8_t *row_mask;
-    const int64_t *rowlist;
+    const int64_t *rowlist;    // rows to sweep (compacted), or null for every row
     const int64_t *nlist;
     int64_t splits;            // workgroups per row (1 = whole rows); needs partials
     void *partials;            // [rows * splits] SplitPartial, device scratch
@@ -54,7 +54,9 @@ struct SplitPartial {
 // Launch shape for a row of nvec 16-byte vectors: the widest workgroup whose
 // waves each still get at least four full steps.  512 threads x 2 vectors was
 // the fastest shape measured on MI355X for 152064-wide bf16 rows (6.7 TB/s of
-// the ~7.0 TB/s streaming-read ceiling), 256 x 4 next.
+// the ~7.0 TB/s streaming-read ceiling).  256 x 4 is not offered: the
+// compiler gives that instantiation over 256 registers per lane (one wave
+// per SIMD), and it measured at half the rate.
 struct Shape {
     int block, U;
 };
@@ -63,8 +65,6 @@ inline Shape pick_shape(int64_t nvec)
 {
     if (nvec >= 4 * 512 * 2)
         return {512, 2};
-    if (nvec >= 4 * 256 * 4)
-        return {256, 4};
     if (nvec >= 4 * 128 * 4)
         return {128, 4};
     return {64, 4};

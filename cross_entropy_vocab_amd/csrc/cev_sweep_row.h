@@ -214,7 +214,7 @@ struct RowStats {
 // from re-reading the one step where each maximal lane first saw the maximum.
 // Every thread of the workgroup returns the same statistics.
 template <int DT, int BLOCK, int U, bool WANT_H, bool WANT_ARG, bool NT, bool WANT_Z = false>
-__device__ RowStats sweep_row(const char *rowp, int64_t V, int64_t t, int64_t part, int64_t parts,
+__device__ __forceinline__ RowStats sweep_row(const char *rowp, int64_t V, int64_t t, int64_t part, int64_t parts,
                               float c, float inv_t, float *sh_f, double *sh_d, int64_t *sh_i)
 {
     constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize, W = BLOCK / kWave;

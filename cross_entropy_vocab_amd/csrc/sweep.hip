@@ -42,7 +42,8 @@ __device__ void close_row(const SweepArgs &a, int64_t r, const char *rowp, int64
 // Single-target sweep: sls_forward and the sweep stage of ce_forward.  With
 // SPLIT, `a.splits` workgroups share one row (block b * splits + p takes part
 // p of compacted row b) and each writes a partial record for k_merge instead
-// of closing the row.
+// of closing the row.  Without a row list, block r takes row r (ignored rows
+// only write their zero outputs).
 template <int DT, int BLOCK, int U, bool WANT_H, bool WANT_ARG, bool SPLIT, bool WANT_Z>
 __global__ __launch_bounds__(BLOCK) void k_sls_sweep(SweepArgs a)
 {
@@ -60,25 +61,36 @@ __global__ __launch_bounds__(BLOCK) void k_sls_sweep(SweepArgs a)
     }
     int64_t r;
     if (a.rowlist) {
-        if (b >= *a.nlist)
+        if (b >= load_uniform(a.nlist))
             return;
-        r = a.rowlist[b];
+        r = load_uniform(a.rowlist + b);
     } else {
         r = b;
     }
     const int64_t V = a.vocab;
-    const int64_t t = a.labels[r];
+    const int64_t t = load_uniform(a.labels + r);
     if (!a.rowlist) {
-        const bool masked = a.row_mask && a.row_mask[r] == 0;
+        const bool masked = a.row_mask && mask_byte(a.row_mask, r) == 0;
         const bool ignored = masked || t == a.ignore_index;
         const bool bad = !ignored && (t < 0 || t >= V);
         if (ignored || bad) {
             if (tid == 0) {
-                a.logp[r] = 0.0f;
+                if (a.logp)
+                    a.logp[r] = 0.0f;
+                if (a.loss)
+                    a.loss[r] = 0.0f;
                 if (a.entropy)
                     a.entropy[r] = 0.0f;
                 if (a.argmax)
                     a.argmax[r] = -1;
+                if (a.saved) {
+                    cev_saved z;
+                    z.m_z = 0.0f;
+                    z.log2_d = 0.0f;
+                    z.q = 0.0f;
+                    z.flags = 0;
+                    a.saved[r] = z;
+                }
                 if (bad && a.status)
                     atomicOr(a.status, (int32_t)CEV_STATUS_BAD_LABEL);
             }
@@ -387,7 +399,7 @@ hipError_t launch_sls_sweep_cfg(int dtype, const SweepArgs &a, bool want_h, bool
                                  : launch_sls_t<CEV_F32, B, UU, false>(a, want_h, want_arg, s);
     CEV_SLS_CASE(64, 4)
     CEV_SLS_CASE(128, 4)
-    CEV_SLS_CASE(256, 4)
+    CEV_SLS_CASE(256, 2)
     CEV_SLS_CASE(512, 2)
     CEV_SLS_CASE(512, 4)
 #undef CEV_SLS_CASE
@@ -396,10 +408,11 @@ hipError_t launch_sls_sweep_cfg(int dtype, const SweepArgs &a, bool want_h, bool
 
 int64_t sweep_splits(int64_t rows, int64_t vocab, int dtype)
 {
-    // Measured on MI355X (152064-wide bf16 rows, ce_forward): splitting wins
-    // at 8 and 64 rows (16.1 -> 14.9 us, 21.6 -> 17.9 us) and loses from 256
-    // rows up, where the extra merge launch costs more than the occupancy gains.
-    constexpr int64_t kMaxSplitRows = 128;
+    // Measured on MI355X (152064-wide bf16 rows, sweep + merge against the
+    // whole-row sweep): splitting wins at 8 rows (14.5 against 16.6 us), breaks
+    // even at 32 and loses from 64 rows up (64: 24.8 against 20.6 us), where
+    // the whole-row workgroups already cover the chip's memory channels.
+    constexpr int64_t kMaxSplitRows = 16;
     constexpr int64_t kTargetBlocks = 2048;  // 8 workgroups per CU on 256 CUs
     constexpr int64_t kMinPartVectors = 2048;
     constexpr int64_t kMaxSplits = 256;
@@ -417,8 +430,10 @@ hipError_t launch_sls_sweep(int dtype, const SweepArgs &a, bool want_h, bool wan
                             hipStream_t s)
 {
     if (a.splits > 1 && a.partials && a.rowlist) {
-        hipError_t e = dtype == CEV_BF16 ? launch_sls_t<CEV_BF16, 256, 4, true>(a, want_h, want_arg, s)
-                                         : launch_sls_t<CEV_F32, 256, 4, true>(a, want_h, want_arg, s);
+        // 512 x 2 per part: 14.5 us at 8 rows against 15.1 (256 x 4) and 15.9
+        // (128 x 4).
+        hipError_t e = dtype == CEV_BF16 ? launch_sls_t<CEV_BF16, 512, 2, true>(a, want_h, want_arg, s)
+                                         : launch_sls_t<CEV_F32, 512, 2, true>(a, want_h, want_arg, s);
         if (e != hipSuccess)
             return e;
         return dtype == CEV_BF16 ? launch_merge_t<CEV_BF16>(a, want_h, want_arg, s)

@@ -193,7 +193,7 @@ int sls_topk_backward(const void *logits, int64_t rows, int64_t vocab, int64_t r
  *   valid_rows    [rows] int64 out or NULL: the first *n_valid entries are the
  *                 valid rows in ascending order; the rest are left untouched
  *   n_valid       device int64 out or NULL: the number of valid rows
- *   workspace     device scratch, or NULL.  With fewer than 128 rows and long
+ *   workspace     device scratch, or NULL.  With fewer than 16 rows and long
  *                 rows, each row is split over several workgroups whose partial
  *                 (max, sum) records are merged in a fixed order afterwards; this
  *                 needs workspace_bytes >= cev_workspace_size(rows, vocab, dtype)

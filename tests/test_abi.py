@@ -67,7 +67,8 @@ def test_version_and_strings(lib):
     assert lib.cev_workspace_size(8192, 152064, 1) == 8193 * 8  # enough rows: no split
     # few long rows split over workgroups: 40-byte partial records (max, its
     # column, sum, entropy term, value sum) follow the 32-byte aligned list
-    assert lib.cev_workspace_size(64, 152064, 1) == 544 + 64 * 9 * 40
+    assert lib.cev_workspace_size(12, 152064, 1) == 128 + 12 * 9 * 40
+    assert lib.cev_workspace_size(64, 152064, 1) == 65 * 8     # 64 rows: whole rows
     assert lib.cev_workspace_size(-1, 100, 0) == 0
     assert lib.cev_workspace_size(10, 100, 5) == 0
 

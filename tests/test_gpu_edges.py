@@ -285,7 +285,7 @@ def _ce_raw(w, workspace_bytes, eps=0.0):
 
 
 @pytest.mark.parametrize("rows,V,dtype,T", [(1, 152064, "bf16", 1.0), (3, 151936, "f32", 0.9),
-                                            (64, 152064, "bf16", 1.0), (100, 65537, "f32", 0.7),
+                                            (12, 152064, "bf16", 1.0), (15, 65537, "f32", 0.7),
                                             (7, 40001, "bf16", 1.3)])
 def test_split_rows_match_oracle_and_whole_rows(rows, V, dtype, T):
     """Few long rows: the split-row sweep (partials + fixed-order merge) and the

@@ -113,7 +113,7 @@ def test_label_smoothing_matches_oracle(name, eps):
     say(f"  max rel err smoothed loss {e_loss:.2e}")
 
 
-@pytest.mark.parametrize("rows,V,dtype", [(3, 151936, "f32"), (64, 152064, "bf16")])
+@pytest.mark.parametrize("rows,V,dtype", [(3, 151936, "f32"), (12, 152064, "bf16")])
 def test_label_smoothing_split_rows(rows, V, dtype):
     """Few long rows take the split sweep, whose merge sums the parts' value
     sums; the smoothed loss matches the oracle and the whole-row sweep."""
