@@ -96,8 +96,8 @@ def write_traffic(fetch_csv, write_csv, rows=8192, vocab=152064):
     for name in sorted(fetch):
         short = name.replace("void ", "").replace("cev::(anonymous namespace)::", "").split("(")[0]
         key = next((k for k in algo if short.startswith(k)), None)
-        if key == "k_backward" and short.endswith("true>"):
-            key = None                     # the vocab-shard instantiation
+        if key == "k_backward" and short.split("<")[1].rstrip(">").split(",")[3].strip() == "true":
+            key = None                     # the vocab-shard instantiation (SHARD = true)
         rd = fetch[name] * 1024.0 * f_scale
         wr = write.get(name, 0.0) * 1024.0 * w_scale
         entry = {"kernel": short, "fetch_kib": fetch[name], "write_kib": write.get(name),
@@ -130,9 +130,9 @@ def write_traffic(fetch_csv, write_csv, rows=8192, vocab=152064):
         "traffic_over_algorithmic": e["ratio"],
         "commands": [
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/prof_fetch -o grpo -- "
-            "python bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration",
+            "python bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-linear --no-jsd --copy-calibration",
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/prof_write -o grpo -- "
-            "python bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration",
+            "python bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-linear --no-jsd --copy-calibration",
             "python bench.py --traffic-from <out>/prof_fetch/grpo_counter_collection.csv "
             "<out>/prof_write/grpo_counter_collection.csv"],
     }
