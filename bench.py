@@ -306,6 +306,101 @@ def bench_jsd(args, torch, cev, workloads, dev):
     return res
 
 
+def _time_calls(torch, calls, iters, warmup=3):
+    """Mean GPU time in ms of each call in `calls` (a list of zero-argument
+    functions run in order, iters times), from HIP events recorded on the
+    library's stream between the calls."""
+    for _ in range(warmup):
+        for c in calls:
+            c(0)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+          for _ in range(iters)]
+    torch.cuda.synchronize()
+    for i, e in enumerate(ev):
+        e[0].record()
+        for k, c in enumerate(calls):
+            c(i)
+            e[k + 1].record()
+    torch.cuda.synchronize()
+    return [float(np.mean([e[k].elapsed_time(e[k + 1]) for e in ev])) for k in range(len(calls))]
+
+
+def bench_configs(args, torch, cev, workloads, dev):
+    """The other workloads of the scope table, timed on their own entry
+    points: the tiny and sparse-supervision cases (launch-bound, in us), the
+    chunked selective log-softmax and its top-K form on 4096 x 32768 bf16
+    (three input copies in rotation, so the 256 MB Infinity Cache cannot hold
+    the next call's input), and the peaked-row stress rows in fp32 and bf16 at
+    T = 1 and 0.9 (forward with entropy and argmax, then the backward)."""
+    iters = max(10, args.steps)
+    res = {}
+
+    def dev_logits(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    for name, w in (("tiny_64x4096_f32", workloads.tiny()),
+                    ("sparse_1922x4096_f32", workloads.sparse())):
+        z = dev_logits(w["logits"])
+        lab = torch.from_numpy(w["labels"]).to(dev)
+        g = torch.from_numpy(w["g"]).to(dev)
+        T = w["temperature"]
+        out = cev.ce_forward(z, lab, T, logp=True, argmax=True)
+        dl = torch.empty_like(z)
+        f, b = _time_calls(torch, [
+            lambda i: cev.ce_forward(z, lab, T, logp=True, argmax=True, out=out),
+            lambda i: cev.ce_backward(z, lab, g, out["saved"], T, dlogits=dl)], iters)
+        res[name] = {"calls": "ce_forward (compaction + sweep) + ce_backward",
+                     "valid_rows": int(out["n_valid"].item()),
+                     "ce_forward_us": f * 1e3, "ce_backward_us": b * 1e3}
+        log(f"[bench] {name}: forward {f * 1e3:.1f} us, backward {b * 1e3:.1f} us")
+
+    w = workloads.chunk()
+    R, V = w["logits"].shape
+    copies = [dev_logits(w["logits"])]
+    copies += [copies[0].clone() for _ in range(2)]
+    lab = torch.from_numpy(w["labels"]).to(dev)
+    idx = torch.from_numpy(w["indices"]).to(dev)
+    T = w["temperature"]
+    f, k = _time_calls(torch, [
+        lambda i: cev.sls_forward(copies[i % 3], lab, T),
+        lambda i: cev.sls_topk_forward(copies[(i + 1) % 3], idx, T)], iters)
+    nbytes = R * V * 2
+    res["chunk_4096x32768_bf16"] = {
+        "calls": "sls_forward (T = 0.7); sls_topk_forward (K = 8)", "bytes_per_call": nbytes,
+        "ideal_us_at_peak": nbytes / PEAK_HBM_GBS / 1e3,
+        "sls_forward_us": f * 1e3, "sls_forward_GBps": nbytes / (f / 1e3) / 1e9,
+        "sls_topk_forward_us": k * 1e3, "sls_topk_forward_GBps": nbytes / (k / 1e3) / 1e9}
+    log(f"[bench] chunk: sls_forward {f * 1e3:.1f} us, sls_topk_forward {k * 1e3:.1f} us")
+    del copies
+
+    for dt in ("f32", "bf16"):
+        w = workloads.peaked(dt)
+        R, V = w["logits"].shape
+        ES = 2 if dt == "bf16" else 4
+        z = dev_logits(w["logits"])
+        lab = torch.from_numpy(w["labels"]).to(dev)
+        g = torch.from_numpy(w["g"]).to(dev)
+        dl = torch.empty_like(z)
+        for T in (1.0, 0.9):
+            out = cev.ce_forward(z, lab, T, logp=True, entropy=True, argmax=True)
+            f, b = _time_calls(torch, [
+                lambda i: cev.ce_forward(z, lab, T, logp=True, entropy=True, argmax=True,
+                                         out=out),
+                lambda i: cev.ce_backward(z, lab, g, out["saved"], T, dlogits=dl)], iters)
+            fb, bb = R * V * ES, 2 * R * V * ES
+            res[f"peaked_{R}x{V}_{dt}_T{T:g}"] = {
+                "calls": "ce_forward (entropy, argmax) + ce_backward",
+                "ce_forward_us": f * 1e3, "ce_backward_us": b * 1e3,
+                "ce_forward_GBps": fb / (f / 1e3) / 1e9, "ce_backward_GBps": bb / (b / 1e3) / 1e9,
+                "step_frac_of_peak": (fb + bb) / ((f + b) / 1e3) / 1e9 / PEAK_HBM_GBS}
+            log(f"[bench] peaked {dt} T={T:g}: forward {f * 1e3:.1f} us, backward {b * 1e3:.1f} us")
+        del z, dl
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -322,6 +417,8 @@ def main():
                     help="skip the student/teacher JSD measurement (2048 x 151936)")
     ap.add_argument("--no-linear", action="store_true",
                     help="skip the linear cross-entropy measurement (8192 x 2560 x 151936)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (tiny, chunked + top-K, sparse, peaked)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: turn the two counter runs' csv files into the "
                          "committed traffic figures and print the counter table")
@@ -443,6 +540,7 @@ def main():
     torch.cuda.empty_cache()
     linear = None if args.no_linear else bench_linear(args, torch, cev, workloads, dev)
     jsd = None if args.no_jsd else bench_jsd(args, torch, cev, workloads, dev)
+    configs = None if args.no_configs else bench_configs(args, torch, cev, workloads, dev)
 
     ES = 2
     fwd_bytes = n_valid * V * ES                    # valid rows read once
@@ -489,6 +587,7 @@ def main():
                   "frac_of_peak": (fwd_bytes + R * V * ES) / (fused_ms / 1e3) / 1e9 / PEAK_HBM_GBS},
         "linear_ce": linear,
         "jsd": jsd,
+        "configs": configs,
         "vocab_shard": {"entry": f"one rank of {P}-way vocab parallelism: "
                                  "ce_vocab_shard_forward on its contiguous shard, ce_vocab_merge "
                                  f"of {P} shards' records, ce_vocab_shard_backward",

@@ -51,20 +51,23 @@ struct SplitPartial {
     double zs;                 // sum of the part's non-target stored values
 };
 
-// Launch shape for a row of nvec 16-byte vectors: the widest workgroup whose
-// waves each still get at least four full steps.  512 threads x 2 vectors was
-// the fastest shape measured on MI355X for 152064-wide bf16 rows (6.7 TB/s of
-// the ~7.0 TB/s streaming-read ceiling).  256 x 4 is not offered: the
-// compiler gives that instantiation over 256 registers per lane (one wave
-// per SIMD), and it measured at half the rate.
+// Launch shape for a row of nvec 16-byte vectors.  512 threads x 2 vectors
+// was the fastest shape measured on MI355X for 152064-wide bf16 rows (6.7 TB/s
+// of the ~7.0 TB/s streaming-read ceiling); on 32768-wide bf16 rows (4096
+// vectors) 256 x 2 beat it, 50 against 55-58 us for 4096 rows, as more rows
+// in flight hide each row's closing step.  256 x 4 is not offered: the
+// compiler gives that instantiation over 256 registers per lane (one wave per
+// SIMD), and it measured at half the rate.
 struct Shape {
     int block, U;
 };
 
 inline Shape pick_shape(int64_t nvec)
 {
-    if (nvec >= 4 * 512 * 2)
+    if (nvec >= 8192)
         return {512, 2};
+    if (nvec >= 4096)
+        return {256, 2};
     if (nvec >= 4 * 128 * 4)
         return {128, 4};
     return {64, 4};
@@ -281,5 +284,6 @@ hipError_t launch_sls_sweep_cfg(int dtype, const SweepArgs &a, bool want_entropy
                                 bool want_argmax, int block, int U, hipStream_t stream);
 hipError_t launch_backward_cfg(int dtype, const BackwardArgs &a, int block, int U, int iters,
                                int reverse, int store_nt, hipStream_t stream);
+hipError_t launch_topk_sweep_cfg(int dtype, const SweepArgs &a, int block, int U, hipStream_t stream);
 
 } // namespace cev

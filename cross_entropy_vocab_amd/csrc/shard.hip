@@ -175,7 +175,7 @@ hipError_t launch_shard_sweep(int dtype, const ShardArgs &a, bool want_h, bool w
     }
     CEV_SHARD_CASE(64, 4)
     CEV_SHARD_CASE(128, 4)
-    CEV_SHARD_CASE(256, 4)
+    CEV_SHARD_CASE(256, 2)
     CEV_SHARD_CASE(512, 2)
 #undef CEV_SHARD_CASE
     return hipErrorInvalidValue;
