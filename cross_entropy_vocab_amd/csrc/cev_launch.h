@@ -241,6 +241,7 @@ struct JsdArgs {
 
 hipError_t launch_jsd_forward(int dtype, const JsdArgs &a, hipStream_t stream);
 hipError_t launch_jsd_backward(int dtype, const JsdArgs &a, hipStream_t stream);
+hipError_t launch_jsd_tiles_cfg(int dtype, const JsdArgs &a, int block, int U, hipStream_t stream);
 
 // Forward + backward in one call, one workgroup per row (rows 16-byte aligned).
 struct FusedArgs {

@@ -731,11 +731,12 @@ __global__ __launch_bounds__(BB) void k_jsd_backward(JsdArgs a)
 
 // One-shot slices (beta < 1, every row 16-byte aligned): workgroup b handles
 // vectors [per sl, per (sl + 1)) of row b / slices, plus the row's tail
-// columns in its last slice; the argmax entry comes from the record.
-constexpr int kTB = 256, kTU = 4;
-
-template <int DT, int MODE>
-__global__ __launch_bounds__(kTB) void k_jsd_bwd_tiles(JsdArgs a, int slices, int64_t per)
+// columns in its last slice; the argmax entry comes from the record.  The
+// row's inputs are read through the scalar cache and the slice's first step
+// of both rows goes out as soon as the record says the tile path owns the
+// row, before the other per-row checks resolve.
+template <int DT, int MODE, int TB, int TU>
+__global__ __launch_bounds__(TB) void k_jsd_bwd_tiles(JsdArgs a, int slices, int64_t per)
 {
     constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize;
     const int tid = threadIdx.x;
@@ -745,24 +746,37 @@ __global__ __launch_bounds__(kTB) void k_jsd_bwd_tiles(JsdArgs a, int slices, in
     const int64_t v0 = (int64_t)sl * per, v1 = v0 + per < nv ? v0 + per : nv;
     char *rd = static_cast<char *>(a.dstudent) + (size_t)r * (size_t)a.d_stride * ES;
     u32x4 *dvp = reinterpret_cast<u32x4 *>(rd);
-    const bool masked = (a.row_mask && a.row_mask[r] == 0) ||
-                        (a.labels && a.labels[r] == a.ignore_index);
     const cev_jsd_saved sv = a.saved_in[r];
+    const float gr = load_uniform(a.g + r);
+    const int64_t lab = a.labels ? load_uniform(a.labels + r) : 0;
+    const char *rs = static_cast<const char *>(a.student) + (size_t)r * (size_t)a.s_stride * ES;
+    const char *rt = static_cast<const char *>(a.teacher) + (size_t)r * (size_t)a.t_stride * ES;
+    const int64_t base0 = v0 + tid;
+    float xs[TU][VE], xt[TU][VE];
+    if ((sv.flags & 3) == 3) {
+#pragma unroll
+        for (int u = 0; u < TU; ++u) {
+            const int64_t j = base0 + (int64_t)u * TB;
+            if (j < v1) {
+                load_vec<DT>(rs, j, xs[u], true);
+                load_vec<DT>(rt, j, xt[u], true);
+            }
+        }
+    }
+    const bool masked = (a.row_mask && mask_byte(a.row_mask, r) == 0) ||
+                        (a.labels && lab == a.ignore_index);
     if (!masked && (sv.flags & 3) == 1)
         return;   // valid, no argmax entry in the record: the per-row kernel's
     if (masked || !(sv.flags & 1)) {
         const u32x4 zero = {0u, 0u, 0u, 0u};
-        for (int64_t j = v0 + tid; j < v1; j += kTB)
+        for (int64_t j = base0; j < v1; j += TB)
             store16_stream(zero, dvp + j);
         if (sl == slices - 1 && nv * VE + tid < V)
             store_one<DT>(rd, nv * VE + tid, 0.0f);
         return;
     }
-    const char *rs = static_cast<const char *>(a.student) + (size_t)r * (size_t)a.s_stride * ES;
-    const char *rt = static_cast<const char *>(a.teacher) + (size_t)r * (size_t)a.t_stride * ES;
     const float c = a.c, inv_t = a.inv_t;
     const JsdRow rc = jsd_row(sv.ms, sv.ls0, sv.mt, sv.lt0, sv.dl);
-    const float gr = a.g[r];
     const float wabs = fabsf(gr) * inv_t * (MODE == 2 ? (float)(1.0 - a.beta) : 1.0f);
     const float lw = __log2f(wabs);
     const float es = rc.ls2 - lw - (MODE == 0 ? 0.0f : 24.0f), et = rc.lt2 - lw;
@@ -770,19 +784,20 @@ __global__ __launch_bounds__(kTB) void k_jsd_bwd_tiles(JsdArgs a, int slices, in
     const MixW mw = mix_w(a.beta);
     const float darg = gr * inv_t * sv.garg;
     double unused = 0.0;
-    for (int64_t base = v0 + tid; base < v1; base += (int64_t)kTB * kTU) {
-        float xs[kTU][VE], xt[kTU][VE];
+    for (int64_t base = base0; base < v1; base += (int64_t)TB * TU) {
+        if (base != base0) {
 #pragma unroll
-        for (int u = 0; u < kTU; ++u) {
-            const int64_t j = base + (int64_t)u * kTB;
-            if (j < v1) {
-                load_vec<DT>(rs, j, xs[u], true);
-                load_vec<DT>(rt, j, xt[u], true);
+            for (int u = 0; u < TU; ++u) {
+                const int64_t j = base + (int64_t)u * TB;
+                if (j < v1) {
+                    load_vec<DT>(rs, j, xs[u], true);
+                    load_vec<DT>(rt, j, xt[u], true);
+                }
             }
         }
 #pragma unroll
-        for (int u = 0; u < kTU; ++u) {
-            const int64_t j = base + (int64_t)u * kTB;
+        for (int u = 0; u < TU; ++u) {
+            const int64_t j = base + (int64_t)u * TB;
             if (j < v1) {
                 float d[VE];
                 const int col0 = (int)(j * VE);
@@ -798,12 +813,26 @@ __global__ __launch_bounds__(kTB) void k_jsd_bwd_tiles(JsdArgs a, int slices, in
     }
     if (sl == slices - 1 && nv * VE + tid < V) {
         const int64_t j = nv * VE + tid;
-        const float xs[1] = {load_one<DT>(rs, j)}, xt[1] = {load_one<DT>(rt, j)};
+        const float xs1[1] = {load_one<DT>(rs, j)}, xt1[1] = {load_one<DT>(rt, j)};
         float d[1];
-        grad_terms<MODE, false>(xs, xt, rc, es, et, c, inv_t, mw, sv.k, sgn, (int)j, sv.arg,
+        grad_terms<MODE, false>(xs1, xt1, rc, es, et, c, inv_t, mw, sv.k, sgn, (int)j, sv.arg,
                                 d, unused);
         store_one<DT>(rd, j, j == sv.arg ? darg : d[0]);
     }
+}
+
+template <int DT, int MODE, int TB, int TU>
+void launch_tiles_t(const JsdArgs &a, hipStream_t s)
+{
+    const int64_t nv = a.vocab / Elem<DT>::kVE;
+    int64_t per = (int64_t)TB * TU;
+    int64_t slices = nv > 0 ? (nv + per - 1) / per : 1;
+    while ((uint64_t)a.rows * (uint64_t)slices * TB > 0xFFFFFFFFull && slices > 1) {
+        per *= 2;
+        slices = (nv + per - 1) / per;
+    }
+    hipLaunchKernelGGL((k_jsd_bwd_tiles<DT, MODE, TB, TU>), dim3((unsigned)(a.rows * slices)),
+                       dim3(TB), 0, s, a, (int)slices, per);
 }
 
 template <int DT>
@@ -822,20 +851,16 @@ template <int DT>
 void launch_bwd_t(const JsdArgs &a, int mode, hipStream_t s)
 {
     if (mode != 1 && a.vec) {
-        const int64_t nv = a.vocab / Elem<DT>::kVE;
-        int64_t per = (int64_t)kTB * kTU;
-        int64_t slices = nv > 0 ? (nv + per - 1) / per : 1;
-        while ((uint64_t)a.rows * (uint64_t)slices * kTB > 0xFFFFFFFFull && slices > 1) {
-            per *= 2;
-            slices = (nv + per - 1) / per;
-        }
-        const dim3 tgrid((unsigned)(a.rows * slices)), tblock(kTB), grid((unsigned)a.rows);
+        const dim3 grid((unsigned)a.rows), block(kJB);
+        // Tile shapes measured on 2048 x 151936 bf16 rows: 256 threads x 2
+        // vectors at beta = 0 (271 us against 299 us for 256 x 4), 256 x 1 in
+        // between (274 against 295 us).
         if (mode == 0) {
-            hipLaunchKernelGGL((k_jsd_bwd_tiles<DT, 0>), tgrid, tblock, 0, s, a, (int)slices, per);
-            hipLaunchKernelGGL((k_jsd_backward<DT, 0, kJB, true>), grid, tblock, 0, s, a);
+            launch_tiles_t<DT, 0, 256, 2>(a, s);
+            hipLaunchKernelGGL((k_jsd_backward<DT, 0, kJB, true>), grid, block, 0, s, a);
         } else {
-            hipLaunchKernelGGL((k_jsd_bwd_tiles<DT, 2>), tgrid, tblock, 0, s, a, (int)slices, per);
-            hipLaunchKernelGGL((k_jsd_backward<DT, 2, kJB, true>), grid, tblock, 0, s, a);
+            launch_tiles_t<DT, 2, 256, 1>(a, s);
+            hipLaunchKernelGGL((k_jsd_backward<DT, 2, kJB, true>), grid, block, 0, s, a);
         }
         return;
     }
@@ -851,6 +876,31 @@ void launch_bwd_t(const JsdArgs &a, int mode, hipStream_t s)
 int jsd_mode(double beta) { return beta == 0.0 ? 0 : beta == 1.0 ? 1 : 2; }
 
 } // namespace
+
+// Tuning: the beta < 1 tile backward alone with an explicit shape (rows
+// 16-byte aligned; the rows without an argmax entry are not written).
+hipError_t launch_jsd_tiles_cfg(int dtype, const JsdArgs &a, int block, int U, hipStream_t s)
+{
+    const int mode = jsd_mode(a.beta);
+    if (mode == 1 || !a.vec)
+        return hipErrorInvalidValue;
+#define CEV_JT_CASE(B, UU)                                                                      \
+    if (block == B && U == UU) {                                                                \
+        if (dtype == CEV_BF16)                                                                  \
+            mode == 0 ? launch_tiles_t<CEV_BF16, 0, B, UU>(a, s) : launch_tiles_t<CEV_BF16, 2, B, UU>(a, s); \
+        else                                                                                    \
+            mode == 0 ? launch_tiles_t<CEV_F32, 0, B, UU>(a, s) : launch_tiles_t<CEV_F32, 2, B, UU>(a, s);   \
+        return hipGetLastError();                                                               \
+    }
+    CEV_JT_CASE(128, 1)
+    CEV_JT_CASE(128, 2)
+    CEV_JT_CASE(256, 1)
+    CEV_JT_CASE(256, 2)
+    CEV_JT_CASE(256, 4)
+    CEV_JT_CASE(64, 2)
+#undef CEV_JT_CASE
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_jsd_forward(int dtype, const JsdArgs &a, hipStream_t s)
 {
