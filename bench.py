@@ -363,17 +363,26 @@ def bench_configs(args, torch, cev, workloads, dev):
     lab = torch.from_numpy(w["labels"]).to(dev)
     idx = torch.from_numpy(w["indices"]).to(dev)
     T = w["temperature"]
-    f, k = _time_calls(torch, [
+    gk = torch.from_numpy(np.random.default_rng(1).standard_normal(
+        tuple(w["indices"].shape), dtype=np.float32)).to(dev)
+    tk = cev.sls_topk_forward(copies[0], idx, T, saved=True)
+    dl = torch.empty_like(copies[0])
+    f, k, kb = _time_calls(torch, [
         lambda i: cev.sls_forward(copies[i % 3], lab, T),
-        lambda i: cev.sls_topk_forward(copies[(i + 1) % 3], idx, T)], iters)
+        lambda i: cev.sls_topk_forward(copies[(i + 1) % 3], idx, T),
+        lambda i: cev.sls_topk_backward(copies[0], idx, gk, tk[2], tk[1], T, dlogits=dl)], iters)
     nbytes = R * V * 2
     res["chunk_4096x32768_bf16"] = {
-        "calls": "sls_forward (T = 0.7); sls_topk_forward (K = 8)", "bytes_per_call": nbytes,
+        "calls": "sls_forward (T = 0.7); sls_topk_forward (K = 8); sls_topk_backward (K = 8, "
+                 "g ~ N(0, 1) per index)", "bytes_per_call": nbytes,
         "ideal_us_at_peak": nbytes / PEAK_HBM_GBS / 1e3,
         "sls_forward_us": f * 1e3, "sls_forward_GBps": nbytes / (f / 1e3) / 1e9,
-        "sls_topk_forward_us": k * 1e3, "sls_topk_forward_GBps": nbytes / (k / 1e3) / 1e9}
-    log(f"[bench] chunk: sls_forward {f * 1e3:.1f} us, sls_topk_forward {k * 1e3:.1f} us")
-    del copies
+        "sls_topk_forward_us": k * 1e3, "sls_topk_forward_GBps": nbytes / (k / 1e3) / 1e9,
+        "sls_topk_backward_us": kb * 1e3,
+        "sls_topk_backward_GBps": 2 * nbytes / (kb / 1e3) / 1e9}
+    log(f"[bench] chunk: sls_forward {f * 1e3:.1f} us, sls_topk_forward {k * 1e3:.1f} us, "
+        f"sls_topk_backward {kb * 1e3:.1f} us")
+    del copies, dl
 
     for dt in ("f32", "bf16"):
         w = workloads.peaked(dt)

@@ -251,7 +251,20 @@ __global__ __launch_bounds__(BLOCK) void k_topk_backward(TopkBackwardArgs a, int
         return j >= v0 && j < v1;
     };
     const cev_saved sv = a.saved[r];
-    const bool masked = (a.row_mask && a.row_mask[r] == 0) || !(sv.flags & 1);
+    // The slice's first step goes out as soon as the record says the row was
+    // read, before the gathered indices and g are processed.
+    const u32x4 *lvp = reinterpret_cast<const u32x4 *>(lrow + head * ES);
+    const int64_t base0 = v0 + tid;
+    u32x4 w[U];
+    if (!scalar_path && (sv.flags & 1)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t j = base0 + (int64_t)u * BLOCK;
+            if (j < v1)
+                w[u] = load16_stream(lvp + j);
+        }
+    }
+    const bool masked = (a.row_mask && mask_byte(a.row_mask, r) == 0) || !(sv.flags & 1);
     const int64_t *idx = a.indices + (size_t)r * (size_t)a.index_row_stride;
     const float *gk = a.g + (size_t)r * (size_t)K;
     const float *qk = a.q + (size_t)r * (size_t)K;
@@ -329,7 +342,6 @@ __global__ __launch_bounds__(BLOCK) void k_topk_backward(TopkBackwardArgs a, int
         }
         return;
     }
-    const u32x4 *lvp = reinterpret_cast<const u32x4 *>(lrow + head * ES);
     u32x4 *dvp = reinterpret_cast<u32x4 *>(drow + head * ES);
     if (sl == 0 && tid < head) {
         const float v = masked ? 0.0f : value(load_elem<DT>(lrow, tid), tid);
@@ -342,17 +354,18 @@ __global__ __launch_bounds__(BLOCK) void k_topk_backward(TopkBackwardArgs a, int
     }
     if (masked) {
         const u32x4 zero = {0u, 0u, 0u, 0u};
-        for (int64_t j = v0 + tid; j < v1; j += BLOCK)
+        for (int64_t j = base0; j < v1; j += BLOCK)
             store16_stream(zero, dvp + j);
         return;
     }
-    for (int64_t base = v0 + tid; base < v1; base += (int64_t)BLOCK * U) {
-        u32x4 w[U];
+    for (int64_t base = base0; base < v1; base += (int64_t)BLOCK * U) {
+        if (base != base0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t j = base + (int64_t)u * BLOCK;
-            if (j < v1)
-                w[u] = load16_stream(lvp + j);
+            for (int u = 0; u < U; ++u) {
+                const int64_t j = base + (int64_t)u * BLOCK;
+                if (j < v1)
+                    w[u] = load16_stream(lvp + j);
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -448,10 +461,10 @@ hipError_t launch_backward(int dtype, const BackwardArgs &a, hipStream_t s)
     return launch_backward_cfg(dtype, a, 128, 2, 1, 0, 1, s);
 }
 
-hipError_t launch_topk_backward(int dtype, const TopkBackwardArgs &a, hipStream_t s)
+template <int DT, int B, int UU>
+void launch_topk_bwd_t(const TopkBackwardArgs &a, hipStream_t s)
 {
-    constexpr int B = 256, UU = 4;
-    const int64_t nvec = a.vocab / (dtype == CEV_BF16 ? 8 : 4);
+    const int64_t nvec = a.vocab / Elem<DT>::kVE;
     int64_t per = (int64_t)B * UU;
     int64_t slices = (nvec + per - 1) / per;
     slices = slices < 1 ? 1 : slices;
@@ -459,13 +472,33 @@ hipError_t launch_topk_backward(int dtype, const TopkBackwardArgs &a, hipStream_
         per *= 2;
         slices = (nvec + per - 1) / per;
     }
-    dim3 grid((unsigned)(a.rows * slices)), block(B);
     const size_t lds = (size_t)a.K * (sizeof(int64_t) + 4 * sizeof(float));
-    if (dtype == CEV_BF16)
-        hipLaunchKernelGGL((k_topk_backward<CEV_BF16, B, UU>), grid, block, lds, s, a, (int)slices, per);
-    else
-        hipLaunchKernelGGL((k_topk_backward<CEV_F32, B, UU>), grid, block, lds, s, a, (int)slices, per);
-    return hipGetLastError();
+    hipLaunchKernelGGL((k_topk_backward<DT, B, UU>), dim3((unsigned)(a.rows * slices)), dim3(B), lds,
+                       s, a, (int)slices, per);
+}
+
+hipError_t launch_topk_backward_cfg(int dtype, const TopkBackwardArgs &a, int block, int U,
+                                    hipStream_t s)
+{
+#define CEV_TKB_CASE(B, UU)                                                                     \
+    if (block == B && U == UU) {                                                                \
+        if (dtype == CEV_BF16)                                                                  \
+            launch_topk_bwd_t<CEV_BF16, B, UU>(a, s);                                           \
+        else                                                                                    \
+            launch_topk_bwd_t<CEV_F32, B, UU>(a, s);                                            \
+        return hipGetLastError();                                                               \
+    }
+    CEV_TKB_CASE(128, 2)
+    CEV_TKB_CASE(256, 1)
+    CEV_TKB_CASE(256, 2)
+    CEV_TKB_CASE(256, 4)
+#undef CEV_TKB_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_topk_backward(int dtype, const TopkBackwardArgs &a, hipStream_t s)
+{
+    return launch_topk_backward_cfg(dtype, a, 256, 4, s);
 }
 
 } // namespace cev
