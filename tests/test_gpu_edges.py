@@ -390,3 +390,43 @@ def test_ce_fused_equals_separate_calls():
     assert_close("fused vs two-pass dlogits", a["dlogits"], b["dlogits"], 8e-3, 2.0 ** -126)
     again = _run_fused(w, entropy=False)
     assert np.array_equal(again["dlogits"], a["dlogits"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mask_views_at_every_byte_offset(dtype):
+    """The kernels read a row's mask byte as the aligned 4-byte word holding
+    it: a mask that is a view starting at byte offsets 0-3 of a larger buffer,
+    with a row count that is not a multiple of 4, must give the same results
+    as the oracle for ce_forward/ce_backward, sls_forward and sls_topk_forward
+    (the bytes around the view are the opposite of the row's own)."""
+    from gpu_helpers import DEV, to_dev, to_host
+    rows, V = 13, 3000
+    w = _rand_case(rows, V, dtype, T=0.9, seed=31, mask_frac=0.4, n_ignored=2)
+    host_mask = w["row_mask"]
+    ref = oracle.ce_rows(w["logits"], w["labels"], w["temperature"], row_mask=host_mask)
+    kind = "bf16" if dtype == "bf16" else "f32"
+    tol = RTOL[kind]
+    idx = np.stack([np.arange(4) * 7 + r for r in range(rows)]).astype(np.int64)
+    tref, _ = oracle.topk_rows(w["logits"], idx, w["temperature"], row_mask=host_mask)
+    logits = to_dev(w["logits"])
+    labels = to_dev(w["labels"])
+    g = to_dev(w["g"])
+    for off in range(4):
+        buf = np.empty(rows + 8, dtype=np.uint8)
+        buf[:] = 1 - np.resize(host_mask, rows + 8)          # neighbours disagree
+        buf[off:off + rows] = host_mask
+        mask = to_dev(buf)[off:off + rows]
+        assert mask.is_contiguous() and mask.data_ptr() % 4 == off % 4
+        out = cev.ce_forward(logits, labels, w["temperature"], row_mask=mask, argmax=True)
+        dl = cev.ce_backward(logits, labels, g, out["saved"], w["temperature"], row_mask=mask)
+        s = cev.sls_forward(logits, labels, w["temperature"], row_mask=mask)
+        tk = cev.sls_topk_forward(logits, to_dev(idx), w["temperature"], row_mask=mask)
+        torch.cuda.synchronize()
+        name = f"{dtype} mask offset {off}"
+        assert_close(f"{name} loss", to_host(out["loss"]), ref["loss"], tol["loss"])
+        assert_close(f"{name} sls logp", to_host(s["logp"]), ref["logp"], tol["logp"])
+        assert_close(f"{name} topk logp", to_host(tk), tref, tol["logp"])
+        assert np.array_equal(to_host(out["argmax"]), ref["argmax"]), name
+        valid = (host_mask != 0) & (w["labels"] != -100)
+        d = to_host(dl)
+        assert np.all(d[~valid] == 0) and np.all(np.any(d[valid] != 0, axis=1)), name
