@@ -34,8 +34,11 @@ __device__ inline cev_saved close_row_fp64(const RowOutputs &o, int64_t r, float
 {
     const float B = fmaxf(M, -FLT_MAX);
     const double u = S > 0.0 ? log(S) + ((double)B - (double)zt) / T : -INFINITY;
-    const double loss = softplus64(u);
-    const double q = sigmoid64(u);
+    // softplus(u) and sigmoid(u) share e = e^{-|u|} (one fp64 exp instead of
+    // two; the same values as the separate forms, bit for bit).
+    const double e = exp(-fabs(u));
+    const double loss = fmax(u, 0.0) + log1p(e);
+    const double q = (u < 0.0 ? e : 1.0) / (1.0 + e);
     const double lse = (double)zt / T + loss;
     if (o.logp)
         o.logp[r] = (float)(-loss);
