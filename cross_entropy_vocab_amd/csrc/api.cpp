@@ -16,6 +16,7 @@ using cev::CompactArgs;
 using cev::SweepArgs;
 
 constexpr int64_t kMaxRows = 1 << 22;         // one workgroup per row; the grid stays < 2^32 work-items
+constexpr int64_t kInPlaceBytes = (int64_t)64 << 20;  // ce_forward sweeps in place up to 64 MB of logits
 constexpr int64_t kMaxVocab = INT32_MAX / 2;  // step codes are 32-bit
 constexpr int64_t kMaxK = 1024;               // gathered indices per row held in LDS
 constexpr int64_t kMaxParts = 4096;           // shards merged by ce_vocab_merge
@@ -261,28 +262,14 @@ int ce_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stri
     else
         splits = 1;
 
-    CompactArgs ca{};
-    ca.rows = rows;
-    ca.vocab = vocab;
-    ca.labels = labels;
-    ca.ignore_index = ignore_index;
-    ca.row_mask = row_mask;
-    ca.rowlist = list;
-    ca.nlist = count;
-    ca.logp = logp;
-    ca.loss = loss;
-    ca.entropy = entropy;
-    ca.argmax = argmax;
-    ca.saved = static_cast<cev_saved *>(saved);
-    ca.status = status;
-    hipError_t e = cev::launch_compact(ca, to_hip(stream));
-    if (e != hipSuccess)
-        return CEV_ELAUNCH;
-
-    // The sweep takes the compacted rows in order: valid rows go round-robin
-    // over the chip whatever the mask pattern (sweeping every row in place
-    // and letting ignored rows exit measured 3 us faster with a random mask
-    // but 15 us slower when the ignored rows fell on some XCDs only).
+    // Launch-bound sizes sweep every row in place, ignored rows exiting at
+    // once, with the compaction in workgroups appended to the same launch:
+    // one launch instead of two.  Larger ones compact first and sweep the
+    // listed rows, which deals the valid rows round-robin over the chip
+    // whatever the mask pattern (in-place sweeping measured 3 us faster with
+    // a random mask on 8192 x 152064 bf16 rows but 15 us slower when the
+    // ignored rows all fell on some XCDs).
+    const bool in_place = splits == 1 && rows * vocab * (int64_t)elem_size(dtype) <= kInPlaceBytes;
     SweepArgs a{};
     a.logits = logits;
     a.rows = rows;
@@ -291,8 +278,30 @@ int ce_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stri
     a.labels = labels;
     a.ignore_index = ignore_index;
     a.row_mask = row_mask;
-    a.rowlist = list;
-    a.nlist = count;
+    if (in_place) {
+        a.out_list = list;
+        a.out_count = count;
+    } else {
+        CompactArgs ca{};
+        ca.rows = rows;
+        ca.vocab = vocab;
+        ca.labels = labels;
+        ca.ignore_index = ignore_index;
+        ca.row_mask = row_mask;
+        ca.rowlist = list;
+        ca.nlist = count;
+        ca.logp = logp;
+        ca.loss = loss;
+        ca.entropy = entropy;
+        ca.argmax = argmax;
+        ca.saved = static_cast<cev_saved *>(saved);
+        ca.status = status;
+        hipError_t e = cev::launch_compact(ca, to_hip(stream));
+        if (e != hipSuccess)
+            return CEV_ELAUNCH;
+        a.rowlist = list;
+        a.nlist = count;
+    }
     a.splits = splits;
     a.partials = partials;
     fill_temperature(a, temperature);

@@ -94,7 +94,7 @@ __device__ __forceinline__ bool compact_tile(const CompactTile &c, int64_t ti, i
 
 // Tiles of whole BLOCK-row sub-tiles, at most kMaxTiles of them.
 constexpr int64_t kMaxCompactTiles = 64;
-inline int64_t compact_tile_rows(int64_t rows, int block)
+__host__ __device__ inline int64_t compact_tile_rows(int64_t rows, int block)
 {
     const int64_t sub = (rows + block - 1) / block;
     const int64_t per = (sub + kMaxCompactTiles - 1) / kMaxCompactTiles;

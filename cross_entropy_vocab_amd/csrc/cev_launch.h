@@ -26,6 +26,8 @@ struct SweepArgs {
     const uint8_t *row_mask;
     const int64_t *rowlist;    // rows to sweep (compacted), or null for every row
     const int64_t *nlist;
+    int64_t *out_list;         // every-row sweeps only: if set, compaction workgroups
+    int64_t *out_count;        //   appended to the grid write the valid rows here
     int64_t splits;            // workgroups per row (1 = whole rows); needs partials
     void *partials;            // [rows * splits] SplitPartial, device scratch
     double temperature;

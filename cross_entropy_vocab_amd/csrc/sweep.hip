@@ -12,6 +12,7 @@
 // mask only in the one step that holds the target.  The sum is based at m_o,
 // the largest NON-target logit, so it is >= 1 and cannot underflow to zero
 // even when every other term is below the fp32 normal range.
+#include "cev_compact.h"
 #include "cev_device.h"
 #include "cev_launch.h"
 #include "cev_rowclose.h"
@@ -43,7 +44,9 @@ __device__ void close_row(const SweepArgs &a, int64_t r, const char *rowp, int64
 // SPLIT, `a.splits` workgroups share one row (block b * splits + p takes part
 // p of compacted row b) and each writes a partial record for k_merge instead
 // of closing the row.  Without a row list, block r takes row r (ignored rows
-// only write their zero outputs).
+// only write their zero outputs); with a.out_list set, the blocks after the
+// last row compact the valid rows into it (they are dispatched last, so the
+// compaction overlaps the final rows' sweeps and costs no launch of its own).
 template <int DT, int BLOCK, int U, bool WANT_H, bool WANT_ARG, bool SPLIT, bool WANT_Z>
 __global__ __launch_bounds__(BLOCK) void k_sls_sweep(SweepArgs a)
 {
@@ -51,7 +54,25 @@ __global__ __launch_bounds__(BLOCK) void k_sls_sweep(SweepArgs a)
     __shared__ float sh_f[W];
     __shared__ double sh_d[W];
     __shared__ int64_t sh_i[W];
+    __shared__ int sh_c[W];
     const int tid = threadIdx.x;
+
+    if constexpr (!SPLIT) {
+        if (a.out_list && (int64_t)blockIdx.x >= a.rows) {
+            CompactTile c;
+            c.labels = a.labels;
+            c.row_mask = a.row_mask;
+            c.ignore_index = a.ignore_index;
+            c.vocab = a.vocab;
+            c.rows = a.rows;
+            c.tile = compact_tile_rows(a.rows, BLOCK);
+            c.ntiles = (a.rows + c.tile - 1) / c.tile;
+            c.list = a.out_list;
+            c.count = a.out_count;
+            compact_tile<BLOCK>(c, (int64_t)blockIdx.x - a.rows, sh_c);
+            return;
+        }
+    }
 
     int64_t b = blockIdx.x, part = 0, parts = 1;
     if constexpr (SPLIT) {
@@ -353,7 +374,10 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
 template <int DT, int BLOCK, int U, bool SPLIT, bool WANT_Z>
 void launch_sls_z(const SweepArgs &a, bool want_h, bool want_arg, hipStream_t s)
 {
-    dim3 grid((unsigned)(a.rows * (SPLIT ? a.splits : 1))), block(BLOCK);
+    int64_t extra = 0;   // compaction workgroups of an every-row sweep
+    if (!SPLIT && !a.rowlist && a.out_list)
+        extra = (a.rows + compact_tile_rows(a.rows, BLOCK) - 1) / compact_tile_rows(a.rows, BLOCK);
+    dim3 grid((unsigned)(a.rows * (SPLIT ? a.splits : 1) + extra)), block(BLOCK);
     if (want_h && want_arg)
         hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, true, true, SPLIT, WANT_Z>), grid, block, 0, s, a);
     else if (want_h)
