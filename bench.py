@@ -130,9 +130,9 @@ def write_traffic(fetch_csv, write_csv, rows=8192, vocab=152064):
         "traffic_over_algorithmic": e["ratio"],
         "commands": [
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/prof_fetch -o grpo -- "
-            "python bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-linear --no-jsd --copy-calibration",
+            "python bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-linear --no-jsd --no-configs --copy-calibration",
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/prof_write -o grpo -- "
-            "python bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-linear --no-jsd --copy-calibration",
+            "python bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-linear --no-jsd --no-configs --copy-calibration",
             "python bench.py --traffic-from <out>/prof_fetch/grpo_counter_collection.csv "
             "<out>/prof_write/grpo_counter_collection.csv"],
     }
