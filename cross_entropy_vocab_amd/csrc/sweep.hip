@@ -205,6 +205,7 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
     __shared__ double sh_d[W];
     __shared__ int64_t xcol[kMaxK];
     __shared__ float xz[kMaxK];
+    __shared__ double xterm[kMaxK];
     __shared__ unsigned char xfirst[kMaxK];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int64_t r = blockIdx.x;
@@ -339,6 +340,12 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
     const float Ball = fmaxf(Mall, -FLT_MAX);
     const double T = a.temperature;
     const double s_rest = S > 0.0 ? S * exp(((double)B - (double)Ball) / T) : 0.0;
+    // Each gathered column's term e^{(z - Ball)/T}, computed once (in
+    // parallel over the indices) and summed below in index order by every
+    // index that needs it.
+    for (int k = tid; k < K; k += BLOCK)
+        xterm[k] = xfirst[k] ? exp(((double)xz[k] - (double)Ball) / T) : 0.0;
+    __syncthreads();
     for (int k = tid; k < K; k += BLOCK) {
         if (xcol[k] < 0) {
             out[k] = 0.0f;
@@ -349,11 +356,13 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
         double s = s_rest;
         for (int k2 = 0; k2 < K; ++k2)
             if (xfirst[k2] && xcol[k2] != xcol[k])
-                s += exp(((double)xz[k2] - (double)Ball) / T);
+                s += xterm[k2];
         const double u = s > 0.0 ? log(s) + ((double)Ball - (double)xz[k]) / T : -INFINITY;
-        out[k] = (float)(-softplus64(u));
+        // softplus(u) and sigmoid(u) from one e^{-|u|}
+        const double e = exp(-fabs(u));
+        out[k] = (float)(-(fmax(u, 0.0) + log1p(e)));
         if (qout)
-            qout[k] = (float)sigmoid64(u);
+            qout[k] = (float)((u < 0.0 ? e : 1.0) / (1.0 + e));
     }
     if (a.saved && tid == 0) {
         // The row's normaliser over all columns, for the top-K backward:
@@ -361,7 +370,7 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
         double d = s_rest;
         for (int k2 = 0; k2 < K; ++k2)
             if (xfirst[k2])
-                d += exp(((double)xz[k2] - (double)Ball) / T);
+                d += xterm[k2];
         cev_saved sv;
         sv.m_z = Mall;
         sv.log2_d = (float)(log(d) * kLog2e);
