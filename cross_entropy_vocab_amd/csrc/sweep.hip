@@ -203,10 +203,13 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
     constexpr int64_t CH = (int64_t)kWave * U;
     __shared__ float sh_f[W];
     __shared__ double sh_d[W];
-    __shared__ int64_t xcol[kMaxK];
-    __shared__ float xz[kMaxK];
-    __shared__ double xterm[kMaxK];
-    __shared__ unsigned char xfirst[kMaxK];
+    // Dynamic LDS sized by K: the gathered columns, their values and terms,
+    // and first-occurrence flags (K <= kMaxK).
+    extern __shared__ __align__(16) unsigned char xlds[];
+    int64_t *xcol = reinterpret_cast<int64_t *>(xlds);
+    double *xterm = reinterpret_cast<double *>(xcol + a.K);
+    float *xz = reinterpret_cast<float *>(xterm + a.K);
+    unsigned char *xfirst = reinterpret_cast<unsigned char *>(xz + a.K);
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int64_t r = blockIdx.x;
     const int64_t V = a.vocab;
@@ -482,12 +485,13 @@ hipError_t launch_sls_sweep(int dtype, const SweepArgs &a, bool want_h, bool wan
 hipError_t launch_topk_sweep_cfg(int dtype, const SweepArgs &a, int block, int U, hipStream_t s)
 {
     dim3 grid((unsigned)a.rows);
+    const size_t lds = (size_t)a.K * (sizeof(int64_t) + sizeof(double) + sizeof(float) + 1);
 #define CEV_TOPK_CASE(B, UU)                                                                    \
     if (block == B && U == UU) {                                                                \
         if (dtype == CEV_BF16)                                                                  \
-            hipLaunchKernelGGL((k_topk_sweep<CEV_BF16, B, UU>), grid, dim3(B), 0, s, a);        \
+            hipLaunchKernelGGL((k_topk_sweep<CEV_BF16, B, UU>), grid, dim3(B), lds, s, a);      \
         else                                                                                    \
-            hipLaunchKernelGGL((k_topk_sweep<CEV_F32, B, UU>), grid, dim3(B), 0, s, a);         \
+            hipLaunchKernelGGL((k_topk_sweep<CEV_F32, B, UU>), grid, dim3(B), lds, s, a);       \
         return hipGetLastError();                                                               \
     }
     CEV_TOPK_CASE(128, 4)
