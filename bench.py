@@ -466,14 +466,26 @@ def main():
     torch.cuda.synchronize()
     assert int(out["n_valid"].item()) == n_valid
 
-    # K back-to-back steps: wall clock around all of them, and HIP events
-    # recorded on the library's stream (torch's current stream) between the
-    # calls.  The host runs ahead of the GPU, so each event pair brackets the
-    # GPU time of one call (its kernels plus the short dispatch gap).
+    # K back-to-back steps timed by the wall clock between synchronizations
+    # (value); the same K steps again with HIP events recorded on the
+    # library's stream (torch's current stream) between the calls, for the
+    # per-call times (the host runs ahead of the GPU, so each event pair
+    # brackets one call's kernels plus the short dispatch gap); then the K
+    # steps once more by the wall clock, an A/A rerun whose gap to the first
+    # is the run-to-run noise.
+    def timed_steps():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            cev.ce_forward(logits, labels, T, row_mask=mask, logp=True, argmax=True, out=out)
+            cev.ce_backward(logits, labels, g, out["saved"], T, row_mask=mask, dlogits=dl)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / args.steps * 1e3
+
     log(f"[bench] timing {args.steps} steps")
+    ms_step = timed_steps()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for e0, e1, e2 in ev:
         e0.record()
         cev.ce_forward(logits, labels, T, row_mask=mask, logp=True, argmax=True, out=out)
@@ -481,12 +493,11 @@ def main():
         cev.ce_backward(logits, labels, g, out["saved"], T, row_mask=mask, dlogits=dl)
         e2.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall / args.steps * 1e3
     fwd_ms = [e0.elapsed_time(e1) for e0, e1, _ in ev]
     bwd_ms = [e1.elapsed_time(e2) for _, e1, e2 in ev]
     fwd = float(np.mean(fwd_ms))
     bwd = float(np.mean(bwd_ms))
+    ms_step_aa = timed_steps()
 
     # The same step as one call (g known up front): ce_fused.
     fout = cev.ce_fused(logits, labels, g, T, row_mask=mask, logp=True, argmax=True,
@@ -577,7 +588,15 @@ def main():
         "hbm_GBps": step_bytes / (ms_step / 1e3) / 1e9,
         "hbm_frac_of_peak": step_bytes / (ms_step / 1e3) / 1e9 / PEAK_HBM_GBS,
         "step_algorithmic_bytes": step_bytes,
+        "aa_rerun": {"ms_per_step": ms_step_aa,
+                     "relative_difference": (ms_step_aa - ms_step) / ms_step},
         "kernels_ms": {"ce_forward": fwd, "ce_backward": bwd,
+                       "ce_forward_median": float(np.median(fwd_ms)),
+                       "ce_forward_p10_p90": [float(np.percentile(fwd_ms, 10)),
+                                              float(np.percentile(fwd_ms, 90))],
+                       "ce_backward_median": float(np.median(bwd_ms)),
+                       "ce_backward_p10_p90": [float(np.percentile(bwd_ms, 10)),
+                                               float(np.percentile(bwd_ms, 90))],
                        "ce_backward_min": float(np.min(bwd_ms)),
                        "ce_backward_max": float(np.max(bwd_ms)),
                        "ce_forward_GBps": fwd_bytes / (fwd / 1e3) / 1e9,
@@ -606,7 +625,7 @@ def main():
                         "shard_forward_GBps": n_valid * Vs * ES / (s_fwd / 1e3) / 1e9,
                         "shard_backward_GBps": (n_valid + R) * Vs * ES / (s_bwd / 1e3) / 1e9},
     }
-    log(f"[bench] {ms_step:.3f} ms/step, fwd {fwd:.3f} ms, bwd {bwd:.3f} ms; "
+    log(f"[bench] {ms_step:.3f} ms/step (A/A rerun {ms_step_aa:.3f}), fwd {fwd:.3f} ms, bwd {bwd:.3f} ms; "
         f"fused {fused_wall:.3f} ms/step; vocab shard {shard_wall:.3f} ms/step "
         f"(fwd {s_fwd:.3f}, merge {s_mrg:.3f}, bwd {s_bwd:.3f})")
     if args.copy_calibration:
