@@ -306,13 +306,19 @@ def bench_jsd(args, torch, cev, workloads, dev):
     return res
 
 
-def _time_calls(torch, calls, iters, warmup=3):
-    """Mean GPU time in ms of each call in `calls` (a list of zero-argument
-    functions run in order, iters times), from HIP events recorded on the
-    library's stream between the calls."""
-    for _ in range(warmup):
+def _time_calls(torch, calls, iters, warmup_s=0.05):
+    """Mean GPU time in ms of each call in `calls` (functions of the iteration
+    index, run in order, iters times), from HIP events recorded on the
+    library's stream between the calls.  The calls first run back to back for
+    at least warmup_s seconds: after the host-side input generation the GPU
+    has idled, and its clocks take a while to come back up."""
+    t_end = time.perf_counter() + warmup_s
+    n = 0
+    while n < 3 or time.perf_counter() < t_end:
         for c in calls:
-            c(0)
+            c(n)
+        torch.cuda.synchronize()
+        n += 1
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
           for _ in range(iters)]
     torch.cuda.synchronize()
