@@ -272,10 +272,12 @@ def bench_jsd(args, torch, cev, workloads, dev):
     dl = torch.empty_like(st)
     for beta in (0.0, 0.5, 1.0):
         out = cev.jsd_forward(st, te, 1.0, beta, labels=lab, row_mask=msk)
-        for _ in range(2):
+        t_end = time.perf_counter() + 0.05          # warm up for 50 ms (GPU clocks)
+        while time.perf_counter() < t_end:
             cev.jsd_forward(st, te, 1.0, beta, labels=lab, row_mask=msk, out=out)
             cev.jsd_backward(st, te, g, out["saved"], 1.0, beta, labels=lab, row_mask=msk,
                              dstudent=dl)
+            torch.cuda.synchronize()
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         torch.cuda.synchronize()
         for e0, e1, e2 in ev:
