@@ -281,12 +281,12 @@ hipError_t launch_backward(int dtype, const BackwardArgs &a, hipStream_t stream)
 
 // Explicit launch configurations (workgroup size, 16-byte vectors per thread
 // per step, and for the backward the steps per workgroup, 0 = a whole row,
-// and whether rows are walked from the last to the first).
+// and the tile order: 0 row order, 1 rows from the last, 2 XCD-contiguous).
 // The entry points above pick one of these; tuning harnesses call them directly.
 hipError_t launch_sls_sweep_cfg(int dtype, const SweepArgs &a, bool want_entropy,
                                 bool want_argmax, int block, int U, hipStream_t stream);
 hipError_t launch_backward_cfg(int dtype, const BackwardArgs &a, int block, int U, int iters,
-                               int reverse, int store_nt, hipStream_t stream);
+                               int order, int store_nt, hipStream_t stream);
 hipError_t launch_topk_sweep_cfg(int dtype, const SweepArgs &a, int block, int U, hipStream_t stream);
 hipError_t launch_topk_backward_cfg(int dtype, const TopkBackwardArgs &a, int block, int U,
                                     hipStream_t stream);
