@@ -364,6 +364,22 @@ def bench_configs(args, torch, cev, workloads, dev):
                      "ce_forward_us": f * 1e3, "ce_backward_us": b * 1e3}
         log(f"[bench] {name}: forward {f * 1e3:.1f} us, backward {b * 1e3:.1f} us")
 
+    # Few long rows: ce_forward splits each row over several workgroups and
+    # merges their partial records (the workspace the binding allocates holds
+    # them).
+    w = workloads.grpo(rows=8)
+    z = dev_logits(w["logits"])
+    lab = torch.from_numpy(w["labels"]).to(dev)
+    out = cev.ce_forward(z, lab, 1.0, logp=True, argmax=True)
+    (f,) = _time_calls(torch, [lambda i: cev.ce_forward(z, lab, 1.0, logp=True, argmax=True,
+                                                         out=out)], iters)
+    nb = z.shape[0] * z.shape[1] * 2
+    res["split_8x152064_bf16"] = {"calls": "ce_forward (split rows: partial records + merge)",
+                                  "ce_forward_us": f * 1e3,
+                                  "ce_forward_GBps": nb / (f / 1e3) / 1e9}
+    log(f"[bench] split 8 rows: ce_forward {f * 1e3:.1f} us")
+    del z
+
     w = workloads.chunk()
     R, V = w["logits"].shape
     copies = [dev_logits(w["logits"])]
