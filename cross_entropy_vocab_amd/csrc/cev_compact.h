@@ -92,7 +92,7 @@ __device__ __forceinline__ bool compact_tile(const CompactTile &c, int64_t ti, i
     return bad_seen;
 }
 
-// Tiles of whole BLOCK-row sub-tiles, at most kMaxTiles of them.
+// Tiles of whole BLOCK-row sub-tiles, at most kMaxCompactTiles of them.
 constexpr int64_t kMaxCompactTiles = 64;
 __host__ __device__ inline int64_t compact_tile_rows(int64_t rows, int block)
 {
