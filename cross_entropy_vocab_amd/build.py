@@ -35,6 +35,9 @@ def compile_flags() -> list:
         "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC,
         # packed fp32 VALU forms are kept out of generated code on purpose
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # leading scalar kernel arguments arrive in SGPRs at wave start (gfx950
+        # kernel-argument preloading; kernels taking one struct are unaffected)
+        "-mllvm", "-amdgpu-kernarg-preload-count=14",
     ]
 
 

@@ -211,6 +211,99 @@ __global__ __launch_bounds__(BLOCK) void k_backward(BackwardArgs a, int slices, 
 }
 
 // ------------------------------------------------------------------------
+// One-shot tiles for calls whose rows all start 16-byte aligned in both
+// matrices and hold a whole number of 16-byte vectors (no head or tail
+// columns), with the values that decide the tile's first load passed as
+// leading scalar kernel arguments.  Those arrive in SGPRs when the wave
+// starts (kernel-argument preloading on gfx950), so the saved record is the
+// only load in front of the tile's stream: one scalar round trip instead of
+// two (the argument block, then the record).  The remaining inputs (labels,
+// g, mask, constants) are loaded while the logits are in flight.
+//
+// Tiles are numbered in row order; workgroup b runs on XCD b % 8 and takes
+// tile (b % 8) * g8 + b / 8, so each XCD sweeps a contiguous eighth of the
+// matrix (a row's tiles then share one L2 for its record).  The row of tile
+// n is n / slices, computed as (n * mul) >> shift from host-side constants
+// (exact for n < 2^31).
+template <int DT, int BLOCK, int U, bool SHARD, bool SNT>
+__global__ __launch_bounds__(BLOCK) void k_backward_tile(const cev_saved *saved, const char *logits,
+                                                         uint64_t row_bytes, uint64_t mul,
+                                                         uint32_t shift, uint32_t slices,
+                                                         uint32_t g8, uint32_t total, BackwardArgs a)
+{
+    constexpr int VE = Elem<DT>::kVE;
+    constexpr uint32_t per = (uint32_t)BLOCK * U;
+    const int tid = threadIdx.x;
+    const uint32_t bid = (blockIdx.x % 8) * g8 + blockIdx.x / 8;
+    if (bid >= total)
+        return;
+    const uint32_t r = (uint32_t)(((uint64_t)bid * mul) >> shift);
+    const uint32_t sl = bid - r * slices;
+    const u32x4 rec = load_uniform(reinterpret_cast<const u32x4 *>(saved + r));
+    const uint32_t v0 = sl * per;
+    const u32x4 *lvp = reinterpret_cast<const u32x4 *>(logits + (size_t)r * row_bytes) + v0;
+    const int64_t nvec = a.vocab / VE;
+    const uint32_t nv = (uint32_t)(nvec - v0 < (int64_t)per ? nvec - v0 : per);
+    u32x4 w[U];
+    if (rec[3] & 1u) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t j = (uint32_t)(u * BLOCK + tid);
+            if (j < nv)
+                w[u] = load16_stream(lvp + j);
+        }
+    }
+    const int64_t tg = load_uniform(a.labels + r);
+    const float graw = load_uniform(a.g + r);
+    const bool masked = a.row_mask && mask_byte(a.row_mask, r) == 0;
+    const bool ignored = masked || tg == a.ignore_index;
+    const int64_t VT = SHARD ? a.vocab_total : a.vocab;
+    const bool bad = !ignored && (tg < 0 || tg >= VT);
+    if (bad && sl == 0 && tid == 0 && a.status)
+        atomicOr(a.status, (int32_t)CEV_STATUS_BAD_LABEL);
+    // The target column relative to the tile's first column (outside the
+    // tile, or the shard, when another holds it).
+    const int64_t t = (SHARD ? tg - a.col_offset : tg) - (int64_t)v0 * VE;
+    RowConst rc;
+    rc.valid = !ignored && !bad && (rec[3] & 1u);
+    rc.mz = __uint_as_float(rec[0]);
+    rc.sgn = 0u;
+    rc.kexp = 0.0f;
+    rc.ev = 0.0f;
+    rc.tval = 0.0f;
+    if (rc.valid) {
+        const float gp = graw * a.inv_t;
+        const float ag = fabsf(gp);
+        rc.sgn = __float_as_uint(gp) & 0x80000000u;
+        rc.kexp = __uint_as_float(rec[1]) - __log2f(ag);
+        rc.ev = ag * a.eps_over_v;
+        rc.tval = -(ag * ((__uint_as_float(rec[2]) - a.eps) + a.eps_over_v));
+    }
+    u32x4 *dvp = reinterpret_cast<u32x4 *>(static_cast<char *>(a.dlogits) +
+                                           (size_t)r * (size_t)a.d_row_stride * Elem<DT>::kSize) + v0;
+    if (!rc.valid) {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t j = (uint32_t)(u * BLOCK + tid);
+            if (j < nv)
+                store16<SNT>(zero, dvp + j);
+        }
+        return;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t j = (uint32_t)(u * BLOCK + tid);
+        if (j < nv) {
+            float z[VE], o[VE];
+            unpack16<DT>(w[u], z);
+            grad_vec<DT>(z, o, rc, a.c, (int64_t)j * VE, t);
+            store16<SNT>(pack_vec<DT>(o, rc.sgn), dvp + j);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
 // Top-K backward: gradient of sum_k g_k log p_{i_k} with respect to the
 // logits (ms-swift PR #10337, PR information: gradients through top-K
 // indices), dL/dz_j = (1/T) sum_k g_k ([j = i_k] - p_j).  Every column gets
@@ -425,6 +518,55 @@ hipError_t launch_bwd_t(const BackwardArgs &a, int iters, int order, hipStream_t
     return hipGetLastError();
 }
 
+// Multiply-shift division by d: for n < 2^31, n / d == (n * mul) >> shift
+// with shift = 32 + ceil(log2 d) and mul = ceil(2^shift / d).
+struct DivMagic {
+    uint64_t mul;
+    uint32_t shift;
+};
+
+inline DivMagic div_magic(uint32_t d)
+{
+    uint32_t l = 0;
+    while (((uint64_t)1 << l) < d)
+        ++l;
+    DivMagic m;
+    m.shift = 32 + l;
+    m.mul = (uint64_t)((((unsigned __int128)1 << m.shift) + d - 1) / d);
+    return m;
+}
+
+template <int DT, int BLOCK, int U, bool SHARD, bool SNT>
+hipError_t launch_bwd_tile_t(const BackwardArgs &a, hipStream_t s)
+{
+    const int64_t nvec = a.vocab / Elem<DT>::kVE;
+    const int64_t per = (int64_t)BLOCK * U;
+    const int64_t slices = (nvec + per - 1) / per;
+    const int64_t total = a.rows * slices;   // < 2^31, checked by the caller
+    const uint32_t g8 = (uint32_t)((total + 7) / 8);
+    const DivMagic dm = div_magic((uint32_t)slices);
+    const uint64_t row_bytes = (uint64_t)a.row_stride * Elem<DT>::kSize;
+    hipLaunchKernelGGL((k_backward_tile<DT, BLOCK, U, SHARD, SNT>), dim3(g8 * 8), dim3(BLOCK), 0, s,
+                       a.saved, static_cast<const char *>(a.logits), row_bytes, dm.mul, dm.shift,
+                       (uint32_t)slices, g8, (uint32_t)total, a);
+    return hipGetLastError();
+}
+
+// Tiles of `per` 16-byte vectors over every row.
+inline int64_t tile_count(const BackwardArgs &a, int es, int64_t per)
+{
+    const int64_t nvec = a.vocab * es / 16;
+    return a.rows * ((nvec + per - 1) / per);
+}
+
+// Whether every row of both matrices starts 16-byte aligned and holds whole
+// 16-byte vectors (the one-shot tile form's precondition).
+inline bool tile_form_ok(const BackwardArgs &a, int es)
+{
+    return ((uintptr_t)a.logits & 15u) == 0 && ((uintptr_t)a.dlogits & 15u) == 0 &&
+           (a.row_stride * es) % 16 == 0 && (a.d_row_stride * es) % 16 == 0 && (a.vocab * es) % 16 == 0;
+}
+
 } // namespace
 
 // Launch configuration, exposed for tuning harnesses.
@@ -460,14 +602,57 @@ hipError_t launch_backward_cfg(int dtype, const BackwardArgs &a, int block, int 
     return hipErrorInvalidValue;
 }
 
+// One-shot tile form with preloaded arguments, for tuning harnesses (rows
+// 16-byte aligned in both matrices, whole vectors; checked here).
+hipError_t launch_backward_tile_cfg(int dtype, const BackwardArgs &a, int block, int U, int store_nt,
+                                    hipStream_t s)
+{
+    const int es = dtype == CEV_BF16 ? 2 : 4;
+    if (!tile_form_ok(a, es) || tile_count(a, es, (int64_t)block * U) >= ((int64_t)1 << 31) ||
+        a.col_offset != 0 || a.vocab_total != a.vocab)
+        return hipErrorInvalidValue;
+#define CEV_BWT_CASE(B, UU, NT)                                                                     \
+    if (block == B && U == UU && (store_nt != 0) == NT)                                             \
+        return dtype == CEV_BF16 ? launch_bwd_tile_t<CEV_BF16, B, UU, false, NT>(a, s)              \
+                                 : launch_bwd_tile_t<CEV_F32, B, UU, false, NT>(a, s);
+    CEV_BWT_CASE(64, 4, true)
+    CEV_BWT_CASE(128, 1, true)
+    CEV_BWT_CASE(128, 2, true)
+    CEV_BWT_CASE(128, 2, false)
+    CEV_BWT_CASE(128, 4, true)
+    CEV_BWT_CASE(256, 1, true)
+    CEV_BWT_CASE(256, 1, false)
+    CEV_BWT_CASE(256, 2, true)
+    CEV_BWT_CASE(256, 2, false)
+    CEV_BWT_CASE(512, 1, true)
+    CEV_BWT_CASE(512, 1, false)
+#undef CEV_BWT_CASE
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_backward(int dtype, const BackwardArgs &a, hipStream_t s)
 {
-    // 4 KB workgroups (128 threads x 2 vectors, nontemporal stores): on the
-    // 8192 x 152064 bf16 backward 753-758 us against 781-821 us for
-    // 256 x 4 vectors, the best of 20 shapes (64-256 threads, 1-4 vectors,
-    // 1-3 steps, either store policy).  A vocab shard gets its own
-    // instantiation (and kernel name in traces).
-    if (a.col_offset != 0 || a.vocab_total != a.vocab)
+    const bool shard = a.col_offset != 0 || a.vocab_total != a.vocab;
+    // Rows 16-byte aligned in both matrices: one-shot 4 KB tiles of 256
+    // threads x 1 vector with preloaded arguments (on the 8192 x 152064 bf16
+    // backward 688 us against 706 us for the general kernel's 128 x 2 tiles,
+    // and 689-731 us for 128 x 1, 128 x 2, 256 x 2, 512 x 1, 64 x 4 and
+    // 128 x 4).  A vocab shard gets its own instantiation (and kernel name in
+    // traces).
+    const int es = dtype == CEV_BF16 ? 2 : 4;
+    if (tile_form_ok(a, es) && tile_count(a, es, 256) < ((int64_t)1 << 31)) {
+        if (dtype == CEV_BF16)
+            return shard ? launch_bwd_tile_t<CEV_BF16, 256, 1, true, true>(a, s)
+                         : launch_bwd_tile_t<CEV_BF16, 256, 1, false, true>(a, s);
+        return shard ? launch_bwd_tile_t<CEV_F32, 256, 1, true, true>(a, s)
+                     : launch_bwd_tile_t<CEV_F32, 256, 1, false, true>(a, s);
+    }
+    // Otherwise the general kernel (head and tail columns, rows whose two
+    // matrices disagree modulo 16 bytes): 4 KB workgroups of 128 threads x 2
+    // vectors with nontemporal stores, 753-758 us against 781-821 us for
+    // 256 x 4 on the same backward, the best of 20 shapes (64-256 threads,
+    // 1-4 vectors, 1-3 steps, either store policy).
+    if (shard)
         return dtype == CEV_BF16 ? launch_bwd_t<CEV_BF16, 128, 2, true, true>(a, 1, 2, s)
                                  : launch_bwd_t<CEV_F32, 128, 2, true, true>(a, 1, 2, s);
     return launch_backward_cfg(dtype, a, 128, 2, 1, 2, 1, s);

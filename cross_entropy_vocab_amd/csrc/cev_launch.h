@@ -287,6 +287,8 @@ hipError_t launch_sls_sweep_cfg(int dtype, const SweepArgs &a, bool want_entropy
                                 bool want_argmax, int block, int U, hipStream_t stream);
 hipError_t launch_backward_cfg(int dtype, const BackwardArgs &a, int block, int U, int iters,
                                int order, int store_nt, hipStream_t stream);
+hipError_t launch_backward_tile_cfg(int dtype, const BackwardArgs &a, int block, int U, int store_nt,
+                                    hipStream_t stream);
 hipError_t launch_topk_sweep_cfg(int dtype, const SweepArgs &a, int block, int U, hipStream_t stream);
 hipError_t launch_topk_backward_cfg(int dtype, const TopkBackwardArgs &a, int block, int U,
                                     hipStream_t stream);
