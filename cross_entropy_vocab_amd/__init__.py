@@ -17,7 +17,7 @@ import torch
 from . import _lib
 
 __all__ = ["sls_forward", "sls_topk_forward", "sls_topk_backward", "ce_forward",
-           "ce_backward", "ce_fused", "ce_vocab_shard_forward", "ce_vocab_merge",
+           "ce_forward_noalloc", "noalloc_scratch_bytes", "ce_backward", "ce_fused", "ce_vocab_shard_forward", "ce_vocab_merge",
            "ce_vocab_shard_backward", "lce_forward", "lce_backward", "lce_workspace_size",
            "jsd_forward", "jsd_backward", "workspace_size", "JSD_SAVED_BYTES",
            "status_string", "version", "CEV_F32", "CEV_BF16", "STATUS_BAD_LABEL",
@@ -245,6 +245,39 @@ def ce_forward(logits, labels, temperature=1.0, row_mask=None, ignore_index=-100
                                _stream(dev))
     _check("ce_forward", rc)
     return o
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(_lib.get().cev_noalloc_scratch_bytes())
+
+
+def ce_forward_noalloc(logits, labels, temperature=1.0, row_mask=None, ignore_index=-100,
+                       status=None, label_smoothing=0.0, *, loss, saved, logp=None, entropy=None,
+                       argmax=None, valid_rows=None, n_valid=None):
+    """ce_forward into caller-provided outputs, with the library's static
+    per-GPU scratch in place of a workspace: no device memory is allocated
+    here or in the library.  Outputs as in ce_forward (loss and saved
+    required, the others optional); calls that overlap on one GPU race."""
+    rows, vocab, stride = _check_logits(logits)
+    dev = logits.device
+    _dev(labels, "labels", torch.int64, (rows,), dev)
+    m = _mask(row_mask, rows, dev)
+    _dev(status, "status", torch.int32, (1,), dev)
+    _dev(loss, "loss", torch.float32, (rows,), dev)
+    _dev(saved, "saved", torch.uint8, (rows, SAVED_BYTES), dev)
+    for t, name, dt, shape in ((logp, "logp", torch.float32, (rows,)),
+                               (entropy, "entropy", torch.float32, (rows,)),
+                               (argmax, "argmax", torch.int64, (rows,)),
+                               (valid_rows, "valid_rows", torch.int64, (rows,)),
+                               (n_valid, "n_valid", torch.int64, (1,))):
+        if t is not None:
+            _dev(t, name, dt, shape, dev)
+    rc = _lib.get().ce_forward_noalloc(_ptr(logits), rows, vocab, stride, _dtype_code(logits),
+                                       _ptr(labels), int(ignore_index), float(temperature),
+                                       float(label_smoothing), _ptr(m), _ptr(loss), _ptr(saved),
+                                       _ptr(logp), _ptr(entropy), _ptr(argmax), _ptr(valid_rows),
+                                       _ptr(n_valid), _ptr(status), _stream(dev))
+    _check("ce_forward_noalloc", rc)
 
 
 def ce_backward(logits, labels, g, saved, temperature=1.0, row_mask=None, ignore_index=-100,

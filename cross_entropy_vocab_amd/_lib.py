@@ -26,6 +26,9 @@ SIGNATURES = {
                                 P, P]),
     "ce_forward": (I32, [P, I64, I64, I64, I32, P, I64, D, D, P, P, P, P, P, P, P, P, P, SZ, P,
                          P]),
+    "ce_forward_noalloc": (I32, [P, I64, I64, I64, I32, P, I64, D, D, P, P, P, P, P, P, P, P, P,
+                                 P]),
+    "cev_noalloc_scratch_bytes": (SZ, []),
     "ce_backward": (I32, [P, I64, I64, I64, I32, P, I64, D, D, P, P, P, P, I64, P, P]),
     "ce_fused": (I32, [P, I64, I64, I64, I32, P, I64, D, D, P, P, P, P, P, P, P, P, I64, P, P, P,
                        SZ, P, P]),

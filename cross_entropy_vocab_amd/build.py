@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcevocab.so")
 SOURCES = ["sweep.hip", "backward.hip", "compact.hip", "fused.hip", "shard.hip", "lce.hip", "jsd.hip",
-           "api.cpp"]
+           "noalloc.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

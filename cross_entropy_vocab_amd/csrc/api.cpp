@@ -871,6 +871,8 @@ const char *cev_status_string(int code)
     case CEV_ELAUNCH: return "kernel launch failed";
     case CEV_ESMOOTH: return "label_smoothing must be finite and in [0, 1]";
     case CEV_EBETA: return "beta must be finite and in [0, 1]";
+    case CEV_ESCRATCH: return "ce_forward_noalloc: the call needs more than the static scratch "
+                              "(rows > 524287), or its device address could not be looked up";
     default: return "unknown error code";
     }
 }

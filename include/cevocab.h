@@ -77,7 +77,9 @@ enum cev_error {
     CEV_EALIAS = -8,       /* dlogits overlaps logits */
     CEV_ELAUNCH = -9,      /* the HIP runtime refused a launch */
     CEV_ESMOOTH = -10,     /* label_smoothing not finite or outside [0, 1] */
-    CEV_EBETA = -11        /* jsd beta not finite or outside [0, 1] */
+    CEV_EBETA = -11,       /* jsd beta not finite or outside [0, 1] */
+    CEV_ESCRATCH = -12     /* ce_forward_noalloc: the call needs more than the static scratch,
+                              or the scratch's device address could not be looked up */
 };
 
 /* Bits ORed into the optional device status word. */
@@ -208,6 +210,30 @@ int ce_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stri
                double label_smoothing, const uint8_t *row_mask, float *loss, void *saved, float *logp, float *entropy,
                int64_t *argmax, int64_t *valid_rows, int64_t *n_valid, void *workspace,
                size_t workspace_bytes, int32_t *status, cev_stream_t stream);
+
+/*
+ * ce_forward_noalloc -- ce_forward without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments, outputs,
+ * errors and results as ce_forward (bit for bit); the workspace lives in a
+ * static device array of cev_noalloc_scratch_bytes() bytes (4 MiB) that each
+ * GPU holds until the process ends.  A call whose cev_workspace_size(rows,
+ * vocab, dtype) exceeds it (rows > 524287) returns CEV_ESCRATCH before
+ * anything is enqueued.  The first call on each device looks up the array's
+ * device address (hipGetSymbolAddress, no allocation); a caller that captures
+ * graphs makes one ordinary call on that device first.  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (different streams,
+ * or host threads) race and must be serialized by the caller.  Nothing is
+ * allocated, freed or synchronized.
+ */
+int ce_forward_noalloc(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride,
+                       int dtype, const int64_t *labels, int64_t ignore_index, double temperature,
+                       double label_smoothing, const uint8_t *row_mask, float *loss, void *saved,
+                       float *logp, float *entropy, int64_t *argmax, int64_t *valid_rows,
+                       int64_t *n_valid, int32_t *status, cev_stream_t stream);
+
+/* Size in bytes of the static scratch that ce_forward_noalloc uses per GPU. */
+size_t cev_noalloc_scratch_bytes(void);
 
 /*
  * ce_backward -- analytic gradient of the per-row loss with respect to the
