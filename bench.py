@@ -156,6 +156,9 @@ def cpu_baseline(w, valid_rows, seconds=12.0, threads=None):
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
+    # One GPU's share of the machine's host cores is 16 threads, whatever the
+    # machine's total; the oracle uses that share (or fewer if fewer are
+    # available to this process).
     threads = threads or min(16, oracle.default_threads())
     rng = np.random.default_rng(123)
     order = rng.permutation(valid_rows)
@@ -176,9 +179,28 @@ def cpu_baseline(w, valid_rows, seconds=12.0, threads=None):
             list(ex.map(grad_row, rows))
             done += rows.shape[0]
     dt = time.perf_counter() - t0
+    try:
+        affinity = sorted(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = []
     return {"value": done / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "host_cpu_count": os.cpu_count(), "affinity_cpus": len(affinity),
+            "affinity": _cpu_ranges(affinity),
+            "threads_note": "capped at 16 threads, one GPU's share of the host's cores",
             "sample": f"{done} random valid rows of the 8192x152064 bf16 workload "
                       f"(forward with argmax + full gradient row each), {dt:.1f} s wall"}
+
+
+def _cpu_ranges(cpus):
+    """'0-15,32-47' style text for a sorted list of CPU ids."""
+    out, i = [], 0
+    while i < len(cpus):
+        j = i
+        while j + 1 < len(cpus) and cpus[j + 1] == cpus[j] + 1:
+            j += 1
+        out.append(f"{cpus[i]}" if i == j else f"{cpus[i]}-{cpus[j]}")
+        i = j + 1
+    return ",".join(out)
 
 
 def bench_linear(args, torch, cev, workloads, dev):
@@ -439,6 +461,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="back-to-back steps for at least this long before the counted warmup")
     ap.add_argument("--rows", type=int, default=8192)
     ap.add_argument("--vocab", type=int, default=152064)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -483,10 +507,25 @@ def main():
     dl = torch.empty((R, V), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
+    def step():
         cev.ce_forward(logits, labels, T, row_mask=mask, logp=True, argmax=True, out=out)
         cev.ce_backward(logits, labels, g, out["saved"], T, row_mask=mask, dlogits=dl)
+
+    # The GPU idled during the host-side input generation and its clocks take
+    # a while to come back: settle them with back-to-back steps (synchronized
+    # every 10) for at least --settle-ms before the counted warmup.
+    log(f"[bench] settling clocks for {args.settle_ms:.0f} ms, then warmup {args.warmup}")
+    t_settle = time.perf_counter()
+    settle_steps = 0
+    while settle_steps < 10 or (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        step()
+        settle_steps += 1
+        if settle_steps % 10 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
     assert int(out["n_valid"].item()) == n_valid
 
@@ -501,8 +540,7 @@ def main():
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
-            cev.ce_forward(logits, labels, T, row_mask=mask, logp=True, argmax=True, out=out)
-            cev.ce_backward(logits, labels, g, out["saved"], T, row_mask=mask, dlogits=dl)
+            step()
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / args.steps * 1e3
 
@@ -522,6 +560,29 @@ def main():
     fwd = float(np.mean(fwd_ms))
     bwd = float(np.mean(bwd_ms))
     ms_step_aa = timed_steps()
+
+    # Scrub A/B for the backward: the same call timed right after ce_forward
+    # (as in the step) and after a 1 GiB read that leaves none of the logits
+    # in the 256 MB Infinity Cache (a read, so that no dirty lines of the
+    # scrub itself are written back during the backward).  Equal times mean
+    # the backward's rate is HBM's, not the cache's.
+    scrub = torch.ones(2 ** 28, dtype=torch.float32, device=dev)
+    scrub_ab = {"after_forward": [], "after_scrub": []}
+    for i in range(2 * max(4, args.steps // 2)):
+        key = "after_scrub" if i % 2 else "after_forward"
+        cev.ce_forward(logits, labels, T, row_mask=mask, logp=True, argmax=True, out=out)
+        if key == "after_scrub":
+            scrub_sum = scrub.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cev.ce_backward(logits, labels, g, out["saved"], T, row_mask=mask, dlogits=dl)
+        e1.record()
+        torch.cuda.synchronize()
+        scrub_ab[key].append(e0.elapsed_time(e1))
+    del scrub
+    scrub_ab = {k: float(np.median(v)) for k, v in scrub_ab.items()}
+    scrub_ab["scrub"] = "1 GiB float32 read (torch sum) between ce_forward and ce_backward"
+    del scrub_sum
 
     # The same step as one call (g known up front): ce_fused.
     fout = cev.ce_fused(logits, labels, g, T, row_mask=mask, logp=True, argmax=True,
@@ -614,6 +675,9 @@ def main():
         "step_algorithmic_bytes": step_bytes,
         "aa_rerun": {"ms_per_step": ms_step_aa,
                      "relative_difference": (ms_step_aa - ms_step) / ms_step},
+        "clock_settle": {"ms": settle_ms, "steps": settle_steps,
+                         "note": "back-to-back steps before the counted warmup"},
+        "backward_scrub_ab_ms": scrub_ab,
         "kernels_ms": {"ce_forward": fwd, "ce_backward": bwd,
                        "ce_forward_median": float(np.median(fwd_ms)),
                        "ce_forward_p10_p90": [float(np.percentile(fwd_ms, 10)),

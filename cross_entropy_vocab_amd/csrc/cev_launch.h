@@ -28,6 +28,7 @@ struct SweepArgs {
     const int64_t *nlist;
     int64_t *out_list;         // every-row sweeps only: if set, compaction workgroups
     int64_t *out_count;        //   appended to the grid write the valid rows here
+    int swizzle;               // every-row sweeps: block b takes row swizzle_row(b)
     int64_t splits;            // workgroups per row (1 = whole rows); needs partials
     void *partials;            // [rows * splits] SplitPartial, device scratch
     double temperature;

@@ -128,8 +128,14 @@ __device__ __forceinline__ RowGeom row_geom(const char *rowp, int64_t V, int64_t
     int64_t h = (int64_t)(((16u - ((unsigned)(uintptr_t)rowp & 15u)) & 15u) / ES);
     g.ahead = h < V ? h : V;
     const int64_t nv = (V - g.ahead) / VE;
-    g.vbeg = nv * p / parts;
-    g.nvec = nv * (p + 1) / parts - g.vbeg;
+    if (parts == 1) {
+        // whole rows: no 64-bit divisions in front of the first load
+        g.vbeg = 0;
+        g.nvec = nv;
+    } else {
+        g.vbeg = nv * p / parts;
+        g.nvec = nv * (p + 1) / parts - g.vbeg;
+    }
     g.nfull = g.nvec / CH;
     g.nrem = g.nvec - g.nfull * CH;
     g.head = p == 0 ? (int)g.ahead : 0;
@@ -225,6 +231,16 @@ __device__ __forceinline__ RowStats sweep_row(const char *rowp, int64_t V, int64
     const int64_t col_v = g.ahead + g.vbeg * VE;   // first column of the range's vectors
     LaneState st{-INFINITY, 0.0f, 0.0f, 0.0f, 0.0f, -1};
 
+    // The wave's first step goes out before anything that needs the target
+    // column (whose load may still be in flight).
+    int64_t k = wave;
+    u32x4 cur[U], nxt[U];
+    if (k < g.nfull) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            cur[u] = load16<NT>(vp + k * CH + u * kWave + lane);
+    }
+
     if (tid < g.head) {
         float v[1] = {tid == t ? -INFINITY : load_elem<DT>(rowp, tid)};
         fold<DT, 1, WANT_H, WANT_ARG, true, WANT_Z>(st, v, tid, c, inv_t);
@@ -233,13 +249,6 @@ __device__ __forceinline__ RowStats sweep_row(const char *rowp, int64_t V, int64
     // Full wave steps, interleaved over the waves, one step of loads in flight
     // ahead of the arithmetic.
     {
-        int64_t k = wave;
-        u32x4 cur[U], nxt[U];
-        if (k < g.nfull) {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                cur[u] = load16<NT>(vp + k * CH + u * kWave + lane);
-        }
         for (; k < g.nfull; k += W) {
             const int64_t kn = k + W;
             if (kn < g.nfull) {

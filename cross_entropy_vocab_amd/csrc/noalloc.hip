@@ -15,7 +15,7 @@
 
 namespace {
 
-constexpr size_t kScratchBytes = (size_t)4 << 20;  // rows <= 524287 (the list and its count)
+constexpr size_t kScratchBytes = (size_t)4 << 20;  // the list and count of up to 524287 rows
 constexpr int kMaxDevices = 64;
 
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];

@@ -39,6 +39,20 @@ __device__ void close_row(const SweepArgs &a, int64_t r, const char *rowp, int64
                    a.label_smoothing, a.vocab);
 }
 
+// Row of block b in a swizzled every-row sweep.  Workgroup b runs on XCD
+// b % 8; within each whole group of 8 blocks the rows are rotated by a hash
+// of the group index (Fibonacci hashing, the top 3 bits of g * 2^32/phi), so
+// that the rows a periodic mask ignores (every 2nd ... 100th) land on all
+// XCDs about equally -- in row order every 10th row would fall on 4 of the 8
+// -- while each group still covers 8 neighbouring rows.
+__device__ __forceinline__ int64_t swizzle_row(int64_t b, int64_t rows)
+{
+    if (b >= (rows & ~(int64_t)7))
+        return b;
+    const uint32_t rot = ((uint32_t)((uint64_t)b >> 3) * 0x9E3779B1u) >> 29;
+    return (b & ~(int64_t)7) | ((b + rot) & 7);
+}
+
 // ------------------------------------------------------------------------
 // Single-target sweep: sls_forward and the sweep stage of ce_forward.  With
 // SPLIT, `a.splits` workgroups share one row (block b * splits + p takes part
@@ -86,7 +100,7 @@ __global__ __launch_bounds__(BLOCK) void k_sls_sweep(SweepArgs a)
             return;
         r = load_uniform(a.rowlist + b);
     } else {
-        r = b;
+        r = a.swizzle ? swizzle_row(b, a.rows) : b;
     }
     const int64_t V = a.vocab;
     const int64_t t = load_uniform(a.labels + r);
@@ -142,23 +156,17 @@ __global__ __launch_bounds__(BLOCK) void k_sls_sweep(SweepArgs a)
     }
 }
 
-// Merge of the split partials (fixed order, fp64), then the closing step: one
-// wave per compacted row.  Part p holds, over its columns, the largest
-// non-target logit m_p, its lowest column, the sum S_p based at B_p =
-// max(m_p, -FLT_MAX) and the entropy term H_p at the same base; moving to the
-// common base B multiplies both by e^{(B_p - B)/T} and adds (B - B_p)/T * S_p
-// to H_p (the partial/combine rescaling of the unsloth-zoo #2080 Summary
-// quoted on the Liger-Kernel PR #1555 page).
+// Merge of a row's split partials (fixed order, fp64), then the closing step,
+// by one wave: lane l reads parts l, l + 64, ...  Part p holds, over its
+// columns, the largest non-target logit m_p, its lowest column, the sum S_p
+// based at B_p = max(m_p, -FLT_MAX) and the entropy term H_p at the same
+// base; moving to the common base B multiplies both by e^{(B_p - B)/T} and
+// adds (B - B_p)/T * S_p to H_p (the partial/combine rescaling of the
+// unsloth-zoo #2080 Summary quoted on the Liger-Kernel PR #1555 page).
 template <int DT, bool WANT_H, bool WANT_ARG>
-__global__ __launch_bounds__(256) void k_merge(SweepArgs a)
+__device__ __forceinline__ void merge_close(const SweepArgs &a, int64_t r, const SplitPartial *pp,
+                                            int parts, int lane)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t b = (int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
-    if (b >= *a.nlist)
-        return;
-    const int64_t r = a.rowlist[b];
-    const int parts = a.splits;
-    const SplitPartial *pp = static_cast<const SplitPartial *>(a.partials) + b * parts;
     float m = -INFINITY;
     for (int p = lane; p < parts; p += kWave)
         m = fmaxf(m, pp[p].m);
@@ -191,6 +199,18 @@ __global__ __launch_bounds__(256) void k_merge(SweepArgs a)
                            (size_t)r * (size_t)a.row_stride * Elem<DT>::kSize;
         close_row<DT, WANT_H, WANT_ARG>(a, r, rowp, a.labels[r], M, S, H, Z, arg);
     }
+}
+
+// The split-row merge as its own launch: one wave per compacted row.
+template <int DT, bool WANT_H, bool WANT_ARG>
+__global__ __launch_bounds__(256) void k_merge(SweepArgs a)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t b = (int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+    if (b >= *a.nlist)
+        return;
+    merge_close<DT, WANT_H, WANT_ARG>(a, a.rowlist[b], static_cast<const SplitPartial *>(a.partials) +
+                                                          b * a.splits, (int)a.splits, lane);
 }
 
 // ------------------------------------------------------------------------

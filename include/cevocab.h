@@ -202,7 +202,9 @@ int sls_topk_backward(const void *logits, int64_t rows, int64_t vocab, int64_t r
  *                 and a 32-byte aligned workspace, else whole rows are swept
  *                 (same results up to rounding, lower occupancy).  When
  *                 valid_rows or n_valid is NULL the workspace also holds them and
- *                 must be at least (rows + 1) * 8 bytes, 8-byte aligned.
+ *                 must be at least (rows + 1) * 8 bytes, 8-byte aligned;
+ *                 when both are NULL it may be NULL too, and then every row
+ *                 is swept in place with no list (same results).
  *                 The workspace is overwritten; calls that share one race.
  */
 int ce_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stride, int dtype,
@@ -218,8 +220,8 @@ int ce_forward(const void *logits, int64_t rows, int64_t vocab, int64_t row_stri
  * errors and results as ce_forward (bit for bit); the workspace lives in a
  * static device array of cev_noalloc_scratch_bytes() bytes (4 MiB) that each
  * GPU holds until the process ends.  A call whose cev_workspace_size(rows,
- * vocab, dtype) exceeds it (rows > 524287) returns CEV_ESCRATCH before
- * anything is enqueued.  The first call on each device looks up the array's
+ * vocab, dtype) exceeds it (more than 524287 rows) returns CEV_ESCRATCH
+ * before anything is enqueued.  The first call on each device looks up the array's
  * device address (hipGetSymbolAddress, no allocation); a caller that captures
  * graphs makes one ordinary call on that device first.  Every call on a GPU
  * shares that GPU's array: calls that overlap on one GPU (different streams,

@@ -166,7 +166,10 @@ def test_ce_forward_validation(lib):
                               a["saved"],
                               a["logp"], a["ent"], a["arg"], a["vr"], a["nv"], a["ws"], a["wsb"],
                               a["status"], None)
-    assert call() == E["NULL"]                       # no list/count and no workspace
+    # A list output asked for without the other and without a workspace (both
+    # absent with no workspace is accepted: every row is swept in place).
+    assert call(vr=A) == E["NULL"]
+    assert call(nv=A) == E["NULL"]
     assert call(ws=A, wsb=39) == E["WORKSPACE"]      # needs (4 + 1) * 8 = 40 bytes
     assert call(ws=A + 4, wsb=40) == E["ALIGN"]
     assert call(vr=A, nv=A, saved=A + 8) == E["ALIGN"]  # saved records are 16-byte aligned

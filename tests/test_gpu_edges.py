@@ -355,8 +355,9 @@ FUSED_CASES = {
 
 @pytest.mark.parametrize("name", sorted(FUSED_CASES))
 def test_ce_fused_matches_oracle(name):
-    """ce_fused against the oracle on every output, in both its one-pass form
-    (row resident in registers) and its two-pass fallback."""
+    """ce_fused against the oracle on every output, in both its fused form
+    (16-byte-aligned rows: one workgroup sweeps, closes and re-reads each row)
+    and its fallback to ce_forward + ce_backward (other alignments)."""
     w = FUSED_CASES[name]()
     got = _run_fused(w)
     _check_against_oracle(w, got, f"fused {name}")
@@ -430,3 +431,49 @@ def test_mask_views_at_every_byte_offset(dtype):
         valid = (host_mask != 0) & (w["labels"] != -100)
         d = to_host(dl)
         assert np.all(d[~valid] == 0) and np.all(np.any(d[valid] != 0, axis=1)), name
+
+def test_ce_fused_unaligned_rows_without_workspace():
+    """ce_fused on rows that are not 16-byte aligned (its fallback to
+    ce_forward + ce_backward) with no list outputs and no workspace, through
+    the C ABI: accepted as the aligned form is, and equal to the oracle; the
+    same call with a large input (every row swept in place, no list)."""
+    import ctypes
+    from gpu_helpers import DEV, strided_dev, to_dev, to_host
+    from cross_entropy_vocab_amd import _lib
+    lib = _lib.get()
+    for rows, V, stride, dt in ((24, 4099, 4101, "f32"), (260, 152064, 152067, "bf16")):
+        w = _rand_case(rows, V, dt, T=0.9, seed=rows, n_ignored=3, mask_frac=0.1)
+        logits = strided_dev(w["logits"], stride)
+        assert logits.stride(0) == stride and (stride * logits.element_size()) % 16 != 0
+        lab = to_dev(w["labels"])
+        mask = to_dev(w["row_mask"])
+        g = to_dev(w["g"])
+        loss = torch.empty(rows, dtype=torch.float32, device=DEV)
+        logp = torch.empty(rows, dtype=torch.float32, device=DEV)
+        argmax = torch.empty(rows, dtype=torch.int64, device=DEV)
+        saved = torch.empty((rows, 16), dtype=torch.uint8, device=DEV)
+        dl = torch.empty((rows, V), dtype=logits.dtype, device=DEV)
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
+        code = cev.CEV_BF16 if dt == "bf16" else cev.CEV_F32
+        rc = lib.ce_fused(logits.data_ptr(), rows, V, stride, code, lab.data_ptr(), -100,
+                          w["temperature"], 0.0, mask.data_ptr(), g.data_ptr(), loss.data_ptr(),
+                          saved.data_ptr(), logp.data_ptr(), None, argmax.data_ptr(),
+                          dl.data_ptr(), V, None, None, None, 0, status.data_ptr(),
+                          ctypes.c_void_p(torch.cuda.current_stream(DEV).cuda_stream))
+        assert rc == 0, rc
+        torch.cuda.synchronize()
+        kind = "bf16" if dt == "bf16" else "f32"
+        tol = RTOL[kind]
+        ref = oracle.ce_rows(w["logits"], w["labels"], w["temperature"], row_mask=w["row_mask"],
+                             want_entropy=False)
+        assert_close(f"fused unaligned {rows}x{V} loss", to_host(loss), ref["loss"], tol["loss"])
+        assert_close(f"fused unaligned {rows}x{V} logp", to_host(logp), ref["logp"], tol["logp"])
+        assert np.array_equal(to_host(argmax), ref["argmax"])
+        sample = np.arange(0, rows, max(1, rows // 12))
+        g64 = np.asarray(w["g"], np.float64)
+        dref = np.concatenate([oracle.ce_grad_rows(w["logits"], w["labels"], g64, w["temperature"],
+                                                   row_mask=w["row_mask"], r0=int(r), r1=int(r) + 1)
+                               for r in sample])
+        assert_close(f"fused unaligned {rows}x{V} dlogits", to_host(dl)[sample], dref,
+                     tol["dlogits"], atol=2.0 ** -126)
+        assert int(status.item()) == 0

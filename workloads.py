@@ -278,7 +278,7 @@ def distill(rows=2048, vocab=151936, seed=6, dtype="bf16", temperature=1.0, peak
                 col = cs[k] if which == "student" else ct[k]
                 lead = ms[k] if which == "student" else mt[k]
                 z[i, col] = -np.inf
-                z[i, col] = rnd(np.float32(z[i].max() + lead))
+                z[i, col] = np.asarray(rnd(np.float32(z[i].max() + lead))).reshape(-1)[0]
             return bf16_bits(z) if dtype == "bf16" else z
         return f
 
