@@ -59,95 +59,224 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
-def _counter_means(csv_path, counter):
-    """Mean value per dispatch of one rocprofv3 counter, by kernel name."""
+# ---------------------------------------------------------------- counters
+# One workload's calls, run a few times under rocprofv3 (one counter per
+# pass), and the table that turns those counter runs plus a kernel-trace run
+# of the same command into per-kernel durations, bandwidth and traffic
+# against algorithmic bytes.  Each kernel is matched by a regular expression
+# on its name without the namespace and argument list.
+COUNTER_WORKLOADS = ("grpo", "chunk", "peaked_f32", "peaked_bf16", "jsd_b0", "jsd_b05", "jsd_b1")
+
+
+def _short_name(name):
+    return name.replace("void ", "").replace("cev::(anonymous namespace)::", "").split("(")[0].strip()
+
+
+def run_counter_workload(name, torch, cev, workloads, dev, reps=3):
+    """Runs workload `name`'s calls `reps` times, then torch's float32 add over
+    2^28 elements (2^30 bytes in, 2^30 out: the counter calibration).
+    Returns the metadata the summary needs: the workload's description and
+    each kernel's algorithmic bytes per launch."""
+    def dev_logits(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    kernels = []
+    if name == "grpo":
+        w = workloads.grpo()
+        R, V = w["logits"].shape
+        z = dev_logits(w["logits"])
+        lab, msk = torch.from_numpy(w["labels"]).to(dev), torch.from_numpy(w["row_mask"]).to(dev)
+        g = torch.from_numpy(w["g"]).to(dev)
+        nv = int(((w["labels"] != -100) & (w["row_mask"] != 0)).sum())
+        P, Vs = 8, V // 8
+        parts = torch.empty((P, R, cev.PARTIAL_BYTES), dtype=torch.uint8, device=dev)
+        shard = z[:, :Vs].contiguous()
+        dls = torch.empty((R, Vs), dtype=torch.bfloat16, device=dev)
+        for p in range(1, P):
+            cev.ce_vocab_shard_forward(z[:, p * Vs:(p + 1) * Vs], lab, p * Vs, V, 1.0, row_mask=msk,
+                                       partials=parts[p])
+        dl = torch.empty_like(z)
+        for _ in range(reps):
+            out = cev.ce_forward(z, lab, 1.0, row_mask=msk, logp=True, argmax=True)
+            cev.ce_backward(z, lab, g, out["saved"], 1.0, row_mask=msk, dlogits=dl)
+            cev.ce_fused(z, lab, g, 1.0, row_mask=msk, logp=True, argmax=True, dlogits=dl)
+            cev.ce_vocab_shard_forward(shard, lab, 0, V, 1.0, row_mask=msk, partials=parts[0])
+            mo = cev.ce_vocab_merge(parts, lab, V, 1.0, row_mask=msk, argmax=True)
+            cev.ce_vocab_shard_backward(shard, lab, g, mo["saved"], 0, V, 1.0, row_mask=msk,
+                                        dlogits=dls)
+        desc = f"grpo-shaped {R}x{V} bf16, {nv} valid rows; one rank of 8-way vocab parallelism on {R}x{Vs}"
+        kernels = [
+            dict(regex=r"^k_sls_sweep<", call="ce_forward", read=nv * V * 2, write=0),
+            dict(regex=r"^k_backward_tile<1, 256, 1, false", call="ce_backward",
+                 read=nv * V * 2, write=R * V * 2, roofline=True),
+            dict(regex=r"^k_fused_stream<", call="ce_fused", read=nv * V * 2, write=R * V * 2),
+            dict(regex=r"^k_shard_sweep<", call="ce_vocab_shard_forward", read=nv * Vs * 2, write=0),
+            dict(regex=r"^k_backward_tile<1, 256, 1, true", call="ce_vocab_shard_backward",
+                 read=nv * Vs * 2, write=R * Vs * 2)]
+    elif name == "chunk":
+        w = workloads.chunk()
+        R, V = w["logits"].shape
+        z = dev_logits(w["logits"])
+        lab, idx = torch.from_numpy(w["labels"]).to(dev), torch.from_numpy(w["indices"]).to(dev)
+        gk = torch.from_numpy(np.random.default_rng(1).standard_normal(
+            tuple(w["indices"].shape), dtype=np.float32)).to(dev)
+        dl = torch.empty_like(z)
+        for _ in range(reps):
+            cev.sls_forward(z, lab, 0.7)
+            lp, q, sv = cev.sls_topk_forward(z, idx, 0.7, saved=True)
+            cev.sls_topk_backward(z, idx, gk, sv, q, 0.7, dlogits=dl)
+        desc = f"chunked selective log-softmax {R}x{V} bf16, T = 0.7, top-8"
+        kernels = [
+            dict(regex=r"^k_sls_sweep<", call="sls_forward", read=R * V * 2, write=0),
+            dict(regex=r"^k_topk_sweep<", call="sls_topk_forward", read=R * V * 2, write=0),
+            dict(regex=r"^k_topk_backward<", call="sls_topk_backward", read=R * V * 2, write=R * V * 2)]
+    elif name in ("peaked_f32", "peaked_bf16"):
+        dt = name.split("_")[1]
+        w = workloads.peaked(dt)
+        R, V = w["logits"].shape
+        es = 2 if dt == "bf16" else 4
+        z = dev_logits(w["logits"])
+        lab, g = torch.from_numpy(w["labels"]).to(dev), torch.from_numpy(w["g"]).to(dev)
+        dl = torch.empty_like(z)
+        for _ in range(reps):
+            out = cev.ce_forward(z, lab, 1.0, logp=True, entropy=True, argmax=True)
+            cev.ce_backward(z, lab, g, out["saved"], 1.0, dlogits=dl)
+        desc = f"peaked rows {R}x{V} {dt}, T = 1, forward with entropy and argmax"
+        kernels = [
+            dict(regex=r"^k_sls_sweep<", call="ce_forward", read=R * V * es, write=0),
+            dict(regex=r"^k_backward_tile<", call="ce_backward", read=R * V * es, write=R * V * es)]
+    elif name.startswith("jsd_"):
+        beta = {"jsd_b0": 0.0, "jsd_b05": 0.5, "jsd_b1": 1.0}[name]
+        w = workloads.distill()
+        R, V = w["student"].shape
+        st, te = dev_logits(w["student"]), dev_logits(w["teacher"])
+        lab, msk = torch.from_numpy(w["labels"]).to(dev), torch.from_numpy(w["row_mask"]).to(dev)
+        g = torch.from_numpy(w["g"]).to(dev)
+        nv = int(((w["labels"] != -100) & (w["row_mask"] != 0)).sum())
+        d = torch.empty_like(st)
+        for _ in range(reps):
+            out = cev.jsd_forward(st, te, 1.0, beta, labels=lab, row_mask=msk)
+            cev.jsd_backward(st, te, g, out["saved"], 1.0, beta, labels=lab, row_mask=msk, dstudent=d)
+        desc = f"student/teacher {R}x{V} bf16, beta = {beta:g}, {nv} valid rows"
+        # the backward's bytes: both rows of each valid pair read, every
+        # gradient row written (whichever of its kernels does the row)
+        kernels = [
+            dict(regex=r"^k_jsd_forward<", call="jsd_forward", read=2 * nv * V * 2, write=0),
+            dict(regex=r"^k_jsd_(bwd_tiles|backward)<", call="jsd_backward",
+                 read=2 * nv * V * 2, write=R * V * 2, per_call=True)]
+    else:
+        raise SystemExit(f"unknown counter workload {name!r}; one of {COUNTER_WORKLOADS}")
+    src = torch.ones(2 ** 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.add(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    return {"workload": name, "description": desc, "reps": reps, "kernels": kernels,
+            "kernel_source_sha": kernel_source_hash()}
+
+
+def _stats_by_kernel(stats_csv):
+    import csv
+    out = {}
+    with open(stats_csv) as f:
+        for row in csv.DictReader(f):
+            out[_short_name(row["Name"])] = dict(calls=int(row["Calls"]),
+                                                 avg_us=float(row["AverageNs"]) / 1e3,
+                                                 min_us=float(row["MinNs"]) / 1e3,
+                                                 max_us=float(row["MaxNs"]) / 1e3,
+                                                 total_us=float(row["TotalDurationNs"]) / 1e3)
+    return out
+
+
+def _counter_sums(csv_path, counter):
+    """Sum and dispatch count of one rocprofv3 counter, by short kernel name."""
     import csv
     acc = {}
     with open(csv_path) as f:
         for row in csv.DictReader(f):
             if row["Counter_Name"] == counter:
-                acc.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
-    return {k: float(np.mean(v)) for k, v in acc.items()}
+                k = _short_name(row["Kernel_Name"])
+                a = acc.setdefault(k, [0.0, set()])
+                a[0] += float(row["Counter_Value"])
+                a[1].add(row["Dispatch_Id"])
+    return {k: (v[0], len(v[1])) for k, v in acc.items()}
 
 
-def write_traffic(fetch_csv, write_csv, rows=8192, vocab=152064):
-    """Turn the two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE, of
-    `bench.py --copy-calibration`) into HBM bytes per launch: each counter is
-    scaled by what it reads for torch's float32 add over exactly 2^30 bytes in
-    and 2^30 bytes out.  Writes the backward's figures to the traffic file and
-    prints a table of every kernel of the step."""
-    import workloads
-    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
-    write = _counter_means(write_csv, "WRITE_SIZE")
+def summarize_profile(meta_json, stats_csv, fetch_csv, write_csv):
+    """Markdown summary of one counter workload: per kernel, its trace
+    duration, rate on algorithmic bytes, and FETCH_SIZE / WRITE_SIZE scaled
+    by the calibration copy's counters.  For the grpo workload it also writes
+    the backward's traffic record that bench.py reports as roofline.traffic."""
+    import re
+    with open(meta_json) as f:
+        meta = json.load(f)
+    stats = _stats_by_kernel(stats_csv)
+    fetch, write = _counter_sums(fetch_csv, "FETCH_SIZE"), _counter_sums(write_csv, "WRITE_SIZE")
     cal = [k for k in fetch if "vectorized_elementwise_kernel" in k and "_add" in k]
     if len(cal) != 1:
         raise SystemExit(f"calibration kernel not found exactly once: {cal}")
-    true = float(2 ** 30)
-    f_scale = true / (fetch[cal[0]] * 1024.0)
-    w_scale = true / (write[cal[0]] * 1024.0)
-    _, labels, mask, _ = workloads.grpo_rows(rows, vocab)
-    n_valid = int(((labels != -100) & (mask != 0)).sum())
-    ES = 2
-    algo = {"k_backward": (n_valid * vocab * ES, rows * vocab * ES),
-            "k_sls_sweep": (n_valid * vocab * ES, 0),
-            "k_fused_stream": (n_valid * vocab * ES, rows * vocab * ES)}
-    table = []
-    backward = None
-    for name in sorted(fetch):
-        short = name.replace("void ", "").replace("cev::(anonymous namespace)::", "").split("(")[0]
-        key = next((k for k in algo if short.startswith(k)), None)
-        if key == "k_backward" and short.split("<")[1].rstrip(">").split(",")[3].strip() == "true":
-            key = None                     # the vocab-shard instantiation (SHARD = true)
-        rd = fetch[name] * 1024.0 * f_scale
-        wr = write.get(name, 0.0) * 1024.0 * w_scale
-        entry = {"kernel": short, "fetch_kib": fetch[name], "write_kib": write.get(name),
-                 "read_bytes": rd, "write_bytes": wr}
-        if key:
-            a_rd, a_wr = algo[key]
-            entry.update(algorithmic_read=a_rd, algorithmic_write=a_wr,
-                         ratio=(rd + wr) / (a_rd + a_wr))
-            if key == "k_backward":
-                backward = (name, entry)
-        table.append(entry)
-    if backward is None:
-        raise SystemExit("no k_backward dispatch in the counter runs")
-    name, e = backward
-    out = {
-        "kernel": name,
-        "workload": f"grpo-shaped {rows}x{vocab} bf16, {n_valid} valid rows",
-        "kernel_source_sha": kernel_source_hash(),
-        "kernel_sources": KERNEL_SOURCES,
-        "fetch_size_kib_per_dispatch": e["fetch_kib"],
-        "write_size_kib_per_dispatch": e["write_kib"],
-        "calibration": {"kernel": "torch float32 add over 2^28 elements", "true_read_bytes": 2 ** 30,
-                        "true_write_bytes": 2 ** 30, "fetch_size_kib": fetch[cal[0]],
-                        "write_size_kib": write[cal[0]], "fetch_scale": f_scale,
-                        "write_scale": w_scale},
-        "read_bytes_per_launch": e["read_bytes"],
-        "write_bytes_per_launch": e["write_bytes"],
-        "bytes_per_launch": e["read_bytes"] + e["write_bytes"],
-        "algorithmic_bytes_per_launch": e["algorithmic_read"] + e["algorithmic_write"],
-        "traffic_over_algorithmic": e["ratio"],
-        "commands": [
-            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/prof_fetch -o grpo -- "
-            "python bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-linear --no-jsd --no-configs --copy-calibration",
-            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/prof_write -o grpo -- "
-            "python bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-linear --no-jsd --no-configs --copy-calibration",
-            "python bench.py --traffic-from <out>/prof_fetch/grpo_counter_collection.csv "
-            "<out>/prof_write/grpo_counter_collection.csv"],
-    }
-    with open(TRAFFIC_FILE, "w") as f:
-        json.dump(out, f, indent=2)
-        f.write("\n")
-    print(f"scales: fetch {f_scale:.4f}, write {w_scale:.4f}")
-    print("| Kernel | FETCH_SIZE (KiB/dispatch) | WRITE_SIZE (KiB/dispatch) | Read bytes | "
-          "Written bytes | Algorithmic bytes | Measured / algorithmic |")
-    print("|---|---|---|---|---|---|---|")
-    for e in table:
-        a = e.get("algorithmic_read", 0) + e.get("algorithmic_write", 0)
-        print(f"| {e['kernel']} | {e['fetch_kib']:.0f} | {e['write_kib'] or 0:.0f} | "
-              f"{e['read_bytes']:.4e} | {e['write_bytes']:.4e} | {a:.4e} | "
-              f"{e.get('ratio', float('nan')):.4f} |")
+    fk, fn = fetch[cal[0]]
+    wk, wn = write[cal[0]]
+    f_scale = 2.0 ** 30 / (fk / fn * 1024.0)
+    w_scale = 2.0 ** 30 / (wk / wn * 1024.0)
+    lines = [f"Workload: {meta['description']}.", "",
+             f"Calibration (torch float32 add, 2^30 B read and 2^30 B written per dispatch): "
+             f"FETCH_SIZE {fk / fn:.0f} KiB, WRITE_SIZE {wk / wn:.0f} KiB per dispatch, so read "
+             f"bytes = FETCH_SIZE x 1024 x {f_scale:.4f} and written bytes = WRITE_SIZE x 1024 x "
+             f"{w_scale:.4f}.", "",
+             "| Kernel (call) | Calls | Avg us | Min us | Algorithmic bytes | GB/s (algorithmic) | "
+             "% of 8 TB/s | Read bytes (counter) | Written bytes (counter) | Counter / algorithmic |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    traffic = None
+    for kinfo in meta["kernels"]:
+        rx = re.compile(kinfo["regex"])
+        names = [k for k in set(stats) | set(fetch) if rx.search(k)]
+        if not names:
+            lines.append(f"| {kinfo['regex']} ({kinfo['call']}) | 0 | - | - | - | - | - | - | - | - |")
+            continue
+        calls = sum(stats[k]["calls"] for k in names if k in stats)
+        tot = sum(stats[k]["total_us"] for k in names if k in stats)
+        mn = min(stats[k]["min_us"] for k in names if k in stats)
+        # per call of the entry point: kernels matched together (e.g. the JSD
+        # backward's two kernels) add up per call
+        ncall = meta["reps"] if kinfo.get("per_call") else calls
+        avg = tot / max(ncall, 1)
+        algo = kinfo["read"] + kinfo["write"]
+        gbs = algo / (avg * 1e-6) / 1e9
+        rd = sum(fetch[k][0] for k in names if k in fetch) * 1024.0 * f_scale / max(ncall, 1)
+        wr = sum(write[k][0] for k in names if k in write) * 1024.0 * w_scale / max(ncall, 1)
+        label = " + ".join(f"`{k}`" for k in sorted(names))
+        lines.append(f"| {label} ({kinfo['call']}) | {calls} | {avg:.1f} | {mn:.1f} | {algo:,} | "
+                     f"{gbs:.0f} | {gbs / PEAK_HBM_GBS * 100:.1f}% | {rd:.4e} | {wr:.4e} | "
+                     f"{(rd + wr) / algo:.4f} |")
+        if kinfo.get("roofline"):
+            traffic = dict(kernel=label, read=rd, write=wr, algo=algo, avg_us=avg)
+    other = [k for k in stats if not any(re.search(ki["regex"], k) for ki in meta["kernels"])]
+    if other:
+        lines += ["", "Other kernels in the same process (calibration, input copies, merges):", "",
+                  "| Kernel | Calls | Avg us |", "|---|---|---|"]
+        lines += [f"| `{k}` | {stats[k]['calls']} | {stats[k]['avg_us']:.1f} |" for k in sorted(other)]
+    print("\n".join(lines))
+    if traffic is not None and meta["workload"] == "grpo":
+        rec = {"kernel": traffic["kernel"], "workload": meta["description"],
+               "kernel_source_sha": meta["kernel_source_sha"], "kernel_sources": KERNEL_SOURCES,
+               "calibration": {"fetch_size_kib": fk / fn, "write_size_kib": wk / wn,
+                               "fetch_scale": f_scale, "write_scale": w_scale},
+               "read_bytes_per_launch": traffic["read"], "write_bytes_per_launch": traffic["write"],
+               "bytes_per_launch": traffic["read"] + traffic["write"],
+               "algorithmic_bytes_per_launch": traffic["algo"],
+               "traffic_over_algorithmic": (traffic["read"] + traffic["write"]) / traffic["algo"],
+               "trace_average_us": traffic["avg_us"]}
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=2)
+            f.write("\n")
+
+
+def bwd_bytes_all(rows, vocab, n_valid, es=2):
+    """Algorithmic bytes of one ce_backward: each valid row read, every row written."""
+    return n_valid * vocab * es + rows * vocab * es
 
 
 def cpu_baseline(w, valid_rows, seconds=12.0, threads=None):
@@ -476,12 +605,17 @@ def main():
                     help="skip the linear cross-entropy measurement (8192 x 2560 x 151936)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads (tiny, chunked + top-K, sparse, peaked)")
-    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="no GPU work: turn the two counter runs' csv files into the "
-                         "committed traffic figures and print the counter table")
+    ap.add_argument("--counters", choices=COUNTER_WORKLOADS,
+                    help="run only this workload's calls (for rocprofv3 counter and trace "
+                         "passes) and write its metadata to --counter-meta")
+    ap.add_argument("--counter-meta", default=None,
+                    help="metadata file written by --counters and read by --summarize")
+    ap.add_argument("--summarize", nargs=3, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: print the markdown summary of a counter workload from "
+                         "its kernel-trace stats and its FETCH_SIZE and WRITE_SIZE runs")
     args = ap.parse_args()
-    if args.traffic_from:
-        write_traffic(*args.traffic_from, rows=args.rows, vocab=args.vocab)
+    if args.summarize:
+        summarize_profile(args.counter_meta, *args.summarize)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
@@ -494,6 +628,13 @@ def main():
     import workloads
 
     dev = torch.device("cuda:0")
+    if args.counters:
+        meta = run_counter_workload(args.counters, torch, cev, workloads, dev)
+        if args.counter_meta:
+            with open(args.counter_meta, "w") as f:
+                json.dump(meta, f, indent=2)
+        print(json.dumps({"counters": args.counters, "kernels": len(meta["kernels"])}))
+        return
     log(f"[bench] generating {args.rows}x{args.vocab} bf16 workload")
     w = workloads.grpo(rows=args.rows, vocab=args.vocab)
     R, V = w["logits"].shape
@@ -562,27 +703,32 @@ def main():
     ms_step_aa = timed_steps()
 
     # Scrub A/B for the backward: the same call timed right after ce_forward
-    # (as in the step) and after a 1 GiB read that leaves none of the logits
-    # in the 256 MB Infinity Cache (a read, so that no dirty lines of the
-    # scrub itself are written back during the backward).  Equal times mean
-    # the backward's rate is HBM's, not the cache's.
+    # (as in the step), after a 1 GiB read that leaves none of the logits in
+    # the 256 MB Infinity Cache (a read, so that no dirty lines of the scrub
+    # itself are written back during the backward), after that scrub and then
+    # ce_forward, and right after another ce_backward.  The scrubbed time is
+    # the backward's rate from HBM alone.
     scrub = torch.ones(2 ** 28, dtype=torch.float32, device=dev)
-    scrub_ab = {"after_forward": [], "after_scrub": []}
-    for i in range(2 * max(4, args.steps // 2)):
-        key = "after_scrub" if i % 2 else "after_forward"
-        cev.ce_forward(logits, labels, T, row_mask=mask, logp=True, argmax=True, out=out)
-        if key == "after_scrub":
+    conds = ("after_forward", "after_scrub", "after_scrub_then_forward", "after_backward")
+    scrub_ab = {k: [] for k in conds}
+    for i in range(len(conds) * max(4, args.steps // 2)):
+        key = conds[i % len(conds)]
+        if key in ("after_scrub", "after_scrub_then_forward"):
             scrub_sum = scrub.sum()
+        if key in ("after_forward", "after_scrub_then_forward"):
+            cev.ce_forward(logits, labels, T, row_mask=mask, logp=True, argmax=True, out=out)
+        if key == "after_backward":
+            cev.ce_backward(logits, labels, g, out["saved"], T, row_mask=mask, dlogits=dl)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         cev.ce_backward(logits, labels, g, out["saved"], T, row_mask=mask, dlogits=dl)
         e1.record()
         torch.cuda.synchronize()
         scrub_ab[key].append(e0.elapsed_time(e1))
-    del scrub
+    del scrub, scrub_sum
     scrub_ab = {k: float(np.median(v)) for k, v in scrub_ab.items()}
-    scrub_ab["scrub"] = "1 GiB float32 read (torch sum) between ce_forward and ce_backward"
-    del scrub_sum
+    scrub_ab["scrub"] = "1 GiB float32 read (torch sum)"
+    scrub_ab["hbm_only_GBps"] = bwd_bytes_all(R, V, n_valid) / (scrub_ab["after_scrub"] / 1e3) / 1e9
 
     # The same step as one call (g known up front): ce_fused.
     fout = cev.ce_fused(logits, labels, g, T, row_mask=mask, logp=True, argmax=True,

@@ -1,16 +1,21 @@
 """Element-by-element comparison of the HIP path's outputs with the fp64 oracle.
 
 Bars (float32 logits / bfloat16 logits):
-  log p, loss, top-K log p   |d| <= 2e-6 |ref|        / 4e-3 |ref|
-  entropy                    |d| <= 1e-5 |ref|        / 4e-3 |ref|
+  log p, loss, top-K log p   |d| <= 2e-6 |ref|        / 2e-6 |ref|
+  entropy                    |d| <= 1e-5 |ref|        / 1e-5 |ref|
   dlogits (each element)     |d| <= 2e-5 |ref| + 2^-126 / 4e-3 |ref| + 2^-126
   dlogits row sum            |sum| <= tol * sum|dl| + V 2^-126
   argmax, valid_rows, n_valid  bit-exact
-The 2e-6 and 4e-3 bounds are the required ones; the entropy and fp32 dlogits
-bounds follow from fp32 accumulation (about 1e-6 relative) plus one fp32
-rounding of each output, and the 2^-126 floor admits fp32 subnormal outputs
-that the hardware exp flushes to zero.  A bf16 dlogit is one round-to-nearest
-step (<= 2^-8 relative) from an fp32 value accurate to ~1e-6, inside 4e-3.
+The required bars are 2e-6 on fp32 log p and loss and 4e-3 on every output
+for bf16 logits.  Only dlogits is rounded to bf16, so only dlogits needs the
+4e-3 bar: log p, loss, entropy and top-K log p are fp32 outputs formed in
+fp32 / fp64 from the exactly widened bf16 values, and are held to the fp32
+bars whatever the input dtype (tighter than required).  The entropy and fp32
+dlogits bounds follow from fp32 accumulation (about 1e-6 relative) plus one
+fp32 rounding of each output, and the 2^-126 floor admits fp32 subnormal
+outputs that the hardware exp flushes to zero.  A bf16 dlogit is one
+round-to-nearest step (<= 2^-8 relative) from an fp32 value accurate to
+~1e-6, inside 4e-3.
 """
 from __future__ import annotations
 
@@ -23,7 +28,7 @@ SUBNORMAL = 2.0 ** -149
 
 RTOL = {
     "f32": dict(logp=2e-6, loss=2e-6, topk=2e-6, entropy=1e-5, dlogits=2e-5),
-    "bf16": dict(logp=4e-3, loss=4e-3, topk=4e-3, entropy=4e-3, dlogits=4e-3),
+    "bf16": dict(logp=2e-6, loss=2e-6, topk=2e-6, entropy=1e-5, dlogits=4e-3),
 }
 
 
