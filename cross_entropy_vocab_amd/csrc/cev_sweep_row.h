@@ -53,38 +53,49 @@ __device__ __forceinline__ void fold(LaneState &st, float (&v)[N], int code, flo
     st.comp *= f;
     st.m = mnew;
 
-    float e[N];
-    if constexpr (DT == CEV_F32) {
-        // (z - b) first: exact for the terms near the maximum that dominate.
+    // The exponentials 8 at a time: the pairwise tree over N values is the
+    // tree over the 8-value chunks' trees, and the entropy term is a running
+    // chain, so the result is the same as over all N at once while only one
+    // chunk's exponentials are live (fewer registers, more waves per SIMD).
+    constexpr int C = N < 8 ? N : 8, NC = N / C;
+    const float nb = fminf(-bnew * c, kBig);
+    float part[NC], zpart[NC];
+    float ph = 0.0f;
 #pragma unroll
-        for (int i = 0; i < N; ++i)
-            e[i] = exp2_hw((v[i] - bnew) * c);
-    } else {
-        const float nb = fminf(-bnew * c, kBig);
+    for (int q = 0; q < NC; ++q) {
+        float e[C];
 #pragma unroll
-        for (int i = 0; i < N; ++i)
-            e[i] = exp2_hw(fmaf(v[i], c, nb));
-    }
-    if constexpr (WANT_H) {
-        float ph = 0.0f;
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            float d = (bnew - v[i]) * inv_t;
-            if constexpr (MAYBE_INF)
-                d = fminf(d, kBig);
-            ph = fmaf(e[i], d, ph);
+        for (int i = 0; i < C; ++i) {
+            if constexpr (DT == CEV_F32)
+                // (z - b) first: exact for the terms near the maximum that dominate.
+                e[i] = exp2_hw((v[q * C + i] - bnew) * c);
+            else
+                e[i] = exp2_hw(fmaf(v[q * C + i], c, nb));
         }
-        st.h += ph;
-    }
-    if constexpr (WANT_Z) {
-        // sum of the stored values (excluded columns count 0)
-        float zv[N];
+        if constexpr (WANT_H) {
 #pragma unroll
-        for (int i = 0; i < N; ++i)
-            zv[i] = MAYBE_INF ? (v[i] == -INFINITY ? 0.0f : v[i]) : v[i];
-        st.zs += tree_sum(zv);
+            for (int i = 0; i < C; ++i) {
+                float d = (bnew - v[q * C + i]) * inv_t;
+                if constexpr (MAYBE_INF)
+                    d = fminf(d, kBig);
+                ph = fmaf(e[i], d, ph);
+            }
+        }
+        if constexpr (WANT_Z) {
+            // sum of the stored values (excluded columns count 0)
+            float zv[C];
+#pragma unroll
+            for (int i = 0; i < C; ++i)
+                zv[i] = MAYBE_INF ? (v[q * C + i] == -INFINITY ? 0.0f : v[q * C + i]) : v[q * C + i];
+            zpart[q] = tree_sum(zv);
+        }
+        part[q] = tree_sum(e);
     }
-    const float ps = tree_sum(e);
+    if constexpr (WANT_H)
+        st.h += ph;
+    if constexpr (WANT_Z)
+        st.zs += tree_sum(zpart);
+    const float ps = tree_sum(part);
     const float y = ps - st.comp;
     const float tsum = st.s + y;
     st.comp = (tsum - st.s) - y;
@@ -150,48 +161,96 @@ __device__ __forceinline__ RowGeom row_geom(const char *rowp, int64_t V, int64_t
 //   16 + k                          wave step (chunk) k of the range
 //   16 + nfull + i                  remainder vector vbeg + nfull*CH + i
 //   16 + nfull + nrem + i           tail column tail0 + i
+// The argmax re-read, in two halves so that its loads are in flight while
+// the workgroup reduces its sums: rescan_issue loads the vectors of the step
+// named by `code` (the one where this lane first saw its maximum M; a lane
+// whose maximum is not M loads nothing), rescan_finish finds the lowest
+// column there holding M, the target excepted.
+template <int DT, int U> struct Rescan {
+    u32x4 w[U];
+    int64_t col0;   // first column of w[0]; vector u starts 64 u vectors later
+    int kind;       // 0 nothing, 1 a head column, 2 a wave step, 3 one vector, 4 a tail column
+    int64_t col;    // kinds 1 and 4: the column itself
+};
+
 template <int DT, int U>
-__device__ int64_t rescan_argmax(const char *rowp, const RowGeom &g, int code, float M, int64_t t)
+__device__ __forceinline__ Rescan<DT, U> rescan_issue(const char *rowp, const RowGeom &g, int code,
+                                                      bool mine)
 {
     constexpr int VE = Elem<DT>::kVE;
     constexpr int64_t CH = (int64_t)kWave * U;
     const int lane = threadIdx.x & (kWave - 1);
     const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp + (size_t)g.ahead * Elem<DT>::kSize);
-    int64_t found = INT64_MAX;
-    if (code < 16)
-        return code;
+    Rescan<DT, U> r;
+    r.kind = 0;
+    r.col0 = 0;
+    r.col = 0;
+    if (!mine)
+        return r;
+    if (code < 16) {
+        r.kind = 1;
+        r.col = code;
+        return r;
+    }
     int64_t c2 = code - 16;
     if (c2 < g.nfull) {
-        const int64_t k = c2;
+        const int64_t j0 = g.vbeg + c2 * CH + lane;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t j = g.vbeg + k * CH + u * kWave + lane;
-            float v[VE];
-            unpack16<DT>(load16_stream(vp + j), v);
-#pragma unroll
-            for (int e = 0; e < VE; ++e) {
-                const int64_t col = g.ahead + j * VE + e;
-                if (found == INT64_MAX && v[e] == M && col != t)
-                    found = col;
-            }
-        }
-        return found;
+        for (int u = 0; u < U; ++u)
+            r.w[u] = load16_stream(vp + j0 + u * kWave);
+        r.kind = 2;
+        r.col0 = g.ahead + j0 * VE;
+        return r;
     }
     c2 -= g.nfull;
     if (c2 < g.nrem) {
         const int64_t j = g.vbeg + g.nfull * CH + c2;
-        float v[VE];
-        unpack16<DT>(load16_stream(vp + j), v);
-#pragma unroll
-        for (int e = 0; e < VE; ++e) {
-            const int64_t col = g.ahead + j * VE + e;
-            if (found == INT64_MAX && v[e] == M && col != t)
-                found = col;
-        }
-        return found;
+        r.w[0] = load16_stream(vp + j);
+        r.kind = 3;
+        r.col0 = g.ahead + j * VE;
+        return r;
     }
     c2 -= g.nrem;
-    return g.tail0 + c2;
+    r.kind = 4;
+    r.col = g.tail0 + c2;
+    return r;
+}
+
+// Lowest column of one 16-byte vector (first column col0) holding M, the
+// target column t excepted; INT64_MAX if none.
+template <int DT>
+__device__ __forceinline__ int64_t scan_vec(const u32x4 &w, int64_t col0, float M, int64_t t)
+{
+    constexpr int VE = Elem<DT>::kVE;
+    float v[VE];
+    unpack16<DT>(w, v);
+    const int64_t dt = t - col0;
+    const int te = (dt >= 0 && dt < VE) ? (int)dt : -1;
+    int first = VE;
+#pragma unroll
+    for (int e = VE - 1; e >= 0; --e)
+        if (v[e] == M && e != te)
+            first = e;
+    return first < VE ? col0 + first : INT64_MAX;
+}
+
+template <int DT, int U>
+__device__ __forceinline__ int64_t rescan_finish(const Rescan<DT, U> &r, float M, int64_t t)
+{
+    constexpr int VE = Elem<DT>::kVE;
+    if (r.kind == 0)
+        return INT64_MAX;
+    if (r.kind == 1 || r.kind == 4)
+        return r.col;
+    if (r.kind == 3)
+        return scan_vec<DT>(r.w[0], r.col0, M, t);
+    int64_t found = INT64_MAX;
+#pragma unroll
+    for (int u = U - 1; u >= 0; --u) {
+        const int64_t f = scan_vec<DT>(r.w[u], r.col0 + (int64_t)u * kWave * VE, M, t);
+        found = f != INT64_MAX ? f : found;
+    }
+    return found;
 }
 
 
@@ -259,17 +318,19 @@ __device__ __forceinline__ RowStats sweep_row(const char *rowp, int64_t V, int64
             float v[U * VE];
             unpack_step<DT, U>(cur, v);
             const int64_t lo = col_v + k * CH * VE;
-            if ((uint64_t)(t - lo) < (uint64_t)(CH * VE)) {
+            const bool has_t = (uint64_t)(t - lo) < (uint64_t)(CH * VE);
+            if (has_t) {
 #pragma unroll
                 for (int u = 0; u < U; ++u)
 #pragma unroll
                     for (int e = 0; e < VE; ++e)
                         if (col_v + (k * CH + u * kWave + lane) * VE + e == t)
                             v[u * VE + e] = -INFINITY;
-                fold<DT, U * VE, WANT_H, WANT_ARG, true, WANT_Z>(st, v, 16 + (int)k, c, inv_t);
-            } else {
-                fold<DT, U * VE, WANT_H, WANT_ARG, false, WANT_Z>(st, v, 16 + (int)k, c, inv_t);
             }
+            if (has_t)
+                fold<DT, U * VE, WANT_H, WANT_ARG, true, WANT_Z>(st, v, 16 + (int)k, c, inv_t);
+            else
+                fold<DT, U * VE, WANT_H, WANT_ARG, false, WANT_Z>(st, v, 16 + (int)k, c, inv_t);
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 cur[u] = nxt[u];
@@ -293,8 +354,12 @@ __device__ __forceinline__ RowStats sweep_row(const char *rowp, int64_t V, int64
     }
 
     // Combine the lanes: exact maximum first, then each lane rescales its own
-    // sum once to the common base and the sums are added in fp64.
+    // sum once to the common base and the sums are added in fp64.  The argmax
+    // re-read goes out as soon as the maximum is known.
     const float M = block_max<BLOCK>(st.m, sh_f);
+    Rescan<DT, U> rsc;
+    if constexpr (WANT_ARG)
+        rsc = rescan_issue<DT, U>(rowp, g, st.best, M != -INFINITY && st.m == M);
     const float B = fmaxf(M, -FLT_MAX);
     const float bl = fmaxf(st.m, -FLT_MAX);
     const float f = exp2_hw((bl - B) * c);
@@ -308,12 +373,8 @@ __device__ __forceinline__ RowStats sweep_row(const char *rowp, int64_t V, int64
     if constexpr (WANT_Z)
         Zs = block_sum<BLOCK>((double)st.zs, sh_d);
     int64_t a_o = INT64_MAX;
-    if constexpr (WANT_ARG) {
-        int64_t mine = INT64_MAX;
-        if (M != -INFINITY && st.m == M)
-            mine = rescan_argmax<DT, U>(rowp, g, st.best, M, t);
-        a_o = block_min<BLOCK>(mine, sh_i);
-    }
+    if constexpr (WANT_ARG)
+        a_o = block_min<BLOCK>(rescan_finish<DT, U>(rsc, M, t), sh_i);
 
     return RowStats{M, S, Hs, Zs, a_o};
 }

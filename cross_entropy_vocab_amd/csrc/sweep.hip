@@ -216,6 +216,21 @@ __global__ __launch_bounds__(256) void k_merge(SweepArgs a)
 // ------------------------------------------------------------------------
 // Top-K sweep: the sum runs over the columns outside the gathered set; each
 // gathered column's complement is that sum plus the other gathered terms.
+
+// One gathered index's closing step in fp64: s = the sum of the other columns'
+// terms based at B, zk the index's stored value.  log p = -softplus(u) and
+// q = 1 - p = sigmoid(u), u = log s + (B - zk)/T, both from one e^{-|u|}.
+// Kept out of line: inlined into the per-index loop, its fp64 constants were
+// hoisted into vector registers that stayed live across the whole kernel.
+__device__ __noinline__ void topk_close(double s, double B, double zk, double T, float *logp,
+                                        float *q)
+{
+    const double u = s > 0.0 ? log(s) + (B - zk) / T : -INFINITY;
+    const double e = exp(-fabs(u));
+    *logp = (float)(-(fmax(u, 0.0) + log1p(e)));
+    if (q)
+        *q = (float)((u < 0.0 ? e : 1.0) / (1.0 + e));
+}
 template <int DT, int BLOCK, int U>
 __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
 {
@@ -299,6 +314,16 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
         fold<DT, 1, false, false, true>(st, v, 0, c, inv_t);
     }
     {
+        // With at most 64 gathered columns, lane l holds the wave step that
+        // column l falls in (-1 if none), so that each step's test is one
+        // compare and a ballot rather than K 64-bit range checks.
+        const bool small_k = K <= kWave;
+        int my_step = -1;
+        if (small_k && lane < K) {
+            const int64_t x = xcol[lane];
+            if (x >= g.ahead && x < g.ahead + g.nfull * CH * VE)
+                my_step = (int)((x - g.ahead) / (CH * VE));
+        }
         int64_t k = wave;
         for (; k < g.nfull; k += W) {
             const int64_t kn = k + W;
@@ -310,21 +335,31 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
             float v[U * VE];
             unpack_step<DT, U>(cur, v);
             const int64_t lo = g.ahead + k * CH * VE;
-            bool any = false;
-            for (int kk = 0; kk < K; kk += kWave) {
-                const int64_t x = kk + lane < K ? xcol[kk + lane] : -1;
-                any |= __any(x >= 0 && (uint64_t)(x - lo) < (uint64_t)(CH * VE)) != 0;
+            bool any;
+            if (small_k) {
+                any = __any(my_step == (int)k) != 0;
+            } else {
+                any = false;
+                for (int kk = 0; kk < K; kk += kWave) {
+                    const int64_t x = kk + lane < K ? xcol[kk + lane] : -1;
+                    any |= __any(x >= 0 && (uint64_t)(x - lo) < (uint64_t)(CH * VE)) != 0;
+                }
             }
             if (any) {
+                // A gathered column at offset d in this step sits in lane
+                // (d / VE) % 64, vector d / (64 VE) of the lane, element d % VE.
                 for (int k2 = 0; k2 < K; ++k2) {
                     const int64_t x = xcol[k2];
-                    if (x >= 0 && (uint64_t)(x - lo) < (uint64_t)(CH * VE)) {
+                    const int64_t d = x - lo;
+                    if (x >= 0 && (uint64_t)d < (uint64_t)(CH * VE)) {
+                        const int dd = (int)d;
+                        if (((dd / VE) & (kWave - 1)) == lane) {
+                            const int i = (dd / (kWave * VE)) * VE + dd % VE;
 #pragma unroll
-                        for (int u = 0; u < U; ++u)
-#pragma unroll
-                            for (int e = 0; e < VE; ++e)
-                                if (g.ahead + (k * CH + u * kWave + lane) * VE + e == x)
-                                    v[u * VE + e] = -INFINITY;
+                            for (int j = 0; j < U * VE; ++j)
+                                if (j == i)
+                                    v[j] = -INFINITY;
+                        }
                     }
                 }
                 fold<DT, U * VE, false, false, true>(st, v, 0, c, inv_t);
@@ -380,12 +415,7 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
         for (int k2 = 0; k2 < K; ++k2)
             if (xfirst[k2] && xcol[k2] != xcol[k])
                 s += xterm[k2];
-        const double u = s > 0.0 ? log(s) + ((double)Ball - (double)xz[k]) / T : -INFINITY;
-        // softplus(u) and sigmoid(u) from one e^{-|u|}
-        const double e = exp(-fabs(u));
-        out[k] = (float)(-(fmax(u, 0.0) + log1p(e)));
-        if (qout)
-            qout[k] = (float)((u < 0.0 ? e : 1.0) / (1.0 + e));
+        topk_close(s, (double)Ball, (double)xz[k], T, out + k, qout ? qout + k : nullptr);
     }
     if (a.saved && tid == 0) {
         // The row's normaliser over all columns, for the top-K backward:
