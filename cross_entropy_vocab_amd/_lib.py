@@ -9,7 +9,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcevocab.so")
+# CEV_LIBRARY names another build of the same library (the host-sanitized one).
+LIB_PATH = os.environ.get("CEV_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                          "libcevocab.so")
 
 P = ctypes.c_void_p
 I64 = ctypes.c_int64

@@ -1,8 +1,10 @@
 """Build libcevocab.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-    python -m cross_entropy_vocab_amd.build
+    python -m cross_entropy_vocab_amd.build [--sanitize]
 
 Objects go to cross_entropy_vocab_amd/_build/, the library next to this file.
+--sanitize builds _build/libcevocab_san.so, the same library with its host code
+(the C ABI's argument checks) under ASan and UBSan.
 """
 from __future__ import annotations
 
@@ -41,6 +43,48 @@ def compile_flags() -> list:
     ]
 
 
+# Host-side sanitizers for the C ABI's argument checks: ASan and UBSan on the
+# host code of api.cpp and noalloc.hip only (each flag after -Xarch_host, so no
+# device code is instrumented), linked with the regular device objects.
+SANITIZED_SOURCES = ["api.cpp", "noalloc.hip"]
+SAN_LIB = os.path.join(BUILD, "libcevocab_san.so")
+
+
+def san_flags() -> list:
+    out = []
+    for f in ("-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=all", "-g",
+              "-fno-omit-frame-pointer"):
+        out += ["-Xarch_host", f]
+    return out
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """libcevocab_san.so: the library with its host code under ASan + UBSan
+    (load it with the compiler's ASan runtime preloaded)."""
+    if not all(os.path.exists(os.path.join(BUILD, os.path.splitext(s)[0] + ".o")) for s in SOURCES):
+        build(verbose)
+    cc = hipcc()
+    objs = []
+    for src in SOURCES:
+        base = os.path.splitext(src)[0]
+        if src not in SANITIZED_SOURCES:
+            objs.append(os.path.join(BUILD, base + ".o"))
+            continue
+        obj = os.path.join(BUILD, base + "_san.o")
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        r = subprocess.run([cc, *compile_flags(), *san_flags(), *lang, "-c", os.path.join(CSRC, src),
+                            "-o", obj], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}{r.stderr}")
+        objs.append(obj)
+    link_san = []
+    for f in ("-fsanitize=address", "-fsanitize=undefined", "-shared-libsan"):
+        link_san += ["-Xarch_host", f]
+    subprocess.check_call([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_san, "-o", SAN_LIB,
+                           *objs])
+    return SAN_LIB
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
@@ -72,4 +116,7 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -286,6 +286,9 @@ hipError_t launch_backward(int dtype, const BackwardArgs &a, hipStream_t stream)
 // The entry points above pick one of these; tuning harnesses call them directly.
 hipError_t launch_sls_sweep_cfg(int dtype, const SweepArgs &a, bool want_entropy,
                                 bool want_argmax, int block, int U, hipStream_t stream);
+hipError_t launch_sls_sweep_lds_cfg(int dtype, const SweepArgs &a, bool want_entropy,
+                                    bool want_argmax, int block, int U, size_t lds,
+                                    hipStream_t stream);
 hipError_t launch_backward_cfg(int dtype, const BackwardArgs &a, int block, int U, int iters,
                                int order, int store_nt, hipStream_t stream);
 hipError_t launch_backward_tile_cfg(int dtype, const BackwardArgs &a, int block, int U, int store_nt,

@@ -433,32 +433,35 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
     }
 }
 
+// lds: dynamic LDS reserved per workgroup (unused by the kernel), which caps
+// how many workgroups a CU holds at once.
 template <int DT, int BLOCK, int U, bool SPLIT, bool WANT_Z>
-void launch_sls_z(const SweepArgs &a, bool want_h, bool want_arg, hipStream_t s)
+void launch_sls_z(const SweepArgs &a, bool want_h, bool want_arg, hipStream_t s, size_t lds = 0)
 {
     int64_t extra = 0;   // compaction workgroups of an every-row sweep
     if (!SPLIT && !a.rowlist && a.out_list)
         extra = (a.rows + compact_tile_rows(a.rows, BLOCK) - 1) / compact_tile_rows(a.rows, BLOCK);
     dim3 grid((unsigned)(a.rows * (SPLIT ? a.splits : 1) + extra)), block(BLOCK);
     if (want_h && want_arg)
-        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, true, true, SPLIT, WANT_Z>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, true, true, SPLIT, WANT_Z>), grid, block, lds, s, a);
     else if (want_h)
-        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, true, false, SPLIT, WANT_Z>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, true, false, SPLIT, WANT_Z>), grid, block, lds, s, a);
     else if (want_arg)
-        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, false, true, SPLIT, WANT_Z>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, false, true, SPLIT, WANT_Z>), grid, block, lds, s, a);
     else
-        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, false, false, SPLIT, WANT_Z>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_sls_sweep<DT, BLOCK, U, false, false, SPLIT, WANT_Z>), grid, block, lds, s, a);
 }
 
 // The running sum of the stored values is taken only when label smoothing
 // needs it.
 template <int DT, int BLOCK, int U, bool SPLIT>
-hipError_t launch_sls_t(const SweepArgs &a, bool want_h, bool want_arg, hipStream_t s)
+hipError_t launch_sls_t(const SweepArgs &a, bool want_h, bool want_arg, hipStream_t s,
+                        size_t lds = 0)
 {
     if (a.label_smoothing != 0.0)
-        launch_sls_z<DT, BLOCK, U, SPLIT, true>(a, want_h, want_arg, s);
+        launch_sls_z<DT, BLOCK, U, SPLIT, true>(a, want_h, want_arg, s, lds);
     else
-        launch_sls_z<DT, BLOCK, U, SPLIT, false>(a, want_h, want_arg, s);
+        launch_sls_z<DT, BLOCK, U, SPLIT, false>(a, want_h, want_arg, s, lds);
     return hipGetLastError();
 }
 
@@ -492,6 +495,20 @@ hipError_t launch_sls_sweep_cfg(int dtype, const SweepArgs &a, bool want_h, bool
     CEV_SLS_CASE(512, 2)
     CEV_SLS_CASE(512, 4)
 #undef CEV_SLS_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_sls_sweep_lds_cfg(int dtype, const SweepArgs &a, bool want_h, bool want_arg,
+                                    int block, int U, size_t lds, hipStream_t s)
+{
+#define CEV_SLSL_CASE(B, UU)                                                                    \
+    if (block == B && U == UU)                                                                  \
+        return dtype == CEV_BF16 ? launch_sls_t<CEV_BF16, B, UU, false>(a, want_h, want_arg, s, lds) \
+                                 : launch_sls_t<CEV_F32, B, UU, false>(a, want_h, want_arg, s, lds);
+    CEV_SLSL_CASE(256, 2)
+    CEV_SLSL_CASE(512, 2)
+    CEV_SLSL_CASE(512, 4)
+#undef CEV_SLSL_CASE
     return hipErrorInvalidValue;
 }
 

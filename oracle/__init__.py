@@ -63,6 +63,25 @@ def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
     return out
 
 
+_SAN_LIB = os.path.join(_HERE, "liboracle_cev_san.so")
+_CLANG = "/opt/rocm/lib/llvm/bin/clang"
+
+
+def build_sanitized(src: str = _SRC, out: str = _SAN_LIB) -> str:
+    """liboracle_cev_san.so: the oracle under ASan + UBSan (clang, the same IEEE
+    flags; load it with clang's ASan runtime preloaded).  Used when the
+    environment sets CEV_ORACLE_SANITIZE=1."""
+    tmp = out + ".tmp"
+    subprocess.check_call([
+        _CLANG, "-O1", "-g", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+        "-fno-fast-math", "-Wall", "-Wextra", "-fsanitize=address,undefined",
+        "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-shared-libsan",
+        "-o", tmp, src, "-lm",
+    ])
+    os.replace(tmp, out)
+    return out
+
+
 def load_library(path: str):
     """Load an oracle library built from oracle_cev.c (or a test's mutant of it)."""
     lib = ctypes.CDLL(path)
@@ -90,9 +109,14 @@ def _load(lib=None):
     if lib is not None:
         return lib
     if _default is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=True)
-        _default = load_library(_LIB)
+        if os.environ.get("CEV_ORACLE_SANITIZE") == "1":
+            if not os.path.exists(_SAN_LIB) or os.path.getmtime(_SAN_LIB) < os.path.getmtime(_SRC):
+                build_sanitized()
+            _default = load_library(_SAN_LIB)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+            _default = load_library(_LIB)
     return _default
 
 
