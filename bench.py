@@ -837,7 +837,7 @@ def main():
                        "ce_backward_GBps": achieved},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": "k_backward (ce_backward)", "bytes_per_launch": bwd_bytes},
+                     "kernel": "k_backward_tile (ce_backward)", "bytes_per_launch": bwd_bytes},
         "cpu_baseline": None,
         "fused": {"entry": "ce_fused: the same outputs in one call for a g known up front; "
                            "each valid row swept once and re-read at once (largely from the "
