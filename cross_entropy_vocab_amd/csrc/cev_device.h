@@ -109,30 +109,86 @@ __device__ __forceinline__ unsigned short to_bf16(float a) { return (unsigned sh
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------- reductions
+// Wave-wide reductions without the LDS crossbar (ds_bpermute costs an LDS
+// round trip per step).  Six steps, each combining a lane with a partner that
+// holds the same number of values: DPP inside each 16-lane row (quad_perm
+// [1,0,3,2], quad_perm [2,3,0,1], then row_half_mirror, lane i of 8 reading
+// 7 - i, and row_mirror, lane i of 16 reading 15 - i), then gfx950's
+// v_permlane16_swap (row 2k with row 2k + 1) and v_permlane32_swap (the two
+// half-waves).  Both lanes of a pair form op(a, b) of the same two values with
+// a commutative op, so every lane ends with the same bits.
+constexpr int kDppQuad1 = 0xB1, kDppQuad2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL> __device__ __forceinline__ unsigned dpp_u32(unsigned x)
+{
+    return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+// A value of 4 or 8 bytes as 32-bit words, for the cross-lane moves.
+template <class T> struct Words {
+    static constexpr int N = sizeof(T) / 4;
+    unsigned w[N];
+};
+template <class T> __device__ __forceinline__ Words<T> to_words(T x)
+{
+    Words<T> r;
+    __builtin_memcpy(r.w, &x, sizeof(T));
+    return r;
+}
+template <class T> __device__ __forceinline__ T from_words(const Words<T> &r)
+{
+    T x;
+    __builtin_memcpy(&x, r.w, sizeof(T));
+    return x;
+}
+
+template <int CTRL, class T> __device__ __forceinline__ T dpp_move(T x)
+{
+    Words<T> r = to_words(x);
+#pragma unroll
+    for (int i = 0; i < Words<T>::N; ++i)
+        r.w[i] = dpp_u32<CTRL>(r.w[i]);
+    return from_words<T>(r);
+}
+
+// op over the value pair that v_permlane{16,32}_swap hands each lane: the even
+// row (lower half-wave) value first, the odd row (upper half) value second.
+template <bool HALF, class T, class Op> __device__ __forceinline__ T swap_combine(T x, Op op)
+{
+    Words<T> a = to_words(x), b = a;
+#pragma unroll
+    for (int i = 0; i < Words<T>::N; ++i) {
+        const auto sw = HALF ? __builtin_amdgcn_permlane32_swap(a.w[i], a.w[i], false, false)
+                             : __builtin_amdgcn_permlane16_swap(a.w[i], a.w[i], false, false);
+        a.w[i] = sw[0];
+        b.w[i] = sw[1];
+    }
+    return op(from_words<T>(a), from_words<T>(b));
+}
+
+template <class T, class Op> __device__ __forceinline__ T wave_reduce(T x, Op op)
+{
+    x = op(x, dpp_move<kDppQuad1>(x));
+    x = op(x, dpp_move<kDppQuad2>(x));
+    x = op(x, dpp_move<kDppHalfMirror>(x));
+    x = op(x, dpp_move<kDppMirror>(x));
+    x = swap_combine<false>(x, op);
+    return swap_combine<true>(x, op);
+}
+
 __device__ __forceinline__ float wave_max(float v)
 {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1)
-        v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    return wave_reduce(v, [](float p, float q) { return fmaxf(p, q); });
 }
 
 __device__ __forceinline__ double wave_sum(double v)
 {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1)
-        v += __shfl_xor(v, o);
-    return v;
+    return wave_reduce(v, [](double p, double q) { return p + q; });
 }
 
 __device__ __forceinline__ int64_t wave_min(int64_t v)
 {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-        int64_t w = __shfl_xor(v, o);
-        v = w < v ? w : v;
-    }
-    return v;
+    return wave_reduce(v, [](int64_t p, int64_t q) { return q < p ? q : p; });
 }
 
 // Block-wide reductions; every thread gets the result.  `sh` is LDS scratch of
@@ -172,6 +228,34 @@ template <int BLOCK> __device__ __forceinline__ double block_sum(double v, doubl
         r += sh[i];
     __syncthreads();
     return r;
+}
+
+// N sums over the workgroup in one exchange (`sh`: N * BLOCK / 64 entries);
+// each is the same fixed-order sum block_sum forms.
+template <int BLOCK, int N> __device__ __forceinline__ void block_sum_n(double (&v)[N], double *sh)
+{
+    constexpr int W = BLOCK / kWave;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] = wave_sum(v[i]);
+    if constexpr (W == 1)
+        return;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            sh[i * W + wave] = v[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        double r = sh[i * W];
+#pragma unroll
+        for (int w = 1; w < W; ++w)
+            r += sh[i * W + w];
+        v[i] = r;
+    }
+    __syncthreads();
 }
 
 template <int BLOCK> __device__ __forceinline__ int64_t block_min(int64_t v, int64_t *sh)

@@ -15,7 +15,7 @@ struct LaneState {
     float m;    // exact largest stored value seen, -inf if none
     float s;    // sum of 2^((z - b) c), b = max(m, -FLT_MAX), c = log2(e)/T
     float comp; // Kahan compensation: the true sum is about s - comp
-    float h;    // sum of 2^((z - b) c) (b - z) / T, for the entropy
+    float h;    // sum of 2^((z - b) c) (b - z), for the entropy (1/T applied at the end)
     float zs;   // plain sum of the stored values (label smoothing only)
     int best;   // code of the first step in which m was reached
 };
@@ -32,9 +32,11 @@ template <int N> __device__ __forceinline__ float tree_sum(float (&e)[N])
 
 // Fold one step of N values into the lane state.  Excluded columns arrive as
 // -inf; MAYBE_INF selects the guarded entropy term for such steps.  WANT_Z
-// also sums the stored values.
+// also sums the stored values.  The entropy term is kept in units of the
+// stored values (one subtract and one FMA per column) and scaled by 1/T once
+// per lane when the workgroup combines.
 template <int DT, int N, bool WANT_H, bool WANT_ARG, bool MAYBE_INF, bool WANT_Z = false>
-__device__ __forceinline__ void fold(LaneState &st, float (&v)[N], int code, float c, float inv_t)
+__device__ __forceinline__ void fold(LaneState &st, float (&v)[N], int code, float c)
 {
     float sm = v[0];
 #pragma unroll
@@ -48,7 +50,7 @@ __device__ __forceinline__ void fold(LaneState &st, float (&v)[N], int code, flo
     // Rescale to the new base; f == 1 exactly when the maximum did not move.
     const float f = exp2_hw((bold - bnew) * c);
     if constexpr (WANT_H)
-        st.h = f * fmaf(fminf((bnew - bold) * inv_t, kBig), st.s, st.h);
+        st.h = f * fmaf(fminf(bnew - bold, kBig), st.s, st.h);
     st.s *= f;
     st.comp *= f;
     st.m = mnew;
@@ -75,7 +77,7 @@ __device__ __forceinline__ void fold(LaneState &st, float (&v)[N], int code, flo
         if constexpr (WANT_H) {
 #pragma unroll
             for (int i = 0; i < C; ++i) {
-                float d = (bnew - v[q * C + i]) * inv_t;
+                float d = bnew - v[q * C + i];
                 if constexpr (MAYBE_INF)
                     d = fminf(d, kBig);
                 ph = fmaf(e[i], d, ph);
@@ -270,39 +272,71 @@ struct RowStats {
     double Hs;     // sum of e^{(z - B)/T} (B - z)/T (entropy only)
     double Zs;     // sum of the non-target stored values of the range (WANT_Z)
     int64_t a_o;   // lowest non-target column holding M (argmax only)
+    float zt;      // the stored target logit (WANT_ZT only)
 };
+
+// The first wave step of a sweep: the row's geometry and this wave's first
+// vectors, whose loads depend only on the row's address.  Issued before the
+// row's label is known, so that the stream is in flight during that load.
+template <int DT, int U> struct SweepStart {
+    RowGeom g;
+    u32x4 cur[U];
+};
+
+template <int DT, int U, bool NT>
+__device__ __forceinline__ SweepStart<DT, U> sweep_start(const char *rowp, int64_t V, int64_t part,
+                                                        int64_t parts)
+{
+    constexpr int ES = Elem<DT>::kSize;
+    constexpr int64_t CH = (int64_t)kWave * U;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    SweepStart<DT, U> s0;
+    s0.g = row_geom<DT, U>(rowp, V, part, parts);
+    const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp + (size_t)s0.g.ahead * ES) + s0.g.vbeg;
+    if (wave < s0.g.nfull) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            s0.cur[u] = load16<NT>(vp + (int64_t)wave * CH + u * kWave + lane);
+    }
+    return s0;
+}
 
 // Sweep part `part` of `parts` of a row with one workgroup: per lane, fold the
 // range's columns (the target column t excluded) into (max, Kahan sum, entropy
 // term, first step of the max), then combine the lanes: the exact maximum
 // first, one rescale per lane to the common base, fp64 sums; the argmax comes
 // from re-reading the one step where each maximal lane first saw the maximum.
-// Every thread of the workgroup returns the same statistics.
-template <int DT, int BLOCK, int U, bool WANT_H, bool WANT_ARG, bool NT, bool WANT_Z = false>
-__device__ __forceinline__ RowStats sweep_row(const char *rowp, int64_t V, int64_t t, int64_t part, int64_t parts,
-                              float c, float inv_t, float *sh_f, double *sh_d, int64_t *sh_i)
+// Every thread of the workgroup returns the same statistics.  s0 holds the
+// range's geometry and the wave's first step (sweep_start); sh_d holds
+// 3 * BLOCK / 64 doubles.
+template <int DT, int BLOCK, int U, bool WANT_H, bool WANT_ARG, bool NT, bool WANT_Z = false,
+          bool WANT_ZT = false>
+__device__ __forceinline__ RowStats sweep_row_from(const char *rowp, int64_t t, const SweepStart<DT, U> &s0,
+                                                   float c, float inv_t, float *sh_f, double *sh_d,
+                                                   int64_t *sh_i)
 {
     constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize, W = BLOCK / kWave;
     constexpr int64_t CH = (int64_t)kWave * U;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const RowGeom g = row_geom<DT, U>(rowp, V, part, parts);
+    const RowGeom &g = s0.g;
     const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp + (size_t)g.ahead * ES) + g.vbeg;
     const int64_t col_v = g.ahead + g.vbeg * VE;   // first column of the range's vectors
     LaneState st{-INFINITY, 0.0f, 0.0f, 0.0f, 0.0f, -1};
 
-    // The wave's first step goes out before anything that needs the target
-    // column (whose load may still be in flight).
     int64_t k = wave;
     u32x4 cur[U], nxt[U];
-    if (k < g.nfull) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            cur[u] = load16<NT>(vp + k * CH + u * kWave + lane);
-    }
+    for (int u = 0; u < U; ++u)
+        cur[u] = s0.cur[u];
+    // The closing step's target logit, loaded after the first step so that
+    // waiting for that step never waits for it.
+    float zt = 0.0f;
+    if constexpr (WANT_ZT)
+        zt = load_elem<DT>(rowp, t);
 
     if (tid < g.head) {
         float v[1] = {tid == t ? -INFINITY : load_elem<DT>(rowp, tid)};
-        fold<DT, 1, WANT_H, WANT_ARG, true, WANT_Z>(st, v, tid, c, inv_t);
+        fold<DT, 1, WANT_H, WANT_ARG, true, WANT_Z>(st, v, tid, c);
     }
 
     // Full wave steps, interleaved over the waves, one step of loads in flight
@@ -328,9 +362,9 @@ __device__ __forceinline__ RowStats sweep_row(const char *rowp, int64_t V, int64
                             v[u * VE + e] = -INFINITY;
             }
             if (has_t)
-                fold<DT, U * VE, WANT_H, WANT_ARG, true, WANT_Z>(st, v, 16 + (int)k, c, inv_t);
+                fold<DT, U * VE, WANT_H, WANT_ARG, true, WANT_Z>(st, v, 16 + (int)k, c);
             else
-                fold<DT, U * VE, WANT_H, WANT_ARG, false, WANT_Z>(st, v, 16 + (int)k, c, inv_t);
+                fold<DT, U * VE, WANT_H, WANT_ARG, false, WANT_Z>(st, v, 16 + (int)k, c);
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 cur[u] = nxt[u];
@@ -344,18 +378,19 @@ __device__ __forceinline__ RowStats sweep_row(const char *rowp, int64_t V, int64
         for (int e = 0; e < VE; ++e)
             if (col_v + j * VE + e == t)
                 v[e] = -INFINITY;
-        fold<DT, VE, WANT_H, WANT_ARG, true, WANT_Z>(st, v, 16 + (int)(g.nfull + (j - g.nfull * CH)), c,
-                                             inv_t);
+        fold<DT, VE, WANT_H, WANT_ARG, true, WANT_Z>(st, v, 16 + (int)(g.nfull + (j - g.nfull * CH)), c);
     }
     if (g.tail0 + tid < g.tail1) {
         const int64_t col = g.tail0 + tid;
         float v[1] = {col == t ? -INFINITY : load_elem<DT>(rowp, col)};
-        fold<DT, 1, WANT_H, WANT_ARG, true, WANT_Z>(st, v, 16 + (int)(g.nfull + g.nrem + tid), c, inv_t);
+        fold<DT, 1, WANT_H, WANT_ARG, true, WANT_Z>(st, v, 16 + (int)(g.nfull + g.nrem + tid), c);
     }
 
     // Combine the lanes: exact maximum first, then each lane rescales its own
-    // sum once to the common base and the sums are added in fp64.  The argmax
-    // re-read goes out as soon as the maximum is known.
+    // sum once to the common base and the sums are added in fp64 (one LDS
+    // exchange for all of them).  The argmax re-read goes out as soon as the
+    // row's maximum is known, from the lanes that hold it.  (Issuing it after
+    // the wave's maximum instead, from every wave, measured slower.)
     const float M = block_max<BLOCK>(st.m, sh_f);
     Rescan<DT, U> rsc;
     if constexpr (WANT_ARG)
@@ -364,19 +399,36 @@ __device__ __forceinline__ RowStats sweep_row(const char *rowp, int64_t V, int64
     const float bl = fmaxf(st.m, -FLT_MAX);
     const float f = exp2_hw((bl - B) * c);
     const float sl = st.s - st.comp;
-    const double S = block_sum<BLOCK>((double)sl * (double)f, sh_d);
+    constexpr int NS = 1 + (WANT_H ? 1 : 0) + (WANT_Z ? 1 : 0);
+    double sums[NS];
+    sums[0] = (double)sl * (double)f;
+    if constexpr (WANT_H)
+        sums[1] = (double)f * (double)fmaf(fminf(B - bl, kBig), sl, st.h);
+    if constexpr (WANT_Z)
+        sums[NS - 1] = (double)st.zs;
+    block_sum_n<BLOCK, NS>(sums, sh_d);
+    const double S = sums[0];
     double Hs = 0.0;
     if constexpr (WANT_H)
-        Hs = block_sum<BLOCK>((double)f * (double)fmaf(fminf((B - bl) * inv_t, kBig), sl, st.h),
-                              sh_d);
+        Hs = sums[1] * (double)inv_t;
     double Zs = 0.0;
     if constexpr (WANT_Z)
-        Zs = block_sum<BLOCK>((double)st.zs, sh_d);
+        Zs = sums[NS - 1];
     int64_t a_o = INT64_MAX;
     if constexpr (WANT_ARG)
         a_o = block_min<BLOCK>(rescan_finish<DT, U>(rsc, M, t), sh_i);
 
-    return RowStats{M, S, Hs, Zs, a_o};
+    return RowStats{M, S, Hs, Zs, a_o, zt};
+}
+
+template <int DT, int BLOCK, int U, bool WANT_H, bool WANT_ARG, bool NT, bool WANT_Z = false,
+          bool WANT_ZT = false>
+__device__ __forceinline__ RowStats sweep_row(const char *rowp, int64_t V, int64_t t, int64_t part, int64_t parts,
+                              float c, float inv_t, float *sh_f, double *sh_d, int64_t *sh_i)
+{
+    const SweepStart<DT, U> s0 = sweep_start<DT, U, NT>(rowp, V, part, parts);
+    return sweep_row_from<DT, BLOCK, U, WANT_H, WANT_ARG, NT, WANT_Z, WANT_ZT>(rowp, t, s0, c, inv_t,
+                                                                               sh_f, sh_d, sh_i);
 }
 
 } // namespace cev

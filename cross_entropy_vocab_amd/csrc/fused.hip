@@ -43,7 +43,7 @@ __global__ __launch_bounds__(BLOCK) void k_fused_stream(FusedArgs a)
     constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize, W = BLOCK / kWave;
     constexpr int U2 = 4;
     __shared__ float sh_f[W];
-    __shared__ double sh_d[W];
+    __shared__ double sh_d[3 * W];
     __shared__ int64_t sh_i[W];
     __shared__ float sh_bc[4];
     __shared__ unsigned sh_sgn;

@@ -21,7 +21,7 @@ __global__ __launch_bounds__(BLOCK) void k_shard_sweep(ShardArgs a)
 {
     constexpr int ES = Elem<DT>::kSize, W = BLOCK / kWave;
     __shared__ float sh_f[W];
-    __shared__ double sh_d[W];
+    __shared__ double sh_d[3 * W];
     __shared__ int64_t sh_i[W];
     const int tid = threadIdx.x;
     const int64_t r = blockIdx.x;
