@@ -461,10 +461,12 @@ def bench_jsd(args, torch, cev, workloads, dev):
 
 def _time_calls(torch, calls, iters, warmup_s=0.05):
     """Mean GPU time in ms of each call in `calls` (functions of the iteration
-    index, run in order, iters times), from HIP events recorded on the
-    library's stream between the calls.  The calls first run back to back for
-    at least warmup_s seconds: after the host-side input generation the GPU
-    has idled, and its clocks take a while to come back up."""
+    index): each call runs iters times back to back between two HIP events
+    recorded on the library's stream, as a training or serving loop issues
+    it, so the time includes the dispatch gaps between its own launches but
+    no host work.  The calls first run in order, back to back, for at least
+    warmup_s seconds: after the host-side input generation the GPU has idled,
+    and its clocks take a while to come back up."""
     t_end = time.perf_counter() + warmup_s
     n = 0
     while n < 3 or time.perf_counter() < t_end:
@@ -472,16 +474,17 @@ def _time_calls(torch, calls, iters, warmup_s=0.05):
             c(n)
         torch.cuda.synchronize()
         n += 1
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-          for _ in range(iters)]
-    torch.cuda.synchronize()
-    for i, e in enumerate(ev):
-        e[0].record()
-        for k, c in enumerate(calls):
+    out = []
+    for c in calls:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(iters):
             c(i)
-            e[k + 1].record()
-    torch.cuda.synchronize()
-    return [float(np.mean([e[k].elapsed_time(e[k + 1]) for e in ev])) for k in range(len(calls))]
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / iters)
+    return out
 
 
 def bench_configs(args, torch, cev, workloads, dev):

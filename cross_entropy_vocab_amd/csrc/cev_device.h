@@ -230,6 +230,33 @@ template <int BLOCK> __device__ __forceinline__ double block_sum(double v, doubl
     return r;
 }
 
+// N maxima over the workgroup in one exchange (`sh`: N * BLOCK / 64 entries).
+template <int BLOCK, int N> __device__ __forceinline__ void block_max_n(float (&v)[N], float *sh)
+{
+    constexpr int W = BLOCK / kWave;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] = wave_max(v[i]);
+    if constexpr (W == 1)
+        return;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            sh[i * W + wave] = v[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        float r = sh[i * W];
+#pragma unroll
+        for (int w = 1; w < W; ++w)
+            r = fmaxf(r, sh[i * W + w]);
+        v[i] = r;
+    }
+    __syncthreads();
+}
+
 // N sums over the workgroup in one exchange (`sh`: N * BLOCK / 64 entries);
 // each is the same fixed-order sum block_sum forms.
 template <int BLOCK, int N> __device__ __forceinline__ void block_sum_n(double (&v)[N], double *sh)

@@ -236,12 +236,48 @@ __device__ __noinline__ void topk_close(double s, double B, double zk, double T,
     if (q)
         *q = (float)((u < 0.0 ? e : 1.0) / (1.0 + e));
 }
-template <int DT, int BLOCK, int U>
+// Masks gathered column x in a wave step whose first column is lo: a column
+// at offset d sits in lane (d / VE) % 64, vector d / (64 VE) of the lane,
+// element d % VE.
+template <int DT, int U>
+__device__ __forceinline__ void mask_gathered(float (&v)[U * Elem<DT>::kVE], int64_t x, int64_t lo,
+                                              int lane)
+{
+    constexpr int VE = Elem<DT>::kVE;
+    const int64_t d = x - lo;
+    if (x >= 0 && (uint64_t)d < (uint64_t)((int64_t)kWave * U * VE)) {
+        const int dd = (int)d;
+        if (((dd / VE) & (kWave - 1)) == lane) {
+            const int i = (dd / (kWave * VE)) * VE + dd % VE;
+#pragma unroll
+            for (int j = 0; j < U * VE; ++j)
+                if (j == i)
+                    v[j] = -INFINITY;
+        }
+    }
+}
+
+// Lane values of a wave as wave-uniform scalars (v_readlane).
+__device__ __forceinline__ int64_t lane_value(int64_t v, int l)
+{
+    const uint64_t u = (uint64_t)v;
+    const unsigned lo = __builtin_amdgcn_readlane((unsigned)u, l);
+    const unsigned hi = __builtin_amdgcn_readlane((unsigned)(u >> 32), l);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// SMALLK (K <= 64): every wave holds the K gathered columns in its lanes
+// (lane k: column k, -1 if ignored or out of range), read straight from the
+// index row, so the sweep starts one round trip after the row does and needs
+// no LDS for its exclusion tests; the gathered values are loaded while the
+// sweep runs and only the closing step reads them.  Otherwise the columns go
+// through LDS first.
+template <int DT, int BLOCK, int U, bool SMALLK>
 __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
 {
     constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize, W = BLOCK / kWave;
     constexpr int64_t CH = (int64_t)kWave * U;
-    __shared__ float sh_f[W];
+    __shared__ float sh_f[2 * W];
     __shared__ double sh_d[W];
     // Dynamic LDS sized by K: the gathered columns, their values and terms,
     // and first-occurrence flags (K <= kMaxK).
@@ -274,9 +310,9 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
         return;
     }
     const char *rowp = static_cast<const char *>(a.logits) + (size_t)r * (size_t)a.row_stride * ES;
+    const int64_t *irow = a.indices + (size_t)r * (size_t)a.index_row_stride;
     // The wave's first step of the row goes out before the gathered indices
-    // and values are read, so the stream is in flight during those two
-    // dependent round trips.
+    // are read, so the stream is in flight during that round trip.
     const RowGeom g = row_geom<DT, U>(rowp, V, 0, 1);
     const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp + (size_t)g.ahead * ES);
     u32x4 cur[U], nxt[U];
@@ -285,32 +321,48 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
         for (int u = 0; u < U; ++u)
             cur[u] = load16_stream(vp + (int64_t)wave * CH + u * kWave + lane);
     }
-    bool bad = false;
-    for (int k = tid; k < K; k += BLOCK) {
-        const int64_t i = a.indices[(size_t)r * (size_t)a.index_row_stride + k];
-        const bool ok = i != a.ignore_index && i >= 0 && i < V;
-        bad |= (i != a.ignore_index && !ok);
-        xcol[k] = ok ? i : -1;
-        xz[k] = ok ? load_elem<DT>(rowp, i) : -INFINITY;
+
+    int64_t mycol = -1;   // SMALLK: this lane's gathered column
+    float myz = -INFINITY;
+    if constexpr (SMALLK) {
+        if (lane < K) {
+            const int64_t i = irow[lane];
+            const bool ok = i != a.ignore_index && i >= 0 && i < V;
+            if (wave == 0 && i != a.ignore_index && !ok && a.status)
+                atomicOr(a.status, (int32_t)CEV_STATUS_BAD_INDEX);
+            mycol = ok ? i : -1;
+            if (ok)
+                myz = load_elem<DT>(rowp, i);   // used after the sweep
+        }
+    } else {
+        bool bad = false;
+        for (int k = tid; k < K; k += BLOCK) {
+            const int64_t i = irow[k];
+            const bool ok = i != a.ignore_index && i >= 0 && i < V;
+            bad |= (i != a.ignore_index && !ok);
+            xcol[k] = ok ? i : -1;
+            xz[k] = ok ? load_elem<DT>(rowp, i) : -INFINITY;
+        }
+        if (bad && a.status)
+            atomicOr(a.status, (int32_t)CEV_STATUS_BAD_INDEX);
+        __syncthreads();
+        for (int k = tid; k < K; k += BLOCK) {
+            bool first = xcol[k] >= 0;
+            for (int k2 = 0; k2 < k && first; ++k2)
+                first = xcol[k2] != xcol[k];
+            xfirst[k] = first;
+        }
+        __syncthreads();
     }
-    if (bad && a.status)
-        atomicOr(a.status, (int32_t)CEV_STATUS_BAD_INDEX);
-    __syncthreads();
-    for (int k = tid; k < K; k += BLOCK) {
-        bool first = xcol[k] >= 0;
-        for (int k2 = 0; k2 < k && first; ++k2)
-            first = xcol[k2] != xcol[k];
-        xfirst[k] = first;
-    }
-    __syncthreads();
 
     const float c = a.c;
     LaneState st{-INFINITY, 0.0f, 0.0f, 0.0f, 0.0f, -1};
 
+    // Whether column col is gathered (per lane; the lanes' columns may differ).
     auto excluded = [&](int64_t col) {
         bool x = false;
         for (int k = 0; k < K; ++k)
-            x |= xcol[k] == col;
+            x |= (SMALLK ? lane_value(mycol, k) : xcol[k]) == col;
         return x;
     };
 
@@ -319,15 +371,12 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
         fold<DT, 1, false, false, true>(st, v, 0, c);
     }
     {
-        // With at most 64 gathered columns, lane l holds the wave step that
-        // column l falls in (-1 if none), so that each step's test is one
-        // compare and a ballot rather than K 64-bit range checks.
-        const bool small_k = K <= kWave;
+        // Lane l holds the wave step that gathered column l falls in (-1 if
+        // none), so each step's test is one compare and a ballot.
         int my_step = -1;
-        if (small_k && lane < K) {
-            const int64_t x = xcol[lane];
-            if (x >= g.ahead && x < g.ahead + g.nfull * CH * VE)
-                my_step = (int)((x - g.ahead) / (CH * VE));
+        if constexpr (SMALLK) {
+            if (mycol >= g.ahead && mycol < g.ahead + g.nfull * CH * VE)
+                my_step = (int)((mycol - g.ahead) / (CH * VE));
         }
         int64_t k = wave;
         for (; k < g.nfull; k += W) {
@@ -341,36 +390,28 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
             unpack_step<DT, U>(cur, v);
             const int64_t lo = g.ahead + k * CH * VE;
             bool any;
-            if (small_k) {
-                any = __any(my_step == (int)k) != 0;
+            if constexpr (SMALLK) {
+                uint64_t hits = __ballot(my_step == (int)k);
+                any = hits != 0;
+                while (hits) {
+                    const int k2 = __builtin_ctzll(hits);
+                    hits &= hits - 1;
+                    mask_gathered<DT, U>(v, lane_value(mycol, k2), lo, lane);
+                }
             } else {
                 any = false;
                 for (int kk = 0; kk < K; kk += kWave) {
                     const int64_t x = kk + lane < K ? xcol[kk + lane] : -1;
                     any |= __any(x >= 0 && (uint64_t)(x - lo) < (uint64_t)(CH * VE)) != 0;
                 }
+                if (any)
+                    for (int k2 = 0; k2 < K; ++k2)
+                        mask_gathered<DT, U>(v, xcol[k2], lo, lane);
             }
-            if (any) {
-                // A gathered column at offset d in this step sits in lane
-                // (d / VE) % 64, vector d / (64 VE) of the lane, element d % VE.
-                for (int k2 = 0; k2 < K; ++k2) {
-                    const int64_t x = xcol[k2];
-                    const int64_t d = x - lo;
-                    if (x >= 0 && (uint64_t)d < (uint64_t)(CH * VE)) {
-                        const int dd = (int)d;
-                        if (((dd / VE) & (kWave - 1)) == lane) {
-                            const int i = (dd / (kWave * VE)) * VE + dd % VE;
-#pragma unroll
-                            for (int j = 0; j < U * VE; ++j)
-                                if (j == i)
-                                    v[j] = -INFINITY;
-                        }
-                    }
-                }
+            if (any)
                 fold<DT, U * VE, false, false, true>(st, v, 0, c);
-            } else {
+            else
                 fold<DT, U * VE, false, false, false>(st, v, 0, c);
-            }
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 cur[u] = nxt[u];
@@ -391,6 +432,58 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
         fold<DT, 1, false, false, true>(st, v, 0, c);
     }
 
+    const double T = a.temperature;
+    if constexpr (SMALLK) {
+        // The maxima over the swept and the gathered columns in one exchange;
+        // then wave 0's lane k closes index k from registers.
+        float mx[2] = {st.m, myz};
+        block_max_n<BLOCK, 2>(mx, sh_f);
+        const float M = mx[0];
+        const float Mall = fmaxf(mx[1], M);
+        const float B = fmaxf(M, -FLT_MAX);
+        const float bl = fmaxf(st.m, -FLT_MAX);
+        const float f = exp2_hw((bl - B) * c);
+        const double S = block_sum<BLOCK>((double)(st.s - st.comp) * (double)f, sh_d);
+        if (wave != 0)
+            return;
+        const float Ball = fmaxf(Mall, -FLT_MAX);
+        const double s_rest = S > 0.0 ? S * exp(((double)B - (double)Ball) / T) : 0.0;
+        // This lane's column counts once in the others' sums when it is the
+        // first occurrence of its column.
+        bool first = mycol >= 0;
+        for (int k2 = 0; k2 < K; ++k2)
+            first = first && !(k2 < lane && lane_value(mycol, k2) == mycol);
+        const double term = first ? exp(((double)myz - (double)Ball) / T) : 0.0;
+        double s_mine = s_rest, d = s_rest;   // sum over the others; over all columns
+        for (int k2 = 0; k2 < K; ++k2) {
+            const double tk = __builtin_bit_cast(double, lane_value(__builtin_bit_cast(int64_t, term), k2));
+            d += tk;
+            if (lane_value(mycol, k2) != mycol)
+                s_mine += tk;
+        }
+        if (lane < K) {
+            if (mycol < 0) {
+                out[lane] = 0.0f;
+                if (qout)
+                    qout[lane] = 0.0f;
+            } else {
+                topk_close(s_mine, (double)Ball, (double)myz, T, out + lane,
+                           qout ? qout + lane : nullptr);
+            }
+        }
+        if (a.saved && lane == 0) {
+            // The row's normaliser over all columns, for the top-K backward:
+            // d = sum_j e^{(z_j - m_z)/T} with m_z the exact row maximum.
+            cev_saved sv;
+            sv.m_z = Mall;
+            sv.log2_d = (float)(log(d) * kLog2e);
+            sv.q = 0.0f;
+            sv.flags = 1;
+            a.saved[r] = sv;
+        }
+        return;
+    }
+
     const float M = block_max<BLOCK>(st.m, sh_f);
     const float B = fmaxf(M, -FLT_MAX);
     const float bl = fmaxf(st.m, -FLT_MAX);
@@ -401,7 +494,6 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
         gm = fmaxf(gm, xz[k]);
     const float Mall = fmaxf(block_max<BLOCK>(gm, sh_f), M);
     const float Ball = fmaxf(Mall, -FLT_MAX);
-    const double T = a.temperature;
     const double s_rest = S > 0.0 ? S * exp(((double)B - (double)Ball) / T) : 0.0;
     // Each gathered column's term e^{(z - Ball)/T}, computed once (in
     // parallel over the indices) and summed below in index order by every
@@ -562,15 +654,20 @@ hipError_t launch_topk_sweep_cfg(int dtype, const SweepArgs &a, int block, int U
     const size_t lds = (size_t)a.K * (sizeof(int64_t) + sizeof(double) + sizeof(float) + 1);
 #define CEV_TOPK_CASE(B, UU)                                                                    \
     if (block == B && U == UU) {                                                                \
-        if (dtype == CEV_BF16)                                                                  \
-            hipLaunchKernelGGL((k_topk_sweep<CEV_BF16, B, UU>), grid, dim3(B), lds, s, a);      \
-        else                                                                                    \
-            hipLaunchKernelGGL((k_topk_sweep<CEV_F32, B, UU>), grid, dim3(B), lds, s, a);       \
+        if (a.K <= kWave) {                                                                     \
+            if (dtype == CEV_BF16)                                                              \
+                hipLaunchKernelGGL((k_topk_sweep<CEV_BF16, B, UU, true>), grid, dim3(B), lds, s, a); \
+            else                                                                                \
+                hipLaunchKernelGGL((k_topk_sweep<CEV_F32, B, UU, true>), grid, dim3(B), lds, s, a); \
+        } else {                                                                                \
+            if (dtype == CEV_BF16)                                                              \
+                hipLaunchKernelGGL((k_topk_sweep<CEV_BF16, B, UU, false>), grid, dim3(B), lds, s, a); \
+            else                                                                                \
+                hipLaunchKernelGGL((k_topk_sweep<CEV_F32, B, UU, false>), grid, dim3(B), lds, s, a); \
+        }                                                                                       \
         return hipGetLastError();                                                               \
     }
-    CEV_TOPK_CASE(128, 4)
     CEV_TOPK_CASE(256, 2)
-    CEV_TOPK_CASE(256, 4)
     CEV_TOPK_CASE(512, 2)
 #undef CEV_TOPK_CASE
     return hipErrorInvalidValue;
@@ -578,8 +675,9 @@ hipError_t launch_topk_sweep_cfg(int dtype, const SweepArgs &a, int block, int U
 
 hipError_t launch_topk_sweep(int dtype, const SweepArgs &a, hipStream_t s)
 {
-    // 256 x 2 (76 VGPRs): 62 us on 4096 x 32768 bf16 rows with K = 8, against
-    // 81-82 us for 256 x 4 (132 VGPRs) and 512 x 2, 68 us for 128 x 4.
+    // 256 x 2: on 4096 x 32768 bf16 rows with K = 8, 62 us against 81-82 us
+    // for 256 x 4 and 512 x 2 and 68 us for 128 x 4 (LDS-held indices); 52 us
+    // with the indices held in lanes (K <= 64).
     return launch_topk_sweep_cfg(dtype, a, 256, 2, s);
 }
 

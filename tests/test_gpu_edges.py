@@ -217,6 +217,44 @@ def test_topk_duplicates_ignored_and_bad_indices():
     assert_nonpositive("topk dup", got)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_topk_register_path_boundary(dtype):
+    """K = 64 (indices held in lanes) and K = 65 (indices in LDS) on rows that
+    start at every alignment (padded stride, NaN canaries), with gathered
+    columns in the unaligned head, the ragged tail and the last full step,
+    duplicates, an ignored entry and out-of-range ones: both against the
+    oracle, and the two paths agreeing bit for bit on the shared indices."""
+    from gpu_helpers import DEV, strided_dev, to_dev, to_host
+    R, V = 16, 3001
+    w = _rand_case(R, V, dtype, T=0.8, seed=21, mask_frac=0.2)
+    rng = np.random.default_rng(22)
+    idx = np.stack([rng.choice(V, 64, replace=False) for _ in range(R)]).astype(np.int64)
+    idx[:, 0] = np.arange(R) % 7           # head columns
+    idx[:, 1] = V - 1 - np.arange(R) % 3   # ragged tail
+    idx[:, 2] = idx[:, 5]                  # duplicate
+    idx[3, 9] = -100                       # ignored
+    idx[5, 10] = V                         # out of range
+    idx[7, 11] = -2                        # out of range
+    idx65 = np.concatenate([idx, np.full((R, 1), -100, np.int64)], axis=1)
+    logits = strided_dev(w["logits"], V + 3)
+    mask = to_dev(w["row_mask"])
+    got = {}
+    for K, ix in ((64, idx), (65, idx65)):
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
+        lp, q, saved = cev.sls_topk_forward(logits, to_dev(ix), 0.8, row_mask=mask, status=status,
+                                            saved=True)
+        torch.cuda.synchronize()
+        got[K] = (to_host(lp), to_host(q), saved.cpu().numpy(), int(status.item()))
+        assert got[K][3] & cev.STATUS_BAD_INDEX, K
+        want, _ = oracle.topk_rows(w["logits"], ix, 0.8, row_mask=w["row_mask"])
+        assert_close(f"topk K={K}", got[K][0], want, RTOL[dtype]["topk"])
+        assert_nonpositive(f"topk K={K}", got[K][0])
+    assert np.array_equal(got[64][0], got[65][0][:, :64])
+    assert np.array_equal(got[64][1], got[65][1][:, :64])
+    assert np.all(got[65][0][:, 64] == 0) and np.all(got[65][1][:, 64] == 0)
+    assert np.array_equal(got[64][2], got[65][2])
+
+
 def test_topk_large_k_and_peaked():
     """K = 100 gathered columns on peaked rows: the peak's own log p keeps its
     tiny complement (never 0, never positive)."""
