@@ -329,10 +329,11 @@ __device__ __forceinline__ RowStats sweep_row_from(const char *rowp, int64_t t, 
     for (int u = 0; u < U; ++u)
         cur[u] = s0.cur[u];
     // The closing step's target logit, loaded after the first step so that
-    // waiting for that step never waits for it.
+    // waiting for that step never waits for it (column 0 when the range holds
+    // no target, t < 0; the value is then unused).
     float zt = 0.0f;
     if constexpr (WANT_ZT)
-        zt = load_elem<DT>(rowp, t);
+        zt = load_elem<DT>(rowp, t >= 0 ? t : 0);
 
     if (tid < g.head) {
         float v[1] = {tid == t ? -INFINITY : load_elem<DT>(rowp, tid)};

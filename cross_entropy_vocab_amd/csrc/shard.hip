@@ -25,8 +25,8 @@ __global__ __launch_bounds__(BLOCK) void k_shard_sweep(ShardArgs a)
     __shared__ int64_t sh_i[W];
     const int tid = threadIdx.x;
     const int64_t r = blockIdx.x;
-    const int64_t tg = a.labels[r];
-    const bool masked = a.row_mask && a.row_mask[r] == 0;
+    const int64_t tg = load_uniform(a.labels + r);
+    const bool masked = a.row_mask && mask_byte(a.row_mask, r) == 0;
     const bool ignored = masked || tg == a.ignore_index;
     const bool bad = !ignored && (tg < 0 || tg >= a.vocab_total);
     if (ignored || bad) {
@@ -49,12 +49,14 @@ __global__ __launch_bounds__(BLOCK) void k_shard_sweep(ShardArgs a)
     const int64_t tl = tg - a.col_offset;
     const bool owns = tl >= 0 && tl < a.vocab;
     const char *rowp = static_cast<const char *>(a.logits) + (size_t)r * (size_t)a.row_stride * ES;
-    const RowStats rs = sweep_row<DT, BLOCK, U, WANT_H, true, true, WANT_Z>(
+    // The shard's target logit, when it holds the label, is loaded with the
+    // sweep's first step (column 0 stands in otherwise, unused).
+    const RowStats rs = sweep_row<DT, BLOCK, U, WANT_H, true, true, WANT_Z, true>(
         rowp, a.vocab, owns ? tl : -1, 0, 1, a.c, a.inv_t, sh_f, sh_d, sh_i);
     if (tid == 0) {
         cev_vocab_partial p;
         p.m = rs.M;
-        p.zt = owns ? load_elem<DT>(rowp, tl) : 0.0f;
+        p.zt = owns ? rs.zt : 0.0f;
         p.arg = rs.a_o == INT64_MAX ? INT64_MAX : rs.a_o + a.col_offset;
         p.s = rs.S;
         p.h = rs.Hs;
