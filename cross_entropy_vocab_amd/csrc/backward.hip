@@ -496,6 +496,127 @@ __global__ __launch_bounds__(BLOCK) void k_topk_backward(TopkBackwardArgs a, int
     }
 }
 
+// The top-K backward for K <= 64 on rows of whole 16-byte vectors: one-shot
+// tiles of BLOCK * U vectors in row order (tile n of row n / slices, the
+// division by multiply-shift), the saved record read first and the tile's
+// loads issued as soon as it marks the row as read.  Every wave holds the K
+// entries in its lanes (lane k: index k, its g and q), forms Gs and, for the
+// first occurrence of each gathered column, G_j and the two terms of that
+// column from the lanes with v_readlane, in the same order as the general
+// kernel; no LDS and no barrier.  A gathered column is applied by the lane
+// that holds its vector.
+template <int DT, int BLOCK, int U>
+__global__ __launch_bounds__(BLOCK) void k_topk_backward_tile(const cev_saved *saved, const char *logits,
+                                                              uint64_t row_bytes, uint64_t mul,
+                                                              uint32_t shift, uint32_t slices,
+                                                              uint32_t total, TopkBackwardArgs a)
+{
+    constexpr int VE = Elem<DT>::kVE;
+    constexpr uint32_t per = (uint32_t)BLOCK * U;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const uint32_t bid = blockIdx.x;
+    if (bid >= total)
+        return;
+    const uint32_t r = (uint32_t)(((uint64_t)bid * mul) >> shift);
+    const uint32_t sl = bid - r * slices;
+    const u32x4 rec = load_uniform(reinterpret_cast<const u32x4 *>(saved + r));
+    const uint32_t v0 = sl * per;
+    const u32x4 *lvp = reinterpret_cast<const u32x4 *>(logits + (size_t)r * row_bytes) + v0;
+    const int64_t V = a.vocab;
+    const int64_t nvec = V / VE;
+    const uint32_t nv = (uint32_t)(nvec - v0 < (int64_t)per ? nvec - v0 : per);
+    u32x4 w[U];
+    if (rec[3] & 1u) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t j = (uint32_t)(u * BLOCK + tid);
+            if (j < nv)
+                w[u] = load16_stream(lvp + j);
+        }
+    }
+    const bool masked = (a.row_mask && mask_byte(a.row_mask, r) == 0) || !(rec[3] & 1u);
+    const int K = (int)a.K;
+    int64_t col = -1;
+    float g = 0.0f, q = 0.0f;
+    bool bad = false;
+    if (lane < K) {
+        const int64_t i = a.indices[(size_t)r * (size_t)a.index_row_stride + lane];
+        g = a.g[(size_t)r * (size_t)K + lane];
+        q = a.q[(size_t)r * (size_t)K + lane];
+        const bool ok = i != a.ignore_index && i >= 0 && i < V;
+        bad = i != a.ignore_index && !ok;
+        col = ok ? i : -1;
+    }
+    if (sl == 0 && wave == 0 && !masked && __any(bad) && lane == 0 && a.status)
+        atomicOr(a.status, (int32_t)CEV_STATUS_BAD_INDEX);
+    // Gs: the valid g_k summed in fp64 (the same value in every lane and tile).
+    const float gs = (float)wave_sum(col >= 0 ? (double)g : 0.0);
+    // This lane's column: first occurrence, and G_j over its later duplicates.
+    bool first = col >= 0;
+    double gj = 0.0;
+    for (int k2 = 0; k2 < K; ++k2) {
+        const int64_t c2 = lane_value(col, k2);
+        if (c2 == col) {
+            if (k2 < lane)
+                first = false;
+            else
+                gj += (double)lane_value(g, k2);
+        }
+    }
+    const float la = first ? (float)(gj * (double)q * (double)a.inv_t) : 0.0f;
+    const float lb = first ? (float)(((double)gs - gj) * (double)a.inv_t) : 0.0f;
+    // The tile-relative vector of this lane's column, if the tile writes it.
+    const int64_t jj = first ? col / VE - (int64_t)v0 : -1;
+    const bool mine = jj >= 0 && jj < (int64_t)nv;
+
+    u32x4 *dvp = reinterpret_cast<u32x4 *>(static_cast<char *>(a.dlogits) +
+                                           (size_t)r * (size_t)a.d_row_stride * Elem<DT>::kSize) + v0;
+    if (masked) {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t j = (uint32_t)(u * BLOCK + tid);
+            if (j < nv)
+                store16_stream(zero, dvp + j);
+        }
+        return;
+    }
+    const float mz = __uint_as_float(rec[0]), l2d = __uint_as_float(rec[1]), c = a.c;
+    const float gsT = gs * a.inv_t;
+    const float kexp = l2d - __log2f(fabsf(gsT));
+    // Every column but the gathered ones is -(Gs/T) p_j: the sign applied to
+    // the bits is the opposite of Gs's; gathered values are pre-flipped.
+    const unsigned sgn = (__float_as_uint(gsT) & 0x80000000u) ^ 0x80000000u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t j = (uint32_t)(u * BLOCK + tid);
+        float z[VE], o[VE];
+        unpack16<DT>(w[u], z);
+#pragma unroll
+        for (int e = 0; e < VE; ++e)
+            o[e] = exp2_hw(fmaf(z[e] - mz, c, -kexp));
+        // gathered columns in this wave's vectors of step u
+        uint64_t hits = __ballot(mine && jj / BLOCK == u && (jj % BLOCK) / kWave == wave);
+        while (hits) {
+            const int k2 = __builtin_ctzll(hits);
+            hits &= hits - 1;
+            const int64_t c2 = lane_value(col, k2);
+            if ((int64_t)((c2 / VE - (int64_t)v0) % kWave) == lane) {
+                const float a2 = lane_value(la, k2), b2 = lane_value(lb, k2);
+                const int e2 = (int)(c2 % VE);
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    if (e == e2) {
+                        const float p = exp2_hw(fmaf(z[e] - mz, c, -l2d));
+                        o[e] = __uint_as_float(__float_as_uint(a2 - p * b2) ^ sgn);
+                    }
+            }
+        }
+        if (j < nv)
+            store16_stream(pack_vec<DT>(o, sgn), dvp + j);
+    }
+}
+
 template <int DT, int BLOCK, int U, bool SHARD, bool SNT>
 hipError_t launch_bwd_t(const BackwardArgs &a, int iters, int order, hipStream_t s)
 {
@@ -693,8 +814,52 @@ hipError_t launch_topk_backward_cfg(int dtype, const TopkBackwardArgs &a, int bl
     return hipErrorInvalidValue;
 }
 
+template <int DT, int B, int UU>
+hipError_t launch_topk_bwd_tile_t(const TopkBackwardArgs &a, hipStream_t s)
+{
+    const int64_t nvec = a.vocab / Elem<DT>::kVE;
+    const int64_t per = (int64_t)B * UU;
+    const int64_t slices = (nvec + per - 1) / per;
+    const int64_t total = a.rows * slices;   // < 2^31, checked by the caller
+    const DivMagic dm = div_magic((uint32_t)slices);
+    hipLaunchKernelGGL((k_topk_backward_tile<DT, B, UU>), dim3((unsigned)total), dim3(B), 0, s,
+                       a.saved, static_cast<const char *>(a.logits),
+                       (uint64_t)a.row_stride * Elem<DT>::kSize, dm.mul, dm.shift, (uint32_t)slices,
+                       (uint32_t)total, a);
+    return hipGetLastError();
+}
+
+// Whether the lane-held form applies: K <= 64 and every row of both matrices
+// starting 16-byte aligned with whole 16-byte vectors.
+inline bool topk_tile_ok(const TopkBackwardArgs &a, int es)
+{
+    const int64_t per = 256;   // the smallest tile launched
+    return a.K <= kWave && ((uintptr_t)a.logits & 15u) == 0 && ((uintptr_t)a.dlogits & 15u) == 0 &&
+           (a.row_stride * es) % 16 == 0 && (a.d_row_stride * es) % 16 == 0 &&
+           (a.vocab * es) % 16 == 0 &&
+           a.rows * ((a.vocab * es / 16 + per - 1) / per) < ((int64_t)1 << 31);
+}
+
+hipError_t launch_topk_backward_tile_cfg(int dtype, const TopkBackwardArgs &a, int block, int U,
+                                         hipStream_t s)
+{
+    if (!topk_tile_ok(a, dtype == CEV_BF16 ? 2 : 4))
+        return hipErrorInvalidValue;
+#define CEV_TKT_CASE(B, UU)                                                                     \
+    if (block == B && U == UU)                                                                  \
+        return dtype == CEV_BF16 ? launch_topk_bwd_tile_t<CEV_BF16, B, UU>(a, s)                \
+                                 : launch_topk_bwd_tile_t<CEV_F32, B, UU>(a, s);
+    CEV_TKT_CASE(256, 1)
+    CEV_TKT_CASE(256, 2)
+    CEV_TKT_CASE(256, 4)
+#undef CEV_TKT_CASE
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_topk_backward(int dtype, const TopkBackwardArgs &a, hipStream_t s)
 {
+    if (topk_tile_ok(a, dtype == CEV_BF16 ? 2 : 4))
+        return launch_topk_backward_tile_cfg(dtype, a, 256, 2, s);
     return launch_topk_backward_cfg(dtype, a, 256, 4, s);
 }
 

@@ -191,6 +191,23 @@ __device__ __forceinline__ int64_t wave_min(int64_t v)
     return wave_reduce(v, [](int64_t p, int64_t q) { return q < p ? q : p; });
 }
 
+// A lane's value as a wave-uniform scalar (v_readlane).
+__device__ __forceinline__ int64_t lane_value(int64_t v, int l)
+{
+    const uint64_t u = (uint64_t)v;
+    const unsigned lo = __builtin_amdgcn_readlane((unsigned)u, l);
+    const unsigned hi = __builtin_amdgcn_readlane((unsigned)(u >> 32), l);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ float lane_value(float v, int l)
+{
+    return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), l));
+}
+__device__ __forceinline__ double lane_value(double v, int l)
+{
+    return __builtin_bit_cast(double, lane_value(__builtin_bit_cast(int64_t, v), l));
+}
+
 // Block-wide reductions; every thread gets the result.  `sh` is LDS scratch of
 // BLOCK / 64 entries that the caller does not touch in between.  The combine
 // order is fixed, so results are deterministic.

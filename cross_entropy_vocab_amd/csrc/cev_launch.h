@@ -142,6 +142,10 @@ struct TopkBackwardArgs {
 };
 
 hipError_t launch_topk_backward(int dtype, const TopkBackwardArgs &a, hipStream_t stream);
+// The lane-held tile form (K <= 64, rows of whole aligned 16-byte vectors), for
+// tuning harnesses; hipErrorInvalidValue where it does not apply.
+hipError_t launch_topk_backward_tile_cfg(int dtype, const TopkBackwardArgs &a, int block, int U,
+                                         hipStream_t stream);
 
 // Vocab-parallel shard sweep: one partial record per row over one shard.
 struct ShardArgs {

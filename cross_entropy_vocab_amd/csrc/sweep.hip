@@ -257,15 +257,6 @@ __device__ __forceinline__ void mask_gathered(float (&v)[U * Elem<DT>::kVE], int
     }
 }
 
-// Lane values of a wave as wave-uniform scalars (v_readlane).
-__device__ __forceinline__ int64_t lane_value(int64_t v, int l)
-{
-    const uint64_t u = (uint64_t)v;
-    const unsigned lo = __builtin_amdgcn_readlane((unsigned)u, l);
-    const unsigned hi = __builtin_amdgcn_readlane((unsigned)(u >> 32), l);
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
 // SMALLK (K <= 64): every wave holds the K gathered columns in its lanes
 // (lane k: column k, -1 if ignored or out of range), read straight from the
 // index row, so the sweep starts one round trip after the row does and needs
@@ -456,7 +447,7 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
         const double term = first ? exp(((double)myz - (double)Ball) / T) : 0.0;
         double s_mine = s_rest, d = s_rest;   // sum over the others; over all columns
         for (int k2 = 0; k2 < K; ++k2) {
-            const double tk = __builtin_bit_cast(double, lane_value(__builtin_bit_cast(int64_t, term), k2));
+            const double tk = lane_value(term, k2);
             d += tk;
             if (lane_value(mycol, k2) != mycol)
                 s_mine += tk;

@@ -225,6 +225,39 @@ def test_topk_backward_duplicates_ignored_bad_and_masked():
     assert got["status"] & cev.STATUS_BAD_INDEX
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_topk_backward_lane_form_boundary(dtype):
+    """K = 64 (tiles with the entries held in lanes) and K = 65 (the general
+    kernel): against the oracle, and equal bit for bit on the shared entries,
+    with duplicates (three at one column), an ignored entry, bad entries,
+    masked rows, and gathered columns in the first and last vector of a row
+    and on a tile boundary."""
+    from gpu_helpers import run_topk_fb
+    R, V = 12, 12288
+    w = _rand_case(R, V, dtype, T=0.9, seed=51, mask_frac=0.25)
+    w["row_mask"][:4] = 1
+    w["row_mask"][5] = 0
+    rng = np.random.default_rng(52)
+    idx = np.stack([rng.choice(V, 64, replace=False) for _ in range(R)]).astype(np.int64)
+    idx[:, 0] = 0
+    idx[:, 1] = V - 1
+    tile = 512 * (8 if dtype == "bf16" else 4)    # columns per 256 x 2 tile
+    idx[:, 2] = tile * (1 + np.arange(R) % 2) - np.arange(R) % 2   # a tile's last or first column
+    idx[:, 3] = idx[:, 5]
+    idx[0, 4] = idx[0, 5]
+    idx[2, 9] = -100
+    idx[3, 10] = V
+    g = rng.standard_normal((R, 64)).astype(np.float32)
+    got64 = run_topk_fb(w, idx, g)
+    _check_topk(w, idx, g, got64, "K=64")
+    idx65 = np.concatenate([idx, np.full((R, 1), -100, np.int64)], axis=1)
+    g65 = np.concatenate([g, rng.standard_normal((R, 1)).astype(np.float32)], axis=1)
+    got65 = run_topk_fb(w, idx65, g65)
+    _check_topk(w, idx65, g65, got65, "K=65")
+    assert got64["status"] & cev.STATUS_BAD_INDEX and got65["status"] & cev.STATUS_BAD_INDEX
+    assert np.array_equal(got64["dlogits"], got65["dlogits"])
+
+
 def test_topk_backward_peaked_large_k():
     """K = 100 on peaked rows with the peak gathered: the peak's gradient is
     G q - p (Gs - G) without cancellation in 1 - p."""
