@@ -131,7 +131,8 @@ def run_counter_workload(name, torch, cev, workloads, dev, reps=3):
         kernels = [
             dict(regex=r"^k_sls_sweep<", call="sls_forward", read=R * V * 2, write=0),
             dict(regex=r"^k_topk_sweep<", call="sls_topk_forward", read=R * V * 2, write=0),
-            dict(regex=r"^k_topk_backward<", call="sls_topk_backward", read=R * V * 2, write=R * V * 2)]
+            dict(regex=r"^k_topk_backward(_tile)?<", call="sls_topk_backward", read=R * V * 2,
+                 write=R * V * 2)]
     elif name in ("peaked_f32", "peaked_bf16"):
         dt = name.split("_")[1]
         w = workloads.peaked(dt)
