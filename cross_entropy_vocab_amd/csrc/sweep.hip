@@ -580,6 +580,7 @@ hipError_t launch_sls_sweep_cfg(int dtype, const SweepArgs &a, bool want_h, bool
     CEV_SLS_CASE(64, 4)
     CEV_SLS_CASE(128, 4)
     CEV_SLS_CASE(256, 2)
+    CEV_SLS_CASE(256, 4)
     CEV_SLS_CASE(512, 2)
     CEV_SLS_CASE(512, 4)
 #undef CEV_SLS_CASE
@@ -635,7 +636,14 @@ hipError_t launch_sls_sweep(int dtype, const SweepArgs &a, bool want_h, bool wan
     }
     if (a.rowlist)
         return hipErrorInvalidValue; // a row list comes only with split rows
-    const Shape sh = pick_shape(a.vocab / (dtype == CEV_BF16 ? 8 : 4));
+    Shape sh = pick_shape(a.vocab / (dtype == CEV_BF16 ? 8 : 4));
+    // Long rows: 512 x 4 where it still holds seven or eight waves per SIMD
+    // (fp32; bf16 without the entropy term, 73 VGPRs), 512 x 2 for bf16 with
+    // the entropy term (81 VGPRs at 512 x 4).  Same-process A/B against
+    // 512 x 2: grpo forward 328.6 against 332.2 us, peaked fp32 with entropy
+    // 187.3 against 191.0 us, peaked bf16 with entropy 105.7 against 103.1 us.
+    if (sh.block == 512 && sh.U == 2 && (dtype == CEV_F32 || !want_h))
+        sh.U = 4;
     return launch_sls_sweep_cfg(dtype, a, want_h, want_arg, sh.block, sh.U, s);
 }
 
