@@ -65,7 +65,8 @@ def measured_traffic():
 # of the same command into per-kernel durations, bandwidth and traffic
 # against algorithmic bytes.  Each kernel is matched by a regular expression
 # on its name without the namespace and argument list.
-COUNTER_WORKLOADS = ("grpo", "chunk", "peaked_f32", "peaked_bf16", "jsd_b0", "jsd_b05", "jsd_b1")
+COUNTER_WORKLOADS = ("grpo", "chunk", "peaked_f32", "peaked_bf16", "jsd_b0", "jsd_b05", "jsd_b1",
+                     "linear")
 
 
 def _short_name(name):
@@ -167,6 +168,31 @@ def run_counter_workload(name, torch, cev, workloads, dev, reps=3):
             dict(regex=r"^k_jsd_forward<", call="jsd_forward", read=2 * nv * V * 2, write=0),
             dict(regex=r"^k_jsd_(bwd_tiles|backward)<", call="jsd_backward",
                  read=2 * nv * V * 2, write=R * V * 2, per_call=True)]
+    elif name == "linear":
+        R, H, V = 8192, 2560, 151936
+        w = workloads.linear(rows=R, hidden=H, vocab=V)
+        hid = torch.from_numpy(w["hidden"].view(np.int16)).to(dev).view(torch.bfloat16)
+        head = torch.from_numpy(w["weight"].view(np.int16)).to(dev).view(torch.bfloat16)
+        lab, msk = torch.from_numpy(w["labels"]).to(dev), torch.from_numpy(w["row_mask"]).to(dev)
+        gl = torch.from_numpy(w["g"]).to(dev)
+        for _ in range(reps):
+            out = cev.lce_forward(hid, head, lab, 1.0, row_mask=msk, argmax=True)
+            cev.lce_backward(hid, head, lab, gl, out["saved"], 1.0, row_mask=msk,
+                             workspace=out["workspace"])
+        desc = (f"linear CE, hidden {R}x{H}, head {V}x{H} bf16, forward with argmax and the "
+                f"frozen-head backward (dhidden); bytes are each operand read once and each "
+                f"output written once (the kernels are bound by the matrix cores, not HBM)")
+        ops = R * H * 2 + V * H * 2
+        kernels = [
+            dict(regex=r"^k_lce_fwd<", call="lce_forward", read=ops, write=0),
+            dict(regex=r"^k_lce_dl", call="lce_backward: logits again, dlogits", read=ops,
+                 write=R * V * 2),
+            dict(regex=r"^k_transpose", call="lce_backward: head transposed", read=V * H * 2,
+                 write=V * H * 2),
+            dict(regex=r"^k_lce_gemm", call="lce_backward: dhidden, split-K partials",
+                 read=R * V * 2 + V * H * 2, write=4 * R * H * 4),
+            dict(regex=r"^k_splitk_reduce", call="lce_backward: split-K sum", read=4 * R * H * 4,
+                 write=R * H * 4)]
     else:
         raise SystemExit(f"unknown counter workload {name!r}; one of {COUNTER_WORKLOADS}")
     src = torch.ones(2 ** 28, dtype=torch.float32, device=dev)
