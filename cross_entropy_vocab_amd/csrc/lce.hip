@@ -21,8 +21,8 @@
 //             product runs with both operands contiguous along the contraction.
 //
 // Tiles: 8 waves in a 4 x 2 grid (two per SIMD), each wave 64 x 128 of C as
-// 2 x 4 blocks of 32 x 32; K steps of 64, staged through registers into a
-// double-buffered LDS tile of 2 x 64 KB.  A 256 x 256 workgroup tile needs
+// 2 x 4 blocks of 32 x 32; K steps of 64, copied from global memory straight
+// into a double-buffered LDS tile of 2 x 64 KB (LDS-DMA).  A 256 x 256 workgroup tile needs
 // 64 KB of operands per 256 x 256 x 64 MACs, half the traffic per MAC of a
 // 128 x 256 tile, and the second wave on each SIMD covers the first's loads
 // and barriers; the LDS-fragment + MFMA loop alone runs at 88% of the bf16
@@ -45,7 +45,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kLT = 512;                         // threads per workgroup (8 waves)
 constexpr int kBM = 256, kBN = 256, kBK = 64;    // workgroup tile
 constexpr int kTM = 2, kTN = 4;                  // 32 x 32 blocks per wave (64 x 128)
-constexpr int kChunks = kBM * kBK / 8 / kLT;     // 16-byte loads per thread per operand
+constexpr int kChunks = kBM * kBK / 8 / kLT;     // 16-byte copies per thread per operand
 constexpr float kBigL = 3.0e38f;
 
 struct GemmSmem {
@@ -70,29 +70,43 @@ __device__ __forceinline__ int perm_b(int q)
 }
 
 // Rows [r0, r0 + 256) x k [k0, k0 + 64) of a K-contiguous bf16 matrix
-// X[row * ld + k] into registers (tile row q from matrix row r0 + q, or
-// r0 + perm_b(q) for a B tile); rows past `rows` re-read the last row
-// (their results are never used).
+// X[row * ld + k] copied from global memory straight into the LDS tile `lds`
+// (global_load_lds_dwordx4: each lane's 16 bytes land at M0 + 16 * lane, with
+// no VGPR or LDS-store instruction in between).  Wave w's instruction i fills
+// the 64 chunks [512 i + 64 w, +64) of the tile, so each lane fetches the
+// chunk that the swizzled layout keeps at its position: tile row q = p / 8,
+// logical chunk (p % 8) ^ (q % 8), from matrix row r0 + q (r0 + perm_b(q) for
+// a B tile); rows past `rows` re-read the last row (their results are never
+// used).  The copies complete in order with the other vector-memory
+// operations of the wave, so dma_wait() (vmcnt 0) followed by a barrier
+// makes the whole tile visible to every wave.  M0 is set in the same asm
+// statement, one wait state before its use.
 template <bool PERM>
-__device__ __forceinline__ void load_tile(const unsigned short *X, int64_t ld, int64_t rows,
-                                          int64_t r0, int64_t k0, u32x4 (&r)[kChunks], int tid)
+__device__ __forceinline__ void dma_tile(const unsigned short *X, int64_t ld, int64_t rows,
+                                         int64_t r0, int64_t k0, unsigned short *lds, int tid)
 {
+    const int lane = tid & 63, w = tid >> 6;
+    const unsigned base =
+        (unsigned)(uintptr_t)(const __attribute__((address_space(3))) unsigned short *)lds;
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
-        const int c = tid + kLT * i;
-        const int q = PERM ? perm_b(c >> 3) : (c >> 3);
-        const int64_t gr = r0 + q < rows ? r0 + q : rows - 1;
-        r[i] = *reinterpret_cast<const u32x4 *>(X + gr * ld + k0 + (c & 7) * 8);
+        const int p = kLT * i + 64 * w + lane;
+        const int q = p >> 3;
+        const int lc = (p & 7) ^ (q & 7);
+        const int mr = PERM ? perm_b(q) : q;
+        const int64_t gr = r0 + mr < rows ? r0 + mr : rows - 1;
+        const unsigned short *src = X + gr * ld + k0 + lc * 8;
+        const unsigned m0 =
+            __builtin_amdgcn_readfirstlane(base + (unsigned)(kLT * i + 64 * w) * 16u);
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :: "s"(m0), "v"(src) : "memory");
     }
 }
 
-__device__ __forceinline__ void store_tile(unsigned short *lds, const u32x4 (&r)[kChunks], int tid)
+// Wait for this wave's tile copies (and its other vector-memory operations).
+__device__ __forceinline__ void dma_wait()
 {
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-        const int c = tid + kLT * i;
-        *reinterpret_cast<u32x4 *>(lds + lds_at(c >> 3, (c & 7) * 8)) = r[i];
-    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Fragments of K sub-step ks (16 deep) for this wave: A rows wm*64 + 32 mb +
@@ -113,14 +127,21 @@ __device__ __forceinline__ void frag_load(const unsigned short *la, const unsign
 }
 
 // One K step of 64 from LDS: 4 sub-steps of 16, 8 MFMAs each per wave, with
-// the fragments of sub-step ks + 1 read before the MFMAs of sub-step ks
-// (double-buffered in registers; 7% faster on MI355X with the interleaved
-// schedule than reading each sub-step's fragments just before its MFMAs).
+// the fragments of sub-step ks + 1 read while the MFMAs of sub-step ks issue
+// (one MFMA, one LDS read, in turn).  issue() runs once the first sub-step's
+// reads are out: the caller starts the next K step's tile copies there.
+struct NoIssue {
+    __device__ void operator()() const {}
+};
+
+template <class F = NoIssue>
 __device__ __forceinline__ void mma_stage(const unsigned short *la, const unsigned short *lb,
-                                          f32x16 (&acc)[kTM][kTN], int wm, int wn, int lane)
+                                          f32x16 (&acc)[kTM][kTN], int wm, int wn, int lane,
+                                          F &&issue = NoIssue{})
 {
     bf16x8 af[2][kTM], bf[2][kTN];
     frag_load(la, lb, af[0], bf[0], 0, wm, wn, lane);
+    issue();
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
         if (ks + 1 < kBK / 16)
@@ -131,6 +152,15 @@ __device__ __forceinline__ void mma_stage(const unsigned short *la, const unsign
             for (int nb = 0; nb < kTN; ++nb)
                 acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     af[ks & 1][mb], bf[ks & 1][nb], acc[mb][nb], 0, 0, 0);
+        if (ks + 1 < kBK / 16) {
+            // scheduling groups (mask 0x008: MFMA, 0x100: LDS read)
+#pragma unroll
+            for (int q = 0; q < kTM + kTN; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, kTM * kTN - (kTM + kTN), 0);
+        }
     }
 }
 
@@ -146,16 +176,17 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[kTM][kTN])
 }
 
 // The K loop over every (N tile, K step) pair of one workgroup, with the next
-// pair's global loads in flight during the current pair's MFMAs; after the
+// pair's tile copies in flight during the current pair's MFMAs; after the
 // last K step of a tile, epi(tile, acc) consumes the accumulators.  A: rows
 // [row0, row0 + 256) of XA; B: 256-row tiles [t_begin, t_end) of XB (staged
-// permuted, see perm_b); nk K steps of 64.
+// permuted, see perm_b); nk K steps of 64.  Each step ends with dma_wait and a
+// barrier: the next buffer is then complete and the current one free.
 //
-// All but the last K step of a tile run a branch-free body (loads of the next
-// step, MFMAs, LDS stores, barrier) that the compiler's MFMA/LDS interleaving
-// strategy (iglp_opt 0) schedules as one region: 15% faster than its default
-// schedule on MI355X.  The last step of a tile is peeled so that the
-// epilogue runs while the next tile's first loads are in flight.
+// The last step of a tile is peeled so that the epilogue runs while the next
+// tile's first copies are in flight.  Copying straight into LDS (instead of
+// through registers and LDS stores) took the forward from 6.8 to 6.3-6.5 ms and
+// the dlogits and gradient products by 3-5% on MI355X at 8192 x 2560 x 151936,
+// with bit-identical results.
 template <class Epi>
 __device__ __forceinline__ void gemm_tiles(GemmSmem &sm, const unsigned short *XA, int64_t lda,
                                            int64_t rowsA, int64_t row0, const unsigned short *XB,
@@ -168,46 +199,40 @@ __device__ __forceinline__ void gemm_tiles(GemmSmem &sm, const unsigned short *X
         return;
     f32x16 acc[kTM][kTN];
     zero_acc(acc);
-    u32x4 ra[kChunks], rb[kChunks];
-    load_tile<false>(XA, lda, rowsA, row0, 0, ra, tid);
-    load_tile<true>(XB, ldb, rowsB, t_begin * kBN, 0, rb, tid);
-    store_tile(sm.a[0], ra, tid);
-    store_tile(sm.b[0], rb, tid);
+    dma_tile<false>(XA, lda, rowsA, row0, 0, sm.a[0], tid);
+    dma_tile<true>(XB, ldb, rowsB, t_begin * kBN, 0, sm.b[0], tid);
+    dma_wait();
     __syncthreads();
     int buf = 0;
     for (int64_t tile = t_begin; tile < t_end; ++tile) {
         const int64_t b0 = tile * kBN;
         for (int64_t kt = 1; kt < nk; ++kt) {
-            load_tile<false>(XA, lda, rowsA, row0, kt * kBK, ra, tid);
-            load_tile<true>(XB, ldb, rowsB, b0, kt * kBK, rb, tid);
-            mma_stage(sm.a[buf], sm.b[buf], acc, wm, wn, lane);
-            store_tile(sm.a[buf ^ 1], ra, tid);
-            store_tile(sm.b[buf ^ 1], rb, tid);
-            __builtin_amdgcn_iglp_opt(0);
+            mma_stage(sm.a[buf], sm.b[buf], acc, wm, wn, lane, [&] {
+                dma_tile<false>(XA, lda, rowsA, row0, kt * kBK, sm.a[buf ^ 1], tid);
+                dma_tile<true>(XB, ldb, rowsB, b0, kt * kBK, sm.b[buf ^ 1], tid);
+            });
+            dma_wait();
             __syncthreads();
             buf ^= 1;
         }
         const bool more = tile + 1 < t_end;
         if (more) {
-            load_tile<false>(XA, lda, rowsA, row0, 0, ra, tid);
-            load_tile<true>(XB, ldb, rowsB, b0 + kBN, 0, rb, tid);
+            dma_tile<false>(XA, lda, rowsA, row0, 0, sm.a[buf ^ 1], tid);
+            dma_tile<true>(XB, ldb, rowsB, b0 + kBN, 0, sm.b[buf ^ 1], tid);
         }
         mma_stage(sm.a[buf], sm.b[buf], acc, wm, wn, lane);
         epi(tile, acc);
         zero_acc(acc);
-        if (more) {
-            store_tile(sm.a[buf ^ 1], ra, tid);
-            store_tile(sm.b[buf ^ 1], rb, tid);
-        }
+        dma_wait();
         __syncthreads();
         buf ^= 1;
     }
 }
 
 // One output tile of a long contraction (the gradient products): the same
-// K step as gemm_tiles in one branch-free loop (the last step reloads its own
-// K range, unused), accumulators returned to the caller.  Measured on MI355X
-// for the dhidden shape: 12% faster than running it through gemm_tiles.
+// K step as gemm_tiles in one branch-free loop (the last step copies its own
+// K range again, unused), accumulators returned to the caller.  Measured on
+// MI355X for the dhidden shape: 12% faster than running it through gemm_tiles.
 __device__ __forceinline__ void gemm_one_tile(GemmSmem &sm, const unsigned short *XA,
                                               int64_t lda, int64_t rowsA, int64_t row0,
                                               const unsigned short *XB, int64_t ldb,
@@ -219,21 +244,18 @@ __device__ __forceinline__ void gemm_one_tile(GemmSmem &sm, const unsigned short
     zero_acc(acc);
     if (nk <= 0)
         return;
-    u32x4 ra[kChunks], rb[kChunks];
-    load_tile<false>(XA, lda, rowsA, row0, 0, ra, tid);
-    load_tile<true>(XB, ldb, rowsB, col0, 0, rb, tid);
-    store_tile(sm.a[0], ra, tid);
-    store_tile(sm.b[0], rb, tid);
+    dma_tile<false>(XA, lda, rowsA, row0, 0, sm.a[0], tid);
+    dma_tile<true>(XB, ldb, rowsB, col0, 0, sm.b[0], tid);
+    dma_wait();
     __syncthreads();
     int buf = 0;
     for (int64_t it = 0; it < nk; ++it) {
         const int64_t nx = it + 1 < nk ? it + 1 : it;
-        load_tile<false>(XA, lda, rowsA, row0, nx * kBK, ra, tid);
-        load_tile<true>(XB, ldb, rowsB, col0, nx * kBK, rb, tid);
-        mma_stage(sm.a[buf], sm.b[buf], acc, wm, wn, lane);
-        store_tile(sm.a[buf ^ 1], ra, tid);
-        store_tile(sm.b[buf ^ 1], rb, tid);
-        __builtin_amdgcn_iglp_opt(0);
+        mma_stage(sm.a[buf], sm.b[buf], acc, wm, wn, lane, [&] {
+            dma_tile<false>(XA, lda, rowsA, row0, nx * kBK, sm.a[buf ^ 1], tid);
+            dma_tile<true>(XB, ldb, rowsB, col0, nx * kBK, sm.b[buf ^ 1], tid);
+        });
+        dma_wait();
         __syncthreads();
         buf ^= 1;
     }
