@@ -6,13 +6,16 @@
 //
 //   forward   k_lce_fwd: each workgroup owns 256 rows and one vocab split; per
 //             256-column tile it runs the K loop over the hidden size, then
-//             folds the tile into target-excluded softmax statistics (the
-//             tile's maximum, first column of the maximum and sum at the
-//             maximum are reduced across the 32 lanes of each row, then merged
-//             into a running state that one lane per row keeps; entropy and
-//             value sums when asked).  At the end of its split each row gets
-//             one cev_vocab_partial record, and k_vocab_merge closes the rows
-//             exactly as for vocab-parallel logits.
+//             folds the tile into target-excluded softmax statistics: every
+//             lane forms its terms at the row's running maximum, and one
+//             reduce-scatter over the 32 lanes that hold a row slot hands
+//             each slot's sum to the lane that keeps that row's running
+//             state (entropy and value sums alike, when asked); the tile's
+//             maximum and its first column are reduced only for a slot where
+//             some value exceeds the running maximum.  At the end of its
+//             split each row gets one cev_vocab_partial record, and
+//             k_vocab_merge closes the rows exactly as for vocab-parallel
+//             logits.
 //   backward  k_lce_dl recomputes each logit tile and writes
 //             dlogits = (g/T)(softmax - onehot) in bf16 (the per-element
 //             formula of k_backward, from the saved record); k_lce_gemm then
@@ -125,6 +128,10 @@ __device__ __forceinline__ void frag_load(const unsigned short *la, const unsign
         bf[nb] = *reinterpret_cast<const bf16x8 *>(
             lb + lds_at(wn * 128 + nb * 32 + (lane & 31), kk));
 }
+
+template <bool B> struct Flag {
+    static constexpr bool value = B;
+};
 
 // One K step of 64 from LDS: 4 sub-steps of 16, 8 MFMAs each per wave, with
 // the fragments of sub-step ks + 1 read while the MFMAs of sub-step ks issue
@@ -311,6 +318,57 @@ __device__ __forceinline__ int row_min(int x)
     return row_reduce(x, [](int p, int q) { return min(p, q); });
 }
 
+// Reduce-scatter over the 32 lanes of each half-wave: x[k] holds this lane's
+// share of row slot k (k < 32); on return lane l holds op over the 32 lanes
+// of its half of slot l % 32.  Five exchange stages halve the slots a lane
+// carries: lane bit 4 by v_permlane16_swap, which hands the lane pair
+// (l, l + 16) of x[k] and x[k + 16] in one instruction (the lane in the
+// lower row keeps slot k, the upper one slot k + 16); lane bits 3, 2, 1, 0 by
+// DPP (row rotate by 8, half-row mirror, quad swaps), each lane sending the
+// half of its slots that its partner keeps.  31 combines in all, against 32
+// five-step broadcast reductions.
+template <int CTRL, class T> __device__ __forceinline__ T dpp_t(T x)
+{
+    unsigned u;
+    __builtin_memcpy(&u, &x, 4);
+    u = (unsigned)__builtin_amdgcn_update_dpp(0, (int)u, CTRL, 0xF, 0xF, false);
+    T r;
+    __builtin_memcpy(&r, &u, 4);
+    return r;
+}
+
+template <int CTRL, int N, class T, class Op>
+__device__ __forceinline__ void rs_stage(T (&x)[32], bool upper, Op op)
+{
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        const T send = upper ? x[j] : x[j + N];
+        const T keep = upper ? x[j + N] : x[j];
+        x[j] = op(keep, dpp_t<CTRL>(send));
+    }
+}
+
+template <class T, class Op> __device__ __forceinline__ T reduce_scatter32(T (&x)[32], int lane, Op op)
+{
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        unsigned a, b;
+        __builtin_memcpy(&a, &x[k], 4);
+        __builtin_memcpy(&b, &x[k + 16], 4);
+        const auto sw = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+        T p, q;
+        const unsigned u0 = sw[0], u1 = sw[1];
+        __builtin_memcpy(&p, &u0, 4);
+        __builtin_memcpy(&q, &u1, 4);
+        x[k] = op(p, q);
+    }
+    rs_stage<0x128, 8>(x, (lane & 8) != 0, op);    // row_ror:8, partner l ^ 8
+    rs_stage<kHalfMirror, 4>(x, (lane & 4) != 0, op);
+    rs_stage<kQuadSwap2, 2>(x, (lane & 2) != 0, op);
+    rs_stage<kQuadSwap1, 1>(x, (lane & 1) != 0, op);
+    return x[0];
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b on XCD
 // b % 8), each with its own L2.  The forward and dlogits grids are renumbered
 // so that the workgroups one XCD runs together form a contiguous run of
@@ -380,45 +438,80 @@ __global__ __launch_bounds__(kLT) void k_lce_fwd(LceArgs a)
     __syncthreads();
 
     const float c = a.c, inv_t = a.inv_t;
-    // Lane j of each half-wave keeps the state of the half's row j (rows
-    // numbered mb * 16 + v).
+    // Row slot k = mb * 16 + v of a lane is accumulator row v of block mb: in
+    // half h of the wave it is row acc_row(wm, mb, v, lane), and lane
+    // h * 32 + k keeps that row's running state.  Every lane of the half also
+    // needs each slot's running maximum, which the owners publish in s_mr
+    // after each tile.
     RowState st = RowState{-INFINITY, 0.0f, 0.0f, 0.0f, INT32_MAX};
+    __shared__ __align__(16) float s_mr[kLT / kWave][kWave];
+    s_mr[w][lane] = -INFINITY;
+    // the label of row wm * 64 + lane: which tiles hold a target for this wave
+    const int mylab = s_lab[wm * 64 + lane];
 
-    auto epi = [&](int64_t tile, f32x16 (&acc)[kTM][kTN]) {
+    // One tile: MASK (wave-uniform, rare) when some of this wave's columns
+    // lie past V or hold the target of one of its rows; those columns count
+    // as -inf, and the lane holding a target records z_t.
+    auto tile_body = [&](int64_t tile, f32x16(&acc)[kTM][kTN], auto mask) {
+        constexpr bool MASK = decltype(mask)::value;
         const int el = opaque_lane();
         const int64_t c0 = lane_col(tile, wn, el);
+        // Each slot's terms at the running maximum; where some lane of the
+        // wave sees a larger value (wave-uniform branch, about ln(tiles) times
+        // per row), at the tile's maximum instead, whose value and first
+        // column the slot's owner picks up.
+        const int half = el >> 5;
+        float mr[32];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const float4 m4 = *reinterpret_cast<const float4 *>(&s_mr[w][half * 32 + 4 * q]);
+            mr[4 * q] = m4.x;
+            mr[4 * q + 1] = m4.y;
+            mr[4 * q + 2] = m4.z;
+            mr[4 * q + 3] = m4.w;
+        }
+        float ts[32], th[32], tz[32];
+        float own_tm = -INFINITY;
+        int own_arg = INT32_MAX;
 #pragma unroll
         for (int mb = 0; mb < kTM; ++mb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int ri = mb * 16 + v;
-                const int rl = acc_row(wm, mb, v, el);
-                const int64_t d = (int64_t)s_lab[rl] - c0;   // the target among this lane's four?
-                const int tn = d >= 0 && d < kTN ? (int)d : -1;
-                float x[kTN], zt = 0.0f;
-                float lmax = -INFINITY;
-                int larg = INT32_MAX;
+                const int k = mb * 16 + v;
+                float x[kTN];
 #pragma unroll
-                for (int nb = 0; nb < kTN; ++nb) {
-                    float z = acc[mb][nb][v];
-                    if (nb == tn) {
-                        zt = z;
-                        z = -INFINITY;
-                    }
-                    if (c0 + nb >= V)
-                        z = -INFINITY;
-                    x[nb] = z;
-                    if (z > lmax) {
-                        lmax = z;
-                        larg = (int)(c0 + nb);
+                for (int nb = 0; nb < kTN; ++nb)
+                    x[nb] = acc[mb][nb][v];
+                if constexpr (MASK) {
+                    const int rl = acc_row(wm, mb, v, el);
+                    const int64_t d = (int64_t)s_lab[rl] - c0;
+#pragma unroll
+                    for (int nb = 0; nb < kTN; ++nb) {
+                        if (d == nb) {
+                            s_zt[rl] = x[nb];
+                            s_own[rl] = 1;
+                        }
+                        if (d == nb || c0 + nb >= V)
+                            x[nb] = -INFINITY;
                     }
                 }
-                if (tn >= 0) {
-                    s_zt[rl] = zt;
-                    s_own[rl] = 1;
+                const float lm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+                float b = mr[k];
+                if (__any(lm > b)) {
+                    const float tm = row_max(lm);
+                    int cand = INT32_MAX;
+#pragma unroll
+                    for (int nb = kTN - 1; nb >= 0; --nb)
+                        if (x[nb] == tm)
+                            cand = (int)(c0 + nb);
+                    const int targ = row_min(tm != -INFINITY ? cand : INT32_MAX);
+                    if ((el & 31) == k) {
+                        own_tm = tm;
+                        own_arg = targ;
+                    }
+                    b = fmaxf(b, tm);
                 }
-                const float tmax = row_max(lmax);
-                const float base = fmaxf(tmax, -FLT_MAX);
+                const float base = fmaxf(b, -FLT_MAX);
                 float ls = 0.0f, lh = 0.0f, lz = 0.0f;
 #pragma unroll
                 for (int nb = 0; nb < kTN; ++nb) {
@@ -429,32 +522,44 @@ __global__ __launch_bounds__(kLT) void k_lce_fwd(LceArgs a)
                     if constexpr (WANT_Z)
                         lz += x[nb] == -INFINITY ? 0.0f : x[nb];
                 }
-                const float tsum = row_sum(ls);
-                const int targ = row_min(lmax == tmax && tmax != -INFINITY ? larg : INT32_MAX);
-                float th = 0.0f, tz = 0.0f;
-                if constexpr (WANT_H)
-                    th = row_sum(lh);
-                if constexpr (WANT_Z)
-                    tz = row_sum(lz);
-                if ((lane & 31) == ri) {
-                    // merge the tile (tmax, tsum and th at base) into the row's state
-                    RowState &r = st;
-                    const float M = fmaxf(r.m, tmax);
-                    const float bo = fmaxf(r.m, -FLT_MAX), bn = fmaxf(M, -FLT_MAX);
-                    const float fo = exp2_hw((bo - bn) * c), ft = exp2_hw((base - bn) * c);
-                    if constexpr (WANT_H)
-                        r.h = fo * fmaf(fminf((bn - bo) * inv_t, kBigL), r.s, r.h) +
-                              ft * fmaf(fminf((bn - base) * inv_t, kBigL), tsum, th);
-                    r.s = r.s * fo + tsum * ft;
-                    if (tmax > r.m)
-                        r.arg = targ;
-                    else if (tmax == r.m && tmax != -INFINITY)
-                        r.arg = min(r.arg, targ);
-                    r.m = M;
-                    if constexpr (WANT_Z)
-                        r.zs += tz;
-                }
+                ts[k] = ls;
+                th[k] = lh;
+                tz[k] = lz;
             }
+        const auto add = [](float p, float q) { return p + q; };
+        const float tsum = reduce_scatter32(ts, el, add);
+        float hsum = 0.0f, zsum = 0.0f;
+        if constexpr (WANT_H)
+            hsum = reduce_scatter32(th, el, add);
+        if constexpr (WANT_Z)
+            zsum = reduce_scatter32(tz, el, add);
+        // merge into the owner's state: the tile's terms are at base
+        // max(running max, tile max)
+        if (own_tm > st.m) {
+            const float bo = fmaxf(st.m, -FLT_MAX), bn = fmaxf(own_tm, -FLT_MAX);
+            const float fo = exp2_hw((bo - bn) * c);
+            if constexpr (WANT_H)
+                st.h = fo * fmaf(fminf((bn - bo) * inv_t, kBigL), st.s, st.h) + hsum;
+            st.s = st.s * fo + tsum;
+            st.m = own_tm;
+            st.arg = own_arg;
+        } else {
+            st.s += tsum;
+            if constexpr (WANT_H)
+                st.h += hsum;
+        }
+        if constexpr (WANT_Z)
+            st.zs += zsum;
+        s_mr[w][el] = st.m;
+    };
+    auto epi = [&](int64_t tile, f32x16(&acc)[kTM][kTN]) {
+        const int64_t cw = tile * kBN + wn * 128;   // this wave's first column
+        const bool tail = cw + 128 > V;
+        const bool hit = __any(mylab >= cw && mylab < cw + 128);
+        if (tail || hit)
+            tile_body(tile, acc, Flag<true>{});
+        else
+            tile_body(tile, acc, Flag<false>{});
     };
     gemm_tiles(sm, a.hidden, a.ldh, a.rows, row0, a.weight, a.ldw, V, a.hidden_dim / kBK, t0, t1,
                epi);
