@@ -667,9 +667,15 @@ __global__ __launch_bounds__(kLT) void k_lce_dl(LceArgs a)
     const float c = a.c;
     unsigned short *dl = a.dlogits;
 
+    // the label of row wm * 64 + lane: which tiles hold a target for this wave
+    const int mylab = s_ls[wm * 64 + lane].x;
+
     // Each lane writes its four adjacent columns of a row as one 8-byte store
     // (ldd is a multiple of 64, so a group of four is wholly inside or past it).
-    auto epi = [&](int64_t tile, f32x16 (&acc)[kTM][kTN]) {
+    // MASK (wave-uniform, rare): some of this wave's columns lie past V or
+    // hold the target of one of its rows.
+    auto tile_body = [&](int64_t tile, f32x16(&acc)[kTM][kTN], auto mask) {
+        constexpr bool MASK = decltype(mask)::value;
         const int el = opaque_lane();
         const int64_t c0 = lane_col(tile, wn, el);
         if (c0 >= ldd)
@@ -683,23 +689,34 @@ __global__ __launch_bounds__(kLT) void k_lce_dl(LceArgs a)
                 if (r >= a.rows)
                     continue;
                 const DlRow rc = s_rc[rl];
-                const int2 ls = s_ls[rl];
+                const unsigned sgn = (unsigned)s_ls[rl].y;
                 float o[kTN];
 #pragma unroll
                 for (int nb = 0; nb < kTN; ++nb) {
-                    const int64_t col = c0 + nb;
                     float e = exp2_hw(fmaf(acc[mb][nb][v] - rc.mz, c, -rc.kexp)) - rc.ev;
-                    if (col == ls.x)
-                        e = rc.tv;
-                    if (col >= V)
-                        e = 0.0f;
-                    o[nb] = __uint_as_float(__float_as_uint(e) ^ (unsigned)ls.y);
+                    if constexpr (MASK) {
+                        const int64_t col = c0 + nb;
+                        if (col == s_ls[rl].x)
+                            e = rc.tv;
+                        if (col >= V)
+                            e = 0.0f;
+                    }
+                    o[nb] = __uint_as_float(__float_as_uint(e) ^ sgn);
                 }
                 uint2 pk;
                 pk.x = pack_bf16x2(o[0], o[1]);
                 pk.y = pack_bf16x2(o[2], o[3]);
                 *reinterpret_cast<uint2 *>(dl + r * ldd + c0) = pk;
             }
+    };
+    auto epi = [&](int64_t tile, f32x16(&acc)[kTM][kTN]) {
+        const int64_t cw = tile * kBN + wn * 128;   // this wave's first column
+        const bool tail = cw + 128 > V;
+        const bool hit = __any(mylab >= cw && mylab < cw + 128);
+        if (tail || hit)
+            tile_body(tile, acc, Flag<true>{});
+        else
+            tile_body(tile, acc, Flag<false>{});
     };
     gemm_tiles(sm, a.hidden, a.ldh, a.rows, row0, a.weight, a.ldw, V, a.hidden_dim / kBK, t0, t1,
                epi);
