@@ -116,17 +116,165 @@ __device__ __forceinline__ void dma_wait()
 // (lane % 32), B rows wn*128 + 32 nb + (lane % 32), k = 16 ks + 8 (lane / 32).
 __device__ __forceinline__ void frag_load(const unsigned short *la, const unsigned short *lb,
                                           bf16x8 (&af)[kTM], bf16x8 (&bf)[kTN], int ks, int wm,
-                                          int wn, int lane)
+                                          int wn, int lane, bool with_b = true)
 {
     const int kk = ks * 16 + (lane >> 5) * 8;
 #pragma unroll
     for (int mb = 0; mb < kTM; ++mb)
         af[mb] = *reinterpret_cast<const bf16x8 *>(
             la + lds_at(wm * 64 + mb * 32 + (lane & 31), kk));
+    if (!with_b)
+        return;
 #pragma unroll
     for (int nb = 0; nb < kTN; ++nb)
         bf[nb] = *reinterpret_cast<const bf16x8 *>(
             lb + lds_at(wn * 128 + nb * 32 + (lane & 31), kk));
+}
+
+// The same copies with a uniform base: a lane's byte offset from a tile's
+// origin does not depend on the K step (nor, up to a uniform row offset, on the
+// chunk i), so each copy takes the origin in SGPRs and the lane's offset as a
+// 32-bit VGPR (global_load_lds_dwordx4 v, s[..]); the K loops then keep one
+// VGPR per operand instead of eight 64-bit addresses.  Used when the tile lies
+// inside the matrix and the offsets fit 32 bits (leading dimension < 2^24).
+// The asm waits 5 states before the copy in case the base was just moved into
+// SGPRs by a vector instruction.
+__device__ __forceinline__ unsigned lds_u32(const unsigned short *lds)
+{
+    return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) unsigned short *)lds;
+}
+
+__device__ __forceinline__ void dma_copy_s(const unsigned short *base, unsigned voff, unsigned m0)
+{
+    // (readfirstlane returns int: each half goes through unsigned, so that the
+    // low half is not sign-extended into the high one)
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(b >> 32));
+    const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b);
+    const uint64_t sb = (hi << 32) | lo;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(m0), "v"(voff), "s"(sb) : "memory");
+}
+
+constexpr int64_t kFastLd = 1 << 24;
+
+// Uniform row offset of chunk i of a K-contiguous tile (row q = 64 i + x of
+// the tile, x the lane's row within a chunk; for a B tile, perm_b(q) =
+// 128 (i / 2) + 2 (i % 2) + 4 (x % 32) + x / 32).
+template <bool PERM> __device__ __forceinline__ int chunk_row(int i)
+{
+    return PERM ? 128 * (i >> 1) + 2 * (i & 1) : 64 * i;
+}
+
+// The lane's byte offset within a K-contiguous tile (see dma_tile).
+template <bool PERM> __device__ __forceinline__ unsigned dma_voff(int64_t ld, int tid)
+{
+    const int lane = tid & 63, w = tid >> 6;
+    const int x = 8 * w + (lane >> 3);
+    const int lc = (lane & 7) ^ ((lane >> 3) & 7);
+    const int row = PERM ? 4 * (x & 31) + (x >> 5) : x;
+    return (unsigned)(((int64_t)row * ld + lc * 8) * 2);
+}
+
+template <bool PERM>
+__device__ __forceinline__ void dma_tile_s(const unsigned short *X, int64_t ld, int64_t r0,
+                                           int64_t k0, unsigned voff, unsigned short *lds,
+                                           int tid)
+{
+    const unsigned base = lds_u32(lds) + (unsigned)(tid >> 6) * 1024u;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i)
+        dma_copy_s(X + (r0 + chunk_row<PERM>(i)) * ld + k0, voff,
+                   __builtin_amdgcn_readfirstlane(base + (unsigned)i * (kLT * 16)));
+}
+
+// B tiles of an N-contiguous operand X[k * ld + n] (the head as stored, for
+// dhidden = dlogits x head) are staged as they lie: 64 K rows of 256 columns,
+// 512 bytes each, and the MFMA fragments are formed by gfx950's transposing
+// LDS reads.  Chunk c (16 bytes) of row k is stored at position c ^ 4 kn_swz(k):
+// one transposing read touches rows {r, r+1, r+2, r+3, r+8, .., r+11} (r a
+// multiple of 4) at four adjacent chunks, which the swizzle spreads over eight
+// distinct groups of four chunks.
+__device__ __forceinline__ int kn_swz(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
+
+// Rows [k0, k0 + 64) x columns [n0, n0 + 256) of X into the LDS tile, by
+// LDS-DMA as in dma_tile: position p holds row p / 32, chunk (p % 32) ^
+// 4 kn_swz(row).  Rows past kr re-read row kr - 1 and columns past nc the
+// last chunk of the row (the matching A columns are zero, or the output
+// columns are never stored).
+__device__ __forceinline__ void dma_tile_kn(const unsigned short *X, int64_t ld, int64_t kr,
+                                            int64_t nc, int64_t k0, int64_t n0,
+                                            unsigned short *lds, int tid)
+{
+    const int lane = tid & 63, w = tid >> 6;
+    const unsigned base =
+        (unsigned)(uintptr_t)(const __attribute__((address_space(3))) unsigned short *)lds;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+        const int p = kLT * i + 64 * w + lane;
+        const int k = p >> 5;
+        const int lc = (p & 31) ^ (4 * kn_swz(k));
+        const int64_t gk = k0 + k < kr ? k0 + k : kr - 1;
+        const int64_t gn = n0 + lc * 8 < nc ? n0 + lc * 8 : nc - 8;
+        const unsigned short *src = X + gk * ld + gn;
+        const unsigned m0 =
+            __builtin_amdgcn_readfirstlane(base + (unsigned)(kLT * i + 64 * w) * 16u);
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :: "s"(m0), "v"(src) : "memory");
+    }
+}
+
+// The lane's byte offset within an N-contiguous tile: row 2 w + lane / 32 of
+// each 16-row chunk, chunk (lane % 32) ^ 4 kn_swz(row) (the same for every
+// chunk i), whose columns past nc re-read the row's last chunk.
+__device__ __forceinline__ unsigned dma_voff_kn(int64_t ld, int64_t n0, int64_t nc, int tid)
+{
+    const int lane = tid & 63, w = tid >> 6;
+    const int k = 2 * w + (lane >> 5);
+    const int lc = (lane & 31) ^ (4 * kn_swz(k));
+    const int64_t gn = n0 + lc * 8 < nc ? lc * 8 : nc - 8 - n0;
+    return (unsigned)(((int64_t)k * ld + gn) * 2);
+}
+
+__device__ __forceinline__ void dma_tile_kn_s(const unsigned short *X, int64_t ld, int64_t k0,
+                                              int64_t n0, unsigned voff, unsigned short *lds,
+                                              int tid)
+{
+    const unsigned base = lds_u32(lds) + (unsigned)(tid >> 6) * 1024u;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i)
+        dma_copy_s(X + (k0 + 16 * i) * ld + n0, voff,
+                   __builtin_amdgcn_readfirstlane(base + (unsigned)i * (kLT * 16)));
+}
+
+// B fragments of K sub-step ks from an N-contiguous tile.  ds_read_b64_tr_b16
+// works on groups of 16 lanes: lane i of a group reads 4 consecutive values,
+// and lane j receives value j % 4 of the reads of lanes j / 4, j / 4 + 4,
+// j / 4 + 8, j / 4 + 12 (checked on the device).  Lane i reads row
+// k + i / 4 at columns 4 (i % 4) .. +3, so lane j gets column j of rows
+// k .. k + 3: two reads give the 8 K values of one column that the
+// 32x32x16 MFMA takes from a lane (column l % 32, K 8 (l / 32) .. +8).
+__device__ __forceinline__ void frag_load_b_kn(const unsigned short *lb, bf16x8 (&bf)[kTN], int ks,
+                                               int wn, int lane)
+{
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int nb = 0; nb < kTN; ++nb) {
+        const int col = wn * 128 + nb * 32 + 16 * (g & 1) + 4 * (i & 3);
+        v4s h[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int k = ks * 16 + 8 * (g >> 1) + 4 * t + (i >> 2);
+            const int e = k * kBN + ((((col >> 3) ^ (4 * kn_swz(k))) & 31) << 3) + (col & 7);
+            h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4s *)(const_cast<unsigned short *>(lb) + e));
+        }
+        const short v8 __attribute__((ext_vector_type(8))) = {h[0][0], h[0][1], h[0][2], h[0][3],
+                                                              h[1][0], h[1][1], h[1][2], h[1][3]};
+        __builtin_memcpy(&bf[nb], &v8, 16);
+    }
 }
 
 template <bool B> struct Flag {
@@ -141,18 +289,27 @@ struct NoIssue {
     __device__ void operator()() const {}
 };
 
-template <class F = NoIssue>
+template <bool BKN = false, class F = NoIssue>
 __device__ __forceinline__ void mma_stage(const unsigned short *la, const unsigned short *lb,
                                           f32x16 (&acc)[kTM][kTN], int wm, int wn, int lane,
                                           F &&issue = NoIssue{})
 {
     bf16x8 af[2][kTM], bf[2][kTN];
-    frag_load(la, lb, af[0], bf[0], 0, wm, wn, lane);
+    auto frags = [&](int ks, bf16x8 (&a)[kTM], bf16x8 (&b)[kTN]) {
+        if constexpr (BKN) {
+            bf16x8 unused[kTN];
+            frag_load(la, lb, a, unused, ks, wm, wn, lane, false);
+            frag_load_b_kn(lb, b, ks, wn, lane);
+        } else {
+            frag_load(la, lb, a, b, ks, wm, wn, lane);
+        }
+    };
+    frags(0, af[0], bf[0]);
     issue();
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
         if (ks + 1 < kBK / 16)
-            frag_load(la, lb, af[(ks + 1) & 1], bf[(ks + 1) & 1], ks + 1, wm, wn, lane);
+            frags(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
 #pragma unroll
         for (int mb = 0; mb < kTM; ++mb)
 #pragma unroll
@@ -206,27 +363,34 @@ __device__ __forceinline__ void gemm_tiles(GemmSmem &sm, const unsigned short *X
         return;
     f32x16 acc[kTM][kTN];
     zero_acc(acc);
-    dma_tile<false>(XA, lda, rowsA, row0, 0, sm.a[0], tid);
-    dma_tile<true>(XB, ldb, rowsB, t_begin * kBN, 0, sm.b[0], tid);
+    const bool fast_a = row0 + kBM <= rowsA && lda < kFastLd, ld_b = ldb < kFastLd;
+    const unsigned voff_a = dma_voff<false>(lda, tid), voff_b = dma_voff<true>(ldb, tid);
+    auto copy = [&](int64_t b0, int64_t k0, int to) {
+        if (fast_a)
+            dma_tile_s<false>(XA, lda, row0, k0, voff_a, sm.a[to], tid);
+        else
+            dma_tile<false>(XA, lda, rowsA, row0, k0, sm.a[to], tid);
+        if (ld_b && b0 + kBN <= rowsB)
+            dma_tile_s<true>(XB, ldb, b0, k0, voff_b, sm.b[to], tid);
+        else
+            dma_tile<true>(XB, ldb, rowsB, b0, k0, sm.b[to], tid);
+    };
+    copy(t_begin * kBN, 0, 0);
     dma_wait();
     __syncthreads();
     int buf = 0;
     for (int64_t tile = t_begin; tile < t_end; ++tile) {
         const int64_t b0 = tile * kBN;
         for (int64_t kt = 1; kt < nk; ++kt) {
-            mma_stage(sm.a[buf], sm.b[buf], acc, wm, wn, lane, [&] {
-                dma_tile<false>(XA, lda, rowsA, row0, kt * kBK, sm.a[buf ^ 1], tid);
-                dma_tile<true>(XB, ldb, rowsB, b0, kt * kBK, sm.b[buf ^ 1], tid);
-            });
+            mma_stage(sm.a[buf], sm.b[buf], acc, wm, wn, lane,
+                      [&] { copy(b0, kt * kBK, buf ^ 1); });
             dma_wait();
             __syncthreads();
             buf ^= 1;
         }
         const bool more = tile + 1 < t_end;
-        if (more) {
-            dma_tile<false>(XA, lda, rowsA, row0, 0, sm.a[buf ^ 1], tid);
-            dma_tile<true>(XB, ldb, rowsB, b0 + kBN, 0, sm.b[buf ^ 1], tid);
-        }
+        if (more)
+            copy(b0 + kBN, 0, buf ^ 1);
         mma_stage(sm.a[buf], sm.b[buf], acc, wm, wn, lane);
         epi(tile, acc);
         zero_acc(acc);
@@ -240,28 +404,49 @@ __device__ __forceinline__ void gemm_tiles(GemmSmem &sm, const unsigned short *X
 // K step as gemm_tiles in one branch-free loop (the last step copies its own
 // K range again, unused), accumulators returned to the caller.  Measured on
 // MI355X for the dhidden shape: 12% faster than running it through gemm_tiles.
+// B is K-contiguous (rowsB rows, staged permuted) or, with BKN, N-contiguous:
+// rowsB K rows of at least ncols columns, output columns col0 + 0..255.
+template <bool BKN = false>
 __device__ __forceinline__ void gemm_one_tile(GemmSmem &sm, const unsigned short *XA,
                                               int64_t lda, int64_t rowsA, int64_t row0,
                                               const unsigned short *XB, int64_t ldb,
                                               int64_t rowsB, int64_t col0, int64_t nk,
-                                              f32x16 (&acc)[kTM][kTN])
+                                              f32x16 (&acc)[kTM][kTN], int64_t ncols = 0)
 {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 1, wn = w & 1;
     zero_acc(acc);
     if (nk <= 0)
         return;
-    dma_tile<false>(XA, lda, rowsA, row0, 0, sm.a[0], tid);
-    dma_tile<true>(XB, ldb, rowsB, col0, 0, sm.b[0], tid);
+    const bool fast_a = row0 + kBM <= rowsA && lda < kFastLd;
+    const bool fast_b = BKN ? ldb < kFastLd : (col0 + kBN <= rowsB && ldb < kFastLd);
+    const unsigned voff_a = dma_voff<false>(lda, tid);
+    const unsigned voff_b = BKN ? dma_voff_kn(ldb, col0, ncols, tid) : dma_voff<true>(ldb, tid);
+    auto copy = [&](int64_t kstep, int to) {
+        const int64_t k0 = kstep * kBK;
+        if (fast_a)
+            dma_tile_s<false>(XA, lda, row0, k0, voff_a, sm.a[to], tid);
+        else
+            dma_tile<false>(XA, lda, rowsA, row0, k0, sm.a[to], tid);
+        if constexpr (BKN) {
+            if (fast_b && k0 + kBK <= rowsB)
+                dma_tile_kn_s(XB, ldb, k0, col0, voff_b, sm.b[to], tid);
+            else
+                dma_tile_kn(XB, ldb, rowsB, ncols, k0, col0, sm.b[to], tid);
+        } else {
+            if (fast_b)
+                dma_tile_s<true>(XB, ldb, col0, k0, voff_b, sm.b[to], tid);
+            else
+                dma_tile<true>(XB, ldb, rowsB, col0, k0, sm.b[to], tid);
+        }
+    };
+    copy(0, 0);
     dma_wait();
     __syncthreads();
     int buf = 0;
     for (int64_t it = 0; it < nk; ++it) {
         const int64_t nx = it + 1 < nk ? it + 1 : it;
-        mma_stage(sm.a[buf], sm.b[buf], acc, wm, wn, lane, [&] {
-            dma_tile<false>(XA, lda, rowsA, row0, nx * kBK, sm.a[buf ^ 1], tid);
-            dma_tile<true>(XB, ldb, rowsB, col0, nx * kBK, sm.b[buf ^ 1], tid);
-        });
+        mma_stage<BKN>(sm.a[buf], sm.b[buf], acc, wm, wn, lane, [&] { copy(nx, buf ^ 1); });
         dma_wait();
         __syncthreads();
         buf ^= 1;
@@ -727,12 +912,15 @@ __global__ __launch_bounds__(kLT) void k_lce_dl(LceArgs a)
 // fastest).  Split along K: workgroup split s covers K steps
 // [nk s / splits, nk (s + 1) / splits) of 64 and writes its partial product to
 // C + s * cstride (reduced afterwards in split order).  vec4: C and ldc allow
-// 16-byte stores.
+// 16-byte stores.  BKN: B is N-contiguous instead (B[k * ldb + n], kr rows),
+// and each lane holds one column of each 32-column block (4-byte stores,
+// 32 adjacent columns per half-wave).
+template <bool BKN>
 __global__ __launch_bounds__(kLT) void k_lce_gemm(const unsigned short *XA, int64_t lda,
                                                  int64_t M, const unsigned short *XB,
                                                  int64_t ldb, int64_t N, int64_t nk,
                                                  int64_t splits, float *C, int64_t ldc,
-                                                 int64_t cstride, int vec4)
+                                                 int64_t cstride, int vec4, int64_t kr)
 {
     __shared__ GemmSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -744,6 +932,25 @@ __global__ __launch_bounds__(kLT) void k_lce_gemm(const unsigned short *XA, int6
     const int64_t k0 = nk * sp / splits, k1 = nk * (sp + 1) / splits;
     float *Cs = C + sp * cstride;
     f32x16 acc[kTM][kTN];
+    if constexpr (BKN) {
+        gemm_one_tile<true>(sm, XA + k0 * kBK, lda, M, row0, XB + k0 * kBK * ldb, ldb,
+                            kr - k0 * kBK, nt * kBN, k1 - k0, acc, N);
+        const int64_t cb = nt * kBN + wn * 128 + (lane & 31);
+#pragma unroll
+        for (int mb = 0; mb < kTM; ++mb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t r = row0 + acc_row(wm, mb, v, lane);
+                if (r >= M)
+                    continue;
+                float *dst = Cs + r * ldc;
+#pragma unroll
+                for (int nb = 0; nb < kTN; ++nb)
+                    if (cb + 32 * nb < N)
+                        dst[cb + 32 * nb] = acc[mb][nb][v];
+            }
+        return;
+    }
     gemm_one_tile(sm, XA + k0 * kBK, lda, M, row0, XB + k0 * kBK, ldb, N, nt * kBN, k1 - k0,
                   acc);
     const int64_t c0 = lane_col(nt, wn, lane);
@@ -923,25 +1130,26 @@ hipError_t launch_lce_backward(const LceArgs &a, void *workspace, float *dhidden
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    // dhidden[R, H] = dlogits[R, V] x head[V, H]: the head transposed to
-    // [H, vp] (zero columns past V) so both operands run along the vocab.
-    // Few output tiles and a long contraction: split along K so the grid fills
-    // the chip; the partials live where dlogits^T and hidden^T go later.
-    launch_transpose(a.weight, a.ldw, V, H, wt, vp, s);
+    // dhidden[R, H] = dlogits[R, V] x head[V, H]: dlogits runs along the
+    // vocab, the head is read as stored (its K rows past V re-read row V - 1
+    // against zero dlogits columns).  Few output tiles and a long contraction:
+    // split along K so the grid fills the chip; the partials live where
+    // dlogits^T and hidden^T go later.
+    (void)wt;
     const int64_t tiles = nrb * ((H + kBN - 1) / kBN);
     const size_t room = align256((size_t)V * rp * 2) + align256((size_t)H * rp * 2);
     const int64_t S = gemm_splits(tiles, vp / kBK, room / ((size_t)R * H * 4));
     if (S > 1) {
         float *part = reinterpret_cast<float *>(dlt);
-        hipLaunchKernelGGL(k_lce_gemm, dim3((unsigned)(tiles * S)), dim3(kLT), 0, s, dl, vp, R, wt,
-                           vp, H, vp / kBK, S, part, H, R * H, 1);
+        hipLaunchKernelGGL(k_lce_gemm<true>, dim3((unsigned)(tiles * S)), dim3(kLT), 0, s, dl, vp,
+                           R, a.weight, a.ldw, H, vp / kBK, S, part, H, R * H, 0, V);
         const int64_t n = R * (H / 4);
         hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                            part, S, R, H, dhidden, ldo);
     } else {
-        hipLaunchKernelGGL(k_lce_gemm, dim3((unsigned)tiles), dim3(kLT), 0, s, dl, vp, R, wt, vp,
-                           H, vp / kBK, (int64_t)1, dhidden, ldo, (int64_t)0,
-                           vec4_ok(dhidden, ldo));
+        hipLaunchKernelGGL(k_lce_gemm<true>, dim3((unsigned)tiles), dim3(kLT), 0, s, dl, vp, R,
+                           a.weight, a.ldw, H, vp / kBK, (int64_t)1, dhidden, ldo, (int64_t)0, 0,
+                           V);
     }
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
@@ -950,9 +1158,9 @@ hipError_t launch_lce_backward(const LceArgs &a, void *workspace, float *dhidden
         launch_transpose(dl, vp, R, V, dlt, rp, s);
         launch_transpose(a.hidden, a.ldh, R, H, ht, rp, s);
         const int64_t wtiles = ((V + kBM - 1) / kBM) * ((H + kBN - 1) / kBN);
-        hipLaunchKernelGGL(k_lce_gemm, dim3((unsigned)wtiles), dim3(kLT), 0, s, dlt, rp, V, ht,
-                           rp, H, rp / kBK, (int64_t)1, dweight, ldw_out, (int64_t)0,
-                           vec4_ok(dweight, ldw_out));
+        hipLaunchKernelGGL(k_lce_gemm<false>, dim3((unsigned)wtiles), dim3(kLT), 0, s, dlt, rp, V,
+                           ht, rp, H, rp / kBK, (int64_t)1, dweight, ldw_out, (int64_t)0,
+                           vec4_ok(dweight, ldw_out), (int64_t)0);
         e = hipGetLastError();
     }
     return e;
