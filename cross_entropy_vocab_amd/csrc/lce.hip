@@ -19,9 +19,10 @@
 //   backward  k_lce_dl recomputes each logit tile and writes
 //             dlogits = (g/T)(softmax - onehot) in bf16 (the per-element
 //             formula of k_backward, from the saved record); k_lce_gemm then
-//             forms dhidden = dlogits x head (and, for a trainable head,
-//             dhead = dlogits^T x hidden) from transposed copies, so that every
-//             product runs with both operands contiguous along the contraction.
+//             forms dhidden = dlogits x head with the head read as stored (its
+//             MFMA fragments formed by transposing LDS reads) and, for a
+//             trainable head, dhead = dlogits^T x hidden from transposed
+//             copies of both.
 //
 // Tiles: 8 waves in a 4 x 2 grid (two per SIMD), each wave 64 x 128 of C as
 // 2 x 4 blocks of 32 x 32; K steps of 64, copied from global memory straight
@@ -1099,13 +1100,14 @@ hipError_t launch_lce_forward(const LceArgs &a, bool want_h, bool want_z, hipStr
     return hipGetLastError();
 }
 
-// Backward workspace: dlogits [R, round64(V)], head^T [H, round64(V)], and
-// for the head gradient dlogits^T [V, round64(R)] and hidden^T [H, round64(R)].
+// Backward workspace: dlogits [R, round64(V)], and for the head gradient
+// dlogits^T [V, round64(R)] and hidden^T [H, round64(R)] (the dhidden split-K
+// partials use that second region first).
 size_t lce_backward_workspace(int64_t rows, int64_t hidden_dim, int64_t vocab)
 {
     const size_t vp = (size_t)round64(vocab), rp = (size_t)round64(rows);
-    return align256((size_t)rows * vp * 2) + align256((size_t)hidden_dim * vp * 2) +
-           align256((size_t)vocab * rp * 2) + align256((size_t)hidden_dim * rp * 2);
+    return align256((size_t)rows * vp * 2) + align256((size_t)vocab * rp * 2) +
+           align256((size_t)hidden_dim * rp * 2);
 }
 
 hipError_t launch_lce_backward(const LceArgs &a, void *workspace, float *dhidden, int64_t ldo,
@@ -1116,8 +1118,6 @@ hipError_t launch_lce_backward(const LceArgs &a, void *workspace, float *dhidden
     char *ws = static_cast<char *>(workspace);
     unsigned short *dl = reinterpret_cast<unsigned short *>(ws);
     ws += align256((size_t)R * vp * 2);
-    unsigned short *wt = reinterpret_cast<unsigned short *>(ws);
-    ws += align256((size_t)H * vp * 2);
     unsigned short *dlt = reinterpret_cast<unsigned short *>(ws);
     ws += align256((size_t)V * rp * 2);
     unsigned short *ht = reinterpret_cast<unsigned short *>(ws);
@@ -1135,7 +1135,6 @@ hipError_t launch_lce_backward(const LceArgs &a, void *workspace, float *dhidden
     // against zero dlogits columns).  Few output tiles and a long contraction:
     // split along K so the grid fills the chip; the partials live where
     // dlogits^T and hidden^T go later.
-    (void)wt;
     const int64_t tiles = nrb * ((H + kBN - 1) / kBN);
     const size_t room = align256((size_t)V * rp * 2) + align256((size_t)H * rp * 2);
     const int64_t S = gemm_splits(tiles, vp / kBK, room / ((size_t)R * H * 4));
