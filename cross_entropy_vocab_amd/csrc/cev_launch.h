@@ -207,8 +207,9 @@ struct LceArgs {
     cev_vocab_partial *partials;    // forward: [splits][rows]
     const float *g;                 // backward: [rows]
     const cev_saved *saved;         // backward: [rows]
-    unsigned short *dlogits;        // backward: [rows, ldd] bf16 scratch
+    unsigned short *dlogits;        // backward: [dl_rows, ldd] bf16 scratch
     int64_t ldd;                    // multiple of 64, >= vocab
+    int64_t dl_rows;                // rows of dlogits written (>= rows; rows past rows are zero)
     int32_t *status;
 };
 

@@ -21,8 +21,8 @@
 //             formula of k_backward, from the saved record); k_lce_gemm then
 //             forms dhidden = dlogits x head with the head read as stored (its
 //             MFMA fragments formed by transposing LDS reads) and, for a
-//             trainable head, dhead = dlogits^T x hidden from transposed
-//             copies of both.
+//             trainable head, dhead = dlogits^T x hidden with both read
+//             as stored too.
 //
 // Tiles: 8 waves in a 4 x 2 grid (two per SIMD), each wave 64 x 128 of C as
 // 2 x 4 blocks of 32 x 32; K steps of 64, copied from global memory straight
@@ -115,21 +115,32 @@ __device__ __forceinline__ void dma_wait()
 
 // Fragments of K sub-step ks (16 deep) for this wave: A rows wm*64 + 32 mb +
 // (lane % 32), B rows wn*128 + 32 nb + (lane % 32), k = 16 ks + 8 (lane / 32).
+template <int NBLK>
+__device__ __forceinline__ void frag_load_kn(const unsigned short *lt, bf16x8 (&f)[NBLK], int ks,
+                                             int c0, int lane);
+
+template <bool AKN, bool BKN>
 __device__ __forceinline__ void frag_load(const unsigned short *la, const unsigned short *lb,
                                           bf16x8 (&af)[kTM], bf16x8 (&bf)[kTN], int ks, int wm,
-                                          int wn, int lane, bool with_b = true)
+                                          int wn, int lane)
 {
     const int kk = ks * 16 + (lane >> 5) * 8;
+    if constexpr (AKN) {
+        frag_load_kn<kTM>(la, af, ks, wm * 64, lane);
+    } else {
 #pragma unroll
-    for (int mb = 0; mb < kTM; ++mb)
-        af[mb] = *reinterpret_cast<const bf16x8 *>(
-            la + lds_at(wm * 64 + mb * 32 + (lane & 31), kk));
-    if (!with_b)
-        return;
+        for (int mb = 0; mb < kTM; ++mb)
+            af[mb] = *reinterpret_cast<const bf16x8 *>(
+                la + lds_at(wm * 64 + mb * 32 + (lane & 31), kk));
+    }
+    if constexpr (BKN) {
+        frag_load_kn<kTN>(lb, bf, ks, wn * 128, lane);
+    } else {
 #pragma unroll
-    for (int nb = 0; nb < kTN; ++nb)
-        bf[nb] = *reinterpret_cast<const bf16x8 *>(
-            lb + lds_at(wn * 128 + nb * 32 + (lane & 31), kk));
+        for (int nb = 0; nb < kTN; ++nb)
+            bf[nb] = *reinterpret_cast<const bf16x8 *>(
+                lb + lds_at(wn * 128 + nb * 32 + (lane & 31), kk));
+    }
 }
 
 // The same copies with a uniform base: a lane's byte offset from a tile's
@@ -248,33 +259,36 @@ __device__ __forceinline__ void dma_tile_kn_s(const unsigned short *X, int64_t l
                    __builtin_amdgcn_readfirstlane(base + (unsigned)i * (kLT * 16)));
 }
 
-// B fragments of K sub-step ks from an N-contiguous tile.  ds_read_b64_tr_b16
-// works on groups of 16 lanes: lane i of a group reads 4 consecutive values,
-// and lane j receives value j % 4 of the reads of lanes j / 4, j / 4 + 4,
-// j / 4 + 8, j / 4 + 12 (checked on the device).  Lane i reads row
-// k + i / 4 at columns 4 (i % 4) .. +3, so lane j gets column j of rows
-// k .. k + 3: two reads give the 8 K values of one column that the
-// 32x32x16 MFMA takes from a lane (column l % 32, K 8 (l / 32) .. +8).
-__device__ __forceinline__ void frag_load_b_kn(const unsigned short *lb, bf16x8 (&bf)[kTN], int ks,
-                                               int wn, int lane)
+// Fragments of K sub-step ks from a tile staged K rows x 256 columns (an
+// N-contiguous B, or an M-contiguous A): nblk blocks of 32 columns from column
+// c0.  ds_read_b64_tr_b16 works on groups of 16 lanes: lane i of a group reads
+// 4 consecutive values, and lane j receives value j % 4 of the reads of lanes
+// j / 4, j / 4 + 4, j / 4 + 8, j / 4 + 12 (checked on the device).  Lane i
+// reads row k + i / 4 at columns 4 (i % 4) .. +3, so lane j gets column j of
+// rows k .. k + 3: two reads give the 8 K values of one column that the
+// 32x32x16 MFMA takes from a lane (column l % 32, K 8 (l / 32) .. +8), for A
+// as for B.
+template <int NBLK>
+__device__ __forceinline__ void frag_load_kn(const unsigned short *lt, bf16x8 (&f)[NBLK], int ks,
+                                             int c0, int lane)
 {
     typedef short v4s __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) v4s lds_v4s;
     const int g = lane >> 4, i = lane & 15;
 #pragma unroll
-    for (int nb = 0; nb < kTN; ++nb) {
-        const int col = wn * 128 + nb * 32 + 16 * (g & 1) + 4 * (i & 3);
+    for (int nb = 0; nb < NBLK; ++nb) {
+        const int col = c0 + nb * 32 + 16 * (g & 1) + 4 * (i & 3);
         v4s h[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int k = ks * 16 + 8 * (g >> 1) + 4 * t + (i >> 2);
             const int e = k * kBN + ((((col >> 3) ^ (4 * kn_swz(k))) & 31) << 3) + (col & 7);
             h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_v4s *)(const_cast<unsigned short *>(lb) + e));
+                (lds_v4s *)(const_cast<unsigned short *>(lt) + e));
         }
         const short v8 __attribute__((ext_vector_type(8))) = {h[0][0], h[0][1], h[0][2], h[0][3],
                                                               h[1][0], h[1][1], h[1][2], h[1][3]};
-        __builtin_memcpy(&bf[nb], &v8, 16);
+        __builtin_memcpy(&f[nb], &v8, 16);
     }
 }
 
@@ -290,20 +304,14 @@ struct NoIssue {
     __device__ void operator()() const {}
 };
 
-template <bool BKN = false, class F = NoIssue>
+template <bool AKN = false, bool BKN = false, class F = NoIssue>
 __device__ __forceinline__ void mma_stage(const unsigned short *la, const unsigned short *lb,
                                           f32x16 (&acc)[kTM][kTN], int wm, int wn, int lane,
                                           F &&issue = NoIssue{})
 {
     bf16x8 af[2][kTM], bf[2][kTN];
     auto frags = [&](int ks, bf16x8 (&a)[kTM], bf16x8 (&b)[kTN]) {
-        if constexpr (BKN) {
-            bf16x8 unused[kTN];
-            frag_load(la, lb, a, unused, ks, wm, wn, lane, false);
-            frag_load_b_kn(lb, b, ks, wn, lane);
-        } else {
-            frag_load(la, lb, a, b, ks, wm, wn, lane);
-        }
+        frag_load<AKN, BKN>(la, lb, a, b, ks, wm, wn, lane);
     };
     frags(0, af[0], bf[0]);
     issue();
@@ -405,35 +413,45 @@ __device__ __forceinline__ void gemm_tiles(GemmSmem &sm, const unsigned short *X
 // K step as gemm_tiles in one branch-free loop (the last step copies its own
 // K range again, unused), accumulators returned to the caller.  Measured on
 // MI355X for the dhidden shape: 12% faster than running it through gemm_tiles.
-// B is K-contiguous (rowsB rows, staged permuted) or, with BKN, N-contiguous:
-// rowsB K rows of at least ncols columns, output columns col0 + 0..255.
-template <bool BKN = false>
+// Each operand is K-contiguous (A: rowsA rows from row0; B: rowsB rows from
+// col0, staged permuted) or, with AKN / BKN, stored as K rows of contiguous
+// M / N values (kA / kB rows, at least mA / nB of them readable per row;
+// output rows row0 + 0..255 and columns col0 + 0..255).
+template <bool AKN = false, bool BKN = false>
 __device__ __forceinline__ void gemm_one_tile(GemmSmem &sm, const unsigned short *XA,
                                               int64_t lda, int64_t rowsA, int64_t row0,
                                               const unsigned short *XB, int64_t ldb,
                                               int64_t rowsB, int64_t col0, int64_t nk,
-                                              f32x16 (&acc)[kTM][kTN], int64_t ncols = 0)
+                                              f32x16 (&acc)[kTM][kTN], int64_t mA = 0,
+                                              int64_t nB = 0)
 {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 1, wn = w & 1;
     zero_acc(acc);
     if (nk <= 0)
         return;
-    const bool fast_a = row0 + kBM <= rowsA && lda < kFastLd;
+    const bool fast_a = AKN ? lda < kFastLd : (row0 + kBM <= rowsA && lda < kFastLd);
     const bool fast_b = BKN ? ldb < kFastLd : (col0 + kBN <= rowsB && ldb < kFastLd);
-    const unsigned voff_a = dma_voff<false>(lda, tid);
-    const unsigned voff_b = BKN ? dma_voff_kn(ldb, col0, ncols, tid) : dma_voff<true>(ldb, tid);
+    const unsigned voff_a = AKN ? dma_voff_kn(lda, row0, mA, tid) : dma_voff<false>(lda, tid);
+    const unsigned voff_b = BKN ? dma_voff_kn(ldb, col0, nB, tid) : dma_voff<true>(ldb, tid);
     auto copy = [&](int64_t kstep, int to) {
         const int64_t k0 = kstep * kBK;
-        if (fast_a)
-            dma_tile_s<false>(XA, lda, row0, k0, voff_a, sm.a[to], tid);
-        else
-            dma_tile<false>(XA, lda, rowsA, row0, k0, sm.a[to], tid);
+        if constexpr (AKN) {
+            if (fast_a && k0 + kBK <= rowsA)
+                dma_tile_kn_s(XA, lda, k0, row0, voff_a, sm.a[to], tid);
+            else
+                dma_tile_kn(XA, lda, rowsA, mA, k0, row0, sm.a[to], tid);
+        } else {
+            if (fast_a)
+                dma_tile_s<false>(XA, lda, row0, k0, voff_a, sm.a[to], tid);
+            else
+                dma_tile<false>(XA, lda, rowsA, row0, k0, sm.a[to], tid);
+        }
         if constexpr (BKN) {
             if (fast_b && k0 + kBK <= rowsB)
                 dma_tile_kn_s(XB, ldb, k0, col0, voff_b, sm.b[to], tid);
             else
-                dma_tile_kn(XB, ldb, rowsB, ncols, k0, col0, sm.b[to], tid);
+                dma_tile_kn(XB, ldb, rowsB, nB, k0, col0, sm.b[to], tid);
         } else {
             if (fast_b)
                 dma_tile_s<true>(XB, ldb, col0, k0, voff_b, sm.b[to], tid);
@@ -447,7 +465,7 @@ __device__ __forceinline__ void gemm_one_tile(GemmSmem &sm, const unsigned short
     int buf = 0;
     for (int64_t it = 0; it < nk; ++it) {
         const int64_t nx = it + 1 < nk ? it + 1 : it;
-        mma_stage<BKN>(sm.a[buf], sm.b[buf], acc, wm, wn, lane, [&] { copy(nx, buf ^ 1); });
+        mma_stage<AKN, BKN>(sm.a[buf], sm.b[buf], acc, wm, wn, lane, [&] { copy(nx, buf ^ 1); });
         dma_wait();
         __syncthreads();
         buf ^= 1;
@@ -872,7 +890,7 @@ __global__ __launch_bounds__(kLT) void k_lce_dl(LceArgs a)
             for (int v = 0; v < 16; ++v) {
                 const int rl = acc_row(wm, mb, v, el);
                 const int64_t r = row0 + rl;
-                if (r >= a.rows)
+                if (r >= a.dl_rows)   // rows in [rows, dl_rows) come out as zeros
                     continue;
                 const DlRow rc = s_rc[rl];
                 const unsigned sgn = (unsigned)s_ls[rl].y;
@@ -913,15 +931,17 @@ __global__ __launch_bounds__(kLT) void k_lce_dl(LceArgs a)
 // fastest).  Split along K: workgroup split s covers K steps
 // [nk s / splits, nk (s + 1) / splits) of 64 and writes its partial product to
 // C + s * cstride (reduced afterwards in split order).  vec4: C and ldc allow
-// 16-byte stores.  BKN: B is N-contiguous instead (B[k * ldb + n], kr rows),
-// and each lane holds one column of each 32-column block (4-byte stores,
-// 32 adjacent columns per half-wave).
-template <bool BKN>
+// 16-byte stores.  AKN: A is stored as ka K rows of contiguous M values
+// (A[k * lda + m], am of them readable per row); BKN: B likewise
+// (B[k * ldb + n], kb rows), and each lane then holds one column of each
+// 32-column block (4-byte stores, 32 adjacent columns per half-wave).
+template <bool AKN, bool BKN>
 __global__ __launch_bounds__(kLT) void k_lce_gemm(const unsigned short *XA, int64_t lda,
                                                  int64_t M, const unsigned short *XB,
                                                  int64_t ldb, int64_t N, int64_t nk,
                                                  int64_t splits, float *C, int64_t ldc,
-                                                 int64_t cstride, int vec4, int64_t kr)
+                                                 int64_t cstride, int vec4, int64_t ka,
+                                                 int64_t am, int64_t kb)
 {
     __shared__ GemmSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -933,9 +953,11 @@ __global__ __launch_bounds__(kLT) void k_lce_gemm(const unsigned short *XA, int6
     const int64_t k0 = nk * sp / splits, k1 = nk * (sp + 1) / splits;
     float *Cs = C + sp * cstride;
     f32x16 acc[kTM][kTN];
+    const unsigned short *A0 = AKN ? XA + k0 * kBK * lda : XA + k0 * kBK;
+    const unsigned short *B0 = BKN ? XB + k0 * kBK * ldb : XB + k0 * kBK;
+    gemm_one_tile<AKN, BKN>(sm, A0, lda, AKN ? ka - k0 * kBK : M, row0, B0, ldb,
+                            BKN ? kb - k0 * kBK : N, nt * kBN, k1 - k0, acc, am, N);
     if constexpr (BKN) {
-        gemm_one_tile<true>(sm, XA + k0 * kBK, lda, M, row0, XB + k0 * kBK * ldb, ldb,
-                            kr - k0 * kBK, nt * kBN, k1 - k0, acc, N);
         const int64_t cb = nt * kBN + wn * 128 + (lane & 31);
 #pragma unroll
         for (int mb = 0; mb < kTM; ++mb)
@@ -952,8 +974,6 @@ __global__ __launch_bounds__(kLT) void k_lce_gemm(const unsigned short *XA, int6
             }
         return;
     }
-    gemm_one_tile(sm, XA + k0 * kBK, lda, M, row0, XB + k0 * kBK, ldb, N, nt * kBN, k1 - k0,
-                  acc);
     const int64_t c0 = lane_col(nt, wn, lane);
     if (c0 >= N)
         return;
@@ -1002,54 +1022,8 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *P, int64_t s
     dst[3] = acc.w;
 }
 
-// D[c][r] = S[r][c] for r < R (zeros for R <= r < rp), c < C.  Each lane
-// moves one 8 x 8 block in registers: eight 16-byte row pieces in, eight
-// 16-byte column pieces out, the 16-bit halves regrouped with shifts and
-// masks.  A wave covers 64 r x 64 c (lane = 8 r-blocks x 8 c-blocks), a
-// workgroup 256 r x 64 c.  Needs S rows 16-byte aligned with ld a multiple of
-// 8 and rp a multiple of 64; a piece past column C stays inside S's row when
-// ld >= round64(C) or C is a multiple of 64 (every caller), and D rows
-// c >= C are not written.
-__global__ __launch_bounds__(256) void k_transpose(const unsigned short *S, int64_t ld, int64_t R,
-                                                   int64_t C, unsigned short *D, int64_t rp)
-{
-    const int64_t rtiles = (rp + 255) / 256;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int64_t r = (blockIdx.x % rtiles) * 256 + w * 64 + (lane >> 3) * 8;
-    const int64_t c = (blockIdx.x / rtiles) * 64 + (lane & 7) * 8;
-    if (r >= rp)
-        return;
-    u32x4 in[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        in[k] = r + k < R ? *reinterpret_cast<const u32x4 *>(S + (r + k) * ld + c) : z;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        if (c + j >= C)
-            break;
-        u32x4 o;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const unsigned x = in[2 * m][j >> 1], y = in[2 * m + 1][j >> 1];
-            o[m] = (j & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-        }
-        *reinterpret_cast<u32x4 *>(D + (c + j) * rp + r) = o;
-    }
-}
-
-void launch_transpose(const unsigned short *S, int64_t ld, int64_t R, int64_t C,
-                      unsigned short *D, int64_t rp, hipStream_t s)
-{
-    const int64_t tiles = ((rp + 255) / 256) * ((C + 63) / 64);
-    hipLaunchKernelGGL(k_transpose, dim3((unsigned)tiles), dim3(256), 0, s, S, ld, R, C, D, rp);
-}
-
 int64_t round64(int64_t x) { return (x + 63) / 64 * 64; }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-
-int vec4_ok(const float *p, int64_t ld) { return ((uintptr_t)p % 16 == 0 && ld % 4 == 0) ? 1 : 0; }
 
 // K splits for a product of `tiles` output tiles with nk K steps: the fewest
 // splits that minimise the number of full-chip rounds per split (a grid of
@@ -1100,14 +1074,14 @@ hipError_t launch_lce_forward(const LceArgs &a, bool want_h, bool want_z, hipStr
     return hipGetLastError();
 }
 
-// Backward workspace: dlogits [R, round64(V)], and for the head gradient
-// dlogits^T [V, round64(R)] and hidden^T [H, round64(R)] (the dhidden split-K
-// partials use that second region first).
+// Backward workspace: dlogits [round64(R), round64(V)] (zero past row R and
+// column V) and room for up to kMaxSplitK fp32 partial products of dhidden.
+constexpr int64_t kMaxSplitK = 8;
+
 size_t lce_backward_workspace(int64_t rows, int64_t hidden_dim, int64_t vocab)
 {
     const size_t vp = (size_t)round64(vocab), rp = (size_t)round64(rows);
-    return align256((size_t)rows * vp * 2) + align256((size_t)vocab * rp * 2) +
-           align256((size_t)hidden_dim * rp * 2);
+    return align256(rp * vp * 2) + align256((size_t)kMaxSplitK * rows * hidden_dim * 4);
 }
 
 hipError_t launch_lce_backward(const LceArgs &a, void *workspace, float *dhidden, int64_t ldo,
@@ -1117,14 +1091,13 @@ hipError_t launch_lce_backward(const LceArgs &a, void *workspace, float *dhidden
     const int64_t vp = round64(V), rp = round64(R);
     char *ws = static_cast<char *>(workspace);
     unsigned short *dl = reinterpret_cast<unsigned short *>(ws);
-    ws += align256((size_t)R * vp * 2);
-    unsigned short *dlt = reinterpret_cast<unsigned short *>(ws);
-    ws += align256((size_t)V * rp * 2);
-    unsigned short *ht = reinterpret_cast<unsigned short *>(ws);
+    ws += align256((size_t)rp * vp * 2);
+    float *part = reinterpret_cast<float *>(ws);
 
     LceArgs b = a;
     b.dlogits = dl;
     b.ldd = vp;
+    b.dl_rows = rp;
     const int64_t nrb = (R + kBM - 1) / kBM;
     hipLaunchKernelGGL(k_lce_dl, dim3((unsigned)(nrb * b.splits)), dim3(kLT), 0, s, b);
     hipError_t e = hipGetLastError();
@@ -1133,33 +1106,30 @@ hipError_t launch_lce_backward(const LceArgs &a, void *workspace, float *dhidden
     // dhidden[R, H] = dlogits[R, V] x head[V, H]: dlogits runs along the
     // vocab, the head is read as stored (its K rows past V re-read row V - 1
     // against zero dlogits columns).  Few output tiles and a long contraction:
-    // split along K so the grid fills the chip; the partials live where
-    // dlogits^T and hidden^T go later.
+    // split along K so the grid fills the chip.
     const int64_t tiles = nrb * ((H + kBN - 1) / kBN);
-    const size_t room = align256((size_t)V * rp * 2) + align256((size_t)H * rp * 2);
-    const int64_t S = gemm_splits(tiles, vp / kBK, room / ((size_t)R * H * 4));
+    const int64_t S = gemm_splits(tiles, vp / kBK, (size_t)kMaxSplitK);
     if (S > 1) {
-        float *part = reinterpret_cast<float *>(dlt);
-        hipLaunchKernelGGL(k_lce_gemm<true>, dim3((unsigned)(tiles * S)), dim3(kLT), 0, s, dl, vp,
-                           R, a.weight, a.ldw, H, vp / kBK, S, part, H, R * H, 0, V);
+        hipLaunchKernelGGL((k_lce_gemm<false, true>), dim3((unsigned)(tiles * S)), dim3(kLT), 0,
+                           s, dl, vp, R, a.weight, a.ldw, H, vp / kBK, S, part, H, R * H, 0,
+                           (int64_t)0, (int64_t)0, V);
         const int64_t n = R * (H / 4);
         hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                            part, S, R, H, dhidden, ldo);
     } else {
-        hipLaunchKernelGGL(k_lce_gemm<true>, dim3((unsigned)tiles), dim3(kLT), 0, s, dl, vp, R,
-                           a.weight, a.ldw, H, vp / kBK, (int64_t)1, dhidden, ldo, (int64_t)0, 0,
-                           V);
+        hipLaunchKernelGGL((k_lce_gemm<false, true>), dim3((unsigned)tiles), dim3(kLT), 0, s, dl,
+                           vp, R, a.weight, a.ldw, H, vp / kBK, (int64_t)1, dhidden, ldo,
+                           (int64_t)0, 0, (int64_t)0, (int64_t)0, V);
     }
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
-    // dhead[V, H] = dlogits^T x hidden: both transposed to run along the rows.
+    // dhead[V, H] = dlogits^T x hidden, both read as stored: K runs over the
+    // rows (dlogits' rows past R are zero, hidden's re-read row R - 1).
     if (dweight) {
-        launch_transpose(dl, vp, R, V, dlt, rp, s);
-        launch_transpose(a.hidden, a.ldh, R, H, ht, rp, s);
         const int64_t wtiles = ((V + kBM - 1) / kBM) * ((H + kBN - 1) / kBN);
-        hipLaunchKernelGGL(k_lce_gemm<false>, dim3((unsigned)wtiles), dim3(kLT), 0, s, dlt, rp, V,
-                           ht, rp, H, rp / kBK, (int64_t)1, dweight, ldw_out, (int64_t)0,
-                           vec4_ok(dweight, ldw_out), (int64_t)0);
+        hipLaunchKernelGGL((k_lce_gemm<true, true>), dim3((unsigned)wtiles), dim3(kLT), 0, s, dl,
+                           vp, V, a.hidden, a.ldh, H, rp / kBK, (int64_t)1, dweight, ldw_out,
+                           (int64_t)0, 0, rp, vp, R);
         e = hipGetLastError();
     }
     return e;
