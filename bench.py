@@ -187,8 +187,6 @@ def run_counter_workload(name, torch, cev, workloads, dev, reps=3):
             dict(regex=r"^k_lce_fwd<", call="lce_forward", read=ops, write=0),
             dict(regex=r"^k_lce_dl", call="lce_backward: logits again, dlogits", read=ops,
                  write=R * V * 2),
-            dict(regex=r"^k_transpose", call="lce_backward: head transposed", read=V * H * 2,
-                 write=V * H * 2),
             dict(regex=r"^k_lce_gemm", call="lce_backward: dhidden, split-K partials",
                  read=R * V * 2 + V * H * 2, write=4 * R * H * 4),
             dict(regex=r"^k_splitk_reduce", call="lce_backward: split-K sum", read=4 * R * H * 4,
