@@ -179,6 +179,17 @@ def test_lce_exact_smoothing_and_strides():
     check_exact(w, got, "smoothing+strides", eps=0.1)
 
 
+def test_lce_exact_wide_hidden_stride():
+    """A hidden row stride of 2^24 + 64 elements: the operand copies that read
+    hidden (both logit products, and the head gradient's B operand) take
+    clamped per-lane addresses instead of an SGPR base with 32-bit offsets."""
+    from gpu_helpers import say
+    say("[lce exact] hidden stride 2^24 + 64")
+    w = grid_case(R=3, H=64, V=300, seed=9, n_ignored=1)
+    got = run_lce(w, hs=(1 << 24) + 64)
+    check_exact(w, got, "wide hidden stride")
+
+
 def test_lce_bad_labels_and_determinism():
     w = grid_case(R=70, H=64, V=500, seed=8)
     w["labels"][3] = 500
