@@ -33,10 +33,10 @@
 // peak on MI355X.  Fragment layout of the 32x32x16 bf16 MFMA on gfx950 (checked on the
 // device): lane l supplies A[l % 32][8 (l / 32) .. +8] and B[same k][l % 32];
 // accumulator element v of lane l is C[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
-// The B rows are staged permuted so that the four 32-column blocks of a wave
-// interleave: lane l of block nb holds output column 4 (l % 32) + nb of the
-// wave's 128, so each lane owns four adjacent columns of every row it holds
-// (8- and 16-byte stores of dlogits and of the gradients).
+// In the logit products the B rows are staged permuted so that the four
+// 32-column blocks of a wave interleave: lane l of block nb holds output column
+// 4 (l % 32) + nb of the wave's 128, so each lane owns four adjacent columns
+// of every row it holds (8-byte stores of dlogits).
 #include "cev_device.h"
 #include "cev_launch.h"
 
@@ -73,6 +73,12 @@ __device__ __forceinline__ int perm_b(int q)
     return (q & 128) | ((q & 31) << 2) | ((q >> 5) & 3);
 }
 
+// LDS byte address of a shared-memory pointer.
+__device__ __forceinline__ unsigned lds_u32(const unsigned short *lds)
+{
+    return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) unsigned short *)lds;
+}
+
 // Rows [r0, r0 + 256) x k [k0, k0 + 64) of a K-contiguous bf16 matrix
 // X[row * ld + k] copied from global memory straight into the LDS tile `lds`
 // (global_load_lds_dwordx4: each lane's 16 bytes land at M0 + 16 * lane, with
@@ -90,8 +96,7 @@ __device__ __forceinline__ void dma_tile(const unsigned short *X, int64_t ld, in
                                          int64_t r0, int64_t k0, unsigned short *lds, int tid)
 {
     const int lane = tid & 63, w = tid >> 6;
-    const unsigned base =
-        (unsigned)(uintptr_t)(const __attribute__((address_space(3))) unsigned short *)lds;
+    const unsigned base = lds_u32(lds);
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
         const int p = kLT * i + 64 * w + lane;
@@ -113,11 +118,14 @@ __device__ __forceinline__ void dma_wait()
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// Fragments of K sub-step ks (16 deep) for this wave: A rows wm*64 + 32 mb +
-// (lane % 32), B rows wn*128 + 32 nb + (lane % 32), k = 16 ks + 8 (lane / 32).
 template <int NBLK>
 __device__ __forceinline__ void frag_load_kn(const unsigned short *lt, bf16x8 (&f)[NBLK], int ks,
                                              int c0, int lane);
+
+// Fragments of K sub-step ks (16 deep) for this wave: A rows wm*64 + 32 mb +
+// (lane % 32), B rows wn*128 + 32 nb + (lane % 32), k = 16 ks + 8 (lane / 32);
+// an operand staged K rows x 256 columns (AKN / BKN) goes through
+// frag_load_kn instead.
 
 template <bool AKN, bool BKN>
 __device__ __forceinline__ void frag_load(const unsigned short *la, const unsigned short *lb,
@@ -151,11 +159,6 @@ __device__ __forceinline__ void frag_load(const unsigned short *la, const unsign
 // inside the matrix and the offsets fit 32 bits (leading dimension < 2^24).
 // The asm waits 5 states before the copy in case the base was just moved into
 // SGPRs by a vector instruction.
-__device__ __forceinline__ unsigned lds_u32(const unsigned short *lds)
-{
-    return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) unsigned short *)lds;
-}
-
 __device__ __forceinline__ void dma_copy_s(const unsigned short *base, unsigned voff, unsigned m0)
 {
     // (readfirstlane returns int: each half goes through unsigned, so that the
@@ -219,8 +222,7 @@ __device__ __forceinline__ void dma_tile_kn(const unsigned short *X, int64_t ld,
                                             unsigned short *lds, int tid)
 {
     const int lane = tid & 63, w = tid >> 6;
-    const unsigned base =
-        (unsigned)(uintptr_t)(const __attribute__((address_space(3))) unsigned short *)lds;
+    const unsigned base = lds_u32(lds);
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
         const int p = kLT * i + 64 * w + lane;
