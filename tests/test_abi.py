@@ -334,9 +334,8 @@ def test_lce_validation(lib):
     assert fwd(eps=-1.0) == E["SMOOTH"]
     assert fwd(V=0) == E["SHAPE"]
     assert fwd(rows=0, h=None, w=None) == E["OK"]
-    # dlogits [R, V64], dlogits^T [V, R64], hidden^T [H, R64] (bf16)
-    assert lib.lce_workspace_size(8192, 2560, 151936) == 2 * (8192 * 151936 +
-                                                              151936 * 8192 + 2560 * 8192)
+    # dlogits [R64, V64] (bf16) and up to 8 split-K partial products of dhidden (fp32)
+    assert lib.lce_workspace_size(8192, 2560, 151936) == 2 * 8192 * 151936 + 8 * 8192 * 2560 * 4
     assert lib.lce_workspace_size(8, 100, 10) == 0
 
     def bwd(**kw):
