@@ -406,6 +406,22 @@ def bench_linear(args, torch, cev, workloads, dev):
     del o2
     log(f"[bench] linear CE: forward {f_ms:.2f} ms, backward {b_ms:.2f} ms; "
         f"forward at {r2} rows {f2_ms:.2f} ms")
+    # Memory for time: the forward also stores the fp32 logits (R x V x 4
+    # bytes), and the backward reads them back instead of recomputing them.
+    zs = torch.empty((R, Vl), dtype=torch.float32, device=dev)
+    sf_ms, sb_ms = _time_calls(torch, [
+        lambda i: cev.lce_forward(hid, head, lab, 1.0, row_mask=msk, argmax=True, out=out,
+                                  logits=zs),
+        lambda i: cev.lce_backward(hid, head, lab, gl, out["saved"], 1.0, row_mask=msk,
+                                   workspace=out["workspace"], dhidden=dh, logits=zs)], steps)
+    zbytes = R * Vl * 4
+    stored = {"entry": "lce_forward(logits=) + lce_backward(logits=): fp32 logits kept in HBM",
+              "logits_bytes": zbytes, "forward_ms": sf_ms, "backward_ms": sb_ms,
+              "step_ms": sf_ms + sb_ms, "rows_per_s": R / ((sf_ms + sb_ms) / 1e3),
+              "forward_TFLOPs": flop / (sf_ms / 1e3) / 1e12,
+              "backward_TFLOPs": flop / (sb_ms / 1e3) / 1e12}
+    del zs
+    log(f"[bench] linear CE, stored logits: forward {sf_ms:.2f} ms, backward {sb_ms:.2f} ms")
     res = {"entry": "lce_forward + lce_backward (frozen head: dhidden only), logits never "
                     "stored; 2560 x 151936 head as in the unsloth-zoo #2080 Speed section",
            "shape": {"rows": R, "hidden": H, "vocab": Vl}, "steps": steps,
@@ -416,6 +432,7 @@ def bench_linear(args, torch, cev, workloads, dev):
            "step_TFLOPs": 3 * flop / ((f_ms + b_ms) / 1e3) / 1e12,
            "forward_2048_rows_ms": f2_ms,
            "forward_2048_rows_TFLOPs": flop * r2 / R / (f2_ms / 1e3) / 1e12,
+           "stored_logits": stored,
            "roofline": {"bound": "mfma", "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "achieved": 3 * flop / ((f_ms + b_ms) / 1e3) / 1e12,
                         "frac": 3 * flop / ((f_ms + b_ms) / 1e3) / 1e12 / PEAK_BF16_TFLOPS}}

@@ -502,13 +502,33 @@ def _lce_workspace(o, rows, H, V, dev):
     return ws, need
 
 
+def _lce_logits(logits, rows, V, dev, allocate):
+    """(tensor, row stride) of a stored-logits buffer: None, True (allocate
+    [rows, V] fp32, rows padded to 16 bytes) or an fp32 [rows, V] view with
+    unit column stride, 16-byte aligned rows and a row stride a multiple of 4."""
+    if logits is None or logits is False:
+        return None, 0
+    if logits is True:
+        if not allocate:
+            raise ValueError("logits must be the tensor lce_forward stored them in")
+        # rows padded to a multiple of 4 floats (16-byte aligned rows)
+        logits = torch.empty((rows, V + (-V) % 4), dtype=torch.float32, device=dev)[:, :V]
+    if not logits.is_cuda or logits.device != dev or logits.dtype != torch.float32 \
+            or tuple(logits.shape) != (rows, V) or (V > 1 and logits.stride(1) != 1):
+        raise ValueError("logits must be a float32 [rows, vocab] GPU tensor on the same device")
+    stride = logits.stride(0) if rows > 1 else V + (-V) % 4
+    return logits, stride
+
+
 def lce_forward(hidden, weight, labels, temperature=1.0, row_mask=None, ignore_index=-100,
                 label_smoothing=0.0, logp=True, entropy=False, argmax=False, status=None,
-                out=None):
+                out=None, logits=None):
     """Linear cross-entropy forward: logits = hidden x weight^T (bf16 in, fp32
-    accumulate, never stored), then the collapse-safe per-row CE.  Returns a
-    dict with loss, saved (for lce_backward) and optionally logp, entropy,
-    argmax, plus the workspace it used."""
+    accumulate), then the collapse-safe per-row CE.  The logits are never
+    stored unless `logits` is True (a new fp32 [rows, vocab] tensor) or such a
+    tensor: then lce_backward can read them back instead of recomputing them.
+    Returns a dict with loss, saved (for lce_backward) and optionally logp,
+    entropy, argmax, logits, plus the workspace it used."""
     rows, H = hidden.shape
     dev = hidden.device
     hs = _check_bf16_2d(hidden, "hidden")
@@ -536,21 +556,24 @@ def lce_forward(hidden, weight, labels, temperature=1.0, row_mask=None, ignore_i
     want("argmax", argmax, torch.int64, (rows,))
     ws, need = _lce_workspace(o, rows, H, V, dev)
     o["workspace"] = ws
+    lg, ldl = _lce_logits(logits, rows, V, dev, allocate=True)
+    o["logits"] = lg
     rc = _lib.get().lce_forward(_ptr(hidden), rows, H, hs, _ptr(weight), V, ws_, _ptr(labels),
                                 int(ignore_index), float(temperature), float(label_smoothing),
                                 _ptr(m), _ptr(o["loss"]), _ptr(o["saved"]), _ptr(o["logp"]),
-                                _ptr(o["entropy"]), _ptr(o["argmax"]), _ptr(ws), need,
-                                _ptr(status), _stream(dev))
+                                _ptr(o["entropy"]), _ptr(o["argmax"]), _ptr(lg), ldl, _ptr(ws),
+                                need, _ptr(status), _stream(dev))
     _check("lce_forward", rc)
     return o
 
 
 def lce_backward(hidden, weight, labels, g, saved, temperature=1.0, row_mask=None,
                  ignore_index=-100, label_smoothing=0.0, dweight=False, status=None,
-                 workspace=None, dhidden=None):
+                 workspace=None, dhidden=None, logits=None):
     """Gradients of sum_r g[r] loss[r] through logits = hidden x weight^T:
     dhidden [rows, hidden_dim] fp32, and dweight [vocab, hidden_dim] fp32 when
-    dweight=True (else None, a frozen head)."""
+    dweight=True (else None, a frozen head).  `logits`: the tensor lce_forward
+    stored the logits in, read instead of recomputing them."""
     rows, H = hidden.shape
     dev = hidden.device
     hs = _check_bf16_2d(hidden, "hidden")
@@ -567,9 +590,10 @@ def lce_backward(hidden, weight, labels, g, saved, temperature=1.0, row_mask=Non
     else:
         _dev(dhidden, "dhidden", torch.float32, (rows, H), dev)
     dw = torch.empty((V, H), dtype=torch.float32, device=dev) if dweight else None
+    lg, ldl = _lce_logits(logits, rows, V, dev, allocate=False)
     rc = _lib.get().lce_backward(_ptr(hidden), rows, H, hs, _ptr(weight), V, ws_, _ptr(labels),
                                  int(ignore_index), float(temperature), float(label_smoothing),
-                                 _ptr(m), _ptr(g), _ptr(saved), _ptr(dhidden), H, _ptr(dw), H,
-                                 _ptr(ws), need, _ptr(status), _stream(dev))
+                                 _ptr(m), _ptr(g), _ptr(saved), _ptr(lg), ldl, _ptr(dhidden), H,
+                                 _ptr(dw), H, _ptr(ws), need, _ptr(status), _stream(dev))
     _check("lce_backward", rc)
     return dhidden, dw

@@ -39,10 +39,10 @@ SIGNATURES = {
     "ce_vocab_merge": (I32, [P, I64, I64, I64, P, I64, D, D, P, P, P, P, P, P, P, P]),
     "ce_vocab_shard_backward": (I32, [P, I64, I64, I64, I32, I64, I64, P, I64, D, D, P, P, P, P,
                                       I64, P, P]),
-    "lce_forward": (I32, [P, I64, I64, I64, P, I64, I64, P, I64, D, D, P, P, P, P, P, P, P, SZ,
-                          P, P]),
+    "lce_forward": (I32, [P, I64, I64, I64, P, I64, I64, P, I64, D, D, P, P, P, P, P, P, P, I64,
+                          P, SZ, P, P]),
     "lce_backward": (I32, [P, I64, I64, I64, P, I64, I64, P, I64, D, D, P, P, P, P, I64, P, I64,
-                           P, SZ, P, P]),
+                           P, I64, P, SZ, P, P]),
     "lce_workspace_size": (SZ, [I64, I64, I64]),
     "jsd_forward": (I32, [P, P, I64, I64, I64, I64, I32, P, I64, D, D, P, P, P, P, P]),
     "jsd_backward": (I32, [P, P, I64, I64, I64, I64, I32, P, I64, D, D, P, P, P, P, I64, P, P]),

@@ -674,12 +674,25 @@ static cev::LceArgs lce_args(const void *hidden, int64_t rows, int64_t hd, int64
     return a;
 }
 
+// Optional stored fp32 logits [rows, logits_stride]: the stride covers the
+// vocabulary and keeps rows 16-byte aligned.
+static int check_lce_logits(const float *logits, int64_t logits_stride, int64_t vocab)
+{
+    if (!logits)
+        return CEV_OK;
+    if (logits_stride < vocab || logits_stride % 4 != 0)
+        return CEV_ESTRIDE;
+    if (!aligned(logits, 16))
+        return CEV_EALIGN;
+    return CEV_OK;
+}
+
 int lce_forward(const void *hidden, int64_t rows, int64_t hidden_dim, int64_t hidden_stride,
                 const void *weight, int64_t vocab, int64_t weight_stride, const int64_t *labels,
                 int64_t ignore_index, double temperature, double label_smoothing,
                 const uint8_t *row_mask, float *loss, void *saved, float *logp, float *entropy,
-                int64_t *argmax, void *workspace, size_t workspace_bytes, int32_t *status,
-                cev_stream_t stream)
+                int64_t *argmax, float *logits, int64_t logits_stride, void *workspace,
+                size_t workspace_bytes, int32_t *status, cev_stream_t stream)
 {
     bool done;
     int rc = check_lce(hidden, rows, hidden_dim, hidden_stride, weight, vocab, weight_stride,
@@ -692,12 +705,16 @@ int lce_forward(const void *hidden, int64_t rows, int64_t hidden_dim, int64_t hi
         !aligned(entropy, 4) || !aligned(argmax, 8) || !aligned(workspace, 16) ||
         !aligned(status, 4))
         return CEV_EALIGN;
+    if ((rc = check_lce_logits(logits, logits_stride, vocab)) != CEV_OK)
+        return rc;
     if (workspace_bytes < lce_workspace_size(rows, hidden_dim, vocab))
         return CEV_EWORKSPACE;
     cev::LceArgs a = lce_args(hidden, rows, hidden_dim, hidden_stride, weight, vocab,
                               weight_stride, labels, ignore_index, temperature, label_smoothing,
                               row_mask, status);
     a.partials = static_cast<cev_vocab_partial *>(workspace);
+    a.logits_out = logits;
+    a.ldl = logits ? logits_stride : 0;
     hipError_t e = cev::launch_lce_forward(a, entropy != nullptr, label_smoothing != 0.0,
                                            to_hip(stream));
     if (e != hipSuccess)
@@ -725,9 +742,9 @@ int lce_backward(const void *hidden, int64_t rows, int64_t hidden_dim, int64_t h
                  const void *weight, int64_t vocab, int64_t weight_stride,
                  const int64_t *labels, int64_t ignore_index, double temperature,
                  double label_smoothing, const uint8_t *row_mask, const float *g,
-                 const void *saved, float *dhidden, int64_t dhidden_stride, float *dweight,
-                 int64_t dweight_stride, void *workspace, size_t workspace_bytes,
-                 int32_t *status, cev_stream_t stream)
+                 const void *saved, const float *logits, int64_t logits_stride, float *dhidden,
+                 int64_t dhidden_stride, float *dweight, int64_t dweight_stride, void *workspace,
+                 size_t workspace_bytes, int32_t *status, cev_stream_t stream)
 {
     bool done;
     int rc = check_lce(hidden, rows, hidden_dim, hidden_stride, weight, vocab, weight_stride,
@@ -741,6 +758,8 @@ int lce_backward(const void *hidden, int64_t rows, int64_t hidden_dim, int64_t h
     if (!aligned(labels, 8) || !aligned(g, 4) || !aligned(saved, 16) || !aligned(dhidden, 4) ||
         !aligned(dweight, 4) || !aligned(workspace, 16) || !aligned(status, 4))
         return CEV_EALIGN;
+    if ((rc = check_lce_logits(logits, logits_stride, vocab)) != CEV_OK)
+        return rc;
     if (workspace_bytes < lce_workspace_size(rows, hidden_dim, vocab))
         return CEV_EWORKSPACE;
     cev::LceArgs a = lce_args(hidden, rows, hidden_dim, hidden_stride, weight, vocab,
@@ -748,6 +767,8 @@ int lce_backward(const void *hidden, int64_t rows, int64_t hidden_dim, int64_t h
                               row_mask, status);
     a.g = g;
     a.saved = static_cast<const cev_saved *>(saved);
+    a.logits_in = logits;
+    a.ldl = logits ? logits_stride : 0;
     return launch_status(cev::launch_lce_backward(a, workspace, dhidden, dhidden_stride,
                                                   dweight, dweight_stride, to_hip(stream)));
 }

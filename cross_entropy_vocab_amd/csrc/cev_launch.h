@@ -210,6 +210,9 @@ struct LceArgs {
     unsigned short *dlogits;        // backward: [dl_rows, ldd] bf16 scratch
     int64_t ldd;                    // multiple of 64, >= vocab
     int64_t dl_rows;                // rows of dlogits written (>= rows; rows past rows are zero)
+    float *logits_out;              // forward: if set, the fp32 logits [rows, ldl] are stored here
+    const float *logits_in;         // backward: if set, dlogits come from these stored logits
+    int64_t ldl;                    // row stride of the stored logits, a multiple of 4, >= vocab
     int32_t *status;
 };
 

@@ -612,7 +612,7 @@ struct RowState {
 };
 
 // ------------------------------------------------------------------ forward
-template <bool WANT_H, bool WANT_Z>
+template <bool WANT_H, bool WANT_Z, bool STORE>
 __global__ __launch_bounds__(kLT) void k_lce_fwd(LceArgs a)
 {
     __shared__ GemmSmem sm;
@@ -688,6 +688,21 @@ __global__ __launch_bounds__(kLT) void k_lce_fwd(LceArgs a)
 #pragma unroll
                 for (int nb = 0; nb < kTN; ++nb)
                     x[nb] = acc[mb][nb][v];
+                if constexpr (STORE) {
+                    // the raw logits of this lane's four columns, one 16-byte store
+                    const int64_t r = row0 + acc_row(wm, mb, v, el);
+                    if (r < a.rows) {
+                        float *dst = a.logits_out + r * a.ldl + c0;
+                        if (c0 + kTN <= V) {
+                            *reinterpret_cast<float4 *>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+                        } else {
+#pragma unroll
+                            for (int nb = 0; nb < kTN; ++nb)
+                                if (c0 + nb < V)
+                                    dst[nb] = x[nb];
+                        }
+                    }
+                }
                 if constexpr (MASK) {
                     const int rl = acc_row(wm, mb, v, el);
                     const int64_t d = (int64_t)s_lab[rl] - c0;
@@ -829,6 +844,35 @@ struct __align__(16) DlRow {
     float mz, kexp, ev, tv;
 };
 
+// The constants of row r (label and sign bit of g through lab, sgn); rows
+// that are masked, ignored, past `rows` or not read by the forward give
+// kexp = inf, so every entry of theirs comes out as 0.
+__device__ __forceinline__ DlRow dl_row(const LceArgs &a, int64_t r, int &lab, unsigned &sgn)
+{
+    const int64_t V = a.vocab;
+    lab = -1;
+    sgn = 0u;
+    DlRow rc{0.0f, INFINITY, 0.0f, 0.0f};
+    if (r < a.rows) {
+        const int64_t t = a.labels[r];
+        const bool masked = a.row_mask && a.row_mask[r] == 0;
+        const cev_saved sv = a.saved[r];
+        if (!masked && t != a.ignore_index && t >= 0 && t < V && (sv.flags & 1)) {
+            const float gp = a.g[r] * a.inv_t;
+            const float ag = fabsf(gp);
+            const float eps = (float)a.label_smoothing;
+            const float epv = (float)(a.label_smoothing / (double)V);
+            lab = (int)t;
+            rc.mz = sv.m_z;
+            rc.kexp = sv.log2_d - __log2f(ag);
+            rc.ev = ag * epv;
+            rc.tv = -(ag * ((sv.q - eps) + epv));
+            sgn = __float_as_uint(gp) & 0x80000000u;
+        }
+    }
+    return rc;
+}
+
 __global__ __launch_bounds__(kLT) void k_lce_dl(LceArgs a)
 {
     __shared__ GemmSmem sm;
@@ -845,28 +889,9 @@ __global__ __launch_bounds__(kLT) void k_lce_dl(LceArgs a)
     const int64_t t0 = ntiles * sp / S, t1 = ntiles * (sp + 1) / S;
 
     if (tid < kBM) {
-        const int64_t r = row0 + tid;
-        int lab = -1;
-        float mz = 0.0f, kexp = INFINITY, ev = 0.0f, tv = 0.0f;   // invalid rows: all zeros
-        unsigned sgn = 0u;
-        if (r < a.rows) {
-            const int64_t t = a.labels[r];
-            const bool masked = a.row_mask && a.row_mask[r] == 0;
-            const cev_saved sv = a.saved[r];
-            if (!masked && t != a.ignore_index && t >= 0 && t < V && (sv.flags & 1)) {
-                const float gp = a.g[r] * a.inv_t;
-                const float ag = fabsf(gp);
-                const float eps = (float)a.label_smoothing;
-                const float epv = (float)(a.label_smoothing / (double)V);
-                lab = (int)t;
-                mz = sv.m_z;
-                kexp = sv.log2_d - __log2f(ag);
-                ev = ag * epv;
-                tv = -(ag * ((sv.q - eps) + epv));
-                sgn = __float_as_uint(gp) & 0x80000000u;
-            }
-        }
-        s_rc[tid] = DlRow{mz, kexp, ev, tv};
+        int lab;
+        unsigned sgn;
+        s_rc[tid] = dl_row(a, row0 + tid, lab, sgn);
         s_ls[tid] = make_int2(lab, (int)sgn);
     }
     __syncthreads();
@@ -926,6 +951,61 @@ __global__ __launch_bounds__(kLT) void k_lce_dl(LceArgs a)
     };
     gemm_tiles(sm, a.hidden, a.ldh, a.rows, row0, a.weight, a.ldw, V, a.hidden_dim / kBK, t0, t1,
                epi);
+}
+
+// dlogits from logits the forward stored (fp32, [rows, ldl]): the per-element
+// steps of k_lce_dl's epilogue on the same fp32 values, so the dlogits are
+// bit-identical to the recomputing path.  One workgroup per row and chunk of
+// kDlsCols columns (4 per thread and step, 16-byte loads, 8-byte stores);
+// rows in [rows, dl_rows) and columns in [vocab, ldd) are written as zeros.
+constexpr int kDlsT = 256, kDlsU = 4, kDlsCols = kDlsT * 4 * kDlsU;
+
+__global__ __launch_bounds__(kDlsT) void k_lce_dl_stored(LceArgs a, int64_t chunks)
+{
+    const int64_t r = blockIdx.x / chunks, ch = blockIdx.x % chunks;
+    const int64_t V = a.vocab, ldd = a.ldd;
+    int lab;
+    unsigned sgn;
+    const DlRow rc = dl_row(a, r, lab, sgn);
+    const float c = a.c;
+    const bool have = r < a.rows;
+    const float *lrow = a.logits_in + (have ? r : 0) * a.ldl;
+    unsigned short *drow = a.dlogits + r * ldd;
+#pragma unroll
+    for (int u = 0; u < kDlsU; ++u) {
+        const int64_t col = ch * kDlsCols + (int64_t)(u * kDlsT + threadIdx.x) * 4;
+        if (col >= ldd)
+            continue;
+        float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (have) {
+            if (col + 4 <= V) {
+                const float4 q = *reinterpret_cast<const float4 *>(lrow + col);
+                z[0] = q.x;
+                z[1] = q.y;
+                z[2] = q.z;
+                z[3] = q.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (col + i < V)
+                        z[i] = lrow[col + i];
+            }
+        }
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float e = exp2_hw(fmaf(z[i] - rc.mz, c, -rc.kexp)) - rc.ev;
+            if (col + i == lab)
+                e = rc.tv;
+            if (col + i >= V)
+                e = 0.0f;
+            o[i] = __uint_as_float(__float_as_uint(e) ^ sgn);
+        }
+        uint2 pk;
+        pk.x = pack_bf16x2(o[0], o[1]);
+        pk.y = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<uint2 *>(drow + col) = pk;
+    }
 }
 
 // C[M, N] (fp32, row stride ldc) = sum_k A[m][k] B[n][k], A and B
@@ -1061,18 +1141,27 @@ int64_t lce_splits(int64_t rows, int64_t vocab)
 
 int64_t lce_dl_stride(int64_t vocab) { return round64(vocab); }
 
-hipError_t launch_lce_forward(const LceArgs &a, bool want_h, bool want_z, hipStream_t s)
+template <bool STORE>
+void launch_lce_fwd_t(const LceArgs &a, bool want_h, bool want_z, hipStream_t s)
 {
     const int64_t nrb = (a.rows + kBM - 1) / kBM;
     dim3 grid((unsigned)(nrb * a.splits)), block(kLT);
     if (want_h && want_z)
-        hipLaunchKernelGGL((k_lce_fwd<true, true>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_lce_fwd<true, true, STORE>), grid, block, 0, s, a);
     else if (want_h)
-        hipLaunchKernelGGL((k_lce_fwd<true, false>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_lce_fwd<true, false, STORE>), grid, block, 0, s, a);
     else if (want_z)
-        hipLaunchKernelGGL((k_lce_fwd<false, true>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_lce_fwd<false, true, STORE>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((k_lce_fwd<false, false>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_lce_fwd<false, false, STORE>), grid, block, 0, s, a);
+}
+
+hipError_t launch_lce_forward(const LceArgs &a, bool want_h, bool want_z, hipStream_t s)
+{
+    if (a.logits_out)
+        launch_lce_fwd_t<true>(a, want_h, want_z, s);
+    else
+        launch_lce_fwd_t<false>(a, want_h, want_z, s);
     return hipGetLastError();
 }
 
@@ -1101,7 +1190,13 @@ hipError_t launch_lce_backward(const LceArgs &a, void *workspace, float *dhidden
     b.ldd = vp;
     b.dl_rows = rp;
     const int64_t nrb = (R + kBM - 1) / kBM;
-    hipLaunchKernelGGL(k_lce_dl, dim3((unsigned)(nrb * b.splits)), dim3(kLT), 0, s, b);
+    if (a.logits_in) {
+        const int64_t chunks = (vp + kDlsCols - 1) / kDlsCols;
+        hipLaunchKernelGGL(k_lce_dl_stored, dim3((unsigned)(rp * chunks)), dim3(kDlsT), 0, s, b,
+                           chunks);
+    } else {
+        hipLaunchKernelGGL(k_lce_dl, dim3((unsigned)(nrb * b.splits)), dim3(kLT), 0, s, b);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;

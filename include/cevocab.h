@@ -398,16 +398,23 @@ int ce_vocab_shard_backward(const void *logits, int64_t rows, int64_t shard_voca
 /* lce_forward -- loss, log p, entropy, argmax and the saved record of every
  * row, as ce_forward computes them from the logits hidden x head^T (argmax:
  * lowest column of the largest fp32 logit).  loss and saved are required;
- * logp, entropy and argmax may be NULL. */
+ * logp, entropy and argmax may be NULL.
+ *   logits, logits_stride   NULL (the logits are never stored), or a
+ *                 caller-owned fp32 [rows, logits_stride] buffer (stride >=
+ *                 vocab, a multiple of 4, 16-byte aligned) that receives the
+ *                 logits of every row: memory traded for the backward's
+ *                 recomputation (see lce_backward). */
 int lce_forward(const void *hidden, int64_t rows, int64_t hidden_dim, int64_t hidden_stride,
                 const void *weight, int64_t vocab, int64_t weight_stride, const int64_t *labels,
                 int64_t ignore_index, double temperature, double label_smoothing,
                 const uint8_t *row_mask, float *loss, void *saved, float *logp, float *entropy,
-                int64_t *argmax, void *workspace, size_t workspace_bytes, int32_t *status,
-                cev_stream_t stream);
+                int64_t *argmax, float *logits, int64_t logits_stride, void *workspace,
+                size_t workspace_bytes, int32_t *status, cev_stream_t stream);
 
 /* lce_backward -- with dlogits = ce_backward's gradient of the per-row loss
- * weighted by g (recomputed from hidden, head and the saved record):
+ * weighted by g (from the saved record and the logits, recomputed from
+ * hidden and head, or read from `logits` when the forward stored them there:
+ * the same fp32 values, so the same dlogits bit for bit):
  *   dhidden = dlogits x head   [rows, dhidden_stride] fp32, required
  *   dweight = dlogits^T x hidden   [vocab, dweight_stride] fp32, or NULL for a
  *             frozen head
@@ -417,9 +424,9 @@ int lce_backward(const void *hidden, int64_t rows, int64_t hidden_dim, int64_t h
                  const void *weight, int64_t vocab, int64_t weight_stride,
                  const int64_t *labels, int64_t ignore_index, double temperature,
                  double label_smoothing, const uint8_t *row_mask, const float *g,
-                 const void *saved, float *dhidden, int64_t dhidden_stride, float *dweight,
-                 int64_t dweight_stride, void *workspace, size_t workspace_bytes,
-                 int32_t *status, cev_stream_t stream);
+                 const void *saved, const float *logits, int64_t logits_stride, float *dhidden,
+                 int64_t dhidden_stride, float *dweight, int64_t dweight_stride, void *workspace,
+                 size_t workspace_bytes, int32_t *status, cev_stream_t stream);
 
 /* Bytes of workspace lce_forward and lce_backward need (0 for invalid
  * arguments). */

@@ -313,13 +313,13 @@ def test_product_never_imports_the_oracle():
 def test_lce_validation(lib):
     def fwd(**kw):
         a = dict(h=A, rows=4, hd=128, hs=128, w=B, V=1000, ws=128, labels=A, ig=-100, T=1.0,
-                 eps=0.0, mask=None, loss=A, saved=A, logp=None, ent=None, arg=None, wk=A,
-                 wkb=1 << 30, status=None)
+                 eps=0.0, mask=None, loss=A, saved=A, logp=None, ent=None, arg=None, lg=None,
+                 lgs=0, wk=A, wkb=1 << 30, status=None)
         a.update(kw)
         return lib.lce_forward(a["h"], a["rows"], a["hd"], a["hs"], a["w"], a["V"], a["ws"],
                                a["labels"], a["ig"], a["T"], a["eps"], a["mask"], a["loss"],
-                               a["saved"], a["logp"], a["ent"], a["arg"], a["wk"], a["wkb"],
-                               a["status"], None)
+                               a["saved"], a["logp"], a["ent"], a["arg"], a["lg"], a["lgs"],
+                               a["wk"], a["wkb"], a["status"], None)
     assert fwd(hd=100, hs=104) == E["SHAPE"]          # hidden size not a multiple of 64
     assert fwd(hd=0) == E["SHAPE"]
     assert fwd(hs=120) == E["STRIDE"]
@@ -334,25 +334,32 @@ def test_lce_validation(lib):
     assert fwd(eps=-1.0) == E["SMOOTH"]
     assert fwd(V=0) == E["SHAPE"]
     assert fwd(rows=0, h=None, w=None) == E["OK"]
+    # stored logits: row stride at least the vocab and a multiple of 4, 16-byte aligned
+    assert fwd(lg=A, lgs=996) == E["STRIDE"]
+    assert fwd(lg=A, lgs=1002) == E["STRIDE"]
+    assert fwd(lg=A + 4, lgs=1000) == E["ALIGN"]
+    assert fwd(lg=None, lgs=7, wkb=0) == E["WORKSPACE"]   # stride ignored without logits
     # dlogits [R64, V64] (bf16) and up to 8 split-K partial products of dhidden (fp32)
     assert lib.lce_workspace_size(8192, 2560, 151936) == 2 * 8192 * 151936 + 8 * 8192 * 2560 * 4
     assert lib.lce_workspace_size(8, 100, 10) == 0
 
     def bwd(**kw):
         a = dict(h=A, rows=4, hd=128, hs=128, w=B, V=1000, ws=128, labels=A, ig=-100, T=1.0,
-                 eps=0.0, mask=None, g=A, saved=A, dh=A, dhs=128, dw=None, dws=0, wk=A,
-                 wkb=1 << 30, status=None)
+                 eps=0.0, mask=None, g=A, saved=A, lg=None, lgs=0, dh=A, dhs=128, dw=None,
+                 dws=0, wk=A, wkb=1 << 30, status=None)
         a.update(kw)
         return lib.lce_backward(a["h"], a["rows"], a["hd"], a["hs"], a["w"], a["V"], a["ws"],
                                 a["labels"], a["ig"], a["T"], a["eps"], a["mask"], a["g"],
-                                a["saved"], a["dh"], a["dhs"], a["dw"], a["dws"], a["wk"],
-                                a["wkb"], a["status"], None)
+                                a["saved"], a["lg"], a["lgs"], a["dh"], a["dhs"], a["dw"],
+                                a["dws"], a["wk"], a["wkb"], a["status"], None)
     assert bwd(dhs=64) == E["STRIDE"]
     assert bwd(dw=B, dws=100) == E["STRIDE"]
     assert bwd(dh=None) == E["NULL"]
     assert bwd(g=None) == E["NULL"]
     assert bwd(saved=A + 4) == E["ALIGN"]
     assert bwd(wkb=16) == E["WORKSPACE"]
+    assert bwd(lg=A, lgs=999) == E["STRIDE"]
+    assert bwd(lg=A + 8, lgs=1000) == E["ALIGN"]
     assert bwd(rows=0) == E["OK"]
 
 

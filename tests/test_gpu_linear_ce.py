@@ -65,7 +65,7 @@ def padded_dev(bits, stride):
     return torch.from_numpy(buf.view(np.int16)).to(DEV).view(torch.bfloat16)[:, :H]
 
 
-def run_lce(w, eps=0.0, entropy=True, dweight=True, hs=None, ws=None):
+def run_lce(w, eps=0.0, entropy=True, dweight=True, hs=None, ws=None, logits=None):
     from gpu_helpers import DEV, to_dev, to_host
     R, H = w["hidden"].shape
     V = w["weight"].shape[0]
@@ -77,10 +77,10 @@ def run_lce(w, eps=0.0, entropy=True, dweight=True, hs=None, ws=None):
     T = w["temperature"]
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
     out = cev.lce_forward(hid, wt, labels, T, row_mask=mask, label_smoothing=eps,
-                          entropy=entropy, argmax=True, status=status)
+                          entropy=entropy, argmax=True, status=status, logits=logits)
     dh, dw = cev.lce_backward(hid, wt, labels, g, out["saved"], T, row_mask=mask,
                               label_smoothing=eps, dweight=dweight, status=status,
-                              workspace=out["workspace"])
+                              workspace=out["workspace"], logits=out["logits"])
     torch.cuda.synchronize()
     ldd = (V + 63) // 64 * 64
     dl = out["workspace"][:R * ldd * 2].view(torch.bfloat16).view(R, ldd)
@@ -226,3 +226,65 @@ def test_lce_random_bf16_bound():
         top = z[r].max()
         assert z[r, got["argmax"][r]] >= top - 2 * dz[r], r
     say(f"  worst loss error / bound: {float(np.max(err / bound)):.3f}")
+
+
+STORED = {
+    "200x128x1000": dict(R=200, H=128, V=1000, seed=1, n_ignored=9),
+    "300x256x4099_T0.7": dict(R=300, H=256, V=4099, seed=2, T=0.7, mask_frac=0.1),
+    "64x64x7": dict(R=64, H=64, V=7, seed=4, n_ignored=3),
+    "257x1024x2053_peaked": dict(R=257, H=1024, V=2053, seed=6, peaked=40, mask_frac=0.05),
+}
+
+
+@pytest.mark.parametrize("name", sorted(STORED))
+def test_lce_stored_logits_exact(name):
+    """The forward's stored logits equal the exact product (the oracle's), and
+    a backward that reads them back gives the recomputing backward's dlogits,
+    dhidden and dhead bit for bit (both apply one formula to one fp32 value)."""
+    from gpu_helpers import say
+    say(f"[lce stored logits] {name}")
+    w = grid_case(**STORED[name])
+    V = w["weight"].shape[0]
+    ref = run_lce(w)
+    got = run_lce(w, logits=True)
+    z = oracle.linear_logits(w["hidden"], w["weight"])
+    assert np.array_equal(got["logits"].astype(np.float64), z), name
+    for k in ("loss", "logp", "entropy", "argmax", "saved", "dlogits", "dhidden", "dweight"):
+        assert np.array_equal(got[k], ref[k]), (name, k)
+    check_exact(w, got, name + " stored")
+    assert got["status"] == 0
+
+
+def test_lce_stored_logits_strided_smoothing():
+    """A caller-owned logits buffer with a padded row stride (its padding left
+    untouched) under label smoothing and padded operand strides."""
+    from gpu_helpers import DEV, say
+    say("[lce stored logits] stride 3012, smoothing 0.1")
+    w = grid_case(R=150, H=192, V=3001, seed=7, T=1.1, peaked=30, n_ignored=5)
+    R, V = 150, 3001
+    buf = torch.full((R, 3012), 7.5, dtype=torch.float32, device=DEV)
+    ref = run_lce(w, eps=0.1, hs=200, ws=264)
+    got = run_lce(w, eps=0.1, hs=200, ws=264, logits=buf[:, :V])
+    z = oracle.linear_logits(w["hidden"], w["weight"])
+    assert np.array_equal(buf[:, :V].cpu().numpy().astype(np.float64), z)
+    assert bool((buf[:, V:] == 7.5).all())
+    for k in ("loss", "logp", "entropy", "argmax", "saved", "dlogits", "dhidden", "dweight"):
+        assert np.array_equal(got[k], ref[k]), k
+
+
+def test_lce_stored_logits_random_bf16_identical():
+    """Random bf16 inputs: the stored logits are the forward's own fp32 sums,
+    and the backward reading them matches the recomputing one bit for bit
+    (the product is summed in one order by both)."""
+    from gpu_helpers import say
+    say("[lce stored logits] random 200x2560x6000 bf16")
+    w = workloads.linear(rows=200, hidden=2560, vocab=6000, peaked_frac=0.25)
+    ref = run_lce(w, dweight=True)
+    got = run_lce(w, dweight=True, logits=True)
+    for k in ("loss", "logp", "entropy", "argmax", "saved", "dlogits", "dhidden", "dweight"):
+        assert np.array_equal(got[k], ref[k]), k
+    # the stored logits within the product's fp32 bound of the exact ones
+    H = w["hidden"].shape[1]
+    z = oracle.linear_logits(w["hidden"], w["weight"])
+    absz = np.abs(oracle._widen(w["hidden"])) @ np.abs(oracle._widen(w["weight"])).T
+    assert np.all(np.abs(got["logits"] - z) <= (H / 16 + 2) * U * absz + 1e-30)
