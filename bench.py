@@ -66,7 +66,7 @@ def measured_traffic():
 # against algorithmic bytes.  Each kernel is matched by a regular expression
 # on its name without the namespace and argument list.
 COUNTER_WORKLOADS = ("grpo", "chunk", "peaked_f32", "peaked_bf16", "jsd_b0", "jsd_b05", "jsd_b1",
-                     "linear")
+                     "linear", "linear_stored")
 
 
 def _short_name(name):
@@ -168,23 +168,30 @@ def run_counter_workload(name, torch, cev, workloads, dev, reps=3):
             dict(regex=r"^k_jsd_forward<", call="jsd_forward", read=2 * nv * V * 2, write=0),
             dict(regex=r"^k_jsd_(bwd_tiles|backward)<", call="jsd_backward",
                  read=2 * nv * V * 2, write=R * V * 2, per_call=True)]
-    elif name == "linear":
+    elif name in ("linear", "linear_stored"):
         R, H, V = 8192, 2560, 151936
+        stored = name == "linear_stored"
         w = workloads.linear(rows=R, hidden=H, vocab=V)
         hid = torch.from_numpy(w["hidden"].view(np.int16)).to(dev).view(torch.bfloat16)
         head = torch.from_numpy(w["weight"].view(np.int16)).to(dev).view(torch.bfloat16)
         lab, msk = torch.from_numpy(w["labels"]).to(dev), torch.from_numpy(w["row_mask"]).to(dev)
         gl = torch.from_numpy(w["g"]).to(dev)
+        zs = torch.empty((R, V), dtype=torch.float32, device=dev) if stored else None
         for _ in range(reps):
-            out = cev.lce_forward(hid, head, lab, 1.0, row_mask=msk, argmax=True)
+            out = cev.lce_forward(hid, head, lab, 1.0, row_mask=msk, argmax=True, logits=zs)
             cev.lce_backward(hid, head, lab, gl, out["saved"], 1.0, row_mask=msk,
-                             workspace=out["workspace"])
+                             workspace=out["workspace"], logits=zs)
         desc = (f"linear CE, hidden {R}x{H}, head {V}x{H} bf16, forward with argmax and the "
-                f"frozen-head backward (dhidden); bytes are each operand read once and each "
-                f"output written once (the kernels are bound by the matrix cores, not HBM)")
+                f"frozen-head backward (dhidden)"
+                + (", the fp32 logits stored by the forward and read back by the backward"
+                   if stored else "")
+                + "; bytes are each operand read once and each output written once")
         ops = R * H * 2 + V * H * 2
         kernels = [
-            dict(regex=r"^k_lce_fwd<", call="lce_forward", read=ops, write=0),
+            dict(regex=r"^k_lce_fwd<", call="lce_forward", read=ops,
+                 write=R * V * 4 if stored else 0),
+            dict(regex=r"^k_lce_dl_stored", call="lce_backward: dlogits from the stored logits",
+                 read=R * V * 4, write=R * V * 2) if stored else
             dict(regex=r"^k_lce_dl", call="lce_backward: logits again, dlogits", read=ops,
                  write=R * V * 2),
             dict(regex=r"^k_lce_gemm", call="lce_backward: dhidden, split-K partials",
