@@ -873,11 +873,15 @@ __device__ __forceinline__ DlRow dl_row(const LceArgs &a, int64_t r, int &lab, u
     return rc;
 }
 
+// SMOOTH: label smoothing is on (eps/V comes off every column; without it
+// that term is zero and skipped).
+template <bool SMOOTH>
 __global__ __launch_bounds__(kLT) void k_lce_dl(LceArgs a)
 {
     __shared__ GemmSmem sm;
-    __shared__ DlRow s_rc[kBM];
-    __shared__ int2 s_ls[kBM];     // label, sign bit of g
+    // per row: {m_z, kexp, eps/V term, sign bit of g} and {label, target value}
+    __shared__ float4 s_rc[kBM];
+    __shared__ int2 s_lt[kBM];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 1, wn = w & 1;
     const int64_t S = a.splits;
@@ -891,18 +895,22 @@ __global__ __launch_bounds__(kLT) void k_lce_dl(LceArgs a)
     if (tid < kBM) {
         int lab;
         unsigned sgn;
-        s_rc[tid] = dl_row(a, row0 + tid, lab, sgn);
-        s_ls[tid] = make_int2(lab, (int)sgn);
+        const DlRow rc = dl_row(a, row0 + tid, lab, sgn);
+        s_rc[tid] = make_float4(rc.mz, rc.kexp, rc.ev, __uint_as_float(sgn));
+        s_lt[tid] = make_int2(lab, (int)__float_as_uint(rc.tv));
     }
     __syncthreads();
     const float c = a.c;
-    unsigned short *dl = a.dlogits;
+    // dl_rows is a multiple of 64: a wave's 64 rows are all below it or none is
+    const bool wave_rows = row0 + wm * 64 < a.dl_rows;
 
     // the label of row wm * 64 + lane: which tiles hold a target for this wave
-    const int mylab = s_ls[wm * 64 + lane].x;
+    const int mylab = s_lt[wm * 64 + lane].x;
 
     // Each lane writes its four adjacent columns of a row as one 8-byte store
     // (ldd is a multiple of 64, so a group of four is wholly inside or past it).
+    // The lane's 32 rows are wm * 64 + 4 * half + k for k = 32 mb + 8 (v / 4) +
+    // v % 4, so one 64-bit address per tile plus a wave-uniform k * ldd per row.
     // MASK (wave-uniform, rare): some of this wave's columns lie past V or
     // hold the target of one of its rows.
     auto tile_body = [&](int64_t tile, f32x16(&acc)[kTM][kTN], auto mask) {
@@ -911,24 +919,27 @@ __global__ __launch_bounds__(kLT) void k_lce_dl(LceArgs a)
         const int64_t c0 = lane_col(tile, wn, el);
         if (c0 >= ldd)
             return;
+        const int half = el >> 5;
+        const int rb0 = wm * 64 + 4 * half;
+        unsigned short *lbase = a.dlogits + (row0 + rb0) * ldd + c0;
 #pragma unroll
         for (int mb = 0; mb < kTM; ++mb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int rl = acc_row(wm, mb, v, el);
-                const int64_t r = row0 + rl;
-                if (r >= a.dl_rows)   // rows in [rows, dl_rows) come out as zeros
-                    continue;
-                const DlRow rc = s_rc[rl];
-                const unsigned sgn = (unsigned)s_ls[rl].y;
+                const int k = mb * 32 + 8 * (v / 4) + v % 4;
+                const float4 rc = s_rc[rb0 + k];
+                const unsigned sgn = __float_as_uint(rc.w);
                 float o[kTN];
 #pragma unroll
                 for (int nb = 0; nb < kTN; ++nb) {
-                    float e = exp2_hw(fmaf(acc[mb][nb][v] - rc.mz, c, -rc.kexp)) - rc.ev;
+                    float e = exp2_hw(fmaf(acc[mb][nb][v] - rc.x, c, -rc.y));
+                    if constexpr (SMOOTH)
+                        e -= rc.z;
                     if constexpr (MASK) {
                         const int64_t col = c0 + nb;
-                        if (col == s_ls[rl].x)
-                            e = rc.tv;
+                        const int2 lt = s_lt[rb0 + k];
+                        if (col == lt.x)
+                            e = __int_as_float(lt.y);
                         if (col >= V)
                             e = 0.0f;
                     }
@@ -937,10 +948,12 @@ __global__ __launch_bounds__(kLT) void k_lce_dl(LceArgs a)
                 uint2 pk;
                 pk.x = pack_bf16x2(o[0], o[1]);
                 pk.y = pack_bf16x2(o[2], o[3]);
-                *reinterpret_cast<uint2 *>(dl + r * ldd + c0) = pk;
+                *reinterpret_cast<uint2 *>(lbase + (int64_t)k * ldd) = pk;
             }
     };
     auto epi = [&](int64_t tile, f32x16(&acc)[kTM][kTN]) {
+        if (!wave_rows)   // rows at or past dl_rows: nothing to write
+            return;
         const int64_t cw = tile * kBN + wn * 128;   // this wave's first column
         const bool tail = cw + 128 > V;
         const bool hit = __any(mylab >= cw && mylab < cw + 128);
@@ -1195,7 +1208,12 @@ hipError_t launch_lce_backward(const LceArgs &a, void *workspace, float *dhidden
         hipLaunchKernelGGL(k_lce_dl_stored, dim3((unsigned)(rp * chunks)), dim3(kDlsT), 0, s, b,
                            chunks);
     } else {
-        hipLaunchKernelGGL(k_lce_dl, dim3((unsigned)(nrb * b.splits)), dim3(kLT), 0, s, b);
+        if (a.label_smoothing != 0.0)
+            hipLaunchKernelGGL(k_lce_dl<true>, dim3((unsigned)(nrb * b.splits)), dim3(kLT), 0, s,
+                               b);
+        else
+            hipLaunchKernelGGL(k_lce_dl<false>, dim3((unsigned)(nrb * b.splits)), dim3(kLT), 0,
+                               s, b);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
