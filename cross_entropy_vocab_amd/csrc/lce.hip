@@ -654,6 +654,8 @@ __global__ __launch_bounds__(kLT) void k_lce_fwd(LceArgs a)
     s_mr[w][lane] = -INFINITY;
     // the label of row wm * 64 + lane: which tiles hold a target for this wave
     const int mylab = s_lab[wm * 64 + lane];
+    // every row of this wave's 64 lies below rows (no per-row check on stores)
+    const bool all_rows = row0 + wm * 64 + 64 <= a.rows;
 
     // One tile: MASK (wave-uniform, rare) when some of this wave's columns
     // lie past V or hold the target of one of its rows; those columns count
@@ -662,6 +664,15 @@ __global__ __launch_bounds__(kLT) void k_lce_fwd(LceArgs a)
         constexpr bool MASK = decltype(mask)::value;
         const int el = opaque_lane();
         const int64_t c0 = lane_col(tile, wn, el);
+        // stored logits: this lane's rows are row0 + rb0 + k (k below)
+        const int rb0 = wm * 64 + 4 * (el >> 5);
+        float *lrow0 = STORE ? a.logits_out + (row0 + rb0) * a.ldl + c0 : nullptr;
+        // the row stride as a value the compiler cannot hoist: the 32 products
+        // k * ldl are then formed per tile on the scalar unit instead of being
+        // kept live through the K loop
+        int64_t ldl = a.ldl;
+        if constexpr (STORE)
+            asm volatile("" : "+s"(ldl));
         // Each slot's terms at the running maximum; where some lane of the
         // wave sees a larger value (wave-uniform branch, about ln(tiles) times
         // per row), at the tile's maximum instead, whose value and first
@@ -689,10 +700,14 @@ __global__ __launch_bounds__(kLT) void k_lce_fwd(LceArgs a)
                 for (int nb = 0; nb < kTN; ++nb)
                     x[nb] = acc[mb][nb][v];
                 if constexpr (STORE) {
-                    // the raw logits of this lane's four columns, one 16-byte store
-                    const int64_t r = row0 + acc_row(wm, mb, v, el);
-                    if (r < a.rows) {
-                        float *dst = a.logits_out + r * a.ldl + c0;
+                    // the raw logits of this lane's four columns, one 16-byte
+                    // store at the tile's lane address plus k rows
+                    const int k = mb * 32 + 8 * (v / 4) + v % 4;
+                    float *dst = lrow0 + (int64_t)k * ldl;
+                    if constexpr (!MASK) {
+                        if (all_rows || row0 + rb0 + k < a.rows)
+                            *reinterpret_cast<float4 *>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+                    } else if (row0 + rb0 + k < a.rows) {
                         if (c0 + kTN <= V) {
                             *reinterpret_cast<float4 *>(dst) = make_float4(x[0], x[1], x[2], x[3]);
                         } else {
