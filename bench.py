@@ -187,11 +187,12 @@ def run_counter_workload(name, torch, cev, workloads, dev, reps=3):
                    if stored else "")
                 + "; bytes are each operand read once and each output written once")
         ops = R * H * 2 + V * H * 2
+        nv = int(((w["labels"] != -100) & (w["row_mask"] != 0)).sum())   # rows read back
         kernels = [
             dict(regex=r"^k_lce_fwd<", call="lce_forward", read=ops,
                  write=R * V * 4 if stored else 0),
             dict(regex=r"^k_lce_dl_stored", call="lce_backward: dlogits from the stored logits",
-                 read=R * V * 4, write=R * V * 2) if stored else
+                 read=nv * V * 4, write=R * V * 2) if stored else
             dict(regex=r"^k_lce_dl", call="lce_backward: logits again, dlogits", read=ops,
                  write=R * V * 2),
             dict(regex=r"^k_lce_gemm", call="lce_backward: dhidden, split-K partials",

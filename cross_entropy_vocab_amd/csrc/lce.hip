@@ -992,37 +992,48 @@ __global__ __launch_bounds__(kDlsT) void k_lce_dl_stored(LceArgs a, int64_t chun
 {
     const int64_t r = blockIdx.x / chunks, ch = blockIdx.x % chunks;
     const int64_t V = a.vocab, ldd = a.ldd;
+    // The saved record's valid flag first, then every load of the chunk:
+    // only rows the forward read have logits worth loading (masked, ignored
+    // and padding rows come out as zeros), and the row's other constants
+    // arrive while those loads are in flight.
+    const bool have = r < a.rows && (a.saved[r].flags & 1);
+    const float *lrow = a.logits_in + (have ? r : 0) * a.ldl;
+    float z[kDlsU][4];
+#pragma unroll
+    for (int u = 0; u < kDlsU; ++u) {
+        const int64_t col = ch * kDlsCols + (int64_t)(u * kDlsT + threadIdx.x) * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            z[u][i] = 0.0f;
+        if (have && col < ldd) {
+            if (col + 4 <= V) {
+                const float4 q = *reinterpret_cast<const float4 *>(lrow + col);
+                z[u][0] = q.x;
+                z[u][1] = q.y;
+                z[u][2] = q.z;
+                z[u][3] = q.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (col + i < V)
+                        z[u][i] = lrow[col + i];
+            }
+        }
+    }
     int lab;
     unsigned sgn;
     const DlRow rc = dl_row(a, r, lab, sgn);
     const float c = a.c;
-    const bool have = r < a.rows;
-    const float *lrow = a.logits_in + (have ? r : 0) * a.ldl;
     unsigned short *drow = a.dlogits + r * ldd;
 #pragma unroll
     for (int u = 0; u < kDlsU; ++u) {
         const int64_t col = ch * kDlsCols + (int64_t)(u * kDlsT + threadIdx.x) * 4;
         if (col >= ldd)
             continue;
-        float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (have) {
-            if (col + 4 <= V) {
-                const float4 q = *reinterpret_cast<const float4 *>(lrow + col);
-                z[0] = q.x;
-                z[1] = q.y;
-                z[2] = q.z;
-                z[3] = q.w;
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (col + i < V)
-                        z[i] = lrow[col + i];
-            }
-        }
         float o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float e = exp2_hw(fmaf(z[i] - rc.mz, c, -rc.kexp)) - rc.ev;
+            float e = exp2_hw(fmaf(z[u][i] - rc.mz, c, -rc.kexp)) - rc.ev;
             if (col + i == lab)
                 e = rc.tv;
             if (col + i >= V)
