@@ -229,6 +229,8 @@ def test_lce_random_bf16_bound():
 
 
 STORED = {
+    "1x192x300": dict(R=1, H=192, V=300, seed=5),
+    "70x64x3": dict(R=70, H=64, V=3, seed=10, n_ignored=2),
     "200x128x1000": dict(R=200, H=128, V=1000, seed=1, n_ignored=9),
     "300x256x4099_T0.7": dict(R=300, H=256, V=4099, seed=2, T=0.7, mask_frac=0.1),
     "64x64x7": dict(R=64, H=64, V=7, seed=4, n_ignored=3),
