@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 
 #include "cev_launch.h"
 #include "cevocab.h"
@@ -674,9 +675,24 @@ static cev::LceArgs lce_args(const void *hidden, int64_t rows, int64_t hd, int64
     return a;
 }
 
+// Bytes [b, e) that a row-major matrix of `rows` rows of `cols` elements
+// (row stride `stride`, `es` bytes each) touches; empty for a NULL pointer.
+struct Span {
+    uintptr_t b, e;
+};
+static Span span(const void *p, int64_t rows, int64_t cols, int64_t stride, int64_t es)
+{
+    if (!p || rows <= 0 || cols <= 0)
+        return Span{0, 0};
+    const uintptr_t b = (uintptr_t)p;
+    return Span{b, b + (uintptr_t)(((rows - 1) * stride + cols) * es)};
+}
+
 // Optional stored fp32 logits [rows, logits_stride]: the stride covers the
-// vocabulary and keeps rows 16-byte aligned.
-static int check_lce_logits(const float *logits, int64_t logits_stride, int64_t vocab)
+// vocabulary and keeps rows 16-byte aligned, and the buffer overlaps none of
+// the other arguments' memory (`others`).
+static int check_lce_logits(const float *logits, int64_t logits_stride, int64_t rows,
+                            int64_t vocab, std::initializer_list<Span> others)
 {
     if (!logits)
         return CEV_OK;
@@ -684,6 +700,10 @@ static int check_lce_logits(const float *logits, int64_t logits_stride, int64_t 
         return CEV_ESTRIDE;
     if (!aligned(logits, 16))
         return CEV_EALIGN;
+    const Span z = span(logits, rows, vocab, logits_stride, 4);
+    for (const Span &o : others)
+        if (o.b < z.e && z.b < o.e)
+            return CEV_EALIAS;
     return CEV_OK;
 }
 
@@ -705,7 +725,10 @@ int lce_forward(const void *hidden, int64_t rows, int64_t hidden_dim, int64_t hi
         !aligned(entropy, 4) || !aligned(argmax, 8) || !aligned(workspace, 16) ||
         !aligned(status, 4))
         return CEV_EALIGN;
-    if ((rc = check_lce_logits(logits, logits_stride, vocab)) != CEV_OK)
+    if ((rc = check_lce_logits(logits, logits_stride, rows, vocab,
+                               {span(hidden, rows, hidden_dim, hidden_stride, 2),
+                                span(weight, vocab, hidden_dim, weight_stride, 2),
+                                span(workspace, 1, (int64_t)workspace_bytes, 0, 1)})) != CEV_OK)
         return rc;
     if (workspace_bytes < lce_workspace_size(rows, hidden_dim, vocab))
         return CEV_EWORKSPACE;
@@ -758,7 +781,10 @@ int lce_backward(const void *hidden, int64_t rows, int64_t hidden_dim, int64_t h
     if (!aligned(labels, 8) || !aligned(g, 4) || !aligned(saved, 16) || !aligned(dhidden, 4) ||
         !aligned(dweight, 4) || !aligned(workspace, 16) || !aligned(status, 4))
         return CEV_EALIGN;
-    if ((rc = check_lce_logits(logits, logits_stride, vocab)) != CEV_OK)
+    if ((rc = check_lce_logits(logits, logits_stride, rows, vocab,
+                               {span(dhidden, rows, hidden_dim, dhidden_stride, 4),
+                                span(dweight, vocab, hidden_dim, dweight_stride, 4),
+                                span(workspace, 1, (int64_t)workspace_bytes, 0, 1)})) != CEV_OK)
         return rc;
     if (workspace_bytes < lce_workspace_size(rows, hidden_dim, vocab))
         return CEV_EWORKSPACE;
@@ -894,7 +920,7 @@ const char *cev_status_string(int code)
     case CEV_EDTYPE: return "unknown dtype (expected CEV_F32 or CEV_BF16)";
     case CEV_ETEMP: return "temperature must be finite and > 0";
     case CEV_EWORKSPACE: return "workspace smaller than cev_workspace_size(rows)";
-    case CEV_EALIAS: return "dlogits overlaps logits";
+    case CEV_EALIAS: return "an output overlaps an input it is computed from";
     case CEV_ELAUNCH: return "kernel launch failed";
     case CEV_ESMOOTH: return "label_smoothing must be finite and in [0, 1]";
     case CEV_EBETA: return "beta must be finite and in [0, 1]";

@@ -74,7 +74,7 @@ enum cev_error {
     CEV_EDTYPE = -5,       /* unknown dtype */
     CEV_ETEMP = -6,        /* temperature not finite or not > 0 */
     CEV_EWORKSPACE = -7,   /* workspace too small */
-    CEV_EALIAS = -8,       /* dlogits overlaps logits */
+    CEV_EALIAS = -8,       /* an output overlaps an input it is computed from */
     CEV_ELAUNCH = -9,      /* the HIP runtime refused a launch */
     CEV_ESMOOTH = -10,     /* label_smoothing not finite or outside [0, 1] */
     CEV_EBETA = -11,       /* jsd beta not finite or outside [0, 1] */
@@ -401,9 +401,13 @@ int ce_vocab_shard_backward(const void *logits, int64_t rows, int64_t shard_voca
  * logp, entropy and argmax may be NULL.
  *   logits, logits_stride   NULL (the logits are never stored), or a
  *                 caller-owned fp32 [rows, logits_stride] buffer (stride >=
- *                 vocab, a multiple of 4, 16-byte aligned) that receives the
- *                 logits of every row: memory traded for the backward's
- *                 recomputation (see lce_backward). */
+ *                 vocab, a multiple of 4, 16-byte aligned, overlapping no
+ *                 other argument) that receives z = hidden x head^T (before
+ *                 the temperature) for every row, masked ones included;
+ *                 columns past vocab are left as they were.  Memory traded
+ *                 for the backward's recomputation (see lce_backward).
+ *                 CEV_ESTRIDE / CEV_EALIGN for a bad stride / alignment,
+ *                 CEV_EALIAS if it overlaps hidden, head or the workspace. */
 int lce_forward(const void *hidden, int64_t rows, int64_t hidden_dim, int64_t hidden_stride,
                 const void *weight, int64_t vocab, int64_t weight_stride, const int64_t *labels,
                 int64_t ignore_index, double temperature, double label_smoothing,
@@ -419,7 +423,9 @@ int lce_forward(const void *hidden, int64_t rows, int64_t hidden_dim, int64_t hi
  *   dweight = dlogits^T x hidden   [vocab, dweight_stride] fp32, or NULL for a
  *             frozen head
  * Both strides >= hidden_dim.  dlogits is kept in the workspace in bf16
- * (rounded to nearest even), the operand the two products read. */
+ * (rounded to nearest even), the operand the two products read.  `logits`
+ * (NULL to recompute) is checked as in lce_forward and must not overlap
+ * dhidden, dweight or the workspace (CEV_EALIAS). */
 int lce_backward(const void *hidden, int64_t rows, int64_t hidden_dim, int64_t hidden_stride,
                  const void *weight, int64_t vocab, int64_t weight_stride,
                  const int64_t *labels, int64_t ignore_index, double temperature,

@@ -339,6 +339,13 @@ def test_lce_validation(lib):
     assert fwd(lg=A, lgs=1002) == E["STRIDE"]
     assert fwd(lg=A + 4, lgs=1000) == E["ALIGN"]
     assert fwd(lg=None, lgs=7, wkb=0) == E["WORKSPACE"]   # stride ignored without logits
+    # the stored logits (4 rows x 1000 fp32 = 16000 bytes) overlapping hidden,
+    # the head or the workspace (each case clear of the other two)
+    W2 = 0x80000000
+    assert fwd(lg=A + 512, lgs=1000, wk=W2) == E["ALIAS"]
+    assert fwd(lg=B + 4096, lgs=1000, wk=W2) == E["ALIAS"]
+    assert fwd(lg=0x40000000, lgs=1000, wk=0x40000000 + 16000 - 16) == E["ALIAS"]
+    assert fwd(lg=0x40000000, lgs=1000, wk=0x40000000 + 16000, wkb=0) == E["WORKSPACE"]
     # dlogits [R64, V64] (bf16) and up to 8 split-K partial products of dhidden (fp32)
     assert lib.lce_workspace_size(8192, 2560, 151936) == 2 * 8192 * 151936 + 8 * 8192 * 2560 * 4
     assert lib.lce_workspace_size(8, 100, 10) == 0
@@ -360,6 +367,11 @@ def test_lce_validation(lib):
     assert bwd(wkb=16) == E["WORKSPACE"]
     assert bwd(lg=A, lgs=999) == E["STRIDE"]
     assert bwd(lg=A + 8, lgs=1000) == E["ALIGN"]
+    W2 = 0x80000000
+    assert bwd(lg=A + 1024, lgs=1000, wk=W2) == E["ALIAS"]    # overlaps dhidden
+    assert bwd(lg=0x40000000, lgs=1000, dw=0x40000000 + 4096, dws=128, wk=W2) == E["ALIAS"]
+    assert bwd(lg=0x40000000, lgs=1000, wk=0x40000000 + 15984) == E["ALIAS"]
+    assert bwd(lg=0x40000000, lgs=1000, wk=W2, wkb=16) == E["WORKSPACE"]   # clear of all
     assert bwd(rows=0) == E["OK"]
 
 
