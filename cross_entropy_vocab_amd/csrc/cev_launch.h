@@ -279,8 +279,6 @@ struct FusedArgs {
 };
 
 hipError_t launch_fused(int dtype, const FusedArgs &a, bool want_entropy, hipStream_t stream);
-hipError_t launch_fused_stream_cfg(int dtype, const FusedArgs &a, int block, int U, bool desc,
-                                   size_t lds_bytes, hipStream_t stream);
 
 hipError_t launch_sls_sweep(int dtype, const SweepArgs &a, bool want_entropy, bool want_argmax,
                             hipStream_t stream);
