@@ -380,7 +380,22 @@ def _run_fused(w, logits_dev=None, dl_stride=None, entropy=True):
     return res
 
 
+def _fused_regions_case():
+    """bf16 rows of 77101 columns, targets in every part of ce_fused's row
+    layout: 9637 vectors of 8 make 75 wave steps of 128 vectors (steps 0-31
+    held in registers, 32-63 in LDS, 64-74 read twice), 37 remainder vectors
+    and 5 tail columns; one row peaked on a target in the LDS-held part, one
+    ignored."""
+    w = _rand_case(11, 77101, "bf16", T=0.9, seed=44)
+    w["labels"][:] = [100, 20000, 33000, 60000, 66000, 76000, 76900, 77098, 77100, 40000, -100]
+    z = workloads.bf16_to_f32(w["logits"])
+    z[9, 40000] = z[9].max() + 30.0
+    w["logits"] = workloads.bf16_bits(z)
+    return w
+
+
 FUSED_CASES = {
+    "regions_11x77101_bf16_T0.9": _fused_regions_case,
     "grpo_40x152064_bf16": lambda: workloads.grpo(rows=40, vocab=152064),
     "peaked_16x151936_bf16_T0.9": lambda: workloads.peaked("bf16", 0.9, rows=16),
     "peaked_12x151936_f32_T1_two_pass": lambda: workloads.peaked("f32", 1.0, rows=12),
