@@ -893,7 +893,7 @@ def main():
                      "kernel": "k_backward_tile (ce_backward)", "bytes_per_launch": bwd_bytes},
         "cpu_baseline": None,
         "fused": {"entry": "ce_fused: the same outputs in one call for a g known up front; "
-                           "each valid row swept once, 42% of it held on chip and the rest "
+                           "each valid row swept once, 43% of it held on chip and the rest "
                            "read again at once, every dlogits row written once",
                   "ms_per_step": fused_wall, "kernel_ms": fused_ms,
                   "rows_per_s": R / (fused_wall / 1e3),

@@ -62,8 +62,8 @@ __device__ __forceinline__ void fused_close(const FusedArgs &a, int64_t r, float
 // row order (step k of the row's wave steps is wave k mod 8's).  The vectors
 // of its first S steps stay in registers and those of the next SL steps in
 // LDS (each lane its own) until the second pass, which re-reads only the
-// rest of the row: 8 of the 74 wave steps of each wave's share of a
-// 152064-wide bf16 row, 42% of the row, never leave the CU between the
+// rest of the row: of a 152064-wide bf16 row's 148 wave steps, the 64 that
+// are each wave's first 8 (43% of the row) never leave the CU between the
 // passes.  Registers set the split: more held steps spill.
 template <int DT, bool WANT_H, bool WANT_Z>
 __global__ __launch_bounds__(512, 4) void k_fused_hold(FusedArgs a)
