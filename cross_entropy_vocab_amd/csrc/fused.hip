@@ -64,11 +64,20 @@ __device__ __forceinline__ void fused_close(const FusedArgs &a, int64_t r, float
 // LDS (each lane its own) until the second pass, which re-reads only the
 // rest of the row: of a 152064-wide bf16 row's 148 wave steps, the 64 that
 // are each wave's first 8 (43% of the row) never leave the CU between the
-// passes.  Registers set the split: more held steps spill.
+// passes.  Registers set the split (held_steps): more held steps spill.
+// Wave steps held in registers, per form: as many as fit in 128 VGPRs
+// beside the sweep's own registers with few or no spills (fp32 steps carry
+// half the columns of bf16 ones but unpack into as many registers).
+constexpr int held_steps(int dt, bool want_h, bool want_z)
+{
+    return dt == CEV_F32 ? (want_h && want_z ? 4 : want_h || want_z ? 5 : 6)
+                         : (want_h || want_z ? 3 : 4);
+}
+
 template <int DT, bool WANT_H, bool WANT_Z>
 __global__ __launch_bounds__(512, 4) void k_fused_hold(FusedArgs a)
 {
-    constexpr int BLOCK = 512, U = 2, S = 4, SL = 4;
+    constexpr int BLOCK = 512, U = 2, S = held_steps(DT, WANT_H, WANT_Z), SL = 4;
     constexpr int VE = Elem<DT>::kVE, ES = Elem<DT>::kSize, W = BLOCK / kWave;
     constexpr int64_t CH = (int64_t)kWave * U;
     __shared__ float sh_f[W];
