@@ -1,6 +1,6 @@
 // lce.hip -- linear cross-entropy: logits = hidden x head^T computed tile by
 // tile on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16) and consumed in
-// registers, so the [rows, vocab] logits never reach HBM (the fused linear CE
+// registers, so the [rows, vocab] logits need not reach HBM (the fused linear CE
 // / log-prob setting of the unsloth-zoo #2080 Summary quoted on the
 // Liger-Kernel PR #1555 page).
 //
@@ -18,11 +18,14 @@
 //             logits.
 //   backward  k_lce_dl recomputes each logit tile and writes
 //             dlogits = (g/T)(softmax - onehot) in bf16 (the per-element
-//             formula of k_backward, from the saved record); k_lce_gemm then
-//             forms dhidden = dlogits x head with the head read as stored (its
-//             MFMA fragments formed by transposing LDS reads) and, for a
-//             trainable head, dhead = dlogits^T x hidden with both read
-//             as stored too.
+//             formula of k_backward, from the saved record); when the
+//             forward also stored the fp32 logits (an option that trades
+//             R x V x 4 bytes of memory for the recomputation),
+//             k_lce_dl_stored forms the same dlogits from them instead.
+//             k_lce_gemm then forms dhidden = dlogits x head with the head
+//             read as stored (its MFMA fragments formed by transposing LDS
+//             reads) and, for a trainable head, dhead = dlogits^T x hidden
+//             with both read as stored too.
 //
 // Tiles: 8 waves in a 4 x 2 grid (two per SIMD), each wave 64 x 128 of C as
 // 2 x 4 blocks of 32 x 32; K steps of 64, copied from global memory straight
