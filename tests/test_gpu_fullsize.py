@@ -307,6 +307,25 @@ def test_linear_full_8192x2560x151936():
     say(f"  sampled {rows.size} rows; max logit error bound dz {dz.max():.2e}; "
         f"worst dhidden error / bound {float(np.max(err / bh)):.3f}")
 
+    # The same call pair with the fp32 logits stored by the forward and read
+    # back by the backward: every output bit for bit as recomputed, and the
+    # stored logits of the sampled rows within the product bound of the exact
+    # ones.
+    say("[full] linear 8192x2560x151936 bf16, logits stored")
+    zs = torch.empty((R, V), dtype=torch.float32, device=DEV)
+    o2 = cev.lce_forward(hid, head, labels, T, row_mask=mask, argmax=True, logits=zs)
+    dh2, _ = cev.lce_backward(hid, head, labels, g, o2["saved"], T, row_mask=mask,
+                              workspace=o2["workspace"], logits=zs)
+    torch.cuda.synchronize()
+    for k in ("loss", "logp", "argmax", "saved"):
+        assert torch.equal(o2[k], out[k]), k
+    dl2 = o2["workspace"][:R * ldd * 2].view(torch.int16).view(R, ldd)
+    assert torch.equal(dl2, out["workspace"][:R * ldd * 2].view(torch.int16).view(R, ldd))
+    assert torch.equal(dh2, dh)
+    zsel = zs[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(zsel - z) <= dz[:, None]), float(np.max(np.abs(zsel - z) - dz[:, None]))
+    del zs, o2, dh2
+
 
 @pytest.fixture(scope="module")
 def distill_full():
