@@ -305,8 +305,9 @@ def ce_backward(logits, labels, g, saved, temperature=1.0, row_mask=None, ignore
 def ce_fused(logits, labels, g, temperature=1.0, row_mask=None, ignore_index=-100, logp=True,
              entropy=False, argmax=False, valid_rows=False, dlogits=None, status=None, out=None,
              label_smoothing=0.0):
-    """ce_forward and ce_backward in one call for a g known up front (each row
-    read from HBM about once).  Returns the ce_forward dict plus "dlogits"."""
+    """ce_forward and ce_backward in one call for a g known up front (part of
+    each row held on chip between the sweep and the gradient pass, the rest
+    read again).  Returns the ce_forward dict plus "dlogits"."""
     rows, vocab, stride = _check_logits(logits)
     dev = logits.device
     _dev(labels, "labels", torch.int64, (rows,), dev)
