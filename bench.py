@@ -430,6 +430,16 @@ def bench_linear(args, torch, cev, workloads, dev):
               "backward_TFLOPs": flop / (sb_ms / 1e3) / 1e12}
     del zs
     log(f"[bench] linear CE, stored logits: forward {sf_ms:.2f} ms, backward {sb_ms:.2f} ms")
+    # A trainable head: the backward also forms dhead = dlogits^T x hidden
+    # (one more 2 R H V product), logits recomputed.
+    dwt = torch.empty((Vl, H), dtype=torch.float32, device=dev)
+    (tb_ms,) = _time_calls(torch, [
+        lambda i: cev.lce_backward(hid, head, lab, gl, out["saved"], 1.0, row_mask=msk,
+                                   workspace=out["workspace"], dhidden=dh, dweight=dwt)], steps)
+    del dwt
+    trainable = {"entry": "lce_backward(dweight=True): dlogits, dhidden and dhead",
+                 "backward_ms": tb_ms, "backward_TFLOPs": 3 * flop / (tb_ms / 1e3) / 1e12}
+    log(f"[bench] linear CE, trainable head: backward {tb_ms:.2f} ms")
     res = {"entry": "lce_forward + lce_backward (frozen head: dhidden only), logits never "
                     "stored; 2560 x 151936 head as in the unsloth-zoo #2080 Speed section",
            "shape": {"rows": R, "hidden": H, "vocab": Vl}, "steps": steps,
@@ -441,6 +451,7 @@ def bench_linear(args, torch, cev, workloads, dev):
            "forward_2048_rows_ms": f2_ms,
            "forward_2048_rows_TFLOPs": flop * r2 / R / (f2_ms / 1e3) / 1e12,
            "stored_logits": stored,
+           "trainable_head": trainable,
            "roofline": {"bound": "mfma", "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "achieved": 3 * flop / ((f_ms + b_ms) / 1e3) / 1e12,
                         "frac": 3 * flop / ((f_ms + b_ms) / 1e3) / 1e12 / PEAK_BF16_TFLOPS}}

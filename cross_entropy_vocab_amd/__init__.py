@@ -573,7 +573,7 @@ def lce_backward(hidden, weight, labels, g, saved, temperature=1.0, row_mask=Non
                  workspace=None, dhidden=None, logits=None):
     """Gradients of sum_r g[r] loss[r] through logits = hidden x weight^T:
     dhidden [rows, hidden_dim] fp32, and dweight [vocab, hidden_dim] fp32 when
-    dweight=True (else None, a frozen head).  `logits`: the tensor lce_forward
+    dweight is True or such a tensor to fill (else None, a frozen head).  `logits`: the tensor lce_forward
     stored the logits in, read instead of recomputing them."""
     rows, H = hidden.shape
     dev = hidden.device
@@ -590,7 +590,11 @@ def lce_backward(hidden, weight, labels, g, saved, temperature=1.0, row_mask=Non
         dhidden = torch.empty((rows, H), dtype=torch.float32, device=dev)
     else:
         _dev(dhidden, "dhidden", torch.float32, (rows, H), dev)
-    dw = torch.empty((V, H), dtype=torch.float32, device=dev) if dweight else None
+    if isinstance(dweight, torch.Tensor):
+        _dev(dweight, "dweight", torch.float32, (V, H), dev)
+        dw = dweight
+    else:
+        dw = torch.empty((V, H), dtype=torch.float32, device=dev) if dweight else None
     lg, ldl = _lce_logits(logits, rows, V, dev, allocate=False)
     rc = _lib.get().lce_backward(_ptr(hidden), rows, H, hs, _ptr(weight), V, ws_, _ptr(labels),
                                  int(ignore_index), float(temperature), float(label_smoothing),
