@@ -290,3 +290,21 @@ def test_lce_stored_logits_random_bf16_identical():
     z = oracle.linear_logits(w["hidden"], w["weight"])
     absz = np.abs(oracle._widen(w["hidden"])) @ np.abs(oracle._widen(w["weight"])).T
     assert np.all(np.abs(got["logits"] - z) <= (H / 16 + 2) * U * absz + 1e-30)
+
+
+def test_lce_caller_owned_dweight():
+    """A caller-owned dhead buffer (NaN-filled beforehand) receives the same
+    values, bit for bit, as the one the binding allocates."""
+    from gpu_helpers import DEV, to_dev
+    w = grid_case(R=90, H=128, V=1100, seed=12, n_ignored=4)
+    hid, wt = to_dev(w["hidden"]), to_dev(w["weight"])
+    labels, g = to_dev(w["labels"]), to_dev(np.asarray(w["g"], np.float32))
+    out = cev.lce_forward(hid, wt, labels, 1.0)
+    _, dw = cev.lce_backward(hid, wt, labels, g, out["saved"], 1.0, dweight=True,
+                             workspace=out["workspace"])
+    mine = torch.full((1100, 128), float("nan"), dtype=torch.float32, device=DEV)
+    _, dw2 = cev.lce_backward(hid, wt, labels, g, out["saved"], 1.0, dweight=mine,
+                              workspace=out["workspace"])
+    torch.cuda.synchronize()
+    assert dw2 is mine
+    assert torch.equal(mine, dw)
