@@ -613,7 +613,7 @@ __global__ __launch_bounds__(kJB) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
 // the scale 2^-24.  EXCL: the student's argmax column gets 0 and the entries
 // are summed into sum (the per-row kernel); otherwise every column is written
 // as computed and the caller replaces the argmax one.
-constexpr float kPre = 16777216.0f, kPreInv = 1.0f / 16777216.0f;   // 2^24, 2^-24
+constexpr float kPreInv = 1.0f / 16777216.0f;   // 2^-24: undoes the 2^24 carried in the exponent
 template <int MODE, bool EXCL, int N>
 __device__ __forceinline__ void grad_terms(const float (&zs)[N], const float (&zt)[N],
                                            const JsdRow &rc, float es, float et, float c,

@@ -518,10 +518,6 @@ __device__ __forceinline__ float row_max(float x)
 {
     return row_reduce(x, [](float p, float q) { return fmaxf(p, q); });
 }
-__device__ __forceinline__ float row_sum(float x)
-{
-    return row_reduce(x, [](float p, float q) { return p + q; });
-}
 __device__ __forceinline__ int row_min(int x)
 {
     return row_reduce(x, [](int p, int q) { return min(p, q); });

@@ -21,8 +21,6 @@
 namespace cev {
 namespace {
 
-constexpr int kMaxK = 1024; // gathered indices per row in sls_topk_forward
-
 
 // Per-row closing step (cev_rowclose.h) with the sweep's outputs; zt is the
 // stored target logit.
@@ -271,7 +269,7 @@ __global__ __launch_bounds__(BLOCK) void k_topk_sweep(SweepArgs a)
     __shared__ float sh_f[2 * W];
     __shared__ double sh_d[W];
     // Dynamic LDS sized by K: the gathered columns, their values and terms,
-    // and first-occurrence flags (K <= kMaxK).
+    // and first-occurrence flags (K <= 1024, checked on the host).
     extern __shared__ __align__(16) unsigned char xlds[];
     int64_t *xcol = reinterpret_cast<int64_t *>(xlds);
     double *xterm = reinterpret_cast<double *>(xcol + a.K);
